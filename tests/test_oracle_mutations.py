@@ -1,0 +1,136 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its
+pins catch each one.  A pin set that lets a mutant through is not a pin."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import nystrom_oracle as O
+
+_orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+
+
+def _scale_double(q, k):
+    s = 1.0 / math.sqrt(q.shape[-1])
+    return q * s, k * s
+
+
+def _scale_q_only(q, k):
+    return q / math.sqrt(q.shape[-1]), k
+
+
+def _segments_interleaved(x, m):
+    n, d = x.shape[-2:]
+    return x.reshape(*x.shape[:-2], n // m, m, d).mean(axis=-3)
+
+
+def _softmax_wrong_axis(s, valid=None):
+    s = np.asarray(s, np.float64)
+    e = np.exp(s - s.max(axis=-2, keepdims=True))
+    if valid is not None:
+        e = np.where(np.broadcast_to(valid, s.shape), e, 0.0)
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _softmax_mask_inverted(s, valid=None):
+    return _orig["softmax_rows"](s, None if valid is None else ~np.asarray(valid))
+
+
+def _softmax_no_guard(s, valid=None):
+    s = np.asarray(s, np.float64)
+    if valid is None:
+        return _orig["softmax_rows"](s)
+    sm = np.where(np.broadcast_to(valid, s.shape), s, -np.inf)
+    e = np.exp(sm - sm.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _kernels_no_mask(qs, ks, qt, kt, key_valid=None):
+    return _orig["nystrom_kernels"](qs, ks, qt, kt, None)
+
+
+def _ns_factory(z0_transpose=True, c13=13.0, c15=15.0, c7=7.0, right=True, quarter=0.25):
+    def ns(A, c, n_iter):
+        m = A.shape[-1]
+        I = np.eye(m)
+        Z = (np.swapaxes(A, -1, -2) if z0_transpose else A) / c
+        for _ in range(n_iter):
+            X = A @ Z
+            T = c13 * I - X @ (c15 * I - X @ (c7 * I - X))
+            Z = quarter * (Z @ T if right else T @ Z)
+        return Z
+    return ns
+
+
+def _init_factory(mode):
+    def init(A, init_option):
+        colsum = A.sum(axis=-2)
+        rowsum = A.sum(axis=-1)
+        if mode == "rows_twice":
+            return _plain(rowsum, rowsum, init_option, A)
+        if mode == "no_rowsum":
+            rowsum = np.ones_like(rowsum)
+            return _plain(colsum, rowsum, init_option, A)
+        if mode == "orig_per_head":
+            return _plain(colsum, rowsum, 1, A)
+        if mode == "exact_global":
+            return _plain(colsum, rowsum, 0, A)
+        raise AssertionError(mode)
+    return init
+
+
+def _plain(colsum, rowsum, opt, A):
+    if opt == 0:
+        return np.full(A.shape[:-2] + (1, 1), colsum.max() * rowsum.max())
+    return (colsum.max(-1) * rowsum.max(-1))[..., None, None]
+
+
+def _conv_flipped(v, w):
+    return _orig["depthwise_conv_same"](v, np.asarray(w)[:, ::-1])
+
+
+def _conv_off_by_one(v, w):
+    out = _orig["depthwise_conv_same"](v, w)
+    return np.concatenate([out[..., 1:, :], np.zeros_like(out[..., :1, :])], axis=-2)
+
+
+MUTANTS = {
+    "scale_double": ({"scale_qk": _scale_double}, ["scale", "exact_sdpa"]),
+    "scale_q_only": ({"scale_qk": _scale_q_only}, ["scale"]),
+    "segments_interleaved": ({"segment_means": _segments_interleaved}, ["segment_means_direct"]),
+    "softmax_wrong_axis": ({"softmax_rows": _softmax_wrong_axis}, ["softmax_library"]),
+    "mask_inverted": ({"softmax_rows": _softmax_mask_inverted}, ["softmax_library", "exact_sdpa"]),
+    "zero_valid_nan": ({"softmax_rows": _softmax_no_guard}, ["path_zero_valid"]),
+    "mask_ignored": ({"nystrom_kernels": _kernels_no_mask}, ["path_mask_semantics"]),
+    "z0_no_transpose": ({"newton_schulz_pinv": _ns_factory(z0_transpose=False)}, ["pinv_spectral"]),
+    "coef13_is_12": ({"newton_schulz_pinv": _ns_factory(c13=12.0)}, ["pinv_spectral", "pinv_residual_law", "pinv_diag_worked"]),
+    "coef15_is_14": ({"newton_schulz_pinv": _ns_factory(c15=14.0)}, ["pinv_spectral"]),
+    "coef7_is_6": ({"newton_schulz_pinv": _ns_factory(c7=6.0)}, ["pinv_spectral"]),
+    "left_multiply": ({"newton_schulz_pinv": _ns_factory(right=False)}, ["pinv_spectral"]),
+    "no_quarter": ({"newton_schulz_pinv": _ns_factory(quarter=1.0 / 3.0)}, ["pinv_spectral"]),
+    "init_rows_twice": ({"init_scale": _init_factory("rows_twice")}, ["init_scale"]),
+    "init_no_rowsum": ({"init_scale": _init_factory("no_rowsum")}, ["init_scale"]),
+    "init_original_per_head": ({"init_scale": _init_factory("orig_per_head")}, ["init_scale"]),
+    "init_exact_global": ({"init_scale": _init_factory("exact_global")}, ["init_scale"]),
+    "conv_flipped": ({"depthwise_conv_same": _conv_flipped}, ["conv_library", "conv_delta"]),
+    "conv_off_by_one": ({"depthwise_conv_same": _conv_off_by_one}, ["conv_delta", "conv_direct"]),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_mutant_is_caught(mutant, monkeypatch):
+    patches, pins = MUTANTS[mutant]
+    for name, fn in patches.items():
+        monkeypatch.setattr(O, name, fn)
+    caught = []
+    for pin in pins:
+        fn, tol = P.ALL_PINS[pin]
+        with np.errstate(all="ignore"):
+            try:
+                err = fn(O)
+            except Exception:  # a crash also counts as caught
+                err = float("inf")
+        if not (err < tol):
+            caught.append(pin)
+    assert caught, f"mutant {mutant} passed every pin in {pins}"
