@@ -1,0 +1,154 @@
+"""Nystrom approximate self-attention for MI355X (gfx950).
+
+A thin ctypes binding over libnystrom.so (declared in include/nystrom.h):
+it only marshals arguments.  Every step of the computation runs in the HIP
+kernels of the library; there is no Python or CPU fallback, and importing
+this package fails if the library has not been built
+(``python -m efficient_transformer_attention_segment_amd.build``).
+
+torch is used for device memory and streams only: tensors are passed by
+``data_ptr()`` and work is enqueued on ``torch.cuda.current_stream()``
+unless a stream is given.  The library is loaded on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention",
+    "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
+    "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
+]
+
+NYS_OK, NYS_ERR_INVALID, NYS_ERR_UNSUPPORTED, NYS_ERR_HIP = 0, -1, -2, -3
+HEAD_DIM, CONV_TAPS = 64, 65
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libnystrom.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_lib = None
+
+
+def _load():
+    """Load libnystrom.so once; raise if it has not been built (there is
+    no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m efficient_transformer_attention_segment_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(library_path)
+    lib.nystrom_attention.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.nystrom_attention.restype = _I
+    lib.nystrom_attention_bf16.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.nystrom_attention_bf16.restype = _I
+    lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
+    lib.nystrom_last_error.argtypes = []
+    lib.nystrom_last_error.restype = ctypes.c_char_p
+    lib.nystrom_release.argtypes = []
+    lib.nystrom_release.restype = None
+    lib.nystrom_debug_stages.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.nystrom_debug_stages.restype = _I
+    _lib = lib
+    return lib
+
+
+class NystromError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"nystrom error {code}: {message}")
+        self.code = code
+
+
+def last_error() -> str:
+    return _load().nystrom_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != NYS_OK:
+        raise NystromError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream) or 0)
+
+
+def _raw_call(fn, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
+    B, H, n, d = q.shape
+    return fn(_ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w), B, H, n, d, m, n_iter,
+              init_option, _ptr(out), _stream(stream))
+
+
+def nystrom_attention(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,
+                      out=None, stream=None):
+    """float32 [B,H,n,64] CUDA tensors -> out (allocated when None).
+    key_mask: uint8 [B,n] (1 keeps a key) or None; conv_w: float32 [H,65] or
+    None.  Enqueued on ``stream`` (default: torch's current stream)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_raw_call(_load().nystrom_attention, q, k, v, key_mask, conv_w, m, n_iter, init_option,
+                     out, stream))
+    return out
+
+
+def nystrom_attention_bf16(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,
+                           out=None, stream=None):
+    """bfloat16 [B,H,n,64] CUDA tensors (float32 accumulation) -> out."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check(_raw_call(_load().nystrom_attention_bf16, q, k, v, key_mask, conv_w, m, n_iter,
+                     init_option, out, stream))
+    return out
+
+
+def attention(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0, out=None,
+              stream=None):
+    """Pick the entry point from q's dtype (float32 or bfloat16)."""
+    import torch
+    fn = nystrom_attention_bf16 if q.dtype == torch.bfloat16 else nystrom_attention
+    return fn(q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream)
+
+
+def workspace_bytes(B, H, n, d, m) -> int:
+    return int(_load().nystrom_workspace_bytes(B, H, n, d, m))
+
+
+def release() -> None:
+    _load().nystrom_release()
+
+
+def debug_stages(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,
+                 stream=None):
+    """Run the Nystrom path and return (out, stages) where stages holds the
+    float32 intermediates qt, kt, A, c, Z, BV, W as CUDA tensors."""
+    import torch
+    B, H, n, d = q.shape
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    st = dict(qt=torch.empty(B, H, m, d, **f32), kt=torch.empty(B, H, m, d, **f32),
+              A=torch.empty(B, H, m, m, **f32), c=torch.empty(B * H, **f32),
+              Z=torch.empty(B, H, m, m, **f32), BV=torch.empty(B, H, m, d, **f32),
+              W=torch.empty(B, H, m, d, **f32))
+    out = torch.empty_like(q)
+    dtype = 1 if q.dtype == torch.bfloat16 else 0
+    rc = _load().nystrom_debug_stages(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w),
+                                   B, H, n, d, m, n_iter, init_option, _ptr(out),
+                                   _ptr(st["qt"]), _ptr(st["kt"]), _ptr(st["A"]), _ptr(st["c"]),
+                                   _ptr(st["Z"]), _ptr(st["BV"]), _ptr(st["W"]), _stream(stream))
+    _check(rc)
+    return out, st

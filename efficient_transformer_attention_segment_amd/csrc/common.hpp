@@ -1,0 +1,167 @@
+// Shared device helpers for the gfx950 Nystrom attention kernels.
+//
+// Matrix products run on v_mfma_f32_16x16x32_bf16 (CDNA4).  Lane layout of
+// one 64-lane wave (l = lane, g = l / 16):
+//   A operand (16 x 32): lane holds A[l % 16][8g + e], e = 0..7
+//   B operand (32 x 16): lane holds B[8g + e][l % 16]
+//   C / D     (16 x 16): lane holds C[4g + r][l % 16], r = 0..3
+// Because the contraction index only has to agree between A and B, several
+// kernels feed the C tile of one product straight into the next product as
+// an operand by using the "paired" k order: element e of the 32-wide k step
+// kk is k = 32kk + 4g + e for e < 4 and 32kk + 16 + 4g + (e - 4) for e >= 4,
+// which is exactly what two stacked C tiles hold in one lane.
+//
+// float32 accuracy from bf16 matrix cores: a float x is split into
+// hi = bf16(x) and lo = bf16(x - hi); a product uses hi*hi + hi*lo + lo*hi
+// (relative error about 2^-16).  Operands that are exact in bf16 (bf16
+// inputs) skip the split.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nys {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int HD = 64;     // head size d
+constexpr int TAPS = 65;   // depthwise conv taps
+constexpr int HALO = 32;   // TAPS / 2
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float NEG_BIG = -1.0e30f;  // finite "minus infinity" for running maxima
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Frag2 {
+  bf16x8 hi, lo;
+};
+
+// acc += A * B with NS = 1 (hi only) or NS = 3 (hi*hi + hi*lo + lo*hi).
+template <int NS>
+__device__ __forceinline__ f32x4 mma(const Frag2& a, const Frag2& b, f32x4 c) {
+  c = mfma(a.hi, b.hi, c);
+  if constexpr (NS == 3) {
+    c = mfma(a.hi, b.lo, c);
+    c = mfma(a.lo, b.hi, c);
+  }
+  return c;
+}
+
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ Frag2 split8(const float* x) {
+  Frag2 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h, l;
+    split1(x[e], h, l);
+    f.hi[e] = h;
+    f.lo[e] = l;
+  }
+  return f;
+}
+
+__device__ __forceinline__ float bf16u_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ u16 f32_to_bf16u(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum / max across the 16 lanes that share l / 16 (xor over lane bits 0..3).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+// Sum / max across the four lanes l, l^16, l^32, l^48 (the g groups).
+__device__ __forceinline__ float sum_g(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float max_g(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = max16(v);
+  return max_g(v);
+}
+
+// ---- I/O element access (float32 or raw bfloat16 bits) -------------------
+template <typename IO>
+struct IOTraits;
+
+template <>
+struct IOTraits<float> {
+  static constexpr int NS = 3;  // products need the hi/lo split
+  // load 8 consecutive elements (32-byte aligned)
+  __device__ static __forceinline__ void load8(const float* p, float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ static __forceinline__ void store16(float* p, const float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  }
+};
+
+template <>
+struct IOTraits<u16> {
+  static constexpr int NS = 1;  // bf16 inputs are exact operands
+  __device__ static __forceinline__ void load8(const u16* p, float* x) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void store16(u16* p, const float* x) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = (uint32_t)f32_to_bf16u(x[2 * i]) | ((uint32_t)f32_to_bf16u(x[2 * i + 1]) << 16);
+    reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+};
+
+// 8 floats -> operand fragment (hi, and lo when NS == 3)
+template <int NS>
+__device__ __forceinline__ Frag2 make_frag(const float* x) {
+  if constexpr (NS == 3) {
+    return split8(x);
+  } else {
+    Frag2 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.hi[e] = (__bf16)x[e];
+    return f;
+  }
+}
+
+}  // namespace nys

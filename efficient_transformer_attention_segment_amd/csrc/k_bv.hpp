@@ -1,0 +1,334 @@
+// Streamed softmax-weighted sums over the keys: B V for the Nystrom path
+// and the exact-attention branch.
+//
+// Pages: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), section 2.4
+// (kernel_3 B = softmax(Qt Ks^T + mask), the only place the mask enters, and
+// new_value = B V) and section 2.1 (exact attention when m equals n);
+// Hugging Face Transformers docs (zh), Nystromformer model page
+// (attention_mask: 1 keeps a token, 0 masks it).
+//
+// A workgroup owns up to 64 "columns" (landmarks for B V, queries for the
+// exact branch; 16 per wave and tile) and streams 32-key tiles of K and V
+// through LDS (K row-major, V transposed), double buffered with the next
+// tile's global loads in flight.  Per tile and wave:
+//   S^T (32 keys x 16 columns) = K_tile Qcol^T on the matrix cores,
+//   an online softmax down each column (running max / sum, the row max taken
+//   over the four lane groups by cross-lane shuffles),
+//   acc^T (64 d x 16 columns) += V_tile^T P^T, with the probabilities used
+//   straight from the S^T C tile as the B operand (paired k order).
+// The m x n matrix B never leaves registers.  Masked keys get weight 0; a
+// column that saw no valid key keeps max = -1e30, sum = 0, acc = 0.
+#pragma once
+
+#include "common.hpp"
+#include "k_conv.hpp"
+#include "k_pinv.hpp"
+
+namespace nys {
+
+template <typename IO>
+struct KV {
+  static constexpr int NS = IOTraits<IO>::NS;
+  static constexpr int KT = 32;         // keys per tile
+  static constexpr int KLD = HD + 8;    // K tile row stride (bf16 elements)
+  static constexpr int VLD = KT + 8;    // V^T tile row stride
+  static constexpr int K_ELEMS = KT * KLD;
+  static constexpr int V_ELEMS = HD * VLD;
+  static constexpr int PART = K_ELEMS + V_ELEMS;                 // hi (or lo) part
+  static constexpr int BUF_ELEMS = PART * (NS == 3 ? 2 : 1);
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;            // two buffers
+};
+
+// Thread t loads key row key0 + t/8, channels 8 (t % 8) .. +7 of K and V.
+template <typename IO>
+__device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __restrict__ V, int n, int key0,
+                                        float (&kx)[8], float (&vx)[8]) {
+  const int row = key0 + (threadIdx.x >> 3), cc = threadIdx.x & 7;
+  if (row < n) {
+    IOTraits<IO>::load8(K + (size_t)row * HD + 8 * cc, kx);
+    IOTraits<IO>::load8(V + (size_t)row * HD + 8 * cc, vx);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kx[e] = vx[e] = 0.f;
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[8], const float (&vx)[8]) {
+  using C = KV<IO>;
+  const int kk = threadIdx.x >> 3, cc = threadIdx.x & 7;
+  const Frag2 kf = make_frag<C::NS>(kx);
+  *reinterpret_cast<bf16x8*>(buf + kk * C::KLD + 8 * cc) = kf.hi;
+  if constexpr (C::NS == 3) *reinterpret_cast<bf16x8*>(buf + C::PART + kk * C::KLD + 8 * cc) = kf.lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h, l;
+    split1(vx[e], h, l);
+    buf[C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = h;
+    if constexpr (C::NS == 3) buf[C::PART + C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = l;
+  }
+}
+
+// One 32-key tile for the wave's owned column tiles.
+template <typename IO, int TPW>
+__device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&qf)[TPW][2], int nown, int key0,
+                                               int n, const uint8_t* __restrict__ mask, float lscale,
+                                               float (&mrun)[TPW], float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+  using C = KV<IO>;
+  constexpr int NS = C::NS;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  bool valid[8];
+#pragma unroll
+  for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 * kst + 4 * g + r;
+      bool v = key < n;
+      if (mask != nullptr && v) v = mask[key] != 0;
+      valid[4 * kst + r] = v;
+    }
+  Frag2 kf[2][2];
+#pragma unroll
+  for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int off = (16 * kst + c16) * C::KLD + 32 * ks + 8 * g;
+      kf[kst][ks].hi = *reinterpret_cast<const bf16x8*>(buf + off);
+      if constexpr (NS == 3) kf[kst][ks].lo = *reinterpret_cast<const bf16x8*>(buf + C::PART + off);
+    }
+  Frag2 vf[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int off = C::K_ELEMS + dperm(dt, c16) * C::VLD + 4 * g;
+    vf[dt].hi = cat44(*reinterpret_cast<const bf16x4*>(buf + off), *reinterpret_cast<const bf16x4*>(buf + off + 16));
+    if constexpr (NS == 3)
+      vf[dt].lo = cat44(*reinterpret_cast<const bf16x4*>(buf + C::PART + off),
+                        *reinterpret_cast<const bf16x4*>(buf + C::PART + off + 16));
+  }
+#pragma unroll
+  for (int o = 0; o < TPW; ++o) {
+    if (o >= nown) break;
+    f32x4 s[2];
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      s[kst] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
+    }
+    float lg[8];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = valid[4 * kst + r] ? s[kst][r] * lscale : -INFINITY;
+        lg[4 * kst + r] = x;
+        tm = fmaxf(tm, x);
+      }
+    tm = max_g(tm);
+    const float mnew = fmaxf(mrun[o], tm);
+    const float alpha = fast_exp2((mrun[o] - mnew) * LOG2E);
+    mrun[o] = mnew;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2((lg[e] - mnew) * LOG2E);
+      ps += p[e];
+    }
+    lsum[o] = lsum[o] * alpha + ps;
+    const Frag2 pf = make_frag<NS>(p);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      acc[o][dt] *= alpha;
+      acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
+    }
+  }
+}
+
+// Stream key tiles [tile0, tile1) of one head.
+template <typename IO, int TPW>
+__device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, int n,
+                                          const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
+                                          __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
+                                          float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+  using C = KV<IO>;
+  float kx[8], vx[8];
+  if (tile0 < tile1) {
+    kv_load<IO>(K, V, n, tile0 * C::KT, kx, vx);
+    kv_store<IO>(lds, kx, vx);
+  }
+  __syncthreads();
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int cur = (tile - tile0) & 1;
+    const bool more = tile + 1 < tile1;
+    if (more) kv_load<IO>(K, V, n, (tile + 1) * C::KT, kx, vx);
+    kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
+    if (more) kv_store<IO>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
+    __syncthreads();
+  }
+}
+
+struct BvArgs {
+  const void* k;
+  const void* v;
+  const uint8_t* key_mask;  // [B][n] or null
+  const __bf16* qt_hi;      // [BH][M][64]
+  const __bf16* qt_lo;
+  float* pmax;              // [BH][S][M]
+  float* psum;              // [BH][S][M]
+  float* pacc;              // [BH][S][M][64]
+  int n, H, S, tpc, ntiles;
+  float lscale;             // d^-1/4 (Qt carries the other factor)
+};
+
+// Partial B V of one (head, key chunk): all M landmarks, wave w owning the
+// landmark tiles {w, w+4, ...}.
+template <typename IO, int M>
+__device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
+  constexpr int TM = M / 16;
+  constexpr int TPW = (TM + 3) / 4;
+  constexpr int NS = IOTraits<IO>::NS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int b = bh / a.H;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  const int nown = wave < TM ? (TM - wave + 3) / 4 : 0;
+
+  Frag2 qf[TPW][2];
+  float mrun[TPW], lsum[TPW];
+  f32x4 acc[TPW][4];
+#pragma unroll
+  for (int o = 0; o < TPW; ++o) {
+    const int lt = wave + 4 * o;
+    mrun[o] = NEG_BIG;
+    lsum[o] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[o][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (o < nown) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const size_t off = ((size_t)bh * M + 16 * lt + c16) * HD + 32 * ks + 8 * g;
+        qf[o][ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
+        qf[o][ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
+      }
+    }
+  }
+  const int tile0 = chunk * a.tpc;
+  const int tile1 = min(a.ntiles, tile0 + a.tpc);
+  kv_stream<IO, TPW>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+  (void)NS;
+#pragma unroll
+  for (int o = 0; o < TPW; ++o) {
+    if (o >= nown) break;
+    const int i = 16 * (wave + 4 * o) + c16;
+    const float ls = sum_g(lsum[o]);
+    const size_t row = ((size_t)bh * a.S + chunk) * M + i;
+    if (g == 0) {
+      a.pmax[row] = mrun[o];
+      a.psum[row] = ls;
+    }
+    float* dst = a.pacc + row * HD + 16 * g;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(dst + 4 * dt) = make_float4(acc[o][dt][0], acc[o][dt][1], acc[o][dt][2], acc[o][dt][3]);
+  }
+}
+
+// Blocks [0, npinv) run the fused pseudo-inverse (one per head); the rest
+// run B V partials for (head, chunk).  Dynamic LDS = max of the two.
+template <typename IO, int M>
+__global__ __launch_bounds__(256) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
+  extern __shared__ __align__(16) __bf16 lds_dyn[];
+  if ((int)blockIdx.x < npinv) {
+    if constexpr (M <= 128) pinv_block<M>(pa, blockIdx.x, lds_dyn);
+    return;
+  }
+  const int id = blockIdx.x - npinv;
+  bv_block<IO, M>(ba, id / ba.S, id % ba.S, lds_dyn);
+}
+
+// ---------------------------------------------------------------------------
+// Exact branch (m == n): flash-style attention over all keys, 64 queries per
+// workgroup (16 per wave), then the convolution added in the same C tiles.
+
+struct ExactArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* key_mask;
+  const float* conv_w;  // [H][65] or null
+  void* out;
+  int n, H;
+  float lscale;  // 1 / sqrt(d)
+};
+
+constexpr int EXACT_WIN = 144;            // conv window rows for 64 queries
+constexpr int EXACT_VWLD = EXACT_WIN + 8;
+
+template <typename IO>
+constexpr int exact_lds_bytes() {
+  constexpr int NS = IOTraits<IO>::NS;
+  constexpr int kv = KV<IO>::LDS_BYTES;
+  constexpr int win = HD * EXACT_VWLD * 2 * (NS == 3 ? 2 : 1);
+  return kv > win ? kv : win;
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
+  extern __shared__ __align__(16) __bf16 lds_dyn[];
+  constexpr int NS = IOTraits<IO>::NS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int q0 = blockIdx.x * 64;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+
+  const int tok = q0 + 16 * wave + c16;
+  Frag2 qf[1][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float x[8];
+    if (tok < a.n) {
+      IOTraits<IO>::load8(Q + (size_t)tok * HD + 32 * ks + 8 * g, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    qf[0][ks] = make_frag<NS>(x);
+  }
+  float mrun[1] = {NEG_BIG}, lsum[1] = {0.f};
+  f32x4 acc[1][4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ntiles = (a.n + KV<IO>::KT - 1) / KV<IO>::KT;
+  kv_stream<IO, 1>(K, V, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
+  const float ls = sum_g(lsum[0]);
+  const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[0][dt] *= inv;
+  if (a.conv_w != nullptr) {
+    __bf16* Vh = lds_dyn;
+    __bf16* Vl = lds_dyn + HD * EXACT_VWLD;
+    stage_v_window<IO>(V, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
+    __syncthreads();
+    Frag2 tap[3];
+    conv_taps(a.conv_w + (size_t)h * TAPS, tap);
+    conv_tile<NS>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
+  }
+  if (tok < a.n) {
+    float vals[16];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vals[4 * dt + r] = acc[0][dt][r];
+    IOTraits<IO>::store16(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD + 16 * g, vals);
+  }
+}
+
+}  // namespace nys

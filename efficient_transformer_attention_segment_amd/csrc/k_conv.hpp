@@ -1,0 +1,91 @@
+// Depthwise 65-tap 'same' convolution of V on the matrix cores.
+//
+// Page: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), section 2.6: a
+// per-head depthwise convolution along the sequence (kernel (65, 1),
+// padding 32, no bias) applied to V and added to the attention output.
+// Read as a cross-correlation: out[t] = sum_j w[h][j] V[t + j - 32], V = 0
+// outside [0, n).
+//
+// For a tile of 16 output tokens the convolution is the banded (Toeplitz)
+// product O^T[d][t] += sum_s V^T[d][s] T[s][t] with T[s][t] = w[s - t + 32],
+// over the 80 positions s in [t0 - 32, t0 + 48), run as three 32-deep
+// bf16 matrix-core steps that accumulate into the attention output's own C
+// tiles.  V is staged in LDS transposed (position-contiguous per d row);
+// the Toeplitz operand depends only on (s - t) so each lane builds its three
+// fragments once per head.  Taps are split hi + lo; V is split too for
+// float32 I/O.
+#pragma once
+
+#include "common.hpp"
+
+namespace nys {
+
+// Output row permutation: C-tile row rho of d-tile dt holds channel
+// d = 16 * (rho / 4) + 4 * dt + rho % 4, so that lane (t, g) ends with the
+// 16 contiguous channels [16g, 16g + 16) of token t.
+__device__ __forceinline__ int dperm(int dt, int rho) { return 16 * (rho >> 2) + 4 * dt + (rho & 3); }
+
+// Stage V rows [t0 - 32, t0 - 32 + win) of one head, transposed, into
+// Vh[d * ld + row] (and Vl when split).  Rows outside [0, n) are zero.
+template <typename IO>
+__device__ void stage_v_window(const IO* __restrict__ V, int n, int t0, int win, __bf16* Vh, __bf16* Vl, int ld) {
+  constexpr int NS = IOTraits<IO>::NS;
+  for (int idx = threadIdx.x; idx < win * 8; idx += blockDim.x) {
+    const int row = idx >> 3, cc = idx & 7;
+    const int s = t0 - HALO + row;
+    float x[8];
+    if (s >= 0 && s < n) {
+      IOTraits<IO>::load8(V + (size_t)s * HD + 8 * cc, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split1(x[e], h, l);
+      Vh[(8 * cc + e) * ld + row] = h;
+      if constexpr (NS == 3) Vl[(8 * cc + e) * ld + row] = l;
+    }
+  }
+}
+
+// The three Toeplitz B fragments of this lane for head weights w[0..64].
+__device__ __forceinline__ void conv_taps(const float* __restrict__ w, Frag2 (&tap)[3]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 32 * kk + 8 * g + e - c16;
+      x[e] = (j >= 0 && j < TAPS) ? w[j] : 0.f;
+    }
+    tap[kk] = split8(x);
+  }
+}
+
+// oacc[dt] += conv for the 16-token tile starting at token ts, with the
+// window staged from t0 - 32: wc = ts - t0 (window row of position ts - 32).
+// Reads window rows [wc, wc + 96); the taps beyond the 80 needed are zero.
+template <int NSV>
+__device__ __forceinline__ void conv_tile(const __bf16* Vh, const __bf16* Vl, int ld, int wc, const Frag2 (&tap)[3],
+                                          f32x4 (&oacc)[4]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int base = dperm(dt, c16) * ld + wc + 32 * kk + 8 * g;
+      const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + base);
+      oacc[dt] = mfma(vh, tap[kk].hi, oacc[dt]);
+      oacc[dt] = mfma(vh, tap[kk].lo, oacc[dt]);
+      if constexpr (NSV == 3) {
+        const bf16x8 vl = *reinterpret_cast<const bf16x8*>(Vl + base);
+        oacc[dt] = mfma(vl, tap[kk].hi, oacc[dt]);
+      }
+    }
+  }
+}
+
+}  // namespace nys

@@ -1,0 +1,220 @@
+// Landmarks and the landmark Gram softmax.
+//
+// Pages: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), section 2.2
+// (Q and K each scaled by d^-1/4), section 2.3 (segment means over n/m
+// contiguous tokens), section 2.4 (A = softmax of the landmark products),
+// section 2.5 (the init scale needs the column and row sums of A).
+//
+// One workgroup reduces `lpw` landmarks of one (batch, head) for both Q and
+// K: each landmark's L rows are split over RS row slots of TPR threads (each
+// thread owns 16 contiguous bytes of a row), summed in float32, then the RS
+// slots are folded in LDS in a fixed order (deterministic).  The scale
+// d^-1/4 / L is applied once.  The last workgroup of a head to finish
+// (atomic arrival counter, reset afterwards) computes A = softmax(Qt Kt^T)
+// with split-bf16 matrix-core products (float32-accurate) and the head's
+// maximum column sum and row sum of A.
+#pragma once
+
+#include "common.hpp"
+
+namespace nys {
+
+struct LandmarkArgs {
+  int n, m, L, RS, lpw, BH;
+  float scale;          // d^-1/4 / L
+  float* qt;            // [BH][m][64] float32
+  float* kt;
+  __bf16* qt_hi;        // [BH][m][64] bf16 split of qt / kt
+  __bf16* qt_lo;
+  __bf16* kt_hi;
+  __bf16* kt_lo;
+  float* A;             // [BH][m][m]
+  float* colmax;        // [BH]
+  float* rowmax;        // [BH]
+  unsigned* counter;    // [BH], zero between calls
+};
+
+// A = softmax(Qt Kt^T) for one head, by the 256 threads of the block.
+// M = m (multiple of 32).  csum: LDS scratch of (M/16) * M floats.
+template <int M>
+__device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred) {
+  constexpr int TM = M / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const float* qt = a.qt + (size_t)bh * M * HD;
+  const float* kt = a.kt + (size_t)bh * M * HD;
+  float* A = a.A + (size_t)bh * M * M;
+  float rmax_w = 0.f;
+  for (int rt = wave; rt < TM; rt += 4) {
+    Frag2 af[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float x[8];
+      const float* p = qt + (size_t)(rt * 16 + c16) * HD + ks * 32 + g * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = p[e];
+      af[ks] = split8(x);
+    }
+    f32x4 acc[TM];
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        const float* p = kt + (size_t)(ct * 16 + c16) * HD + ks * 32 + g * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[e];
+        const Frag2 bf = split8(x);
+        acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+      }
+    }
+    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mx = NEG_BIG;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) mx = fmaxf(mx, acc[ct][r]);
+      mx = max16(mx);
+      float s = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        const float p = fast_exp2((acc[ct][r] - mx) * LOG2E);
+        acc[ct][r] = p;
+        s += p;
+      }
+      s = sum16(s);
+      const float inv = 1.0f / s;
+      float rs = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        acc[ct][r] *= inv;
+        rs += acc[ct][r];
+      }
+      rs = sum16(rs);
+      rmax_w = fmaxf(rmax_w, rs);
+    }
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[(size_t)(rt * 16 + g * 4 + r) * M + ct * 16 + c16] = acc[ct][r];
+      // column partial sums over this row tile
+      float cs = acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3];
+      cs = sum_g(cs);
+      if (g == 0) csum[rt * M + ct * 16 + c16] = cs;
+    }
+  }
+  rmax_w = max_g(rmax_w);
+  if (lane == 0) wred[wave] = rmax_w;
+  __syncthreads();
+  // column sums in a fixed order, then the block maximum
+  float cmax = 0.f;
+  for (int j = threadIdx.x; j < M; j += 256) {
+    float s = 0.f;
+    for (int rt = 0; rt < TM; ++rt) s += csum[rt * M + j];
+    cmax = fmaxf(cmax, s);
+  }
+  cmax = wave_max(cmax);
+  __syncthreads();
+  if (lane == 0) wred[4 + wave] = cmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.rowmax[bh] = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+    a.colmax[bh] = fmaxf(fmaxf(wred[4], wred[5]), fmaxf(wred[6], wred[7]));
+  }
+}
+
+// grid: (m / lpw, BH), block 256.  Requires TPR * RS * lpw == 256 where
+// TPR = 64 / (16 bytes / sizeof(IO)).
+template <typename IO, int M>
+__global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, const IO* __restrict__ k,
+                                                   LandmarkArgs a) {
+  constexpr int CH = 16 / sizeof(IO) == 4 ? 4 : 8;  // elements per 16 bytes
+  constexpr int CW = sizeof(IO) == 4 ? 8 : 8;       // elements loaded per thread (8)
+  constexpr int TPR = HD / CW;                       // threads per row = 8
+  (void)CH;
+  __shared__ float red[2][256][CW + 1];
+  __shared__ float csum[(M / 16) * M];
+  __shared__ float wred[8];
+  __shared__ int s_last;
+
+  const int t = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int RS = a.RS, lpw = a.lpw, L = a.L;
+  const int c = t % TPR;
+  const int rs = (t / TPR) % RS;
+  const int j = t / (TPR * RS);
+  const int i = blockIdx.x * lpw + j;
+  const size_t base = ((size_t)bh * a.n + (size_t)i * L) * HD + c * CW;
+
+  float sq[CW], sk[CW];
+#pragma unroll
+  for (int e = 0; e < CW; ++e) sq[e] = sk[e] = 0.f;
+  int r = rs;
+  for (; r + 3 * RS < L; r += 4 * RS) {
+    float xq[4][CW], xk[4][CW];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      IOTraits<IO>::load8(q + base + (size_t)(r + u * RS) * HD, xq[u]);
+      IOTraits<IO>::load8(k + base + (size_t)(r + u * RS) * HD, xk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < CW; ++e) {
+        sq[e] += xq[u][e];
+        sk[e] += xk[u][e];
+      }
+  }
+  for (; r < L; r += RS) {
+    float xq[CW], xk[CW];
+    IOTraits<IO>::load8(q + base + (size_t)r * HD, xq);
+    IOTraits<IO>::load8(k + base + (size_t)r * HD, xk);
+#pragma unroll
+    for (int e = 0; e < CW; ++e) {
+      sq[e] += xq[e];
+      sk[e] += xk[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < CW; ++e) {
+    red[0][t][e] = sq[e];
+    red[1][t][e] = sk[e];
+  }
+  __syncthreads();
+  for (int idx = t; idx < 2 * lpw * HD; idx += 256) {
+    const int which = idx / (lpw * HD);
+    const int rem = idx % (lpw * HD);
+    const int jj = rem / HD, col = rem % HD;
+    const int cc = col / CW, e = col % CW;
+    float s = 0.f;
+    for (int q2 = 0; q2 < RS; ++q2) s += red[which][(jj * RS + q2) * TPR + cc][e];
+    s *= a.scale;
+    const size_t o = ((size_t)bh * a.m + blockIdx.x * lpw + jj) * HD + col;
+    __bf16 hi, lo;
+    split1(s, hi, lo);
+    if (which == 0) {
+      a.qt[o] = s;
+      a.qt_hi[o] = hi;
+      a.qt_lo[o] = lo;
+    } else {
+      a.kt[o] = s;
+      a.kt_hi[o] = hi;
+      a.kt_lo[o] = lo;
+    }
+  }
+  // publish, then let the last block of this head build A
+  __threadfence();
+  __syncthreads();
+  if (t == 0) {
+    const unsigned prev = atomicAdd(&a.counter[bh], 1u);
+    s_last = (prev == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  landmark_gram_tail<M>(a, bh, csum, wred);
+  if (t == 0) a.counter[bh] = 0u;
+}
+
+}  // namespace nys

@@ -1,0 +1,459 @@
+// Host side of libnystrom.so: argument validation, the per-(device, stream)
+// workspace, the launch sequence and the C ABI declared in include/nystrom.h.
+//
+// Launch sequence for one Nystrom call (all on the caller's stream):
+//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo), and per head
+//                  A = softmax(Qt Kt^T), its max column sum and row sum
+//   2 k_pinv_bv    one launch holding both the per-head pseudo-inverse
+//                  blocks (m <= 128) and the B V partial blocks, so the
+//                  pseudo-inverse chain runs beside the K/V stream
+//     (m > 128: k_pinv_init + 4 k_pinv_gemm launches per iteration)
+//   3 k_merge      B V from the partials, then W = Z (B V) per head
+//   4 k_out        F W + conv(V) -> out
+// The exact branch (m == n) is one k_exact launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "../../include/nystrom.h"
+#include "k_bv.hpp"
+#include "k_landmark.hpp"
+#include "k_merge.hpp"
+#include "k_out.hpp"
+#include "k_pinv.hpp"
+
+using namespace nys;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(NYS_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------- plan ---
+struct Plan {
+  int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
+  size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
+  size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2;
+  size_t total;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int pow2floor(int x) {
+  int p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+Plan make_plan(int B, int H, int n, int m) {
+  Plan p{};
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.m = m;
+  p.BH = B * H;
+  p.L = n / m;
+  // landmark blocks: 8 threads per row, RS row slots per landmark, lpw landmarks per block
+  p.RS = std::min(32, std::max(1, pow2floor(std::max(1, p.L / 8))));
+  p.lpw = 32 / p.RS;
+  // key chunks for the B V partials: about two blocks per CU in total
+  p.ntiles = n / 32;
+  const int target = 512;
+  int S = std::max(1, std::min(p.ntiles, (target + p.BH - 1) / p.BH));
+  p.tpc = (p.ntiles + S - 1) / S;
+  p.S = (p.ntiles + p.tpc - 1) / p.tpc;
+  p.npinv = m <= 128 ? p.BH : 0;
+  const size_t BH = p.BH, M = m, D = HD;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p.off_qt = take(BH * M * D * 4);
+  p.off_kt = take(BH * M * D * 4);
+  p.off_qth = take(BH * M * D * 2);
+  p.off_qtl = take(BH * M * D * 2);
+  p.off_kth = take(BH * M * D * 2);
+  p.off_ktl = take(BH * M * D * 2);
+  p.off_A = take(BH * M * M * 4);
+  p.off_Z = take(BH * M * M * 4);
+  p.off_colmax = take(BH * 4);
+  p.off_rowmax = take(BH * 4);
+  p.off_cscale = take(BH * 4);
+  p.off_pmax = take(BH * p.S * M * 4);
+  p.off_psum = take(BH * p.S * M * 4);
+  p.off_pacc = take(BH * p.S * M * D * 4);
+  p.off_BV = take(BH * M * D * 4);
+  p.off_W = take(BH * M * D * 4);
+  p.off_wfh = take(BH * M * D * 2);
+  p.off_wfl = take(BH * M * D * 2);
+  if (m > 128) {
+    p.off_X = take(BH * M * M * 4);
+    p.off_T1 = take(BH * M * M * 4);
+    p.off_T2 = take(BH * M * M * 4);
+    p.off_Z2 = take(BH * M * M * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+// ----------------------------------------------------------- workspace ---
+struct Workspace {
+  char* buf = nullptr;
+  size_t cap = 0;
+  unsigned* cnt = nullptr;  // 2 * cnt_cap counters, zero between calls
+  size_t cnt_cap = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t st, size_t bytes, int BH, Workspace** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  Workspace& w = g_ws[{dev, st}];
+  if (w.cap < bytes || w.cnt_cap < (size_t)BH) {
+    HIP_TRY(hipStreamSynchronize(st));
+  }
+  if (w.cap < bytes) {
+    if (w.buf) HIP_TRY(hipFree(w.buf));
+    w.buf = nullptr;
+    w.cap = 0;
+    HIP_TRY(hipMalloc(&w.buf, bytes));
+    w.cap = bytes;
+  }
+  if (w.cnt_cap < (size_t)BH) {
+    if (w.cnt) HIP_TRY(hipFree(w.cnt));
+    w.cnt = nullptr;
+    w.cnt_cap = 0;
+    const size_t c = std::max<size_t>(BH, 256);
+    HIP_TRY(hipMalloc(&w.cnt, 2 * c * sizeof(unsigned)));
+    HIP_TRY(hipMemsetAsync(w.cnt, 0, 2 * c * sizeof(unsigned), st));
+    w.cnt_cap = c;
+  }
+  *out = &w;
+  return NYS_OK;
+}
+
+template <typename T>
+T* at(Workspace* w, size_t off) {
+  return reinterpret_cast<T*>(w->buf + off);
+}
+
+template <typename F>
+hipError_t allow_lds(F* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+// --------------------------------------------------------- launches ---
+template <typename IO, int M>
+int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
+                   const uint8_t* mask, const float* conv_w, int n_iter, int init_option, void* out,
+                   hipStream_t st) {
+  const float s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  LandmarkArgs la;
+  la.n = p.n;
+  la.m = M;
+  la.L = p.L;
+  la.RS = p.RS;
+  la.lpw = p.lpw;
+  la.BH = p.BH;
+  la.scale = s4 / (float)p.L;
+  la.qt = at<float>(w, p.off_qt);
+  la.kt = at<float>(w, p.off_kt);
+  la.qt_hi = at<__bf16>(w, p.off_qth);
+  la.qt_lo = at<__bf16>(w, p.off_qtl);
+  la.kt_hi = at<__bf16>(w, p.off_kth);
+  la.kt_lo = at<__bf16>(w, p.off_ktl);
+  la.A = at<float>(w, p.off_A);
+  la.colmax = at<float>(w, p.off_colmax);
+  la.rowmax = at<float>(w, p.off_rowmax);
+  la.counter = w->cnt;
+  hipLaunchKernelGGL((k_landmark<IO, M>), dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q, (const IO*)k,
+                     la);
+  HIP_TRY(hipGetLastError());
+
+  PinvArgs pa;
+  pa.A = la.A;
+  pa.colmax = la.colmax;
+  pa.rowmax = la.rowmax;
+  pa.Z = at<float>(w, p.off_Z);
+  pa.cscale = at<float>(w, p.off_cscale);
+  pa.BH = p.BH;
+  pa.n_iter = n_iter;
+  pa.init_option = init_option;
+  BvArgs ba;
+  ba.k = k;
+  ba.v = v;
+  ba.key_mask = mask;
+  ba.qt_hi = la.qt_hi;
+  ba.qt_lo = la.qt_lo;
+  ba.pmax = at<float>(w, p.off_pmax);
+  ba.psum = at<float>(w, p.off_psum);
+  ba.pacc = at<float>(w, p.off_pacc);
+  ba.n = p.n;
+  ba.H = p.H;
+  ba.S = p.S;
+  ba.tpc = p.tpc;
+  ba.ntiles = p.ntiles;
+  ba.lscale = s4;
+  size_t lds2 = KV<IO>::LDS_BYTES;
+  if constexpr (M <= 128) lds2 = std::max<size_t>(lds2, pinv_lds_bytes<M>());
+  HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
+  hipLaunchKernelGGL((k_pinv_bv<IO, M>), dim3(p.npinv + p.BH * p.S), dim3(256), lds2, st, pa, ba, p.npinv);
+  HIP_TRY(hipGetLastError());
+
+  const float* Zfinal = pa.Z;
+  if constexpr (M > 128) {
+    hipLaunchKernelGGL(k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M);
+    HIP_TRY(hipGetLastError());
+    float* Zc = pa.Z;
+    float* Zn = at<float>(w, p.off_Z2);
+    float* X = at<float>(w, p.off_X);
+    float* T1 = at<float>(w, p.off_T1);
+    float* T2 = at<float>(w, p.off_T2);
+    const dim3 gg((M / 32) * (M / 32), p.BH);
+    for (int it = 0; it < n_iter; ++it) {
+      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, pa.A, Zc, X, M, 0.f, 1.f);
+      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, X, T1, M, 7.f, 1.f);
+      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, T1, T2, M, 15.f, 1.f);
+      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, Zc, T2, Zn, M, 13.f, 0.25f);
+      HIP_TRY(hipGetLastError());
+      std::swap(Zc, Zn);
+    }
+    Zfinal = Zc;
+  }
+
+  MergeArgs ma;
+  ma.pmax = ba.pmax;
+  ma.psum = ba.psum;
+  ma.pacc = ba.pacc;
+  ma.Z = Zfinal;
+  ma.BV = at<float>(w, p.off_BV);
+  ma.W = at<float>(w, p.off_W);
+  ma.wf_hi = at<__bf16>(w, p.off_wfh);
+  ma.wf_lo = at<__bf16>(w, p.off_wfl);
+  ma.counter = w->cnt + w->cnt_cap;
+  ma.S = p.S;
+  hipLaunchKernelGGL((k_merge<M>), dim3(M / 16, p.BH), dim3(256), 0, st, ma);
+  HIP_TRY(hipGetLastError());
+
+  OutArgs oa;
+  oa.q = q;
+  oa.v = v;
+  oa.conv_w = conv_w;
+  oa.kt_hi = la.kt_hi;
+  oa.kt_lo = la.kt_lo;
+  oa.wf_hi = ma.wf_hi;
+  oa.wf_lo = ma.wf_lo;
+  oa.out = out;
+  oa.n = p.n;
+  oa.H = p.H;
+  oa.lscale = s4;
+  const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
+  HIP_TRY(allow_lds(k_out<IO, M>, lds4));
+  hipLaunchKernelGGL((k_out<IO, M>), dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), lds4, st, oa);
+  HIP_TRY(hipGetLastError());
+  return NYS_OK;
+}
+
+template <typename IO>
+int launch_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
+                 const float* conv_w, void* out, hipStream_t st) {
+  ExactArgs ea;
+  ea.q = q;
+  ea.k = k;
+  ea.v = v;
+  ea.key_mask = mask;
+  ea.conv_w = conv_w;
+  ea.out = out;
+  ea.n = n;
+  ea.H = H;
+  ea.lscale = 1.0f / sqrtf((float)HD);
+  const size_t lds = exact_lds_bytes<IO>();
+  HIP_TRY(allow_lds(k_exact<IO>, lds));
+  hipLaunchKernelGGL((k_exact<IO>), dim3((n + 63) / 64, B * H), dim3(256), lds, st, ea);
+  HIP_TRY(hipGetLastError());
+  return NYS_OK;
+}
+
+template <typename IO>
+int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
+               const uint8_t* mask, const float* conv_w, int n_iter, int init_option, void* out, hipStream_t st) {
+  switch (m) {
+    case 32: return launch_nystrom<IO, 32>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+    case 64: return launch_nystrom<IO, 64>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+    case 96: return launch_nystrom<IO, 96>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+    case 128: return launch_nystrom<IO, 128>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+    default: break;
+  }
+  if constexpr (sizeof(IO) == 2) {
+    switch (m) {
+      case 160: return launch_nystrom<IO, 160>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+      case 192: return launch_nystrom<IO, 192>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+      case 224: return launch_nystrom<IO, 224>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+      case 256: return launch_nystrom<IO, 256>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+      default: break;
+    }
+  }
+  return fail(NYS_ERR_UNSUPPORTED, "m=%d has no kernel instance", m);
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + bn && pb < pa + an;
+}
+
+int validate(int esize, const void* q, const void* k, const void* v, int B, int H, int n, int d, int m, int n_iter,
+             int init_option, const void* out) {
+  if (!q || !k || !v || !out) return fail(NYS_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (B <= 0 || H <= 0 || n <= 0 || d <= 0 || m <= 0)
+    return fail(NYS_ERR_INVALID, "B, H, n, d, m must be positive (got %d, %d, %d, %d, %d)", B, H, n, d, m);
+  if (m > n) return fail(NYS_ERR_INVALID, "m=%d exceeds n=%d", m, n);
+  if (n % m != 0) return fail(NYS_ERR_INVALID, "n=%d is not a multiple of m=%d", n, m);
+  if (n_iter < 0) return fail(NYS_ERR_INVALID, "n_iter=%d is negative", n_iter);
+  if (init_option != 0 && init_option != 1) return fail(NYS_ERR_INVALID, "init_option=%d is not 0 or 1", init_option);
+  if (d != HD) return fail(NYS_ERR_UNSUPPORTED, "d=%d: only d=64 is built", d);
+  if ((long long)B * H > 65535) return fail(NYS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)B * H);
+  if ((long long)n * HD >= (1LL << 31)) return fail(NYS_ERR_UNSUPPORTED, "n=%d too long", n);
+  if (m != n) {
+    if (m % 32 != 0 || m > NYS_MAX_LANDMARKS)
+      return fail(NYS_ERR_UNSUPPORTED, "m=%d: landmarks must be a multiple of 32 up to 256", m);
+    if (esize == 4 && m > 128) return fail(NYS_ERR_UNSUPPORTED, "m=%d: float32 I/O is built for m <= 128", m);
+  }
+  const size_t bytes = (size_t)B * H * n * d * esize;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(NYS_ERR_INVALID, "out overlaps an input");
+  return NYS_OK;
+}
+
+template <typename IO>
+int run(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int B, int H, int n,
+        int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout) {
+  int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
+  if (rc != NYS_OK) return rc;
+  if (m == n) return launch_exact<IO>(B, H, n, q, k, v, mask, conv_w, out, st);
+  const Plan p = make_plan(B, H, n, m);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace* w = nullptr;
+  rc = get_workspace(st, p.total, p.BH, &w);
+  if (rc != NYS_OK) return rc;
+  rc = dispatch_m<IO>(m, p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+  if (wout) *wout = w;
+  if (pout) *pout = p;
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int nystrom_attention(const float* q, const float* k, const float* v,
+                                                             const uint8_t* key_mask, const float* conv_w, int B,
+                                                             int H, int n, int d, int m, int n_iter,
+                                                             int init_option, float* out,
+                                                             struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    return run<float>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_bf16(const uint16_t* q, const uint16_t* k,
+                                                                  const uint16_t* v, const uint8_t* key_mask,
+                                                                  const float* conv_w, int B, int H, int n, int d,
+                                                                  int m, int n_iter, int init_option, uint16_t* out,
+                                                                  struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    return run<u16>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m) {
+  if (B <= 0 || H <= 0 || n <= 0 || d != HD || m <= 0 || m > n || n % m != 0) return 0;
+  if (m == n) return 0;
+  if (m % 32 != 0 || m > NYS_MAX_LANDMARKS) return 0;
+  return make_plan(B, H, n, m).total;
+}
+
+__attribute__((visibility("default"))) const char* nystrom_last_error(void) { return g_err.c_str(); }
+
+__attribute__((visibility("default"))) void nystrom_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& kv : g_ws) {
+    if (kv.second.buf) (void)hipFree(kv.second.buf);
+    if (kv.second.cnt) (void)hipFree(kv.second.cnt);
+  }
+  g_ws.clear();
+}
+
+__attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const void* q, const void* k,
+                                                                const void* v, const uint8_t* key_mask,
+                                                                const float* conv_w, int B, int H, int n, int d,
+                                                                int m, int n_iter, int init_option, void* out,
+                                                                float* qt, float* kt, float* a, float* cscale,
+                                                                float* z, float* bv, float* wout,
+                                                                struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    if (dtype != 0 && dtype != 1) return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
+    if (m == n) return fail(NYS_ERR_INVALID, "stages exist only on the Nystrom path (m != n)");
+    Workspace* w = nullptr;
+    Plan p{};
+    int rc = dtype == 0 ? run<float>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
+                        : run<u16>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
+    if (rc != NYS_OK) return rc;
+    HIP_TRY(hipStreamSynchronize(stream));
+    std::lock_guard<std::mutex> lk(g_mu);
+    const size_t BH = p.BH, M = m;
+    // after n_iter > 0 with m > 128 the final iterate lives in one of two buffers
+    size_t zoff = p.off_Z;
+    if (m > 128 && (n_iter % 2) == 1) zoff = p.off_Z2;
+    struct Cp {
+      void* dst;
+      size_t off, bytes;
+    } cps[] = {{qt, p.off_qt, BH * M * HD * 4}, {kt, p.off_kt, BH * M * HD * 4}, {a, p.off_A, BH * M * M * 4},
+               {cscale, p.off_cscale, BH * 4},  {z, zoff, BH * M * M * 4},     {bv, p.off_BV, BH * M * HD * 4},
+               {wout, p.off_W, BH * M * HD * 4}};
+    for (const Cp& c : cps)
+      if (c.dst) HIP_TRY(hipMemcpyAsync(c.dst, w->buf + c.off, c.bytes, hipMemcpyDeviceToDevice, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+    return NYS_OK;
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+/*
+ * nystrom.h -- C ABI of the MI355X (gfx950) Nystrom approximate
+ * self-attention library (libnystrom.so).
+ *
+ * What it computes (pages cited by title and section):
+ *   [P1] "Nystromformer 源码解析与实战指南：基于 Nystrom 采样的 O(n) 自注意力近似与
+ *        Transformers 实现" (blog.gitcode.com);
+ *   [P2] Hugging Face Transformers docs (zh), Nystromformer model page.
+ *
+ *   With Qs = q * d^-1/4 and Ks = k * d^-1/4            ([P1] 2.2),
+ *   landmarks Qt, Kt = means of n/m contiguous tokens    ([P1] 2.3),
+ *   F = softmax(Qs Kt^T), A = softmax(Qt Kt^T),
+ *   B = softmax(Qt Ks^T + key mask)                      ([P1] 2.4),
+ *   Z = n_iter steps of Z <- Z (13I - AZ(15I - AZ(7I - AZ))) / 4 from
+ *       Z_0 = A^T / c                                     ([P1] 2.5),
+ *   out = F (Z (B V)) + depthwise conv_w * V (65 taps, 'same')
+ *                                                         ([P1] 2.4, 2.6).
+ *   When m == n the exact attention softmax(Qs Ks^T + mask) V (+ conv) is
+ *   computed instead ([P1] 2.1).
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, out are DEVICE pointers to [B, H, n, d] row-major tensors
+ *     (d fastest).  The caller owns them.  out must not alias q, k or v.
+ *   - key_mask is a DEVICE pointer to uint8 [B, n]: nonzero keeps a key,
+ *     0 masks it ([P2] NystromformerModel.forward attention_mask).  NULL
+ *     means no padding.  The mask enters B only (and the scores of the
+ *     exact branch); padded tokens still enter the landmarks, F, A and the
+ *     convolution.  A batch row with no kept key gets B V = 0, so its
+ *     output is the convolution alone (no NaN).
+ *   - conv_w is a DEVICE pointer to float32 [H, 65] (tap j multiplies V at
+ *     token offset j - 32, zero outside [0, n); one filter per head shared
+ *     by all d columns).  NULL disables the convolution ([P1] 2.6).
+ *   - d must be 64; m must be a multiple of 32 with 32 <= m <= 256 and
+ *     n % m == 0, unless m == n (exact branch, any n >= 1).
+ *   - init_option 0 ("original", the default): c = (max column sum of A) *
+ *     (max row sum of A), both maxima over every (batch, head) of the call.
+ *     init_option 1 (exact coefficient): the same maxima per (batch, head).
+ *     Ignored when m == n.
+ *   - n_iter >= 0 (0 returns Z_0).  The pages' default is 6.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and is asynchronous: out is valid once the stream has synchronised.
+ *     The library keeps one grow-only device workspace per (device, stream)
+ *     behind a mutex; calls that share a stream are ordered by it.
+ *   - Return value: NYS_OK, or a negative nys_status.  Every argument is
+ *     validated on the host before anything is launched; on any error no
+ *     kernel runs and out is not written.  nystrom_last_error() then holds
+ *     a message (thread-local).
+ */
+#ifndef NYSTROM_H
+#define NYSTROM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *` */
+
+typedef enum {
+  NYS_OK = 0,
+  NYS_ERR_INVALID = -1,     /* bad pointer, size or option */
+  NYS_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle */
+  NYS_ERR_HIP = -3          /* a HIP runtime call failed */
+} nys_status;
+
+enum { NYS_INIT_ORIGINAL = 0, NYS_INIT_EXACT = 1 };
+enum { NYS_HEAD_DIM = 64, NYS_CONV_TAPS = 65, NYS_MAX_LANDMARKS = 256 };
+
+/* Nystrom attention, float32 q/k/v/out ([P1] 2.2-2.6; [P2] mask).
+ * Errors: NYS_ERR_INVALID for NULL q/k/v/out, B/H/n/d/m <= 0, n % m != 0,
+ * m > n, n_iter < 0, init_option not 0/1, out overlapping q/k/v;
+ * NYS_ERR_UNSUPPORTED for d != 64 or m outside {32, 64, ..., 256} when
+ * m != n, or sizes whose element counts overflow 2^31 per head;
+ * NYS_ERR_HIP when a HIP call fails. */
+int nystrom_attention(const float* q, const float* k, const float* v,
+                      const uint8_t* key_mask, const float* conv_w,
+                      int B, int H, int n, int d, int m, int n_iter,
+                      int init_option, float* out,
+                      struct ihipStream_t* stream);
+
+/* Same operation and argument list with bfloat16 q/k/v/out (raw 16-bit
+ * patterns, round-to-nearest-even on output); all accumulation is float32.
+ * conv_w stays float32. */
+int nystrom_attention_bf16(const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint8_t* key_mask,
+                           const float* conv_w, int B, int H, int n, int d,
+                           int m, int n_iter, int init_option, uint16_t* out,
+                           struct ihipStream_t* stream);
+
+/* Bytes of device workspace a call of this shape uses (0 for invalid or
+ * unsupported shapes). */
+size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* nystrom_last_error(void);
+
+/* Free every cached workspace (all devices and streams).  Must not be
+ * called while work the library enqueued may still be running. */
+void nystrom_release(void);
+
+/* Test hook: run the Nystrom path (m != n) like nystrom_attention[_bf16]
+ * (dtype selects: 0 = float32 q/k/v/out, 1 = bfloat16) and, after the
+ * stream has synchronised, copy the intermediate stages into the caller's
+ * DEVICE buffers (float32, any may be NULL):
+ *   qt, kt  [B,H,m,64]  landmarks of Qs, Ks          ([P1] 2.3)
+ *   a       [B,H,m,m]   A = softmax(Qt Kt^T)          ([P1] 2.4)
+ *   cscale  [B*H]       init scale c used for each head ([P1] 2.5)
+ *   z       [B,H,m,m]   pseudo-inverse iterate after n_iter steps
+ *   bv      [B,H,m,64]  B V                           ([P1] 2.4)
+ *   w       [B,H,m,64]  Z (B V)
+ * Synchronises `stream`.  Same errors as nystrom_attention; also
+ * NYS_ERR_INVALID when m == n. */
+int nystrom_debug_stages(int dtype, const void* q, const void* k,
+                         const void* v, const uint8_t* key_mask,
+                         const float* conv_w, int B, int H, int n, int d,
+                         int m, int n_iter, int init_option, void* out,
+                         float* qt, float* kt, float* a, float* cscale,
+                         float* z, float* bv, float* w,
+                         struct ihipStream_t* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NYSTROM_H */

@@ -1,0 +1,57 @@
+"""Helpers shared by the GPU parity tests: device transfer, the metric, and
+an unbuffered case announcement (so a crashed run still names its case)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+
+def announce(msg: str) -> None:
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def rel_frob_slices(got, ref):
+    """Max over (b, h) of ||got - ref||_F / ||ref||_F on each [n, d] slice
+    (the absolute norm where a reference slice is exactly zero), and the
+    whole-tensor value."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.sqrt(((got - ref) ** 2).sum(axis=(-1, -2)))
+    den = np.sqrt((ref ** 2).sum(axis=(-1, -2)))
+    per = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    whole = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    return float(per.max()), whole
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t
+
+
+def run_gpu(x, dtype, m, n_iter, init_option, conv=True, mask=True, out=None, stream=None):
+    """Call the library through the binding; returns float64 numpy."""
+    import torch
+
+    import efficient_transformer_attention_segment_amd as nys
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    km = to_dev(x["key_mask"], None) if (mask and x.get("key_mask") is not None) else None
+    cw = to_dev(x["conv_w"], None) if (conv and x.get("conv_w") is not None) else None
+    o = nys.attention(q, k, v, km, cw, m=m, n_iter=n_iter, init_option=init_option, out=out,
+                      stream=stream)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy()
+
+
+def oracle_out(x, m, n_iter, init_option, conv=True, mask=True, **kw):
+    from oracle import nystrom_oracle as O
+    km = x["key_mask"] if mask else None
+    cw = x["conv_w"] if conv else None
+    return O.nystrom_attention(x["q"], x["k"], x["v"], km, cw, m, n_iter, init_option, **kw)
+
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}

@@ -1,0 +1,113 @@
+"""The C ABI: the library loads, exports what include/nystrom.h declares,
+and rejects bad arguments on the host before anything is launched (so these
+run without a GPU: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nystrom.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import efficient_transformer_attention_segment_amd as nys
+    if not os.path.exists(nys.library_path):
+        from efficient_transformer_attention_segment_amd import build
+        build.build()
+    return nys._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nystrom_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("nystrom_attention", "nystrom_attention_bf16", "nystrom_workspace_bytes",
+              "nystrom_last_error", "nystrom_release", "nystrom_debug_stages"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in nystrom.h but not exported"
+
+
+def test_dynamic_symbols_are_c_names():
+    """The entry points are exported unmangled (extern "C")."""
+    import subprocess
+    import efficient_transformer_attention_segment_amd as nys
+    out = subprocess.run(["nm", "-D", "--defined-only", nys.library_path], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x900000)
+NULL = None
+
+
+def call(lib, fn="nystrom_attention", q=FAKE, k=FAKE, v=FAKE, out=FAKE2, B=1, H=2, n=256, d=64,
+         m=64, n_iter=6, init=0):
+    f = getattr(lib, fn)
+    return f(q, k, v, NULL, NULL, B, H, n, d, m, n_iter, init, out, NULL)
+
+
+@pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), -1), (dict(k=NULL), -1), (dict(v=NULL), -1), (dict(out=NULL), -1),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(n=0), -1), (dict(d=0), -1), (dict(m=0), -1),
+    (dict(n=250), -1),                 # n % m != 0
+    (dict(m=512), -1),                 # m > n
+    (dict(n_iter=-1), -1),
+    (dict(init=2), -1),
+    (dict(out=FAKE), -1),              # out aliases q, k, v
+    (dict(d=32, n=256), -2),           # only d = 64 is built
+    (dict(m=48, n=480), -2),           # m not a multiple of 32
+    (dict(m=512, n=1024), -2),         # m above 256 (and not n)
+    (dict(B=300, H=300), -2),          # B*H above the grid limit
+])
+def test_invalid_arguments(lib, fn, kw, code):
+    rc = call(lib, fn, **kw)
+    assert rc == code
+    assert lib.nystrom_last_error().decode() != ""
+
+
+def test_fp32_large_m_unsupported(lib):
+    assert call(lib, "nystrom_attention", n=512, m=256) == -2
+    # the bf16 entry point accepts it (validation passes; not launched here)
+
+
+def test_debug_stages_rejects_exact_branch_and_bad_dtype(lib):
+    f = lib.nystrom_debug_stages
+    args = [FAKE, FAKE, FAKE, NULL, NULL, 1, 2, 64, 64, 64, 6, 0, FAKE2] + [NULL] * 7 + [NULL]
+    assert f(0, *args) == -1          # m == n has no stages
+    args[9] = 32
+    assert f(7, *args) == -1          # dtype must be 0 or 1
+
+
+def test_workspace_bytes(lib):
+    w = lib.nystrom_workspace_bytes
+    assert w(1, 2, 256, 64, 64) > 0
+    assert w(2, 2, 256, 64, 64) > w(1, 2, 256, 64, 64)
+    assert w(1, 2, 256, 32, 64) == 0      # unsupported d
+    assert w(1, 2, 250, 64, 64) == 0      # n % m
+    assert w(1, 2, 256, 64, 256) == 0     # exact branch needs no workspace
+    # fits easily on one GPU at the largest workload
+    assert w(1, 4, 65536, 64, 256) < 64 << 20
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """No fallback: with the library missing the binding raises."""
+    import efficient_transformer_attention_segment_amd as nys
+    monkeypatch.setattr(nys, "_lib", None)
+    monkeypatch.setattr(nys, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        nys.workspace_bytes(1, 1, 64, 64, 32)
