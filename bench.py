@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the Nystrom attention hot path on one MI355X.
+
+One step = one full call of the library (landmarks, A and its
+pseudo-inverse, B V, W, output with the convolution) on one batch of
+synthetic input already resident in HBM.  Steps rotate over several input
+replicas whose total exceeds the 256 MB Infinity Cache, so each step reads
+its Q, K, V from HBM rather than from the previous step's cache lines.
+
+Prints ONE JSON line.  `value` is tokens/s = B * n / step time on the
+headline workload (bf16, B=4 H=12 n=4096 d=64 m=64, the n = 4096 config of
+the target).  `roofline` rates the kernel that takes the most time per step
+(per-kernel durations from hipEvents the library records around its own
+launches, over the same number of steps); `cpu_baseline` times the float64
+oracle on the host cores.  --gpus above 1 is refused: this build runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Nyström-attention tokens/s (B·n/s) on 1 MI355X; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+MALL_BYTES = 256 << 20
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, help="workload index 1..5 (default 3)")
+    ap.add_argument("--also", default="2,4,5", help="other workloads to time briefly ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "efficient_transformer_attention_segment_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w):
+    """Compulsory HBM bytes per launch of each kernel, from the per-head
+    figures: reads of the [n, d] tensors it must consume, writes of the
+    [n, d] output, plus the small per-head operands (landmarks, A, W, mask,
+    conv weights).  Implementation scratch (B V partials, bf16 copies) is
+    not counted."""
+    e = 2 if w.dtype == "bf16" else 4
+    BH, n, d, m = w.B * w.H, w.n, w.d, w.m
+    nd = n * d * e
+    small = 4 * (2 * m * d + m * m)              # Qt, Kt, A (float32) per head
+    mask = w.B * n if w.mask is not None else 0
+    per = {
+        "k_landmark": BH * (2 * nd + small),
+        "k_pinv_bv": BH * (2 * nd + 4 * m * d * 2 + 4 * m * m * 2) + mask,   # K, V, Qt, A, Z, B V
+        "k_merge": BH * 4 * (m * m + 2 * m * d),                              # Z, B V -> W
+        "k_out": BH * (3 * nd + 4 * 2 * m * d) + w.H * 65 * 4,               # Q, V -> O; Kt, W
+        "k_exact": BH * 4 * nd,
+    }
+    path = BH * 4 * nd + mask + w.H * 65 * 4                                  # Q, K, V in, O out
+    return per, path
+
+
+def algorithmic_flops(w):
+    BH, n, d, m = w.B * w.H, w.n, w.d, w.m
+    return BH * (8 * n * m * d + 4 * m * m * d + 8 * w.n_iter * m ** 3 + 130 * n * d)
+
+
+def read_traffic(kernel: str, wname: str, sha: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE,
+    WRITE_SIZE), scaled by the copy-kernel calibration factor; None unless
+    the summary was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wname}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_replicas(w, x, count, torch):
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to(a):
+        return torch.from_numpy(a).to(dev).to(tdt)
+
+    q0, k0, v0 = to(x["q"]), to(x["k"]), to(x["v"])
+    reps = []
+    for i in range(count):
+        q, k, v = (q0, k0, v0) if i == 0 else (q0.clone(), k0.clone(), v0.clone())
+        reps.append((q, k, v, torch.empty_like(q0)))
+    mask = torch.from_numpy(x["key_mask"]).to(dev) if x["key_mask"] is not None else None
+    conv = torch.from_numpy(x["conv_w"]).to(dev)
+    return reps, mask, conv
+
+
+def time_workload(w, steps, warmup, torch, nys):
+    from efficient_transformer_attention_segment_amd.workloads import make_inputs
+    x = make_inputs(w)
+    e = 2 if w.dtype == "bf16" else 4
+    per_rep = 4 * w.B * w.H * w.n * w.d * e
+    count = max(2, min(16, math.ceil(2 * MALL_BYTES / per_rep)))
+    reps, mask, conv = make_replicas(w, x, count, torch)
+    fn = nys.nystrom_attention_bf16 if w.dtype == "bf16" else nys.nystrom_attention
+
+    def step(i):
+        q, k, v, o = reps[i % count]
+        fn(q, k, v, mask, conv, m=w.m, n_iter=w.n_iter, init_option=w.init_option, out=o)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # same steps again with the library's per-kernel hipEvents
+    nys.profile_enable(True)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = nys.profile_collect()
+    nys.profile_enable(False)
+    return ms, prof, count, x
+
+
+def cpu_baseline(w, x, budget_s):
+    import numpy as np
+    from oracle import nystrom_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.nystrom_attention(x["q"], x["k"], x["v"], x["key_mask"], x["conv_w"], w.m, w.n_iter,
+                            w.init_option)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 or time.perf_counter() - t_start > budget_s:
+            break
+    med = float(np.median(times))
+    return {"value": w.tokens / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full float64 oracle calls of {w.name} (median {med:.2f} s each)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def copy_probe(mb, torch):
+    n = (mb << 20) // 4
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world > 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU path is not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb, torch)
+        return
+    import efficient_transformer_attention_segment_amd as nys
+    from efficient_transformer_attention_segment_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    ms, prof, reps, x = time_workload(w, args.steps, args.warmup, torch, nys)
+    value = w.tokens / (ms / 1e3)
+    per_bytes, path_bytes = algorithmic_bytes(w)
+    sha = source_sha()
+    kern = {k: {"avg_us": 1e3 * tot / cnt, "launches_per_step": cnt / args.steps}
+            for k, (tot, cnt) in prof.items()}
+    dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
+    dom_us = kern[dom]["avg_us"]
+    achieved = per_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(dom, w.name, sha), "kernel": dom,
+                "kernel_avg_us": round(dom_us, 2),
+                "algorithmic_bytes_per_launch": per_bytes.get(dom, 0)}
+    flops = algorithmic_flops(w)
+    path = {"bytes": path_bytes, "hbm_frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
+            "roofline_us": round(1e6 * max(path_bytes / (HBM_PEAK_GBS * 1e9),
+                                           flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)), 2)}
+    also = []
+    for s in [s for s in args.also.split(",") if s.strip()]:
+        wi = WORKLOADS[int(s)]
+        if wi.index == w.index:
+            continue
+        msi, profi, _, _ = time_workload(wi, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
+        pb, pathb = algorithmic_bytes(wi)
+        fl = algorithmic_flops(wi)
+        also.append({"workload": wi.name, "dtype": wi.dtype, "ms_per_step": round(msi, 4),
+                     "tokens_per_s": round(wi.tokens / (msi / 1e3), 1),
+                     "path_hbm_frac": round(pathb / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "path_roofline_us": round(1e6 * max(pathb / (HBM_PEAK_GBS * 1e9),
+                                                         fl / (MFMA_PEAK_TFLOPS[wi.dtype] * 1e12)), 2),
+                     "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, x, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, 0.02 N(0,1) conv weights, right-padding masks)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "m": w.m,
+                   "n_iter": w.n_iter, "init_option": w.init_option, "conv_taps": 65,
+                   "mask": (f"valid length U{{{w.mask[0]}..{w.mask[1]}}}" if w.mask else "none"),
+                   "input_replicas": reps, "parallelism": "single GPU"},
+        "roofline": roofline, "path": path, "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()}
+                                                         for k, v in kern.items()},
+        "cpu_baseline": cpu, "also": also, "source_sha": sha,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,7 @@ import os
 __all__ = [
     "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention",
     "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
+    "profile_enable", "profile_collect",
     "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
 ]
 
@@ -56,6 +57,12 @@ def _load():
     lib.nystrom_debug_stages.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P]
     lib.nystrom_debug_stages.restype = _I
+    lib.nystrom_profile_enable.argtypes = [_I]
+    lib.nystrom_profile_enable.restype = None
+    lib.nystrom_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                            ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_int), _I]
+    lib.nystrom_profile_collect.restype = _I
     _lib = lib
     return lib
 
@@ -130,6 +137,23 @@ def workspace_bytes(B, H, n, d, m) -> int:
 
 def release() -> None:
     _load().nystrom_release()
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every kernel launch with hipEvents (see profile_collect)."""
+    _load().nystrom_profile_enable(1 if on else 0)
+
+
+def profile_collect() -> dict:
+    """{kernel name: (total ms, launches)} for launches since the last collect."""
+    lib = _load()
+    cap = 16
+    names = (ctypes.c_char_p * cap)()
+    tot = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int * cap)()
+    k = lib.nystrom_profile_collect(names, tot, cnt, cap)
+    _check(0 if k >= 0 else k)
+    return {names[i].decode(): (float(tot[i]), int(cnt[i])) for i in range(min(k, cap))}
 
 
 def debug_stages(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,

@@ -108,6 +108,50 @@ __device__ __forceinline__ float wave_max(float v) {
   return max_g(v);
 }
 
+// ---- asynchronous global -> LDS copies (gfx950 global_load_lds, 16 bytes) --
+// One wave-wide instruction copies 64 x 16 bytes: lane l's 16 bytes, read
+// from its own global address, land at lds_base + 16 l.  Completion is
+// tracked by the wave's vmcnt; other waves see the data after the issuing
+// wave has waited and all waves have passed a barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier without the memory fence that __syncthreads() carries
+// (which would also drain every in-flight prefetch).  The asm statements
+// keep the compiler from moving memory accesses across it; callers wait for
+// the LDS writes / copies that other waves need before calling it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 4-element chunks addressed by lanes 4r + i / 4, r = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Row-major 64-channel bf16 tiles in LDS are stored with the 16-byte chunk
+// index XOR-swizzled by the row (chunk c of row r at position c ^ (r & 7))
+// so that column-chunk reads of 8 consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * HD + 8 * (chunk ^ (row & 7)); }
+
 // ---- I/O element access (float32 or raw bfloat16 bits) -------------------
 template <typename IO>
 struct IOTraits;

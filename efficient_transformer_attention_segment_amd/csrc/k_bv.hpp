@@ -9,8 +9,10 @@
 //
 // A workgroup owns up to 64 "columns" (landmarks for B V, queries for the
 // exact branch; 16 per wave and tile) and streams 32-key tiles of K and V
-// through LDS (K row-major, V transposed), double buffered with the next
-// tile's global loads in flight.  Per tile and wave:
+// through LDS.  bf16 inputs are copied global -> LDS by DMA, three tiles
+// ahead (K and V row-major; V read back transposed by ds_read_b64_tr_b16);
+// float32 inputs go through registers (split into bf16 hi/lo, V stored
+// transposed), double buffered.  Per tile and wave:
 //   S^T (32 keys x 16 columns) = K_tile Qcol^T on the matrix cores,
 //   an online softmax down each column (running max / sum, the row max taken
 //   over the four lane groups by cross-lane shuffles),
@@ -39,37 +41,103 @@ struct KV {
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;            // two buffers
 };
 
-// Thread t loads key row key0 + t/8, channels 8 (t % 8) .. +7 of K and V.
-template <typename IO>
+// Register staging: the 256 (row, 16-channel chunk) items of a 32-key tile
+// are spread over the NT threads of the block (ITEMS per thread).
+template <int NT>
+struct Items {
+  static constexpr int N = NT >= 256 ? 1 : 256 / NT;
+};
+
+template <typename IO, int NT>
 __device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __restrict__ V, int n, int key0,
-                                        float (&kx)[8], float (&vx)[8]) {
-  const int row = key0 + (threadIdx.x >> 3), cc = threadIdx.x & 7;
-  if (row < n) {
-    IOTraits<IO>::load8(K + (size_t)row * HD + 8 * cc, kx);
-    IOTraits<IO>::load8(V + (size_t)row * HD + 8 * cc, vx);
-  } else {
+                                        float (&kx)[Items<NT>::N][8], float (&vx)[Items<NT>::N][8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kx[e] = vx[e] = 0.f;
+  for (int u = 0; u < Items<NT>::N; ++u) {
+    const int item = threadIdx.x + u * NT;
+    const int row = key0 + (item >> 3), cc = item & 7;
+    if (item < 256 && row < n) {
+      IOTraits<IO>::load8(K + (size_t)row * HD + 8 * cc, kx[u]);
+      IOTraits<IO>::load8(V + (size_t)row * HD + 8 * cc, vx[u]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[u][e] = vx[u][e] = 0.f;
+    }
   }
 }
 
-template <typename IO>
-__device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[8], const float (&vx)[8]) {
+template <typename IO, int NT>
+__device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[Items<NT>::N][8],
+                                         const float (&vx)[Items<NT>::N][8]) {
   using C = KV<IO>;
-  const int kk = threadIdx.x >> 3, cc = threadIdx.x & 7;
-  const Frag2 kf = make_frag<C::NS>(kx);
-  *reinterpret_cast<bf16x8*>(buf + kk * C::KLD + 8 * cc) = kf.hi;
-  if constexpr (C::NS == 3) *reinterpret_cast<bf16x8*>(buf + C::PART + kk * C::KLD + 8 * cc) = kf.lo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h, l;
-    split1(vx[e], h, l);
-    buf[C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = h;
-    if constexpr (C::NS == 3) buf[C::PART + C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = l;
+  for (int u = 0; u < Items<NT>::N; ++u) {
+    const int item = threadIdx.x + u * NT;
+    if (item >= 256) continue;
+    const int kk = item >> 3, cc = item & 7;
+    const Frag2 kf = make_frag<C::NS>(kx[u]);
+    *reinterpret_cast<bf16x8*>(buf + kk * C::KLD + 8 * cc) = kf.hi;
+    if constexpr (C::NS == 3) *reinterpret_cast<bf16x8*>(buf + C::PART + kk * C::KLD + 8 * cc) = kf.lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split1(vx[u][e], h, l);
+      buf[C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = h;
+      if constexpr (C::NS == 3) buf[C::PART + C::K_ELEMS + (8 * cc + e) * C::VLD + kk] = l;
+    }
   }
 }
 
-// One 32-key tile for the wave's owned column tiles.
+// Per-tile math shared by both staging paths: S^T from the K fragments,
+// masked online softmax per column, acc^T += V^T P^T.
+template <int NS, int TPW>
+__device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 (&vf)[4], const bool (&valid)[8],
+                                           const Frag2 (&qf)[TPW][2], int nown, float lscale, float (&mrun)[TPW],
+                                           float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+#pragma unroll
+  for (int o = 0; o < TPW; ++o) {
+    if (o >= nown) break;
+    f32x4 s[2];
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      s[kst] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
+    }
+    // running max kept in units of the raw product; lscale2 = lscale*log2(e)
+    const float lscale2 = lscale * LOG2E;
+    float lg[8];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = valid[4 * kst + r] ? s[kst][r] : -INFINITY;
+        lg[4 * kst + r] = x;
+        tm = fmaxf(tm, x);
+      }
+    tm = max_g(tm);
+    const float mnew = fmaxf(mrun[o], tm);
+    const float alpha = fast_exp2((mrun[o] - mnew) * lscale2);
+    mrun[o] = mnew;
+    const float mb = mnew * lscale2;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(fmaf(lg[e], lscale2, -mb));
+      ps += p[e];
+    }
+    lsum[o] = lsum[o] * alpha + ps;
+    const Frag2 pf = make_frag<NS>(p);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      acc[o][dt] *= alpha;
+      acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
+    }
+  }
+}
+
+// One 32-key tile from the register-staged layout (K row-major, V^T).
 template <typename IO, int TPW>
 __device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&qf)[TPW][2], int nown, int key0,
                                                int n, const uint8_t* __restrict__ mask, float lscale,
@@ -99,74 +167,142 @@ __device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&
   Frag2 vf[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const int off = C::K_ELEMS + dperm(dt, c16) * C::VLD + 4 * g;
+    const int off = C::K_ELEMS + dmap<false>(dt, c16) * C::VLD + 4 * g;
     vf[dt].hi = cat44(*reinterpret_cast<const bf16x4*>(buf + off), *reinterpret_cast<const bf16x4*>(buf + off + 16));
     if constexpr (NS == 3)
       vf[dt].lo = cat44(*reinterpret_cast<const bf16x4*>(buf + C::PART + off),
                         *reinterpret_cast<const bf16x4*>(buf + C::PART + off + 16));
   }
-#pragma unroll
-  for (int o = 0; o < TPW; ++o) {
-    if (o >= nown) break;
-    f32x4 s[2];
-#pragma unroll
-    for (int kst = 0; kst < 2; ++kst) {
-      s[kst] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
-    }
-    float lg[8];
-    float tm = -INFINITY;
-#pragma unroll
-    for (int kst = 0; kst < 2; ++kst)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = valid[4 * kst + r] ? s[kst][r] * lscale : -INFINITY;
-        lg[4 * kst + r] = x;
-        tm = fmaxf(tm, x);
-      }
-    tm = max_g(tm);
-    const float mnew = fmaxf(mrun[o], tm);
-    const float alpha = fast_exp2((mrun[o] - mnew) * LOG2E);
-    mrun[o] = mnew;
-    float p[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2((lg[e] - mnew) * LOG2E);
-      ps += p[e];
-    }
-    lsum[o] = lsum[o] * alpha + ps;
-    const Frag2 pf = make_frag<NS>(p);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      acc[o][dt] *= alpha;
-      acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
-    }
-  }
+  kv_compute<NS, TPW>(kf, vf, valid, qf, nown, lscale, mrun, lsum, acc);
 }
 
-// Stream key tiles [tile0, tile1) of one head.
-template <typename IO, int TPW>
+// Stream key tiles [tile0, tile1) of one head through the register-staged
+// double buffer (used for float32 I/O and for ragged key ranges).
+template <typename IO, int TPW, int NT>
 __device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, int n,
                                           const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
                                           __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
                                           float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
   using C = KV<IO>;
-  float kx[8], vx[8];
+  float kx[Items<NT>::N][8], vx[Items<NT>::N][8];
   if (tile0 < tile1) {
-    kv_load<IO>(K, V, n, tile0 * C::KT, kx, vx);
-    kv_store<IO>(lds, kx, vx);
+    kv_load<IO, NT>(K, V, n, tile0 * C::KT, kx, vx);
+    kv_store<IO, NT>(lds, kx, vx);
   }
   __syncthreads();
   for (int tile = tile0; tile < tile1; ++tile) {
     const int cur = (tile - tile0) & 1;
     const bool more = tile + 1 < tile1;
-    if (more) kv_load<IO>(K, V, n, (tile + 1) * C::KT, kx, vx);
+    if (more) kv_load<IO, NT>(K, V, n, (tile + 1) * C::KT, kx, vx);
     kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
-    if (more) kv_store<IO>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
+    if (more) kv_store<IO, NT>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
     __syncthreads();
   }
+}
+
+// ---- bf16 path: K / V tiles copied global -> LDS by DMA ------------------
+// Ring of DMA_NBUF tiles of 32 keys (K and V row-major with swizzled
+// chunks, plus the tile's 32 mask bytes), DMA_DIST tiles in flight.  Each
+// wave issues the copies of 8 K rows, 8 V rows (and the mask tile) per tile.
+constexpr int DMA_NBUF = 8, DMA_DIST = 6;
+constexpr int DMA_TILE = 32 * HD;  // bf16 elements per K (or V) tile
+constexpr int DMA_LDS_BYTES = DMA_NBUF * (2 * DMA_TILE * 2 + 32);
+
+// The 8 wave-wide copies of a tile (4 for the 32 K rows, 4 for the V rows)
+// are dealt round-robin to the NW waves; every wave also copies the tile's
+// 32 mask bytes (identical data), so each wave issues the same count.
+template <int NW, bool MASK>
+__device__ __forceinline__ void dma_issue_tile(const u16* __restrict__ K, const u16* __restrict__ V,
+                                               const uint8_t* __restrict__ mask, int key0, __bf16* lds, int buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int id = wave; id < 8; id += NW) {
+    const int row = 8 * (id & 3) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const size_t src = (size_t)(key0 + row) * HD + 8 * chunk;
+    __bf16* dst = lds + ((id < 4 ? 0 : DMA_NBUF) + buf) * DMA_TILE + 8 * (id & 3) * HD;
+    dma16((id < 4 ? K : V) + src, dst);
+  }
+  if constexpr (MASK) {
+    uint8_t* mb = reinterpret_cast<uint8_t*>(lds + 2 * DMA_NBUF * DMA_TILE) + 32 * buf;
+    if (lane < 2) dma16(mask + key0 + 16 * lane, mb);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_rt(int k) {
+  // wait until at most k * N copies of this wave are outstanding
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<N>(); break;
+    case 2: wait_vmcnt<2 * N>(); break;
+    case 3: wait_vmcnt<3 * N>(); break;
+    case 4: wait_vmcnt<4 * N>(); break;
+    default: wait_vmcnt<5 * N>(); break;
+  }
+}
+
+template <int TPW, bool MASK>
+__device__ __forceinline__ void dma_tile_update(const __bf16* lds, int buf, const Frag2 (&qf)[TPW][2], int nown,
+                                                float lscale, float (&mrun)[TPW], float (&lsum)[TPW],
+                                                f32x4 (&acc)[TPW][4]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const __bf16* kb = lds + buf * DMA_TILE;
+  const __bf16* vb = lds + (DMA_NBUF + buf) * DMA_TILE;
+  bool valid[8];
+  if constexpr (MASK) {
+    const uint8_t* mb = reinterpret_cast<const uint8_t*>(lds + 2 * DMA_NBUF * DMA_TILE) + 32 * buf;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(mb + 16 * kst + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) valid[4 * kst + r] = ((w >> (8 * r)) & 0xffu) != 0;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) valid[e] = true;
+  }
+  Frag2 kf[2][2];
+#pragma unroll
+  for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      kf[kst][ks].hi = *reinterpret_cast<const bf16x8*>(kb + swz(16 * kst + c16, 4 * ks + g));
+  // V^T fragments by transposed reads: lane j of a 16-lane group points at
+  // row kbase + j/4, channels dmap_run(dt, j%4) .. +3; lane i then holds
+  // keys kbase .. kbase+3 of channel dmap(dt, i) (natural order).
+  Frag2 vf[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int c0 = dmap_run<false>(dt, c16 & 3);
+    const int r0 = 4 * g + (c16 >> 2);
+    const int r1 = 16 + r0;
+    const bf16x4 a = lds_read_tr(vb + r0 * HD + 8 * ((c0 >> 3) ^ (r0 & 7)) + (c0 & 7));
+    const bf16x4 b = lds_read_tr(vb + r1 * HD + 8 * ((c0 >> 3) ^ (r1 & 7)) + (c0 & 7));
+    vf[dt].hi = cat44(a, b);
+  }
+  kv_compute<1, TPW>(kf, vf, valid, qf, nown, lscale, mrun, lsum, acc);
+}
+
+// Stream key tiles [tile0, tile1) (all inside [0, n)) of one head.
+template <int TPW, int NW, bool MASK>
+__device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u16* __restrict__ V,
+                                              const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
+                                              __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
+                                              float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+  constexpr int CNT = 8 / NW + (MASK ? 1 : 0);  // copies per tile and wave
+  static_assert(DMA_DIST - 1 <= 5, "wait_vmcnt_rt covers up to 5 tiles");
+  const int T = tile1 - tile0;
+  for (int j = 0; j < DMA_DIST && j < T; ++j)
+    dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + j) * 32, lds, j % DMA_NBUF);
+  for (int t = 0; t < T; ++t) {
+    wait_vmcnt_rt<CNT>(min(DMA_DIST - 1, T - 1 - t));
+    barrier_only();
+    if (t + DMA_DIST < T)
+      dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + t + DMA_DIST) * 32, lds, (t + DMA_DIST) % DMA_NBUF);
+    dma_tile_update<TPW, MASK>(lds, t % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
+  }
+  barrier_only();
 }
 
 struct BvArgs {
@@ -182,27 +318,34 @@ struct BvArgs {
   float lscale;             // d^-1/4 (Qt carries the other factor)
 };
 
+// Waves of the B V / pseudo-inverse launch: one per 16 landmarks up to 128,
+// four above (each then owning several landmark tiles).
+template <int M>
+constexpr int bv_waves() {
+  return M <= 128 ? nwaves<M>() : 4;
+}
+
 // Partial B V of one (head, key chunk): all M landmarks, wave w owning the
-// landmark tiles {w, w+4, ...}.
+// landmark tiles {w, w + NW, ...}.
 template <typename IO, int M>
 __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   constexpr int TM = M / 16;
-  constexpr int TPW = (TM + 3) / 4;
-  constexpr int NS = IOTraits<IO>::NS;
+  constexpr int NW = bv_waves<M>();
+  constexpr int TPW = (TM + NW - 1) / NW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = bh / a.H;
   const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
   const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
-  const int nown = wave < TM ? (TM - wave + 3) / 4 : 0;
+  const int nown = wave < TM ? (TM - wave + NW - 1) / NW : 0;
 
   Frag2 qf[TPW][2];
   float mrun[TPW], lsum[TPW];
   f32x4 acc[TPW][4];
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
-    const int lt = wave + 4 * o;
+    const int lt = wave + NW * o;
     mrun[o] = NEG_BIG;
     lsum[o] = 0.f;
 #pragma unroll
@@ -218,29 +361,32 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   }
   const int tile0 = chunk * a.tpc;
   const int tile1 = min(a.ntiles, tile0 + a.tpc);
-  kv_stream<IO, TPW>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
-  (void)NS;
+  if constexpr (sizeof(IO) == 2) {
+    if (mask != nullptr)
+      kv_stream_dma<TPW, NW, true>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+    else
+      kv_stream_dma<TPW, NW, false>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+  } else {
+    kv_stream<IO, TPW, 64 * NW>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+  }
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
     if (o >= nown) break;
-    const int i = 16 * (wave + 4 * o) + c16;
+    const int i = 16 * (wave + NW * o) + c16;
     const float ls = sum_g(lsum[o]);
     const size_t row = ((size_t)bh * a.S + chunk) * M + i;
     if (g == 0) {
-      a.pmax[row] = mrun[o];
+      a.pmax[row] = mrun[o] * a.lscale;  // running max is kept unscaled
       a.psum[row] = ls;
     }
-    float* dst = a.pacc + row * HD + 16 * g;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<float4*>(dst + 4 * dt) = make_float4(acc[o][dt][0], acc[o][dt][1], acc[o][dt][2], acc[o][dt][3]);
+    store_row16<float, false>(a.pacc + row * HD, acc[o]);
   }
 }
 
 // Blocks [0, npinv) run the fused pseudo-inverse (one per head); the rest
 // run B V partials for (head, chunk).  Dynamic LDS = max of the two.
 template <typename IO, int M>
-__global__ __launch_bounds__(256) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
+__global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
     if constexpr (M <= 128) pinv_block<M>(pa, blockIdx.x, lds_dyn);
@@ -307,7 +453,7 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ntiles = (a.n + KV<IO>::KT - 1) / KV<IO>::KT;
-  kv_stream<IO, 1>(K, V, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
+  kv_stream<IO, 1, 256>(K, V, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
   const float ls = sum_g(lsum[0]);
   const float inv = ls > 0.f ? 1.0f / ls : 0.f;
 #pragma unroll
@@ -319,16 +465,9 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
     __syncthreads();
     Frag2 tap[3];
     conv_taps(a.conv_w + (size_t)h * TAPS, tap);
-    conv_tile<NS>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
+    conv_tile<NS, false>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
   }
-  if (tok < a.n) {
-    float vals[16];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vals[4 * dt + r] = acc[0][dt][r];
-    IOTraits<IO>::store16(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD + 16 * g, vals);
-  }
+  if (tok < a.n) store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, acc[0]);
 }
 
 }  // namespace nys

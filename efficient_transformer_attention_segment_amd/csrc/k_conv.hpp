@@ -20,10 +20,58 @@
 
 namespace nys {
 
-// Output row permutation: C-tile row rho of d-tile dt holds channel
-// d = 16 * (rho / 4) + 4 * dt + rho % 4, so that lane (t, g) ends with the
-// 16 contiguous channels [16g, 16g + 16) of token t.
-__device__ __forceinline__ int dperm(int dt, int rho) { return 16 * (rho >> 2) + 4 * dt + (rho & 3); }
+// Channel order of the output C tiles.  Row rho of d tile dt holds channel
+// dmap<B16>(dt, rho); lane (t, g) holds rows 4g .. 4g+3 of the four d tiles.
+//   B16 = false (natural): channel 16 dt + rho; lane g owns 16 dt + 4g + r,
+//     so one 16-byte float32 store per d tile covers 64 contiguous bytes of
+//     the row across the four lane groups.
+//   B16 = true: channel 32 (dt / 2) + 8 (rho / 4) + 4 (dt % 2) + rho % 4; lane
+//     g owns 8g .. 8g+7 and 32 + 8g .. 32 + 8g+7, so each 16-byte bf16 store
+//     again covers 64 contiguous bytes.
+// Either way a 4-channel run starts at a multiple of 4, which the
+// transposed LDS reads need.
+template <bool B16>
+__device__ __forceinline__ int dmap(int dt, int rho) {
+  if constexpr (B16) return 32 * (dt >> 1) + 8 * (rho >> 2) + 4 * (dt & 1) + (rho & 3);
+  return 16 * dt + rho;
+}
+// First channel of the 4-run that lanes with (j % 4) == a address in a
+// transposed read for d tile dt.
+template <bool B16>
+__device__ __forceinline__ int dmap_run(int dt, int a) {
+  return dmap<B16>(dt, 4 * a);
+}
+
+// Store the lane's 16 output channels of one token row.
+template <typename IO, bool B16>
+__device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
+  const int g = (threadIdx.x & 63) >> 4;
+  if constexpr (sizeof(IO) == 4) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + dmap<B16>(dt, 4 * g)) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+  } else if constexpr (B16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          w[2 * b + r] = (uint32_t)f32_to_bf16u(acc[2 * h + b][2 * r]) |
+                         ((uint32_t)f32_to_bf16u(acc[2 * h + b][2 * r + 1]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(row) + 32 * h + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint32_t w0 = (uint32_t)f32_to_bf16u(acc[dt][0]) | ((uint32_t)f32_to_bf16u(acc[dt][1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16u(acc[dt][2]) | ((uint32_t)f32_to_bf16u(acc[dt][3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(row) + 16 * dt + 4 * g) = make_uint2(w0, w1);
+    }
+  }
+}
 
 // Stage V rows [t0 - 32, t0 - 32 + win) of one head, transposed, into
 // Vh[d * ld + row] (and Vl when split).  Rows outside [0, n) are zero.
@@ -68,7 +116,7 @@ __device__ __forceinline__ void conv_taps(const float* __restrict__ w, Frag2 (&t
 // oacc[dt] += conv for the 16-token tile starting at token ts, with the
 // window staged from t0 - 32: wc = ts - t0 (window row of position ts - 32).
 // Reads window rows [wc, wc + 96); the taps beyond the 80 needed are zero.
-template <int NSV>
+template <int NSV, bool B16>
 __device__ __forceinline__ void conv_tile(const __bf16* Vh, const __bf16* Vl, int ld, int wc, const Frag2 (&tap)[3],
                                           f32x4 (&oacc)[4]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
@@ -76,7 +124,7 @@ __device__ __forceinline__ void conv_tile(const __bf16* Vh, const __bf16* Vl, in
   for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int base = dperm(dt, c16) * ld + wc + 32 * kk + 8 * g;
+      const int base = dmap<B16>(dt, c16) * ld + wc + 32 * kk + 8 * g;
       const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + base);
       oacc[dt] = mfma(vh, tap[kk].hi, oacc[dt]);
       oacc[dt] = mfma(vh, tap[kk].lo, oacc[dt]);

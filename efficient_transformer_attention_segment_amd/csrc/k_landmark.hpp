@@ -5,14 +5,17 @@
 // contiguous tokens), section 2.4 (A = softmax of the landmark products),
 // section 2.5 (the init scale needs the column and row sums of A).
 //
-// One workgroup reduces `lpw` landmarks of one (batch, head) for both Q and
-// K: each landmark's L rows are split over RS row slots of TPR threads (each
-// thread owns 16 contiguous bytes of a row), summed in float32, then the RS
-// slots are folded in LDS in a fixed order (deterministic).  The scale
-// d^-1/4 / L is applied once.  The last workgroup of a head to finish
-// (atomic arrival counter, reset afterwards) computes A = softmax(Qt Kt^T)
-// with split-bf16 matrix-core products (float32-accurate) and the head's
-// maximum column sum and row sum of A.
+// k_landmark: one workgroup reduces `lpw` landmarks of one (batch, head)
+// for both Q and K.  Each landmark's L rows are split over RS row slots of 8
+// threads (each thread owns 8 contiguous channels of a row), summed in
+// float32 with eight rows in flight per thread, then the RS slots are folded
+// in LDS in a fixed order (deterministic).  The scale d^-1/4 / L is applied
+// once; the landmarks are written in float32 and as bf16 hi/lo operands.
+//
+// k_gram: one workgroup per head computes A = softmax(Qt Kt^T) with
+// split-bf16 matrix-core products (float32-accurate) and the head's maximum
+// column sum and row sum of A.  The kernel boundary between the two is the
+// only synchronisation (no device-wide fences).
 #pragma once
 
 #include "common.hpp"
@@ -31,7 +34,6 @@ struct LandmarkArgs {
   float* A;             // [BH][m][m]
   float* colmax;        // [BH]
   float* rowmax;        // [BH]
-  unsigned* counter;    // [BH], zero between calls
 };
 
 // A = softmax(Qt Kt^T) for one head, by the 256 threads of the block.
@@ -124,19 +126,14 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
   }
 }
 
-// grid: (m / lpw, BH), block 256.  Requires TPR * RS * lpw == 256 where
-// TPR = 64 / (16 bytes / sizeof(IO)).
+// grid: (m / lpw, BH), block 256, with 8 * RS * lpw == 256.
 template <typename IO, int M>
 __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, const IO* __restrict__ k,
                                                    LandmarkArgs a) {
-  constexpr int CH = 16 / sizeof(IO) == 4 ? 4 : 8;  // elements per 16 bytes
-  constexpr int CW = sizeof(IO) == 4 ? 8 : 8;       // elements loaded per thread (8)
-  constexpr int TPR = HD / CW;                       // threads per row = 8
-  (void)CH;
+  constexpr int CW = 8;          // channels per thread
+  constexpr int TPR = HD / CW;   // threads per row
+  constexpr int UNR = 8;         // rows in flight per thread and tensor
   __shared__ float red[2][256][CW + 1];
-  __shared__ float csum[(M / 16) * M];
-  __shared__ float wred[8];
-  __shared__ int s_last;
 
   const int t = threadIdx.x;
   const int bh = blockIdx.y;
@@ -151,15 +148,15 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
 #pragma unroll
   for (int e = 0; e < CW; ++e) sq[e] = sk[e] = 0.f;
   int r = rs;
-  for (; r + 3 * RS < L; r += 4 * RS) {
-    float xq[4][CW], xk[4][CW];
+  for (; r + (UNR - 1) * RS < L; r += UNR * RS) {
+    float xq[UNR][CW], xk[UNR][CW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       IOTraits<IO>::load8(q + base + (size_t)(r + u * RS) * HD, xq[u]);
       IOTraits<IO>::load8(k + base + (size_t)(r + u * RS) * HD, xk[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < UNR; ++u)
 #pragma unroll
       for (int e = 0; e < CW; ++e) {
         sq[e] += xq[u][e];
@@ -203,18 +200,14 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
       a.kt_lo[o] = lo;
     }
   }
-  // publish, then let the last block of this head build A
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const unsigned prev = atomicAdd(&a.counter[bh], 1u);
-    s_last = (prev == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  landmark_gram_tail<M>(a, bh, csum, wred);
-  if (t == 0) a.counter[bh] = 0u;
+}
+
+// grid: BH, block 256.
+template <int M>
+__global__ __launch_bounds__(256) void k_gram(LandmarkArgs a) {
+  __shared__ float csum[(M / 16) * M];
+  __shared__ float wred[8];
+  landmark_gram_tail<M>(a, blockIdx.x, csum, wred);
 }
 
 }  // namespace nys

@@ -11,15 +11,10 @@
 // which is what keeps it self-correcting in finite precision.  Products are
 // split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, float32-accurate).
 //
-// pinv_block<M> (M <= 128): one workgroup per head, everything on chip.
-//   Wave w owns the 16-row tiles {w, w+4} of A, X and Z and keeps them in
-//   registers as operand fragments.  The matrices every wave needs whole
-//   (Z as a right factor, 7I - X, 15I - T1, 13I - T2) pass through two LDS
-//   regions R0 / R1 in column-major bf16 hi/lo form: each step reads one
-//   region and writes the other, so two M x M buffers suffice (M = 128 fits
-//   the 160 KB LDS).  Steps 1 and 4 are computed transposed
-//   (X^T = Z^T A^T, Z'^T = (13I - T2)^T Z^T /4) so that their C tiles land in
-//   each lane as the row fragments the next products need (paired k order).
+// pinv_block<M> (M <= 128): one workgroup per head, everything on chip, one
+//   wave per 16-row tile (see the function comment).  Two row-major LDS
+//   regions of M x (M + 8) bf16 hi/lo suffice: each step reads one and
+//   writes the other (M = 128 fits the 160 KB LDS).
 //
 // k_pinv_init / k_pinv_gemm (M > 128): the same iteration as a sequence of
 //   batched launches, one product per launch, with the matrices in global
@@ -53,20 +48,75 @@ __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
   return a.colmax[bh] * a.rowmax[bh];
 }
 
+// Waves per workgroup for m landmarks: one per 16-row tile, rounded up to a
+// power of two (2, 4 or 8).
+template <int M>
+constexpr int nwaves() {
+  return M / 16 <= 2 ? 2 : (M / 16 <= 4 ? 4 : 8);
+}
+
 template <int M>
 constexpr int pinv_lds_bytes() {
-  return 4 * M * (M + 8) * 2;  // two regions, hi + lo, bf16
+  return 4 * M * (M + 8) * 2;  // two regions, hi + lo, bf16, row stride M + 8
 }
 
 __device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// A operand rows i*16 .. i*16+15 of Y^T (= columns of Y) for one 32-wide k
+// step, read from row-major Y (hi / lo, row stride LD) with two transposed
+// reads.  PAIRED selects the paired k order (k = 4g + e, 16 + 4g + e - 4),
+// otherwise the standard one (k = 8g + e).
+template <int LD, bool PAIRED>
+__device__ __forceinline__ Frag2 colfrag(const __bf16* Yh, const __bf16* Yl, int i, int ks) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int k0 = 32 * ks + (PAIRED ? 4 * g : 8 * g) + (c16 >> 2);
+  const int k1 = k0 + (PAIRED ? 16 : 4);
+  const int col = 16 * i + 4 * (c16 & 3);
+  Frag2 f;
+  f.hi = cat44(lds_read_tr(Yh + k0 * LD + col), lds_read_tr(Yh + k1 * LD + col));
+  f.lo = cat44(lds_read_tr(Yl + k0 * LD + col), lds_read_tr(Yl + k1 * LD + col));
+  return f;
+}
+
+// Store this lane's 4 consecutive elements Y[row][col .. col+3] (hi / lo).
+template <int LD>
+__device__ __forceinline__ void rowstore4(__bf16* Yh, __bf16* Yl, int row, int col, const f32x4 v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    __bf16 a, b;
+    split1(v[r], a, b);
+    h[r] = a;
+    l[r] = b;
+  }
+  *reinterpret_cast<bf16x4*>(Yh + row * LD + col) = h;
+  *reinterpret_cast<bf16x4*>(Yl + row * LD + col) = l;
+}
+
+// Paired-order fragment from two stacked C tiles held by this lane.
+__device__ __forceinline__ Frag2 pairfrag(const f32x4 a, const f32x4 b) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return split8(x);
+}
+
+// One workgroup of nwaves<M>() waves per head; wave t owns rows
+// [16t, 16t + 16) of X, T1, T2 and Z.  Every product is formed transposed,
+// Y^T[:, own rows] = (left)^T (own rows of the right factor)^T, so its C
+// tile gives the lane 4 consecutive elements of one of its own rows:
+//   step 1  X^T  = Z^T A^T                      (Z read from LDS)
+//   step 2  T1^T = 7 X^T - X^T X^T              (X from LDS)
+//   step 3  T2^T = 15 X^T - T1^T X^T            (T1 from LDS)
+//   step 4  Z'^T = (13 Z^T - T2^T Z^T) / 4      (T2 from LDS)
+// which is Z' = Z (13I - X(15I - X(7I - X))) / 4 with X = A Z, expanded.
+// The own-row fragments (A, X, Z) stay in registers; X and Z also stay in
+// float32 for the 7X, 15X and 13Z terms.  LDS holds the matrix each step
+// reads whole, row-major bf16 hi/lo, alternating between two regions.
 template <int M>
 __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   constexpr int TM = M / 16, KS = M / 32, LD = M + 8;
-  constexpr int OWN = (TM + 3) / 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;  // t: own row tile
   const int g = lane >> 4, c16 = lane & 15;
   __bf16* const R0h = lds;
   __bf16* const R0l = lds + M * LD;
@@ -79,165 +129,96 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   const float invc = 1.0f / c;
   if (threadIdx.x == 0) a.cscale[bh] = c;
   if (a.n_iter == 0) {
-    for (int idx = threadIdx.x; idx < M * M; idx += 256) {
+    for (int idx = threadIdx.x; idx < M * M; idx += blockDim.x) {
       const int row = idx / M, col = idx % M;
       Zg[idx] = A[(size_t)col * M + row] * invc;
     }
     return;
   }
+  const bool own = t < TM;
+  const int row = 16 * t + c16;  // the lane's row of X, T1, T2, Z
 
-  Frag2 Af[OWN][KS], Xf[OWN][KS], Zf[OWN][KS];
+  Frag2 Af[KS], Xf[KS], Zf[KS];
+  f32x4 Xacc[TM], Zacc[TM], acc[TM];
+  if (own) {
 #pragma unroll
-  for (int o = 0; o < OWN; ++o) {
-    const int t = wave + 4 * o;
-    if (t < TM) {
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = A[(size_t)(16 * t + c16) * M + 32 * ks + 8 * g + e];
-        Af[o][ks] = split8(x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kp = 32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-          x[e] = A[(size_t)kp * M + 16 * t + c16] * invc;
-        }
-        Zf[o][ks] = split8(x);
-      }
+      for (int e = 0; e < 8; ++e) x[e] = A[(size_t)row * M + 32 * ks + 8 * g + e];
+      Af[ks] = split8(x);
     }
-  }
-  // R0 <- Z_0 column-major: element (row, col) at col * LD + row
-  for (int idx = threadIdx.x; idx < M * M; idx += 256) {
-    const int col = idx / M, row = idx % M;
-    __bf16 h, l;
-    split1(A[(size_t)col * M + row] * invc, h, l);
-    R0h[col * LD + row] = h;
-    R0l[col * LD + row] = l;
+    // Z_0 = A^T / c: Zacc[i][r] = Z_0[row][16i + 4g + r]
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Zacc[i][r] = A[(size_t)(16 * i + 4 * g + r) * M + row] * invc;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) Zf[ks] = pairfrag(Zacc[2 * ks], Zacc[2 * ks + 1]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[i]);
   }
   __syncthreads();
 
   for (int it = 0; it < a.n_iter; ++it) {
     const bool last = (it == a.n_iter - 1);
-    // ---- step 1: X^T[:, t] = Z^T A^T[:, t]; keep X rows, store 7I - X in R1
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-      const int t = wave + 4 * o;
-      if (t >= TM) continue;
-      f32x4 acc[TM];
+    if (own) {  // step 1: X^T = Z^T A^T
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag2 zt;
-          zt.hi = *reinterpret_cast<const bf16x8*>(R0h + (16 * i + c16) * LD + 32 * ks + 8 * g);
-          zt.lo = *reinterpret_cast<const bf16x8*>(R0l + (16 * i + c16) * LD + 32 * ks + 8 * g);
-          acc[i] = mma<3>(zt, Af[o][ks], acc[i]);
-        }
+        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, false>(R0h, R0l, i, ks), Af[ks], acc[i]);
       }
-      // acc[i][r] = X[16t + c16][16i + 4g + r]
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float x[8] = {acc[2 * ks][0], acc[2 * ks][1], acc[2 * ks][2], acc[2 * ks][3],
-                      acc[2 * ks + 1][0], acc[2 * ks + 1][1], acc[2 * ks + 1][2], acc[2 * ks + 1][3]};
-        Xf[o][ks] = split8(x);
+      for (int i = 0; i < TM; ++i) {
+        Xacc[i] = acc[i];
+        rowstore4<LD>(R1h, R1l, row, 16 * i + 4 * g, acc[i]);
       }
-      const int row = 16 * t + c16;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = 16 * i + 4 * g + r;
-          __bf16 h, l;
-          split1((row == col ? 7.f : 0.f) - acc[i][r], h, l);
-          R1h[col * LD + row] = h;
-          R1l[col * LD + row] = l;
-        }
+      for (int ks = 0; ks < KS; ++ks) Xf[ks] = pairfrag(Xacc[2 * ks], Xacc[2 * ks + 1]);
     }
     __syncthreads();
-    // ---- steps 2 and 3: T = X (diag - prev); store (next diag - T) column-major
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const __bf16* Bh = step == 0 ? R1h : R0h;
-      const __bf16* Bl = step == 0 ? R1l : R0l;
-      __bf16* Oh = step == 0 ? R0h : R1h;
-      __bf16* Ol = step == 0 ? R0l : R1l;
-      const float diag = step == 0 ? 15.f : 13.f;
-#pragma unroll
-      for (int o = 0; o < OWN; ++o) {
-        const int t = wave + 4 * o;
-        if (t >= TM) continue;
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int col = 16 * j + c16;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = col * LD + 32 * ks + 4 * g;
-            Frag2 bfr;
-            bfr.hi = cat44(*reinterpret_cast<const bf16x4*>(Bh + k0), *reinterpret_cast<const bf16x4*>(Bh + k0 + 16));
-            bfr.lo = cat44(*reinterpret_cast<const bf16x4*>(Bl + k0), *reinterpret_cast<const bf16x4*>(Bl + k0 + 16));
-            acc = mma<3>(Xf[o][ks], bfr, acc);
-          }
-          // acc[r] = T[16t + 4g + r][col]
-          bf16x4 h4, l4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * t + 4 * g + r;
-            __bf16 h, l;
-            split1((row == col ? diag : 0.f) - acc[r], h, l);
-            h4[r] = h;
-            l4[r] = l;
-          }
-          *reinterpret_cast<bf16x4*>(Oh + col * LD + 16 * t + 4 * g) = h4;
-          *reinterpret_cast<bf16x4*>(Ol + col * LD + 16 * t + 4 * g) = l4;
-        }
-      }
-      __syncthreads();
-    }
-    // ---- step 4: Z'^T[:, t] = (13I - T2)^T Z^T[:, t] / 4 (R1 holds 13I - T2)
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-      const int t = wave + 4 * o;
-      if (t >= TM) continue;
-      f32x4 acc[TM];
+    if (own) {  // step 2: T1^T = 7 X^T - X^T X^T
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int k0 = (16 * i + c16) * LD + 32 * ks + 4 * g;
-          Frag2 afr;
-          afr.hi = cat44(*reinterpret_cast<const bf16x4*>(R1h + k0), *reinterpret_cast<const bf16x4*>(R1h + k0 + 16));
-          afr.lo = cat44(*reinterpret_cast<const bf16x4*>(R1l + k0), *reinterpret_cast<const bf16x4*>(R1l + k0 + 16));
-          acc[i] = mma<3>(afr, Zf[o][ks], acc[i]);
-        }
-        acc[i] *= 0.25f;
+        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R1h, R1l, i, ks), Xf[ks], acc[i]);
       }
-      // acc[i][r] = Z'[16t + c16][16i + 4g + r]
-      const int row = 16 * t + c16;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, 7.f * Xacc[i] - acc[i]);
+    }
+    __syncthreads();
+    if (own) {  // step 3: T2^T = 15 X^T - T1^T X^T
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R0h, R0l, i, ks), Xf[ks], acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) rowstore4<LD>(R1h, R1l, row, 16 * i + 4 * g, 15.f * Xacc[i] - acc[i]);
+    }
+    __syncthreads();
+    if (own) {  // step 4: Z'^T = (13 Z^T - T2^T Z^T) / 4
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R1h, R1l, i, ks), Zf[ks], acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) Zacc[i] = 0.25f * (13.f * Zacc[i] - acc[i]);
       if (last) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
           *reinterpret_cast<float4*>(Zg + (size_t)row * M + 16 * i + 4 * g) =
-              make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+              make_float4(Zacc[i][0], Zacc[i][1], Zacc[i][2], Zacc[i][3]);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          float x[8] = {acc[2 * ks][0], acc[2 * ks][1], acc[2 * ks][2], acc[2 * ks][3],
-                        acc[2 * ks + 1][0], acc[2 * ks + 1][1], acc[2 * ks + 1][2], acc[2 * ks + 1][3]};
-          Zf[o][ks] = split8(x);
-        }
+        for (int ks = 0; ks < KS; ++ks) Zf[ks] = pairfrag(Zacc[2 * ks], Zacc[2 * ks + 1]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int col = 16 * i + 4 * g + r;
-            __bf16 h, l;
-            split1(acc[i][r], h, l);
-            R0h[col * LD + row] = h;
-            R0l[col * LD + row] = l;
-          }
+        for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[i]);
       }
     }
     __syncthreads();

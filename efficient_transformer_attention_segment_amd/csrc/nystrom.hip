@@ -2,14 +2,16 @@
 // workspace, the launch sequence and the C ABI declared in include/nystrom.h.
 //
 // Launch sequence for one Nystrom call (all on the caller's stream):
-//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo), and per head
-//                  A = softmax(Qt Kt^T), its max column sum and row sum
-//   2 k_pinv_bv    one launch holding both the per-head pseudo-inverse
+//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo)
+//   2 k_gram       per head A = softmax(Qt Kt^T), its max column / row sum
+//   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
 //                  blocks (m <= 128) and the B V partial blocks, so the
 //                  pseudo-inverse chain runs beside the K/V stream
 //     (m > 128: k_pinv_init + 4 k_pinv_gemm launches per iteration)
-//   3 k_merge      B V from the partials, then W = Z (B V) per head
-//   4 k_out        F W + conv(V) -> out
+//   4 k_merge      B V from the partials
+//   5 k_w          W = Z (B V) and its operand fragments
+//   6 k_out        F W + conv(V) -> out
+// Kernel boundaries are the only cross-workgroup synchronisation.
 // The exact branch (m == n) is one k_exact launch.
 #include <hip/hip_runtime.h>
 
@@ -21,6 +23,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/nystrom.h"
 #include "k_bv.hpp"
@@ -56,11 +59,12 @@ int fail(int code, const char* fmt, ...) {
 struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
-  size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2;
+  size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
   size_t total;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t ZERO_BYTES = 4096;  // zero page at offset 0 of every workspace
 
 int pow2floor(int x) {
   int p = 1;
@@ -93,6 +97,7 @@ Plan make_plan(int B, int H, int n, int m) {
     o = align_up(o + bytes);
     return at;
   };
+  p.off_zero = take(ZERO_BYTES);
   p.off_qt = take(BH * M * D * 4);
   p.off_kt = take(BH * M * D * 4);
   p.off_qth = take(BH * M * D * 2);
@@ -121,39 +126,61 @@ Plan make_plan(int B, int H, int n, int m) {
   return p;
 }
 
+// ------------------------------------------------------- kernel timing ---
+// While enabled, every launch is bracketed by a pair of hipEvents on its
+// stream; nystrom_profile_collect() resolves them into per-kernel sums.
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+struct ProfScope {
+  hipStream_t st;
+  ProfRec rec{nullptr, nullptr, nullptr};
+  ProfScope(hipStream_t s, const char* name) : st(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    rec.name = name;
+    if (hipEventCreate(&rec.a) != hipSuccess || hipEventCreate(&rec.b) != hipSuccess) {
+      rec.name = nullptr;
+      return;
+    }
+    (void)hipEventRecord(rec.a, st);
+  }
+  ~ProfScope() {
+    if (!rec.name) return;
+    (void)hipEventRecord(rec.b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back(rec);
+  }
+};
+
 // ----------------------------------------------------------- workspace ---
 struct Workspace {
   char* buf = nullptr;
   size_t cap = 0;
-  unsigned* cnt = nullptr;  // 2 * cnt_cap counters, zero between calls
-  size_t cnt_cap = 0;
 };
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(hipStream_t st, size_t bytes, int BH, Workspace** out) {
+// Grow-only: a larger request waits for the stream (the old buffer may be in
+// use by work already enqueued on it), then reallocates.
+int get_workspace(hipStream_t st, size_t bytes, Workspace** out) {
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   Workspace& w = g_ws[{dev, st}];
-  if (w.cap < bytes || w.cnt_cap < (size_t)BH) {
-    HIP_TRY(hipStreamSynchronize(st));
-  }
   if (w.cap < bytes) {
+    HIP_TRY(hipStreamSynchronize(st));
     if (w.buf) HIP_TRY(hipFree(w.buf));
     w.buf = nullptr;
     w.cap = 0;
     HIP_TRY(hipMalloc(&w.buf, bytes));
     w.cap = bytes;
-  }
-  if (w.cnt_cap < (size_t)BH) {
-    if (w.cnt) HIP_TRY(hipFree(w.cnt));
-    w.cnt = nullptr;
-    w.cnt_cap = 0;
-    const size_t c = std::max<size_t>(BH, 256);
-    HIP_TRY(hipMalloc(&w.cnt, 2 * c * sizeof(unsigned)));
-    HIP_TRY(hipMemsetAsync(w.cnt, 0, 2 * c * sizeof(unsigned), st));
-    w.cnt_cap = c;
+    HIP_TRY(hipMemsetAsync(w.buf, 0, ZERO_BYTES, st));
   }
   *out = &w;
   return NYS_OK;
@@ -194,10 +221,17 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.A = at<float>(w, p.off_A);
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
-  la.counter = w->cnt;
-  hipLaunchKernelGGL((k_landmark<IO, M>), dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q, (const IO*)k,
-                     la);
-  HIP_TRY(hipGetLastError());
+  {
+    ProfScope ps(st, "k_landmark");
+    hipLaunchKernelGGL((k_landmark<IO, M>), dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
+                       (const IO*)k, la);
+    HIP_TRY(hipGetLastError());
+  }
+  {
+    ProfScope ps(st, "k_gram");
+    hipLaunchKernelGGL((k_gram<M>), dim3(p.BH), dim3(256), 0, st, la);
+    HIP_TRY(hipGetLastError());
+  }
 
   PinvArgs pa;
   pa.A = la.A;
@@ -223,16 +257,23 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.tpc = p.tpc;
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
-  size_t lds2 = KV<IO>::LDS_BYTES;
+  size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
   if constexpr (M <= 128) lds2 = std::max<size_t>(lds2, pinv_lds_bytes<M>());
   HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
-  hipLaunchKernelGGL((k_pinv_bv<IO, M>), dim3(p.npinv + p.BH * p.S), dim3(256), lds2, st, pa, ba, p.npinv);
-  HIP_TRY(hipGetLastError());
+  {
+    ProfScope ps(st, "k_pinv_bv");
+    hipLaunchKernelGGL((k_pinv_bv<IO, M>), dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), lds2, st, pa, ba,
+                       p.npinv);
+    HIP_TRY(hipGetLastError());
+  }
 
   const float* Zfinal = pa.Z;
   if constexpr (M > 128) {
-    hipLaunchKernelGGL(k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M);
-    HIP_TRY(hipGetLastError());
+    {
+      ProfScope ps(st, "k_pinv_init");
+      hipLaunchKernelGGL(k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M);
+      HIP_TRY(hipGetLastError());
+    }
     float* Zc = pa.Z;
     float* Zn = at<float>(w, p.off_Z2);
     float* X = at<float>(w, p.off_X);
@@ -240,6 +281,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     float* T2 = at<float>(w, p.off_T2);
     const dim3 gg((M / 32) * (M / 32), p.BH);
     for (int it = 0; it < n_iter; ++it) {
+      ProfScope ps(st, "k_pinv_gemm x4");
       hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, pa.A, Zc, X, M, 0.f, 1.f);
       hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, X, T1, M, 7.f, 1.f);
       hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, T1, T2, M, 15.f, 1.f);
@@ -259,14 +301,22 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ma.W = at<float>(w, p.off_W);
   ma.wf_hi = at<__bf16>(w, p.off_wfh);
   ma.wf_lo = at<__bf16>(w, p.off_wfl);
-  ma.counter = w->cnt + w->cnt_cap;
   ma.S = p.S;
-  hipLaunchKernelGGL((k_merge<M>), dim3(M / 16, p.BH), dim3(256), 0, st, ma);
-  HIP_TRY(hipGetLastError());
+  {
+    ProfScope ps(st, "k_merge");
+    hipLaunchKernelGGL((k_merge<M>), dim3(M / 16, p.BH), dim3(256), 0, st, ma);
+    HIP_TRY(hipGetLastError());
+  }
+  {
+    ProfScope ps(st, "k_w");
+    hipLaunchKernelGGL((k_w<M, sizeof(IO) == 2>), dim3(M / 32, p.BH), dim3(256), 0, st, ma);
+    HIP_TRY(hipGetLastError());
+  }
 
   OutArgs oa;
   oa.q = q;
   oa.v = v;
+  oa.zero = at<__bf16>(w, p.off_zero);
   oa.conv_w = conv_w;
   oa.kt_hi = la.kt_hi;
   oa.kt_lo = la.kt_lo;
@@ -276,10 +326,13 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.n = p.n;
   oa.H = p.H;
   oa.lscale = s4;
-  const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
+  const size_t lds4 = sizeof(IO) == 2 ? (size_t)OutLayoutDMA<M>::LDS_BYTES : (size_t)OutLayout<IO, M>::LDS_BYTES;
   HIP_TRY(allow_lds(k_out<IO, M>, lds4));
-  hipLaunchKernelGGL((k_out<IO, M>), dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), lds4, st, oa);
-  HIP_TRY(hipGetLastError());
+  {
+    ProfScope ps(st, "k_out");
+    hipLaunchKernelGGL((k_out<IO, M>), dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), lds4, st, oa);
+    HIP_TRY(hipGetLastError());
+  }
   return NYS_OK;
 }
 
@@ -298,8 +351,11 @@ int launch_exact(int B, int H, int n, const void* q, const void* k, const void* 
   ea.lscale = 1.0f / sqrtf((float)HD);
   const size_t lds = exact_lds_bytes<IO>();
   HIP_TRY(allow_lds(k_exact<IO>, lds));
-  hipLaunchKernelGGL((k_exact<IO>), dim3((n + 63) / 64, B * H), dim3(256), lds, st, ea);
-  HIP_TRY(hipGetLastError());
+  {
+    ProfScope ps(st, "k_exact");
+    hipLaunchKernelGGL((k_exact<IO>), dim3((n + 63) / 64, B * H), dim3(256), lds, st, ea);
+    HIP_TRY(hipGetLastError());
+  }
   return NYS_OK;
 }
 
@@ -363,7 +419,7 @@ int run(const void* q, const void* k, const void* v, const uint8_t* mask, const 
   const Plan p = make_plan(B, H, n, m);
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
-  rc = get_workspace(st, p.total, p.BH, &w);
+  rc = get_workspace(st, p.total, &w);
   if (rc != NYS_OK) return rc;
   rc = dispatch_m<IO>(m, p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
   if (wout) *wout = w;
@@ -414,7 +470,6 @@ __attribute__((visibility("default"))) void nystrom_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto& kv : g_ws) {
     if (kv.second.buf) (void)hipFree(kv.second.buf);
-    if (kv.second.cnt) (void)hipFree(kv.second.cnt);
   }
   g_ws.clear();
 }
@@ -454,6 +509,47 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
   }
+}
+
+__attribute__((visibility("default"))) void nystrom_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+}
+
+__attribute__((visibility("default"))) int nystrom_profile_collect(const char** names, double* total_ms,
+                                                                   int* launches, int cap) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  std::vector<const char*> nm;
+  std::vector<double> tot;
+  std::vector<int> cnt;
+  int rc = 0;
+  for (const ProfRec& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) rc = NYS_ERR_HIP;
+    size_t i = 0;
+    while (i < nm.size() && std::strcmp(nm[i], r.name) != 0) ++i;
+    if (i == nm.size()) {
+      nm.push_back(r.name);
+      tot.push_back(0.0);
+      cnt.push_back(0);
+    }
+    tot[i] += ms;
+    cnt[i] += 1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  if (rc != 0) return fail(rc, "hipEvent timing failed");
+  const int k = (int)std::min<size_t>(nm.size(), cap < 0 ? 0 : (size_t)cap);
+  for (int i = 0; i < k; ++i) {
+    if (names) names[i] = nm[i];
+    if (total_ms) total_ms[i] = tot[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return (int)nm.size();
 }
 
 }  // extern "C"

@@ -120,6 +120,18 @@ int nystrom_debug_stages(int dtype, const void* q, const void* k,
                          float* z, float* bv, float* w,
                          struct ihipStream_t* stream);
 
+/* Kernel timing for benchmarks (not part of the computation).  While
+ * enabled (on != 0), every call brackets each kernel it launches with a
+ * pair of hipEvents recorded on the call's stream.  nystrom_profile_collect
+ * waits for those events, then writes up to `cap` entries: names[i] (static
+ * strings: "k_landmark", "k_pinv_bv", "k_pinv_init", "k_pinv_gemm x4",
+ * "k_merge", "k_out", "k_exact"), total_ms[i] (sum of elapsed times) and
+ * launches[i], covering every launch since the previous collect; any of the
+ * arrays may be NULL.  Returns the number of distinct kernels, or
+ * NYS_ERR_HIP if an event could not be resolved. */
+void nystrom_profile_enable(int on);
+int nystrom_profile_collect(const char** names, double* total_ms, int* launches, int cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,13 +2,26 @@
 an unbuffered case announcement (so a crashed run still names its case)."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
 
+CASE_LOG = os.environ.get("NYS_CASE_LOG", os.path.join("gpurun_out", "gpu_cases.log"))
+
 
 def announce(msg: str) -> None:
-    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    """Append the case line to CASE_LOG (bypasses pytest capture) and stderr."""
+    line = f"[gpu-case] {msg}\n"
+    try:
+        os.makedirs(os.path.dirname(CASE_LOG) or ".", exist_ok=True)
+        with open(CASE_LOG, "a") as f:
+            f.write(line)
+            f.flush()
+            os.fsync(f.fileno())
+    except OSError:
+        pass
+    sys.__stderr__.write(line)
     sys.__stderr__.flush()
 
 

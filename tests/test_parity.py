@@ -148,7 +148,7 @@ def test_side_stream_and_error_leaves_out_untouched():
     q, k, v = (to_dev(x[n], "fp32") for n in ("q", "k", "v"))
     out = torch.full_like(q, 7.0)
     with pytest.raises(nys.NystromError) as ei:
-        nys.nystrom_attention(q, k, v, None, None, m=48, out=out)   # unsupported m
-    assert ei.value.code == nys.NYS_ERR_UNSUPPORTED
+        nys.nystrom_attention(q, k, v, None, None, m=48, out=out)   # n % m != 0
+    assert ei.value.code == nys.NYS_ERR_INVALID
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
