@@ -92,16 +92,24 @@ __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, __shfl_xor(v, 8));
   return v;
 }
-// Sum / max across the four lanes l, l^16, l^32, l^48 (the g groups).
+// Sum / max across the four lanes l, l^16, l^32, l^48 (the g groups), with
+// the gfx950 row swaps (VALU, no LDS round trip): permlane16_swap pairs rows
+// (0,1) and (2,3), permlane32_swap pairs rows (0,2) and (1,3).
 __device__ __forceinline__ float sum_g(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float max_g(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_max(float v) {
   v = max16(v);

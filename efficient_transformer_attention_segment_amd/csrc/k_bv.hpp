@@ -19,7 +19,8 @@
 //   acc^T (64 d x 16 columns) += V_tile^T P^T, with the probabilities used
 //   straight from the S^T C tile as the B operand (paired k order).
 // The m x n matrix B never leaves registers.  Masked keys get weight 0; a
-// column that saw no valid key keeps max = -1e30, sum = 0, acc = 0.
+// column that saw no valid key keeps max = -1e30, sum = 0, acc = 0.  Partial
+// maxima are written in log2 units of the scaled logit.
 #pragma once
 
 #include "common.hpp"
@@ -89,9 +90,19 @@ __device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[Items<NT
 
 // Per-tile math shared by both staging paths: S^T from the K fragments,
 // masked online softmax per column, acc^T += V^T P^T.
-template <int NS, int TPW>
+//
+// The running column maximum mrun is kept in log2 units of the scaled logit
+// (x = s * lscale * log2 e).  Probabilities are taken against the stored
+// maximum, p = 2^(x - mrun), which is exact after the final division by the
+// running sum; the maximum (a cross-lane reduction over the four lane
+// groups) and the rescale of sum and accumulators are only redone when some
+// logit in the wave exceeds its stored maximum by RESCALE_LOG2 (p stays
+// below 2^8, far from float overflow).  A wave-uniform vote picks the path.
+constexpr float RESCALE_LOG2 = 8.f;
+
+template <int NS, int TPW, bool MASKED>
 __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 (&vf)[4], const bool (&valid)[8],
-                                           const Frag2 (&qf)[TPW][2], int nown, float lscale, float (&mrun)[TPW],
+                                           const Frag2 (&qf)[TPW][2], int nown, float lscale2, float (&mrun)[TPW],
                                            float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
@@ -103,37 +114,34 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
     }
-    // running max kept in units of the raw product; lscale2 = lscale*log2(e)
-    const float lscale2 = lscale * LOG2E;
-    float lg[8];
-    float tm = -INFINITY;
+    float x[8];
+    float tmax = -INFINITY;
 #pragma unroll
     for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = valid[4 * kst + r] ? s[kst][r] : -INFINITY;
-        lg[4 * kst + r] = x;
-        tm = fmaxf(tm, x);
+        float v = s[kst][r] * lscale2;
+        if constexpr (MASKED) v = valid[4 * kst + r] ? v : -INFINITY;
+        x[4 * kst + r] = v;
+        tmax = fmaxf(tmax, v);
       }
-    tm = max_g(tm);
-    const float mnew = fmaxf(mrun[o], tm);
-    const float alpha = fast_exp2((mrun[o] - mnew) * lscale2);
-    mrun[o] = mnew;
-    const float mb = mnew * lscale2;
+    if (__builtin_amdgcn_ballot_w64(tmax > mrun[o] + RESCALE_LOG2) != 0) {
+      const float mnew = fmaxf(mrun[o], max_g(tmax));
+      const float alpha = fast_exp2(mrun[o] - mnew);
+      mrun[o] = mnew;
+      lsum[o] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[o][dt] *= alpha;
+    }
     float p[8];
-    float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(fmaf(lg[e], lscale2, -mb));
-      ps += p[e];
+      p[e] = fast_exp2(x[e] - mrun[o]);
+      lsum[o] += p[e];
     }
-    lsum[o] = lsum[o] * alpha + ps;
     const Frag2 pf = make_frag<NS>(p);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      acc[o][dt] *= alpha;
-      acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
-    }
+    for (int dt = 0; dt < 4; ++dt) acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
   }
 }
 
@@ -173,16 +181,16 @@ __device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&
       vf[dt].lo = cat44(*reinterpret_cast<const bf16x4*>(buf + C::PART + off),
                         *reinterpret_cast<const bf16x4*>(buf + C::PART + off + 16));
   }
-  kv_compute<NS, TPW>(kf, vf, valid, qf, nown, lscale, mrun, lsum, acc);
+  kv_compute<NS, TPW, true>(kf, vf, valid, qf, nown, lscale * LOG2E, mrun, lsum, acc);
 }
 
 // Stream key tiles [tile0, tile1) of one head through the register-staged
 // double buffer (used for float32 I/O and for ragged key ranges).
-template <typename IO, int TPW, int NT>
+template <typename IO, int TPW, int NT, int KP = 1>
 __device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, int n,
                                           const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
                                           __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
-                                          float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+                                          float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
   using C = KV<IO>;
   float kx[Items<NT>::N][8], vx[Items<NT>::N][8];
   if (tile0 < tile1) {
@@ -194,7 +202,8 @@ __device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __
     const int cur = (tile - tile0) & 1;
     const bool more = tile + 1 < tile1;
     if (more) kv_load<IO, NT>(K, V, n, (tile + 1) * C::KT, kx, vx);
-    kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
+    if (((tile - tile0) % KP) == kp)
+      kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
     if (more) kv_store<IO, NT>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
     __syncthreads();
   }
@@ -281,15 +290,15 @@ __device__ __forceinline__ void dma_tile_update(const __bf16* lds, int buf, cons
     const bf16x4 b = lds_read_tr(vb + r1 * HD + 8 * ((c0 >> 3) ^ (r1 & 7)) + (c0 & 7));
     vf[dt].hi = cat44(a, b);
   }
-  kv_compute<1, TPW>(kf, vf, valid, qf, nown, lscale, mrun, lsum, acc);
+  kv_compute<1, TPW, MASK>(kf, vf, valid, qf, nown, lscale * LOG2E, mrun, lsum, acc);
 }
 
 // Stream key tiles [tile0, tile1) (all inside [0, n)) of one head.
-template <int TPW, int NW, bool MASK>
+template <int TPW, int NW, bool MASK, int KP = 1>
 __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u16* __restrict__ V,
                                               const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
                                               __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
-                                              float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+                                              float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
   constexpr int CNT = 8 / NW + (MASK ? 1 : 0);  // copies per tile and wave
   static_assert(DMA_DIST - 1 <= 5, "wait_vmcnt_rt covers up to 5 tiles");
   const int T = tile1 - tile0;
@@ -300,7 +309,7 @@ __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u
     barrier_only();
     if (t + DMA_DIST < T)
       dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + t + DMA_DIST) * 32, lds, (t + DMA_DIST) % DMA_NBUF);
-    dma_tile_update<TPW, MASK>(lds, t % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
+    if ((t % KP) == kp) dma_tile_update<TPW, MASK>(lds, t % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
   }
   barrier_only();
 }
@@ -325,27 +334,33 @@ constexpr int bv_waves() {
   return M <= 128 ? nwaves<M>() : 4;
 }
 
-// Partial B V of one (head, key chunk): all M landmarks, wave w owning the
-// landmark tiles {w, w + NW, ...}.
+// Partial B V of one (head, key chunk): all M landmarks.  With NW waves
+// and TM landmark tiles, wave w owns landmark tiles {w, w + NW, ...}; when
+// there are twice as many waves as tiles (m <= 64) the tile's two waves
+// take alternate key tiles (KP = 2) and fold their online-softmax states
+// together in LDS at the end.
 template <typename IO, int M>
 __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   constexpr int TM = M / 16;
   constexpr int NW = bv_waves<M>();
-  constexpr int TPW = (TM + NW - 1) / NW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int KP = (M <= 128 && NW % TM == 0) ? NW / TM : 1;
+  constexpr int NWT = KP > 1 ? TM : NW;  // waves per key parity
+  constexpr int TPW = (TM + NWT - 1) / NWT;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wave = w % NWT, kp = w / NWT;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = bh / a.H;
   const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
   const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
-  const int nown = wave < TM ? (TM - wave + NW - 1) / NW : 0;
+  const int nown = (kp < KP && wave < TM) ? (TM - wave + NWT - 1) / NWT : 0;
 
   Frag2 qf[TPW][2];
   float mrun[TPW], lsum[TPW];
   f32x4 acc[TPW][4];
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
-    const int lt = wave + NW * o;
+    const int lt = wave + NWT * o;
     mrun[o] = NEG_BIG;
     lsum[o] = 0.f;
 #pragma unroll
@@ -361,22 +376,49 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   }
   const int tile0 = chunk * a.tpc;
   const int tile1 = min(a.ntiles, tile0 + a.tpc);
+  // the landmark fragments arrive before any K/V copy is issued, so the
+  // copy pipeline below is never drained to wait for them
+  wait_vmcnt<0>();
   if constexpr (sizeof(IO) == 2) {
     if (mask != nullptr)
-      kv_stream_dma<TPW, NW, true>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+      kv_stream_dma<TPW, NW, true, KP>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
     else
-      kv_stream_dma<TPW, NW, false>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+      kv_stream_dma<TPW, NW, false, KP>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   } else {
-    kv_stream<IO, TPW, 64 * NW>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc);
+    kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+  }
+  if constexpr (KP == 2) {
+    // fold the odd-tile waves' states into the even-tile waves (same lanes)
+    float* st = reinterpret_cast<float*>(lds) + (size_t)wave * 64 * 18 + lane;
+    if (kp == 1 && nown > 0) {
+      st[0] = mrun[0];
+      st[64] = lsum[0];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[64 * (2 + 4 * dt + r)] = acc[0][dt][r];
+    }
+    __syncthreads();
+    if (kp == 0 && nown > 0) {
+      const float m1 = st[0], l1 = st[64];
+      const float mn = fmaxf(mrun[0], m1);
+      const float a0 = fast_exp2(mrun[0] - mn), a1 = fast_exp2(m1 - mn);
+      mrun[0] = mn;
+      lsum[0] = lsum[0] * a0 + l1 * a1;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[0][dt][r] = acc[0][dt][r] * a0 + st[64 * (2 + 4 * dt + r)] * a1;
+    }
   }
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
-    if (o >= nown) break;
-    const int i = 16 * (wave + NW * o) + c16;
+    if (o >= nown || kp != 0) break;
+    const int i = 16 * (wave + NWT * o) + c16;
     const float ls = sum_g(lsum[o]);
     const size_t row = ((size_t)bh * a.S + chunk) * M + i;
     if (g == 0) {
-      a.pmax[row] = mrun[o] * a.lscale;  // running max is kept unscaled
+      a.pmax[row] = mrun[o];  // log2 units of the scaled logit
       a.psum[row] = ls;
     }
     store_row16<float, false>(a.pacc + row * HD, acc[o]);

@@ -21,7 +21,7 @@
 namespace nys {
 
 struct MergeArgs {
-  const float* pmax;   // [BH][S][M]
+  const float* pmax;   // [BH][S][M], log2 units
   const float* psum;
   const float* pacc;   // [BH][S][M][64]
   const float* Z;      // [BH][M][M]
@@ -32,20 +32,52 @@ struct MergeArgs {
   int S;
 };
 
-// grid (M/16, BH): B V rows [16 bx, 16 bx + 16).
+// grid (M/16, BH): B V rows [16 bx, 16 bx + 16).  Thread (row, 4-channel
+// quad); the chunk loops are unrolled by 8 so the partial loads overlap.
 template <int M>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+  constexpr int U = 8;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int i = blockIdx.x * 16 + (t >> 4);
   const int d0 = (t & 15) * 4;
+  const size_t base = (size_t)bh * a.S * M + i;  // row of chunk s: base + s * M
   float mx = NEG_BIG;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.pmax[((size_t)bh * a.S + s) * M + i]);
+  int s = 0;
+  for (; s + U <= a.S; s += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = a.pmax[base + (size_t)(s + u) * M];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, v[u]);
+  }
+  for (; s < a.S; ++s) mx = fmaxf(mx, a.pmax[base + (size_t)s * M]);
   float tot = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.S; ++s) {
-    const size_t row = ((size_t)bh * a.S + s) * M + i;
-    const float wgt = fast_exp2((a.pmax[row] - mx) * LOG2E);
+  s = 0;
+  for (; s + U <= a.S; s += U) {
+    float pm[U], ps[U];
+    float4 pa[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t row = base + (size_t)(s + u) * M;
+      pm[u] = a.pmax[row];
+      ps[u] = a.psum[row];
+      pa[u] = *reinterpret_cast<const float4*>(a.pacc + row * HD + d0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = fast_exp2(pm[u] - mx);
+      tot += ps[u] * wgt;
+      acc[0] += pa[u].x * wgt;
+      acc[1] += pa[u].y * wgt;
+      acc[2] += pa[u].z * wgt;
+      acc[3] += pa[u].w * wgt;
+    }
+  }
+  for (; s < a.S; ++s) {
+    const size_t row = base + (size_t)s * M;
+    const float wgt = fast_exp2(a.pmax[row] - mx);
     tot += a.psum[row] * wgt;
     const float4 p = *reinterpret_cast<const float4*>(a.pacc + row * HD + d0);
     acc[0] += p.x * wgt;

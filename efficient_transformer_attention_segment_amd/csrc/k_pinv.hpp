@@ -12,7 +12,7 @@
 // split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, float32-accurate).
 //
 // pinv_block<M> (M <= 128): one workgroup per head, everything on chip, one
-//   wave per 16-row tile (see the function comment).  Two row-major LDS
+//   or two waves per 16-row tile (see the function comment).  Two row-major LDS
 //   regions of M x (M + 8) bf16 hi/lo suffice: each step reads one and
 //   writes the other (M = 128 fits the 160 KB LDS).
 //
@@ -48,11 +48,16 @@ __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
   return a.colmax[bh] * a.rowmax[bh];
 }
 
-// Waves per workgroup for m landmarks: one per 16-row tile, rounded up to a
-// power of two (2, 4 or 8).
+// Waves per workgroup for m landmarks: one per 16-row tile up to 128
+// landmarks, two per tile (each forming half of the tile's outputs) for
+// m <= 64, rounded up to a power of two (4 or 8).
+template <int M>
+constexpr int pinv_wpt() {
+  return M <= 64 ? 2 : 1;
+}
 template <int M>
 constexpr int nwaves() {
-  return M / 16 <= 2 ? 2 : (M / 16 <= 4 ? 4 : 8);
+  return (M / 16) * pinv_wpt<M>() <= 4 ? 4 : 8;
 }
 
 template <int M>
@@ -95,28 +100,40 @@ __device__ __forceinline__ void rowstore4(__bf16* Yh, __bf16* Yl, int row, int c
   *reinterpret_cast<bf16x4*>(Yl + row * LD + col) = l;
 }
 
-// Paired-order fragment from two stacked C tiles held by this lane.
-__device__ __forceinline__ Frag2 pairfrag(const f32x4 a, const f32x4 b) {
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return split8(x);
+// B operand for the paired k step ks of row `row` of a row-major LDS matrix
+// (hi / lo): elements k = 32ks + 4g + e and 32ks + 16 + 4g + (e - 4).
+template <int LD>
+__device__ __forceinline__ Frag2 rowfrag(const __bf16* Yh, const __bf16* Yl, int row, int ks) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const int k0 = row * LD + 32 * ks + 4 * g;
+  Frag2 f;
+  f.hi = cat44(*reinterpret_cast<const bf16x4*>(Yh + k0), *reinterpret_cast<const bf16x4*>(Yh + k0 + 16));
+  f.lo = cat44(*reinterpret_cast<const bf16x4*>(Yl + k0), *reinterpret_cast<const bf16x4*>(Yl + k0 + 16));
+  return f;
 }
 
-// One workgroup of nwaves<M>() waves per head; wave t owns rows
-// [16t, 16t + 16) of X, T1, T2 and Z.  Every product is formed transposed,
-// Y^T[:, own rows] = (left)^T (own rows of the right factor)^T, so its C
-// tile gives the lane 4 consecutive elements of one of its own rows:
+// One workgroup per head; wave w works on row tile t = w / WPT, i.e. rows
+// [16t, 16t + 16) of X, T1, T2 and Z, and forms the output tiles
+// i = h, h + WPT, ... (h = w % WPT) of each product.  Every product is formed
+// transposed, Y^T[:, own rows] = (left)^T (own rows of the right factor)^T,
+// so its C tile gives the lane 4 consecutive elements of one of its rows:
 //   step 1  X^T  = Z^T A^T                      (Z read from LDS)
 //   step 2  T1^T = 7 X^T - X^T X^T              (X from LDS)
 //   step 3  T2^T = 15 X^T - T1^T X^T            (T1 from LDS)
 //   step 4  Z'^T = (13 Z^T - T2^T Z^T) / 4      (T2 from LDS)
 // which is Z' = Z (13I - X(15I - X(7I - X))) / 4 with X = A Z, expanded.
-// The own-row fragments (A, X, Z) stay in registers; X and Z also stay in
-// float32 for the 7X, 15X and 13Z terms.  LDS holds the matrix each step
-// reads whole, row-major bf16 hi/lo, alternating between two regions.
+// The left operands come from LDS by transposed reads; the right operands
+// are the tile's own rows (A from registers, X and Z re-read from the LDS
+// copy after each barrier); X and Z also stay in float32 for the 7X, 15X
+// and 13Z terms.  LDS holds the matrix each step reads whole, row-major
+// bf16 hi/lo, alternating between two regions.
 template <int M>
 __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   constexpr int TM = M / 16, KS = M / 32, LD = M + 8;
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;  // t: own row tile
+  constexpr int WPT = pinv_wpt<M>();
+  constexpr int NI = TM / WPT;  // output tiles per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = w / WPT, h = w % WPT;
   const int g = lane >> 4, c16 = lane & 15;
   __bf16* const R0h = lds;
   __bf16* const R0l = lds + M * LD;
@@ -139,7 +156,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   const int row = 16 * t + c16;  // the lane's row of X, T1, T2, Z
 
   Frag2 Af[KS], Xf[KS], Zf[KS];
-  f32x4 Xacc[TM], Zacc[TM], acc[TM];
+  f32x4 Xacc[NI], Zacc[NI], acc[NI];
   if (own) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -148,77 +165,82 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
       for (int e = 0; e < 8; ++e) x[e] = A[(size_t)row * M + 32 * ks + 8 * g + e];
       Af[ks] = split8(x);
     }
-    // Z_0 = A^T / c: Zacc[i][r] = Z_0[row][16i + 4g + r]
+    // Z_0 = A^T / c: Zacc[j][r] = Z_0[row][16i + 4g + r], i = h + WPT j
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < NI; ++j) {
+      const int i = h + WPT * j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zacc[i][r] = A[(size_t)(16 * i + 4 * g + r) * M + row] * invc;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) Zf[ks] = pairfrag(Zacc[2 * ks], Zacc[2 * ks + 1]);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[i]);
+      for (int r = 0; r < 4; ++r) Zacc[j][r] = A[(size_t)(16 * i + 4 * g + r) * M + row] * invc;
+      rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[j]);
+    }
   }
   __syncthreads();
 
   for (int it = 0; it < a.n_iter; ++it) {
     const bool last = (it == a.n_iter - 1);
-    if (own) {  // step 1: X^T = Z^T A^T
+    if (own) {  // step 1: X^T = Z^T A^T; Z's own rows kept for step 4
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) Zf[ks] = rowfrag<LD>(R0h, R0l, row, ks);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, false>(R0h, R0l, i, ks), Af[ks], acc[i]);
+      for (int j = 0; j < NI; ++j) {
+        const int i = h + WPT * j;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[j] = mma<3>(colfrag<LD, false>(R0h, R0l, i, ks), Af[ks], acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        Xacc[i] = acc[i];
-        rowstore4<LD>(R1h, R1l, row, 16 * i + 4 * g, acc[i]);
+      for (int j = 0; j < NI; ++j) {
+        Xacc[j] = acc[j];
+        rowstore4<LD>(R1h, R1l, row, 16 * (h + WPT * j) + 4 * g, acc[j]);
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Xf[ks] = pairfrag(Xacc[2 * ks], Xacc[2 * ks + 1]);
     }
     __syncthreads();
     if (own) {  // step 2: T1^T = 7 X^T - X^T X^T
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) Xf[ks] = rowfrag<LD>(R1h, R1l, row, ks);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R1h, R1l, i, ks), Xf[ks], acc[i]);
+      for (int j = 0; j < NI; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[j] = mma<3>(colfrag<LD, true>(R1h, R1l, h + WPT * j, ks), Xf[ks], acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, 7.f * Xacc[i] - acc[i]);
+      for (int j = 0; j < NI; ++j)
+        rowstore4<LD>(R0h, R0l, row, 16 * (h + WPT * j) + 4 * g, 7.f * Xacc[j] - acc[j]);
     }
     __syncthreads();
     if (own) {  // step 3: T2^T = 15 X^T - T1^T X^T
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NI; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R0h, R0l, i, ks), Xf[ks], acc[i]);
+        for (int ks = 0; ks < KS; ++ks)
+          acc[j] = mma<3>(colfrag<LD, true>(R0h, R0l, h + WPT * j, ks), Xf[ks], acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) rowstore4<LD>(R1h, R1l, row, 16 * i + 4 * g, 15.f * Xacc[i] - acc[i]);
+      for (int j = 0; j < NI; ++j)
+        rowstore4<LD>(R1h, R1l, row, 16 * (h + WPT * j) + 4 * g, 15.f * Xacc[j] - acc[j]);
     }
     __syncthreads();
     if (own) {  // step 4: Z'^T = (13 Z^T - T2^T Z^T) / 4
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NI; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[i] = mma<3>(colfrag<LD, true>(R1h, R1l, i, ks), Zf[ks], acc[i]);
+        for (int ks = 0; ks < KS; ++ks)
+          acc[j] = mma<3>(colfrag<LD, true>(R1h, R1l, h + WPT * j, ks), Zf[ks], acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) Zacc[i] = 0.25f * (13.f * Zacc[i] - acc[i]);
-      if (last) {
+      for (int j = 0; j < NI; ++j) Zacc[j] = 0.25f * (13.f * Zacc[j] - acc[j]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          *reinterpret_cast<float4*>(Zg + (size_t)row * M + 16 * i + 4 * g) =
-              make_float4(Zacc[i][0], Zacc[i][1], Zacc[i][2], Zacc[i][3]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Zf[ks] = pairfrag(Zacc[2 * ks], Zacc[2 * ks + 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[i]);
+      for (int j = 0; j < NI; ++j) {
+        const int col = 16 * (h + WPT * j) + 4 * g;
+        if (last)
+          *reinterpret_cast<float4*>(Zg + (size_t)row * M + col) =
+              make_float4(Zacc[j][0], Zacc[j][1], Zacc[j][2], Zacc[j][3]);
+        else
+          rowstore4<LD>(R0h, R0l, row, col, Zacc[j]);
       }
     }
     __syncthreads();

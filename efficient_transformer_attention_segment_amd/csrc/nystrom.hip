@@ -25,7 +25,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/nystrom.h"
+#include "nystrom.h"
 #include "k_bv.hpp"
 #include "k_landmark.hpp"
 #include "k_merge.hpp"
@@ -83,13 +83,15 @@ Plan make_plan(int B, int H, int n, int m) {
   // landmark blocks: 8 threads per row, RS row slots per landmark, lpw landmarks per block
   p.RS = std::min(32, std::max(1, pow2floor(std::max(1, p.L / 8))));
   p.lpw = 32 / p.RS;
-  // key chunks for the B V partials: about two blocks per CU in total
+  // key chunks for the B V partials: as many blocks as stay resident in one
+  // round next to the pseudo-inverse blocks (two blocks per CU)
   p.ntiles = n / 32;
-  const int target = 512;
-  int S = std::max(1, std::min(p.ntiles, (target + p.BH - 1) / p.BH));
+  p.npinv = m <= 128 ? p.BH : 0;
+  const int resident = 2 * 256;
+  const int target = std::max(p.BH, resident - p.npinv);
+  int S = std::max(1, std::min(p.ntiles, target / p.BH));
   p.tpc = (p.ntiles + S - 1) / S;
   p.S = (p.ntiles + p.tpc - 1) / p.tpc;
-  p.npinv = m <= 128 ? p.BH : 0;
   const size_t BH = p.BH, M = m, D = HD;
   size_t o = 0;
   auto take = [&](size_t bytes) {
