@@ -37,6 +37,21 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// float32 matrix core, v_mfma_f32_16x16x4_f32: lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16]; C as above.  mma8_f32 runs eight of them over two
+// 8-element fragments (element e of both operands in instruction e), so it
+// contracts over k(g, e) for whatever k order the two fragments share; with
+// the fragments of the bf16 products it forms the same 16 x 16 x 32 product
+// in plain float32 arithmetic.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma8_f32(const float* a, const float* b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = mfma_f32(a[e], b[e], c);
+  return c;
+}
+
 struct Frag2 {
   bf16x8 hi, lo;
 };

@@ -431,7 +431,12 @@ template <typename IO, int M>
 __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
-    if constexpr (M <= 128) pinv_block<M>(pa, blockIdx.x, lds_dyn);
+    if constexpr (M <= 128) {
+      if constexpr (sizeof(IO) == 4)
+        pinv_block_f32<M>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
+      else
+        pinv_block<M>(pa, blockIdx.x, lds_dyn);
+    }
     return;
   }
   const int id = blockIdx.x - npinv;

@@ -12,9 +12,12 @@
 // in LDS in a fixed order (deterministic).  The scale d^-1/4 / L is applied
 // once; the landmarks are written in float32 and as bf16 hi/lo operands.
 //
-// k_gram: one workgroup per head computes A = softmax(Qt Kt^T) with
-// split-bf16 matrix-core products (float32-accurate) and the head's maximum
-// column sum and row sum of A.  The kernel boundary between the two is the
+// k_gram: one workgroup per head computes A = softmax(Qt Kt^T) and the
+// head's maximum column sum and row sum of A.  For float32 I/O the products
+// run on the float32 matrix core: A feeds the pseudo-inverse iteration, which
+// magnifies an error in A by up to the condition number of A once it has
+// converged, so A is formed in plain float32.  For bf16 I/O they are
+// split-bf16 products (relative error about 2^-16).  The kernel boundary between the two is the
 // only synchronisation (no device-wide fences).
 #pragma once
 
@@ -38,7 +41,7 @@ struct LandmarkArgs {
 
 // A = softmax(Qt Kt^T) for one head, by the 256 threads of the block.
 // M = m (multiple of 32).  csum: LDS scratch of (M/16) * M floats.
-template <int M>
+template <int M, bool F32>
 __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred) {
   constexpr int TM = M / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -48,14 +51,18 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
   float* A = a.A + (size_t)bh * M * M;
   float rmax_w = 0.f;
   for (int rt = wave; rt < TM; rt += 4) {
-    Frag2 af[2];
+    // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
+    float ax[2][8];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float x[8];
       const float* p = qt + (size_t)(rt * 16 + c16) * HD + ks * 32 + g * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = p[e];
-      af[ks] = split8(x);
+      for (int e = 0; e < 8; ++e) ax[ks][e] = p[e];
+    }
+    Frag2 af[2];
+    if constexpr (!F32) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) af[ks] = split8(ax[ks]);
     }
     f32x4 acc[TM];
 #pragma unroll
@@ -67,8 +74,10 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
         const float* p = kt + (size_t)(ct * 16 + c16) * HD + ks * 32 + g * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = p[e];
-        const Frag2 bf = split8(x);
-        acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+        if constexpr (F32)
+          acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
+        else
+          acc[ct] = mma<3>(af[ks], split8(x), acc[ct]);
       }
     }
     // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
@@ -203,11 +212,11 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
 }
 
 // grid: BH, block 256.
-template <int M>
+template <int M, bool F32>
 __global__ __launch_bounds__(256) void k_gram(LandmarkArgs a) {
   __shared__ float csum[(M / 16) * M];
   __shared__ float wred[8];
-  landmark_gram_tail<M>(a, blockIdx.x, csum, wred);
+  landmark_gram_tail<M, F32>(a, blockIdx.x, csum, wred);
 }
 
 }  // namespace nys

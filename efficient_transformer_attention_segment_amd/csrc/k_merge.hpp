@@ -8,7 +8,9 @@
 // k_merge merges 16 landmark rows per block over the S key chunks with the
 // log-sum-exp rule (fixed chunk order, deterministic); a row whose chunks
 // saw no valid key gives B V = 0.  k_w then forms W = Z (B V), 32 rows per
-// block, with split-bf16 matrix-core products, and writes W twice: float32
+// block (float32 matrix-core products for float32 I/O, where a converged Z
+// has large entries whose products cancel; split-bf16 products for bf16
+// I/O), and writes W twice: float32
 // row-major, and as the ready-made bf16 hi/lo A-operand fragments of W^T
 // that the output kernel loads with one 16-byte read per lane (rows in the
 // output kernel's channel order, k in the paired order).  Kernel boundaries order
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 
 // grid (M/32, BH): W rows [32 bx, 32 bx + 32) = Z[rows, :] (B V), then the
 // W^T fragments of k step bx for every d tile.
-template <int M, bool B16>
+template <int M, bool B16, bool F32>
 __global__ __launch_bounds__(256) void k_w(MergeArgs a) {
   constexpr int KS = M / 32;
   __shared__ float wt[32][HD + 1];
@@ -115,7 +117,10 @@ __global__ __launch_bounds__(256) void k_w(MergeArgs a) {
         x[e] = Z[(size_t)(16 * rt + c16) * M + 32 * ks + 8 * g + e];
         y[e] = BV[(size_t)(32 * ks + 8 * g + e) * HD + 16 * dt + c16];
       }
-      acc = mma<3>(split8(x), split8(y), acc);
+      if constexpr (F32)
+        acc = mma8_f32(x, y, acc);
+      else
+        acc = mma<3>(split8(x), split8(y), acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

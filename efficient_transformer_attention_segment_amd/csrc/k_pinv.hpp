@@ -8,13 +8,20 @@
 // option.
 //
 // The iteration is kept literally (X is recomputed from A and Z every step),
-// which is what keeps it self-correcting in finite precision.  Products are
-// split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, float32-accurate).
+// which is what keeps it self-correcting in finite precision.
 //
-// pinv_block<M> (M <= 128): one workgroup per head, everything on chip, one
-//   or two waves per 16-row tile (see the function comment).  Two row-major LDS
-//   regions of M x (M + 8) bf16 hi/lo suffice: each step reads one and
-//   writes the other (M = 128 fits the 160 KB LDS).
+// pinv_block<M> (M <= 128, bf16 I/O): one workgroup per head, everything on
+//   chip, one or two waves per 16-row tile (see the function comment).  Two
+//   row-major LDS regions of M x (M + 8) bf16 hi/lo suffice: each step reads
+//   one and writes the other (M = 128 fits the 160 KB LDS).  Products are
+//   split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, relative error
+//   about 2^-16).
+//
+// pinv_block_f32<M> (M <= 128, float32 I/O): the same schedule on the
+//   float32 matrix core with float32 matrices in LDS.  Once the iteration has
+//   converged, Z approaches A^+ and a relative error e in its products grows
+//   to about e * cond(A) in Z; float32 products keep the result at float32
+//   accuracy where split-bf16 products would not.
 //
 // k_pinv_init / k_pinv_gemm (M > 128): the same iteration as a sequence of
 //   batched launches, one product per launch, with the matrices in global
@@ -112,6 +119,15 @@ __device__ __forceinline__ Frag2 rowfrag(const __bf16* Yh, const __bf16* Yl, int
   return f;
 }
 
+// Z = Z_0 = A^T / c (no iterations), by the whole block.
+template <int M>
+__device__ __forceinline__ void store_z0(const float* A, float* Zg, float invc) {
+  for (int idx = threadIdx.x; idx < M * M; idx += blockDim.x) {
+    const int row = idx / M, col = idx % M;
+    Zg[idx] = A[(size_t)col * M + row] * invc;
+  }
+}
+
 // One workgroup per head; wave w works on row tile t = w / WPT, i.e. rows
 // [16t, 16t + 16) of X, T1, T2 and Z, and forms the output tiles
 // i = h, h + WPT, ... (h = w % WPT) of each product.  Every product is formed
@@ -146,10 +162,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   const float invc = 1.0f / c;
   if (threadIdx.x == 0) a.cscale[bh] = c;
   if (a.n_iter == 0) {
-    for (int idx = threadIdx.x; idx < M * M; idx += blockDim.x) {
-      const int row = idx / M, col = idx % M;
-      Zg[idx] = A[(size_t)col * M + row] * invc;
-    }
+    store_z0<M>(A, Zg, invc);
     return;
   }
   const bool own = t < TM;
@@ -241,6 +254,183 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
               make_float4(Zacc[j][0], Zacc[j][1], Zacc[j][2], Zacc[j][3]);
         else
           rowstore4<LD>(R0h, R0l, row, col, Zacc[j]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 variant.  The same waves, tiles and four steps, in the direct
+// orientation: wave (t, h) forms Y[16t .. 16t+15][16i .. 16i+15] for its
+// tiles i = h, h + WPT, ... as (own rows of the left factor) x (right
+// factor), so the C tile gives the lane 4 consecutive rows of one column.
+// Every matrix is therefore kept in LDS transposed (Y^T row-major, row
+// stride M + 4): a C tile is one 16-byte store, a right-factor operand (a
+// column of Y) is two 16-byte reads, and the own-row operands (rows of Z and
+// X, read once per iteration) are strided single reads; the stride M + 4
+// keeps both patterns free of bank conflicts.  Fragment element e of lane
+// group g is k = 32ks + 4g + e (e < 4) or 32ks + 16 + 4g + (e - 4).
+
+template <int M>
+constexpr int pinv_lds_bytes_f32() {
+  return 2 * M * (M + 4) * 4;  // two float32 regions, row stride M + 4
+}
+
+__device__ __forceinline__ int pk(int ks, int g, int e) { return 32 * ks + (e < 4 ? 4 * g + e : 12 + 4 * g + e); }
+
+// Own-row operand: row `row` of Y, from Y^T stored with row stride LD.
+template <int LD>
+__device__ __forceinline__ void rowop_t(const float* R, int row, int ks, float* f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = R[pk(ks, g, e) * LD + row];
+}
+
+// Right-factor operand: column `col` of Y = row `col` of Y^T (contiguous).
+template <int LD>
+__device__ __forceinline__ void colop_t(const float* R, int col, int ks, float* f) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const float* p = R + col * LD + 32 * ks + 4 * g;
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  const float4 v = *reinterpret_cast<const float4*>(p + 16);
+  f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+  f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+}
+
+// C tile element (row0 + 4g + r, col) for r = 0..3 into Y^T.
+template <int LD>
+__device__ __forceinline__ void store_t(float* R, int col, int row4, const f32x4 v) {
+  *reinterpret_cast<float4*>(R + col * LD + row4) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <int M>
+__device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
+  constexpr int TM = M / 16, KS = M / 32, LD = M + 4;
+  constexpr int WPT = pinv_wpt<M>();
+  constexpr int NI = TM / WPT;  // output tiles per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = w / WPT, h = w % WPT;
+  const int g = lane >> 4, c16 = lane & 15;
+  float* const R0 = lds;
+  float* const R1 = lds + M * LD;
+  const float* A = a.A + (size_t)bh * M * M;
+  float* Zg = a.Z + (size_t)bh * M * M;
+
+  const float c = pinv_scale(a, bh);
+  const float invc = 1.0f / c;
+  if (threadIdx.x == 0) a.cscale[bh] = c;
+  if (a.n_iter == 0) {
+    store_z0<M>(A, Zg, invc);
+    return;
+  }
+  const bool own = t < TM;
+  const int row0 = 16 * t;            // the wave's rows of X, T1, T2, Z
+  const int row = row0 + c16;         // the lane's row in A-operand fragments
+  const int row4 = row0 + 4 * g;      // first of the lane's 4 C-tile rows
+
+  float Af[KS][8], Xf[KS][8], Zf[KS][8];
+  f32x4 Xacc[NI], Zacc[NI], acc[NI];
+  if (own) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float* p = A + (size_t)row * M + 32 * ks + 4 * g;
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      const float4 v = *reinterpret_cast<const float4*>(p + 16);
+      Af[ks][0] = u.x; Af[ks][1] = u.y; Af[ks][2] = u.z; Af[ks][3] = u.w;
+      Af[ks][4] = v.x; Af[ks][5] = v.y; Af[ks][6] = v.z; Af[ks][7] = v.w;
+    }
+    // Z_0 = A^T / c: Zacc[j][r] = Z_0[row4 + r][16i + c16] = A[16i + c16][row4 + r] / c,
+    // and Z_0^T = A / c goes to LDS.
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = 16 * (h + WPT * j) + c16;
+      const float4 z = *reinterpret_cast<const float4*>(A + (size_t)col * M + row4);
+      Zacc[j] = f32x4{z.x * invc, z.y * invc, z.z * invc, z.w * invc};
+      store_t<LD>(R0, col, row4, Zacc[j]);
+    }
+  }
+  __syncthreads();
+
+  for (int it = 0; it < a.n_iter; ++it) {
+    const bool last = (it == a.n_iter - 1);
+    if (own) {  // step 1: X = A Z; Z's own rows kept for step 4
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) rowop_t<LD>(R0, row, ks, Zf[ks]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = 16 * (h + WPT * j) + c16;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float b[8];
+          colop_t<LD>(R0, col, ks, b);
+          acc[j] = mma8_f32(Af[ks], b, acc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        Xacc[j] = acc[j];
+        store_t<LD>(R1, 16 * (h + WPT * j) + c16, row4, acc[j]);
+      }
+    }
+    __syncthreads();
+    if (own) {  // step 2: T1 = 7 X - X X
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) rowop_t<LD>(R1, row, ks, Xf[ks]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = 16 * (h + WPT * j) + c16;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float b[8];
+          colop_t<LD>(R1, col, ks, b);
+          acc[j] = mma8_f32(Xf[ks], b, acc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) store_t<LD>(R0, 16 * (h + WPT * j) + c16, row4, 7.f * Xacc[j] - acc[j]);
+    }
+    __syncthreads();
+    if (own) {  // step 3: T2 = 15 X - X T1
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = 16 * (h + WPT * j) + c16;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float b[8];
+          colop_t<LD>(R0, col, ks, b);
+          acc[j] = mma8_f32(Xf[ks], b, acc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) store_t<LD>(R1, 16 * (h + WPT * j) + c16, row4, 15.f * Xacc[j] - acc[j]);
+    }
+    __syncthreads();
+    if (own) {  // step 4: Z' = (13 Z - Z T2) / 4
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = 16 * (h + WPT * j) + c16;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float b[8];
+          colop_t<LD>(R1, col, ks, b);
+          acc[j] = mma8_f32(Zf[ks], b, acc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        Zacc[j] = 0.25f * (13.f * Zacc[j] - acc[j]);
+        const int col = 16 * (h + WPT * j) + c16;
+        if (last) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Zg[(size_t)(row4 + r) * M + col] = Zacc[j][r];
+        } else {
+          store_t<LD>(R0, col, row4, Zacc[j]);
+        }
       }
     }
     __syncthreads();

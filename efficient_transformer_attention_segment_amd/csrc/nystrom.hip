@@ -231,7 +231,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   }
   {
     ProfScope ps(st, "k_gram");
-    hipLaunchKernelGGL((k_gram<M>), dim3(p.BH), dim3(256), 0, st, la);
+    hipLaunchKernelGGL((k_gram<M, sizeof(IO) == 4>), dim3(p.BH), dim3(256), 0, st, la);
     HIP_TRY(hipGetLastError());
   }
 
@@ -260,7 +260,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
   size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
-  if constexpr (M <= 128) lds2 = std::max<size_t>(lds2, pinv_lds_bytes<M>());
+  if constexpr (M <= 128)
+    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M>());
   HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
   {
     ProfScope ps(st, "k_pinv_bv");
@@ -311,7 +312,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   }
   {
     ProfScope ps(st, "k_w");
-    hipLaunchKernelGGL((k_w<M, sizeof(IO) == 2>), dim3(M / 32, p.BH), dim3(256), 0, st, ma);
+    hipLaunchKernelGGL((k_w<M, sizeof(IO) == 2, sizeof(IO) == 4>), dim3(M / 32, p.BH), dim3(256), 0, st, ma);
     HIP_TRY(hipGetLastError());
   }
 
