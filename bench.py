@@ -10,10 +10,10 @@ its Q, K, V from HBM rather than from the previous step's cache lines.
 Prints ONE JSON line.  `value` is tokens/s = B * n / step time on the
 headline workload (bf16, B=4 H=12 n=4096 d=64 m=64, the n = 4096 config of
 the target).  `roofline` rates the kernel that takes the most time per step
-(per-kernel durations from hipEvents the library records around its own
-launches, over the same number of steps); `cpu_baseline` times the float64
-oracle on the host cores.  --gpus above 1 is refused: this build runs on one
-GPU.
+(per-kernel durations from the hipEvent pair the library attaches to each
+of its launches, stamped with the kernel's own start and end, over the same
+number of steps); `cpu_baseline` times the float64 oracle on the host cores.
+--gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -46,6 +46,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="no GPU work: 'commands W DIR' prints the rocprofv3 runs; 'trace W DIR OUT' "
+                         "and 'traffic W DIR OUT' turn their CSV output into text summaries")
     return ap.parse_args()
 
 
@@ -121,6 +124,25 @@ def make_replicas(w, x, count, torch):
     return reps, mask, conv
 
 
+def copy_bandwidth(torch, mb=1024, reps=10):
+    """Attainable HBM bandwidth of a plain device copy (read + write bytes
+    per second), timed with events on the current stream."""
+    n = (mb << 20) // 4
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbs
+
+
 def time_workload(w, steps, warmup, torch, nys):
     from efficient_transformer_attention_segment_amd.workloads import make_inputs
     x = make_inputs(w)
@@ -142,14 +164,27 @@ def time_workload(w, steps, warmup, torch, nys):
         step(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    # same steps again with the library's per-kernel hipEvents
+    # the same steps with one event at every step boundary on the stream the
+    # library launches on (torch's current stream): the step-time spread
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    st = sorted(1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    pct = lambda f: st[min(len(st) - 1, int(round(f * (len(st) - 1))))]
+    spread = {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
+    # and again with the library's kernel timing on: each launch carries a
+    # hipEvent pair that the runtime stamps with the kernel's own start and
+    # end on that stream
     nys.profile_enable(True)
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     prof = nys.profile_collect()
     nys.profile_enable(False)
-    return ms, prof, count, x
+    return ms, prof, count, x, spread
 
 
 def cpu_baseline(w, x, budget_s):
@@ -170,9 +205,17 @@ def cpu_baseline(w, x, budget_s):
         if len(times) >= 3 or time.perf_counter() - t_start > budget_s:
             break
     med = float(np.median(times))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": w.tokens / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(times)} full float64 oracle calls of {w.name} (median {med:.2f} s each)",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model, "blas_threads": int(threads)}
 
 
 def copy_probe(mb, torch):
@@ -185,8 +228,136 @@ def copy_probe(mb, torch):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    """'void nys::k_out<unsigned short, 64>(nys::OutArgs)' -> 'k_out'."""
+    head = name.split("(")[0].split("<")[0]
+    return head.replace("void ", "").split("::")[-1].strip()
+
+
+# rocprofv3 runs behind the summaries in profiles/ (run from /tmp with
+# TMPDIR=/tmp; {R} = repository root, {O} = output directory, {W} = workload
+# index).  Counter passes each take one counter, on a short bench run.
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {O}/trace -o trace -- "
+             "python3 {R}/bench.py --workload {W} --steps 20 --warmup 5 --also '' --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {O}/fetch -o fetch -- "
+             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {O}/write -o write -- "
+             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {O}/copy_fetch -o copy_fetch -- "
+                  "python3 {R}/bench.py --copy-probe-mb 256",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {O}/copy_write -o copy_write -- "
+                  "python3 {R}/bench.py --copy-probe-mb 256",
+}
+COPY_PROBE_MB = 256
+
+
+def summarize(argv):
+    """Text summaries of rocprofv3 output for profiles/.
+
+    commands W O          print the rocprofv3 command lines for workload W
+    trace W O OUTDIR      kernel_trace_<workload>.txt: rocprofv3 per-kernel
+                          statistics beside the bench's own event timings
+    traffic W O OUTDIR    traffic_<kernel>_<workload>.txt for every library
+                          kernel: FETCH_SIZE / WRITE_SIZE per launch, scaled
+                          by a plain copy of known size
+    """
+    from efficient_transformer_attention_segment_amd.workloads import WORKLOADS
+    kind, widx, odir = argv[0], int(argv[1]), argv[2]
+    w = WORKLOADS[widx]
+    cmds = {k: v.format(R="<repo>", O=odir, W=widx) for k, v in PROFILE_COMMANDS.items()}
+    if kind == "commands":
+        for k, v in PROFILE_COMMANDS.items():
+            print(v.format(R=ROOT, O=odir, W=widx))
+        return
+    outdir = argv[3]
+    sha = source_sha()
+    if kind == "trace":
+        stats = _csv_rows(os.path.join(odir, "trace", "trace_kernel_stats.csv"))
+        bench_line = None   # the same bench command, run without the profiler
+        plain = os.path.join(odir, "plain_bench.json")
+        if os.path.exists(plain):
+            with open(plain) as f:
+                for line in f:
+                    if line.startswith("{"):
+                        bench_line = json.loads(line)
+        lines = [f"# Kernel durations, {w.name}",
+                 f"# command (from /tmp, TMPDIR=/tmp): {cmds['trace']}",
+                 f"# summary: python3 bench.py --summarize trace {widx} {odir} {outdir}",
+                 f"source_sha: {sha}", "",
+                 f"# bench column: {cmds['trace'].split(' -- ', 1)[1]} run alone (no profiler), "
+                 "kernel-stamped hipEvents",
+                 "kernel | calls | rocprof avg_us | min_us | max_us | % of GPU time | bench hipEvent avg_us",
+                 "---|---|---|---|---|---|---"]
+        bk = (bench_line or {}).get("kernels", {})
+        for r in stats:
+            k = _short(r["Name"])
+            ev = bk.get(k, {}).get("avg_us")
+            lines.append(f"{r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.2f} | {'' if ev is None else f'{ev:.2f}'}")
+        if bench_line:
+            lines += ["", f"bench without the profiler: ms_per_step {bench_line['ms_per_step']}, "
+                          f"step_us {bench_line.get('step_us')}, value {bench_line['value']} tokens/s"]
+        path = os.path.join(outdir, f"kernel_trace_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(path)
+        return
+    if kind == "traffic":
+        copy_bytes = COPY_PROBE_MB << 20
+
+        def per_kernel(path):
+            acc = {}
+            for r in _csv_rows(path):
+                acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+            return acc
+
+        def copy_kib(path):
+            return max(float(r["Counter_Value"]) for r in _csv_rows(path) if "copy" in r["Kernel_Name"].lower())
+
+        f_fac = copy_bytes / 1024.0 / copy_kib(os.path.join(odir, "copy_fetch", "copy_fetch_counter_collection.csv"))
+        w_fac = copy_bytes / 1024.0 / copy_kib(os.path.join(odir, "copy_write", "copy_write_counter_collection.csv"))
+        fk = per_kernel(os.path.join(odir, "fetch", "fetch_counter_collection.csv"))
+        wk = per_kernel(os.path.join(odir, "write", "write_counter_collection.csv"))
+        per_bytes, _ = algorithmic_bytes(w)
+        for k in sorted(fk):
+            if not k.startswith("k_"):
+                continue
+            fkib = sum(fk[k]) / len(fk[k])
+            wkib = sum(wk.get(k, [0.0])) / max(1, len(wk.get(k, [])))
+            hbm = (fkib * f_fac + wkib * w_fac) * 1024.0
+            lines = [f"# HBM traffic per launch of {k}, {w.name}",
+                     f"# commands (from /tmp, TMPDIR=/tmp):",
+                     *[f"#   {cmds[c]}" for c in ("fetch", "write", "copy_fetch", "copy_write")],
+                     f"# summary: python3 bench.py --summarize traffic {widx} {odir} {outdir}",
+                     f"# factors: a {COPY_PROBE_MB} MiB device copy reads {COPY_PROBE_MB} MiB and writes "
+                     f"{COPY_PROBE_MB} MiB; FETCH_SIZE / WRITE_SIZE read for it give the scale factors below",
+                     f"workload: {w.name}", f"kernel: {k}", f"source_sha: {sha}",
+                     f"dispatches: {len(fk[k])}",
+                     f"fetch_kib_per_launch: {fkib:.1f}", f"write_kib_per_launch: {wkib:.1f}",
+                     f"copy_fetch_factor: {f_fac:.3f}", f"copy_write_factor: {w_fac:.3f}",
+                     f"hbm_bytes_per_launch: {hbm:.0f}",
+                     f"algorithmic_bytes_per_launch: {per_bytes.get(k, 'n/a')}"]
+            path = os.path.join(outdir, f"traffic_{k}_{w.name}.txt")
+            with open(path, "w") as f:
+                f.write("\n".join(lines) + "\n")
+            print(path)
+        return
+    raise SystemExit(f"unknown summary kind {kind!r}")
+
+
 def main():
     args = parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -201,7 +372,7 @@ def main():
     from efficient_transformer_attention_segment_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    ms, prof, reps, x = time_workload(w, args.steps, args.warmup, torch, nys)
+    ms, prof, reps, x, spread = time_workload(w, args.steps, args.warmup, torch, nys)
     value = w.tokens / (ms / 1e3)
     per_bytes, path_bytes = algorithmic_bytes(w)
     sha = source_sha()
@@ -225,7 +396,7 @@ def main():
         wi = WORKLOADS[int(s)]
         if wi.index == w.index:
             continue
-        msi, profi, _, _ = time_workload(wi, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
+        msi, profi, _, _, _ = time_workload(wi, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
         pb, pathb = algorithmic_bytes(wi)
         fl = algorithmic_flops(wi)
         also.append({"workload": wi.name, "dtype": wi.dtype, "ms_per_step": round(msi, 4),
@@ -234,6 +405,10 @@ def main():
                      "path_roofline_us": round(1e6 * max(pathb / (HBM_PEAK_GBS * 1e9),
                                                          fl / (MFMA_PEAK_TFLOPS[wi.dtype] * 1e12)), 2),
                      "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
+    copy_gbs = copy_bandwidth(torch)
+    roofline["attainable_copy_GBps"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    path["frac_of_copy"] = round(path_bytes / (ms * 1e-3) / 1e9 / copy_gbs, 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, x, args.cpu_seconds)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -244,6 +419,7 @@ def main():
                    "n_iter": w.n_iter, "init_option": w.init_option, "conv_taps": 65,
                    "mask": (f"valid length U{{{w.mask[0]}..{w.mask[1]}}}" if w.mask else "none"),
                    "input_replicas": reps, "parallelism": "single GPU"},
+        "step_us": spread,
         "roofline": roofline, "path": path, "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()}
                                                          for k, v in kern.items()},
         "cpu_baseline": cpu, "also": also, "source_sha": sha,

@@ -14,6 +14,7 @@
 // Kernel boundaries are the only cross-workgroup synchronisation.
 // The exact branch (m == n) is one k_exact launch.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -129,8 +130,11 @@ Plan make_plan(int B, int H, int n, int m) {
 }
 
 // ------------------------------------------------------- kernel timing ---
-// While enabled, every launch is bracketed by a pair of hipEvents on its
-// stream; nystrom_profile_collect() resolves them into per-kernel sums.
+// Every launch goes through launch().  While timing is enabled it uses
+// hipExtLaunchKernelGGL with a start / stop event pair, which the runtime
+// stamps with the kernel's own begin and end (no extra marker packets, so
+// the figures match a kernel trace and the queue is not slowed);
+// nystrom_profile_collect() resolves them into per-kernel sums.
 struct ProfRec {
   const char* name;
   hipEvent_t a, b;
@@ -139,26 +143,30 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
-struct ProfScope {
-  hipStream_t st;
-  ProfRec rec{nullptr, nullptr, nullptr};
-  ProfScope(hipStream_t s, const char* name) : st(s) {
+template <typename... Args, typename F = void (*)(Args...)>
+hipError_t launch(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                  Args... args) {
+  bool on;
+  {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
-    rec.name = name;
-    if (hipEventCreate(&rec.a) != hipSuccess || hipEventCreate(&rec.b) != hipSuccess) {
-      rec.name = nullptr;
-      return;
-    }
-    (void)hipEventRecord(rec.a, st);
+    on = g_prof_on;
   }
-  ~ProfScope() {
-    if (!rec.name) return;
-    (void)hipEventRecord(rec.b, st);
+  ProfRec rec{nullptr, nullptr, nullptr};
+  if (on && hipEventCreate(&rec.a) == hipSuccess) {
+    if (hipEventCreate(&rec.b) == hipSuccess)
+      rec.name = name;
+    else
+      (void)hipEventDestroy(rec.a);
+  }
+  if (rec.name) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, rec.a, rec.b, 0, args...);
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof.push_back(rec);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
   }
-};
+  return hipGetLastError();
+}
 
 // ----------------------------------------------------------- workspace ---
 struct Workspace {
@@ -223,17 +231,9 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.A = at<float>(w, p.off_A);
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
-  {
-    ProfScope ps(st, "k_landmark");
-    hipLaunchKernelGGL((k_landmark<IO, M>), dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
-                       (const IO*)k, la);
-    HIP_TRY(hipGetLastError());
-  }
-  {
-    ProfScope ps(st, "k_gram");
-    hipLaunchKernelGGL((k_gram<M, sizeof(IO) == 4>), dim3(p.BH), dim3(256), 0, st, la);
-    HIP_TRY(hipGetLastError());
-  }
+  HIP_TRY(launch("k_landmark", k_landmark<IO, M>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
+                 (const IO*)k, la));
+  HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(256), 0, st, la));
 
   PinvArgs pa;
   pa.A = la.A;
@@ -263,20 +263,12 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   if constexpr (M <= 128)
     lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M>());
   HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
-  {
-    ProfScope ps(st, "k_pinv_bv");
-    hipLaunchKernelGGL((k_pinv_bv<IO, M>), dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), lds2, st, pa, ba,
-                       p.npinv);
-    HIP_TRY(hipGetLastError());
-  }
+  HIP_TRY(launch("k_pinv_bv", k_pinv_bv<IO, M>, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()),
+                 (uint32_t)lds2, st, pa, ba, p.npinv));
 
   const float* Zfinal = pa.Z;
   if constexpr (M > 128) {
-    {
-      ProfScope ps(st, "k_pinv_init");
-      hipLaunchKernelGGL(k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M);
-      HIP_TRY(hipGetLastError());
-    }
+    HIP_TRY(launch("k_pinv_init", k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M));
     float* Zc = pa.Z;
     float* Zn = at<float>(w, p.off_Z2);
     float* X = at<float>(w, p.off_X);
@@ -284,12 +276,14 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     float* T2 = at<float>(w, p.off_T2);
     const dim3 gg((M / 32) * (M / 32), p.BH);
     for (int it = 0; it < n_iter; ++it) {
-      ProfScope ps(st, "k_pinv_gemm x4");
-      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, pa.A, Zc, X, M, 0.f, 1.f);
-      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, X, T1, M, 7.f, 1.f);
-      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, X, T1, T2, M, 15.f, 1.f);
-      hipLaunchKernelGGL(k_pinv_gemm, gg, dim3(256), 0, st, Zc, T2, Zn, M, 13.f, 0.25f);
-      HIP_TRY(hipGetLastError());
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X, M,
+                     0.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1, M,
+                     7.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2, M,
+                     15.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn, M,
+                     13.f, 0.25f));
       std::swap(Zc, Zn);
     }
     Zfinal = Zc;
@@ -305,16 +299,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ma.wf_hi = at<__bf16>(w, p.off_wfh);
   ma.wf_lo = at<__bf16>(w, p.off_wfl);
   ma.S = p.S;
-  {
-    ProfScope ps(st, "k_merge");
-    hipLaunchKernelGGL((k_merge<M>), dim3(M / 16, p.BH), dim3(256), 0, st, ma);
-    HIP_TRY(hipGetLastError());
-  }
-  {
-    ProfScope ps(st, "k_w");
-    hipLaunchKernelGGL((k_w<M, sizeof(IO) == 2, sizeof(IO) == 4>), dim3(M / 32, p.BH), dim3(256), 0, st, ma);
-    HIP_TRY(hipGetLastError());
-  }
+  HIP_TRY(launch("k_merge", k_merge<M>, dim3(M / 16, p.BH), dim3(256), 0, st, ma));
+  HIP_TRY(launch("k_w", k_w<M, sizeof(IO) == 2, sizeof(IO) == 4>, dim3(M / 32, p.BH), dim3(256), 0, st, ma));
 
   OutArgs oa;
   oa.q = q;
@@ -331,11 +317,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.lscale = s4;
   const size_t lds4 = sizeof(IO) == 2 ? (size_t)OutLayoutDMA<M>::LDS_BYTES : (size_t)OutLayout<IO, M>::LDS_BYTES;
   HIP_TRY(allow_lds(k_out<IO, M>, lds4));
-  {
-    ProfScope ps(st, "k_out");
-    hipLaunchKernelGGL((k_out<IO, M>), dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), lds4, st, oa);
-    HIP_TRY(hipGetLastError());
-  }
+  HIP_TRY(launch("k_out", k_out<IO, M>, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
   return NYS_OK;
 }
 
@@ -354,11 +336,7 @@ int launch_exact(int B, int H, int n, const void* q, const void* k, const void* 
   ea.lscale = 1.0f / sqrtf((float)HD);
   const size_t lds = exact_lds_bytes<IO>();
   HIP_TRY(allow_lds(k_exact<IO>, lds));
-  {
-    ProfScope ps(st, "k_exact");
-    hipLaunchKernelGGL((k_exact<IO>), dim3((n + 63) / 64, B * H), dim3(256), lds, st, ea);
-    HIP_TRY(hipGetLastError());
-  }
+  HIP_TRY(launch("k_exact", k_exact<IO>, dim3((n + 63) / 64, B * H), dim3(256), (uint32_t)lds, st, ea));
   return NYS_OK;
 }
 
