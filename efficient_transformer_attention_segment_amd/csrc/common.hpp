@@ -170,6 +170,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+__device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Row-major 64-channel bf16 tiles in LDS are stored with the 16-byte chunk
 // index XOR-swizzled by the row (chunk c of row r at position c ^ (r & 7))
 // so that column-chunk reads of 8 consecutive rows hit distinct banks.

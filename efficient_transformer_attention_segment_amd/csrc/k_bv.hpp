@@ -434,8 +434,10 @@ __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvA
     if constexpr (M <= 128) {
       if constexpr (sizeof(IO) == 4)
         pinv_block_f32<M>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
+      else if (pa.f16)
+        pinv_block<M, true>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
       else
-        pinv_block<M>(pa, blockIdx.x, lds_dyn);
+        pinv_block<M, false>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
     }
     return;
   }

@@ -39,6 +39,7 @@ struct PinvArgs {
   float* Z;             // [BH][M][M] out
   float* cscale;        // [BH] out
   int BH, n_iter, init_option;
+  int f16;              // bf16 I/O: 1 = single fp16 products, 0 = split bf16
 };
 
 __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
@@ -67,55 +68,127 @@ constexpr int nwaves() {
   return (M / 16) * pinv_wpt<M>() <= 4 ? 4 : 8;
 }
 
-template <int M>
+// ---------------------------------------------------------------------------
+// bf16-I/O variant.  Operands live in LDS as 16-bit planes, in one of two
+// encodings:
+//   split bf16 (F16 = false): planes hi and lo, products hi*hi + hi*lo +
+//     lo*hi (relative error about 2^-16);
+//   single fp16 (F16 = true): one plane, one v_mfma_f32_16x16x32_f16 per
+//     product (11-bit operands, float32 accumulation): a third of the
+//     matrix-core work and half the LDS traffic.
+// The host takes fp16 for iteration counts up to 8: the iterate after t
+// steps is a fixed polynomial of A A^T applied to A^T, so its sensitivity to
+// operand rounding grows with t (a converged iterate magnifies errors by up
+// to the condition number of A), and the split encoding beyond that.
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+template <bool F16>
+struct POp;
+
+template <>
+struct POp<false> {
+  static constexpr int NP = 2;  // planes
+  typedef Frag2 Frag;
+  __device__ static __forceinline__ Frag make(const float* x) { return split8(x); }
+  __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) { return nys::mma<3>(a, b, c); }
+  __device__ static __forceinline__ void set(Frag& f, int p, s16x8 v) {
+    if (p == 0)
+      f.hi = __builtin_bit_cast(bf16x8, v);
+    else
+      f.lo = __builtin_bit_cast(bf16x8, v);
+  }
+  // 4 floats -> plane words
+  __device__ static __forceinline__ void enc4(const f32x4 v, s16x4* w) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      __bf16 a, b;
+      split1(v[r], a, b);
+      h[r] = a;
+      l[r] = b;
+    }
+    w[0] = __builtin_bit_cast(s16x4, h);
+    w[1] = __builtin_bit_cast(s16x4, l);
+  }
+};
+
+template <>
+struct POp<true> {
+  static constexpr int NP = 1;
+  struct Frag {
+    f16x8 v;
+  };
+  __device__ static __forceinline__ Frag make(const float* x) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = (_Float16)x[e];
+    return f;
+  }
+  __device__ static __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ void set(Frag& f, int, s16x8 v) { f.v = __builtin_bit_cast(f16x8, v); }
+  __device__ static __forceinline__ void enc4(const f32x4 v, s16x4* w) {
+    f16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (_Float16)v[r];
+    w[0] = __builtin_bit_cast(s16x4, h);
+  }
+};
+
+template <int M, bool F16>
 constexpr int pinv_lds_bytes() {
-  return 4 * M * (M + 8) * 2;  // two regions, hi + lo, bf16, row stride M + 8
+  return 2 * POp<F16>::NP * M * (M + 8) * 2;  // two regions of NP planes, row stride M + 8
 }
 
-__device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
+__device__ __forceinline__ s16x4 lds_tr_raw(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+}
+
+__device__ __forceinline__ s16x8 cat44(s16x4 a, s16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // A operand rows i*16 .. i*16+15 of Y^T (= columns of Y) for one 32-wide k
-// step, read from row-major Y (hi / lo, row stride LD) with two transposed
-// reads.  PAIRED selects the paired k order (k = 4g + e, 16 + 4g + e - 4),
-// otherwise the standard one (k = 8g + e).
-template <int LD, bool PAIRED>
-__device__ __forceinline__ Frag2 colfrag(const __bf16* Yh, const __bf16* Yl, int i, int ks) {
+// step, read from row-major Y (row stride LD, planes PL apart) with two
+// transposed reads per plane.  PAIRED selects the paired k order
+// (k = 4g + e, 16 + 4g + e - 4), otherwise the standard one (k = 8g + e).
+template <int LD, int PL, bool PAIRED, bool F16>
+__device__ __forceinline__ typename POp<F16>::Frag colfrag(const u16* Y, int i, int ks) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int k0 = 32 * ks + (PAIRED ? 4 * g : 8 * g) + (c16 >> 2);
   const int k1 = k0 + (PAIRED ? 16 : 4);
   const int col = 16 * i + 4 * (c16 & 3);
-  Frag2 f;
-  f.hi = cat44(lds_read_tr(Yh + k0 * LD + col), lds_read_tr(Yh + k1 * LD + col));
-  f.lo = cat44(lds_read_tr(Yl + k0 * LD + col), lds_read_tr(Yl + k1 * LD + col));
+  typename POp<F16>::Frag f;
+#pragma unroll
+  for (int p = 0; p < POp<F16>::NP; ++p)
+    POp<F16>::set(f, p, cat44(lds_tr_raw(Y + p * PL + k0 * LD + col), lds_tr_raw(Y + p * PL + k1 * LD + col)));
   return f;
 }
 
-// Store this lane's 4 consecutive elements Y[row][col .. col+3] (hi / lo).
-template <int LD>
-__device__ __forceinline__ void rowstore4(__bf16* Yh, __bf16* Yl, int row, int col, const f32x4 v) {
-  bf16x4 h, l;
+// Store this lane's 4 consecutive elements Y[row][col .. col+3].
+template <int LD, int PL, bool F16>
+__device__ __forceinline__ void rowstore4(u16* Y, int row, int col, const f32x4 v) {
+  s16x4 w[POp<F16>::NP];
+  POp<F16>::enc4(v, w);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    __bf16 a, b;
-    split1(v[r], a, b);
-    h[r] = a;
-    l[r] = b;
-  }
-  *reinterpret_cast<bf16x4*>(Yh + row * LD + col) = h;
-  *reinterpret_cast<bf16x4*>(Yl + row * LD + col) = l;
+  for (int p = 0; p < POp<F16>::NP; ++p) *reinterpret_cast<s16x4*>(Y + p * PL + row * LD + col) = w[p];
 }
 
-// B operand for the paired k step ks of row `row` of a row-major LDS matrix
-// (hi / lo): elements k = 32ks + 4g + e and 32ks + 16 + 4g + (e - 4).
-template <int LD>
-__device__ __forceinline__ Frag2 rowfrag(const __bf16* Yh, const __bf16* Yl, int row, int ks) {
+// B operand for the paired k step ks of row `row` of a row-major LDS
+// matrix: elements k = 32ks + 4g + e and 32ks + 16 + 4g + (e - 4).
+template <int LD, int PL, bool F16>
+__device__ __forceinline__ typename POp<F16>::Frag rowfrag(const u16* Y, int row, int ks) {
   const int g = (threadIdx.x & 63) >> 4;
   const int k0 = row * LD + 32 * ks + 4 * g;
-  Frag2 f;
-  f.hi = cat44(*reinterpret_cast<const bf16x4*>(Yh + k0), *reinterpret_cast<const bf16x4*>(Yh + k0 + 16));
-  f.lo = cat44(*reinterpret_cast<const bf16x4*>(Yl + k0), *reinterpret_cast<const bf16x4*>(Yl + k0 + 16));
+  typename POp<F16>::Frag f;
+#pragma unroll
+  for (int p = 0; p < POp<F16>::NP; ++p)
+    POp<F16>::set(f, p, cat44(*reinterpret_cast<const s16x4*>(Y + p * PL + k0),
+                              *reinterpret_cast<const s16x4*>(Y + p * PL + k0 + 16)));
   return f;
 }
 
@@ -141,20 +214,20 @@ __device__ __forceinline__ void store_z0(const float* A, float* Zg, float invc) 
 // The left operands come from LDS by transposed reads; the right operands
 // are the tile's own rows (A from registers, X and Z re-read from the LDS
 // copy after each barrier); X and Z also stay in float32 for the 7X, 15X
-// and 13Z terms.  LDS holds the matrix each step reads whole, row-major
-// bf16 hi/lo, alternating between two regions.
-template <int M>
-__device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
-  constexpr int TM = M / 16, KS = M / 32, LD = M + 8;
+// and 13Z terms.  LDS holds the matrix each step reads whole, row-major,
+// alternating between two regions.
+template <int M, bool F16>
+__device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
+  typedef POp<F16> P;
+  typedef typename P::Frag Frag;
+  constexpr int TM = M / 16, KS = M / 32, LD = M + 8, PL = M * LD;
   constexpr int WPT = pinv_wpt<M>();
   constexpr int NI = TM / WPT;  // output tiles per wave
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = w / WPT, h = w % WPT;
   const int g = lane >> 4, c16 = lane & 15;
-  __bf16* const R0h = lds;
-  __bf16* const R0l = lds + M * LD;
-  __bf16* const R1h = lds + 2 * M * LD;
-  __bf16* const R1l = lds + 3 * M * LD;
+  u16* const R0 = lds;
+  u16* const R1 = lds + P::NP * PL;
   const float* A = a.A + (size_t)bh * M * M;
   float* Zg = a.Z + (size_t)bh * M * M;
 
@@ -168,7 +241,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
   const bool own = t < TM;
   const int row = 16 * t + c16;  // the lane's row of X, T1, T2, Z
 
-  Frag2 Af[KS], Xf[KS], Zf[KS];
+  Frag Af[KS], Xf[KS], Zf[KS];
   f32x4 Xacc[NI], Zacc[NI], acc[NI];
   if (own) {
 #pragma unroll
@@ -176,7 +249,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = A[(size_t)row * M + 32 * ks + 8 * g + e];
-      Af[ks] = split8(x);
+      Af[ks] = P::make(x);
     }
     // Z_0 = A^T / c: Zacc[j][r] = Z_0[row][16i + 4g + r], i = h + WPT j
 #pragma unroll
@@ -184,7 +257,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
       const int i = h + WPT * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) Zacc[j][r] = A[(size_t)(16 * i + 4 * g + r) * M + row] * invc;
-      rowstore4<LD>(R0h, R0l, row, 16 * i + 4 * g, Zacc[j]);
+      rowstore4<LD, PL, F16>(R0, row, 16 * i + 4 * g, Zacc[j]);
     }
   }
   __syncthreads();
@@ -193,34 +266,34 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
     const bool last = (it == a.n_iter - 1);
     if (own) {  // step 1: X^T = Z^T A^T; Z's own rows kept for step 4
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Zf[ks] = rowfrag<LD>(R0h, R0l, row, ks);
+      for (int ks = 0; ks < KS; ++ks) Zf[ks] = rowfrag<LD, PL, F16>(R0, row, ks);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int i = h + WPT * j;
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[j] = mma<3>(colfrag<LD, false>(R0h, R0l, i, ks), Af[ks], acc[j]);
+        for (int ks = 0; ks < KS; ++ks) acc[j] = P::mma(colfrag<LD, PL, false, F16>(R0, i, ks), Af[ks], acc[j]);
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         Xacc[j] = acc[j];
-        rowstore4<LD>(R1h, R1l, row, 16 * (h + WPT * j) + 4 * g, acc[j]);
+        rowstore4<LD, PL, F16>(R1, row, 16 * (h + WPT * j) + 4 * g, acc[j]);
       }
     }
     __syncthreads();
     if (own) {  // step 2: T1^T = 7 X^T - X^T X^T
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Xf[ks] = rowfrag<LD>(R1h, R1l, row, ks);
+      for (int ks = 0; ks < KS; ++ks) Xf[ks] = rowfrag<LD, PL, F16>(R1, row, ks);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[j] = mma<3>(colfrag<LD, true>(R1h, R1l, h + WPT * j, ks), Xf[ks], acc[j]);
+          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R1, h + WPT * j, ks), Xf[ks], acc[j]);
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        rowstore4<LD>(R0h, R0l, row, 16 * (h + WPT * j) + 4 * g, 7.f * Xacc[j] - acc[j]);
+        rowstore4<LD, PL, F16>(R0, row, 16 * (h + WPT * j) + 4 * g, 7.f * Xacc[j] - acc[j]);
     }
     __syncthreads();
     if (own) {  // step 3: T2^T = 15 X^T - T1^T X^T
@@ -229,11 +302,11 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[j] = mma<3>(colfrag<LD, true>(R0h, R0l, h + WPT * j, ks), Xf[ks], acc[j]);
+          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R0, h + WPT * j, ks), Xf[ks], acc[j]);
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        rowstore4<LD>(R1h, R1l, row, 16 * (h + WPT * j) + 4 * g, 15.f * Xacc[j] - acc[j]);
+        rowstore4<LD, PL, F16>(R1, row, 16 * (h + WPT * j) + 4 * g, 15.f * Xacc[j] - acc[j]);
     }
     __syncthreads();
     if (own) {  // step 4: Z'^T = (13 Z^T - T2^T Z^T) / 4
@@ -242,7 +315,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
         acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[j] = mma<3>(colfrag<LD, true>(R1h, R1l, h + WPT * j, ks), Zf[ks], acc[j]);
+          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R1, h + WPT * j, ks), Zf[ks], acc[j]);
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) Zacc[j] = 0.25f * (13.f * Zacc[j] - acc[j]);
@@ -253,7 +326,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, __bf16* lds) {
           *reinterpret_cast<float4*>(Zg + (size_t)row * M + col) =
               make_float4(Zacc[j][0], Zacc[j][1], Zacc[j][2], Zacc[j][3]);
         else
-          rowstore4<LD>(R0h, R0l, row, col, Zacc[j]);
+          rowstore4<LD, PL, F16>(R0, row, col, Zacc[j]);
       }
     }
     __syncthreads();

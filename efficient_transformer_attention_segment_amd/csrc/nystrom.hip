@@ -66,6 +66,10 @@ struct Plan {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t ZERO_BYTES = 4096;  // zero page at offset 0 of every workspace
+// bf16 I/O: the pseudo-inverse iteration uses single fp16 products up to this
+// many iterations and split-bf16 products beyond (the iterate's sensitivity
+// to operand rounding grows with the iteration count).
+constexpr int PINV_F16_MAX_ITER = 8;
 
 int pow2floor(int x) {
   int p = 1;
@@ -244,6 +248,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.BH = p.BH;
   pa.n_iter = n_iter;
   pa.init_option = init_option;
+  pa.f16 = (sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER) ? 1 : 0;
   BvArgs ba;
   ba.k = k;
   ba.v = v;
@@ -261,7 +266,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.lscale = s4;
   size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
   if constexpr (M <= 128)
-    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M>());
+    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M, false>());
   HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
   HIP_TRY(launch("k_pinv_bv", k_pinv_bv<IO, M>, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()),
                  (uint32_t)lds2, st, pa, ba, p.npinv));
