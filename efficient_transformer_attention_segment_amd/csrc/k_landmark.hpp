@@ -37,11 +37,14 @@ struct LandmarkArgs {
   float* A;             // [BH][m][m]
   float* colmax;        // [BH]
   float* rowmax;        // [BH]
+  unsigned* sync;       // [4] cross-block maxima + arrival count, zeroed by k_landmark
 };
 
-// A = softmax(Qt Kt^T) for one head, by the 256 threads of the block.
-// M = m (multiple of 32).  csum: LDS scratch of (M/16) * M floats.
-template <int M, bool F32>
+// A = softmax(Qt Kt^T) for one head, by the NW waves of the block; writes A
+// and the head's maximum column and row sums (also returned in wred[0] and
+// wred[1] to every thread).  M = m (multiple of 32).  csum: LDS scratch of
+// (M/16) * M floats; wred: 2 * NW floats.
+template <int M, bool F32, int NW>
 __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred) {
   constexpr int TM = M / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -50,7 +53,7 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
   const float* kt = a.kt + (size_t)bh * M * HD;
   float* A = a.A + (size_t)bh * M * M;
   float rmax_w = 0.f;
-  for (int rt = wave; rt < TM; rt += 4) {
+  for (int rt = wave; rt < TM; rt += NW) {
     // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
     float ax[2][8];
 #pragma unroll
@@ -120,19 +123,28 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
   __syncthreads();
   // column sums in a fixed order, then the block maximum
   float cmax = 0.f;
-  for (int j = threadIdx.x; j < M; j += 256) {
+  for (int j = threadIdx.x; j < M; j += 64 * NW) {
     float s = 0.f;
     for (int rt = 0; rt < TM; ++rt) s += csum[rt * M + j];
     cmax = fmaxf(cmax, s);
   }
   cmax = wave_max(cmax);
+  if (lane == 0) wred[NW + wave] = cmax;
   __syncthreads();
-  if (lane == 0) wred[4 + wave] = cmax;
+  float rm = 0.f, cm = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    rm = fmaxf(rm, wred[i]);
+    cm = fmaxf(cm, wred[NW + i]);
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    a.rowmax[bh] = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    a.colmax[bh] = fmaxf(fmaxf(wred[4], wred[5]), fmaxf(wred[6], wred[7]));
+    a.rowmax[bh] = rm;
+    a.colmax[bh] = cm;
+    wred[0] = cm;
+    wred[1] = rm;
   }
+  __syncthreads();
 }
 
 // grid: (m / lpw, BH), block 256, with 8 * RS * lpw == 256.
@@ -152,6 +164,7 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   const int j = t / (TPR * RS);
   const int i = blockIdx.x * lpw + j;
   const size_t base = ((size_t)bh * a.n + (size_t)i * L) * HD + c * CW;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && t < 4) a.sync[t] = 0u;  // read by the next launch
 
   float sq[CW], sk[CW];
 #pragma unroll
@@ -216,7 +229,7 @@ template <int M, bool F32>
 __global__ __launch_bounds__(256) void k_gram(LandmarkArgs a) {
   __shared__ float csum[(M / 16) * M];
   __shared__ float wred[8];
-  landmark_gram_tail<M, F32>(a, blockIdx.x, csum, wred);
+  landmark_gram_tail<M, F32, 4>(a, blockIdx.x, csum, wred);
 }
 
 }  // namespace nys

@@ -29,6 +29,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "k_landmark.hpp"
 
 namespace nys {
 
@@ -40,7 +41,14 @@ struct PinvArgs {
   float* cscale;        // [BH] out
   int BH, n_iter, init_option;
   int f16;              // bf16 I/O: 1 = single fp16 products, 0 = split bf16
+  int fuse_gram;        // 1: each block forms its own head's A first (m <= 128)
+  int npinv;            // pseudo-inverse blocks in the launch (the rendezvous count)
+  LandmarkArgs la;      // landmarks in, A / colmax / rowmax out (fuse_gram)
 };
+
+// Bound on the rendezvous wait (about a second of polls); past it the
+// scale becomes NaN so that the result is visibly wrong instead of hanging.
+constexpr unsigned RENDEZVOUS_SPINS = 1u << 20;
 
 __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
   if (a.init_option == 0) {
@@ -54,6 +62,202 @@ __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
     return cm * rm;
   }
   return a.colmax[bh] * a.rowmax[bh];
+}
+
+// LDS use before the iteration starts (float offsets).  Qt and Kt are staged
+// at the bottom (dead once A is formed); A (row stride M + 4), the column-sum
+// scratch and the wave maxima sit above both the staging area and the
+// iteration's first region R0 (R0_BYTES), so that Z_0 can be written to R0
+// while A is still being read.
+template <int M, int R0_BYTES, int NW>
+struct ProLayout {
+  static constexpr int QLD = HD + 4, ALD = M + 4, TM = M / 16;
+  static constexpr int OFF_QT = 0, OFF_KT = M * QLD;
+  static constexpr int OFF_A = (R0_BYTES / 4 > 2 * M * QLD) ? R0_BYTES / 4 : 2 * M * QLD;
+  static constexpr int OFF_CSUM = OFF_A + M * ALD;
+  static constexpr int OFF_WRED = OFF_CSUM + TM * M;
+  static constexpr int BYTES = 4 * (OFF_WRED + 2 * NW);
+};
+
+// A = softmax(Qt Kt^T) for one head into LDS (and to global for the stage
+// hook), with the head's maximum column and row sums in wred[0], wred[1]
+// (and in colmax / rowmax).  Qt and Kt come into LDS in one coalesced pass
+// first, so the products read LDS instead of waiting on global loads.
+// float32 products for float32 I/O, split-bf16 for bf16 I/O (as k_gram).
+template <int M, bool F32, int NW, class Ly>
+__device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
+  constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  float* const Qs = L + Ly::OFF_QT;
+  float* const Ks = L + Ly::OFF_KT;
+  float* const Al = L + Ly::OFF_A;
+  float* const csum = L + Ly::OFF_CSUM;
+  float* const wred = L + Ly::OFF_WRED;
+  const float4* qt = reinterpret_cast<const float4*>(a.qt + (size_t)bh * M * HD);
+  const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
+  float* A = a.A + (size_t)bh * M * M;
+  for (int i = tid; i < M * (HD / 4); i += 64 * NW) {
+    const int row = i >> 4, c4 = i & 15;
+    const float4 x = qt[i], y = kt[i];
+    *reinterpret_cast<float4*>(Qs + row * QLD + 4 * c4) = x;
+    *reinterpret_cast<float4*>(Ks + row * QLD + 4 * c4) = y;
+  }
+  __syncthreads();
+  float rmax_w = 0.f;
+  for (int rt = wave; rt < TM; rt += NW) {
+    // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
+    float ax[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float* p = Qs + (16 * rt + c16) * QLD + 32 * ks + 8 * g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ax[ks][e] = p[e];
+    }
+    Frag2 af[2];
+    if constexpr (!F32) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) af[ks] = split8(ax[ks]);
+    }
+    f32x4 acc[TM];
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        const float* p = Ks + (16 * ct + c16) * QLD + 32 * ks + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[e];
+        if constexpr (F32)
+          acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
+        else
+          acc[ct] = mma<3>(af[ks], split8(x), acc[ct]);
+      }
+    }
+    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mx = NEG_BIG;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) mx = fmaxf(mx, acc[ct][r]);
+      mx = max16(mx);
+      float s = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        const float p = fast_exp2((acc[ct][r] - mx) * LOG2E);
+        acc[ct][r] = p;
+        s += p;
+      }
+      s = sum16(s);
+      const float inv = 1.0f / s;
+      float rs = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        acc[ct][r] *= inv;
+        rs += acc[ct][r];
+      }
+      rs = sum16(rs);
+      rmax_w = fmaxf(rmax_w, rs);
+    }
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * g + r;
+        Al[row * ALD + 16 * ct + c16] = acc[ct][r];
+        A[(size_t)row * M + 16 * ct + c16] = acc[ct][r];
+      }
+      float cs = acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3];
+      cs = sum_g(cs);
+      if (g == 0) csum[rt * M + 16 * ct + c16] = cs;
+    }
+  }
+  rmax_w = max_g(rmax_w);
+  if (lane == 0) wred[wave] = rmax_w;
+  __syncthreads();
+  // column sums in a fixed order, then the block maximum
+  float cmax = 0.f;
+  for (int j = tid; j < M; j += 64 * NW) {
+    float s = 0.f;
+    for (int rt = 0; rt < TM; ++rt) s += csum[rt * M + j];
+    cmax = fmaxf(cmax, s);
+  }
+  cmax = wave_max(cmax);
+  if (lane == 0) wred[NW + wave] = cmax;
+  __syncthreads();
+  float rm = 0.f, cm = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    rm = fmaxf(rm, wred[i]);
+    cm = fmaxf(cm, wred[NW + i]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.rowmax[bh] = rm;
+    a.colmax[bh] = cm;
+    wred[0] = cm;
+    wred[1] = rm;
+  }
+  __syncthreads();
+}
+
+// c for one head's block; on return A is in LDS at Ly::OFF_A (row stride
+// M + 4).  With fuse_gram the block forms A itself (gram_lds); otherwise it
+// copies the A of the separate Gram launch.  Option 1 needs only this head.
+// Option 0 needs the maxima over every head: the pseudo-inverse blocks are
+// the first npinv blocks of the launch (dispatched first, all resident: the
+// host fuses only while npinv is well under the CU count), and meet once:
+// each folds its two maxima into sync[0..1] with agent-scope atomic max,
+// then bumps the count sync[2] with an add whose operand depends on both max
+// results (so the maxima are in place first); each then waits for the count
+// to reach npinv and reads the maxima back with agent-scope atomic loads.
+// No fence is involved, so other blocks' writes are not flushed.
+template <int M, bool F32, int NW, class Ly>
+__device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
+  float* const wred = L + Ly::OFF_WRED;
+  if (!a.fuse_gram) {
+    const float4* A = reinterpret_cast<const float4*>(a.A + (size_t)bh * M * M);
+    for (int i = threadIdx.x; i < M * M / 4; i += 64 * NW) {
+      const int row = i / (M / 4), c4 = i % (M / 4);
+      *reinterpret_cast<float4*>(L + Ly::OFF_A + row * Ly::ALD + 4 * c4) = A[i];
+    }
+    __syncthreads();
+    return pinv_scale(a, bh);
+  }
+  gram_lds<M, F32, NW, Ly>(a.la, bh, L);
+  const float cm = wred[0], rm = wred[1];
+  if (a.init_option != 0) return cm * rm;
+  __syncthreads();  // every thread has read wred
+  if (threadIdx.x == 0) {
+    const unsigned r0 = __hip_atomic_fetch_max(a.la.sync + 0, __float_as_uint(cm), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned r1 = __hip_atomic_fetch_max(a.la.sync + 1, __float_as_uint(rm), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned inc = (r0 == 0xffffffffu && r1 == 0xffffffffu) ? 2u : 1u;  // depends on both results
+    __hip_atomic_fetch_add(a.la.sync + 2, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float c = __builtin_nanf("");
+    for (unsigned it = 0; it < RENDEZVOUS_SPINS; ++it) {
+      if (__hip_atomic_load(a.la.sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.npinv) {
+        c = __uint_as_float(__hip_atomic_load(a.la.sync + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) *
+            __uint_as_float(__hip_atomic_load(a.la.sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    wred[0] = c;
+  }
+  __syncthreads();
+  return wred[0];
+}
+
+// Z = Z_0 = A^T / c (no iterations), from A in LDS, by the whole block.
+template <int M, int ALD>
+__device__ __forceinline__ void store_z0_lds(const float* Al, float* Zg, float invc) {
+  for (int idx = threadIdx.x; idx < M * M; idx += blockDim.x) {
+    const int row = idx / M, col = idx % M;
+    Zg[idx] = Al[col * ALD + row] * invc;
+  }
 }
 
 // Waves per workgroup for m landmarks: one per 16-row tile up to 128
@@ -141,7 +345,9 @@ struct POp<true> {
 
 template <int M, bool F16>
 constexpr int pinv_lds_bytes() {
-  return 2 * POp<F16>::NP * M * (M + 8) * 2;  // two regions of NP planes, row stride M + 8
+  constexpr int iter = 2 * POp<F16>::NP * M * (M + 8) * 2;  // two regions of NP planes, row stride M + 8
+  constexpr int pro = ProLayout<M, POp<F16>::NP * M * (M + 8) * 2, nwaves<M>()>::BYTES;
+  return iter > pro ? iter : pro;
 }
 
 __device__ __forceinline__ s16x4 lds_tr_raw(const u16* p) {
@@ -192,15 +398,6 @@ __device__ __forceinline__ typename POp<F16>::Frag rowfrag(const u16* Y, int row
   return f;
 }
 
-// Z = Z_0 = A^T / c (no iterations), by the whole block.
-template <int M>
-__device__ __forceinline__ void store_z0(const float* A, float* Zg, float invc) {
-  for (int idx = threadIdx.x; idx < M * M; idx += blockDim.x) {
-    const int row = idx / M, col = idx % M;
-    Zg[idx] = A[(size_t)col * M + row] * invc;
-  }
-}
-
 // One workgroup per head; wave w works on row tile t = w / WPT, i.e. rows
 // [16t, 16t + 16) of X, T1, T2 and Z, and forms the output tiles
 // i = h, h + WPT, ... (h = w % WPT) of each product.  Every product is formed
@@ -228,14 +425,15 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   const int g = lane >> 4, c16 = lane & 15;
   u16* const R0 = lds;
   u16* const R1 = lds + P::NP * PL;
-  const float* A = a.A + (size_t)bh * M * M;
   float* Zg = a.Z + (size_t)bh * M * M;
 
-  const float c = pinv_scale(a, bh);
+  using Ly = ProLayout<M, P::NP * PL * 2, nwaves<M>()>;
+  const float c = pinv_prologue<M, false, nwaves<M>(), Ly>(a, bh, reinterpret_cast<float*>(lds));
   const float invc = 1.0f / c;
+  const float* const Al = reinterpret_cast<const float*>(lds) + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
   if (a.n_iter == 0) {
-    store_z0<M>(A, Zg, invc);
+    store_z0_lds<M, Ly::ALD>(Al, Zg, invc);
     return;
   }
   const bool own = t < TM;
@@ -248,7 +446,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = A[(size_t)row * M + 32 * ks + 8 * g + e];
+      for (int e = 0; e < 8; ++e) x[e] = Al[row * Ly::ALD + 32 * ks + 8 * g + e];
       Af[ks] = P::make(x);
     }
     // Z_0 = A^T / c: Zacc[j][r] = Z_0[row][16i + 4g + r], i = h + WPT j
@@ -256,7 +454,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     for (int j = 0; j < NI; ++j) {
       const int i = h + WPT * j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zacc[j][r] = A[(size_t)(16 * i + 4 * g + r) * M + row] * invc;
+      for (int r = 0; r < 4; ++r) Zacc[j][r] = Al[(16 * i + 4 * g + r) * Ly::ALD + row] * invc;
       rowstore4<LD, PL, F16>(R0, row, 16 * i + 4 * g, Zacc[j]);
     }
   }
@@ -347,7 +545,9 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
 
 template <int M>
 constexpr int pinv_lds_bytes_f32() {
-  return 2 * M * (M + 4) * 4;  // two float32 regions, row stride M + 4
+  constexpr int iter = 2 * M * (M + 4) * 4;  // two float32 regions, row stride M + 4
+  constexpr int pro = ProLayout<M, M * (M + 4) * 4, nwaves<M>()>::BYTES;
+  return iter > pro ? iter : pro;
 }
 
 __device__ __forceinline__ int pk(int ks, int g, int e) { return 32 * ks + (e < 4 ? 4 * g + e : 12 + 4 * g + e); }
@@ -387,14 +587,15 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   const int g = lane >> 4, c16 = lane & 15;
   float* const R0 = lds;
   float* const R1 = lds + M * LD;
-  const float* A = a.A + (size_t)bh * M * M;
   float* Zg = a.Z + (size_t)bh * M * M;
 
-  const float c = pinv_scale(a, bh);
+  using Ly = ProLayout<M, M * LD * 4, nwaves<M>()>;
+  const float c = pinv_prologue<M, true, nwaves<M>(), Ly>(a, bh, lds);
   const float invc = 1.0f / c;
+  const float* const Al = lds + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
   if (a.n_iter == 0) {
-    store_z0<M>(A, Zg, invc);
+    store_z0_lds<M, Ly::ALD>(Al, Zg, invc);
     return;
   }
   const bool own = t < TM;
@@ -407,7 +608,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   if (own) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float* p = A + (size_t)row * M + 32 * ks + 4 * g;
+      const float* p = Al + row * Ly::ALD + 32 * ks + 4 * g;
       const float4 u = *reinterpret_cast<const float4*>(p);
       const float4 v = *reinterpret_cast<const float4*>(p + 16);
       Af[ks][0] = u.x; Af[ks][1] = u.y; Af[ks][2] = u.z; Af[ks][3] = u.w;
@@ -418,7 +619,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int col = 16 * (h + WPT * j) + c16;
-      const float4 z = *reinterpret_cast<const float4*>(A + (size_t)col * M + row4);
+      const float4 z = *reinterpret_cast<const float4*>(Al + col * Ly::ALD + row4);
       Zacc[j] = f32x4{z.x * invc, z.y * invc, z.z * invc, z.w * invc};
       store_t<LD>(R0, col, row4, Zacc[j]);
     }

@@ -61,6 +61,7 @@ struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
+  size_t off_sync;
   size_t total;
 };
 
@@ -70,6 +71,10 @@ constexpr size_t ZERO_BYTES = 4096;  // zero page at offset 0 of every workspace
 // many iterations and split-bf16 products beyond (the iterate's sensitivity
 // to operand rounding grows with the iteration count).
 constexpr int PINV_F16_MAX_ITER = 8;
+// The pseudo-inverse blocks form their head's A themselves (no separate Gram
+// launch) for the exact-coefficient init, and for the original init while
+// they are few enough to be resident together for its one rendezvous.
+constexpr int FUSED_GRAM_MAX_BLOCKS = 128;
 
 int pow2floor(int x) {
   int p = 1;
@@ -105,6 +110,7 @@ Plan make_plan(int B, int H, int n, int m) {
     return at;
   };
   p.off_zero = take(ZERO_BYTES);
+  p.off_sync = take(16);
   p.off_qt = take(BH * M * D * 4);
   p.off_kt = take(BH * M * D * 4);
   p.off_qth = take(BH * M * D * 2);
@@ -235,9 +241,11 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.A = at<float>(w, p.off_A);
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
+  la.sync = at<unsigned>(w, p.off_sync);
   HIP_TRY(launch("k_landmark", k_landmark<IO, M>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
-  HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(256), 0, st, la));
+  const bool fuse_gram = M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
+  if (!fuse_gram) HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(256), 0, st, la));
 
   PinvArgs pa;
   pa.A = la.A;
@@ -249,6 +257,9 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.n_iter = n_iter;
   pa.init_option = init_option;
   pa.f16 = (sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER) ? 1 : 0;
+  pa.fuse_gram = fuse_gram ? 1 : 0;
+  pa.npinv = p.npinv;
+  pa.la = la;
   BvArgs ba;
   ba.k = k;
   ba.v = v;
@@ -266,7 +277,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.lscale = s4;
   size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
   if constexpr (M <= 128)
-    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M, false>());
+    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
+                                                  : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
   HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
   HIP_TRY(launch("k_pinv_bv", k_pinv_bv<IO, M>, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()),
                  (uint32_t)lds2, st, pa, ba, p.npinv));
