@@ -12,8 +12,8 @@
 //
 // pinv_block<M> (M <= 128, bf16 I/O): one workgroup per head, everything on
 //   chip, one or two waves per 16-row tile (see the function comment).  Two
-//   row-major LDS regions of M x (M + 8) bf16 hi/lo suffice: each step reads
-//   one and writes the other (M = 128 fits the 160 KB LDS).  Products are
+//   row-major (chunk-swizzled) LDS regions of 16-bit planes suffice: each step
+//   reads one and writes the other (M = 128 fits the 160 KB LDS).  Products are
 //   split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, relative error
 //   about 2^-16).
 //
@@ -27,6 +27,8 @@
 //   batched launches, one product per launch, with the matrices in global
 //   memory; the kernel boundaries are the step barriers.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "k_landmark.hpp"
@@ -343,10 +345,17 @@ struct POp<true> {
   }
 };
 
+// Row stride (16-bit elements) of the bf16-I/O iteration's LDS matrices: a
+// multiple of 64 elements (128 bytes), as the chunk swizzle needs.
+template <int M>
+constexpr int pinv_ld() {
+  return (M + 63) / 64 * 64;
+}
+
 template <int M, bool F16>
 constexpr int pinv_lds_bytes() {
-  constexpr int iter = 2 * POp<F16>::NP * M * (M + 8) * 2;  // two regions of NP planes, row stride M + 8
-  constexpr int pro = ProLayout<M, POp<F16>::NP * M * (M + 8) * 2, nwaves<M>()>::BYTES;
+  constexpr int iter = 2 * POp<F16>::NP * M * pinv_ld<M>() * 2;  // two regions of NP planes
+  constexpr int pro = ProLayout<M, POp<F16>::NP * M * pinv_ld<M>() * 2, nwaves<M>()>::BYTES;
   return iter > pro ? iter : pro;
 }
 
@@ -358,49 +367,64 @@ __device__ __forceinline__ s16x8 cat44(s16x4 a, s16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Matrices are row-major with the 8-byte chunk index of each row XORed with
+// 4 (row & 3) + ((row >> 2) & 3) (row stride a multiple of 128 bytes).  The
+// two access patterns of the iteration then hit 16 distinct 8-byte bank
+// slots per 16 lanes: a transposed read (4 consecutive rows x 4 consecutive
+// chunks, both aligned to 4) and a row read or store (16 consecutive rows,
+// one chunk).  Within a row the map is a bijection.
+__device__ __forceinline__ int pswz(int row, int chunk) {
+  return 4 * (chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)));
+}
+
 // A operand rows i*16 .. i*16+15 of Y^T (= columns of Y) for one 32-wide k
-// step, read from row-major Y (row stride LD, planes PL apart) with two
-// transposed reads per plane.  PAIRED selects the paired k order
-// (k = 4g + e, 16 + 4g + e - 4), otherwise the standard one (k = 8g + e).
+// step, read from Y (row stride LD, planes PL apart) with two transposed
+// reads per plane.  PAIRED selects the paired k order (k = 4g + e,
+// 16 + 4g + e - 4), otherwise the standard one (k = 8g + e).
 template <int LD, int PL, bool PAIRED, bool F16>
 __device__ __forceinline__ typename POp<F16>::Frag colfrag(const u16* Y, int i, int ks) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int k0 = 32 * ks + (PAIRED ? 4 * g : 8 * g) + (c16 >> 2);
   const int k1 = k0 + (PAIRED ? 16 : 4);
-  const int col = 16 * i + 4 * (c16 & 3);
+  const int ch = 4 * i + (c16 & 3);
+  const int a0 = k0 * LD + pswz(k0, ch), a1 = k1 * LD + pswz(k1, ch);
   typename POp<F16>::Frag f;
 #pragma unroll
   for (int p = 0; p < POp<F16>::NP; ++p)
-    POp<F16>::set(f, p, cat44(lds_tr_raw(Y + p * PL + k0 * LD + col), lds_tr_raw(Y + p * PL + k1 * LD + col)));
+    POp<F16>::set(f, p, cat44(lds_tr_raw(Y + p * PL + a0), lds_tr_raw(Y + p * PL + a1)));
   return f;
 }
 
-// Store this lane's 4 consecutive elements Y[row][col .. col+3].
+// Store this lane's 4 consecutive elements Y[row][col .. col+3] (col % 4 == 0).
 template <int LD, int PL, bool F16>
 __device__ __forceinline__ void rowstore4(u16* Y, int row, int col, const f32x4 v) {
   s16x4 w[POp<F16>::NP];
   POp<F16>::enc4(v, w);
+  const int a = row * LD + pswz(row, col >> 2);
 #pragma unroll
-  for (int p = 0; p < POp<F16>::NP; ++p) *reinterpret_cast<s16x4*>(Y + p * PL + row * LD + col) = w[p];
+  for (int p = 0; p < POp<F16>::NP; ++p) *reinterpret_cast<s16x4*>(Y + p * PL + a) = w[p];
 }
 
-// B operand for the paired k step ks of row `row` of a row-major LDS
-// matrix: elements k = 32ks + 4g + e and 32ks + 16 + 4g + (e - 4).
+// B operand for the paired k step ks of row `row` of an LDS matrix:
+// elements k = 32ks + 4g + e and 32ks + 16 + 4g + (e - 4).
 template <int LD, int PL, bool F16>
 __device__ __forceinline__ typename POp<F16>::Frag rowfrag(const u16* Y, int row, int ks) {
   const int g = (threadIdx.x & 63) >> 4;
-  const int k0 = row * LD + 32 * ks + 4 * g;
+  const int a0 = row * LD + pswz(row, 8 * ks + g), a1 = row * LD + pswz(row, 8 * ks + 4 + g);
   typename POp<F16>::Frag f;
 #pragma unroll
   for (int p = 0; p < POp<F16>::NP; ++p)
-    POp<F16>::set(f, p, cat44(*reinterpret_cast<const s16x4*>(Y + p * PL + k0),
-                              *reinterpret_cast<const s16x4*>(Y + p * PL + k0 + 16)));
+    POp<F16>::set(f, p, cat44(*reinterpret_cast<const s16x4*>(Y + p * PL + a0),
+                              *reinterpret_cast<const s16x4*>(Y + p * PL + a1)));
   return f;
 }
 
-// One workgroup per head; wave w works on row tile t = w / WPT, i.e. rows
-// [16t, 16t + 16) of X, T1, T2 and Z, and forms the output tiles
-// i = h, h + WPT, ... (h = w % WPT) of each product.  Every product is formed
+// One workgroup per head.  Wave w = (t, h) works on row group t: row tiles
+// RT t .. RT t + RT - 1 (rows of X, T1, T2 and Z), and forms the output
+// column tiles i = h, h + WPG, ... of each product for all of them, so every
+// left-operand fragment it reads from LDS feeds RT products (RT = 2 for the
+// fp16 encoding at m = 128, which halves the LDS traffic of the step; the
+// split encoding keeps RT = 1 for registers).  Every product is formed
 // transposed, Y^T[:, own rows] = (left)^T (own rows of the right factor)^T,
 // so its C tile gives the lane 4 consecutive elements of one of its rows:
 //   step 1  X^T  = Z^T A^T                      (Z read from LDS)
@@ -409,19 +433,26 @@ __device__ __forceinline__ typename POp<F16>::Frag rowfrag(const u16* Y, int row
 //   step 4  Z'^T = (13 Z^T - T2^T Z^T) / 4      (T2 from LDS)
 // which is Z' = Z (13I - X(15I - X(7I - X))) / 4 with X = A Z, expanded.
 // The left operands come from LDS by transposed reads; the right operands
-// are the tile's own rows (A from registers, X and Z re-read from the LDS
+// are the wave's own rows (A from registers, X and Z re-read from the LDS
 // copy after each barrier); X and Z also stay in float32 for the 7X, 15X
 // and 13Z terms.  LDS holds the matrix each step reads whole, row-major,
 // alternating between two regions.
 template <int M, bool F16>
+constexpr int pinv_rt() {
+  return (M == 128 && F16) ? 2 : 1;
+}
+
+template <int M, bool F16>
 __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   typedef POp<F16> P;
   typedef typename P::Frag Frag;
-  constexpr int TM = M / 16, KS = M / 32, LD = M + 8, PL = M * LD;
-  constexpr int WPT = pinv_wpt<M>();
-  constexpr int NI = TM / WPT;  // output tiles per wave
+  constexpr int TM = M / 16, KS = M / 32, LD = pinv_ld<M>(), PL = M * LD;
+  constexpr int RT = pinv_rt<M, F16>();
+  constexpr int WPG = RT == 2 ? 2 : pinv_wpt<M>();  // waves per row group
+  constexpr int CT = TM / WPG;                       // output column tiles per wave
+  static_assert((TM / RT) * WPG <= nwaves<M>(), "row groups exceed the block");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int t = w / WPT, h = w % WPT;
+  const int t = w / WPG, h = w % WPG;
   const int g = lane >> 4, c16 = lane & 15;
   u16* const R0 = lds;
   u16* const R1 = lds + P::NP * PL;
@@ -436,96 +467,107 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     store_z0_lds<M, Ly::ALD>(Al, Zg, invc);
     return;
   }
-  const bool own = t < TM;
-  const int row = 16 * t + c16;  // the lane's row of X, T1, T2, Z
+  const bool own = t < TM / RT;
+  int rows[RT];  // the lane's rows of X, T1, T2, Z, one per row tile
+#pragma unroll
+  for (int r = 0; r < RT; ++r) rows[r] = 16 * (RT * t + r) + c16;
 
-  Frag Af[KS], Xf[KS], Zf[KS];
-  f32x4 Xacc[NI], Zacc[NI], acc[NI];
+  Frag Af[RT][KS], Xf[RT][KS], Zf[RT][KS];
+  f32x4 Xacc[RT][CT], Zacc[RT][CT], acc[RT][CT];
   if (own) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float x[8];
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = Al[row * Ly::ALD + 32 * ks + 8 * g + e];
-      Af[ks] = P::make(x);
-    }
-    // Z_0 = A^T / c: Zacc[j][r] = Z_0[row][16i + 4g + r], i = h + WPT j
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int i = h + WPT * j;
+        for (int e = 0; e < 8; ++e) x[e] = Al[rows[r] * Ly::ALD + 32 * ks + 8 * g + e];
+        Af[r][ks] = P::make(x);
+      }
+    // Z_0 = A^T / c: Zacc[r][j][q] = Z_0[rows[r]][16i + 4g + q], i = h + WPG j
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zacc[j][r] = Al[(16 * i + 4 * g + r) * Ly::ALD + row] * invc;
-      rowstore4<LD, PL, F16>(R0, row, 16 * i + 4 * g, Zacc[j]);
-    }
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const int i = h + WPG * j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Zacc[r][j][q] = Al[(16 * i + 4 * g + q) * Ly::ALD + rows[r]] * invc;
+        rowstore4<LD, PL, F16>(R0, rows[r], 16 * i + 4 * g, Zacc[r][j]);
+      }
   }
   __syncthreads();
+
+  // acc[r][j] = (left^T column tile i) x Rf[r]: PAIRED selects the k order
+  // of the left operand to match Rf
+  auto product = [&](const u16* Lsrc, const Frag (&Rf)[RT][KS], auto paired) {
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const Frag lf = colfrag<LD, PL, decltype(paired)::value, F16>(Lsrc, h + WPG * j, ks);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r][j] = P::mma(lf, Rf[r][ks], acc[r][j]);
+      }
+    }
+  };
+  using Std = std::integral_constant<bool, false>;
+  using Pair = std::integral_constant<bool, true>;
 
   for (int it = 0; it < a.n_iter; ++it) {
     const bool last = (it == a.n_iter - 1);
     if (own) {  // step 1: X^T = Z^T A^T; Z's own rows kept for step 4
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Zf[ks] = rowfrag<LD, PL, F16>(R0, row, ks);
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int i = h + WPT * j;
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) Zf[r][ks] = rowfrag<LD, PL, F16>(R0, rows[r], ks);
+      product(R0, Af, Std{});
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[j] = P::mma(colfrag<LD, PL, false, F16>(R0, i, ks), Af[ks], acc[j]);
-      }
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        Xacc[j] = acc[j];
-        rowstore4<LD, PL, F16>(R1, row, 16 * (h + WPT * j) + 4 * g, acc[j]);
-      }
+        for (int j = 0; j < CT; ++j) {
+          Xacc[r][j] = acc[r][j];
+          rowstore4<LD, PL, F16>(R1, rows[r], 16 * (h + WPG * j) + 4 * g, acc[r][j]);
+        }
     }
     __syncthreads();
     if (own) {  // step 2: T1^T = 7 X^T - X^T X^T
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Xf[ks] = rowfrag<LD, PL, F16>(R1, row, ks);
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) Xf[r][ks] = rowfrag<LD, PL, F16>(R1, rows[r], ks);
+      product(R1, Xf, Pair{});
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R1, h + WPT * j, ks), Xf[ks], acc[j]);
-      }
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        rowstore4<LD, PL, F16>(R0, row, 16 * (h + WPT * j) + 4 * g, 7.f * Xacc[j] - acc[j]);
+        for (int j = 0; j < CT; ++j)
+          rowstore4<LD, PL, F16>(R0, rows[r], 16 * (h + WPG * j) + 4 * g, 7.f * Xacc[r][j] - acc[r][j]);
     }
     __syncthreads();
     if (own) {  // step 3: T2^T = 15 X^T - T1^T X^T
+      product(R0, Xf, Pair{});
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R0, h + WPT * j, ks), Xf[ks], acc[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        rowstore4<LD, PL, F16>(R1, row, 16 * (h + WPT * j) + 4 * g, 15.f * Xacc[j] - acc[j]);
+        for (int j = 0; j < CT; ++j)
+          rowstore4<LD, PL, F16>(R1, rows[r], 16 * (h + WPG * j) + 4 * g, 15.f * Xacc[r][j] - acc[r][j]);
     }
     __syncthreads();
     if (own) {  // step 4: Z'^T = (13 Z^T - T2^T Z^T) / 4
+      product(R1, Zf, Pair{});
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[j] = P::mma(colfrag<LD, PL, true, F16>(R1, h + WPT * j, ks), Zf[ks], acc[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < NI; ++j) Zacc[j] = 0.25f * (13.f * Zacc[j] - acc[j]);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int col = 16 * (h + WPT * j) + 4 * g;
-        if (last)
-          *reinterpret_cast<float4*>(Zg + (size_t)row * M + col) =
-              make_float4(Zacc[j][0], Zacc[j][1], Zacc[j][2], Zacc[j][3]);
-        else
-          rowstore4<LD, PL, F16>(R0, row, col, Zacc[j]);
-      }
+        for (int j = 0; j < CT; ++j) {
+          Zacc[r][j] = 0.25f * (13.f * Zacc[r][j] - acc[r][j]);
+          const int col = 16 * (h + WPG * j) + 4 * g;
+          if (last)
+            *reinterpret_cast<float4*>(Zg + (size_t)rows[r] * M + col) =
+                make_float4(Zacc[r][j][0], Zacc[r][j][1], Zacc[r][j][2], Zacc[r][j][3]);
+          else
+            rowstore4<LD, PL, F16>(R0, rows[r], col, Zacc[r][j]);
+        }
     }
     __syncthreads();
   }
