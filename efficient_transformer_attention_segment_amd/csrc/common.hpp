@@ -92,19 +92,30 @@ __device__ __forceinline__ u16 f32_to_bf16u(float x) { return __builtin_bit_cast
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum / max across the 16 lanes that share l / 16 (xor over lane bits 0..3).
+// Sum / max across the 16 lanes of a row (lanes sharing l / 16) with DPP
+// lane permutes (VALU, no LDS crossbar round trip): quad_perm [1,0,3,2] and
+// [2,3,0,1] combine each quad, row_half_mirror pairs the two quads of each
+// half row, row_mirror the two halves.  Every step adds two values that the
+// partner lane adds in the other order, so all 16 lanes end with the same
+// bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_QUAD_1032 = 0xb1, DPP_QUAD_2301 = 0x4e, DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
+
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp<DPP_QUAD_1032>(v);
+  v += dpp<DPP_QUAD_2301>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
   return v;
 }
 __device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
   return v;
 }
 // Sum / max across the four lanes l, l^16, l^32, l^48 (the g groups), with

@@ -74,8 +74,10 @@ __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
 template <int M, int R0_BYTES, int NW>
 struct ProLayout {
   static constexpr int QLD = HD + 4, ALD = M + 4, TM = M / 16;
-  static constexpr int OFF_QT = 0, OFF_KT = M * QLD;
-  static constexpr int OFF_A = (R0_BYTES / 4 > 2 * M * QLD) ? R0_BYTES / 4 : 2 * M * QLD;
+  static constexpr int OFF_QT = 0, OFF_KT = M * QLD;  // float32 staging (float32 I/O)
+  static constexpr int BLD = HD + 8;                  // bf16 hi/lo staging row stride (bf16 I/O)
+  static constexpr int STAGE = (2 * M * QLD > 2 * M * BLD) ? 2 * M * QLD : 2 * M * BLD;  // floats
+  static constexpr int OFF_A = (R0_BYTES / 4 > STAGE) ? R0_BYTES / 4 : STAGE;
   static constexpr int OFF_CSUM = OFF_A + M * ALD;
   static constexpr int OFF_WRED = OFF_CSUM + TM * M;
   static constexpr int BYTES = 4 * (OFF_WRED + 2 * NW);
@@ -83,43 +85,59 @@ struct ProLayout {
 
 // A = softmax(Qt Kt^T) for one head into LDS (and to global for the stage
 // hook), with the head's maximum column and row sums in wred[0], wred[1]
-// (and in colmax / rowmax).  Qt and Kt come into LDS in one coalesced pass
-// first, so the products read LDS instead of waiting on global loads.
-// float32 products for float32 I/O, split-bf16 for bf16 I/O (as k_gram).
+// (and in colmax / rowmax).  The landmarks come into LDS in one coalesced
+// pass first, so the products read LDS instead of waiting on global loads:
+// float32 Qt, Kt for float32 I/O (float32 products), and for bf16 I/O the
+// bf16 hi / lo planes the landmark kernel already wrote (split-bf16
+// products with no conversion work here).
 template <int M, bool F32, int NW, class Ly>
 __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
-  constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD;
+  constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD, BLD = Ly::BLD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   float* const Qs = L + Ly::OFF_QT;
   float* const Ks = L + Ly::OFF_KT;
+  __bf16* const Bs = reinterpret_cast<__bf16*>(L);  // planes qt_hi, qt_lo, kt_hi, kt_lo, M x BLD each
   float* const Al = L + Ly::OFF_A;
   float* const csum = L + Ly::OFF_CSUM;
   float* const wred = L + Ly::OFF_WRED;
-  const float4* qt = reinterpret_cast<const float4*>(a.qt + (size_t)bh * M * HD);
-  const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
   float* A = a.A + (size_t)bh * M * M;
-  for (int i = tid; i < M * (HD / 4); i += 64 * NW) {
-    const int row = i >> 4, c4 = i & 15;
-    const float4 x = qt[i], y = kt[i];
-    *reinterpret_cast<float4*>(Qs + row * QLD + 4 * c4) = x;
-    *reinterpret_cast<float4*>(Ks + row * QLD + 4 * c4) = y;
+  if constexpr (F32) {
+    const float4* qt = reinterpret_cast<const float4*>(a.qt + (size_t)bh * M * HD);
+    const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
+    for (int i = tid; i < M * (HD / 4); i += 64 * NW) {
+      const int row = i >> 4, c4 = i & 15;
+      const float4 x = qt[i], y = kt[i];
+      *reinterpret_cast<float4*>(Qs + row * QLD + 4 * c4) = x;
+      *reinterpret_cast<float4*>(Ks + row * QLD + 4 * c4) = y;
+    }
+  } else {
+    const __bf16* src[4] = {a.qt_hi, a.qt_lo, a.kt_hi, a.kt_lo};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint4* s4 = reinterpret_cast<const uint4*>(src[p] + (size_t)bh * M * HD);
+      for (int i = tid; i < M * (HD / 8); i += 64 * NW) {
+        const int row = i >> 3, c8 = i & 7;
+        *reinterpret_cast<uint4*>(Bs + (p * M + row) * BLD + 8 * c8) = s4[i];
+      }
+    }
   }
   __syncthreads();
   float rmax_w = 0.f;
   for (int rt = wave; rt < TM; rt += NW) {
     // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
     float ax[2][8];
+    Frag2 af[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const float* p = Qs + (16 * rt + c16) * QLD + 32 * ks + 8 * g;
+      const int row = 16 * rt + c16, col = 32 * ks + 8 * g;
+      if constexpr (F32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ax[ks][e] = p[e];
-    }
-    Frag2 af[2];
-    if constexpr (!F32) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) af[ks] = split8(ax[ks]);
+        for (int e = 0; e < 8; ++e) ax[ks][e] = Qs[row * QLD + col + e];
+      } else {
+        af[ks].hi = *reinterpret_cast<const bf16x8*>(Bs + row * BLD + col);
+        af[ks].lo = *reinterpret_cast<const bf16x8*>(Bs + (M + row) * BLD + col);
+      }
     }
     f32x4 acc[TM];
 #pragma unroll
@@ -127,15 +145,22 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
       acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-        const float* p = Ks + (16 * ct + c16) * QLD + 32 * ks + 8 * g;
+        const int row = 16 * ct + c16, col = 32 * ks + 8 * g;
+        if constexpr (F32) {
+          float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[e];
-        if constexpr (F32)
+          for (int e = 0; e < 8; ++e) x[e] = Ks[row * QLD + col + e];
           acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
-        else
-          acc[ct] = mma<3>(af[ks], split8(x), acc[ct]);
+        } else {
+          Frag2 bf;
+          bf.hi = *reinterpret_cast<const bf16x8*>(Bs + (2 * M + row) * BLD + col);
+          bf.lo = *reinterpret_cast<const bf16x8*>(Bs + (3 * M + row) * BLD + col);
+          acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+        }
       }
+      // keep the next tile's operand reads from being hoisted above this
+      // tile (all of them at once would not fit the register budget)
+      asm volatile("" ::: "memory");
     }
     // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
 #pragma unroll
@@ -345,11 +370,11 @@ struct POp<true> {
   }
 };
 
-// Row stride (16-bit elements) of the bf16-I/O iteration's LDS matrices: a
-// multiple of 64 elements (128 bytes), as the chunk swizzle needs.
+// Row stride (16-bit elements) of the bf16-I/O iteration's LDS matrices (see
+// pswz).
 template <int M>
 constexpr int pinv_ld() {
-  return (M + 63) / 64 * 64;
+  return M + 16;
 }
 
 template <int M, bool F16>
@@ -367,14 +392,17 @@ __device__ __forceinline__ s16x8 cat44(s16x4 a, s16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Matrices are row-major with the 8-byte chunk index of each row XORed with
-// 4 (row & 3) + ((row >> 2) & 3) (row stride a multiple of 128 bytes).  The
-// two access patterns of the iteration then hit 16 distinct 8-byte bank
-// slots per 16 lanes: a transposed read (4 consecutive rows x 4 consecutive
-// chunks, both aligned to 4) and a row read or store (16 consecutive rows,
-// one chunk).  Within a row the map is a bijection.
+// Matrices are row-major with row stride M + 16 elements (4 or 12 8-byte
+// chunks past a multiple of 16) and the low two bits of each row's 8-byte
+// chunk index XORed with (row >> 2) & 3.  The two access patterns of the
+// iteration then hit 16 distinct 8-byte bank slots per 16 lanes: a
+// transposed read (4 consecutive rows, aligned to 4, x 4 consecutive chunks,
+// aligned to 4: the stride separates the rows) and a row read or store (16
+// consecutive rows, one chunk: the stride separates row & 3, the XOR
+// row >> 2).  Because only the low chunk bits are permuted, the tile and k
+// step parts of every address stay plain additive offsets.
 __device__ __forceinline__ int pswz(int row, int chunk) {
-  return 4 * (chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)));
+  return 4 * (chunk ^ ((row >> 2) & 3));
 }
 
 // A operand rows i*16 .. i*16+15 of Y^T (= columns of Y) for one 32-wide k
@@ -384,10 +412,13 @@ __device__ __forceinline__ int pswz(int row, int chunk) {
 template <int LD, int PL, bool PAIRED, bool F16>
 __device__ __forceinline__ typename POp<F16>::Frag colfrag(const u16* Y, int i, int ks) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-  const int k0 = 32 * ks + (PAIRED ? 4 * g : 8 * g) + (c16 >> 2);
-  const int k1 = k0 + (PAIRED ? 16 : 4);
-  const int ch = 4 * i + (c16 & 3);
-  const int a0 = k0 * LD + pswz(k0, ch), a1 = k1 * LD + pswz(k1, ch);
+  // rows k0 = 32 ks + r0 and k1 = k0 + (PAIRED ? 16 : 4); chunk 4 i + (c16 & 3).
+  // (k >> 2) & 3 does not depend on ks, so pswz is written out as a lane
+  // part plus the additive 32 ks LD + 16 i (immediate offsets).
+  const int r0 = (PAIRED ? 4 * g : 8 * g) + (c16 >> 2);
+  const int r1 = r0 + (PAIRED ? 16 : 4);
+  const int a0 = r0 * LD + 4 * ((c16 & 3) ^ ((r0 >> 2) & 3)) + 32 * ks * LD + 16 * i;
+  const int a1 = r1 * LD + 4 * ((c16 & 3) ^ ((r1 >> 2) & 3)) + 32 * ks * LD + 16 * i;
   typename POp<F16>::Frag f;
 #pragma unroll
   for (int p = 0; p < POp<F16>::NP; ++p)
@@ -400,7 +431,7 @@ template <int LD, int PL, bool F16>
 __device__ __forceinline__ void rowstore4(u16* Y, int row, int col, const f32x4 v) {
   s16x4 w[POp<F16>::NP];
   POp<F16>::enc4(v, w);
-  const int a = row * LD + pswz(row, col >> 2);
+  const int a = row * LD + 4 * (((col >> 2) & 3) ^ ((row >> 2) & 3)) + (col & ~15);  // = row LD + pswz(row, col / 4)
 #pragma unroll
   for (int p = 0; p < POp<F16>::NP; ++p) *reinterpret_cast<s16x4*>(Y + p * PL + a) = w[p];
 }
@@ -410,7 +441,8 @@ __device__ __forceinline__ void rowstore4(u16* Y, int row, int col, const f32x4 
 template <int LD, int PL, bool F16>
 __device__ __forceinline__ typename POp<F16>::Frag rowfrag(const u16* Y, int row, int ks) {
   const int g = (threadIdx.x & 63) >> 4;
-  const int a0 = row * LD + pswz(row, 8 * ks + g), a1 = row * LD + pswz(row, 8 * ks + 4 + g);
+  const int base = row * LD + 4 * (g ^ ((row >> 2) & 3));  // chunks 8 ks + g and 8 ks + 4 + g
+  const int a0 = base + 32 * ks, a1 = base + 32 * ks + 16;
   typename POp<F16>::Frag f;
 #pragma unroll
   for (int p = 0; p < POp<F16>::NP; ++p)
@@ -474,6 +506,22 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
 
   Frag Af[RT][KS], Xf[RT][KS], Zf[RT][KS];
   f32x4 Xacc[RT][CT], Zacc[RT][CT], acc[RT][CT];
+  // With one wave per row group (WPG == 1) the wave's C tiles hold all of its
+  // own rows: tiles 2 ks and 2 ks + 1 are exactly the paired-order elements
+  // of k step ks, so the own-row operands are encoded from the float32
+  // accumulators (the same values the LDS copy was encoded from) instead of
+  // being kept in registers or read back.
+  auto own_frags = [&](const f32x4 (&src)[RT][CT], Frag (&dst)[RT][KS]) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float x[8] = {src[r][2 * ks][0],     src[r][2 * ks][1],     src[r][2 * ks][2],
+                            src[r][2 * ks][3],     src[r][2 * ks + 1][0], src[r][2 * ks + 1][1],
+                            src[r][2 * ks + 1][2], src[r][2 * ks + 1][3]};
+        dst[r][ks] = P::make(x);
+      }
+  };
   if (own) {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -518,10 +566,12 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   for (int it = 0; it < a.n_iter; ++it) {
     const bool last = (it == a.n_iter - 1);
     if (own) {  // step 1: X^T = Z^T A^T; Z's own rows kept for step 4
+      if constexpr (WPG > 1) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Zf[r][ks] = rowfrag<LD, PL, F16>(R0, rows[r], ks);
+          for (int ks = 0; ks < KS; ++ks) Zf[r][ks] = rowfrag<LD, PL, F16>(R0, rows[r], ks);
+      }
       product(R0, Af, Std{});
 #pragma unroll
       for (int r = 0; r < RT; ++r)
@@ -533,10 +583,14 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     }
     __syncthreads();
     if (own) {  // step 2: T1^T = 7 X^T - X^T X^T
+      if constexpr (WPG > 1) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Xf[r][ks] = rowfrag<LD, PL, F16>(R1, rows[r], ks);
+          for (int ks = 0; ks < KS; ++ks) Xf[r][ks] = rowfrag<LD, PL, F16>(R1, rows[r], ks);
+      } else {
+        own_frags(Xacc, Xf);
+      }
       product(R1, Xf, Pair{});
 #pragma unroll
       for (int r = 0; r < RT; ++r)
@@ -546,6 +600,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     }
     __syncthreads();
     if (own) {  // step 3: T2^T = 15 X^T - T1^T X^T
+      if constexpr (WPG == 1) own_frags(Xacc, Xf);
       product(R0, Xf, Pair{});
 #pragma unroll
       for (int r = 0; r < RT; ++r)
@@ -555,6 +610,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     }
     __syncthreads();
     if (own) {  // step 4: Z'^T = (13 Z^T - T2^T Z^T) / 4
+      if constexpr (WPG == 1) own_frags(Zacc, Zf);
       product(R1, Zf, Pair{});
 #pragma unroll
       for (int r = 0; r < RT; ++r)
