@@ -61,7 +61,7 @@ struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
-  size_t off_sync;
+  size_t off_sync, off_junk;
   size_t total;
 };
 
@@ -111,6 +111,7 @@ Plan make_plan(int B, int H, int n, int m) {
   };
   p.off_zero = take(ZERO_BYTES);
   p.off_sync = take(16);
+  p.off_junk = take(16 * HD * 2);  // output rows of tiles past a workgroup's range
   p.off_qt = take(BH * M * D * 4);
   p.off_kt = take(BH * M * D * 4);
   p.off_qth = take(BH * M * D * 2);
@@ -332,9 +333,26 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.n = p.n;
   oa.H = p.H;
   oa.lscale = s4;
-  const size_t lds4 = sizeof(IO) == 2 ? (size_t)OutLayoutDMA<M>::LDS_BYTES : (size_t)OutLayout<IO, M>::LDS_BYTES;
-  HIP_TRY(allow_lds(k_out<IO, M>, lds4));
-  HIP_TRY(launch("k_out", k_out<IO, M>, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
+  if constexpr (sizeof(IO) == 2) {
+    // persistent output pass: a token range of one head per workgroup, sized
+    // so the grid fills the CUs at the occupancy its LDS allows
+    // persistent workgroups: at most one resident round (a second, partial
+    // round would cost a whole workgroup lifetime)
+    constexpr size_t lds4 = OutStreamLayout<M>::LDS_BYTES;
+    constexpr int per_cu = std::min<int>(4, (int)(160 * 1024 / lds4));
+    const int slots = 256 * per_cu;
+    const int want = std::max(1, slots / p.BH);  // workgroups per head
+    const int R = OUTS_UNIT * ((p.n + want * OUTS_UNIT - 1) / (want * OUTS_UNIT));
+    const int nbh = (p.n + R - 1) / R;
+    if (conv_w != nullptr)
+      HIP_TRY(launch("k_out", k_out_stream<M, true>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
+    else
+      HIP_TRY(launch("k_out", k_out_stream<M, false>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
+  } else {
+    const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
+    HIP_TRY(allow_lds(k_out<IO, M>, lds4));
+    HIP_TRY(launch("k_out", k_out<IO, M>, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
+  }
   return NYS_OK;
 }
 
