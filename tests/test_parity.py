@@ -75,6 +75,16 @@ def test_landmark_counts(dtype, m, n):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_many_heads(dtype):
+    """More (batch, head) pairs than the fused Gram rendezvous allows (the
+    original init then takes the separate Gram launch), ragged masks, both
+    inits."""
+    x = make_custom(3, 48, 128, 64, seed=760, dtype=dtype, lengths=[128, 70, 1])
+    _check("heads144-init0", x, dtype, 32, 6, 0)
+    _check("heads144-init1", x, dtype, 32, 6, 1)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("n_iter", [0, 1, 2, 12])
 def test_iteration_counts(dtype, n_iter):
     x = make_custom(2, 2, 512, 64, seed=800 + n_iter, dtype=dtype, lengths=[512, 300])
