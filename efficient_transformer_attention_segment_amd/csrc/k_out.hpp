@@ -286,38 +286,34 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
 // bf16 I/O: persistent, pipelined output pass.  A workgroup owns a
 // contiguous token range of one head and walks it in units of 64 tokens (one
 // 16-token tile per wave).  The key landmarks, the W^T fragments and the
-// conv taps are loaded once per workgroup.  V streams through a ring of six
-// 64-row groups in LDS: during unit u the workgroup loads group u / 64 + 4
-// into registers and writes the group loaded one unit earlier into its slot,
-// two units before its first use; each unit's Q rows load into registers one
-// unit ahead.  Only ordinary loads feed the loop (the ring is not filled by
-// LDS DMA), so the compiler's waits track exactly the registers each step
-// needs and the output stores stay in flight across units.
+// conv taps are loaded once per workgroup.  V streams through a ring of four
+// 64-row groups in LDS (absolute token row r at ring row r & 255): during
+// unit u the workgroup writes group u / 64 + 2 (loaded into registers during
+// the previous unit) into the slot that unit last read, and loads group
+// u / 64 + 3; each unit's Q rows load into registers two units ahead.  Only
+// ordinary loads feed the loop, so the compiler's waits track exactly the
+// registers each step needs and the output stores stay in flight across
+// units.  48 KB of LDS at m = 64 lets three workgroups share a CU.
 //
-// Ring layout: absolute token row r sits at slot (r / 64) mod 6, row r mod 64,
-// with its 16-byte chunk c at chunk position c ^ (2 (r & 3)), so the four rows
-// of one transposed conv read fall on different bank halves.
+// Ring layout: row r has its 16-byte chunk c at chunk position c ^ (2 (r & 3)),
+// so the four rows of one transposed conv read fall on different bank halves.
+// Each lane's conv reads sit at a fixed row offset from the unit's first token,
+// so their addresses are a per-unit row term plus per-lane constants.
 
-constexpr int OUTS_UNIT = 64;  // tokens per unit (and rows per ring group)
-constexpr int OUTS_SLOTS = 6;  // groups resident: 3 read, 1 written last unit, 1 written now, 1 free
+constexpr int OUTS_UNIT = 64;   // tokens per unit (and rows per ring group)
+constexpr int OUTS_RING = 256;  // ring rows (4 groups)
 
 template <int M>
 struct OutStreamLayout {
   static constexpr int KS = M / 32;
   static constexpr int KT_ELEMS = M * HD;
   static constexpr int WF_ELEMS = 4 * KS * 64 * 8;
-  static constexpr int RING_ELEMS = OUTS_SLOTS * OUTS_UNIT * HD;
+  static constexpr int RING_ELEMS = OUTS_RING * HD;
   static constexpr int LDS_BYTES = 2 * (KT_ELEMS + WF_ELEMS + RING_ELEMS);
 };
 
-__device__ __forceinline__ int vring_row(int r) {
-  const int grp = r >> 6;  // floor division (r may be negative)
-  int slot = grp % OUTS_SLOTS;
-  if (slot < 0) slot += OUTS_SLOTS;
-  return slot * OUTS_UNIT + (r & (OUTS_UNIT - 1));
-}
 __device__ __forceinline__ int vring_pos(int r, int chunk) {
-  return vring_row(r) * HD + 8 * (chunk ^ (2 * (r & 3)));
+  return (r & (OUTS_RING - 1)) * HD + 8 * (chunk ^ (2 * (r & 3)));
 }
 
 // One group in flight through registers: thread t holds 32 bytes of row
@@ -344,18 +340,42 @@ __device__ __forceinline__ void vgroup_store(const VGroup& b, int G, __bf16* rin
     *reinterpret_cast<uint4*>(ring + vring_pos(r, 2 * (t & 3) + c)) = b.x[c];
 }
 
-// Convolution of the 16-token tile starting at ts from the ring (window rows
-// ts - 32 .. ts + 63 in three 32-row steps; taps beyond the 80 needed are 0).
-__device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int ts, const Frag2 (&tap)[3], f32x4 (&oacc)[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+// Per-lane constants of the conv reads of the wave's tile: read (kk, half, dt)
+// of the unit starting at token t0 is at ring row (t0 + rel[kk][half]) & 255,
+// element offset coff[kk][half][dt] within that row.
+struct ConvLane {
+  int rel[3][2];
+  int coff[3][2][4];
+};
+__device__ __forceinline__ void conv_lane_init(ConvLane& cl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rel = 16 * wave - HALO + 32 * kk + 8 * g + (c16 >> 2) + 4 * half;
+      cl.rel[kk][half] = rel;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c0 = dmap_run<true>(dt, c16 & 3);
+        cl.coff[kk][half][dt] = 8 * ((c0 >> 3) ^ (2 * (rel & 3))) + (c0 & 7);  // rel & 3 == row & 3
+      }
+    }
+}
+
+// Convolution of the wave's 16-token tile of the unit starting at t0 from
+// the ring (window rows ts - 32 .. ts + 63 in three 32-row steps; taps beyond
+// the 80 needed are 0).
+__device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int t0, const ConvLane& cl, const Frag2 (&tap)[3],
+                                               f32x4 (&oacc)[4]) {
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    const int r0 = ts - HALO + 32 * kk + 8 * g + (c16 >> 2);
+    const __bf16* r0 = ring + ((t0 + cl.rel[kk][0]) & (OUTS_RING - 1)) * HD;
+    const __bf16* r1 = ring + ((t0 + cl.rel[kk][1]) & (OUTS_RING - 1)) * HD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int c0 = dmap_run<true>(dt, c16 & 3);
-      const bf16x4 x0 = lds_read_tr(ring + vring_pos(r0, c0 >> 3) + (c0 & 7));
-      const bf16x4 x1 = lds_read_tr(ring + vring_pos(r0 + 4, c0 >> 3) + (c0 & 7));
+      const bf16x4 x0 = lds_read_tr(r0 + cl.coff[kk][0][dt]);
+      const bf16x4 x1 = lds_read_tr(r1 + cl.coff[kk][1][dt]);
       const bf16x8 vh = cat44(x0, x1);
       oacc[dt] = mfma(vh, tap[kk].hi, oacc[dt]);
       oacc[dt] = mfma(vh, tap[kk].lo, oacc[dt]);
@@ -372,11 +392,8 @@ __device__ __forceinline__ void load_q16(const u16* Q, int n, int tok, bf16x8 (&
 
 // grid (blocks per head, B H), 256 threads; workgroup x covers tokens
 // [x R, min(n, (x + 1) R)), R a multiple of 64.  junk: >= 16 * 64 bf16, the
-// destination of tiles past the range.  Two register buffers of each kind
-// alternate between even and odd units, so every load is issued two units
-// before its data is used: unit u writes the V group loaded at unit u - 2
-// (group u / 64 + 3, first read at unit u + 2) and loads group u / 64 + 5, and
-// uses the Q rows loaded at unit u - 2 before loading those of unit u + 2.
+// destination of tiles past the range.  Two Q register buffers alternate
+// between even and odd units (loaded two units before use).
 template <int M, bool CONV>
 __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk) {
   using Ly = OutStreamLayout<M>;
@@ -394,8 +411,8 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
   const u16* V = reinterpret_cast<const u16*>(a.v) + (size_t)bh * a.n * HD;
   u16* O = reinterpret_cast<u16*>(a.out) + (size_t)bh * a.n * HD;
 
-  // ---- prologue: landmarks and W^T fragments (DMA), V groups G0 - 1 .. G0 + 2
-  // (through registers), groups G0 + 3, G0 + 4 and the Q rows of units 0, 1 in flight
+  // ---- prologue: landmarks and W^T fragments (DMA), V groups G0 - 1 .. G0 + 1
+  // (through registers), group G0 + 2 and the Q rows of units 0, 1 in flight
   {
     const __bf16* kt = a.kt_hi + (size_t)bh * M * HD;
     const __bf16* wf = a.wf_hi + (size_t)bh * 4 * KS * 64 * 8;
@@ -408,32 +425,36 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     for (int c = wave; c < 4 * KS; c += 4) dma16(wf + (size_t)c * 512 + 8 * lane, wf_s + 512 * c);
   }
   const int G0 = tb / OUTS_UNIT;
-  VGroup vb[2];
+  const int Glast = G0 + nunits;  // last group any unit reads (rows up to the range end + 32)
+  VGroup vb;
+  ConvLane cl;
   if constexpr (CONV) {
-    VGroup pre[4];
+    VGroup pre[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vgroup_load(V, a.n, G0 - 1 + i, pre[i]);
+    for (int i = 0; i < 3; ++i)
+      if (G0 - 1 + i <= Glast) vgroup_load(V, a.n, G0 - 1 + i, pre[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vgroup_store(pre[i], G0 - 1 + i, ring);
-    vgroup_load(V, a.n, G0 + 3, vb[0]);
-    vgroup_load(V, a.n, G0 + 4, vb[1]);
+    for (int i = 0; i < 3; ++i)
+      if (G0 - 1 + i <= Glast) vgroup_store(pre[i], G0 - 1 + i, ring);
+    if (G0 + 2 <= Glast) vgroup_load(V, a.n, G0 + 2, vb);
+    conv_lane_init(cl);
   }
   bf16x8 qb[2][2];
   load_q16(Q, a.n, tb + 16 * wave + c16, qb[0]);
-  load_q16(Q, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
+  if (nunits > 1) load_q16(Q, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
   Frag2 tap[3];
   if constexpr (CONV) conv_taps(a.conv_w + (size_t)h * TAPS, tap);
   wait_vmcnt<0>();  // the landmark / fragment copies (the register loads are tracked by the compiler)
   __syncthreads();
 
   const float ls2 = a.lscale * LOG2E;
-  auto unit = [&](int u, VGroup& vbu, bf16x8(&q)[2]) {
+  auto unit = [&](int u, bf16x8(&q)[2]) {
     const int t0 = tb + OUTS_UNIT * u;
     const int G = t0 / OUTS_UNIT;
-    if (u > 0) __syncthreads();  // last unit's ring writes are visible; reads of the slot reused below are done
+    if (u > 0) __syncthreads();  // last unit's ring writes are visible; its reads of the slot reused below are done
     if constexpr (CONV) {
-      vgroup_store(vbu, G + 3, ring);  // slot of G - 3: last read two units ago
-      vgroup_load(V, a.n, G + 5, vbu);
+      if (G + 2 <= Glast) vgroup_store(vb, G + 2, ring);  // slot of G - 2: last read by the previous unit
+      if (G + 3 <= Glast) vgroup_load(V, a.n, G + 3, vb);
     }
     const int ts = t0 + 16 * wave;
     // S^T = Kt Q^T: sacc[it][r] = logit(token ts + c16, landmark 16 it + 4g + r)
@@ -447,7 +468,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
         sacc[it] = mfma(kf, q[ks], sacc[it]);
       }
     }
-    load_q16(Q, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
+    if (u + 2 < nunits) load_q16(Q, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < TM; ++it)
@@ -484,16 +505,16 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
         oacc[dt] = mfma(wf, pf, oacc[dt]);
       }
     }
-    if constexpr (CONV) conv_tile_ring(ring, ts, tap, oacc);
+    if constexpr (CONV) conv_tile_ring(ring, t0, cl, tap, oacc);
     u16* dst = ts < te ? O + (size_t)(ts + c16) * HD : junk + c16 * HD;
     store_row16<u16, true>(dst, oacc);
   };
   int u = 0;
   for (; u + 1 < nunits; u += 2) {
-    unit(u, vb[0], qb[0]);
-    unit(u + 1, vb[1], qb[1]);
+    unit(u, qb[0]);
+    unit(u + 1, qb[1]);
   }
-  if (u < nunits) unit(u, vb[0], qb[0]);
+  if (u < nunits) unit(u, qb[0]);
 }
 
 }  // namespace nys

@@ -345,9 +345,9 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     const int R = OUTS_UNIT * ((p.n + want * OUTS_UNIT - 1) / (want * OUTS_UNIT));
     const int nbh = (p.n + R - 1) / R;
     if (conv_w != nullptr)
-      HIP_TRY(launch("k_out", k_out_stream<M, true>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
+      HIP_TRY(launch("k_out_stream", k_out_stream<M, true>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
     else
-      HIP_TRY(launch("k_out", k_out_stream<M, false>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
+      HIP_TRY(launch("k_out_stream", k_out_stream<M, false>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
   } else {
     const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
     HIP_TRY(allow_lds(k_out<IO, M>, lds4));
