@@ -20,6 +20,9 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # no packed-FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs (no accvgpr copies before
+    # the VALU work on them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]

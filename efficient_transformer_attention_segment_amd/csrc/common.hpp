@@ -90,6 +90,15 @@ __device__ __forceinline__ float bf16u_to_f32(uint32_t bits16) { return __uint_a
 
 __device__ __forceinline__ u16 f32_to_bf16u(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+// Two floats -> two round-to-nearest-even bf16 in one word (low = a): one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum / max across the 16 lanes of a row (lanes sharing l / 16) with DPP
@@ -226,8 +235,7 @@ struct IOTraits<u16> {
   __device__ static __forceinline__ void store16(u16* p, const float* x) {
     uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i] = (uint32_t)f32_to_bf16u(x[2 * i]) | ((uint32_t)f32_to_bf16u(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
     reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }

@@ -58,16 +58,14 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-          w[2 * b + r] = (uint32_t)f32_to_bf16u(acc[2 * h + b][2 * r]) |
-                         ((uint32_t)f32_to_bf16u(acc[2 * h + b][2 * r + 1]) << 16);
+        for (int r = 0; r < 2; ++r) w[2 * b + r] = pack_bf16x2(acc[2 * h + b][2 * r], acc[2 * h + b][2 * r + 1]);
       *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(row) + 32 * h + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint32_t w0 = (uint32_t)f32_to_bf16u(acc[dt][0]) | ((uint32_t)f32_to_bf16u(acc[dt][1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16u(acc[dt][2]) | ((uint32_t)f32_to_bf16u(acc[dt][3]) << 16);
+      const uint32_t w0 = pack_bf16x2(acc[dt][0], acc[dt][1]);
+      const uint32_t w1 = pack_bf16x2(acc[dt][2], acc[dt][3]);
       *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(row) + 16 * dt + 4 * g) = make_uint2(w0, w1);
     }
   }

@@ -493,12 +493,10 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = (__bf16)(sacc[2 * ks][e] * inv);
-        pf[4 + e] = (__bf16)(sacc[2 * ks + 1][e] * inv);
-      }
+      const f32x8 pv = {sacc[2 * ks][0] * inv,     sacc[2 * ks][1] * inv,     sacc[2 * ks][2] * inv,
+                        sacc[2 * ks][3] * inv,     sacc[2 * ks + 1][0] * inv, sacc[2 * ks + 1][1] * inv,
+                        sacc[2 * ks + 1][2] * inv, sacc[2 * ks + 1][3] * inv};
+      const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wf_s + ((dt * KS + ks) * 64 + lane) * 8);
