@@ -40,32 +40,55 @@ struct LandmarkArgs {
   unsigned* sync;       // [4] cross-block maxima + arrival count, zeroed by k_landmark
 };
 
+// LDS staging of Kt for the Gram (elements): bf16 hi / lo planes with row
+// stride 72 (bf16 I/O) or float32 rows with stride 68 (float32 I/O).
+template <int M, bool F32>
+constexpr int gram_kst_bytes() {
+  return F32 ? M * 68 * 4 : 2 * M * 72 * 2;
+}
+
 // A = softmax(Qt Kt^T) for one head, by the NW waves of the block; writes A
 // and the head's maximum column and row sums (also returned in wred[0] and
-// wred[1] to every thread).  M = m (multiple of 32).  csum: LDS scratch of
-// (M/16) * M floats; wred: 2 * NW floats.
+// wred[1] to every thread).  M = m (multiple of 32).  Kt comes into LDS (kst,
+// gram_kst_bytes) in one coalesced pass first; each wave takes row tiles
+// wave, wave + NW, ...  csum: LDS scratch of (M/16) * M floats; wred: 2 * NW.
 template <int M, bool F32, int NW>
-__device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred) {
+__device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred, void* kst) {
   constexpr int TM = M / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const float* qt = a.qt + (size_t)bh * M * HD;
-  const float* kt = a.kt + (size_t)bh * M * HD;
   float* A = a.A + (size_t)bh * M * M;
+  float* const kf32 = reinterpret_cast<float*>(kst);
+  __bf16* const kb16 = reinterpret_cast<__bf16*>(kst);
+  if constexpr (F32) {
+    const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
+    for (int i = threadIdx.x; i < M * (HD / 4); i += 64 * NW)
+      *reinterpret_cast<float4*>(kf32 + (i >> 4) * 68 + 4 * (i & 15)) = kt[i];
+  } else {
+    const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * HD);
+    const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * HD);
+    for (int i = threadIdx.x; i < M * (HD / 8); i += 64 * NW) {
+      *reinterpret_cast<uint4*>(kb16 + (i >> 3) * 72 + 8 * (i & 7)) = kh[i];
+      *reinterpret_cast<uint4*>(kb16 + (M + (i >> 3)) * 72 + 8 * (i & 7)) = kl[i];
+    }
+  }
+  __syncthreads();
   float rmax_w = 0.f;
   for (int rt = wave; rt < TM; rt += NW) {
     // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
     float ax[2][8];
+    Frag2 af[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const float* p = qt + (size_t)(rt * 16 + c16) * HD + ks * 32 + g * 8;
+      const size_t off = (size_t)(rt * 16 + c16) * HD + ks * 32 + g * 8;
+      if constexpr (F32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ax[ks][e] = p[e];
-    }
-    Frag2 af[2];
-    if constexpr (!F32) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) af[ks] = split8(ax[ks]);
+        for (int e = 0; e < 8; ++e) ax[ks][e] = qt[off + e];
+      } else {
+        af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + (size_t)bh * M * HD + off);
+        af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + (size_t)bh * M * HD + off);
+      }
     }
     f32x4 acc[TM];
 #pragma unroll
@@ -73,14 +96,18 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
       acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-        const float* p = kt + (size_t)(ct * 16 + c16) * HD + ks * 32 + g * 8;
+        const int row = ct * 16 + c16, col = ks * 32 + g * 8;
+        if constexpr (F32) {
+          float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[e];
-        if constexpr (F32)
+          for (int e = 0; e < 8; ++e) x[e] = kf32[row * 68 + col + e];
           acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
-        else
-          acc[ct] = mma<3>(af[ks], split8(x), acc[ct]);
+        } else {
+          Frag2 bf;
+          bf.hi = *reinterpret_cast<const bf16x8*>(kb16 + row * 72 + col);
+          bf.lo = *reinterpret_cast<const bf16x8*>(kb16 + (M + row) * 72 + col);
+          acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+        }
       }
     }
     // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
@@ -224,12 +251,21 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   }
 }
 
-// grid: BH, block 256.
+// grid: BH, block 64 gram_waves<M>() threads, dynamic LDS gram_lds_bytes<M, F32>().
+template <int M>
+constexpr int gram_waves() {
+  return M / 16 < 16 ? (M / 16 < 4 ? 4 : M / 16) : 16;
+}
 template <int M, bool F32>
-__global__ __launch_bounds__(256) void k_gram(LandmarkArgs a) {
-  __shared__ float csum[(M / 16) * M];
-  __shared__ float wred[8];
-  landmark_gram_tail<M, F32, 4>(a, blockIdx.x, csum, wred);
+constexpr int gram_lds_bytes() {
+  return gram_kst_bytes<M, F32>() + 4 * ((M / 16) * M + 2 * gram_waves<M>());
+}
+template <int M, bool F32>
+__global__ __launch_bounds__(64 * gram_waves<M>()) void k_gram(LandmarkArgs a) {
+  extern __shared__ __align__(16) float gram_smem[];
+  float* const csum = gram_smem + gram_kst_bytes<M, F32>() / 4;
+  float* const wred = csum + (M / 16) * M;
+  landmark_gram_tail<M, F32, gram_waves<M>()>(a, blockIdx.x, csum, wred, gram_smem);
 }
 
 }  // namespace nys

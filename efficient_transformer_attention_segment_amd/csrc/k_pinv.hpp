@@ -813,17 +813,22 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
 // M > 128: the iteration as a launch sequence over global memory.
 
 // grid: BH blocks of 256: c, then Z = A^T / c.
+// grid ((M/32)^2, BH), block 256: c, then the 32 x 32 tile (tr, tc) of
+// Z = A^T / c through an LDS tile (coalesced reads and writes).
 __global__ __launch_bounds__(256) void k_pinv_init(PinvArgs a, int M) {
-  const int bh = blockIdx.x;
+  __shared__ float tile[32][33];
+  const int bh = blockIdx.y;
+  const int nb = M / 32;
+  const int tr = blockIdx.x / nb, tc = blockIdx.x % nb;
   const float c = pinv_scale(a, bh);
   const float invc = 1.0f / c;
-  if (threadIdx.x == 0) a.cscale[bh] = c;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.cscale[bh] = c;
   const float* A = a.A + (size_t)bh * M * M;
   float* Z = a.Z + (size_t)bh * M * M;
-  for (int idx = threadIdx.x; idx < M * M; idx += 256) {
-    const int row = idx / M, col = idx % M;
-    Z[idx] = A[(size_t)col * M + row] * invc;
-  }
+  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
+  for (int y = y0; y < 32; y += 8) tile[y][x] = A[(size_t)(32 * tc + y) * M + 32 * tr + x];  // A rows of Z's columns
+  __syncthreads();
+  for (int y = y0; y < 32; y += 8) Z[(size_t)(32 * tr + y) * M + 32 * tc + x] = tile[x][y] * invc;
 }
 
 // C = alpha * P * Q' with Q' = Q when beta == 0, else beta * I - Q.

@@ -246,7 +246,12 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   HIP_TRY(launch("k_landmark", k_landmark<IO, M>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
   const bool fuse_gram = M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
-  if (!fuse_gram) HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(256), 0, st, la));
+  if (!fuse_gram) {
+    constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4>();
+    HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4>, glds));
+    HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(64 * gram_waves<M>()), (uint32_t)glds, st,
+                   la));
+  }
 
   PinvArgs pa;
   pa.A = la.A;
@@ -286,7 +291,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
 
   const float* Zfinal = pa.Z;
   if constexpr (M > 128) {
-    HIP_TRY(launch("k_pinv_init", k_pinv_init, dim3(p.BH), dim3(256), 0, st, pa, M));
+    HIP_TRY(launch("k_pinv_init", k_pinv_init, dim3((M / 32) * (M / 32), p.BH), dim3(256), 0, st, pa, M));
     float* Zc = pa.Z;
     float* Zn = at<float>(w, p.off_Z2);
     float* X = at<float>(w, p.off_X);
