@@ -74,7 +74,7 @@ def algorithmic_bytes(w):
     per = {
         "k_landmark": BH * (2 * nd + small),
         "k_pinv_bv": BH * (2 * nd + 4 * m * d * 2 + 4 * m * m * 2) + mask,   # K, V, Qt, A, Z, B V
-        "k_merge": BH * 4 * (m * m + 2 * m * d),                              # Z, B V -> W
+        "k_mw": BH * 4 * (m * m + 2 * m * d),                                 # Z, B V -> W
         "k_out": BH * (3 * nd + 4 * 2 * m * d) + w.H * 65 * 4,               # Q, V -> O; Kt, W
         "k_out_stream": BH * (3 * nd + 2 * 2 * m * d) + w.H * 65 * 4,        # Q, V -> O; Kt, W^T (bf16)
         "k_exact": BH * 4 * nd,

@@ -9,7 +9,7 @@
 //
 // A workgroup owns up to 64 "columns" (landmarks for B V, queries for the
 // exact branch; 16 per wave and tile) and streams 32-key tiles of K and V
-// through LDS.  bf16 inputs are copied global -> LDS by DMA, three tiles
+// through LDS.  bf16 inputs are copied global -> LDS by DMA, six tiles
 // ahead (K and V row-major; V read back transposed by ds_read_b64_tr_b16);
 // float32 inputs go through registers (split into bf16 hi/lo, V stored
 // transposed), double buffered.  Per tile and wave:
@@ -300,16 +300,22 @@ __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u
                                               __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
                                               float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
   constexpr int CNT = 8 / NW + (MASK ? 1 : 0);  // copies per tile and wave
-  static_assert(DMA_DIST - 1 <= 5, "wait_vmcnt_rt covers up to 5 tiles");
+  static_assert(DMA_DIST - KP <= 5, "wait_vmcnt_rt covers up to 5 tiles");
+  // a tile's buffer is refilled only after the step that read it
+  static_assert(DMA_DIST + KP <= DMA_NBUF, "ring too short for the copy distance");
   const int T = tile1 - tile0;
   for (int j = 0; j < DMA_DIST && j < T; ++j)
     dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + j) * 32, lds, j % DMA_NBUF);
-  for (int t = 0; t < T; ++t) {
-    wait_vmcnt_rt<CNT>(min(DMA_DIST - 1, T - 1 - t));
+  // one step per KP tiles: the KP wave groups work on their tiles of the
+  // step at the same time, between one barrier and the next
+  for (int t = 0; t < T; t += KP) {
+    wait_vmcnt_rt<CNT>(max(0, min(DMA_DIST - KP, T - t - KP)));
     barrier_only();
-    if (t + DMA_DIST < T)
-      dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + t + DMA_DIST) * 32, lds, (t + DMA_DIST) % DMA_NBUF);
-    if ((t % KP) == kp) dma_tile_update<TPW, MASK>(lds, t % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      if (t + DMA_DIST + i < T)
+        dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + t + DMA_DIST + i) * 32, lds, (t + DMA_DIST + i) % DMA_NBUF);
+    if (t + kp < T) dma_tile_update<TPW, MASK>(lds, (t + kp) % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
   }
   barrier_only();
 }
@@ -322,7 +328,7 @@ struct BvArgs {
   const __bf16* qt_lo;
   float* pmax;              // [BH][S][M]
   float* psum;              // [BH][S][M]
-  float* pacc;              // [BH][S][M][64]
+  float* pacc;              // [BH][S][16][M][4]: 4-channel runs, each run's rows contiguous
   int n, H, S, tpc, ntiles;
   float lscale;             // d^-1/4 (Qt carries the other factor)
 };
@@ -337,8 +343,9 @@ constexpr int bv_waves() {
 // Partial B V of one (head, key chunk): all M landmarks.  With NW waves
 // and TM landmark tiles, wave w owns landmark tiles {w, w + NW, ...}; when
 // there are twice as many waves as tiles (m <= 64) the tile's two waves
-// take alternate key tiles (KP = 2) and fold their online-softmax states
-// together in LDS at the end.
+// take alternate key tiles (KP = 2), both tiles of a pair in the same
+// barrier step, and fold their online-softmax states together in LDS at
+// the end.
 template <typename IO, int M>
 __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   constexpr int TM = M / 16;
@@ -421,7 +428,12 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
       a.pmax[row] = mrun[o];  // log2 units of the scaled logit
       a.psum[row] = ls;
     }
-    store_row16<float, false>(a.pacc + row * HD, acc[o]);
+    // lane (c16, g) holds channels 16 dt + 4 g .. + 3 of row i: run 4 dt + g
+    float* const pr = a.pacc + ((size_t)bh * a.S + chunk) * 16 * M * 4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(pr + ((size_t)(4 * dt + g) * M + i) * 4) =
+          make_float4(acc[o][dt][0], acc[o][dt][1], acc[o][dt][2], acc[o][dt][3]);
   }
 }
 

@@ -3,15 +3,21 @@
 //
 // Launch sequence for one Nystrom call (all on the caller's stream):
 //   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo)
-//   2 k_gram       per head A = softmax(Qt Kt^T), its max column / row sum
+//   2 k_gram       per head A = softmax(Qt Kt^T), its max column / row sum;
+//                  only when the pseudo-inverse blocks cannot form A
+//                  themselves (m > 128, or the original init with more
+//                  heads than can meet in one resident round)
 //   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
 //                  blocks (m <= 128) and the B V partial blocks, so the
 //                  pseudo-inverse chain runs beside the K/V stream
 //     (m > 128: k_pinv_init + 4 k_pinv_gemm launches per iteration)
-//   4 k_merge      B V from the partials
-//   5 k_w          W = Z (B V) and its operand fragments
-//   6 k_out        F W + conv(V) -> out
-// Kernel boundaries are the only cross-workgroup synchronisation.
+//   4 k_mw         B V from the partials, W = Z (B V) and its operand
+//                  fragments
+//   5 k_out_stream F W + conv(V) -> out (bf16 I/O; k_out for float32)
+// Kernel boundaries are the only cross-workgroup synchronisation, apart
+// from the one meeting of the pseudo-inverse blocks for the original init
+// (data handed between workgroups of one launch across XCDs would need L2
+// write-back and invalidation, which cost far more here than a launch).
 // The exact branch (m == n) is one k_exact launch.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -322,8 +328,18 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ma.wf_hi = at<__bf16>(w, p.off_wfh);
   ma.wf_lo = at<__bf16>(w, p.off_wfl);
   ma.S = p.S;
-  HIP_TRY(launch("k_merge", k_merge<M>, dim3(M / 16, p.BH), dim3(256), 0, st, ma));
-  HIP_TRY(launch("k_w", k_w<M, sizeof(IO) == 2, sizeof(IO) == 4>, dim3(M / 32, p.BH), dim3(256), 0, st, ma));
+  ma.BH = p.BH;
+  // threads per block: enough chunk subsets per row that each thread folds
+  // one batch of 8 chunks (up to 1024 threads; 512 for m = 32)
+  const int need = M * ((p.S + 7) / 8);
+  constexpr bool B16 = sizeof(IO) == 2;
+  constexpr int NT_MAX = M >= 64 ? 1024 : 512;
+  if (need <= 256)
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 256>, dim3(mw_blocks(p.BH)), dim3(256), 0, st, ma));
+  else if (need <= 512 || NT_MAX == 512)
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 512>, dim3(mw_blocks(p.BH)), dim3(512), 0, st, ma));
+  else
+    HIP_TRY(launch("k_mw", k_mw<M, B16, NT_MAX>, dim3(mw_blocks(p.BH)), dim3(NT_MAX), 0, st, ma));
 
   OutArgs oa;
   oa.q = q;
@@ -340,9 +356,9 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.lscale = s4;
   if constexpr (sizeof(IO) == 2) {
     // persistent output pass: a token range of one head per workgroup, sized
-    // so the grid fills the CUs at the occupancy its LDS allows
-    // persistent workgroups: at most one resident round (a second, partial
-    // round would cost a whole workgroup lifetime)
+    // so the grid fills the CUs at the occupancy its LDS allows in at most
+    // one resident round (a second, partial round would cost a whole
+    // workgroup lifetime)
     constexpr size_t lds4 = OutStreamLayout<M>::LDS_BYTES;
     constexpr int per_cu = std::min<int>(4, (int)(160 * 1024 / lds4));
     const int slots = 256 * per_cu;
