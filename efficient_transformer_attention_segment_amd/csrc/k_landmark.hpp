@@ -37,7 +37,7 @@ struct LandmarkArgs {
   float* A;             // [BH][m][m]
   float* colmax;        // [BH]
   float* rowmax;        // [BH]
-  unsigned* sync;       // [4] cross-block maxima + arrival count, zeroed by k_landmark
+  unsigned long long* slots;  // [BH][2] pseudo-inverse blocks' tagged maxima, cleared by k_landmark
 };
 
 // LDS staging of Kt for the Gram (elements): bf16 hi / lo planes with row
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   const int j = t / (TPR * RS);
   const int i = blockIdx.x * lpw + j;
   const size_t base = ((size_t)bh * a.n + (size_t)i * L) * HD + c * CW;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && t < 4) a.sync[t] = 0u;  // read by the next launch
+  if (blockIdx.x == 0 && t < 2) a.slots[2 * blockIdx.y + t] = 0ull;  // written in the next launch
 
   float sq[CW], sk[CW];
 #pragma unroll

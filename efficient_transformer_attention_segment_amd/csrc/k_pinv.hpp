@@ -44,7 +44,8 @@ struct PinvArgs {
   int BH, n_iter, init_option;
   int f16;              // bf16 I/O: 1 = single fp16 products, 0 = split bf16
   int fuse_gram;        // 1: each block forms its own head's A first (m <= 128)
-  int npinv;            // pseudo-inverse blocks in the launch (the rendezvous count)
+  int npinv;            // pseudo-inverse blocks in the launch (<= 128: slots polled by one wave)
+  int record;           // 1: also write A to global (fuse_gram; for the stage hook)
   LandmarkArgs la;      // landmarks in, A / colmax / rowmax out (fuse_gram)
 };
 
@@ -75,52 +76,66 @@ template <int M, int R0_BYTES, int NW>
 struct ProLayout {
   static constexpr int QLD = HD + 4, ALD = M + 4, TM = M / 16;
   static constexpr int OFF_QT = 0, OFF_KT = M * QLD;  // float32 staging (float32 I/O)
-  static constexpr int BLD = HD + 8;                  // bf16 hi/lo staging row stride (bf16 I/O)
-  static constexpr int STAGE = (2 * M * QLD > 2 * M * BLD) ? 2 * M * QLD : 2 * M * BLD;  // floats
+  static constexpr int STAGE = 2 * M * QLD;           // floats: float32 Qt, Kt, or the four bf16 planes
   static constexpr int OFF_A = (R0_BYTES / 4 > STAGE) ? R0_BYTES / 4 : STAGE;
   static constexpr int OFF_CSUM = OFF_A + M * ALD;
   static constexpr int OFF_WRED = OFF_CSUM + TM * M;
   static constexpr int BYTES = 4 * (OFF_WRED + 2 * NW);
 };
 
-// A = softmax(Qt Kt^T) for one head into LDS (and to global for the stage
-// hook), with the head's maximum column and row sums in wred[0], wred[1]
-// (and in colmax / rowmax).  The landmarks come into LDS in one coalesced
+// A = softmax(Qt Kt^T) for one head into LDS (store_a_lds copies it to
+// global for the stage hook later), with the head's maximum column and row
+// sums in wred[0], wred[1] (and in colmax / rowmax).  The landmarks come into LDS in one coalesced
 // pass first, so the products read LDS instead of waiting on global loads:
 // float32 Qt, Kt for float32 I/O (float32 products), and for bf16 I/O the
 // bf16 hi / lo planes the landmark kernel already wrote (split-bf16
 // products with no conversion work here).
 template <int M, bool F32, int NW, class Ly>
 __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
-  constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD, BLD = Ly::BLD;
+  constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   float* const Qs = L + Ly::OFF_QT;
   float* const Ks = L + Ly::OFF_KT;
-  __bf16* const Bs = reinterpret_cast<__bf16*>(L);  // planes qt_hi, qt_lo, kt_hi, kt_lo, M x BLD each
+  __bf16* const Bs = reinterpret_cast<__bf16*>(L);  // planes qt_hi, qt_lo, kt_hi, kt_lo, M x 64 each (swz)
   float* const Al = L + Ly::OFF_A;
   float* const csum = L + Ly::OFF_CSUM;
   float* const wred = L + Ly::OFF_WRED;
-  float* A = a.A + (size_t)bh * M * M;
+  // every load of the staging pass is issued before the first LDS store
+  constexpr int NT = 64 * NW;
   if constexpr (F32) {
+    constexpr int TOT = M * (HD / 4), CNT = (TOT + NT - 1) / NT;
     const float4* qt = reinterpret_cast<const float4*>(a.qt + (size_t)bh * M * HD);
     const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
-    for (int i = tid; i < M * (HD / 4); i += 64 * NW) {
-      const int row = i >> 4, c4 = i & 15;
-      const float4 x = qt[i], y = kt[i];
-      *reinterpret_cast<float4*>(Qs + row * QLD + 4 * c4) = x;
-      *reinterpret_cast<float4*>(Ks + row * QLD + 4 * c4) = y;
-    }
-  } else {
-    const __bf16* src[4] = {a.qt_hi, a.qt_lo, a.kt_hi, a.kt_lo};
+    float4 x[CNT], y[CNT];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint4* s4 = reinterpret_cast<const uint4*>(src[p] + (size_t)bh * M * HD);
-      for (int i = tid; i < M * (HD / 8); i += 64 * NW) {
-        const int row = i >> 3, c8 = i & 7;
-        *reinterpret_cast<uint4*>(Bs + (p * M + row) * BLD + 8 * c8) = s4[i];
+    for (int k = 0; k < CNT; ++k) {
+      const int i = tid + k * NT;
+      if (i < TOT) {
+        x[k] = qt[i];
+        y[k] = kt[i];
       }
     }
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) {
+      const int i = tid + k * NT, row = i >> 4, c4 = i & 15;
+      if (i < TOT) {
+        *reinterpret_cast<float4*>(Qs + row * QLD + 4 * c4) = x[k];
+        *reinterpret_cast<float4*>(Ks + row * QLD + 4 * c4) = y[k];
+      }
+    }
+  } else {
+    // the four planes, M rows of 128 bytes each with XOR-swizzled 16-byte
+    // chunks (swz), copied global -> LDS by DMA: one wave instruction moves
+    // 8 rows (lane l: row l / 8, LDS chunk l % 8)
+    const __bf16* src[4] = {a.qt_hi, a.qt_lo, a.kt_hi, a.kt_lo};
+    for (int c = wave; c < 4 * (M / 8); c += NW) {
+      const int p = c / (M / 8), r8 = c % (M / 8);
+      const int row = 8 * r8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row & 7);
+      dma16(src[p] + ((size_t)bh * M + row) * HD + 8 * chunk, Bs + (p * M + 8 * r8) * HD);
+    }
+    wait_vmcnt<0>();
   }
   __syncthreads();
   float rmax_w = 0.f;
@@ -135,8 +150,8 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ax[ks][e] = Qs[row * QLD + col + e];
       } else {
-        af[ks].hi = *reinterpret_cast<const bf16x8*>(Bs + row * BLD + col);
-        af[ks].lo = *reinterpret_cast<const bf16x8*>(Bs + (M + row) * BLD + col);
+        af[ks].hi = *reinterpret_cast<const bf16x8*>(Bs + swz(row, 4 * ks + g));
+        af[ks].lo = *reinterpret_cast<const bf16x8*>(Bs + M * HD + swz(row, 4 * ks + g));
       }
     }
     f32x4 acc[TM];
@@ -153,8 +168,8 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
           acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
         } else {
           Frag2 bf;
-          bf.hi = *reinterpret_cast<const bf16x8*>(Bs + (2 * M + row) * BLD + col);
-          bf.lo = *reinterpret_cast<const bf16x8*>(Bs + (3 * M + row) * BLD + col);
+          bf.hi = *reinterpret_cast<const bf16x8*>(Bs + 2 * M * HD + swz(row, 4 * ks + g));
+          bf.lo = *reinterpret_cast<const bf16x8*>(Bs + 3 * M * HD + swz(row, 4 * ks + g));
           acc[ct] = mma<3>(af[ks], bf, acc[ct]);
         }
       }
@@ -193,7 +208,6 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * rt + 4 * g + r;
         Al[row * ALD + 16 * ct + c16] = acc[ct][r];
-        A[(size_t)row * M + 16 * ct + c16] = acc[ct][r];
       }
       float cs = acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3];
       cs = sum_g(cs);
@@ -234,20 +248,27 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
 // copies the A of the separate Gram launch.  Option 1 needs only this head.
 // Option 0 needs the maxima over every head: the pseudo-inverse blocks are
 // the first npinv blocks of the launch (dispatched first, all resident: the
-// host fuses only while npinv is well under the CU count), and meet once:
-// each folds its two maxima into sync[0..1] with agent-scope atomic max,
-// then bumps the count sync[2] with an add whose operand depends on both max
-// results (so the maxima are in place first); each then waits for the count
-// to reach npinv and reads the maxima back with agent-scope atomic loads.
-// No fence is involved, so other blocks' writes are not flushed.
+// host fuses only while npinv is at most 128, half the CU count), and meet
+// once.  Each publishes its two maxima as 64-bit words (valid bit 32 above
+// the float bits) with single agent-scope atomic stores into its own slots,
+// which the landmark launch cleared; wave 0 of every block then polls all
+// slots (one 64-bit atomic load per slot, two slots per lane) until every
+// one is valid, and takes the maxima.  A word is written whole, so a valid
+// one carries its maximum; there is no other shared data and no fence.
 template <int M, bool F32, int NW, class Ly>
 __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
   float* const wred = L + Ly::OFF_WRED;
   if (!a.fuse_gram) {
+    constexpr int NT = 64 * NW, TOT = M * M / 4, CNT = (TOT + NT - 1) / NT;
     const float4* A = reinterpret_cast<const float4*>(a.A + (size_t)bh * M * M);
-    for (int i = threadIdx.x; i < M * M / 4; i += 64 * NW) {
-      const int row = i / (M / 4), c4 = i % (M / 4);
-      *reinterpret_cast<float4*>(L + Ly::OFF_A + row * Ly::ALD + 4 * c4) = A[i];
+    float4 x[CNT];
+#pragma unroll
+    for (int k = 0; k < CNT; ++k)
+      if (threadIdx.x + k * NT < TOT) x[k] = A[threadIdx.x + k * NT];
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) {
+      const int i = threadIdx.x + k * NT, row = i / (M / 4), c4 = i % (M / 4);
+      if (i < TOT) *reinterpret_cast<float4*>(L + Ly::OFF_A + row * Ly::ALD + 4 * c4) = x[k];
     }
     __syncthreads();
     return pinv_scale(a, bh);
@@ -256,26 +277,53 @@ __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
   const float cm = wred[0], rm = wred[1];
   if (a.init_option != 0) return cm * rm;
   __syncthreads();  // every thread has read wred
+  constexpr unsigned long long VALID = 1ull << 32;
+  unsigned long long* const slots = a.la.slots;
   if (threadIdx.x == 0) {
-    const unsigned r0 = __hip_atomic_fetch_max(a.la.sync + 0, __float_as_uint(cm), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned r1 = __hip_atomic_fetch_max(a.la.sync + 1, __float_as_uint(rm), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned inc = (r0 == 0xffffffffu && r1 == 0xffffffffu) ? 2u : 1u;  // depends on both results
-    __hip_atomic_fetch_add(a.la.sync + 2, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slots + 2 * bh, VALID | __float_as_uint(cm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slots + 2 * bh + 1, VALID | __float_as_uint(rm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     float c = __builtin_nanf("");
     for (unsigned it = 0; it < RENDEZVOUS_SPINS; ++it) {
-      if (__hip_atomic_load(a.la.sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.npinv) {
-        c = __uint_as_float(__hip_atomic_load(a.la.sync + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) *
-            __uint_as_float(__hip_atomic_load(a.la.sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      bool ok = true;
+      float cmx = 0.f, rmx = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int b = lane + 64 * k;
+        if (b < a.npinv) {
+          const unsigned long long v0 = __hip_atomic_load(slots + 2 * b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const unsigned long long v1 =
+              __hip_atomic_load(slots + 2 * b + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = ok && (v0 & VALID) && (v1 & VALID);
+          cmx = fmaxf(cmx, __uint_as_float((unsigned)v0));
+          rmx = fmaxf(rmx, __uint_as_float((unsigned)v1));
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+        c = wave_max(cmx) * wave_max(rmx);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    wred[0] = c;
+    if (lane == 0) wred[0] = c;
   }
   __syncthreads();
   return wred[0];
+}
+
+// The A the block formed itself (fuse_gram), from LDS to global when the
+// stage hook asks for it; called before the LDS copy of A is overwritten.
+template <int M, int ALD>
+__device__ __forceinline__ void store_a_lds(const PinvArgs& a, const float* Al, int bh) {
+  if (!a.fuse_gram || !a.record) return;
+  float* A = a.la.A + (size_t)bh * M * M;
+  for (int i = threadIdx.x; i < M * M / 4; i += blockDim.x) {
+    const int row = i / (M / 4), c4 = i % (M / 4);
+    *reinterpret_cast<float4*>(A + (size_t)row * M + 4 * c4) =
+        *reinterpret_cast<const float4*>(Al + row * ALD + 4 * c4);
+  }
 }
 
 // Z = Z_0 = A^T / c (no iterations), from A in LDS, by the whole block.
@@ -495,6 +543,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   const float invc = 1.0f / c;
   const float* const Al = reinterpret_cast<const float*>(lds) + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
+  store_a_lds<M, Ly::ALD>(a, Al, bh);
   if (a.n_iter == 0) {
     store_z0_lds<M, Ly::ALD>(Al, Zg, invc);
     return;
@@ -692,6 +741,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   const float invc = 1.0f / c;
   const float* const Al = lds + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
+  store_a_lds<M, Ly::ALD>(a, Al, bh);
   if (a.n_iter == 0) {
     store_z0_lds<M, Ly::ALD>(Al, Zg, invc);
     return;

@@ -65,9 +65,10 @@ int fail(int code, const char* fmt, ...) {
 // ---------------------------------------------------------------- plan ---
 struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
+  bool record;  // keep every intermediate in the workspace (stage hook)
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
-  size_t off_sync, off_junk;
+  size_t off_slots, off_junk;
   size_t total;
 };
 
@@ -116,7 +117,7 @@ Plan make_plan(int B, int H, int n, int m) {
     return at;
   };
   p.off_zero = take(ZERO_BYTES);
-  p.off_sync = take(16);
+  p.off_slots = take(BH * 16);
   p.off_junk = take(16 * HD * 2);  // output rows of tiles past a workgroup's range
   p.off_qt = take(BH * M * D * 4);
   p.off_kt = take(BH * M * D * 4);
@@ -248,7 +249,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.A = at<float>(w, p.off_A);
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
-  la.sync = at<unsigned>(w, p.off_sync);
+  la.slots = at<unsigned long long>(w, p.off_slots);
   HIP_TRY(launch("k_landmark", k_landmark<IO, M>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
   const bool fuse_gram = M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
@@ -271,6 +272,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.f16 = (sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER) ? 1 : 0;
   pa.fuse_gram = fuse_gram ? 1 : 0;
   pa.npinv = p.npinv;
+  pa.record = p.record ? 1 : 0;
   pa.la = la;
   BvArgs ba;
   ba.k = k;
@@ -453,7 +455,8 @@ int run(const void* q, const void* k, const void* v, const uint8_t* mask, const 
   int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
   if (rc != NYS_OK) return rc;
   if (m == n) return launch_exact<IO>(B, H, n, q, k, v, mask, conv_w, out, st);
-  const Plan p = make_plan(B, H, n, m);
+  Plan p = make_plan(B, H, n, m);
+  p.record = pout != nullptr;  // the stage hook reads the intermediates back
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
