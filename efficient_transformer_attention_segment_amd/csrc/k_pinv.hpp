@@ -14,8 +14,8 @@
 //   chip, one or two waves per 16-row tile (see the function comment).  Two
 //   row-major (chunk-swizzled) LDS regions of 16-bit planes suffice: each step
 //   reads one and writes the other (M = 128 fits the 160 KB LDS).  Products are
-//   split-bf16 matrix-core products (hi*hi + hi*lo + lo*hi, relative error
-//   about 2^-16).
+//   single fp16 matrix-core products up to 8 iterations and split-bf16
+//   products (hi*hi + hi*lo + lo*hi, relative error about 2^-16) beyond.
 //
 // pinv_block_f32<M> (M <= 128, float32 I/O): the same schedule on the
 //   float32 matrix core with float32 matrices in LDS.  Once the iteration has
