@@ -387,10 +387,15 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   // copy pipeline below is never drained to wait for them
   wait_vmcnt<0>();
   if constexpr (sizeof(IO) == 2) {
+    // whole 32-key tiles by DMA; a ragged last tile (n % 32 != 0) through
+    // registers, which zero and mask the keys past n
+    const int tfull = min(tile1, a.n / 32);
     if (mask != nullptr)
-      kv_stream_dma<TPW, NW, true, KP>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+      kv_stream_dma<TPW, NW, true, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
     else
-      kv_stream_dma<TPW, NW, false, KP>(K, V, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+      kv_stream_dma<TPW, NW, false, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+    if (tfull < tile1)
+      kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   } else {
     kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   }

@@ -27,6 +27,7 @@ namespace nys {
 
 struct LandmarkArgs {
   int n, m, L, RS, lpw, BH;
+  int mr;               // landmarks of the method; m = mr rounded up to 32 (rows mr .. m-1 are zero)
   float scale;          // d^-1/4 / L
   float* qt;            // [BH][m][64] float32
   float* kt;
@@ -40,6 +41,16 @@ struct LandmarkArgs {
   unsigned long long* slots;  // [BH][2] pseudo-inverse blocks' tagged maxima, cleared by k_landmark
 };
 
+// Logits of padding landmark columns (16 ct + lane % 16 >= mr) -> -inf, in a
+// row of C tiles acc[ct] (rows 4g + r, column lane % 16).
+template <int TM>
+__device__ __forceinline__ void pad_mask_cols(f32x4 (&acc)[TM], int mr) {
+  const int c16 = threadIdx.x & 15;
+#pragma unroll
+  for (int ct = 0; ct < TM; ++ct)
+    if (16 * ct + c16 >= mr) acc[ct] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+}
+
 // LDS staging of Kt for the Gram (elements): bf16 hi / lo planes with row
 // stride 72 (bf16 I/O) or float32 rows with stride 68 (float32 I/O).
 template <int M, bool F32>
@@ -49,7 +60,7 @@ constexpr int gram_kst_bytes() {
 
 // A = softmax(Qt Kt^T) for one head, by the NW waves of the block; writes A
 // and the head's maximum column and row sums (also returned in wred[0] and
-// wred[1] to every thread).  M = m (multiple of 32).  Kt comes into LDS (kst,
+// wred[1] to every thread).  M: landmarks padded to a multiple of 32.  Kt comes into LDS (kst,
 // gram_kst_bytes) in one coalesced pass first; each wave takes row tiles
 // wave, wave + NW, ...  csum: LDS scratch of (M/16) * M floats; wred: 2 * NW.
 template <int M, bool F32, int NW>
@@ -110,7 +121,9 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
         }
       }
     }
-    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
+    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15;
+    // padding columns take no weight and padding rows are zero
+    if (a.mr < M) pad_mask_cols(acc, a.mr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float mx = NEG_BIG;
@@ -125,7 +138,7 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
         s += p;
       }
       s = sum16(s);
-      const float inv = 1.0f / s;
+      const float inv = rt * 16 + g * 4 + r < a.mr ? 1.0f / s : 0.f;
       float rs = 0.f;
 #pragma unroll
       for (int ct = 0; ct < TM; ++ct) {
@@ -190,13 +203,14 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   const int rs = (t / TPR) % RS;
   const int j = t / (TPR * RS);
   const int i = blockIdx.x * lpw + j;
-  const size_t base = ((size_t)bh * a.n + (size_t)i * L) * HD + c * CW;
+  const bool live = i < a.mr;  // padding landmarks stay zero
+  const size_t base = ((size_t)bh * a.n + (size_t)(live ? i : 0) * L) * HD + c * CW;
   if (blockIdx.x == 0 && t < 2) a.slots[2 * blockIdx.y + t] = 0ull;  // written in the next launch
 
   float sq[CW], sk[CW];
 #pragma unroll
   for (int e = 0; e < CW; ++e) sq[e] = sk[e] = 0.f;
-  int r = rs;
+  int r = live ? rs : L;
   for (; r + (UNR - 1) * RS < L; r += UNR * RS) {
     float xq[UNR][CW], xk[UNR][CW];
 #pragma unroll

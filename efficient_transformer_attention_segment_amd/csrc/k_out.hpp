@@ -37,8 +37,20 @@ struct OutArgs {
   const __bf16* wf_lo;
   void* out;
   int n, H;
+  int mr;                // landmarks of the method (M = mr rounded up to 32)
   float lscale;          // d^-1/4
 };
+
+// Logits of padding landmarks (16 it + 4g + r >= mr) -> -inf, in S^T tiles.
+template <int TM>
+__device__ __forceinline__ void pad_mask_rows(f32x4 (&sacc)[TM], int mr) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int it = 0; it < TM; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * it + 4 * g + r >= mr) sacc[it][r] = -INFINITY;
+}
 
 constexpr int OUT_TOK = 128;                 // tokens per workgroup
 constexpr int OUT_WIN = OUT_TOK + 80;        // V window rows (t0-32 .. t0+176)
@@ -230,6 +242,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
         sacc[it] = mma<NS>(kf, qf[ks], sacc[it]);
       }
     }
+    if (a.mr < M) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < TM; ++it)
@@ -278,7 +291,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
       else
         conv_tile<NS, DMA>(vh, vl, OUT_VWLD, ts - t0, tap, oacc);
     }
-    store_row16<IO, DMA>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, oacc);
+    if (tok < a.n) store_row16<IO, DMA>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, oacc);
   }
 }
 
@@ -469,6 +482,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
       }
     }
     if (u + 2 < nunits) load_q16(Q, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
+    if (a.mr < M) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < TM; ++it)
@@ -504,7 +518,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
       }
     }
     if constexpr (CONV) conv_tile_ring(ring, t0, cl, tap, oacc);
-    u16* dst = ts < te ? O + (size_t)(ts + c16) * HD : junk + c16 * HD;
+    u16* dst = ts + c16 < te ? O + (size_t)(ts + c16) * HD : junk + c16 * HD;
     store_row16<u16, true>(dst, oacc);
   };
   int u = 0;

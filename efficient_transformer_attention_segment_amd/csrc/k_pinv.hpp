@@ -177,7 +177,9 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
       // tile (all of them at once would not fit the register budget)
       asm volatile("" ::: "memory");
     }
-    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15
+    // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15;
+    // padding columns take no weight and padding rows are zero
+    if (a.mr < M) pad_mask_cols(acc, a.mr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float mx = NEG_BIG;
@@ -192,7 +194,7 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
         s += p;
       }
       s = sum16(s);
-      const float inv = 1.0f / s;
+      const float inv = 16 * rt + 4 * g + r < a.mr ? 1.0f / s : 0.f;
       float rs = 0.f;
 #pragma unroll
       for (int ct = 0; ct < TM; ++ct) {

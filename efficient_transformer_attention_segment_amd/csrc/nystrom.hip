@@ -65,6 +65,7 @@ int fail(int code, const char* fmt, ...) {
 // ---------------------------------------------------------------- plan ---
 struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
+  int mr;       // landmarks of the method; m is mr rounded up to a multiple of 32
   bool record;  // keep every intermediate in the workspace (stage hook)
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
@@ -89,20 +90,28 @@ int pow2floor(int x) {
   return p;
 }
 
-Plan make_plan(int B, int H, int n, int m) {
+// Landmark count of the kernels: the method's m rounded up to a multiple of
+// 32.  The padding landmarks are zero rows of Qt and Kt, get no weight in
+// any softmax over landmarks and zero rows in A, so they stay zero through
+// the pseudo-inverse and contribute nothing to W or the output.
+int padded_m(int m) { return (m + 31) & ~31; }
+
+Plan make_plan(int B, int H, int n, int mr) {
   Plan p{};
+  const int m = padded_m(mr);
   p.B = B;
   p.H = H;
   p.n = n;
   p.m = m;
+  p.mr = mr;
   p.BH = B * H;
-  p.L = n / m;
+  p.L = n / mr;
   // landmark blocks: 8 threads per row, RS row slots per landmark, lpw landmarks per block
   p.RS = std::min(32, std::max(1, pow2floor(std::max(1, p.L / 8))));
   p.lpw = 32 / p.RS;
   // key chunks for the B V partials: as many blocks as stay resident in one
   // round next to the pseudo-inverse blocks (two blocks per CU)
-  p.ntiles = n / 32;
+  p.ntiles = (n + 31) / 32;  // the last tile is ragged when n % 32 != 0
   p.npinv = m <= 128 ? p.BH : 0;
   const int resident = 2 * 256;
   const int target = std::max(p.BH, resident - p.npinv);
@@ -235,6 +244,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   LandmarkArgs la;
   la.n = p.n;
   la.m = M;
+  la.mr = p.mr;
   la.L = p.L;
   la.RS = p.RS;
   la.lpw = p.lpw;
@@ -356,6 +366,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.n = p.n;
   oa.H = p.H;
   oa.lscale = s4;
+  oa.mr = p.mr;
   if constexpr (sizeof(IO) == 2) {
     // persistent output pass: a token range of one head per workgroup, sized
     // so the grid fills the CUs at the occupancy its LDS allows in at most
@@ -439,8 +450,7 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
   if ((long long)B * H > 65535) return fail(NYS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)B * H);
   if ((long long)n * HD >= (1LL << 31)) return fail(NYS_ERR_UNSUPPORTED, "n=%d too long", n);
   if (m != n) {
-    if (m % 32 != 0 || m > NYS_MAX_LANDMARKS)
-      return fail(NYS_ERR_UNSUPPORTED, "m=%d: landmarks must be a multiple of 32 up to 256", m);
+    if (m > NYS_MAX_LANDMARKS) return fail(NYS_ERR_UNSUPPORTED, "m=%d: at most 256 landmarks (unless m == n)", m);
     if (esize == 4 && m > 128) return fail(NYS_ERR_UNSUPPORTED, "m=%d: float32 I/O is built for m <= 128", m);
   }
   const size_t bytes = (size_t)B * H * n * d * esize;
@@ -461,7 +471,7 @@ int run(const void* q, const void* k, const void* v, const uint8_t* mask, const 
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
   if (rc != NYS_OK) return rc;
-  rc = dispatch_m<IO>(m, p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+  rc = dispatch_m<IO>(p.m, p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
   if (wout) *wout = w;
   if (pout) *pout = p;
   return rc;
@@ -500,7 +510,7 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16(const uint16_t
 __attribute__((visibility("default"))) size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m) {
   if (B <= 0 || H <= 0 || n <= 0 || d != HD || m <= 0 || m > n || n % m != 0) return 0;
   if (m == n) return 0;
-  if (m % 32 != 0 || m > NYS_MAX_LANDMARKS) return 0;
+  if (m > NYS_MAX_LANDMARKS) return 0;
   return make_plan(B, H, n, m).total;
 }
 
@@ -532,18 +542,31 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     if (rc != NYS_OK) return rc;
     HIP_TRY(hipStreamSynchronize(stream));
     std::lock_guard<std::mutex> lk(g_mu);
-    const size_t BH = p.BH, M = m;
+    const size_t BH = p.BH, M = p.m, mr = p.mr;  // workspace rows M, caller rows mr
     // after n_iter > 0 with m > 128 the final iterate lives in one of two buffers
     size_t zoff = p.off_Z;
-    if (m > 128 && (n_iter % 2) == 1) zoff = p.off_Z2;
-    struct Cp {
-      void* dst;
-      size_t off, bytes;
-    } cps[] = {{qt, p.off_qt, BH * M * HD * 4}, {kt, p.off_kt, BH * M * HD * 4}, {a, p.off_A, BH * M * M * 4},
-               {cscale, p.off_cscale, BH * 4},  {z, zoff, BH * M * M * 4},     {bv, p.off_BV, BH * M * HD * 4},
-               {wout, p.off_W, BH * M * HD * 4}};
-    for (const Cp& c : cps)
-      if (c.dst) HIP_TRY(hipMemcpyAsync(c.dst, w->buf + c.off, c.bytes, hipMemcpyDeviceToDevice, stream));
+    if (M > 128 && (n_iter % 2) == 1) zoff = p.off_Z2;
+    char* const base = static_cast<char*>(w->buf);
+    // [BH][M][64] -> [BH][mr][64]
+    struct Rows {
+      float* dst;
+      size_t off;
+    } rows[] = {{qt, p.off_qt}, {kt, p.off_kt}, {bv, p.off_BV}, {wout, p.off_W}};
+    for (const Rows& r : rows)
+      if (r.dst)
+        HIP_TRY(hipMemcpy2DAsync(r.dst, mr * HD * 4, base + r.off, M * HD * 4, mr * HD * 4, BH,
+                                 hipMemcpyDeviceToDevice, stream));
+    // [BH][M][M] -> [BH][mr][mr]
+    struct Mats {
+      float* dst;
+      size_t off;
+    } mats[] = {{a, p.off_A}, {z, zoff}};
+    for (const Mats& mt : mats)
+      if (mt.dst)
+        for (size_t h = 0; h < BH; ++h)
+          HIP_TRY(hipMemcpy2DAsync(mt.dst + h * mr * mr, mr * 4, base + mt.off + h * M * M * 4, M * 4, mr * 4, mr,
+                                   hipMemcpyDeviceToDevice, stream));
+    if (cscale) HIP_TRY(hipMemcpyAsync(cscale, base + p.off_cscale, BH * 4, hipMemcpyDeviceToDevice, stream));
     HIP_TRY(hipStreamSynchronize(stream));
     return NYS_OK;
   } catch (...) {

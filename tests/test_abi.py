@@ -70,7 +70,6 @@ def call(lib, fn="nystrom_attention", q=FAKE, k=FAKE, v=FAKE, out=FAKE2, B=1, H=
     (dict(init=2), -1),
     (dict(out=FAKE), -1),              # out aliases q, k, v
     (dict(d=32, n=256), -2),           # only d = 64 is built
-    (dict(m=48, n=480), -2),           # m not a multiple of 32
     (dict(m=512, n=1024), -2),         # m above 256 (and not n)
     (dict(B=300, H=300), -2),          # B*H above the grid limit
 ])
@@ -100,6 +99,9 @@ def test_workspace_bytes(lib):
     assert w(1, 2, 256, 32, 64) == 0      # unsupported d
     assert w(1, 2, 250, 64, 64) == 0      # n % m
     assert w(1, 2, 256, 64, 256) == 0     # exact branch needs no workspace
+    # any landmark count up to 256 (padded to a multiple of 32 inside)
+    assert w(1, 2, 480, 64, 48) > 0 and w(1, 2, 400, 64, 50) > 0 and w(1, 2, 64, 64, 1) > 0
+    assert w(1, 2, 1200, 64, 300) == 0    # above 256 landmarks
     # fits easily on one GPU at the largest workload
     assert w(1, 4, 65536, 64, 256) < 64 << 20
 

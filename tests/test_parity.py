@@ -74,6 +74,23 @@ def test_landmark_counts(dtype, m, n):
     _check(f"m{m}-n{n}-init1-noconv", x, dtype, m, 6, 1, conv=False)
 
 
+@pytest.mark.parametrize("dtype,m,n", [
+    ("fp32", 16, 256), ("fp32", 7, 224), ("fp32", 100, 400), ("fp32", 1, 64), ("fp32", 5, 200),
+    ("bf16", 48, 480), ("bf16", 50, 400), ("bf16", 144, 576), ("bf16", 200, 1000), ("bf16", 3, 96),
+    ("bf16", 11, 440),
+])
+def test_unpadded_landmark_counts(dtype, m, n):
+    """Landmark counts that are not multiples of 32 (padded inside to the
+    next one with landmarks that take no weight): multiples of 16, odd
+    counts, a single landmark; and with them sequence lengths that are not
+    multiples of 32 or 16 (a ragged last key tile and output tile)."""
+    x = make_custom(2, 2, n, 64, seed=720 + m + n, dtype=dtype, lengths=[n, n - n // 4])
+    _check(f"m{m}-n{n}", x, dtype, m, 6, 0)
+    _check(f"m{m}-n{n}-init1-noconv", x, dtype, m, 6, 1, conv=False)
+    y = make_custom(1, 3, n, 64, seed=721 + m + n, dtype=dtype, scale=4.0, lengths=None)
+    _check(f"m{m}-n{n}-peaked", y, dtype, m, 6, 0, conv=False)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_many_heads(dtype):
     """More (batch, head) pairs than the fused Gram rendezvous allows (the

@@ -4,7 +4,7 @@ oracle's own intermediates."""
 import numpy as np
 import pytest
 
-from efficient_transformer_attention_segment_amd.workloads import WORKLOADS, make_inputs
+from efficient_transformer_attention_segment_amd.workloads import WORKLOADS, make_custom, make_inputs
 from gpu_util import announce, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -45,5 +45,30 @@ def test_stages(idx, peak):
                 W=_rel(got["W"], ref["W"]))
     announce("  " + " ".join(f"{k2}={v2:.2e}" for k2, v2 in errs.items()))
     tol = STAGE_TOL[w.dtype]
+    bad = {k2: v2 for k2, v2 in errs.items() if not v2 < tol[k2]}
+    assert not bad, f"stage errors above tolerance: {bad}"
+
+
+@pytest.mark.parametrize("dtype,m,n", [("fp32", 48, 480), ("bf16", 50, 400), ("bf16", 144, 576)])
+def test_stages_padded_landmarks(dtype, m, n):
+    """Landmark counts padded inside to a multiple of 32: the hook returns
+    the m-landmark intermediates (the padding never shows) and they match
+    the oracle's."""
+    import torch
+
+    import efficient_transformer_attention_segment_amd as nys
+    from oracle import nystrom_oracle as O
+    x = make_custom(2, 2, n, 64, seed=730 + m, dtype=dtype, lengths=[n, n // 2])
+    announce(f"stages {dtype} m{m} n{n}")
+    q, k, v = (to_dev(x[n2], dtype) for n2 in ("q", "k", "v"))
+    _, st = nys.debug_stages(q, k, v, to_dev(x["key_mask"], None), to_dev(x["conv_w"], None), m=m, n_iter=6,
+                             init_option=0)
+    torch.cuda.synchronize()
+    _, ref = O.nystrom_attention(x["q"], x["k"], x["v"], x["key_mask"], x["conv_w"], m, 6, 0, return_stages=True)
+    got = {k2: t.double().cpu().numpy() for k2, t in st.items()}
+    assert got["A"].shape == (2, 2, m, m) and got["Z"].shape == (2, 2, m, m) and got["BV"].shape == (2, 2, m, 64)
+    errs = {k2: _rel(got[k2], ref[k2]) for k2 in ("qt", "kt", "A", "Z", "BV", "W")}
+    announce("  " + " ".join(f"{k2}={v2:.2e}" for k2, v2 in errs.items()))
+    tol = STAGE_TOL[dtype]
     bad = {k2: v2 for k2, v2 in errs.items() if not v2 < tol[k2]}
     assert not bad, f"stage errors above tolerance: {bad}"
