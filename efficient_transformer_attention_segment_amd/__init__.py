@@ -48,6 +48,10 @@ def _load():
     lib.nystrom_attention.restype = _I
     lib.nystrom_attention_bf16.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]
     lib.nystrom_attention_bf16.restype = _I
+    lib.nystrom_attention_conv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.nystrom_attention_conv.restype = _I
+    lib.nystrom_attention_bf16_conv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.nystrom_attention_bf16_conv.restype = _I
     lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
     lib.nystrom_last_error.argtypes = []
@@ -99,16 +103,31 @@ def _raw_call(fn, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream
               init_option, _ptr(out), _stream(stream))
 
 
+def _raw_call_conv(fn, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
+    """The same call with conv_w's kernel size (its last dimension) passed."""
+    B, H, n, d = q.shape
+    return fn(_ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w), int(conv_w.shape[-1]), B, H, n,
+              d, m, n_iter, init_option, _ptr(out), _stream(stream))
+
+
+def _call(name, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
+    lib = _load()
+    if conv_w is None or conv_w.shape[-1] == CONV_TAPS:
+        return _raw_call(getattr(lib, name), q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream)
+    return _raw_call_conv(getattr(lib, name + "_conv"), q, k, v, key_mask, conv_w, m, n_iter, init_option,
+                          out, stream)
+
+
 def nystrom_attention(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,
                       out=None, stream=None):
     """float32 [B,H,n,64] CUDA tensors -> out (allocated when None).
-    key_mask: uint8 [B,n] (1 keeps a key) or None; conv_w: float32 [H,65] or
-    None.  Enqueued on ``stream`` (default: torch's current stream)."""
+    key_mask: uint8 [B,n] (1 keeps a key) or None; conv_w: float32 [H,K]
+    (K odd, up to 65; the pages' default is 65) or None.  Enqueued on
+    ``stream`` (default: torch's current stream)."""
     import torch
     if out is None:
         out = torch.empty_like(q)
-    _check(_raw_call(_load().nystrom_attention, q, k, v, key_mask, conv_w, m, n_iter, init_option,
-                     out, stream))
+    _check(_call("nystrom_attention", q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream))
     return out
 
 
@@ -118,8 +137,7 @@ def nystrom_attention_bf16(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, 
     import torch
     if out is None:
         out = torch.empty_like(q)
-    _check(_raw_call(_load().nystrom_attention_bf16, q, k, v, key_mask, conv_w, m, n_iter,
-                     init_option, out, stream))
+    _check(_call("nystrom_attention_bf16", q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream))
     return out
 
 

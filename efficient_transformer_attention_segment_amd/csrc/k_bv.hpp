@@ -471,7 +471,8 @@ struct ExactArgs {
   const void* k;
   const void* v;
   const uint8_t* key_mask;
-  const float* conv_w;  // [H][65] or null
+  const float* conv_w;  // [H][conv_k] or null
+  int conv_k;           // odd taps, 1 .. 65
   void* out;
   int n, H;
   float lscale;  // 1 / sqrt(d)
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
     stage_v_window<IO>(V, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
     __syncthreads();
     Frag2 tap[3];
-    conv_taps(a.conv_w + (size_t)h * TAPS, tap);
+    conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
     conv_tile<NS, false>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
   }
   if (tok < a.n) store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, acc[0]);

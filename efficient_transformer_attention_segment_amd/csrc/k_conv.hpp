@@ -96,16 +96,19 @@ __device__ void stage_v_window(const IO* __restrict__ V, int n, int t0, int win,
   }
 }
 
-// The three Toeplitz B fragments of this lane for head weights w[0..64].
-__device__ __forceinline__ void conv_taps(const float* __restrict__ w, Frag2 (&tap)[3]) {
+// The three Toeplitz B fragments of this lane for head weights w[0..K-1],
+// K odd, 1 <= K <= 65: window offset j (token t + j - 32) takes tap
+// j - 32 + K / 2, zero outside [0, K); K = 65 is the pages' default.
+__device__ __forceinline__ void conv_taps(const float* __restrict__ w, int K, Frag2 (&tap)[3]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int shift = K / 2 - HALO;
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = 32 * kk + 8 * g + e - c16;
-      x[e] = (j >= 0 && j < TAPS) ? w[j] : 0.f;
+      const int j = 32 * kk + 8 * g + e - c16 + shift;
+      x[e] = (j >= 0 && j < K) ? w[j] : 0.f;
     }
     tap[kk] = split8(x);
   }

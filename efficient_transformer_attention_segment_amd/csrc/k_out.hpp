@@ -30,7 +30,8 @@ struct OutArgs {
   const void* q;
   const void* v;
   const __bf16* zero;    // >= 128 zero bytes (rows outside the sequence)
-  const float* conv_w;   // [H][65] or null
+  const float* conv_w;   // [H][conv_k] or null
+  int conv_k;            // odd taps, 1 .. 65
   const __bf16* kt_hi;   // [BH][M][64]
   const __bf16* kt_lo;
   const __bf16* wf_hi;   // [BH][4][M/32][64][8]
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   int coff[2][4];
   if constexpr (DMA) conv_dma_offsets(coff);
   Frag2 tap[3];
-  if (a.conv_w != nullptr) conv_taps(a.conv_w + (size_t)h * TAPS, tap);
+  if (a.conv_w != nullptr) conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
   if constexpr (DMA) {
     wait_vmcnt<0>();
     barrier_only();
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
   load_q16(Q, a.n, tb + 16 * wave + c16, qb[0]);
   if (nunits > 1) load_q16(Q, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
   Frag2 tap[3];
-  if constexpr (CONV) conv_taps(a.conv_w + (size_t)h * TAPS, tap);
+  if constexpr (CONV) conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
   wait_vmcnt<0>();  // the landmark / fragment copies (the register loads are tracked by the compiler)
   __syncthreads();
 

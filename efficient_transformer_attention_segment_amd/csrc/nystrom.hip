@@ -238,7 +238,7 @@ hipError_t allow_lds(F* fn, size_t bytes) {
 // --------------------------------------------------------- launches ---
 template <typename IO, int M>
 int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
-                   const uint8_t* mask, const float* conv_w, int n_iter, int init_option, void* out,
+                   const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
                    hipStream_t st) {
   const float s4 = 1.0f / sqrtf(sqrtf((float)HD));
   LandmarkArgs la;
@@ -358,6 +358,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.v = v;
   oa.zero = at<__bf16>(w, p.off_zero);
   oa.conv_w = conv_w;
+  oa.conv_k = conv_k;
   oa.kt_hi = la.kt_hi;
   oa.kt_lo = la.kt_lo;
   oa.wf_hi = ma.wf_hi;
@@ -392,13 +393,14 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
 
 template <typename IO>
 int launch_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
-                 const float* conv_w, void* out, hipStream_t st) {
+                 const float* conv_w, int conv_k, void* out, hipStream_t st) {
   ExactArgs ea;
   ea.q = q;
   ea.k = k;
   ea.v = v;
   ea.key_mask = mask;
   ea.conv_w = conv_w;
+  ea.conv_k = conv_k;
   ea.out = out;
   ea.n = n;
   ea.H = H;
@@ -411,20 +413,21 @@ int launch_exact(int B, int H, int n, const void* q, const void* k, const void* 
 
 template <typename IO>
 int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
-               const uint8_t* mask, const float* conv_w, int n_iter, int init_option, void* out, hipStream_t st) {
+               const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
+               hipStream_t st) {
   switch (m) {
-    case 32: return launch_nystrom<IO, 32>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-    case 64: return launch_nystrom<IO, 64>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-    case 96: return launch_nystrom<IO, 96>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-    case 128: return launch_nystrom<IO, 128>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+    case 32: return launch_nystrom<IO, 32>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+    case 64: return launch_nystrom<IO, 64>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+    case 96: return launch_nystrom<IO, 96>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+    case 128: return launch_nystrom<IO, 128>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
     default: break;
   }
   if constexpr (sizeof(IO) == 2) {
     switch (m) {
-      case 160: return launch_nystrom<IO, 160>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-      case 192: return launch_nystrom<IO, 192>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-      case 224: return launch_nystrom<IO, 224>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
-      case 256: return launch_nystrom<IO, 256>(p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+      case 160: return launch_nystrom<IO, 160>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+      case 192: return launch_nystrom<IO, 192>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+      case 224: return launch_nystrom<IO, 224>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+      case 256: return launch_nystrom<IO, 256>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
       default: break;
     }
   }
@@ -460,18 +463,24 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
 }
 
 template <typename IO>
-int run(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int B, int H, int n,
+int run(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k, int B,
+        int H, int n,
         int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout) {
   int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
   if (rc != NYS_OK) return rc;
-  if (m == n) return launch_exact<IO>(B, H, n, q, k, v, mask, conv_w, out, st);
+  if (conv_w != nullptr) {
+    if (conv_k < 1 || conv_k % 2 == 0)
+      return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
+    if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
+  }
+  if (m == n) return launch_exact<IO>(B, H, n, q, k, v, mask, conv_w, conv_k, out, st);
   Plan p = make_plan(B, H, n, m);
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
   if (rc != NYS_OK) return rc;
-  rc = dispatch_m<IO>(p.m, p, w, q, k, v, mask, conv_w, n_iter, init_option, out, st);
+  rc = dispatch_m<IO>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
   if (wout) *wout = w;
   if (pout) *pout = p;
   return rc;
@@ -488,7 +497,8 @@ __attribute__((visibility("default"))) int nystrom_attention(const float* q, con
                                                              struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<float>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, nullptr, nullptr);
+    return run<float>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+                      nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
   }
@@ -501,7 +511,37 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16(const uint16_t
                                                                   struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<u16>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, nullptr, nullptr);
+    return run<u16>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+                    nullptr);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_conv(const float* q, const float* k, const float* v,
+                                                                  const uint8_t* key_mask, const float* conv_w,
+                                                                  int conv_kernel_size, int B, int H, int n, int d,
+                                                                  int m, int n_iter, int init_option, float* out,
+                                                                  struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    return run<float>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option, out, stream,
+                      nullptr, nullptr);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_bf16_conv(const uint16_t* q, const uint16_t* k,
+                                                                       const uint16_t* v, const uint8_t* key_mask,
+                                                                       const float* conv_w, int conv_kernel_size,
+                                                                       int B, int H, int n, int d, int m, int n_iter,
+                                                                       int init_option, uint16_t* out,
+                                                                       struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    return run<u16>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option, out, stream,
+                    nullptr, nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
   }
@@ -537,8 +577,9 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     if (m == n) return fail(NYS_ERR_INVALID, "stages exist only on the Nystrom path (m != n)");
     Workspace* w = nullptr;
     Plan p{};
-    int rc = dtype == 0 ? run<float>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
-                        : run<u16>(q, k, v, key_mask, conv_w, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
+    int rc = dtype == 0
+                 ? run<float>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
+                 : run<u16>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
     if (rc != NYS_OK) return rc;
     HIP_TRY(hipStreamSynchronize(stream));
     std::lock_guard<std::mutex> lk(g_mu);

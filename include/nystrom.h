@@ -91,6 +91,26 @@ int nystrom_attention_bf16(const uint16_t* q, const uint16_t* k,
                            int m, int n_iter, int init_option, uint16_t* out,
                            struct ihipStream_t* stream);
 
+/* The same two operations with the depthwise convolution's kernel size as
+ * an argument (the pages' conv_kernel_size, [P1] 2.6 and 3.1; the calls
+ * above fix it at 65).  conv_w is float32 [H, conv_kernel_size]: tap j
+ * multiplies V at token offset j - conv_kernel_size / 2, zero outside
+ * [0, n).  conv_kernel_size is read only when conv_w is not NULL.
+ * Errors: those of nystrom_attention[_bf16], plus NYS_ERR_INVALID for an
+ * even or non-positive conv_kernel_size ('same' padding needs a centre tap)
+ * and NYS_ERR_UNSUPPORTED above 65 taps. */
+int nystrom_attention_conv(const float* q, const float* k, const float* v,
+                           const uint8_t* key_mask, const float* conv_w,
+                           int conv_kernel_size, int B, int H, int n, int d,
+                           int m, int n_iter, int init_option, float* out,
+                           struct ihipStream_t* stream);
+int nystrom_attention_bf16_conv(const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const uint8_t* key_mask,
+                                const float* conv_w, int conv_kernel_size,
+                                int B, int H, int n, int d, int m, int n_iter,
+                                int init_option, uint16_t* out,
+                                struct ihipStream_t* stream);
+
 /* Bytes of device workspace a call of this shape uses (0 for invalid or
  * unsupported shapes). */
 size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);

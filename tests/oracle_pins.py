@@ -301,16 +301,20 @@ def pin_conv_direct(O):
 def pin_conv_library(O):
     """The same convolution through torch.nn.functional.conv1d (groups = H,
     padding = K//2, float64), a library routine with Conv2d's (K,1) semantics
-    along the sequence."""
+    along the sequence; at the default 65 taps and at other odd kernel sizes
+    (the conv_kernel_size field, [P1] 3.1)."""
     rng = RNG(12)
-    B, H, n, d, K = 2, 3, 100, 4, 65
-    v = rng.standard_normal((B, H, n, d))
-    w = rng.standard_normal((H, K))
-    got = O.depthwise_conv_same(v, w)
-    x = torch.from_numpy(v).permute(0, 3, 1, 2).reshape(B * d, H, n)
-    y = torch.nn.functional.conv1d(x, torch.from_numpy(w)[:, None, :], padding=K // 2, groups=H)
-    ref = y.reshape(B, d, H, n).permute(0, 2, 3, 1).numpy()
-    return _rel(got, ref)
+    B, H, n, d = 2, 3, 100, 4
+    err = 0.0
+    for K in (65, 1, 3, 31):
+        v = rng.standard_normal((B, H, n, d))
+        w = rng.standard_normal((H, K))
+        got = O.depthwise_conv_same(v, w)
+        x = torch.from_numpy(v).permute(0, 3, 1, 2).reshape(B * d, H, n)
+        y = torch.nn.functional.conv1d(x, torch.from_numpy(w)[:, None, :], padding=K // 2, groups=H)
+        ref = y.reshape(B, d, H, n).permute(0, 2, 3, 1).numpy()
+        err = max(err, _rel(got, ref))
+    return err
 
 
 def pin_conv_delta(O):

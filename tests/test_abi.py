@@ -79,6 +79,17 @@ def test_invalid_arguments(lib, fn, kw, code):
     assert lib.nystrom_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("fn", ["nystrom_attention_conv", "nystrom_attention_bf16_conv"])
+@pytest.mark.parametrize("ksize,code", [(4, -1), (0, -1), (-3, -1), (67, -2), (129, -2)])
+def test_conv_kernel_size_validation(lib, fn, ksize, code):
+    """Odd kernel sizes 1 .. 65 only; checked on the host before any launch
+    (every other argument here is valid, so only this check can fail)."""
+    f = getattr(lib, fn)
+    rc = f(FAKE, FAKE, FAKE, NULL, FAKE, ksize, 1, 2, 256, 64, 64, 6, 0, FAKE2, NULL)
+    assert rc == code
+    assert "conv_kernel_size" in lib.nystrom_last_error().decode()
+
+
 def test_fp32_large_m_unsupported(lib):
     assert call(lib, "nystrom_attention", n=512, m=256) == -2
     # the bf16 entry point accepts it (validation passes; not launched here)

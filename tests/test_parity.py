@@ -92,6 +92,18 @@ def test_unpadded_landmark_counts(dtype, m, n):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("ksize", [1, 3, 7, 33, 63])
+def test_conv_kernel_sizes(dtype, ksize):
+    """The conv_kernel_size argument (odd, up to 65) on both branches: the
+    Nystrom path (output kernels) and the exact branch."""
+    x = make_custom(2, 2, 512, 64, seed=740 + ksize, dtype=dtype, lengths=[512, 300], taps=ksize)
+    assert x["conv_w"].shape == (2, ksize)
+    _check(f"conv{ksize}", x, dtype, 64, 6, 0)
+    y = make_custom(1, 2, 200, 64, seed=741 + ksize, dtype=dtype, lengths=[150], taps=ksize)
+    _check(f"conv{ksize}-exact", y, dtype, 200, 6, 0)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_many_heads(dtype):
     """More (batch, head) pairs than the fused Gram rendezvous allows (the
     original init then takes the separate Gram launch), ragged masks, both
