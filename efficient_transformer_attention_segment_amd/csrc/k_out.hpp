@@ -66,9 +66,13 @@ struct OutLayout {
   static constexpr int WF_ELEMS = 4 * KS * 64 * 8;         // per part
   static constexpr int V_ELEMS = HD * OUT_VWLD;            // per part
   static constexpr int PARTS = NS == 3 ? 2 : 1;
+  // the W^T fragments are staged in LDS when everything fits the 160 KB;
+  // otherwise (float32 I/O above 192 landmarks) they are read from global
+  // memory (L2: every workgroup of the head reads the same fragments)
+  static constexpr bool WF_LDS = 2 * PARTS * (KT_ELEMS + WF_ELEMS + V_ELEMS) <= 160 * 1024;
   static constexpr int OFF_KT = 0;
   static constexpr int OFF_WF = OFF_KT + PARTS * KT_ELEMS;
-  static constexpr int OFF_V = OFF_WF + PARTS * WF_ELEMS;
+  static constexpr int OFF_V = OFF_WF + (WF_LDS ? PARTS * WF_ELEMS : 0);
   static constexpr int TOTAL = OFF_V + PARTS * V_ELEMS;
   static constexpr int LDS_BYTES = TOTAL * 2;
 };
@@ -161,8 +165,12 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
 
   __bf16* kth = lds_dyn + Ly::OFF_KT;
   __bf16* ktl = kth + Ly::KT_ELEMS;
-  __bf16* wfh = lds_dyn + Ly::OFF_WF;
-  __bf16* wfl = wfh + Ly::WF_ELEMS;
+  const __bf16* const wsh = a.wf_hi + (size_t)bh * Ly::WF_ELEMS;
+  const __bf16* const wsl = a.wf_lo + (size_t)bh * Ly::WF_ELEMS;
+  __bf16* const wfh_lds = lds_dyn + Ly::OFF_WF;
+  __bf16* const wfl_lds = wfh_lds + Ly::WF_ELEMS;
+  const __bf16* const wfh = Ly::WF_LDS ? wfh_lds : wsh;
+  const __bf16* const wfl = Ly::WF_LDS ? wfl_lds : wsl;
   __bf16* vh = lds_dyn + Ly::OFF_V;
   __bf16* vl = vh + Ly::V_ELEMS;
 
@@ -182,12 +190,12 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
         *reinterpret_cast<bf16x8*>(ktl + row * Ly::KLD + 8 * cc) =
             *reinterpret_cast<const bf16x8*>(src_l + (size_t)row * HD + 8 * cc);
     }
-    const __bf16* wsh = a.wf_hi + (size_t)bh * Ly::WF_ELEMS;
-    const __bf16* wsl = a.wf_lo + (size_t)bh * Ly::WF_ELEMS;
-    for (int idx = threadIdx.x; idx < Ly::WF_ELEMS / 8; idx += 256) {
-      *reinterpret_cast<bf16x8*>(wfh + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsh + 8 * idx);
-      if constexpr (NS == 3)
-        *reinterpret_cast<bf16x8*>(wfl + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsl + 8 * idx);
+    if constexpr (Ly::WF_LDS) {
+      for (int idx = threadIdx.x; idx < Ly::WF_ELEMS / 8; idx += 256) {
+        *reinterpret_cast<bf16x8*>(wfh_lds + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsh + 8 * idx);
+        if constexpr (NS == 3)
+          *reinterpret_cast<bf16x8*>(wfl_lds + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsl + 8 * idx);
+      }
     }
     if (a.conv_w != nullptr) stage_v_window<IO>(V, a.n, t0, OUT_WIN, vh, vl, OUT_VWLD);
   }

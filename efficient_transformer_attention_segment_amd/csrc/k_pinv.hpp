@@ -25,7 +25,8 @@
 //
 // k_pinv_init / k_pinv_gemm (M > 128): the same iteration as a sequence of
 //   batched launches, one product per launch, with the matrices in global
-//   memory; the kernel boundaries are the step barriers.
+//   memory; the kernel boundaries are the step barriers.  Float32 products
+//   for float32 I/O, split-bf16 for bf16 I/O.
 #pragma once
 
 #include <type_traits>
@@ -884,7 +885,9 @@ __global__ __launch_bounds__(256) void k_pinv_init(PinvArgs a, int M) {
 }
 
 // C = alpha * P * Q' with Q' = Q when beta == 0, else beta * I - Q.
-// grid: ((M/32)^2, BH), block 256 (4 waves, one 16x16 tile each).
+// grid: ((M/32)^2, BH), block 256 (4 waves, one 16x16 tile each).  F32:
+// float32 matrix-core products (float32 I/O), else split-bf16 products.
+template <bool F32>
 __global__ __launch_bounds__(256) void k_pinv_gemm(const float* __restrict__ P, const float* __restrict__ Q,
                                                     float* __restrict__ C, int M, float beta, float alpha) {
   const int bh = blockIdx.y;
@@ -905,7 +908,10 @@ __global__ __launch_bounds__(256) void k_pinv_gemm(const float* __restrict__ P, 
       const float qv = Qm[(size_t)k * M + col0 + c16];
       y[e] = beta != 0.f ? ((k == col0 + c16 ? beta : 0.f) - qv) : qv;
     }
-    acc = mma<3>(split8(x), split8(y), acc);
+    if constexpr (F32)
+      acc = mma8_f32(x, y, acc);
+    else
+      acc = mma<3>(split8(x), split8(y), acc);
   }
   float* Cm = C + (size_t)bh * M * M;
 #pragma unroll

@@ -317,13 +317,13 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     float* T2 = at<float>(w, p.off_T2);
     const dim3 gg((M / 32) * (M / 32), p.BH);
     for (int it = 0; it < n_iter; ++it) {
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X, M,
                      0.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1, M,
                      7.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2, M,
                      15.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn, M,
                      13.f, 0.25f));
       std::swap(Zc, Zn);
     }
@@ -422,7 +422,7 @@ int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k,
     case 128: return launch_nystrom<IO, 128>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
     default: break;
   }
-  if constexpr (sizeof(IO) == 2) {
+  {
     switch (m) {
       case 160: return launch_nystrom<IO, 160>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
       case 192: return launch_nystrom<IO, 192>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
@@ -454,7 +454,6 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
   if ((long long)n * HD >= (1LL << 31)) return fail(NYS_ERR_UNSUPPORTED, "n=%d too long", n);
   if (m != n) {
     if (m > NYS_MAX_LANDMARKS) return fail(NYS_ERR_UNSUPPORTED, "m=%d: at most 256 landmarks (unless m == n)", m);
-    if (esize == 4 && m > 128) return fail(NYS_ERR_UNSUPPORTED, "m=%d: float32 I/O is built for m <= 128", m);
   }
   const size_t bytes = (size_t)B * H * n * d * esize;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))

@@ -30,8 +30,8 @@
  *   - conv_w is a DEVICE pointer to float32 [H, 65] (tap j multiplies V at
  *     token offset j - 32, zero outside [0, n); one filter per head shared
  *     by all d columns).  NULL disables the convolution ([P1] 2.6).
- *   - d must be 64; 1 <= m <= 256 with n % m == 0 (m <= 128 for float32
- *     I/O), unless m == n (exact branch, any n >= 1).  Internally the
+ *   - d must be 64; 1 <= m <= 256 with n % m == 0, unless m == n (exact
+ *     branch, any n >= 1).  Internally the
  *     landmarks are padded to a multiple of 32 with landmarks that take no
  *     weight anywhere, so any m in range gives the m-landmark result.
  *   - init_option 0 ("original", the default): c = (max column sum of A) *
@@ -73,7 +73,7 @@ enum { NYS_HEAD_DIM = 64, NYS_CONV_TAPS = 65, NYS_MAX_LANDMARKS = 256 };
 /* Nystrom attention, float32 q/k/v/out ([P1] 2.2-2.6; [P2] mask).
  * Errors: NYS_ERR_INVALID for NULL q/k/v/out, B/H/n/d/m <= 0, n % m != 0,
  * m > n, n_iter < 0, init_option not 0/1, out overlapping q/k/v;
- * NYS_ERR_UNSUPPORTED for d != 64, m > 128 when m != n, or sizes whose
+ * NYS_ERR_UNSUPPORTED for d != 64, m > 256 when m != n, or sizes whose
  * element counts overflow 2^31 per head;
  * NYS_ERR_HIP when a HIP call fails. */
 int nystrom_attention(const float* q, const float* k, const float* v,

@@ -90,9 +90,9 @@ def test_conv_kernel_size_validation(lib, fn, ksize, code):
     assert "conv_kernel_size" in lib.nystrom_last_error().decode()
 
 
-def test_fp32_large_m_unsupported(lib):
-    assert call(lib, "nystrom_attention", n=512, m=256) == -2
-    # the bf16 entry point accepts it (validation passes; not launched here)
+@pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
+def test_landmarks_above_256_unsupported(lib, fn):
+    assert call(lib, fn, n=600, m=300) == -2
 
 
 def test_debug_stages_rejects_exact_branch_and_bad_dtype(lib):

@@ -76,6 +76,7 @@ def test_landmark_counts(dtype, m, n):
 
 @pytest.mark.parametrize("dtype,m,n", [
     ("fp32", 16, 256), ("fp32", 7, 224), ("fp32", 100, 400), ("fp32", 1, 64), ("fp32", 5, 200),
+    ("fp32", 160, 640), ("fp32", 200, 800), ("fp32", 256, 1024), ("fp32", 150, 450),
     ("bf16", 48, 480), ("bf16", 50, 400), ("bf16", 144, 576), ("bf16", 200, 1000), ("bf16", 3, 96),
     ("bf16", 11, 440),
 ])
