@@ -346,7 +346,7 @@ constexpr int bv_waves() {
 // take alternate key tiles (KP = 2), both tiles of a pair in the same
 // barrier step, and fold their online-softmax states together in LDS at
 // the end.
-template <typename IO, int M>
+template <typename IO, int M, bool EDGE>
 __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   constexpr int TM = M / 16;
   constexpr int NW = bv_waves<M>();
@@ -394,8 +394,9 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
       kv_stream_dma<TPW, NW, true, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
     else
       kv_stream_dma<TPW, NW, false, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
-    if (tfull < tile1)
-      kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+    if constexpr (EDGE)
+      if (tfull < tile1)
+        kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   } else {
     kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   }
@@ -444,22 +445,25 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
 
 // Blocks [0, npinv) run the fused pseudo-inverse (one per head); the rest
 // run B V partials for (head, chunk).  Dynamic LDS = max of the two.
-template <typename IO, int M>
+// EDGE: some padding landmarks (m not a multiple of 32) or a ragged last
+// key tile (n not a multiple of 32); the code for them is compiled only into
+// this instance, so the common shapes pay nothing for it.
+template <typename IO, int M, bool EDGE>
 __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
     if constexpr (M <= 128) {
       if constexpr (sizeof(IO) == 4)
-        pinv_block_f32<M>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
+        pinv_block_f32<M, EDGE>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
       else if (pa.f16)
-        pinv_block<M, true>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
+        pinv_block<M, true, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
       else
-        pinv_block<M, false>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
+        pinv_block<M, false, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
     }
     return;
   }
   const int id = blockIdx.x - npinv;
-  bv_block<IO, M>(ba, id / ba.S, id % ba.S, lds_dyn);
+  bv_block<IO, M, EDGE>(ba, id / ba.S, id % ba.S, lds_dyn);
 }
 
 // ---------------------------------------------------------------------------

@@ -76,7 +76,7 @@ struct OutLayout {
   static constexpr int LDS_BYTES = TOTAL * 2;
 };
 
-template <typename IO, int M>
+template <typename IO, int M, bool PAD>
 __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   using Ly = OutLayout<IO, M>;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
         sacc[it] = mma<NS>(kf, qf[ks], sacc[it]);
       }
     }
-    if (a.mr < M) pad_mask_rows(sacc, a.mr);
+    if constexpr (PAD) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < TM; ++it)
@@ -314,7 +314,7 @@ __device__ __forceinline__ void load_q16(const u16* Q, int n, int tok, bf16x8 (&
 // [x R, min(n, (x + 1) R)), R a multiple of 64.  junk: >= 16 * 64 bf16, the
 // destination of tiles past the range.  Two Q register buffers alternate
 // between even and odd units (loaded two units before use).
-template <int M, bool CONV>
+template <int M, bool CONV, bool PAD>
 __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk) {
   using Ly = OutStreamLayout<M>;
   constexpr int KS = Ly::KS, TM = M / 16;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
       }
     }
     if (u + 2 < nunits) load_q16(Q, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
-    if (a.mr < M) pad_mask_rows(sacc, a.mr);
+    if constexpr (PAD) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll
     for (int it = 0; it < TM; ++it)

@@ -91,7 +91,7 @@ struct ProLayout {
 // float32 Qt, Kt for float32 I/O (float32 products), and for bf16 I/O the
 // bf16 hi / lo planes the landmark kernel already wrote (split-bf16
 // products with no conversion work here).
-template <int M, bool F32, int NW, class Ly>
+template <int M, bool F32, int NW, class Ly, bool PAD>
 __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
   constexpr int TM = M / 16, QLD = Ly::QLD, ALD = Ly::ALD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -179,8 +179,8 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
       asm volatile("" ::: "memory");
     }
     // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15;
-    // padding columns take no weight and padding rows are zero
-    if (a.mr < M) pad_mask_cols(acc, a.mr);
+    // (PAD) padding columns take no weight and padding rows are zero
+    if constexpr (PAD) pad_mask_cols(acc, a.mr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float mx = NEG_BIG;
@@ -258,7 +258,7 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
 // slots (one 64-bit atomic load per slot, two slots per lane) until every
 // one is valid, and takes the maxima.  A word is written whole, so a valid
 // one carries its maximum; there is no other shared data and no fence.
-template <int M, bool F32, int NW, class Ly>
+template <int M, bool F32, int NW, class Ly, bool PAD>
 __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
   float* const wred = L + Ly::OFF_WRED;
   if (!a.fuse_gram) {
@@ -276,7 +276,7 @@ __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
     __syncthreads();
     return pinv_scale(a, bh);
   }
-  gram_lds<M, F32, NW, Ly>(a.la, bh, L);
+  gram_lds<M, F32, NW, Ly, PAD>(a.la, bh, L);
   const float cm = wred[0], rm = wred[1];
   if (a.init_option != 0) return cm * rm;
   __syncthreads();  // every thread has read wred
@@ -525,7 +525,7 @@ constexpr int pinv_rt() {
   return (M == 128 && F16) ? 2 : 1;
 }
 
-template <int M, bool F16>
+template <int M, bool F16, bool PAD>
 __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   typedef POp<F16> P;
   typedef typename P::Frag Frag;
@@ -542,7 +542,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   float* Zg = a.Z + (size_t)bh * M * M;
 
   using Ly = ProLayout<M, P::NP * PL * 2, nwaves<M>()>;
-  const float c = pinv_prologue<M, false, nwaves<M>(), Ly>(a, bh, reinterpret_cast<float*>(lds));
+  const float c = pinv_prologue<M, false, nwaves<M>(), Ly, PAD>(a, bh, reinterpret_cast<float*>(lds));
   const float invc = 1.0f / c;
   const float* const Al = reinterpret_cast<const float*>(lds) + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
@@ -727,7 +727,7 @@ __device__ __forceinline__ void store_t(float* R, int col, int row4, const f32x4
   *reinterpret_cast<float4*>(R + col * LD + row4) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <int M>
+template <int M, bool PAD>
 __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   constexpr int TM = M / 16, KS = M / 32, LD = M + 4;
   constexpr int WPT = pinv_wpt<M>();
@@ -740,7 +740,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   float* Zg = a.Z + (size_t)bh * M * M;
 
   using Ly = ProLayout<M, M * LD * 4, nwaves<M>()>;
-  const float c = pinv_prologue<M, true, nwaves<M>(), Ly>(a, bh, lds);
+  const float c = pinv_prologue<M, true, nwaves<M>(), Ly, PAD>(a, bh, lds);
   const float invc = 1.0f / c;
   const float* const Al = lds + Ly::OFF_A;  // A, row stride Ly::ALD
   if (threadIdx.x == 0) a.cscale[bh] = c;
@@ -886,10 +886,12 @@ __global__ __launch_bounds__(256) void k_pinv_init(PinvArgs a, int M) {
 
 // C = alpha * P * Q' with Q' = Q when beta == 0, else beta * I - Q.
 // grid: ((M/32)^2, BH), block 256 (4 waves, one 16x16 tile each).  F32:
-// float32 matrix-core products (float32 I/O), else split-bf16 products.
-template <bool F32>
+// float32 matrix-core products (float32 I/O), else split-bf16 products.  M
+// is a compile-time size so the k loop unrolls and every operand load is
+// issued before the first product (one round trip, not one per k step).
+template <bool F32, int M>
 __global__ __launch_bounds__(256) void k_pinv_gemm(const float* __restrict__ P, const float* __restrict__ Q,
-                                                    float* __restrict__ C, int M, float beta, float alpha) {
+                                                    float* __restrict__ C, float beta, float alpha) {
   const int bh = blockIdx.y;
   const int nb = M / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -899,6 +901,7 @@ __global__ __launch_bounds__(256) void k_pinv_gemm(const float* __restrict__ P, 
   const float* Pm = P + (size_t)bh * M * M;
   const float* Qm = Q + (size_t)bh * M * M;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
   for (int ks = 0; ks < M / 32; ++ks) {
     float x[8], y[8];
 #pragma unroll

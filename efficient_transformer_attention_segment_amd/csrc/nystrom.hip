@@ -303,9 +303,16 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   if constexpr (M <= 128)
     lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
                                                   : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
-  HIP_TRY(allow_lds(k_pinv_bv<IO, M>, lds2));
-  HIP_TRY(launch("k_pinv_bv", k_pinv_bv<IO, M>, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()),
-                 (uint32_t)lds2, st, pa, ba, p.npinv));
+  // the padding-landmark and ragged-tile code only in the instance that needs it
+  const bool pad = p.mr < M, edge = pad || p.n % 32 != 0;
+  auto launch_bv = [&](auto kern) -> int {
+    HIP_TRY(allow_lds(kern, lds2));
+    HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), (uint32_t)lds2, st, pa,
+                   ba, p.npinv));
+    return NYS_OK;
+  };
+  const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true>) : launch_bv(k_pinv_bv<IO, M, false>);
+  if (brc != NYS_OK) return brc;
 
   const float* Zfinal = pa.Z;
   if constexpr (M > 128) {
@@ -317,13 +324,13 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     float* T2 = at<float>(w, p.off_T2);
     const dim3 gg((M / 32) * (M / 32), p.BH);
     for (int it = 0; it < n_iter; ++it) {
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X,
                      0.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1,
                      7.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2,
                      15.f, 1.f));
-      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4>, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn, M,
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn,
                      13.f, 0.25f));
       std::swap(Zc, Zn);
     }
@@ -379,14 +386,25 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     const int want = std::max(1, slots / p.BH);  // workgroups per head
     const int R = OUTS_UNIT * ((p.n + want * OUTS_UNIT - 1) / (want * OUTS_UNIT));
     const int nbh = (p.n + R - 1) / R;
-    if (conv_w != nullptr)
-      HIP_TRY(launch("k_out_stream", k_out_stream<M, true>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
-    else
-      HIP_TRY(launch("k_out_stream", k_out_stream<M, false>, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, at<u16>(w, p.off_junk)));
+    u16* const junk = at<u16>(w, p.off_junk);
+    auto launch_out = [&](auto kern) -> int {
+      HIP_TRY(launch("k_out_stream", kern, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, junk));
+      return NYS_OK;
+    };
+    const int orc = conv_w != nullptr ? (pad ? launch_out(k_out_stream<M, true, true>)
+                                             : launch_out(k_out_stream<M, true, false>))
+                                      : (pad ? launch_out(k_out_stream<M, false, true>)
+                                             : launch_out(k_out_stream<M, false, false>));
+    if (orc != NYS_OK) return orc;
   } else {
     const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
-    HIP_TRY(allow_lds(k_out<IO, M>, lds4));
-    HIP_TRY(launch("k_out", k_out<IO, M>, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
+    auto launch_out = [&](auto kern) -> int {
+      HIP_TRY(allow_lds(kern, lds4));
+      HIP_TRY(launch("k_out", kern, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
+      return NYS_OK;
+    };
+    const int orc = pad ? launch_out(k_out<IO, M, true>) : launch_out(k_out<IO, M, false>);
+    if (orc != NYS_OK) return orc;
   }
   return NYS_OK;
 }
