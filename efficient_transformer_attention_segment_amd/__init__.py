@@ -52,6 +52,10 @@ def _load():
     lib.nystrom_attention_conv.restype = _I
     lib.nystrom_attention_bf16_conv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P]
     lib.nystrom_attention_bf16_conv.restype = _I
+    _L = ctypes.c_longlong
+    lib.nystrom_attention_ex.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                         _P, _L, _L, _L, _P]
+    lib.nystrom_attention_ex.restype = _I
     lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
     lib.nystrom_last_error.argtypes = []
@@ -110,8 +114,26 @@ def _raw_call_conv(fn, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, s
               d, m, n_iter, init_option, _ptr(out), _stream(stream))
 
 
+def _dense(t) -> bool:
+    B, H, n, d = t.shape
+    return t.stride() == (H * n * d, n * d, d, 1)
+
+
 def _call(name, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
     lib = _load()
+    if not (k.shape == v.shape == out.shape == q.shape):
+        raise ValueError("q, k, v and out must have one shape [B, H, n, d]")
+    if not all(_dense(t) for t in (q, k, v, out)):
+        # strided views of [B, H, n, 64] (channels contiguous): one set of
+        # strides for q, k, v and one for out
+        if not (q.stride() == k.stride() == v.stride()) or q.stride(-1) != 1 or out.stride(-1) != 1:
+            raise ValueError("q, k and v must share strides, with contiguous channels (as must out)")
+        B, H, n, d = q.shape
+        dtype = 1 if name.endswith("bf16") else 0
+        ksize = CONV_TAPS if conv_w is None else int(conv_w.shape[-1])
+        return lib.nystrom_attention_ex(dtype, _ptr(q), _ptr(k), _ptr(v), *q.stride()[:3], _ptr(key_mask),
+                                        _ptr(conv_w), ksize, B, H, n, d, m, n_iter, init_option, _ptr(out),
+                                        *out.stride()[:3], _stream(stream))
     if conv_w is None or conv_w.shape[-1] == CONV_TAPS:
         return _raw_call(getattr(lib, name), q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream)
     return _raw_call_conv(getattr(lib, name + "_conv"), q, k, v, key_mask, conv_w, m, n_iter, init_option,
@@ -121,12 +143,15 @@ def _call(name, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
 def nystrom_attention(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0,
                       out=None, stream=None):
     """float32 [B,H,n,64] CUDA tensors -> out (allocated when None).
+    q, k, v (sharing strides) and out may be strided views with contiguous
+    channels, e.g. slices of a fused [B, n, 3, H, 64] projection and a
+    [B, n, H, 64] output; they then go through nystrom_attention_ex.
     key_mask: uint8 [B,n] (1 keeps a key) or None; conv_w: float32 [H,K]
     (K odd, up to 65; the pages' default is 65) or None.  Enqueued on
     ``stream`` (default: torch's current stream)."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     _check(_call("nystrom_attention", q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream))
     return out
 
@@ -136,7 +161,7 @@ def nystrom_attention_bf16(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, 
     """bfloat16 [B,H,n,64] CUDA tensors (float32 accumulation) -> out."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     _check(_call("nystrom_attention_bf16", q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream))
     return out
 

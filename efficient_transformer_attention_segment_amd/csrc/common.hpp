@@ -162,6 +162,14 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
 
+// Element strides of a [B, H, n, 64] tensor view: batch, head and token; the
+// 64 channels of a token are contiguous.  Dense [B, H, n, 64] is
+// {H n 64, n 64, 64}; [B, n, H, 64] is {n H 64, 64, H 64}.
+struct Strides {
+  long long b, h, t;
+  __host__ __device__ long long base(int bh, int H) const { return (long long)(bh / H) * b + (long long)(bh % H) * h; }
+};
+
 // s_waitcnt vmcnt(N) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

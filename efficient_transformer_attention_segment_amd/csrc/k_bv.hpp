@@ -50,15 +50,15 @@ struct Items {
 };
 
 template <typename IO, int NT>
-__device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __restrict__ V, int n, int key0,
-                                        float (&kx)[Items<NT>::N][8], float (&vx)[Items<NT>::N][8]) {
+__device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __restrict__ V, long long st, int n,
+                                        int key0, float (&kx)[Items<NT>::N][8], float (&vx)[Items<NT>::N][8]) {
 #pragma unroll
   for (int u = 0; u < Items<NT>::N; ++u) {
     const int item = threadIdx.x + u * NT;
     const int row = key0 + (item >> 3), cc = item & 7;
     if (item < 256 && row < n) {
-      IOTraits<IO>::load8(K + (size_t)row * HD + 8 * cc, kx[u]);
-      IOTraits<IO>::load8(V + (size_t)row * HD + 8 * cc, vx[u]);
+      IOTraits<IO>::load8(K + row * st + 8 * cc, kx[u]);
+      IOTraits<IO>::load8(V + row * st + 8 * cc, vx[u]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kx[u][e] = vx[u][e] = 0.f;
@@ -187,21 +187,21 @@ __device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&
 // Stream key tiles [tile0, tile1) of one head through the register-staged
 // double buffer (used for float32 I/O and for ragged key ranges).
 template <typename IO, int TPW, int NT, int KP = 1>
-__device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, int n,
+__device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, long long st, int n,
                                           const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
                                           __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
                                           float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
   using C = KV<IO>;
   float kx[Items<NT>::N][8], vx[Items<NT>::N][8];
   if (tile0 < tile1) {
-    kv_load<IO, NT>(K, V, n, tile0 * C::KT, kx, vx);
+    kv_load<IO, NT>(K, V, st, n, tile0 * C::KT, kx, vx);
     kv_store<IO, NT>(lds, kx, vx);
   }
   __syncthreads();
   for (int tile = tile0; tile < tile1; ++tile) {
     const int cur = (tile - tile0) & 1;
     const bool more = tile + 1 < tile1;
-    if (more) kv_load<IO, NT>(K, V, n, (tile + 1) * C::KT, kx, vx);
+    if (more) kv_load<IO, NT>(K, V, st, n, (tile + 1) * C::KT, kx, vx);
     if (((tile - tile0) % KP) == kp)
       kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
     if (more) kv_store<IO, NT>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
@@ -221,14 +221,14 @@ constexpr int DMA_LDS_BYTES = DMA_NBUF * (2 * DMA_TILE * 2 + 32);
 // are dealt round-robin to the NW waves; every wave also copies the tile's
 // 32 mask bytes (identical data), so each wave issues the same count.
 template <int NW, bool MASK>
-__device__ __forceinline__ void dma_issue_tile(const u16* __restrict__ K, const u16* __restrict__ V,
+__device__ __forceinline__ void dma_issue_tile(const u16* __restrict__ K, const u16* __restrict__ V, long long st,
                                                const uint8_t* __restrict__ mask, int key0, __bf16* lds, int buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int id = wave; id < 8; id += NW) {
     const int row = 8 * (id & 3) + (lane >> 3);
     const int chunk = (lane & 7) ^ (row & 7);
-    const size_t src = (size_t)(key0 + row) * HD + 8 * chunk;
+    const long long src = (key0 + row) * st + 8 * chunk;
     __bf16* dst = lds + ((id < 4 ? 0 : DMA_NBUF) + buf) * DMA_TILE + 8 * (id & 3) * HD;
     dma16((id < 4 ? K : V) + src, dst);
   }
@@ -295,7 +295,7 @@ __device__ __forceinline__ void dma_tile_update(const __bf16* lds, int buf, cons
 
 // Stream key tiles [tile0, tile1) (all inside [0, n)) of one head.
 template <int TPW, int NW, bool MASK, int KP = 1>
-__device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u16* __restrict__ V,
+__device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u16* __restrict__ V, long long st,
                                               const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
                                               __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
                                               float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
@@ -305,7 +305,7 @@ __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u
   static_assert(DMA_DIST + KP <= DMA_NBUF, "ring too short for the copy distance");
   const int T = tile1 - tile0;
   for (int j = 0; j < DMA_DIST && j < T; ++j)
-    dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + j) * 32, lds, j % DMA_NBUF);
+    dma_issue_tile<NW, MASK>(K, V, st, mask, (tile0 + j) * 32, lds, j % DMA_NBUF);
   // one step per KP tiles: the KP wave groups work on their tiles of the
   // step at the same time, between one barrier and the next
   for (int t = 0; t < T; t += KP) {
@@ -314,7 +314,7 @@ __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u
 #pragma unroll
     for (int i = 0; i < KP; ++i)
       if (t + DMA_DIST + i < T)
-        dma_issue_tile<NW, MASK>(K, V, mask, (tile0 + t + DMA_DIST + i) * 32, lds, (t + DMA_DIST + i) % DMA_NBUF);
+        dma_issue_tile<NW, MASK>(K, V, st, mask, (tile0 + t + DMA_DIST + i) * 32, lds, (t + DMA_DIST + i) % DMA_NBUF);
     if (t + kp < T) dma_tile_update<TPW, MASK>(lds, (t + kp) % DMA_NBUF, qf, nown, lscale, mrun, lsum, acc);
   }
   barrier_only();
@@ -331,6 +331,7 @@ struct BvArgs {
   float* pacc;              // [BH][S][16][M][4]: 4-channel runs, each run's rows contiguous
   int n, H, S, tpc, ntiles;
   float lscale;             // d^-1/4 (Qt carries the other factor)
+  Strides in;               // of k and v
 };
 
 // Waves of the B V / pseudo-inverse launch: one per 16 landmarks up to 128,
@@ -357,8 +358,9 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   const int wave = w % NWT, kp = w / NWT;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = bh / a.H;
-  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + a.in.base(bh, a.H);
+  const IO* V = reinterpret_cast<const IO*>(a.v) + a.in.base(bh, a.H);
+  const long long st = a.in.t;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   const int nown = (kp < KP && wave < TM) ? (TM - wave + NWT - 1) / NWT : 0;
 
@@ -391,14 +393,15 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
     // registers, which zero and mask the keys past n
     const int tfull = min(tile1, a.n / 32);
     if (mask != nullptr)
-      kv_stream_dma<TPW, NW, true, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+      kv_stream_dma<TPW, NW, true, KP>(K, V, st, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
     else
-      kv_stream_dma<TPW, NW, false, KP>(K, V, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+      kv_stream_dma<TPW, NW, false, KP>(K, V, st, mask, tile0, tfull, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
     if constexpr (EDGE)
       if (tfull < tile1)
-        kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+        kv_stream<IO, TPW, 64 * NW, KP>(K, V, st, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc,
+                                        kp);
   } else {
-    kv_stream<IO, TPW, 64 * NW, KP>(K, V, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+    kv_stream<IO, TPW, 64 * NW, KP>(K, V, st, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
   }
   if constexpr (KP == 2) {
     // fold the odd-tile waves' states into the even-tile waves (same lanes)
@@ -480,6 +483,7 @@ struct ExactArgs {
   void* out;
   int n, H;
   float lscale;  // 1 / sqrt(d)
+  Strides in, out_s;  // of q, k, v and of out
 };
 
 constexpr int EXACT_WIN = 144;            // conv window rows for 64 queries
@@ -501,9 +505,10 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int q0 = blockIdx.x * 64;
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + a.in.base(bh, a.H);
+  const IO* K = reinterpret_cast<const IO*>(a.k) + a.in.base(bh, a.H);
+  const IO* V = reinterpret_cast<const IO*>(a.v) + a.in.base(bh, a.H);
+  const long long st = a.in.t;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
 
   const int tok = q0 + 16 * wave + c16;
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
   for (int ks = 0; ks < 2; ++ks) {
     float x[8];
     if (tok < a.n) {
-      IOTraits<IO>::load8(Q + (size_t)tok * HD + 32 * ks + 8 * g, x);
+      IOTraits<IO>::load8(Q + tok * st + 32 * ks + 8 * g, x);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ntiles = (a.n + KV<IO>::KT - 1) / KV<IO>::KT;
-  kv_stream<IO, 1, 256>(K, V, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
+  kv_stream<IO, 1, 256>(K, V, st, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
   const float ls = sum_g(lsum[0]);
   const float inv = ls > 0.f ? 1.0f / ls : 0.f;
 #pragma unroll
@@ -532,13 +537,14 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
   if (a.conv_w != nullptr) {
     __bf16* Vh = lds_dyn;
     __bf16* Vl = lds_dyn + HD * EXACT_VWLD;
-    stage_v_window<IO>(V, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
+    stage_v_window<IO>(V, st, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
     __syncthreads();
     Frag2 tap[3];
     conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
     conv_tile<NS, false>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
   }
-  if (tok < a.n) store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, acc[0]);
+  if (tok < a.n)
+    store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, acc[0]);
 }
 
 }  // namespace nys

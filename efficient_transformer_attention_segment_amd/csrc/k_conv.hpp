@@ -74,14 +74,15 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
 // Stage V rows [t0 - 32, t0 - 32 + win) of one head, transposed, into
 // Vh[d * ld + row] (and Vl when split).  Rows outside [0, n) are zero.
 template <typename IO>
-__device__ void stage_v_window(const IO* __restrict__ V, int n, int t0, int win, __bf16* Vh, __bf16* Vl, int ld) {
+__device__ void stage_v_window(const IO* __restrict__ V, long long st, int n, int t0, int win, __bf16* Vh, __bf16* Vl,
+                               int ld) {
   constexpr int NS = IOTraits<IO>::NS;
   for (int idx = threadIdx.x; idx < win * 8; idx += blockDim.x) {
     const int row = idx >> 3, cc = idx & 7;
     const int s = t0 - HALO + row;
     float x[8];
     if (s >= 0 && s < n) {
-      IOTraits<IO>::load8(V + (size_t)s * HD + 8 * cc, x);
+      IOTraits<IO>::load8(V + s * st + 8 * cc, x);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;

@@ -26,7 +26,8 @@
 namespace nys {
 
 struct LandmarkArgs {
-  int n, m, L, RS, lpw, BH;
+  int n, m, L, RS, lpw, BH, H;
+  Strides in;           // of q and k
   int mr;               // landmarks of the method; m = mr rounded up to 32 (rows mr .. m-1 are zero)
   float scale;          // d^-1/4 / L
   float* qt;            // [BH][m][64] float32
@@ -204,7 +205,8 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   const int j = t / (TPR * RS);
   const int i = blockIdx.x * lpw + j;
   const bool live = i < a.mr;  // padding landmarks stay zero
-  const size_t base = ((size_t)bh * a.n + (size_t)(live ? i : 0) * L) * HD + c * CW;
+  const long long st = a.in.t;
+  const long long base = a.in.base(bh, a.H) + (long long)(live ? i : 0) * L * st + c * CW;
   if (blockIdx.x == 0 && t < 2) a.slots[2 * blockIdx.y + t] = 0ull;  // written in the next launch
 
   float sq[CW], sk[CW];
@@ -215,8 +217,8 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
     float xq[UNR][CW], xk[UNR][CW];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      IOTraits<IO>::load8(q + base + (size_t)(r + u * RS) * HD, xq[u]);
-      IOTraits<IO>::load8(k + base + (size_t)(r + u * RS) * HD, xk[u]);
+      IOTraits<IO>::load8(q + base + (r + u * RS) * st, xq[u]);
+      IOTraits<IO>::load8(k + base + (r + u * RS) * st, xk[u]);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
@@ -228,8 +230,8 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
   }
   for (; r < L; r += RS) {
     float xq[CW], xk[CW];
-    IOTraits<IO>::load8(q + base + (size_t)r * HD, xq);
-    IOTraits<IO>::load8(k + base + (size_t)r * HD, xk);
+    IOTraits<IO>::load8(q + base + r * st, xq);
+    IOTraits<IO>::load8(k + base + r * st, xk);
 #pragma unroll
     for (int e = 0; e < CW; ++e) {
       sq[e] += xq[e];

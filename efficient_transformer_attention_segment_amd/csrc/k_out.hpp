@@ -39,6 +39,7 @@ struct OutArgs {
   int n, H;
   int mr;                // landmarks of the method (M = mr rounded up to 32)
   float lscale;          // d^-1/4
+  Strides in, out_s;     // of q and v, and of out
 };
 
 // Logits of padding landmarks (16 it + 4g + r >= mr) -> -inf, in S^T tiles.
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, h = bh % a.H;
   const int t0 = blockIdx.x * OUT_TOK;
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + a.in.base(bh, a.H);
+  const IO* V = reinterpret_cast<const IO*>(a.v) + a.in.base(bh, a.H);
+  const long long st = a.in.t;
 
   __bf16* kth = lds_dyn + Ly::OFF_KT;
   __bf16* ktl = kth + Ly::KT_ELEMS;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
           *reinterpret_cast<bf16x8*>(wfl_lds + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsl + 8 * idx);
       }
     }
-    if (a.conv_w != nullptr) stage_v_window<IO>(V, a.n, t0, OUT_WIN, vh, vl, OUT_VWLD);
+    if (a.conv_w != nullptr) stage_v_window<IO>(V, st, a.n, t0, OUT_WIN, vh, vl, OUT_VWLD);
   }
   // Q B fragments of both tiles, in flight with the staging copies
   Frag2 qf2[2][2];
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float x[8];
-      IOTraits<IO>::load8(Q + (size_t)tok * HD + 32 * ks + 8 * g, x);
+      IOTraits<IO>::load8(Q + tok * st + 32 * ks + 8 * g, x);
       qf2[u][ks] = make_frag<NS>(x);
     }
   }
@@ -198,7 +200,8 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
       }
     }
     if (a.conv_w != nullptr) conv_tile<NS, false>(vh, vl, OUT_VWLD, ts - t0, tap, oacc);
-    if (tok < a.n) store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + ((size_t)bh * a.n + tok) * HD, oacc);
+    if (tok < a.n)
+      store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, oacc);
   }
 }
 
@@ -241,11 +244,11 @@ __device__ __forceinline__ int vring_pos(int r, int chunk) {
 struct VGroup {
   uint4 x[2];
 };
-__device__ __forceinline__ void vgroup_load(const u16* V, int n, int G, VGroup& b) {
+__device__ __forceinline__ void vgroup_load(const u16* V, long long st, int n, int G, VGroup& b) {
   const int t = threadIdx.x;
   const int r = OUTS_UNIT * G + (t >> 2);
   if (r >= 0 && r < n) {
-    const uint4* src = reinterpret_cast<const uint4*>(V + (size_t)r * HD) + 2 * (t & 3);
+    const uint4* src = reinterpret_cast<const uint4*>(V + r * st) + 2 * (t & 3);
     b.x[0] = src[0];
     b.x[1] = src[1];
   } else {
@@ -303,9 +306,9 @@ __device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int t0, const
   }
 }
 
-__device__ __forceinline__ void load_q16(const u16* Q, int n, int tok, bf16x8 (&qf)[2]) {
+__device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int tok, bf16x8 (&qf)[2]) {
   const int g = (threadIdx.x & 63) >> 4;
-  const u16* row = Q + (size_t)min(tok, n - 1) * HD + 8 * g;
+  const u16* row = Q + min(tok, n - 1) * st + 8 * g;
   qf[0] = *reinterpret_cast<const bf16x8*>(row);
   qf[1] = *reinterpret_cast<const bf16x8*>(row + 32);
 }
@@ -327,9 +330,10 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
   const int tb = blockIdx.x * R;
   const int te = min(a.n, tb + R);
   const int nunits = (te - tb + OUTS_UNIT - 1) / OUTS_UNIT;
-  const u16* Q = reinterpret_cast<const u16*>(a.q) + (size_t)bh * a.n * HD;
-  const u16* V = reinterpret_cast<const u16*>(a.v) + (size_t)bh * a.n * HD;
-  u16* O = reinterpret_cast<u16*>(a.out) + (size_t)bh * a.n * HD;
+  const u16* Q = reinterpret_cast<const u16*>(a.q) + a.in.base(bh, a.H);
+  const u16* V = reinterpret_cast<const u16*>(a.v) + a.in.base(bh, a.H);
+  u16* O = reinterpret_cast<u16*>(a.out) + a.out_s.base(bh, a.H);
+  const long long st = a.in.t, ot = a.out_s.t;
 
   // ---- prologue: landmarks and W^T fragments (DMA), V groups G0 - 1 .. G0 + 1
   // (through registers), group G0 + 2 and the Q rows of units 0, 1 in flight
@@ -352,16 +356,16 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     VGroup pre[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      if (G0 - 1 + i <= Glast) vgroup_load(V, a.n, G0 - 1 + i, pre[i]);
+      if (G0 - 1 + i <= Glast) vgroup_load(V, st, a.n, G0 - 1 + i, pre[i]);
 #pragma unroll
     for (int i = 0; i < 3; ++i)
       if (G0 - 1 + i <= Glast) vgroup_store(pre[i], G0 - 1 + i, ring);
-    if (G0 + 2 <= Glast) vgroup_load(V, a.n, G0 + 2, vb);
+    if (G0 + 2 <= Glast) vgroup_load(V, st, a.n, G0 + 2, vb);
     conv_lane_init(cl);
   }
   bf16x8 qb[2][2];
-  load_q16(Q, a.n, tb + 16 * wave + c16, qb[0]);
-  if (nunits > 1) load_q16(Q, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
+  load_q16(Q, st, a.n, tb + 16 * wave + c16, qb[0]);
+  if (nunits > 1) load_q16(Q, st, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
   Frag2 tap[3];
   if constexpr (CONV) conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
   wait_vmcnt<0>();  // the landmark / fragment copies (the register loads are tracked by the compiler)
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     if (u > 0) __syncthreads();  // last unit's ring writes are visible; its reads of the slot reused below are done
     if constexpr (CONV) {
       if (G + 2 <= Glast) vgroup_store(vb, G + 2, ring);  // slot of G - 2: last read by the previous unit
-      if (G + 3 <= Glast) vgroup_load(V, a.n, G + 3, vb);
+      if (G + 3 <= Glast) vgroup_load(V, st, a.n, G + 3, vb);
     }
     const int ts = t0 + 16 * wave;
     // S^T = Kt Q^T: sacc[it][r] = logit(token ts + c16, landmark 16 it + 4g + r)
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
         sacc[it] = mfma(kf, q[ks], sacc[it]);
       }
     }
-    if (u + 2 < nunits) load_q16(Q, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
+    if (u + 2 < nunits) load_q16(Q, st, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
     if constexpr (PAD) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
       }
     }
     if constexpr (CONV) conv_tile_ring(ring, t0, cl, tap, oacc);
-    u16* dst = ts + c16 < te ? O + (size_t)(ts + c16) * HD : junk + c16 * HD;
+    u16* dst = ts + c16 < te ? O + (ts + c16) * ot : junk + c16 * HD;
     store_row16<u16, true>(dst, oacc);
   };
   int u = 0;

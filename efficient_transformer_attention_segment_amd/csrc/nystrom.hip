@@ -67,6 +67,7 @@ struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
   int mr;       // landmarks of the method; m is mr rounded up to a multiple of 32
   bool record;  // keep every intermediate in the workspace (stage hook)
+  Strides si, so;  // element strides of q, k, v and of out
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
   size_t off_slots, off_junk;
@@ -243,6 +244,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   const float s4 = 1.0f / sqrtf(sqrtf((float)HD));
   LandmarkArgs la;
   la.n = p.n;
+  la.H = p.H;
+  la.in = p.si;
   la.m = M;
   la.mr = p.mr;
   la.L = p.L;
@@ -299,6 +302,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.tpc = p.tpc;
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
+  ba.in = p.si;
   size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
   if constexpr (M <= 128)
     lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
@@ -374,6 +378,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.n = p.n;
   oa.H = p.H;
   oa.lscale = s4;
+  oa.in = p.si;
+  oa.out_s = p.so;
   oa.mr = p.mr;
   if constexpr (sizeof(IO) == 2) {
     // persistent output pass: a token range of one head per workgroup, sized
@@ -410,7 +416,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
 }
 
 template <typename IO>
-int launch_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
+int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, const void* k, const void* v,
+                 const uint8_t* mask,
                  const float* conv_w, int conv_k, void* out, hipStream_t st) {
   ExactArgs ea;
   ea.q = q;
@@ -419,6 +426,8 @@ int launch_exact(int B, int H, int n, const void* q, const void* k, const void* 
   ea.key_mask = mask;
   ea.conv_w = conv_w;
   ea.conv_k = conv_k;
+  ea.in = si;
+  ea.out_s = so;
   ea.out = out;
   ea.n = n;
   ea.H = H;
@@ -452,10 +461,57 @@ int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k,
   return fail(NYS_ERR_UNSUPPORTED, "m=%d has no kernel instance", m);
 }
 
-bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
-  const char* pa = static_cast<const char*>(a);
-  const char* pb = static_cast<const char*>(b);
-  return pa < pb + bn && pb < pa + an;
+
+// Dense [B, H, n, 64] strides.
+Strides dense(int B, int H, int n) {
+  (void)B;
+  return Strides{(long long)H * n * HD, (long long)n * HD, HD};
+}
+
+// A view's element range [lo, hi] (strides may be negative).
+void view_range(const Strides& s, int B, int H, int n, long long& lo, long long& hi) {
+  lo = hi = 0;
+  const long long ext[3][2] = {{s.b, B}, {s.h, H}, {s.t, n}};
+  for (const auto& e : ext) (e[0] < 0 ? lo : hi) += e[0] * (e[1] - 1);
+  hi += HD - 1;
+}
+
+// Strides of q/k/v (si) and out (so): 16-byte aligned rows, and no two
+// (batch, head, token) rows of out sharing an element (sorted by stride,
+// each dimension must step over everything the smaller ones span).
+int check_strides(int esize, const void* q, const void* k, const void* v, const void* out, Strides si, Strides so,
+                  int B, int H, int n) {
+  const int ext[3] = {B, H, n};
+  for (const Strides* s : {&si, &so}) {
+    const long long st[3] = {s->b, s->h, s->t};
+    for (int i = 0; i < 3; ++i)
+      if (ext[i] > 1 && (st[i] * esize) % 16 != 0)
+        return fail(NYS_ERR_INVALID, "strides (%lld, %lld, %lld) elements: each must keep 16-byte row alignment",
+                    s->b, s->h, s->t);
+  }
+  for (const void* ptr : {q, k, v, out})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(NYS_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+  struct D {
+    long long st;
+    long long ex;
+  } d[4] = {{1, HD}, {so.b < 0 ? -so.b : so.b, B}, {so.h < 0 ? -so.h : so.h, H}, {so.t < 0 ? -so.t : so.t, n}};
+  std::sort(d, d + 4, [](const D& x, const D& y) { return x.st < y.st; });
+  long long span = 0;
+  for (const D& e : d) {
+    if (e.ex <= 1) continue;
+    if (e.st <= span) return fail(NYS_ERR_INVALID, "out strides (%lld, %lld, %lld) make rows overlap", so.b, so.h, so.t);
+    span += e.st * (e.ex - 1);
+  }
+  long long olo, ohi, ilo, ihi;
+  view_range(so, B, H, n, olo, ohi);
+  view_range(si, B, H, n, ilo, ihi);
+  const char* const ob = static_cast<const char*>(out);
+  for (const void* ptr : {q, k, v}) {
+    const char* const ib = static_cast<const char*>(ptr);
+    if (ob + olo * esize <= ib + ihi * esize + (esize - 1) && ib + ilo * esize <= ob + ohi * esize + (esize - 1))
+      return fail(NYS_ERR_INVALID, "out overlaps an input");
+  }
+  return NYS_OK;
 }
 
 int validate(int esize, const void* q, const void* k, const void* v, int B, int H, int n, int d, int m, int n_iter,
@@ -473,26 +529,29 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
   if (m != n) {
     if (m > NYS_MAX_LANDMARKS) return fail(NYS_ERR_UNSUPPORTED, "m=%d: at most 256 landmarks (unless m == n)", m);
   }
-  const size_t bytes = (size_t)B * H * n * d * esize;
-  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
-    return fail(NYS_ERR_INVALID, "out overlaps an input");
+  (void)esize;
   return NYS_OK;
 }
 
 template <typename IO>
-int run(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k, int B,
+int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* mask, const float* conv_w, int conv_k,
+        Strides so, int B,
         int H, int n,
         int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout) {
   int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
+  if (rc != NYS_OK) return rc;
+  rc = check_strides(sizeof(IO), q, k, v, out, si, so, B, H, n);
   if (rc != NYS_OK) return rc;
   if (conv_w != nullptr) {
     if (conv_k < 1 || conv_k % 2 == 0)
       return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
-  if (m == n) return launch_exact<IO>(B, H, n, q, k, v, mask, conv_w, conv_k, out, st);
+  if (m == n) return launch_exact<IO>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, st);
   Plan p = make_plan(B, H, n, m);
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
+  p.si = si;
+  p.so = so;
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
@@ -514,7 +573,7 @@ __attribute__((visibility("default"))) int nystrom_attention(const float* q, con
                                                              struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<float>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+    return run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
                       nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -528,7 +587,7 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16(const uint16_t
                                                                   struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<u16>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+    return run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
                     nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -542,7 +601,7 @@ __attribute__((visibility("default"))) int nystrom_attention_conv(const float* q
                                                                   struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<float>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option, out, stream,
+    return run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, conv_kernel_size, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream,
                       nullptr, nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -557,8 +616,29 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16_conv(const uin
                                                                        struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<u16>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option, out, stream,
+    return run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, conv_kernel_size, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream,
                     nullptr, nullptr);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_ex(
+    int dtype, const void* q, const void* k, const void* v, long long in_batch_stride, long long in_head_stride,
+    long long in_token_stride, const uint8_t* key_mask, const float* conv_w, int conv_kernel_size, int B, int H, int n,
+    int d, int m, int n_iter, int init_option, void* out, long long out_batch_stride, long long out_head_stride,
+    long long out_token_stride, struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    const Strides si{in_batch_stride, in_head_stride, in_token_stride};
+    const Strides so{out_batch_stride, out_head_stride, out_token_stride};
+    if (dtype == 0)
+      return run<float>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                        stream, nullptr, nullptr);
+    if (dtype == 1)
+      return run<u16>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                      stream, nullptr, nullptr);
+    return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
   }
@@ -595,8 +675,8 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     Workspace* w = nullptr;
     Plan p{};
     int rc = dtype == 0
-                 ? run<float>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
-                 : run<u16>(q, k, v, key_mask, conv_w, TAPS, B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
+                 ? run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
+                 : run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
     if (rc != NYS_OK) return rc;
     HIP_TRY(hipStreamSynchronize(stream));
     std::lock_guard<std::mutex> lk(g_mu);

@@ -111,6 +111,26 @@ int nystrom_attention_bf16_conv(const uint16_t* q, const uint16_t* k,
                                 int init_option, uint16_t* out,
                                 struct ihipStream_t* stream);
 
+/* The general form: dtype 0 (float32 q/k/v/out) or 1 (bfloat16), the conv
+ * kernel size as in nystrom_attention_conv, and q, k, v (one set of strides)
+ * and out (another) as strided views of [B, H, n, 64]: element
+ * (b, h, t, c) of q is q[b * in_batch_stride + h * in_head_stride +
+ * t * in_token_stride + c], in elements; the 64 channels of a token are
+ * contiguous.  This reads, for example, q, k and v straight out of a fused
+ * [B, n, 3, H, 64] projection (strides n*3*H*64, 64, 3*H*64) and writes out
+ * as [B, n, H*64] (strides n*H*64, 64, H*64), the module's layouts ([P1]
+ * 2.7), with no transposes.  Errors: those of nystrom_attention_conv, plus
+ * NYS_ERR_INVALID for a dtype other than 0/1, a pointer or stride that
+ * breaks 16-byte alignment of the token rows, out strides under which two
+ * (b, h, t) rows share an element, or out overlapping q, k or v. */
+int nystrom_attention_ex(int dtype, const void* q, const void* k, const void* v,
+                         long long in_batch_stride, long long in_head_stride,
+                         long long in_token_stride, const uint8_t* key_mask,
+                         const float* conv_w, int conv_kernel_size, int B, int H,
+                         int n, int d, int m, int n_iter, int init_option, void* out,
+                         long long out_batch_stride, long long out_head_stride,
+                         long long out_token_stride, struct ihipStream_t* stream);
+
 /* Bytes of device workspace a call of this shape uses (0 for invalid or
  * unsupported shapes). */
 size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);

@@ -90,6 +90,27 @@ def test_conv_kernel_size_validation(lib, fn, ksize, code):
     assert "conv_kernel_size" in lib.nystrom_last_error().decode()
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -1),
+    (dict(ist=60), -1),                  # bf16 token rows of 120 bytes: not 16-byte aligned
+    (dict(ost=32), -1),                  # out rows overlap
+    (dict(ob=0, oh=0), -1),              # every (batch, head) writes the same rows
+    (dict(out=FAKE), -1),                # out is q
+    (dict(q=ctypes.c_void_p(0x100008)), -1),   # misaligned pointer
+])
+def test_strided_validation(lib, kw, code):
+    """nystrom_attention_ex rejects unaligned or self-overlapping layouts
+    on the host (everything else valid, so nothing is launched)."""
+    B, H, n = 1, 2, 256
+    a = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, ib=H * n * 64, ih=n * 64, ist=64, out=FAKE2,
+             ob=H * n * 64, oh=n * 64, ost=64)
+    a.update(kw)
+    rc = lib.nystrom_attention_ex(a["dtype"], a["q"], a["k"], a["v"], a["ib"], a["ih"], a["ist"], NULL, NULL, 65,
+                                  B, H, n, 64, 64, 6, 0, a["out"], a["ob"], a["oh"], a["ost"], NULL)
+    assert rc == code
+    assert lib.nystrom_last_error().decode() != ""
+
+
 @pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
 def test_landmarks_above_256_unsupported(lib, fn):
     assert call(lib, fn, n=600, m=300) == -2

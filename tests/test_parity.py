@@ -105,6 +105,38 @@ def test_conv_kernel_sizes(dtype, ksize):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("m,n", [(64, 512), (50, 400), (200, 200), (20, 100)])
+def test_strided_layouts(dtype, m, n):
+    """q, k, v read straight out of a fused [B, n, 3, H, 64] projection and
+    out written as [B, n, H, 64] (the module's layouts), through strided
+    views: the same result as the dense call."""
+    import torch
+
+    import efficient_transformer_attention_segment_amd as nys
+    from gpu_util import to_dev
+    B, H = 2, 3
+    x = make_custom(B, H, n, 64, seed=750 + m + n, dtype=dtype, lengths=[n, n - n // 3])
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qkv = torch.empty(B, n, 3, H, 64, dtype=tdt, device="cuda")
+    for i, name in enumerate(("q", "k", "v")):
+        qkv[:, :, i] = torch.from_numpy(x[name]).to("cuda").to(tdt).permute(0, 2, 1, 3)
+    q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    out_buf = torch.full((B, n, H * 64), float("nan"), dtype=tdt, device="cuda")
+    out = out_buf.view(B, n, H, 64).permute(0, 2, 1, 3)
+    announce(f"strided dtype={dtype} m={m} n={n} q.stride={q.stride()} out.stride={out.stride()}")
+    nys.attention(q, k, v, to_dev(x["key_mask"], None), to_dev(x["conv_w"], None), m=m, n_iter=6, init_option=0,
+                  out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    per, _ = rel_frob_slices(got, oracle_out(x, m, 6, 0))
+    announce(f"strided: max rel Frobenius {per:.3e}")
+    assert per < TOL[dtype]
+    dense = run_gpu(x, dtype, m, 6, 0)
+    assert np.array_equal(got, dense), "strided and dense calls differ"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_many_heads(dtype):
     """More (batch, head) pairs than the fused Gram rendezvous allows (the
     original init then takes the separate Gram launch), ragged masks, both
