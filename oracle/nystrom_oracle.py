@@ -45,7 +45,12 @@ R10 product order F (Z (B V)) (P1 2.4 groups it (F Z)(B V); equal in exact
 R11 the convolution is a cross-correlation (tap j multiplies V at offset
     j - K//2), zero outside [0, n), one filter per head shared by all d
     columns;
-R12 n_iter = 0 is allowed and returns Z_0.
+R12 n_iter = 0 is allowed and returns Z_0;
+R13 the weights returned on request (output_attentions, P1 2.7 and 5.3)
+    are the matrix P1 2.4 calls attention_probs, F Z (n x m, whose rows
+    are the approximate attention weights; 2.7 and 5.3 name its size
+    "m x n" loosely), and the full softmax(Qs Ks^T + mask) (n x n) when
+    the exact branch runs.
 """
 
 from __future__ import annotations
@@ -174,6 +179,33 @@ def exact_attention(qs, ks, v, key_valid=None):
     m == n (R2), with the key mask applied to the scores (R3)."""
     P = softmax_rows(qs @ np.swapaxes(ks, -1, -2), key_valid)
     return P @ v
+
+
+def attention_probs(q, k, key_mask=None, m=64, n_iter=6, init_option=INIT_ORIGINAL):
+    """[P1 2.4, 2.7, 5.3] The attention weights handed back on request
+    (output_attentions), R13.
+
+    Nystrom path: F Z, kernel_1 times the iterative inverse of kernel_2,
+    [B,H,n,m] (the mask does not enter F or A, R7).  When m == n (R2): the
+    exact branch's softmax(Qs Ks^T + mask), [B,H,n,n] (R3, R5, R6).
+    q, k: raw projections [B,H,n,d]."""
+    q, k = _f64(q), _f64(k)
+    B, H, n, d = q.shape
+    if k.shape != q.shape:
+        raise ValueError("q and k must share one shape")
+    if m <= 0 or m > n or n % m != 0:
+        raise ValueError("need 0 < m <= n and n % m == 0")
+    if n_iter < 0:
+        raise ValueError("n_iter must be >= 0")
+    valid = _key_valid(key_mask, B, n)
+    qs, ks = scale_qk(q, k)
+    if m == n:
+        return softmax_rows(qs @ np.swapaxes(ks, -1, -2), valid)
+    qt = segment_means(qs, m)
+    kt = segment_means(ks, m)
+    F, A, _ = nystrom_kernels(qs, ks, qt, kt, valid)
+    Z = newton_schulz_pinv(A, init_scale(A, init_option), n_iter)
+    return F @ Z
 
 
 def _key_valid(key_mask, B, n):

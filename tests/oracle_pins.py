@@ -436,6 +436,89 @@ def pin_path_composition(O):
     return max(e1, e2, e3, e4)
 
 
+# ------------------------------------------------ attention weights ---
+
+def pin_probs_exact_bruteforce(O):
+    """[P1 2.1, 2.7] m == n: the returned weights are softmax(q k^T / sqrt(d))
+    over the kept keys, written out element by element; a batch row with no
+    kept key gives zero rows."""
+    rng = RNG(31)
+    B, H, n, d = 2, 2, 6, 4
+    q = rng.standard_normal((B, H, n, d))
+    k = rng.standard_normal((B, H, n, d))
+    mask = np.ones((B, n), np.uint8)
+    mask[0, [1, 4]] = 0
+    mask[1, :] = 0
+    got = O.attention_probs(q, k, mask, m=n)
+    ref = np.zeros((B, H, n, n))
+    for b in range(B):
+        for h in range(H):
+            for i in range(n):
+                keep = [j for j in range(n) if mask[b, j]]
+                if not keep:
+                    continue
+                s = {j: sum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) / math.sqrt(d) for j in keep}
+                top = max(s.values())
+                tot = sum(math.exp(s[j] - top) for j in keep)
+                for j in keep:
+                    ref[b, h, i, j] = math.exp(s[j] - top) / tot
+    if got.shape != ref.shape:
+        return float("inf")
+    return float(np.abs(got - ref).max())
+
+
+def _landmark_kernels_lib(q, k, m):
+    """F and A from library softmax and reshaped means, d^-1/4 on each side."""
+    d = q.shape[-1]
+    qs, ks = q * d ** -0.25, k * d ** -0.25
+    lead, n = q.shape[:-2], q.shape[-2]
+    qt = qs.reshape(*lead, m, n // m, d).mean(-2)
+    kt = ks.reshape(*lead, m, n // m, d).mean(-2)
+    F = scipy.special.softmax(qs @ np.swapaxes(kt, -1, -2), axis=-1)
+    A = scipy.special.softmax(qt @ np.swapaxes(kt, -1, -2), axis=-1)
+    return F, A, ks, qt
+
+
+def pin_probs_converged_inverse(O):
+    """[P1 2.4, 2.5] With the iteration run to convergence the weights are
+    F A^-1 (LAPACK inverse), and their rows sum to 1 (A 1 = 1, so
+    A^-1 1 = 1, and F 1 = 1)."""
+    rng = RNG(32)
+    B, H, n, d, m = 1, 3, 48, 8, 12
+    q = rng.standard_normal((B, H, n, d))
+    k = rng.standard_normal((B, H, n, d))
+    got = O.attention_probs(q, k, None, m=m, n_iter=40, init_option=1)
+    F, A, _, _ = _landmark_kernels_lib(q, k, m)
+    ref = F @ np.linalg.inv(A)
+    if got.shape != (B, H, n, m):
+        return float("inf")
+    return max(_rel(got, ref), float(np.abs(got.sum(-1) - 1).max()))
+
+
+def pin_probs_output_consistency(O):
+    """[P1 2.4] The weights times B V, plus the convolution, give the output:
+    B formed here with the library softmax over kept keys, a partial mask,
+    six iterations, both initialisations."""
+    rng = RNG(33)
+    B, H, n, d, m = 2, 2, 64, 16, 16
+    q = rng.standard_normal((B, H, n, d))
+    k = rng.standard_normal((B, H, n, d))
+    v = rng.standard_normal((B, H, n, d))
+    w = rng.standard_normal((H, 65)) * 0.02
+    lens = np.array([64, 41])
+    mask = (np.arange(n)[None] < lens[:, None]).astype(np.uint8)
+    _, _, ks, qt = _landmark_kernels_lib(q, k, m)
+    s = qt @ np.swapaxes(ks, -1, -2)
+    s = np.where(mask[:, None, None, :] != 0, s, -np.inf)
+    Bm = scipy.special.softmax(s, axis=-1)
+    err = 0.0
+    for opt in (0, 1):
+        P = O.attention_probs(q, k, mask, m=m, n_iter=6, init_option=opt)
+        out = O.nystrom_attention(q, k, v, mask, w, m=m, n_iter=6, init_option=opt)
+        err = max(err, _rel(P @ (Bm @ v) + O.depthwise_conv_same(v, w), out))
+    return err
+
+
 ALL_PINS = {
     "scale": (pin_scale, 1e-12),
     "segment_means_direct": (pin_segment_means_direct, 1e-12),
@@ -458,4 +541,7 @@ ALL_PINS = {
     "path_mask_semantics": (pin_path_mask_semantics, 1e-12),
     "path_zero_valid": (pin_path_zero_valid, 1e-12),
     "path_composition": (pin_path_composition, 1e-12),
+    "probs_exact_bruteforce": (pin_probs_exact_bruteforce, 1e-12),
+    "probs_converged_inverse": (pin_probs_converged_inverse, 1e-9),
+    "probs_output_consistency": (pin_probs_output_consistency, 1e-12),
 }

@@ -95,6 +95,32 @@ def _conv_off_by_one(v, w):
     return np.concatenate([out[..., 1:, :], np.zeros_like(out[..., :1, :])], axis=-2)
 
 
+def _probs_factory(mode):
+    real = O.attention_probs
+
+    def probs(q, k, key_mask=None, m=64, n_iter=6, init_option=0):
+        if mode == "exact_no_mask" and m == q.shape[-2]:
+            return real(q, k, None, m, n_iter, init_option)
+        if m == q.shape[-2]:
+            return real(q, k, key_mask, m, n_iter, init_option)
+        qs, ks = O.scale_qk(np.asarray(q, np.float64), np.asarray(k, np.float64))
+        qt, kt = O.segment_means(qs, m), O.segment_means(ks, m)
+        valid = None if key_mask is None else (np.asarray(key_mask) != 0)[:, None, None, :]
+        F, A, _ = O.nystrom_kernels(qs, ks, qt, kt, None)
+        Z = O.newton_schulz_pinv(A, O.init_scale(A, init_option), n_iter)
+        if mode == "z_transposed":
+            return F @ np.swapaxes(Z, -1, -2)
+        if mode == "f_only":
+            return F
+        if mode == "full_fzb":
+            Bm = O.softmax_rows(qt @ np.swapaxes(ks, -1, -2), valid)
+            return F @ Z @ Bm
+        if mode == "a_not_inverted":
+            return F @ A
+        return F @ Z
+    return probs
+
+
 MUTANTS = {
     "scale_double": ({"scale_qk": _scale_double}, ["scale", "exact_sdpa"]),
     "scale_q_only": ({"scale_qk": _scale_q_only}, ["scale"]),
@@ -115,6 +141,14 @@ MUTANTS = {
     "init_exact_global": ({"init_scale": _init_factory("exact_global")}, ["init_scale"]),
     "conv_flipped": ({"depthwise_conv_same": _conv_flipped}, ["conv_library", "conv_delta"]),
     "conv_off_by_one": ({"depthwise_conv_same": _conv_off_by_one}, ["conv_delta", "conv_direct"]),
+    "probs_z_transposed": ({"attention_probs": _probs_factory("z_transposed")}, ["probs_converged_inverse"]),
+    "probs_f_only": ({"attention_probs": _probs_factory("f_only")},
+                     ["probs_converged_inverse", "probs_output_consistency"]),
+    "probs_full_fzb": ({"attention_probs": _probs_factory("full_fzb")},
+                       ["probs_converged_inverse", "probs_output_consistency"]),
+    "probs_a_not_inverted": ({"attention_probs": _probs_factory("a_not_inverted")},
+                             ["probs_converged_inverse", "probs_output_consistency"]),
+    "probs_exact_no_mask": ({"attention_probs": _probs_factory("exact_no_mask")}, ["probs_exact_bruteforce"]),
 }
 
 
