@@ -43,6 +43,7 @@ def parse_args():
     ap.add_argument("--workload", type=int, default=3, help="workload index 1..5 (default 3)")
     ap.add_argument("--also", default="2,4,5", help="other workloads to time briefly ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probs", action="store_true", help="skip timing the attention-weights call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -186,6 +187,47 @@ def time_workload(w, steps, warmup, torch, nys):
     prof = nys.profile_collect()
     nys.profile_enable(False)
     return ms, prof, count, x, spread
+
+
+def time_probs(w, x, steps, warmup, torch, nys):
+    """The same workload through nystrom_attention_probs (the output plus the
+    attention weights F A^+, [B,H,n,m]): step time and the k_probs launch
+    against its compulsory bytes (Q in, weights out, Kt and Z per head)."""
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v"))
+    mask = torch.from_numpy(x["key_mask"]).to(dev) if x["key_mask"] is not None else None
+    conv = torch.from_numpy(x["conv_w"]).to(dev)
+    out = torch.empty_like(q)
+    probs = torch.empty((w.B, w.H, w.n, w.m), dtype=tdt, device=dev)
+
+    def step():
+        nys.attention_with_probs(q, k, v, mask, conv, m=w.m, n_iter=w.n_iter, init_option=w.init_option,
+                                 out=out, probs=probs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nys.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = nys.profile_collect()
+    nys.profile_enable(False)
+    e = 2 if w.dtype == "bf16" else 4
+    BH, M = w.B * w.H, 32 * ((w.m + 31) // 32)
+    nbytes = BH * (w.n * w.d * e + w.n * w.m * e + 2 * 2 * M * w.d + 4 * M * M)
+    tot, cnt = prof["k_probs"]
+    us = 1e3 * tot / cnt
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"call": "nystrom_attention_probs", "ms_per_step": round(ms, 5), "kernel": "k_probs",
+            "kernel_avg_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes,
+            "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -406,6 +448,8 @@ def main():
                      "path_roofline_us": round(1e6 * max(pathb / (HBM_PEAK_GBS * 1e9),
                                                          fl / (MFMA_PEAK_TFLOPS[wi.dtype] * 1e12)), 2),
                      "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
+    weights = None if args.no_probs else time_probs(w, x, max(5, args.steps // 5), max(2, args.warmup // 2),
+                                                    torch, nys)
     copy_gbs = copy_bandwidth(torch)
     roofline["attainable_copy_GBps"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
@@ -423,7 +467,7 @@ def main():
         "step_us": spread,
         "roofline": roofline, "path": path, "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()}
                                                          for k, v in kern.items()},
-        "cpu_baseline": cpu, "also": also, "source_sha": sha,
+        "cpu_baseline": cpu, "also": also, "attention_weights": weights, "source_sha": sha,
     }
     print(json.dumps(line))
 

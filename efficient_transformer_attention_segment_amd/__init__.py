@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = [
-    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention",
+    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs",
     "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
     "profile_enable", "profile_collect",
     "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
@@ -56,6 +56,9 @@ def _load():
     lib.nystrom_attention_ex.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                          _P, _L, _L, _L, _P]
     lib.nystrom_attention_ex.restype = _I
+    lib.nystrom_attention_probs.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                            _P, _L, _L, _L, _P, _P]
+    lib.nystrom_attention_probs.restype = _I
     lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
     lib.nystrom_last_error.argtypes = []
@@ -172,6 +175,36 @@ def attention(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0
     import torch
     fn = nystrom_attention_bf16 if q.dtype == torch.bfloat16 else nystrom_attention
     return fn(q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream)
+
+
+def attention_with_probs(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0, out=None,
+                         probs=None, stream=None):
+    """The attention output and the attention weights (output_attentions):
+    probs [B,H,n,m] = F A^+ when m < n, the exact softmax [B,H,n,n] when
+    m == n; both in q's dtype (float32 or bfloat16).  q, k, v (sharing
+    strides) and out may be strided views with contiguous channels; probs
+    is dense.  Returns (out, probs)."""
+    import torch
+    if not (k.shape == v.shape == q.shape):
+        raise ValueError("q, k and v must have one shape [B, H, n, d]")
+    if q.stride() != k.stride() or k.stride() != v.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k and v must share strides, with contiguous channels")
+    B, H, n, d = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if out.shape != q.shape or out.stride(-1) != 1:
+        raise ValueError("out must be [B, H, n, d] with contiguous channels")
+    if probs is None:
+        probs = torch.empty((B, H, n, m), dtype=q.dtype, device=q.device)
+    if probs.shape != (B, H, n, m) or not probs.is_contiguous():
+        raise ValueError("probs must be a dense [B, H, n, m] tensor")
+    dtype = 1 if q.dtype == torch.bfloat16 else 0
+    ksize = CONV_TAPS if conv_w is None else int(conv_w.shape[-1])
+    lib = _load()
+    _check(lib.nystrom_attention_probs(dtype, _ptr(q), _ptr(k), _ptr(v), *q.stride()[:3], _ptr(key_mask),
+                                       _ptr(conv_w), ksize, B, H, n, d, m, n_iter, init_option, _ptr(out),
+                                       *out.stride()[:3], _ptr(probs), _stream(stream)))
+    return out, probs
 
 
 def workspace_bytes(B, H, n, d, m) -> int:

@@ -38,6 +38,7 @@
 #include "k_merge.hpp"
 #include "k_out.hpp"
 #include "k_pinv.hpp"
+#include "k_probs.hpp"
 
 using namespace nys;
 
@@ -68,6 +69,7 @@ struct Plan {
   int mr;       // landmarks of the method; m is mr rounded up to a multiple of 32
   bool record;  // keep every intermediate in the workspace (stage hook)
   Strides si, so;  // element strides of q, k, v and of out
+  void* probs;     // attention weights [B, H, n, mr] on request, else null
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
   size_t off_slots, off_junk;
@@ -412,13 +414,38 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     const int orc = pad ? launch_out(k_out<IO, M, true>) : launch_out(k_out<IO, M, false>);
     if (orc != NYS_OK) return orc;
   }
+
+  if (p.probs != nullptr) {
+    ProbsArgs pr{};
+    pr.q = q;
+    pr.kt_hi = la.kt_hi;
+    pr.kt_lo = la.kt_lo;
+    pr.Z = Zfinal;
+    pr.probs = p.probs;
+    pr.n = p.n;
+    pr.H = p.H;
+    pr.mr = p.mr;
+    pr.ldp = p.mr;
+    pr.lscale = s4;
+    pr.in = p.si;
+    using PL = ProbsLayout<IO, M>;
+    const int ntb = (p.n + PROBS_TOK - 1) / PROBS_TOK;
+    const dim3 grid(((ntb + 7) / 8) * 8 * PL::NCB, p.BH);
+    auto launch_probs = [&](auto kern) -> int {
+      HIP_TRY(allow_lds(kern, PL::LDS_BYTES));
+      HIP_TRY(launch("k_probs", kern, grid, dim3(256), (uint32_t)PL::LDS_BYTES, st, pr));
+      return NYS_OK;
+    };
+    const int prc = pad ? launch_probs(k_probs<IO, M, true>) : launch_probs(k_probs<IO, M, false>);
+    if (prc != NYS_OK) return prc;
+  }
   return NYS_OK;
 }
 
 template <typename IO>
 int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, const void* k, const void* v,
                  const uint8_t* mask,
-                 const float* conv_w, int conv_k, void* out, hipStream_t st) {
+                 const float* conv_w, int conv_k, void* out, void* probs, hipStream_t st) {
   ExactArgs ea;
   ea.q = q;
   ea.k = k;
@@ -435,6 +462,21 @@ int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, con
   const size_t lds = exact_lds_bytes<IO>();
   HIP_TRY(allow_lds(k_exact<IO>, lds));
   HIP_TRY(launch("k_exact", k_exact<IO>, dim3((n + 63) / 64, B * H), dim3(256), (uint32_t)lds, st, ea));
+  if (probs != nullptr) {
+    ProbsArgs pr{};
+    pr.q = q;
+    pr.k = k;
+    pr.key_mask = mask;
+    pr.probs = probs;
+    pr.n = n;
+    pr.H = H;
+    pr.mr = n;
+    pr.ldp = n;
+    pr.lscale = ea.lscale;
+    pr.in = si;
+    HIP_TRY(launch("k_exact_probs", k_exact_probs<IO>, dim3((n + 4 * XPROBS_Q - 1) / (4 * XPROBS_Q), B * H),
+                   dim3(256), 0, st, pr));
+  }
   return NYS_OK;
 }
 
@@ -514,6 +556,24 @@ int check_strides(int esize, const void* q, const void* k, const void* v, const 
   return NYS_OK;
 }
 
+// The weights buffer: dense [B, H, n, m] (n x n when m == n), 16-byte
+// aligned, overlapping none of q, k, v and out.
+int check_probs(int esize, const void* q, const void* k, const void* v, const void* out, const void* probs,
+                Strides si, Strides so, int B, int H, int n, int m) {
+  if (reinterpret_cast<uintptr_t>(probs) % 16 != 0) return fail(NYS_ERR_INVALID, "probs must be 16-byte aligned");
+  const char* const pb = static_cast<const char*>(probs);
+  const char* const pe = pb + (size_t)B * H * n * m * esize;
+  const void* const views[4] = {q, k, v, out};
+  for (int i = 0; i < 4; ++i) {
+    long long lo, hi;
+    view_range(i < 3 ? si : so, B, H, n, lo, hi);
+    const char* const b = static_cast<const char*>(views[i]);
+    if (pb < b + (hi + 1) * esize && b + lo * esize < pe)
+      return fail(NYS_ERR_INVALID, "probs overlaps %s", i < 3 ? "an input" : "out");
+  }
+  return NYS_OK;
+}
+
 int validate(int esize, const void* q, const void* k, const void* v, int B, int H, int n, int d, int m, int n_iter,
              int init_option, const void* out) {
   if (!q || !k || !v || !out) return fail(NYS_ERR_INVALID, "q, k, v and out must be non-NULL");
@@ -537,21 +597,27 @@ template <typename IO>
 int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* mask, const float* conv_w, int conv_k,
         Strides so, int B,
         int H, int n,
-        int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout) {
+        int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout,
+        void* probs = nullptr) {
   int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
   if (rc != NYS_OK) return rc;
   rc = check_strides(sizeof(IO), q, k, v, out, si, so, B, H, n);
   if (rc != NYS_OK) return rc;
+  if (probs != nullptr) {
+    rc = check_probs(sizeof(IO), q, k, v, out, probs, si, so, B, H, n, m);
+    if (rc != NYS_OK) return rc;
+  }
   if (conv_w != nullptr) {
     if (conv_k < 1 || conv_k % 2 == 0)
       return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
-  if (m == n) return launch_exact<IO>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, st);
+  if (m == n) return launch_exact<IO>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
   Plan p = make_plan(B, H, n, m);
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
   p.si = si;
   p.so = so;
+  p.probs = probs;
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
@@ -638,6 +704,28 @@ __attribute__((visibility("default"))) int nystrom_attention_ex(
     if (dtype == 1)
       return run<u16>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
                       stream, nullptr, nullptr);
+    return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_probs(
+    int dtype, const void* q, const void* k, const void* v, long long in_batch_stride, long long in_head_stride,
+    long long in_token_stride, const uint8_t* key_mask, const float* conv_w, int conv_kernel_size, int B, int H, int n,
+    int d, int m, int n_iter, int init_option, void* out, long long out_batch_stride, long long out_head_stride,
+    long long out_token_stride, void* probs, struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    if (probs == nullptr) return fail(NYS_ERR_INVALID, "probs must be non-NULL");
+    const Strides si{in_batch_stride, in_head_stride, in_token_stride};
+    const Strides so{out_batch_stride, out_head_stride, out_token_stride};
+    if (dtype == 0)
+      return run<float>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                        stream, nullptr, nullptr, probs);
+    if (dtype == 1)
+      return run<u16>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                      stream, nullptr, nullptr, probs);
     return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");

@@ -131,6 +131,29 @@ int nystrom_attention_ex(int dtype, const void* q, const void* k, const void* v,
                          long long out_batch_stride, long long out_head_stride,
                          long long out_token_stride, struct ihipStream_t* stream);
 
+/* nystrom_attention_ex, and also the attention weights (output_attentions).
+ *
+ * Page [P1] section 2.4 names attention_probs = kernel_1 times the iterative
+ * inverse of kernel_2, F Z, an n x m matrix whose rows are the approximate
+ * attention weights; sections 2.7 and 5.3 say output_attentions returns
+ * them (the full n x n softmax when the exact branch runs).  So:
+ *   m <  n: probs [B, H, n, m] = F Z (the key mask does not enter F or A);
+ *   m == n: probs [B, H, n, n] = softmax(q k^T / sqrt(d) + mask), masked
+ *           keys 0, a row with no kept key all zeros.
+ * probs is a dense DEVICE buffer of the call's dtype (float32 or bf16),
+ * 16-byte aligned, owned by the caller, overlapping none of q, k, v and out.
+ * Every other argument, and the output, as nystrom_attention_ex.  Errors:
+ * as nystrom_attention_ex; NYS_ERR_INVALID also for a NULL, unaligned or
+ * overlapping probs (nothing launched). */
+int nystrom_attention_probs(int dtype, const void* q, const void* k, const void* v,
+                            long long in_batch_stride, long long in_head_stride,
+                            long long in_token_stride, const uint8_t* key_mask,
+                            const float* conv_w, int conv_kernel_size, int B, int H,
+                            int n, int d, int m, int n_iter, int init_option, void* out,
+                            long long out_batch_stride, long long out_head_stride,
+                            long long out_token_stride, void* probs,
+                            struct ihipStream_t* stream);
+
 /* Bytes of device workspace a call of this shape uses (0 for invalid or
  * unsupported shapes). */
 size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);

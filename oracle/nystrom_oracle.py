@@ -46,7 +46,7 @@ R11 the convolution is a cross-correlation (tap j multiplies V at offset
     j - K//2), zero outside [0, n), one filter per head shared by all d
     columns;
 R12 n_iter = 0 is allowed and returns Z_0;
-R13 the weights returned on request (output_attentions, P1 2.7 and 5.3)
+R17 the weights returned on request (output_attentions, P1 2.7 and 5.3)
     are the matrix P1 2.4 calls attention_probs, F Z (n x m, whose rows
     are the approximate attention weights; 2.7 and 5.3 name its size
     "m x n" loosely), and the full softmax(Qs Ks^T + mask) (n x n) when
@@ -183,7 +183,7 @@ def exact_attention(qs, ks, v, key_valid=None):
 
 def attention_probs(q, k, key_mask=None, m=64, n_iter=6, init_option=INIT_ORIGINAL):
     """[P1 2.4, 2.7, 5.3] The attention weights handed back on request
-    (output_attentions), R13.
+    (output_attentions), R17.
 
     Nystrom path: F Z, kernel_1 times the iterative inverse of kernel_2,
     [B,H,n,m] (the mask does not enter F or A, R7).  When m == n (R2): the

@@ -111,6 +111,17 @@ def test_strided_validation(lib, kw, code):
     assert lib.nystrom_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("probs", [None, FAKE, FAKE2, ctypes.c_void_p(0x500008), ctypes.c_void_p(0x11fff0)])
+def test_probs_validation(lib, probs):
+    """nystrom_attention_probs rejects a NULL, misaligned or overlapping
+    weights buffer (q, k, v at FAKE, out at FAKE2) before any launch."""
+    B, H, n = 1, 2, 256
+    rc = lib.nystrom_attention_probs(0, FAKE, FAKE, FAKE, H * n * 64, n * 64, 64, NULL, NULL, 65, B, H, n, 64, 64,
+                                     6, 0, FAKE2, H * n * 64, n * 64, 64, probs, NULL)
+    assert rc == -1
+    assert "probs" in lib.nystrom_last_error().decode()
+
+
 @pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
 def test_landmarks_above_256_unsupported(lib, fn):
     assert call(lib, fn, n=600, m=300) == -2
