@@ -46,6 +46,10 @@ R11 the convolution is a cross-correlation (tap j multiplies V at offset
     j - K//2), zero outside [0, n), one filter per head shared by all d
     columns;
 R12 n_iter = 0 is allowed and returns Z_0;
+R18 the self-attention module (P1 2.2, 2.7): q, k, v are x W^T + b for
+    the stacked query, key and value weights [3 H d, hidden], split into
+    heads as (batch, heads, seq, head_dim); the context goes back to
+    (batch, seq, H d) with head h in columns [h d, (h + 1) d);
 R17 the weights returned on request (output_attentions, P1 2.7 and 5.3)
     are the matrix P1 2.4 calls attention_probs, F Z (n x m, whose rows
     are the approximate attention weights; 2.7 and 5.3 name its size
@@ -179,6 +183,32 @@ def exact_attention(qs, ks, v, key_valid=None):
     m == n (R2), with the key mask applied to the scores (R3)."""
     P = softmax_rows(qs @ np.swapaxes(ks, -1, -2), key_valid)
     return P @ v
+
+
+def self_attention(x, w_qkv, b_qkv, H, key_mask=None, conv_w=None, m=64, n_iter=6,
+                   init_option=INIT_ORIGINAL, return_qkv=False):
+    """[P1 2.2, 2.7] The self-attention module around the core (R18).
+
+    x: [B, n, hidden]; w_qkv: [3 H d, hidden], the query, key and value
+    projection weights stacked in that order (each nn.Linear's [out, in]);
+    b_qkv: [3 H d] or None.  q, k, v = x W^T + b per projection, each split
+    into H heads of d columns -> [B, H, n, d]; the attention output
+    [B, H, n, d] goes back to [B, n, H d].  With ``return_qkv`` also
+    returns the projection [B, n, 3, H, d]."""
+    x = _f64(x)
+    w = _f64(w_qkv)
+    B, n, hidden = x.shape
+    if w.ndim != 2 or w.shape[1] != hidden or w.shape[0] % (3 * H) != 0:
+        raise ValueError("w_qkv must be [3 H d, hidden]")
+    d = w.shape[0] // (3 * H)
+    y = x @ w.T
+    if b_qkv is not None:
+        y = y + _f64(b_qkv)
+    qkv = y.reshape(B, n, 3, H, d)
+    q, k, v = (np.transpose(qkv[:, :, i], (0, 2, 1, 3)) for i in range(3))
+    ctx = nystrom_attention(q, k, v, key_mask, conv_w, m, n_iter, init_option)
+    out = np.transpose(ctx, (0, 2, 1, 3)).reshape(B, n, H * d)
+    return (out, qkv) if return_qkv else out
 
 
 def attention_probs(q, k, key_mask=None, m=64, n_iter=6, init_option=INIT_ORIGINAL):

@@ -519,6 +519,43 @@ def pin_probs_output_consistency(O):
     return err
 
 
+# ---------------------------------------------------------------- module ---
+
+def pin_module_identity_projection(O):
+    """[P1 2.2, 2.7] With hidden = 3 H d, W = I and b = 0, x is q, k, v laid
+    side by side per token: the module must equal the core on those q, k, v
+    (head h of q in columns [h d, (h + 1) d) of the first third), with the
+    context's head h back in columns [h d, (h + 1) d)."""
+    rng = RNG(41)
+    B, H, n, d, m = 2, 3, 32, 8, 8
+    q, k, v = (rng.standard_normal((B, H, n, d)) for _ in range(3))
+    w = rng.standard_normal((H, 65)) * 0.02
+    mask = (np.arange(n)[None] < np.array([32, 20])[:, None]).astype(np.uint8)
+    x = np.zeros((B, n, 3 * H * d))
+    for i, t in enumerate((q, k, v)):
+        for h in range(H):
+            x[:, :, (i * H + h) * d:(i * H + h + 1) * d] = t[:, h]
+    got = O.self_attention(x, np.eye(3 * H * d), None, H, mask, w, m=m)
+    core = O.nystrom_attention(q, k, v, mask, w, m=m)
+    ref = np.zeros((B, n, H * d))
+    for h in range(H):
+        ref[:, :, h * d:(h + 1) * d] = core[:, h]
+    return _rel(got, ref)
+
+
+def pin_module_projection_library(O):
+    """[P1 2.2] The projection is torch's linear layer (x W^T + b), in
+    float64."""
+    rng = RNG(42)
+    B, H, n, d, hidden = 2, 2, 16, 8, 24
+    x = rng.standard_normal((B, n, hidden))
+    wq = rng.standard_normal((3 * H * d, hidden)) * 0.2
+    bq = rng.standard_normal(3 * H * d)
+    _, qkv = O.self_attention(x, wq, bq, H, m=4, return_qkv=True)
+    ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(wq), torch.from_numpy(bq)).numpy()
+    return _rel(qkv.reshape(B, n, -1), ref)
+
+
 ALL_PINS = {
     "scale": (pin_scale, 1e-12),
     "segment_means_direct": (pin_segment_means_direct, 1e-12),
@@ -544,4 +581,6 @@ ALL_PINS = {
     "probs_exact_bruteforce": (pin_probs_exact_bruteforce, 1e-12),
     "probs_converged_inverse": (pin_probs_converged_inverse, 1e-9),
     "probs_output_consistency": (pin_probs_output_consistency, 1e-12),
+    "module_identity_projection": (pin_module_identity_projection, 1e-13),
+    "module_projection_library": (pin_module_projection_library, 1e-13),
 }

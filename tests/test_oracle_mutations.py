@@ -121,6 +121,29 @@ def _probs_factory(mode):
     return probs
 
 
+def _module_factory(mode):
+    def module(x, w_qkv, b_qkv, H, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0, return_qkv=False):
+        x = np.asarray(x, np.float64)
+        w = np.asarray(w_qkv, np.float64)
+        B, n, _ = x.shape
+        d = w.shape[0] // (3 * H)
+        y = x @ w.T + (0 if b_qkv is None else np.asarray(b_qkv, np.float64))
+        if mode == "heads_outer":
+            qkv = y.reshape(B, n, H, 3, d).transpose(0, 1, 3, 2, 4)
+        else:
+            qkv = y.reshape(B, n, 3, H, d)
+        q, k, v = (np.transpose(qkv[:, :, i], (0, 2, 1, 3)) for i in range(3))
+        if mode == "k_v_swapped":
+            k, v = v, k
+        ctx = O.nystrom_attention(q, k, v, key_mask, conv_w, m, n_iter, init_option)
+        if mode == "context_heads_inner":
+            out = np.transpose(ctx, (0, 2, 3, 1)).reshape(B, n, H * d)
+        else:
+            out = np.transpose(ctx, (0, 2, 1, 3)).reshape(B, n, H * d)
+        return (out, qkv) if return_qkv else out
+    return module
+
+
 MUTANTS = {
     "scale_double": ({"scale_qk": _scale_double}, ["scale", "exact_sdpa"]),
     "scale_q_only": ({"scale_qk": _scale_q_only}, ["scale"]),
@@ -149,6 +172,10 @@ MUTANTS = {
     "probs_a_not_inverted": ({"attention_probs": _probs_factory("a_not_inverted")},
                              ["probs_converged_inverse", "probs_output_consistency"]),
     "probs_exact_no_mask": ({"attention_probs": _probs_factory("exact_no_mask")}, ["probs_exact_bruteforce"]),
+    "module_heads_outer": ({"self_attention": _module_factory("heads_outer")}, ["module_identity_projection"]),
+    "module_k_v_swapped": ({"self_attention": _module_factory("k_v_swapped")}, ["module_identity_projection"]),
+    "module_context_heads_inner": ({"self_attention": _module_factory("context_heads_inner")},
+                                   ["module_identity_projection"]),
 }
 
 
