@@ -44,6 +44,7 @@ def parse_args():
     ap.add_argument("--also", default="2,4,5", help="other workloads to time briefly ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probs", action="store_true", help="skip timing the attention-weights call")
+    ap.add_argument("--no-module", action="store_true", help="skip timing the self-attention module call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -228,6 +229,44 @@ def time_probs(w, x, steps, warmup, torch, nys):
     return {"call": "nystrom_attention_probs", "ms_per_step": round(ms, 5), "kernel": "k_probs",
             "kernel_avg_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes,
             "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def time_module(w, steps, warmup, torch, nys, core_ms):
+    """The self-attention module at the workload's shape (hidden = H d): the
+    stacked q/k/v projection (one hipBLASLt GEMM) and the attention reading
+    its output in place.  The projection's share is the step time minus the
+    attention-only step time measured above."""
+    from efficient_transformer_attention_segment_amd.workloads import make_module_inputs
+    hidden = w.H * w.d
+    inp = make_module_inputs(w.B, w.n, hidden, w.H, w.d, seed=2000 + w.index, dtype=w.dtype,
+                             lengths=None if w.mask is None else [w.mask[1]] * w.B)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x, wq, bq = (torch.from_numpy(inp[k]).to(dev).to(tdt) for k in ("x", "w_qkv", "b_qkv"))
+    cw = torch.from_numpy(inp["conv_w"]).to(dev)
+    km = torch.from_numpy(inp["key_mask"]).to(dev) if inp["key_mask"] is not None else None
+    qkv = torch.empty((w.B, w.n, 3, w.H, w.d), dtype=tdt, device=dev)
+    out = torch.empty((w.B, w.n, hidden), dtype=tdt, device=dev)
+
+    def step():
+        nys.self_attention(x, wq, bq, w.H, km, cw, m=w.m, n_iter=w.n_iter, init_option=w.init_option, qkv=qkv,
+                           out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 2 * w.B * w.n * hidden * 3 * w.H * w.d
+    proj_ms = ms - core_ms
+    return {"call": "nystrom_self_attention", "hidden": hidden, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.tokens / (ms / 1e3), 1), "projection_flops": flops,
+            "projection_ms_est": round(proj_ms, 5),
+            "projection_tflops_est": round(flops / (proj_ms * 1e-3) / 1e12, 1) if proj_ms > 0 else None,
+            "note": "inputs resident; the projection's time is the step minus the attention-only step"}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -450,6 +489,8 @@ def main():
                      "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
     weights = None if args.no_probs else time_probs(w, x, max(5, args.steps // 5), max(2, args.warmup // 2),
                                                     torch, nys)
+    module = None if args.no_module else time_module(w, max(5, args.steps // 5), max(2, args.warmup // 2), torch,
+                                                     nys, ms)
     copy_gbs = copy_bandwidth(torch)
     roofline["attainable_copy_GBps"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
@@ -467,7 +508,8 @@ def main():
         "step_us": spread,
         "roofline": roofline, "path": path, "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()}
                                                          for k, v in kern.items()},
-        "cpu_baseline": cpu, "also": also, "attention_weights": weights, "source_sha": sha,
+        "cpu_baseline": cpu, "also": also, "attention_weights": weights, "module": module,
+        "source_sha": sha,
     }
     print(json.dumps(line))
 

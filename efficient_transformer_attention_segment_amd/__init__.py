@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = [
-    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs",
+    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs", "self_attention",
     "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
     "profile_enable", "profile_collect",
     "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
@@ -59,6 +59,8 @@ def _load():
     lib.nystrom_attention_probs.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                             _P, _L, _L, _L, _P, _P]
     lib.nystrom_attention_probs.restype = _I
+    lib.nystrom_self_attention.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]
+    lib.nystrom_self_attention.restype = _I
     lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
     lib.nystrom_last_error.argtypes = []
@@ -205,6 +207,35 @@ def attention_with_probs(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, in
                                        _ptr(conv_w), ksize, B, H, n, d, m, n_iter, init_option, _ptr(out),
                                        *out.stride()[:3], _ptr(probs), _stream(stream)))
     return out, probs
+
+
+def self_attention(x, w_qkv, b_qkv, H, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0, qkv=None,
+                   out=None, stream=None):
+    """The self-attention module: x [B, n, hidden] (float32 or bfloat16),
+    w_qkv [3 H d, hidden] (query, key, value weights stacked), b_qkv [3 H d]
+    or None.  Returns (out [B, n, H d], qkv [B, n, 3, H, d])."""
+    import torch
+    B, n, hidden = x.shape
+    if w_qkv.dim() != 2 or w_qkv.shape[1] != hidden or w_qkv.shape[0] % (3 * H) != 0:
+        raise ValueError("w_qkv must be [3 H d, hidden]")
+    d = w_qkv.shape[0] // (3 * H)
+    for t in (x, w_qkv, b_qkv):
+        if t is not None and (not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError("x, w_qkv and b_qkv must be dense and share x's dtype")
+    if qkv is None:
+        qkv = torch.empty((B, n, 3, H, d), dtype=x.dtype, device=x.device)
+    if out is None:
+        out = torch.empty((B, n, H * d), dtype=x.dtype, device=x.device)
+    if tuple(qkv.shape) != (B, n, 3, H, d) or not qkv.is_contiguous():
+        raise ValueError("qkv must be a dense [B, n, 3, H, d] tensor")
+    if tuple(out.shape) != (B, n, H * d) or not out.is_contiguous():
+        raise ValueError("out must be a dense [B, n, H d] tensor")
+    dtype = 1 if x.dtype == torch.bfloat16 else 0
+    ksize = CONV_TAPS if conv_w is None else int(conv_w.shape[-1])
+    _check(_load().nystrom_self_attention(dtype, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(key_mask), _ptr(conv_w),
+                                          ksize, B, n, hidden, H, d, m, n_iter, init_option, _ptr(qkv), _ptr(out),
+                                          _stream(stream)))
+    return out, qkv
 
 
 def workspace_bytes(B, H, n, d, m) -> int:

@@ -25,6 +25,8 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
+    # the module's q/k/v projection is one library GEMM
+    "-lhipblaslt",
 ]
 
 

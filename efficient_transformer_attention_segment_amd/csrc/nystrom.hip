@@ -21,6 +21,7 @@
 // The exact branch (m == n) is one k_exact launch.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
 #include <cmath>
@@ -30,6 +31,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "nystrom.h"
@@ -593,18 +595,16 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
   return NYS_OK;
 }
 
-template <typename IO>
-int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* mask, const float* conv_w, int conv_k,
-        Strides so, int B,
-        int H, int n,
-        int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout,
-        void* probs = nullptr) {
-  int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, out);
+// Every host-side check of an attention call, before anything is enqueued.
+int check_call(int esize, const void* q, const void* k, const void* v, Strides si, const float* conv_w, int conv_k,
+               Strides so, int B, int H, int n, int d, int m, int n_iter, int init_option, const void* out,
+               const void* probs) {
+  int rc = validate(esize, q, k, v, B, H, n, d, m, n_iter, init_option, out);
   if (rc != NYS_OK) return rc;
-  rc = check_strides(sizeof(IO), q, k, v, out, si, so, B, H, n);
+  rc = check_strides(esize, q, k, v, out, si, so, B, H, n);
   if (rc != NYS_OK) return rc;
   if (probs != nullptr) {
-    rc = check_probs(sizeof(IO), q, k, v, out, probs, si, so, B, H, n, m);
+    rc = check_probs(esize, q, k, v, out, probs, si, so, B, H, n, m);
     if (rc != NYS_OK) return rc;
   }
   if (conv_w != nullptr) {
@@ -612,6 +612,17 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
       return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
+  return NYS_OK;
+}
+
+template <typename IO>
+int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* mask, const float* conv_w, int conv_k,
+        Strides so, int B,
+        int H, int n,
+        int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout,
+        void* probs = nullptr) {
+  int rc = check_call(sizeof(IO), q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, probs);
+  if (rc != NYS_OK) return rc;
   if (m == n) return launch_exact<IO>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
   Plan p = make_plan(B, H, n, m);
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
@@ -626,6 +637,131 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
   if (wout) *wout = w;
   if (pout) *pout = p;
   return rc;
+}
+
+// ------------------------------------------- module: the q/k/v projection ---
+// One library GEMM (hipBLASLt) writes x W^T + b as [B n, 3 H d] = [B, n, 3,
+// H, d]; the attention kernels then read q, k, v from it in place through
+// strides and write the context as [B, n, H d].
+struct LtPlan {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  size_t ws = 0;
+};
+std::mutex g_lt_mu;
+std::map<int, hipblasLtHandle_t> g_lt;                                         // per device
+std::map<std::tuple<int, int, int, int, int, bool>, LtPlan> g_lt_plans;        // dev, dtype, rows, hidden, cols, bias
+std::map<std::pair<int, hipStream_t>, Workspace> g_lt_ws;                      // GEMM workspace per stream
+constexpr size_t LT_MAX_WS = 32u << 20;
+
+#define LT_TRY(expr)                                                                                  \
+  do {                                                                                              \
+    hipblasStatus_t s_ = (expr);                                                                    \
+    if (s_ != HIPBLAS_STATUS_SUCCESS) return fail(NYS_ERR_HIP, "%s: hipBLASLt status %d", #expr, (int)s_); \
+  } while (0)
+
+// y[rows][cols] = x[rows][hidden] W[cols][hidden]^T (+ bias[cols]), row-major,
+// float32 accumulation.  In column-major terms y^T = op_T(W) x^T.
+template <typename IO>
+int qkv_projection(const void* x, const void* w, const void* bias, int rows, int hidden, int cols, void* y,
+                   hipStream_t st) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_lt_mu);
+  hipblasLtHandle_t& h = g_lt[dev];
+  if (h == nullptr) LT_TRY(hipblasLtCreate(&h));
+  const hipDataType t = sizeof(IO) == 4 ? HIP_R_32F : HIP_R_16BF;
+  const auto key = std::make_tuple(dev, (int)sizeof(IO), rows, hidden, cols, bias != nullptr);
+  auto it = g_lt_plans.find(key);
+  if (it == g_lt_plans.end()) {
+    LtPlan p;
+    LT_TRY(hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F));
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta));
+    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb));
+    if (bias != nullptr) {
+      const hipblasLtEpilogue_t epi = HIPBLASLT_EPILOGUE_BIAS;
+      const int32_t bt = t;
+      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi));
+      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bt, sizeof bt));
+      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias));
+    }
+    LT_TRY(hipblasLtMatrixLayoutCreate(&p.la, t, hidden, cols, hidden));
+    LT_TRY(hipblasLtMatrixLayoutCreate(&p.lb, t, hidden, rows, hidden));
+    LT_TRY(hipblasLtMatrixLayoutCreate(&p.lc, t, cols, rows, cols));
+    hipblasLtMatmulPreference_t pref = nullptr;
+    LT_TRY(hipblasLtMatmulPreferenceCreate(&pref));
+    const uint64_t wsmax = LT_MAX_WS;
+    hipblasStatus_t s0 =
+        hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax, sizeof wsmax);
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int nres = 0;
+    if (s0 == HIPBLAS_STATUS_SUCCESS)
+      s0 = hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.la, p.lb, p.lc, p.lc, pref, 1, res, &nres);
+    (void)hipblasLtMatmulPreferenceDestroy(pref);
+    LT_TRY(s0);
+    if (nres < 1) return fail(NYS_ERR_UNSUPPORTED, "hipBLASLt has no algorithm for the %d x %d x %d projection", rows,
+                              cols, hidden);
+    p.algo = res[0].algo;
+    p.ws = res[0].workspaceSize;
+    it = g_lt_plans.emplace(key, p).first;
+  }
+  LtPlan& p = it->second;
+  if (bias != nullptr)
+    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias));
+  Workspace& ws = g_lt_ws[{dev, st}];
+  if (ws.cap < p.ws) {
+    HIP_TRY(hipStreamSynchronize(st));
+    if (ws.buf) HIP_TRY(hipFree(ws.buf));
+    ws.buf = nullptr;
+    ws.cap = 0;
+    HIP_TRY(hipMalloc(&ws.buf, p.ws));
+    ws.cap = p.ws;
+  }
+  const float alpha = 1.f, beta = 0.f;
+  LT_TRY(hipblasLtMatmul(h, p.op, &alpha, w, p.la, x, p.lb, &beta, y, p.lc, y, p.lc, &p.algo, ws.buf, p.ws, st));
+  return NYS_OK;
+}
+
+// Byte ranges [a, a + an) and [b, b + bn) intersect.
+bool ranges_meet(const void* a, size_t an, const void* b, size_t bn) {
+  const char* const pa = static_cast<const char*>(a);
+  const char* const pb = static_cast<const char*>(b);
+  return pa < pb + bn && pb < pa + an;
+}
+
+template <typename IO>
+int run_module(const void* x, const void* w, const void* b, const uint8_t* mask, const float* conv_w, int conv_k,
+               int B, int n, int hidden, int H, int d, int m, int n_iter, int init_option, void* qkv, void* out,
+               hipStream_t st) {
+  if (!x || !w || !qkv || !out) return fail(NYS_ERR_INVALID, "x, w_qkv, qkv and out must be non-NULL");
+  if (B <= 0 || n <= 0 || hidden <= 0 || H <= 0 || d <= 0)
+    return fail(NYS_ERR_INVALID, "B, n, hidden, H, d must be positive (got %d, %d, %d, %d, %d)", B, n, hidden, H, d);
+  const long long rows = (long long)B * n, cols = 3LL * H * d;
+  if (rows > INT32_MAX || cols > INT32_MAX || rows * cols > (1LL << 40))
+    return fail(NYS_ERR_UNSUPPORTED, "projection of %lld x %lld too large", rows, cols);
+  const size_t e = sizeof(IO);
+  if (((size_t)hidden * e) % 16 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(qkv) % 16 != 0)
+    return fail(NYS_ERR_INVALID, "x, w_qkv and qkv must be 16-byte aligned with hidden * element size a multiple of 16");
+  const size_t qkv_bytes = (size_t)rows * cols * e;
+  if (ranges_meet(qkv, qkv_bytes, x, (size_t)rows * hidden * e) ||
+      ranges_meet(qkv, qkv_bytes, w, (size_t)cols * hidden * e) ||
+      (b != nullptr && ranges_meet(qkv, qkv_bytes, b, (size_t)cols * e)) ||
+      ranges_meet(qkv, qkv_bytes, out, (size_t)rows * H * d * e))
+    return fail(NYS_ERR_INVALID, "qkv overlaps x, w_qkv, b_qkv or out");
+  const Strides si{n * cols, d, cols};
+  const Strides so{(long long)n * H * d, d, (long long)H * d};
+  const IO* const q = static_cast<const IO*>(qkv);
+  const IO* const k = q + (size_t)H * d;
+  const IO* const v = q + 2 * (size_t)H * d;
+  int rc = check_call(e, q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, nullptr);
+  if (rc != NYS_OK) return rc;
+  rc = qkv_projection<IO>(x, w, b, (int)rows, hidden, (int)cols, qkv, st);
+  if (rc != NYS_OK) return rc;
+  return run<IO>(q, k, v, si, mask, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, st, nullptr,
+                 nullptr);
 }
 
 }  // namespace
@@ -732,6 +868,24 @@ __attribute__((visibility("default"))) int nystrom_attention_probs(
   }
 }
 
+__attribute__((visibility("default"))) int nystrom_self_attention(
+    int dtype, const void* x, const void* w_qkv, const void* b_qkv, const uint8_t* key_mask, const float* conv_w,
+    int conv_kernel_size, int B, int n, int hidden, int H, int d, int m, int n_iter, int init_option, void* qkv,
+    void* out, struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    if (dtype == 0)
+      return run_module<float>(x, w_qkv, b_qkv, key_mask, conv_w, conv_kernel_size, B, n, hidden, H, d, m, n_iter,
+                               init_option, qkv, out, stream);
+    if (dtype == 1)
+      return run_module<u16>(x, w_qkv, b_qkv, key_mask, conv_w, conv_kernel_size, B, n, hidden, H, d, m, n_iter,
+                             init_option, qkv, out, stream);
+    return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
 __attribute__((visibility("default"))) size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m) {
   if (B <= 0 || H <= 0 || n <= 0 || d != HD || m <= 0 || m > n || n % m != 0) return 0;
   if (m == n) return 0;
@@ -747,6 +901,11 @@ __attribute__((visibility("default"))) void nystrom_release(void) {
     if (kv.second.buf) (void)hipFree(kv.second.buf);
   }
   g_ws.clear();
+  std::lock_guard<std::mutex> lk2(g_lt_mu);
+  for (auto& kv : g_lt_ws) {
+    if (kv.second.buf) (void)hipFree(kv.second.buf);
+  }
+  g_lt_ws.clear();
 }
 
 __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const void* q, const void* k,

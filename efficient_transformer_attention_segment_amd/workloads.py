@@ -117,3 +117,25 @@ def make_custom(B, H, n, d, seed, dtype="fp32", scale=1.0, lengths=None,
     if dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     return dict(q=q, k=k, v=v, key_mask=key_mask, conv_w=conv_w, lengths=lengths)
+
+
+def make_module_inputs(B, n, hidden, H, d, seed, dtype="fp32", lengths=None, bias=True):
+    """Inputs of the self-attention module: hidden states x [B, n, hidden]
+    (standard normal), stacked q/k/v projection weights [3 H d, hidden]
+    (normal with standard deviation hidden^-1/2, so the projections have
+    unit scale), biases [3 H d] (0.02 * standard normal) or None, conv
+    weights [H, 65] and right-padding masks as above.  bf16 rounds x, the
+    weights and the biases; the conv weights stay float32."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, n, hidden), dtype=np.float32)
+    w = rng.standard_normal((3 * H * d, hidden), dtype=np.float32) * np.float32(hidden ** -0.5)
+    b = (np.float32(0.02) * rng.standard_normal(3 * H * d, dtype=np.float32)) if bias else None
+    conv_w = np.float32(0.02) * rng.standard_normal((H, CONV_TAPS), dtype=np.float32)
+    key_mask = None
+    if lengths is not None:
+        lengths = np.asarray(lengths)
+        key_mask = (np.arange(n)[None, :] < lengths[:, None]).astype(np.uint8)
+    if dtype == "bf16":
+        x, w = round_bf16(x), round_bf16(w)
+        b = round_bf16(b) if b is not None else None
+    return dict(x=x, w_qkv=w, b_qkv=b, conv_w=conv_w, key_mask=key_mask, H=H, lengths=lengths)

@@ -154,6 +154,30 @@ int nystrom_attention_probs(int dtype, const void* q, const void* k, const void*
                             long long out_token_stride, void* probs,
                             struct ihipStream_t* stream);
 
+/* The self-attention module around the core ([P1] section 2.2: q, k, v come
+ * from three linear projections of the hidden states, split into heads as
+ * (batch, heads, seq, head_dim); section 2.7: the context goes back to
+ * (batch, seq, heads * head_dim)).
+ *
+ *   x      [B, n, hidden]      hidden states (16-byte aligned rows)
+ *   w_qkv  [3 H d, hidden]     query, key and value weights stacked in that
+ *                              order, each in nn.Linear's [out, in] layout
+ *   b_qkv  [3 H d] or NULL     their biases
+ *   qkv    [B, n, 3, H, d]     receives x w_qkv^T + b_qkv (one hipBLASLt GEMM,
+ *                              float32 accumulation, rounded to the dtype);
+ *                              the attention reads q, k, v from it in place
+ *   out    [B, n, H d]         the context, head h in columns [h d, (h+1) d)
+ * All in the dtype (0 float32, 1 bf16), dense, DEVICE memory owned by the
+ * caller; qkv must not overlap x, w_qkv, b_qkv or out.  key_mask, conv_w,
+ * conv_kernel_size, m, n_iter, init_option and the errors as
+ * nystrom_attention_ex; every check runs before the GEMM is enqueued.
+ * NYS_ERR_UNSUPPORTED also when hipBLASLt has no algorithm for the shape. */
+int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const void* b_qkv,
+                           const uint8_t* key_mask, const float* conv_w, int conv_kernel_size,
+                           int B, int n, int hidden, int H, int d, int m, int n_iter,
+                           int init_option, void* qkv, void* out,
+                           struct ihipStream_t* stream);
+
 /* Bytes of device workspace a call of this shape uses (0 for invalid or
  * unsupported shapes). */
 size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);
