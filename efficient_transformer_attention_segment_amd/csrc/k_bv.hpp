@@ -29,34 +29,35 @@
 
 namespace nys {
 
-template <typename IO>
+template <typename IO, int D = HD>
 struct KV {
   static constexpr int NS = IOTraits<IO>::NS;
   static constexpr int KT = 32;         // keys per tile
-  static constexpr int KLD = HD + 8;    // K tile row stride (bf16 elements)
+  static constexpr int KLD = D + 8;     // K tile row stride (bf16 elements)
   static constexpr int VLD = KT + 8;    // V^T tile row stride
   static constexpr int K_ELEMS = KT * KLD;
-  static constexpr int V_ELEMS = HD * VLD;
+  static constexpr int V_ELEMS = D * VLD;
   static constexpr int PART = K_ELEMS + V_ELEMS;                 // hi (or lo) part
   static constexpr int BUF_ELEMS = PART * (NS == 3 ? 2 : 1);
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;            // two buffers
 };
 
-// Register staging: the 256 (row, 16-channel chunk) items of a 32-key tile
-// are spread over the NT threads of the block (ITEMS per thread).
-template <int NT>
+// Register staging: the 32 x (D / 8) (row, 8-channel chunk) items of a
+// 32-key tile are spread over the NT threads of the block (N per thread).
+template <int NT, int D = HD>
 struct Items {
-  static constexpr int N = NT >= 256 ? 1 : 256 / NT;
+  static constexpr int ALL = 4 * D;
+  static constexpr int N = (ALL + NT - 1) / NT;
 };
 
-template <typename IO, int NT>
+template <typename IO, int NT, int D = HD>
 __device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __restrict__ V, long long st, int n,
-                                        int key0, float (&kx)[Items<NT>::N][8], float (&vx)[Items<NT>::N][8]) {
+                                        int key0, float (&kx)[Items<NT, D>::N][8], float (&vx)[Items<NT, D>::N][8]) {
 #pragma unroll
-  for (int u = 0; u < Items<NT>::N; ++u) {
+  for (int u = 0; u < Items<NT, D>::N; ++u) {
     const int item = threadIdx.x + u * NT;
-    const int row = key0 + (item >> 3), cc = item & 7;
-    if (item < 256 && row < n) {
+    const int row = key0 + item / (D / 8), cc = item % (D / 8);
+    if (item < Items<NT, D>::ALL && row < n) {
       IOTraits<IO>::load8(K + row * st + 8 * cc, kx[u]);
       IOTraits<IO>::load8(V + row * st + 8 * cc, vx[u]);
     } else {
@@ -66,15 +67,15 @@ __device__ __forceinline__ void kv_load(const IO* __restrict__ K, const IO* __re
   }
 }
 
-template <typename IO, int NT>
-__device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[Items<NT>::N][8],
-                                         const float (&vx)[Items<NT>::N][8]) {
-  using C = KV<IO>;
+template <typename IO, int NT, int D = HD>
+__device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[Items<NT, D>::N][8],
+                                         const float (&vx)[Items<NT, D>::N][8]) {
+  using C = KV<IO, D>;
 #pragma unroll
-  for (int u = 0; u < Items<NT>::N; ++u) {
+  for (int u = 0; u < Items<NT, D>::N; ++u) {
     const int item = threadIdx.x + u * NT;
-    if (item >= 256) continue;
-    const int kk = item >> 3, cc = item & 7;
+    if (item >= Items<NT, D>::ALL) continue;
+    const int kk = item / (D / 8), cc = item % (D / 8);
     const Frag2 kf = make_frag<C::NS>(kx[u]);
     *reinterpret_cast<bf16x8*>(buf + kk * C::KLD + 8 * cc) = kf.hi;
     if constexpr (C::NS == 3) *reinterpret_cast<bf16x8*>(buf + C::PART + kk * C::KLD + 8 * cc) = kf.lo;
@@ -100,10 +101,11 @@ __device__ __forceinline__ void kv_store(__bf16* buf, const float (&kx)[Items<NT
 // below 2^8, far from float overflow).  A wave-uniform vote picks the path.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int NS, int TPW, bool MASKED>
-__device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 (&vf)[4], const bool (&valid)[8],
-                                           const Frag2 (&qf)[TPW][2], int nown, float lscale2, float (&mrun)[TPW],
-                                           float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
+template <int NS, int TPW, bool MASKED, int D = HD>
+__device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][D / 32], const Frag2 (&vf)[D / 16],
+                                           const bool (&valid)[8], const Frag2 (&qf)[TPW][D / 32], int nown,
+                                           float lscale2, float (&mrun)[TPW], float (&lsum)[TPW],
+                                           f32x4 (&acc)[TPW][D / 16]) {
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
     if (o >= nown) break;
@@ -112,7 +114,7 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 
     for (int kst = 0; kst < 2; ++kst) {
       s[kst] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
+      for (int ks = 0; ks < D / 32; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
     }
     float x[8];
     float tmax = -INFINITY;
@@ -131,7 +133,7 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 
       mrun[o] = mnew;
       lsum[o] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[o][dt] *= alpha;
+      for (int dt = 0; dt < D / 16; ++dt) acc[o][dt] *= alpha;
     }
     float p[8];
 #pragma unroll
@@ -141,16 +143,16 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][2], const Frag2 
     }
     const Frag2 pf = make_frag<NS>(p);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
+    for (int dt = 0; dt < D / 16; ++dt) acc[o][dt] = mma<NS>(vf[dt], pf, acc[o][dt]);
   }
 }
 
 // One 32-key tile from the register-staged layout (K row-major, V^T).
-template <typename IO, int TPW>
-__device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&qf)[TPW][2], int nown, int key0,
+template <typename IO, int TPW, int D = HD>
+__device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&qf)[TPW][D / 32], int nown, int key0,
                                                int n, const uint8_t* __restrict__ mask, float lscale,
-                                               float (&mrun)[TPW], float (&lsum)[TPW], f32x4 (&acc)[TPW][4]) {
-  using C = KV<IO>;
+                                               float (&mrun)[TPW], float (&lsum)[TPW], f32x4 (&acc)[TPW][D / 16]) {
+  using C = KV<IO, D>;
   constexpr int NS = C::NS;
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   bool valid[8];
@@ -163,48 +165,49 @@ __device__ __forceinline__ void kv_tile_update(const __bf16* buf, const Frag2 (&
       if (mask != nullptr && v) v = mask[key] != 0;
       valid[4 * kst + r] = v;
     }
-  Frag2 kf[2][2];
+  Frag2 kf[2][D / 32];
 #pragma unroll
   for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < D / 32; ++ks) {
       const int off = (16 * kst + c16) * C::KLD + 32 * ks + 8 * g;
       kf[kst][ks].hi = *reinterpret_cast<const bf16x8*>(buf + off);
       if constexpr (NS == 3) kf[kst][ks].lo = *reinterpret_cast<const bf16x8*>(buf + C::PART + off);
     }
-  Frag2 vf[4];
+  Frag2 vf[D / 16];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < D / 16; ++dt) {
     const int off = C::K_ELEMS + dmap<false>(dt, c16) * C::VLD + 4 * g;
     vf[dt].hi = cat44(*reinterpret_cast<const bf16x4*>(buf + off), *reinterpret_cast<const bf16x4*>(buf + off + 16));
     if constexpr (NS == 3)
       vf[dt].lo = cat44(*reinterpret_cast<const bf16x4*>(buf + C::PART + off),
                         *reinterpret_cast<const bf16x4*>(buf + C::PART + off + 16));
   }
-  kv_compute<NS, TPW, true>(kf, vf, valid, qf, nown, lscale * LOG2E, mrun, lsum, acc);
+  kv_compute<NS, TPW, true, D>(kf, vf, valid, qf, nown, lscale * LOG2E, mrun, lsum, acc);
 }
 
 // Stream key tiles [tile0, tile1) of one head through the register-staged
 // double buffer (used for float32 I/O and for ragged key ranges).
-template <typename IO, int TPW, int NT, int KP = 1>
+template <typename IO, int TPW, int NT, int KP = 1, int D = HD>
 __device__ __forceinline__ void kv_stream(const IO* __restrict__ K, const IO* __restrict__ V, long long st, int n,
                                           const uint8_t* __restrict__ mask, int tile0, int tile1, float lscale,
-                                          __bf16* lds, const Frag2 (&qf)[TPW][2], int nown, float (&mrun)[TPW],
-                                          float (&lsum)[TPW], f32x4 (&acc)[TPW][4], int kp = 0) {
-  using C = KV<IO>;
-  float kx[Items<NT>::N][8], vx[Items<NT>::N][8];
+                                          __bf16* lds, const Frag2 (&qf)[TPW][D / 32], int nown, float (&mrun)[TPW],
+                                          float (&lsum)[TPW], f32x4 (&acc)[TPW][D / 16], int kp = 0) {
+  using C = KV<IO, D>;
+  float kx[Items<NT, D>::N][8], vx[Items<NT, D>::N][8];
   if (tile0 < tile1) {
-    kv_load<IO, NT>(K, V, st, n, tile0 * C::KT, kx, vx);
-    kv_store<IO, NT>(lds, kx, vx);
+    kv_load<IO, NT, D>(K, V, st, n, tile0 * C::KT, kx, vx);
+    kv_store<IO, NT, D>(lds, kx, vx);
   }
   __syncthreads();
   for (int tile = tile0; tile < tile1; ++tile) {
     const int cur = (tile - tile0) & 1;
     const bool more = tile + 1 < tile1;
-    if (more) kv_load<IO, NT>(K, V, st, n, (tile + 1) * C::KT, kx, vx);
+    if (more) kv_load<IO, NT, D>(K, V, st, n, (tile + 1) * C::KT, kx, vx);
     if (((tile - tile0) % KP) == kp)
-      kv_tile_update<IO, TPW>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum, acc);
-    if (more) kv_store<IO, NT>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
+      kv_tile_update<IO, TPW, D>(lds + cur * C::BUF_ELEMS, qf, nown, tile * C::KT, n, mask, lscale, mrun, lsum,
+                                 acc);
+    if (more) kv_store<IO, NT, D>(lds + (cur ^ 1) * C::BUF_ELEMS, kx, vx);
     __syncthreads();
   }
 }
@@ -324,11 +327,11 @@ struct BvArgs {
   const void* k;
   const void* v;
   const uint8_t* key_mask;  // [B][n] or null
-  const __bf16* qt_hi;      // [BH][M][64]
+  const __bf16* qt_hi;      // [BH][M][d]
   const __bf16* qt_lo;
   float* pmax;              // [BH][S][M]
   float* psum;              // [BH][S][M]
-  float* pacc;              // [BH][S][16][M][4]: 4-channel runs, each run's rows contiguous
+  float* pacc;              // [BH][S][d/4][M][4]: 4-channel runs, each run's rows contiguous
   int n, H, S, tpc, ntiles;
   float lscale;             // d^-1/4 (Qt carries the other factor)
   Strides in;               // of k and v
@@ -347,7 +350,14 @@ constexpr int bv_waves() {
 // take alternate key tiles (KP = 2), both tiles of a pair in the same
 // barrier step, and fold their online-softmax states together in LDS at
 // the end.
-template <typename IO, int M, bool EDGE>
+// LDS the KP = 2 fold of bv_block needs (floats: max, sum and D/4 channel
+// values per lane of each of the TM waves).
+template <int M, int D>
+constexpr int bv_fold_bytes() {
+  return 4 * (M / 16) * 64 * (2 + D / 4);
+}
+
+template <typename IO, int M, bool EDGE, int D = HD>
 __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   constexpr int TM = M / 16;
   constexpr int NW = bv_waves<M>();
@@ -364,20 +374,20 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   const int nown = (kp < KP && wave < TM) ? (TM - wave + NWT - 1) / NWT : 0;
 
-  Frag2 qf[TPW][2];
+  Frag2 qf[TPW][D / 32];
   float mrun[TPW], lsum[TPW];
-  f32x4 acc[TPW][4];
+  f32x4 acc[TPW][D / 16];
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
     const int lt = wave + NWT * o;
     mrun[o] = NEG_BIG;
     lsum[o] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[o][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < D / 16; ++dt) acc[o][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (o < nown) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const size_t off = ((size_t)bh * M + 16 * lt + c16) * HD + 32 * ks + 8 * g;
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const size_t off = ((size_t)bh * M + 16 * lt + c16) * D + 32 * ks + 8 * g;
         qf[o][ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
         qf[o][ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
       }
@@ -388,7 +398,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
   // the landmark fragments arrive before any K/V copy is issued, so the
   // copy pipeline below is never drained to wait for them
   wait_vmcnt<0>();
-  if constexpr (sizeof(IO) == 2) {
+  if constexpr (sizeof(IO) == 2 && D == HD) {
     // whole 32-key tiles by DMA; a ragged last tile (n % 32 != 0) through
     // registers, which zero and mask the keys past n
     const int tfull = min(tile1, a.n / 32);
@@ -401,16 +411,17 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
         kv_stream<IO, TPW, 64 * NW, KP>(K, V, st, a.n, mask, tfull, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc,
                                         kp);
   } else {
-    kv_stream<IO, TPW, 64 * NW, KP>(K, V, st, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc, kp);
+    kv_stream<IO, TPW, 64 * NW, KP, D>(K, V, st, a.n, mask, tile0, tile1, a.lscale, lds, qf, nown, mrun, lsum, acc,
+                                       kp);
   }
   if constexpr (KP == 2) {
     // fold the odd-tile waves' states into the even-tile waves (same lanes)
-    float* st = reinterpret_cast<float*>(lds) + (size_t)wave * 64 * 18 + lane;
+    float* st = reinterpret_cast<float*>(lds) + (size_t)wave * 64 * (2 + D / 4) + lane;
     if (kp == 1 && nown > 0) {
       st[0] = mrun[0];
       st[64] = lsum[0];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[64 * (2 + 4 * dt + r)] = acc[0][dt][r];
     }
@@ -422,7 +433,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
       mrun[0] = mn;
       lsum[0] = lsum[0] * a0 + l1 * a1;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[0][dt][r] = acc[0][dt][r] * a0 + st[64 * (2 + 4 * dt + r)] * a1;
     }
@@ -438,9 +449,9 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
       a.psum[row] = ls;
     }
     // lane (c16, g) holds channels 16 dt + 4 g .. + 3 of row i: run 4 dt + g
-    float* const pr = a.pacc + ((size_t)bh * a.S + chunk) * 16 * M * 4;
+    float* const pr = a.pacc + ((size_t)bh * a.S + chunk) * (D / 4) * M * 4;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < D / 16; ++dt)
       *reinterpret_cast<float4*>(pr + ((size_t)(4 * dt + g) * M + i) * 4) =
           make_float4(acc[o][dt][0], acc[o][dt][1], acc[o][dt][2], acc[o][dt][3]);
   }
@@ -451,7 +462,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
 // EDGE: some padding landmarks (m not a multiple of 32) or a ragged last
 // key tile (n not a multiple of 32); the code for them is compiled only into
 // this instance, so the common shapes pay nothing for it.
-template <typename IO, int M, bool EDGE>
+template <typename IO, int M, bool EDGE, int D = HD>
 __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvA
     return;
   }
   const int id = blockIdx.x - npinv;
-  bv_block<IO, M, EDGE>(ba, id / ba.S, id % ba.S, lds_dyn);
+  bv_block<IO, M, EDGE, D>(ba, id / ba.S, id % ba.S, lds_dyn);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,15 +500,15 @@ struct ExactArgs {
 constexpr int EXACT_WIN = 144;            // conv window rows for 64 queries
 constexpr int EXACT_VWLD = EXACT_WIN + 8;
 
-template <typename IO>
+template <typename IO, int D = HD>
 constexpr int exact_lds_bytes() {
   constexpr int NS = IOTraits<IO>::NS;
-  constexpr int kv = KV<IO>::LDS_BYTES;
-  constexpr int win = HD * EXACT_VWLD * 2 * (NS == 3 ? 2 : 1);
+  constexpr int kv = KV<IO, D>::LDS_BYTES;
+  constexpr int win = D * EXACT_VWLD * 2 * (NS == 3 ? 2 : 1);
   return kv > win ? kv : win;
 }
 
-template <typename IO>
+template <typename IO, int D = HD>
 __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   constexpr int NS = IOTraits<IO>::NS;
@@ -512,9 +523,9 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
 
   const int tok = q0 + 16 * wave + c16;
-  Frag2 qf[1][2];
+  Frag2 qf[1][D / 32];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < D / 32; ++ks) {
     float x[8];
     if (tok < a.n) {
       IOTraits<IO>::load8(Q + tok * st + 32 * ks + 8 * g, x);
@@ -525,26 +536,26 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
     qf[0][ks] = make_frag<NS>(x);
   }
   float mrun[1] = {NEG_BIG}, lsum[1] = {0.f};
-  f32x4 acc[1][4];
+  f32x4 acc[1][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ntiles = (a.n + KV<IO>::KT - 1) / KV<IO>::KT;
-  kv_stream<IO, 1, 256>(K, V, st, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
+  for (int dt = 0; dt < D / 16; ++dt) acc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ntiles = (a.n + KV<IO, D>::KT - 1) / KV<IO, D>::KT;
+  kv_stream<IO, 1, 256, 1, D>(K, V, st, a.n, mask, 0, ntiles, a.lscale, lds_dyn, qf, 1, mrun, lsum, acc);
   const float ls = sum_g(lsum[0]);
   const float inv = ls > 0.f ? 1.0f / ls : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[0][dt] *= inv;
+  for (int dt = 0; dt < D / 16; ++dt) acc[0][dt] *= inv;
   if (a.conv_w != nullptr) {
     __bf16* Vh = lds_dyn;
-    __bf16* Vl = lds_dyn + HD * EXACT_VWLD;
-    stage_v_window<IO>(V, st, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
+    __bf16* Vl = lds_dyn + D * EXACT_VWLD;
+    stage_v_window<IO, D>(V, st, a.n, q0, EXACT_WIN, Vh, Vl, EXACT_VWLD);
     __syncthreads();
     Frag2 tap[3];
     conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
-    conv_tile<NS, false>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
+    conv_tile<NS, false, D>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
   }
   if (tok < a.n)
-    store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, acc[0]);
+    store_row16<IO, false, D>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, acc[0]);
 }
 
 }  // namespace nys

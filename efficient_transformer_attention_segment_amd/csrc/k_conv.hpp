@@ -42,13 +42,15 @@ __device__ __forceinline__ int dmap_run(int dt, int a) {
   return dmap<B16>(dt, 4 * a);
 }
 
-// Store the lane's 16 output channels of one token row.
-template <typename IO, bool B16>
-__device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
+// Store the lane's D / 4 output channels of one token row (B16 order only
+// for D = 64).
+template <typename IO, bool B16, int D = HD>
+__device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[D / 16]) {
+  static_assert(!B16 || D == 64, "the bf16 channel order is defined for d = 64");
   const int g = (threadIdx.x & 63) >> 4;
   if constexpr (sizeof(IO) == 4) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < D / 16; ++dt)
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + dmap<B16>(dt, 4 * g)) =
           make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
   } else if constexpr (B16) {
@@ -63,7 +65,7 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
     }
   } else {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       const uint32_t w0 = pack_bf16x2(acc[dt][0], acc[dt][1]);
       const uint32_t w1 = pack_bf16x2(acc[dt][2], acc[dt][3]);
       *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(row) + 16 * dt + 4 * g) = make_uint2(w0, w1);
@@ -71,14 +73,15 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[4]) {
   }
 }
 
-// Stage V rows [t0 - 32, t0 - 32 + win) of one head, transposed, into
-// Vh[d * ld + row] (and Vl when split).  Rows outside [0, n) are zero.
-template <typename IO>
+// Stage V rows [t0 - 32, t0 - 32 + win) of one head (D channels),
+// transposed, into Vh[d * ld + row] (and Vl when split).  Rows outside
+// [0, n) are zero.
+template <typename IO, int D = HD>
 __device__ void stage_v_window(const IO* __restrict__ V, long long st, int n, int t0, int win, __bf16* Vh, __bf16* Vl,
                                int ld) {
-  constexpr int NS = IOTraits<IO>::NS;
-  for (int idx = threadIdx.x; idx < win * 8; idx += blockDim.x) {
-    const int row = idx >> 3, cc = idx & 7;
+  constexpr int NS = IOTraits<IO>::NS, CPR = D / 8;
+  for (int idx = threadIdx.x; idx < win * CPR; idx += blockDim.x) {
+    const int row = idx / CPR, cc = idx % CPR;
     const int s = t0 - HALO + row;
     float x[8];
     if (s >= 0 && s < n) {
@@ -118,14 +121,14 @@ __device__ __forceinline__ void conv_taps(const float* __restrict__ w, int K, Fr
 // oacc[dt] += conv for the 16-token tile starting at token ts, with the
 // window staged from t0 - 32: wc = ts - t0 (window row of position ts - 32).
 // Reads window rows [wc, wc + 96); the taps beyond the 80 needed are zero.
-template <int NSV, bool B16>
+template <int NSV, bool B16, int D = HD>
 __device__ __forceinline__ void conv_tile(const __bf16* Vh, const __bf16* Vl, int ld, int wc, const Frag2 (&tap)[3],
-                                          f32x4 (&oacc)[4]) {
+                                          f32x4 (&oacc)[D / 16]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       const int base = dmap<B16>(dt, c16) * ld + wc + 32 * kk + 8 * g;
       const bf16x8 vh = *reinterpret_cast<const bf16x8*>(Vh + base);
       oacc[dt] = mfma(vh, tap[kk].hi, oacc[dt]);

@@ -6,8 +6,8 @@
 // section 2.5 (the init scale needs the column and row sums of A).
 //
 // k_landmark: one workgroup reduces `lpw` landmarks of one (batch, head)
-// for both Q and K.  Each landmark's L rows are split over RS row slots of 8
-// threads (each thread owns 8 contiguous channels of a row), summed in
+// for both Q and K.  Each landmark's L rows are split over RS row slots of
+// d / 8 threads (each thread owns 8 contiguous channels of a row), summed in
 // float32 with eight rows in flight per thread, then the RS slots are folded
 // in LDS in a fixed order (deterministic).  The scale d^-1/4 / L is applied
 // once; the landmarks are written in float32 and as bf16 hi/lo operands.
@@ -30,9 +30,9 @@ struct LandmarkArgs {
   Strides in;           // of q and k
   int mr;               // landmarks of the method; m = mr rounded up to 32 (rows mr .. m-1 are zero)
   float scale;          // d^-1/4 / L
-  float* qt;            // [BH][m][64] float32
+  float* qt;            // [BH][m][d] float32
   float* kt;
-  __bf16* qt_hi;        // [BH][m][64] bf16 split of qt / kt
+  __bf16* qt_hi;        // [BH][m][d] bf16 split of qt / kt
   __bf16* qt_lo;
   __bf16* kt_hi;
   __bf16* kt_lo;
@@ -53,10 +53,10 @@ __device__ __forceinline__ void pad_mask_cols(f32x4 (&acc)[TM], int mr) {
 }
 
 // LDS staging of Kt for the Gram (elements): bf16 hi / lo planes with row
-// stride 72 (bf16 I/O) or float32 rows with stride 68 (float32 I/O).
-template <int M, bool F32>
+// stride D + 8 (bf16 I/O) or float32 rows with stride D + 4 (float32 I/O).
+template <int M, bool F32, int D>
 constexpr int gram_kst_bytes() {
-  return F32 ? M * 68 * 4 : 2 * M * 72 * 2;
+  return F32 ? M * (D + 4) * 4 : 2 * M * (D + 8) * 2;
 }
 
 // A = softmax(Qt Kt^T) for one head, by the NW waves of the block; writes A
@@ -64,42 +64,42 @@ constexpr int gram_kst_bytes() {
 // wred[1] to every thread).  M: landmarks padded to a multiple of 32.  Kt comes into LDS (kst,
 // gram_kst_bytes) in one coalesced pass first; each wave takes row tiles
 // wave, wave + NW, ...  csum: LDS scratch of (M/16) * M floats; wred: 2 * NW.
-template <int M, bool F32, int NW>
+template <int M, bool F32, int NW, int D>
 __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, float* wred, void* kst) {
-  constexpr int TM = M / 16;
+  constexpr int TM = M / 16, DK = D / 32, KLD32 = D + 4, KLD16 = D + 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const float* qt = a.qt + (size_t)bh * M * HD;
+  const float* qt = a.qt + (size_t)bh * M * D;
   float* A = a.A + (size_t)bh * M * M;
   float* const kf32 = reinterpret_cast<float*>(kst);
   __bf16* const kb16 = reinterpret_cast<__bf16*>(kst);
   if constexpr (F32) {
-    const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * HD);
-    for (int i = threadIdx.x; i < M * (HD / 4); i += 64 * NW)
-      *reinterpret_cast<float4*>(kf32 + (i >> 4) * 68 + 4 * (i & 15)) = kt[i];
+    const float4* kt = reinterpret_cast<const float4*>(a.kt + (size_t)bh * M * D);
+    for (int i = threadIdx.x; i < M * (D / 4); i += 64 * NW)
+      *reinterpret_cast<float4*>(kf32 + (i / (D / 4)) * KLD32 + 4 * (i % (D / 4))) = kt[i];
   } else {
-    const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * HD);
-    const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * HD);
-    for (int i = threadIdx.x; i < M * (HD / 8); i += 64 * NW) {
-      *reinterpret_cast<uint4*>(kb16 + (i >> 3) * 72 + 8 * (i & 7)) = kh[i];
-      *reinterpret_cast<uint4*>(kb16 + (M + (i >> 3)) * 72 + 8 * (i & 7)) = kl[i];
+    const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * D);
+    const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * D);
+    for (int i = threadIdx.x; i < M * (D / 8); i += 64 * NW) {
+      *reinterpret_cast<uint4*>(kb16 + (i / (D / 8)) * KLD16 + 8 * (i % (D / 8))) = kh[i];
+      *reinterpret_cast<uint4*>(kb16 + (M + i / (D / 8)) * KLD16 + 8 * (i % (D / 8))) = kl[i];
     }
   }
   __syncthreads();
   float rmax_w = 0.f;
   for (int rt = wave; rt < TM; rt += NW) {
     // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
-    float ax[2][8];
-    Frag2 af[2];
+    float ax[DK][8];
+    Frag2 af[DK];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const size_t off = (size_t)(rt * 16 + c16) * HD + ks * 32 + g * 8;
+    for (int ks = 0; ks < DK; ++ks) {
+      const size_t off = (size_t)(rt * 16 + c16) * D + ks * 32 + g * 8;
       if constexpr (F32) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ax[ks][e] = qt[off + e];
       } else {
-        af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + (size_t)bh * M * HD + off);
-        af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + (size_t)bh * M * HD + off);
+        af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + (size_t)bh * M * D + off);
+        af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + (size_t)bh * M * D + off);
       }
     }
     f32x4 acc[TM];
@@ -107,17 +107,17 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
     for (int ct = 0; ct < TM; ++ct) {
       acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < DK; ++ks) {
         const int row = ct * 16 + c16, col = ks * 32 + g * 8;
         if constexpr (F32) {
           float x[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = kf32[row * 68 + col + e];
+          for (int e = 0; e < 8; ++e) x[e] = kf32[row * KLD32 + col + e];
           acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
         } else {
           Frag2 bf;
-          bf.hi = *reinterpret_cast<const bf16x8*>(kb16 + row * 72 + col);
-          bf.lo = *reinterpret_cast<const bf16x8*>(kb16 + (M + row) * 72 + col);
+          bf.hi = *reinterpret_cast<const bf16x8*>(kb16 + row * KLD16 + col);
+          bf.lo = *reinterpret_cast<const bf16x8*>(kb16 + (M + row) * KLD16 + col);
           acc[ct] = mma<3>(af[ks], bf, acc[ct]);
         }
       }
@@ -188,12 +188,12 @@ __device__ void landmark_gram_tail(const LandmarkArgs& a, int bh, float* csum, f
   __syncthreads();
 }
 
-// grid: (m / lpw, BH), block 256, with 8 * RS * lpw == 256.
-template <typename IO, int M>
+// grid: (m / lpw, BH), block 256, with (D / 8) * RS * lpw == 256.
+template <typename IO, int M, int D>
 __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, const IO* __restrict__ k,
                                                    LandmarkArgs a) {
   constexpr int CW = 8;          // channels per thread
-  constexpr int TPR = HD / CW;   // threads per row
+  constexpr int TPR = D / CW;    // threads per row
   constexpr int UNR = 8;         // rows in flight per thread and tensor
   __shared__ float red[2][256][CW + 1];
 
@@ -244,15 +244,15 @@ __global__ __launch_bounds__(256) void k_landmark(const IO* __restrict__ q, cons
     red[1][t][e] = sk[e];
   }
   __syncthreads();
-  for (int idx = t; idx < 2 * lpw * HD; idx += 256) {
-    const int which = idx / (lpw * HD);
-    const int rem = idx % (lpw * HD);
-    const int jj = rem / HD, col = rem % HD;
+  for (int idx = t; idx < 2 * lpw * D; idx += 256) {
+    const int which = idx / (lpw * D);
+    const int rem = idx % (lpw * D);
+    const int jj = rem / D, col = rem % D;
     const int cc = col / CW, e = col % CW;
     float s = 0.f;
     for (int q2 = 0; q2 < RS; ++q2) s += red[which][(jj * RS + q2) * TPR + cc][e];
     s *= a.scale;
-    const size_t o = ((size_t)bh * a.m + blockIdx.x * lpw + jj) * HD + col;
+    const size_t o = ((size_t)bh * a.m + blockIdx.x * lpw + jj) * D + col;
     __bf16 hi, lo;
     split1(s, hi, lo);
     if (which == 0) {
@@ -272,16 +272,16 @@ template <int M>
 constexpr int gram_waves() {
   return M / 16 < 16 ? (M / 16 < 4 ? 4 : M / 16) : 16;
 }
-template <int M, bool F32>
+template <int M, bool F32, int D>
 constexpr int gram_lds_bytes() {
-  return gram_kst_bytes<M, F32>() + 4 * ((M / 16) * M + 2 * gram_waves<M>());
+  return gram_kst_bytes<M, F32, D>() + 4 * ((M / 16) * M + 2 * gram_waves<M>());
 }
-template <int M, bool F32>
+template <int M, bool F32, int D>
 __global__ __launch_bounds__(64 * gram_waves<M>()) void k_gram(LandmarkArgs a) {
   extern __shared__ __align__(16) float gram_smem[];
-  float* const csum = gram_smem + gram_kst_bytes<M, F32>() / 4;
+  float* const csum = gram_smem + gram_kst_bytes<M, F32, D>() / 4;
   float* const wred = csum + (M / 16) * M;
-  landmark_gram_tail<M, F32, gram_waves<M>()>(a, blockIdx.x, csum, wred, gram_smem);
+  landmark_gram_tail<M, F32, gram_waves<M>(), D>(a, blockIdx.x, csum, wred, gram_smem);
 }
 
 }  // namespace nys

@@ -18,8 +18,8 @@
 //      pass's channel order, k in the paired order.
 // B V and W are also written float32 row-major.  The partial sums are
 // stored run-major ([chunk][run][row][4]), so a wave's loads are contiguous.
-// The 16 workgroups of a head are placed on one XCD (block i runs on XCD
-// i mod 8), so the per-row maxima and sums that all 16 read are fetched
+// The d / 4 workgroups of a head are placed on one XCD (block i runs on XCD
+// i mod 8), so the per-row maxima and sums that all of them read are fetched
 // into one L2 only.
 #pragma once
 
@@ -31,26 +31,26 @@ namespace nys {
 struct MergeArgs {
   const float* pmax;   // [BH][S][M], log2 units
   const float* psum;
-  const float* pacc;   // [BH][S][16][M][4]: 4-channel runs, each run's rows contiguous
+  const float* pacc;   // [BH][S][d/4][M][4]: 4-channel runs, each run's rows contiguous
   const float* Z;      // [BH][M][M]
-  float* BV;           // [BH][M][64]
-  float* W;            // [BH][M][64]
-  __bf16* wf_hi;       // [BH][4][M/32][64][8]
+  float* BV;           // [BH][M][d]
+  float* W;            // [BH][M][d]
+  __bf16* wf_hi;       // [BH][d/16][M/32][64][8]
   __bf16* wf_lo;
   int S, BH;
 };
 
-constexpr int MW_RUNS = HD / 4;  // 4-channel runs per head
-
-// Grid size for BH heads: 16 runs per head, heads in groups of 8 (one per
-// XCD); blocks of a missing head return at once.
-inline int mw_blocks(int BH) { return MW_RUNS * 8 * ((BH + 7) / 8); }
+// Grid size for BH heads of D channels: D / 4 runs per head, heads in
+// groups of 8 (one per XCD); blocks of a missing head return at once.
+inline int mw_blocks(int BH, int D) { return (D / 4) * 8 * ((BH + 7) / 8); }
 
 // (head, run) of block id (id % 8 is the block's XCD)
+template <int D>
 __device__ __forceinline__ void mw_role(int id, int& bh, int& run) {
+  constexpr int RUNS = D / 4;
   const int xcd = id & 7, slot = id >> 3;
-  bh = 8 * (slot / MW_RUNS) + xcd;
-  run = slot % MW_RUNS;
+  bh = 8 * (slot / RUNS) + xcd;
+  run = slot % RUNS;
 }
 
 // k slices per row for the W step: the most (up to NT / M) that split the
@@ -78,8 +78,9 @@ struct MwLayout {
 
 // One (head, 4-channel run): merge, W and fragments (see the top of the
 // file), by a block of NT threads.
-template <int M, bool B16, int NT>
+template <int M, bool B16, int NT, int D>
 __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
+  static_assert(!B16 || D == 64, "the bf16 channel order is defined for d = 64");
   using Ly = MwLayout<M, NT>;
   constexpr int SP = Ly::SP, KSP = Ly::KSP, KPER = Ly::KPER, KS = M / 32;
   float* const part = L + Ly::PART;
@@ -117,7 +118,8 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
           const size_t row = base + (size_t)s * M;
           pm[u] = a.pmax[row];
           ps[u] = a.psum[row];
-          const float4 v = *reinterpret_cast<const float4*>(a.pacc + ((row - i) * 16 + (size_t)(ch >> 2) * M + i) * 4);
+          const float4 v =
+              *reinterpret_cast<const float4*>(a.pacc + ((row - i) * (D / 4) + (size_t)(ch >> 2) * M + i) * 4);
           pa[u][0] = v.x;
           pa[u][1] = v.y;
           pa[u][2] = v.z;
@@ -168,7 +170,7 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
     const float4 bv = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     bvs[t] = bv;
-    *reinterpret_cast<float4*>(a.BV + ((size_t)bh * M + t) * HD + ch) = bv;
+    *reinterpret_cast<float4*>(a.BV + ((size_t)bh * M + t) * D + ch) = bv;
   }
   __syncthreads();
 
@@ -216,7 +218,7 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) wt[t * 5 + c] = w[c];
-    *reinterpret_cast<float4*>(a.W + ((size_t)bh * M + t) * HD + ch) = make_float4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<float4*>(a.W + ((size_t)bh * M + t) * D + ch) = make_float4(w[0], w[1], w[2], w[3]);
   }
   __syncthreads();
 
@@ -230,7 +232,7 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = wt[(32 * kb + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4)) * 5 + b];
     const Frag2 f = split8(x);
-    const size_t ent = ((size_t)bh * 4 * KS + (size_t)dt * KS + kb) * 64 + ln;
+    const size_t ent = ((size_t)bh * (D / 16) * KS + (size_t)dt * KS + kb) * 64 + ln;
     *reinterpret_cast<bf16x8*>(a.wf_hi + ent * 8) = f.hi;
     *reinterpret_cast<bf16x8*>(a.wf_lo + ent * 8) = f.lo;
   }
@@ -238,13 +240,13 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
 
 // grid mw_blocks(BH) x NT: NT = M x (chunk subsets per row), chosen by the
 // host so each thread folds at most one batch of 8 chunks where it can.
-template <int M, bool B16, int NT>
+template <int M, bool B16, int NT, int D>
 __global__ __launch_bounds__(NT) void k_mw(MergeArgs a) {
   __shared__ float L[MwLayout<M, NT>::FLOATS];
   int bh, run;
-  mw_role(blockIdx.x, bh, run);
+  mw_role<D>(blockIdx.x, bh, run);
   if (bh >= a.BH) return;
-  mw_body<M, B16, NT>(a, bh, run, L);
+  mw_body<M, B16, NT, D>(a, bh, run, L);
 }
 
 }  // namespace nys

@@ -4,10 +4,12 @@
 // (kernel_1 F = softmax(Q against the key landmarks), n x m; the context is
 // F times A^+ times B V) and section 2.6 (context += depthwise conv of V).
 //
-// k_out (float32 I/O): a workgroup covers 128 tokens of one head (4 waves
-// x 2 tiles of 16).  The key landmarks, the W^T fragments and a V window
-// (tokens t0 - 32 .. t0 + 176) are staged in LDS once, through registers as
-// bf16 hi/lo with V stored transposed, with every wave's Q rows already
+// k_out (float32 I/O, and bf16 I/O at head sizes other than 64): a
+// workgroup covers 128 tokens of one head (4 waves x 2 tiles of 16; 64
+// tokens at d = 128).  The key landmarks, the W^T fragments and a V window
+// (tokens t0 - 32 .. t0 + tokens + 48) are staged in LDS once, through
+// registers as bf16 hi/lo with V stored transposed (landmarks and fragments
+// stay in L2 where LDS cannot hold them), with every wave's Q rows already
 // loading as B fragments.  Per 16-token tile a wave:
 //   forms S^T = Kt Q^T (m x 16) on the matrix cores,
 //   takes the softmax down each column with the whole F row in registers
@@ -15,7 +17,7 @@
 //   accumulates O^T = W^T F^T, F used directly from the S^T C tiles,
 //   adds the convolution as three banded Toeplitz products into the same
 //   accumulators,
-//   and stores 16 contiguous channels per lane.
+//   and stores d / 4 channels per lane.
 // Qt / Kt carry the d^-1/4 factor, Q does not: logits get the other factor.
 #pragma once
 
@@ -31,9 +33,9 @@ struct OutArgs {
   const __bf16* zero;    // >= 128 zero bytes (rows outside the sequence)
   const float* conv_w;   // [H][conv_k] or null
   int conv_k;            // odd taps, 1 .. 65
-  const __bf16* kt_hi;   // [BH][M][64]
+  const __bf16* kt_hi;   // [BH][M][d]
   const __bf16* kt_lo;
-  const __bf16* wf_hi;   // [BH][4][M/32][64][8]
+  const __bf16* wf_hi;   // [BH][d/16][M/32][64][8]
   const __bf16* wf_lo;
   void* out;
   int n, H;
@@ -53,45 +55,55 @@ __device__ __forceinline__ void pad_mask_rows(f32x4 (&sacc)[TM], int mr) {
       if (16 * it + 4 * g + r >= mr) sacc[it][r] = -INFINITY;
 }
 
-constexpr int OUT_TOK = 128;                 // tokens per workgroup
-constexpr int OUT_WIN = OUT_TOK + 80;        // V window rows (t0-32 .. t0+176)
-constexpr int OUT_VWLD = OUT_WIN + 8;
-
-template <typename IO, int M>
+// Tokens per workgroup (4 waves x U tiles of 16) and the V window rows
+// (t0 - 32 .. t0 + TOK + 48) of the generic output pass.
+template <typename IO, int M, int D>
 struct OutLayout {
   static constexpr int NS = IOTraits<IO>::NS;
+  static constexpr int TOK = D > 64 ? 64 : 128;
+  static constexpr int U = TOK / 64;
+  static constexpr int WIN = TOK + 80;
+  static constexpr int VWLD = WIN + 8;
   static constexpr int KS = M / 32;
-  static constexpr int KLD = HD + 8;
+  static constexpr int KLD = D + 8;
   static constexpr int KT_ELEMS = M * KLD;                 // per part
-  static constexpr int WF_ELEMS = 4 * KS * 64 * 8;         // per part
-  static constexpr int V_ELEMS = HD * OUT_VWLD;            // per part
+  static constexpr int WF_ELEMS = (D / 16) * KS * 64 * 8;  // per part
+  static constexpr int V_ELEMS = D * VWLD;                 // per part
   static constexpr int PARTS = NS == 3 ? 2 : 1;
-  // the W^T fragments are staged in LDS when everything fits the 160 KB;
-  // otherwise (float32 I/O above 192 landmarks) they are read from global
-  // memory (L2: every workgroup of the head reads the same fragments)
-  static constexpr bool WF_LDS = 2 * PARTS * (KT_ELEMS + WF_ELEMS + V_ELEMS) <= 160 * 1024;
+  // the key landmarks, then the W^T fragments, are staged in LDS when they
+  // fit the 160 KB beside the V window; otherwise they are read from global
+  // memory (L2: every workgroup of the head reads the same data)
+  static constexpr bool KT_LDS = 2 * PARTS * (KT_ELEMS + V_ELEMS) <= 160 * 1024;
+  static constexpr bool WF_LDS = KT_LDS && 2 * PARTS * (KT_ELEMS + WF_ELEMS + V_ELEMS) <= 160 * 1024;
   static constexpr int OFF_KT = 0;
-  static constexpr int OFF_WF = OFF_KT + PARTS * KT_ELEMS;
+  static constexpr int OFF_WF = OFF_KT + (KT_LDS ? PARTS * KT_ELEMS : 0);
   static constexpr int OFF_V = OFF_WF + (WF_LDS ? PARTS * WF_ELEMS : 0);
   static constexpr int TOTAL = OFF_V + PARTS * V_ELEMS;
   static constexpr int LDS_BYTES = TOTAL * 2;
+  static_assert(LDS_BYTES <= 160 * 1024, "k_out LDS");
 };
 
-template <typename IO, int M, bool PAD>
+// grid (ceil(n / TOK), BH), block 256, dynamic LDS OutLayout::LDS_BYTES.
+template <typename IO, int M, bool PAD, int D = HD>
 __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
-  using Ly = OutLayout<IO, M>;
-  constexpr int NS = Ly::NS, KS = Ly::KS, TM = M / 16;
+  using Ly = OutLayout<IO, M, D>;
+  constexpr int NS = Ly::NS, KS = Ly::KS, TM = M / 16, DK = D / 32, DT = D / 16, U = Ly::U;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, h = bh % a.H;
-  const int t0 = blockIdx.x * OUT_TOK;
+  const int t0 = blockIdx.x * Ly::TOK;
   const IO* Q = reinterpret_cast<const IO*>(a.q) + a.in.base(bh, a.H);
   const IO* V = reinterpret_cast<const IO*>(a.v) + a.in.base(bh, a.H);
   const long long st = a.in.t;
 
-  __bf16* kth = lds_dyn + Ly::OFF_KT;
-  __bf16* ktl = kth + Ly::KT_ELEMS;
+  const __bf16* const ksh = a.kt_hi + (size_t)bh * M * D;
+  const __bf16* const ksl = a.kt_lo + (size_t)bh * M * D;
+  __bf16* const kth_lds = lds_dyn + Ly::OFF_KT;
+  __bf16* const ktl_lds = kth_lds + Ly::KT_ELEMS;
+  const __bf16* const kth = Ly::KT_LDS ? kth_lds : ksh;
+  const __bf16* const ktl = Ly::KT_LDS ? ktl_lds : ksl;
+  constexpr int KROW = Ly::KT_LDS ? Ly::KLD : D;
   const __bf16* const wsh = a.wf_hi + (size_t)bh * Ly::WF_ELEMS;
   const __bf16* const wsl = a.wf_lo + (size_t)bh * Ly::WF_ELEMS;
   __bf16* const wfh_lds = lds_dyn + Ly::OFF_WF;
@@ -101,18 +113,17 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   __bf16* vh = lds_dyn + Ly::OFF_V;
   __bf16* vl = vh + Ly::V_ELEMS;
 
-  static_assert(sizeof(IO) == 4, "the bf16 output pass is k_out_stream");
   // ---- stage Kt, W^T fragments and the V window
   {
-    const __bf16* src_h = a.kt_hi + (size_t)bh * M * HD;
-    const __bf16* src_l = a.kt_lo + (size_t)bh * M * HD;
-    for (int idx = threadIdx.x; idx < M * 8; idx += 256) {
-      const int row = idx >> 3, cc = idx & 7;
-      *reinterpret_cast<bf16x8*>(kth + row * Ly::KLD + 8 * cc) =
-          *reinterpret_cast<const bf16x8*>(src_h + (size_t)row * HD + 8 * cc);
-      if constexpr (NS == 3)
-        *reinterpret_cast<bf16x8*>(ktl + row * Ly::KLD + 8 * cc) =
-            *reinterpret_cast<const bf16x8*>(src_l + (size_t)row * HD + 8 * cc);
+    if constexpr (Ly::KT_LDS) {
+      for (int idx = threadIdx.x; idx < M * (D / 8); idx += 256) {
+        const int row = idx / (D / 8), cc = idx % (D / 8);
+        *reinterpret_cast<bf16x8*>(kth_lds + row * Ly::KLD + 8 * cc) =
+            *reinterpret_cast<const bf16x8*>(ksh + (size_t)row * D + 8 * cc);
+        if constexpr (NS == 3)
+          *reinterpret_cast<bf16x8*>(ktl_lds + row * Ly::KLD + 8 * cc) =
+              *reinterpret_cast<const bf16x8*>(ksl + (size_t)row * D + 8 * cc);
+      }
     }
     if constexpr (Ly::WF_LDS) {
       for (int idx = threadIdx.x; idx < Ly::WF_ELEMS / 8; idx += 256) {
@@ -121,16 +132,16 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
           *reinterpret_cast<bf16x8*>(wfl_lds + 8 * idx) = *reinterpret_cast<const bf16x8*>(wsl + 8 * idx);
       }
     }
-    if (a.conv_w != nullptr) stage_v_window<IO>(V, st, a.n, t0, OUT_WIN, vh, vl, OUT_VWLD);
+    if (a.conv_w != nullptr) stage_v_window<IO, D>(V, st, a.n, t0, Ly::WIN, vh, vl, Ly::VWLD);
   }
-  // Q B fragments of both tiles, in flight with the staging copies
-  Frag2 qf2[2][2];
+  // Q B fragments of the wave's tiles, in flight with the staging copies
+  Frag2 qf2[U][DK];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ts = t0 + 32 * wave + 16 * u;
+  for (int u = 0; u < U; ++u) {
+    const int ts = t0 + 16 * U * wave + 16 * u;
     const int tok = min(ts + c16, a.n - 1);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < DK; ++ks) {
       float x[8];
       IOTraits<IO>::load8(Q + tok * st + 32 * ks + 8 * g, x);
       qf2[u][ks] = make_frag<NS>(x);
@@ -141,22 +152,22 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
   __syncthreads();
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ts = t0 + 32 * wave + 16 * u;  // tile start
+  for (int u = 0; u < U; ++u) {
+    const int ts = t0 + 16 * U * wave + 16 * u;  // tile start
     if (ts >= a.n) continue;
     const int tok = ts + c16;
-    const Frag2(&qf)[2] = qf2[u];
+    const Frag2(&qf)[DK] = qf2[u];
     // S^T = Kt Q^T: sacc[it][r] = logit(tok, landmark 16 it + 4g + r)
     f32x4 sacc[TM];
 #pragma unroll
     for (int it = 0; it < TM; ++it) {
       sacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < DK; ++ks) {
         Frag2 kf;
-        const int off = (16 * it + c16) * Ly::KLD + 32 * ks + 8 * g;
+        const int off = (16 * it + c16) * KROW + 32 * ks + 8 * g;
         kf.hi = *reinterpret_cast<const bf16x8*>(kth + off);
-        kf.lo = *reinterpret_cast<const bf16x8*>(ktl + off);
+        if constexpr (NS == 3) kf.lo = *reinterpret_cast<const bf16x8*>(ktl + off);
         sacc[it] = mma<NS>(kf, qf[ks], sacc[it]);
       }
     }
@@ -181,9 +192,9 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
     sum = sum_g(sum);
     const float inv = 1.0f / sum;
     // O^T = W^T F^T
-    f32x4 oacc[4];
+    f32x4 oacc[DT];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8] = {sacc[2 * ks][0] * inv,     sacc[2 * ks][1] * inv,     sacc[2 * ks][2] * inv,
@@ -191,17 +202,17 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
                     sacc[2 * ks + 1][2] * inv, sacc[2 * ks + 1][3] * inv};
       const Frag2 pf = make_frag<NS>(x);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
         Frag2 wf;
         const int off = ((dt * KS + ks) * 64 + lane) * 8;
         wf.hi = *reinterpret_cast<const bf16x8*>(wfh + off);
-        wf.lo = *reinterpret_cast<const bf16x8*>(wfl + off);
+        if constexpr (NS == 3) wf.lo = *reinterpret_cast<const bf16x8*>(wfl + off);
         oacc[dt] = mma<NS>(wf, pf, oacc[dt]);
       }
     }
-    if (a.conv_w != nullptr) conv_tile<NS, false>(vh, vl, OUT_VWLD, ts - t0, tap, oacc);
+    if (a.conv_w != nullptr) conv_tile<NS, false, D>(vh, vl, Ly::VWLD, ts - t0, tap, oacc);
     if (tok < a.n)
-      store_row16<IO, false>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, oacc);
+      store_row16<IO, false, D>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, oacc);
   }
 }
 

@@ -68,6 +68,7 @@ int fail(int code, const char* fmt, ...) {
 // ---------------------------------------------------------------- plan ---
 struct Plan {
   int B, H, n, m, BH, L, RS, lpw, S, tpc, ntiles, npinv;
+  int D;        // head size
   int mr;       // landmarks of the method; m is mr rounded up to a multiple of 32
   bool record;  // keep every intermediate in the workspace (stage hook)
   Strides si, so;  // element strides of q, k, v and of out
@@ -101,9 +102,10 @@ int pow2floor(int x) {
 // the pseudo-inverse and contribute nothing to W or the output.
 int padded_m(int m) { return (m + 31) & ~31; }
 
-Plan make_plan(int B, int H, int n, int mr) {
+Plan make_plan(int B, int H, int n, int mr, int d) {
   Plan p{};
   const int m = padded_m(mr);
+  p.D = d;
   p.B = B;
   p.H = H;
   p.n = n;
@@ -111,9 +113,11 @@ Plan make_plan(int B, int H, int n, int mr) {
   p.mr = mr;
   p.BH = B * H;
   p.L = n / mr;
-  // landmark blocks: 8 threads per row, RS row slots per landmark, lpw landmarks per block
-  p.RS = std::min(32, std::max(1, pow2floor(std::max(1, p.L / 8))));
-  p.lpw = 32 / p.RS;
+  // landmark blocks: d / 8 threads per row, RS row slots per landmark, lpw
+  // landmarks per block (at most 32, which divides m)
+  const int tpr = d / 8;
+  p.RS = std::min(256 / tpr, std::max(std::max(1, 256 / (tpr * 32)), pow2floor(std::max(1, p.L / 8))));
+  p.lpw = 256 / (tpr * p.RS);
   // key chunks for the B V partials: as many blocks as stay resident in one
   // round next to the pseudo-inverse blocks (two blocks per CU)
   p.ntiles = (n + 31) / 32;  // the last tile is ragged when n % 32 != 0
@@ -123,7 +127,7 @@ Plan make_plan(int B, int H, int n, int mr) {
   int S = std::max(1, std::min(p.ntiles, target / p.BH));
   p.tpc = (p.ntiles + S - 1) / S;
   p.S = (p.ntiles + p.tpc - 1) / p.tpc;
-  const size_t BH = p.BH, M = m, D = HD;
+  const size_t BH = p.BH, M = m, D = d;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -241,11 +245,11 @@ hipError_t allow_lds(F* fn, size_t bytes) {
 }
 
 // --------------------------------------------------------- launches ---
-template <typename IO, int M>
+template <typename IO, int M, int D>
 int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
                    const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
                    hipStream_t st) {
-  const float s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  const float s4 = 1.0f / sqrtf(sqrtf((float)D));
   LandmarkArgs la;
   la.n = p.n;
   la.H = p.H;
@@ -267,14 +271,16 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
   la.slots = at<unsigned long long>(w, p.off_slots);
-  HIP_TRY(launch("k_landmark", k_landmark<IO, M>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
+  HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
-  const bool fuse_gram = M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
+  // the pseudo-inverse blocks form A themselves only at d = 64 (their LDS
+  // plan holds 64-channel landmarks)
+  const bool fuse_gram = D == HD && M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
   if (!fuse_gram) {
-    constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4>();
-    HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4>, glds));
-    HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4>, dim3(p.BH), dim3(64 * gram_waves<M>()), (uint32_t)glds, st,
-                   la));
+    constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4, D>();
+    HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4, D>, glds));
+    HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4, D>, dim3(p.BH), dim3(64 * gram_waves<M>()), (uint32_t)glds,
+                   st, la));
   }
 
   PinvArgs pa;
@@ -307,7 +313,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
   ba.in = p.si;
-  size_t lds2 = sizeof(IO) == 2 ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO>::LDS_BYTES;
+  size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
+  lds2 = std::max<size_t>(lds2, bv_fold_bytes<M, D>());
   if constexpr (M <= 128)
     lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
                                                   : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
@@ -319,7 +326,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
                    ba, p.npinv));
     return NYS_OK;
   };
-  const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true>) : launch_bv(k_pinv_bv<IO, M, false>);
+  const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D>) : launch_bv(k_pinv_bv<IO, M, false, D>);
   if (brc != NYS_OK) return brc;
 
   const float* Zfinal = pa.Z;
@@ -359,14 +366,16 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   // threads per block: enough chunk subsets per row that each thread folds
   // one batch of 8 chunks (up to 1024 threads; 512 for m = 32)
   const int need = M * ((p.S + 7) / 8);
-  constexpr bool B16 = sizeof(IO) == 2;
+  // the bf16 output pass at d = 64 takes W^T in its own channel order
+  constexpr bool B16 = sizeof(IO) == 2 && D == HD;
   constexpr int NT_MAX = M >= 64 ? 1024 : 512;
+  const dim3 mwg(mw_blocks(p.BH, D));
   if (need <= 256)
-    HIP_TRY(launch("k_mw", k_mw<M, B16, 256>, dim3(mw_blocks(p.BH)), dim3(256), 0, st, ma));
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 256, D>, mwg, dim3(256), 0, st, ma));
   else if (need <= 512 || NT_MAX == 512)
-    HIP_TRY(launch("k_mw", k_mw<M, B16, 512>, dim3(mw_blocks(p.BH)), dim3(512), 0, st, ma));
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 512, D>, mwg, dim3(512), 0, st, ma));
   else
-    HIP_TRY(launch("k_mw", k_mw<M, B16, NT_MAX>, dim3(mw_blocks(p.BH)), dim3(NT_MAX), 0, st, ma));
+    HIP_TRY(launch("k_mw", k_mw<M, B16, NT_MAX, D>, mwg, dim3(NT_MAX), 0, st, ma));
 
   OutArgs oa;
   oa.q = q;
@@ -385,7 +394,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   oa.in = p.si;
   oa.out_s = p.so;
   oa.mr = p.mr;
-  if constexpr (sizeof(IO) == 2) {
+  if constexpr (sizeof(IO) == 2 && D == HD) {
     // persistent output pass: a token range of one head per workgroup, sized
     // so the grid fills the CUs at the occupancy its LDS allows in at most
     // one resident round (a second, partial round would cost a whole
@@ -407,13 +416,14 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
                                              : launch_out(k_out_stream<M, false, false>));
     if (orc != NYS_OK) return orc;
   } else {
-    const size_t lds4 = OutLayout<IO, M>::LDS_BYTES;
+    using OL = OutLayout<IO, M, D>;
     auto launch_out = [&](auto kern) -> int {
-      HIP_TRY(allow_lds(kern, lds4));
-      HIP_TRY(launch("k_out", kern, dim3((p.n + OUT_TOK - 1) / OUT_TOK, p.BH), dim3(256), (uint32_t)lds4, st, oa));
+      HIP_TRY(allow_lds(kern, OL::LDS_BYTES));
+      HIP_TRY(launch("k_out", kern, dim3((p.n + OL::TOK - 1) / OL::TOK, p.BH), dim3(256), (uint32_t)OL::LDS_BYTES, st,
+                     oa));
       return NYS_OK;
     };
-    const int orc = pad ? launch_out(k_out<IO, M, true>) : launch_out(k_out<IO, M, false>);
+    const int orc = pad ? launch_out(k_out<IO, M, true, D>) : launch_out(k_out<IO, M, false, D>);
     if (orc != NYS_OK) return orc;
   }
 
@@ -430,7 +440,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     pr.ldp = p.mr;
     pr.lscale = s4;
     pr.in = p.si;
-    using PL = ProbsLayout<IO, M>;
+    using PL = ProbsLayout<IO, M, D>;
     const int ntb = (p.n + PROBS_TOK - 1) / PROBS_TOK;
     const dim3 grid(((ntb + 7) / 8) * 8 * PL::NCB, p.BH);
     auto launch_probs = [&](auto kern) -> int {
@@ -438,13 +448,13 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
       HIP_TRY(launch("k_probs", kern, grid, dim3(256), (uint32_t)PL::LDS_BYTES, st, pr));
       return NYS_OK;
     };
-    const int prc = pad ? launch_probs(k_probs<IO, M, true>) : launch_probs(k_probs<IO, M, false>);
+    const int prc = pad ? launch_probs(k_probs<IO, M, true, D>) : launch_probs(k_probs<IO, M, false, D>);
     if (prc != NYS_OK) return prc;
   }
   return NYS_OK;
 }
 
-template <typename IO>
+template <typename IO, int D>
 int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, const void* k, const void* v,
                  const uint8_t* mask,
                  const float* conv_w, int conv_k, void* out, void* probs, hipStream_t st) {
@@ -460,10 +470,10 @@ int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, con
   ea.out = out;
   ea.n = n;
   ea.H = H;
-  ea.lscale = 1.0f / sqrtf((float)HD);
-  const size_t lds = exact_lds_bytes<IO>();
-  HIP_TRY(allow_lds(k_exact<IO>, lds));
-  HIP_TRY(launch("k_exact", k_exact<IO>, dim3((n + 63) / 64, B * H), dim3(256), (uint32_t)lds, st, ea));
+  ea.lscale = 1.0f / sqrtf((float)D);
+  const size_t lds = exact_lds_bytes<IO, D>();
+  HIP_TRY(allow_lds(k_exact<IO, D>, lds));
+  HIP_TRY(launch("k_exact", k_exact<IO, D>, dim3((n + 63) / 64, B * H), dim3(256), (uint32_t)lds, st, ea));
   if (probs != nullptr) {
     ProbsArgs pr{};
     pr.q = q;
@@ -476,55 +486,53 @@ int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, con
     pr.ldp = n;
     pr.lscale = ea.lscale;
     pr.in = si;
-    HIP_TRY(launch("k_exact_probs", k_exact_probs<IO>, dim3((n + 4 * XPROBS_Q - 1) / (4 * XPROBS_Q), B * H),
-                   dim3(256), 0, st, pr));
+    constexpr int QB = 4 * xprobs_q<D>();
+    HIP_TRY(launch("k_exact_probs", k_exact_probs<IO, D>, dim3((n + QB - 1) / QB, B * H), dim3(256), 0, st, pr));
   }
   return NYS_OK;
 }
 
-template <typename IO>
+template <typename IO, int D>
 int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
                const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
                hipStream_t st) {
+#define NYS_M(MM) \
+  case MM:        \
+    return launch_nystrom<IO, MM, D>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
   switch (m) {
-    case 32: return launch_nystrom<IO, 32>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-    case 64: return launch_nystrom<IO, 64>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-    case 96: return launch_nystrom<IO, 96>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-    case 128: return launch_nystrom<IO, 128>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+    NYS_M(32)
+    NYS_M(64)
+    NYS_M(96)
+    NYS_M(128)
+    NYS_M(160)
+    NYS_M(192)
+    NYS_M(224)
+    NYS_M(256)
     default: break;
   }
-  {
-    switch (m) {
-      case 160: return launch_nystrom<IO, 160>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-      case 192: return launch_nystrom<IO, 192>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-      case 224: return launch_nystrom<IO, 224>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-      case 256: return launch_nystrom<IO, 256>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
-      default: break;
-    }
-  }
+#undef NYS_M
   return fail(NYS_ERR_UNSUPPORTED, "m=%d has no kernel instance", m);
 }
 
-
-// Dense [B, H, n, 64] strides.
-Strides dense(int B, int H, int n) {
+// Dense [B, H, n, d] strides.
+Strides dense(int B, int H, int n, int d) {
   (void)B;
-  return Strides{(long long)H * n * HD, (long long)n * HD, HD};
+  return Strides{(long long)H * n * d, (long long)n * d, d};
 }
 
 // A view's element range [lo, hi] (strides may be negative).
-void view_range(const Strides& s, int B, int H, int n, long long& lo, long long& hi) {
+void view_range(const Strides& s, int B, int H, int n, int d, long long& lo, long long& hi) {
   lo = hi = 0;
   const long long ext[3][2] = {{s.b, B}, {s.h, H}, {s.t, n}};
   for (const auto& e : ext) (e[0] < 0 ? lo : hi) += e[0] * (e[1] - 1);
-  hi += HD - 1;
+  hi += d - 1;
 }
 
 // Strides of q/k/v (si) and out (so): 16-byte aligned rows, and no two
 // (batch, head, token) rows of out sharing an element (sorted by stride,
 // each dimension must step over everything the smaller ones span).
 int check_strides(int esize, const void* q, const void* k, const void* v, const void* out, Strides si, Strides so,
-                  int B, int H, int n) {
+                  int B, int H, int n, int dh) {
   const int ext[3] = {B, H, n};
   for (const Strides* s : {&si, &so}) {
     const long long st[3] = {s->b, s->h, s->t};
@@ -538,7 +546,7 @@ int check_strides(int esize, const void* q, const void* k, const void* v, const 
   struct D {
     long long st;
     long long ex;
-  } d[4] = {{1, HD}, {so.b < 0 ? -so.b : so.b, B}, {so.h < 0 ? -so.h : so.h, H}, {so.t < 0 ? -so.t : so.t, n}};
+  } d[4] = {{1, dh}, {so.b < 0 ? -so.b : so.b, B}, {so.h < 0 ? -so.h : so.h, H}, {so.t < 0 ? -so.t : so.t, n}};
   std::sort(d, d + 4, [](const D& x, const D& y) { return x.st < y.st; });
   long long span = 0;
   for (const D& e : d) {
@@ -547,8 +555,8 @@ int check_strides(int esize, const void* q, const void* k, const void* v, const 
     span += e.st * (e.ex - 1);
   }
   long long olo, ohi, ilo, ihi;
-  view_range(so, B, H, n, olo, ohi);
-  view_range(si, B, H, n, ilo, ihi);
+  view_range(so, B, H, n, dh, olo, ohi);
+  view_range(si, B, H, n, dh, ilo, ihi);
   const char* const ob = static_cast<const char*>(out);
   for (const void* ptr : {q, k, v}) {
     const char* const ib = static_cast<const char*>(ptr);
@@ -561,14 +569,14 @@ int check_strides(int esize, const void* q, const void* k, const void* v, const 
 // The weights buffer: dense [B, H, n, m] (n x n when m == n), 16-byte
 // aligned, overlapping none of q, k, v and out.
 int check_probs(int esize, const void* q, const void* k, const void* v, const void* out, const void* probs,
-                Strides si, Strides so, int B, int H, int n, int m) {
+                Strides si, Strides so, int B, int H, int n, int d, int m) {
   if (reinterpret_cast<uintptr_t>(probs) % 16 != 0) return fail(NYS_ERR_INVALID, "probs must be 16-byte aligned");
   const char* const pb = static_cast<const char*>(probs);
   const char* const pe = pb + (size_t)B * H * n * m * esize;
   const void* const views[4] = {q, k, v, out};
   for (int i = 0; i < 4; ++i) {
     long long lo, hi;
-    view_range(i < 3 ? si : so, B, H, n, lo, hi);
+    view_range(i < 3 ? si : so, B, H, n, d, lo, hi);
     const char* const b = static_cast<const char*>(views[i]);
     if (pb < b + (hi + 1) * esize && b + lo * esize < pe)
       return fail(NYS_ERR_INVALID, "probs overlaps %s", i < 3 ? "an input" : "out");
@@ -585,9 +593,9 @@ int validate(int esize, const void* q, const void* k, const void* v, int B, int 
   if (n % m != 0) return fail(NYS_ERR_INVALID, "n=%d is not a multiple of m=%d", n, m);
   if (n_iter < 0) return fail(NYS_ERR_INVALID, "n_iter=%d is negative", n_iter);
   if (init_option != 0 && init_option != 1) return fail(NYS_ERR_INVALID, "init_option=%d is not 0 or 1", init_option);
-  if (d != HD) return fail(NYS_ERR_UNSUPPORTED, "d=%d: only d=64 is built", d);
+  if (d != 32 && d != 64 && d != 128) return fail(NYS_ERR_UNSUPPORTED, "d=%d: head sizes 32, 64 and 128 are built", d);
   if ((long long)B * H > 65535) return fail(NYS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)B * H);
-  if ((long long)n * HD >= (1LL << 31)) return fail(NYS_ERR_UNSUPPORTED, "n=%d too long", n);
+  if ((long long)n * d >= (1LL << 31)) return fail(NYS_ERR_UNSUPPORTED, "n=%d too long", n);
   if (m != n) {
     if (m > NYS_MAX_LANDMARKS) return fail(NYS_ERR_UNSUPPORTED, "m=%d: at most 256 landmarks (unless m == n)", m);
   }
@@ -601,10 +609,10 @@ int check_call(int esize, const void* q, const void* k, const void* v, Strides s
                const void* probs) {
   int rc = validate(esize, q, k, v, B, H, n, d, m, n_iter, init_option, out);
   if (rc != NYS_OK) return rc;
-  rc = check_strides(esize, q, k, v, out, si, so, B, H, n);
+  rc = check_strides(esize, q, k, v, out, si, so, B, H, n, d);
   if (rc != NYS_OK) return rc;
   if (probs != nullptr) {
-    rc = check_probs(esize, q, k, v, out, probs, si, so, B, H, n, m);
+    rc = check_probs(esize, q, k, v, out, probs, si, so, B, H, n, d, m);
     if (rc != NYS_OK) return rc;
   }
   if (conv_w != nullptr) {
@@ -623,8 +631,12 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
         void* probs = nullptr) {
   int rc = check_call(sizeof(IO), q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, probs);
   if (rc != NYS_OK) return rc;
-  if (m == n) return launch_exact<IO>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
-  Plan p = make_plan(B, H, n, m);
+  if (m == n) {
+    if (d == 32) return launch_exact<IO, 32>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
+    if (d == 128) return launch_exact<IO, 128>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
+    return launch_exact<IO, 64>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
+  }
+  Plan p = make_plan(B, H, n, m, d);
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
   p.si = si;
   p.so = so;
@@ -633,7 +645,9 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
   Workspace* w = nullptr;
   rc = get_workspace(st, p.total, &w);
   if (rc != NYS_OK) return rc;
-  rc = dispatch_m<IO>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+  rc = d == 32    ? dispatch_m<IO, 32>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st)
+       : d == 128 ? dispatch_m<IO, 128>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st)
+                  : dispatch_m<IO, 64>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
   if (wout) *wout = w;
   if (pout) *pout = p;
   return rc;
@@ -775,7 +789,7 @@ __attribute__((visibility("default"))) int nystrom_attention(const float* q, con
                                                              struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+    return run<float>(q, k, v, dense(B, H, n, d), key_mask, conv_w, TAPS, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
                       nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -789,7 +803,7 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16(const uint16_t
                                                                   struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
+    return run<u16>(q, k, v, dense(B, H, n, d), key_mask, conv_w, TAPS, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream, nullptr,
                     nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -803,7 +817,7 @@ __attribute__((visibility("default"))) int nystrom_attention_conv(const float* q
                                                                   struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, conv_kernel_size, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream,
+    return run<float>(q, k, v, dense(B, H, n, d), key_mask, conv_w, conv_kernel_size, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream,
                       nullptr, nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -818,7 +832,7 @@ __attribute__((visibility("default"))) int nystrom_attention_bf16_conv(const uin
                                                                        struct ihipStream_t* stream) {
   try {
     g_err.clear();
-    return run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, conv_kernel_size, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream,
+    return run<u16>(q, k, v, dense(B, H, n, d), key_mask, conv_w, conv_kernel_size, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream,
                     nullptr, nullptr);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
@@ -887,10 +901,10 @@ __attribute__((visibility("default"))) int nystrom_self_attention(
 }
 
 __attribute__((visibility("default"))) size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m) {
-  if (B <= 0 || H <= 0 || n <= 0 || d != HD || m <= 0 || m > n || n % m != 0) return 0;
+  if (B <= 0 || H <= 0 || n <= 0 || (d != 32 && d != 64 && d != 128) || m <= 0 || m > n || n % m != 0) return 0;
   if (m == n) return 0;
   if (m > NYS_MAX_LANDMARKS) return 0;
-  return make_plan(B, H, n, m).total;
+  return make_plan(B, H, n, m, d).total;
 }
 
 __attribute__((visibility("default"))) const char* nystrom_last_error(void) { return g_err.c_str(); }
@@ -922,8 +936,8 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     Workspace* w = nullptr;
     Plan p{};
     int rc = dtype == 0
-                 ? run<float>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
-                 : run<u16>(q, k, v, dense(B, H, n), key_mask, conv_w, TAPS, dense(B, H, n), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
+                 ? run<float>(q, k, v, dense(B, H, n, d), key_mask, conv_w, TAPS, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p)
+                 : run<u16>(q, k, v, dense(B, H, n, d), key_mask, conv_w, TAPS, dense(B, H, n, d), B, H, n, d, m, n_iter, init_option, out, stream, &w, &p);
     if (rc != NYS_OK) return rc;
     HIP_TRY(hipStreamSynchronize(stream));
     std::lock_guard<std::mutex> lk(g_mu);
@@ -932,14 +946,14 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     size_t zoff = p.off_Z;
     if (M > 128 && (n_iter % 2) == 1) zoff = p.off_Z2;
     char* const base = static_cast<char*>(w->buf);
-    // [BH][M][64] -> [BH][mr][64]
+    // [BH][M][d] -> [BH][mr][d]
     struct Rows {
       float* dst;
       size_t off;
     } rows[] = {{qt, p.off_qt}, {kt, p.off_kt}, {bv, p.off_BV}, {wout, p.off_W}};
     for (const Rows& r : rows)
       if (r.dst)
-        HIP_TRY(hipMemcpy2DAsync(r.dst, mr * HD * 4, base + r.off, M * HD * 4, mr * HD * 4, BH,
+        HIP_TRY(hipMemcpy2DAsync(r.dst, mr * p.D * 4, base + r.off, M * p.D * 4, mr * p.D * 4, BH,
                                  hipMemcpyDeviceToDevice, stream));
     // [BH][M][M] -> [BH][mr][mr]
     struct Mats {

@@ -30,8 +30,8 @@
  *   - conv_w is a DEVICE pointer to float32 [H, 65] (tap j multiplies V at
  *     token offset j - 32, zero outside [0, n); one filter per head shared
  *     by all d columns).  NULL disables the convolution ([P1] 2.6).
- *   - d must be 64; 1 <= m <= 256 with n % m == 0, unless m == n (exact
- *     branch, any n >= 1).  Internally the
+ *   - d (the head size) is 32, 64 or 128; 1 <= m <= 256 with n % m == 0,
+ *     unless m == n (exact branch, any n >= 1).  Internally the
  *     landmarks are padded to a multiple of 32 with landmarks that take no
  *     weight anywhere, so any m in range gives the m-landmark result.
  *   - init_option 0 ("original", the default): c = (max column sum of A) *
@@ -68,12 +68,12 @@ typedef enum {
 } nys_status;
 
 enum { NYS_INIT_ORIGINAL = 0, NYS_INIT_EXACT = 1 };
-enum { NYS_HEAD_DIM = 64, NYS_CONV_TAPS = 65, NYS_MAX_LANDMARKS = 256 };
+enum { NYS_HEAD_DIM = 64, NYS_CONV_TAPS = 65, NYS_MAX_LANDMARKS = 256 };  /* NYS_HEAD_DIM: the pages' head size */
 
 /* Nystrom attention, float32 q/k/v/out ([P1] 2.2-2.6; [P2] mask).
  * Errors: NYS_ERR_INVALID for NULL q/k/v/out, B/H/n/d/m <= 0, n % m != 0,
  * m > n, n_iter < 0, init_option not 0/1, out overlapping q/k/v;
- * NYS_ERR_UNSUPPORTED for d != 64, m > 256 when m != n, or sizes whose
+ * NYS_ERR_UNSUPPORTED for d not 32, 64 or 128, m > 256 when m != n, or sizes whose
  * element counts overflow 2^31 per head;
  * NYS_ERR_HIP when a HIP call fails. */
 int nystrom_attention(const float* q, const float* k, const float* v,
@@ -113,12 +113,12 @@ int nystrom_attention_bf16_conv(const uint16_t* q, const uint16_t* k,
 
 /* The general form: dtype 0 (float32 q/k/v/out) or 1 (bfloat16), the conv
  * kernel size as in nystrom_attention_conv, and q, k, v (one set of strides)
- * and out (another) as strided views of [B, H, n, 64]: element
+ * and out (another) as strided views of [B, H, n, d]: element
  * (b, h, t, c) of q is q[b * in_batch_stride + h * in_head_stride +
- * t * in_token_stride + c], in elements; the 64 channels of a token are
+ * t * in_token_stride + c], in elements; the d channels of a token are
  * contiguous.  This reads, for example, q, k and v straight out of a fused
- * [B, n, 3, H, 64] projection (strides n*3*H*64, 64, 3*H*64) and writes out
- * as [B, n, H*64] (strides n*H*64, 64, H*64), the module's layouts ([P1]
+ * [B, n, 3, H, d] projection (strides n*3*H*d, d, 3*H*d) and writes out
+ * as [B, n, H*d] (strides n*H*d, d, H*d), the module's layouts ([P1]
  * 2.7), with no transposes.  Errors: those of nystrom_attention_conv, plus
  * NYS_ERR_INVALID for a dtype other than 0/1, a pointer or stride that
  * breaks 16-byte alignment of the token rows, out strides under which two
@@ -193,12 +193,12 @@ void nystrom_release(void);
  * (dtype selects: 0 = float32 q/k/v/out, 1 = bfloat16) and, after the
  * stream has synchronised, copy the intermediate stages into the caller's
  * DEVICE buffers (float32, any may be NULL):
- *   qt, kt  [B,H,m,64]  landmarks of Qs, Ks          ([P1] 2.3)
+ *   qt, kt  [B,H,m,d]   landmarks of Qs, Ks          ([P1] 2.3)
  *   a       [B,H,m,m]   A = softmax(Qt Kt^T)          ([P1] 2.4)
  *   cscale  [B*H]       init scale c used for each head ([P1] 2.5)
  *   z       [B,H,m,m]   pseudo-inverse iterate after n_iter steps
- *   bv      [B,H,m,64]  B V                           ([P1] 2.4)
- *   w       [B,H,m,64]  Z (B V)
+ *   bv      [B,H,m,d]   B V                           ([P1] 2.4)
+ *   w       [B,H,m,d]   Z (B V)
  * Synchronises `stream`.  Same errors as nystrom_attention; also
  * NYS_ERR_INVALID when m == n. */
 int nystrom_debug_stages(int dtype, const void* q, const void* k,

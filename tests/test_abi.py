@@ -69,7 +69,8 @@ def call(lib, fn="nystrom_attention", q=FAKE, k=FAKE, v=FAKE, out=FAKE2, B=1, H=
     (dict(n_iter=-1), -1),
     (dict(init=2), -1),
     (dict(out=FAKE), -1),              # out aliases q, k, v
-    (dict(d=32, n=256), -2),           # only d = 64 is built
+    (dict(d=48, n=256), -2),           # head sizes 32, 64, 128 are built
+    (dict(d=256, n=256), -2),
     (dict(m=512, n=1024), -2),         # m above 256 (and not n)
     (dict(B=300, H=300), -2),          # B*H above the grid limit
 ])
@@ -139,7 +140,9 @@ def test_workspace_bytes(lib):
     w = lib.nystrom_workspace_bytes
     assert w(1, 2, 256, 64, 64) > 0
     assert w(2, 2, 256, 64, 64) > w(1, 2, 256, 64, 64)
-    assert w(1, 2, 256, 32, 64) == 0      # unsupported d
+    assert w(1, 2, 256, 48, 64) == 0      # unsupported d
+    # head sizes 32 and 128: the per-landmark buffers scale with d
+    assert 0 < w(1, 2, 256, 32, 64) < w(1, 2, 256, 64, 64) < w(1, 2, 256, 128, 64)
     assert w(1, 2, 250, 64, 64) == 0      # n % m
     assert w(1, 2, 256, 64, 256) == 0     # exact branch needs no workspace
     # any landmark count up to 256 (padded to a multiple of 32 inside)

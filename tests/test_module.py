@@ -48,16 +48,19 @@ def _check(name, inp, dtype, m, n_iter=6, init=0, conv=True):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("B,n,hidden,H,m", [(2, 512, 768, 12, 64), (1, 1024, 256, 4, 128), (2, 400, 96, 2, 50),
-                                            (1, 200, 128, 2, 200), (3, 96, 64, 1, 32)])
-def test_module(dtype, B, n, hidden, H, m):
+@pytest.mark.parametrize("B,n,hidden,H,d,m", [(2, 512, 768, 12, 64, 64), (1, 1024, 256, 4, 64, 128),
+                                              (2, 400, 96, 2, 64, 50), (1, 200, 128, 2, 64, 200),
+                                              (3, 96, 64, 1, 64, 32), (2, 512, 256, 8, 32, 64),
+                                              (1, 512, 512, 4, 128, 64), (1, 256, 256, 2, 128, 256)])
+def test_module(dtype, B, n, hidden, H, d, m):
     """The pages' module shape (hidden 768, 12 heads), other widths and head
-    counts, a landmark count that pads, and the exact branch (m == n)."""
+    counts, head sizes 32 and 128, a landmark count that pads, and the exact
+    branch (m == n)."""
     lengths = [n - (n // 4) * (i % 2) for i in range(B)]
-    inp = make_module_inputs(B, n, hidden, H, 64, seed=900 + n + hidden, dtype=dtype, lengths=lengths)
-    _check(f"B{B}-n{n}-h{hidden}-H{H}-m{m}", inp, dtype, m)
-    nob = make_module_inputs(B, n, hidden, H, 64, seed=901 + n, dtype=dtype, lengths=None, bias=False)
-    _check(f"B{B}-n{n}-h{hidden}-H{H}-m{m}-nobias-init1", nob, dtype, m, init=1, conv=False)
+    inp = make_module_inputs(B, n, hidden, H, d, seed=900 + n + hidden + d, dtype=dtype, lengths=lengths)
+    _check(f"B{B}-n{n}-h{hidden}-H{H}-d{d}-m{m}", inp, dtype, m)
+    nob = make_module_inputs(B, n, hidden, H, d, seed=901 + n + d, dtype=dtype, lengths=None, bias=False)
+    _check(f"B{B}-n{n}-h{hidden}-H{H}-d{d}-m{m}-nobias-init1", nob, dtype, m, init=1, conv=False)
 
 
 def test_module_headline_size():

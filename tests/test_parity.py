@@ -105,25 +105,48 @@ def test_conv_kernel_sizes(dtype, ksize):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("m,n", [(64, 1024), (50, 400), (128, 512), (200, 1000), (256, 2048), (100, 100),
+                                 (32, 96)])
+def test_head_sizes(dtype, d, m, n):
+    """Head sizes 32 and 128 (the d = 64 instances are tuned separately):
+    padded and unpadded landmark counts, both pseudo-inverse paths (up to
+    128 landmarks fused, above in separate launches), ragged tiles, the
+    exact branch; both initialisations, with and without the convolution."""
+    x = make_custom(2, 3, n, d, seed=760 + d + m + n, dtype=dtype, lengths=[n, n - n // 3])
+    _check(f"d{d}-m{m}-n{n}", x, dtype, m, 6, 0)
+    _check(f"d{d}-m{m}-n{n}-init1-noconv", x, dtype, m, 6, 1, conv=False)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [32, 128])
+def test_head_sizes_peaked(dtype, d):
+    """Larger logits at both head sizes, and 12 iterations."""
+    x = make_custom(1, 2, 1024, d, seed=790 + d, dtype=dtype, scale=3.0)
+    _check(f"d{d}-peaked", x, dtype, 64, 12, 1, conv=False)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("m,n", [(64, 512), (50, 400), (200, 200), (20, 100)])
-def test_strided_layouts(dtype, m, n):
-    """q, k, v read straight out of a fused [B, n, 3, H, 64] projection and
-    out written as [B, n, H, 64] (the module's layouts), through strided
+def test_strided_layouts(dtype, d, m, n):
+    """q, k, v read straight out of a fused [B, n, 3, H, d] projection and
+    out written as [B, n, H, d] (the module's layouts), through strided
     views: the same result as the dense call."""
     import torch
 
     import efficient_transformer_attention_segment_amd as nys
     from gpu_util import to_dev
     B, H = 2, 3
-    x = make_custom(B, H, n, 64, seed=750 + m + n, dtype=dtype, lengths=[n, n - n // 3])
+    x = make_custom(B, H, n, d, seed=750 + m + n + d, dtype=dtype, lengths=[n, n - n // 3])
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    qkv = torch.empty(B, n, 3, H, 64, dtype=tdt, device="cuda")
+    qkv = torch.empty(B, n, 3, H, d, dtype=tdt, device="cuda")
     for i, name in enumerate(("q", "k", "v")):
         qkv[:, :, i] = torch.from_numpy(x[name]).to("cuda").to(tdt).permute(0, 2, 1, 3)
     q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
-    out_buf = torch.full((B, n, H * 64), float("nan"), dtype=tdt, device="cuda")
-    out = out_buf.view(B, n, H, 64).permute(0, 2, 1, 3)
-    announce(f"strided dtype={dtype} m={m} n={n} q.stride={q.stride()} out.stride={out.stride()}")
+    out_buf = torch.full((B, n, H * d), float("nan"), dtype=tdt, device="cuda")
+    out = out_buf.view(B, n, H, d).permute(0, 2, 1, 3)
+    announce(f"strided dtype={dtype} d={d} m={m} n={n} q.stride={q.stride()} out.stride={out.stride()}")
     nys.attention(q, k, v, to_dev(x["key_mask"], None), to_dev(x["conv_w"], None), m=m, n_iter=6, init_option=0,
                   out=out)
     torch.cuda.synchronize()

@@ -64,6 +64,15 @@ def test_landmark_counts(dtype, m, n):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("m,n", [(64, 512), (200, 1000), (256, 1024), (96, 96)])
+def test_head_sizes(dtype, d, m, n):
+    """Head sizes 32 and 128, including the exact branch (m == n)."""
+    x = make_custom(2, 2, n, d, seed=860 + d + m, dtype=dtype, lengths=[n, n - n // 4])
+    _check(f"d{d}-m{m}-n{n}", x, dtype, m, 6, 0)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_peaked_and_iterations(dtype):
     """Larger logits, and n_iter 0 (the weights are F Z_0) and 12."""
     x = make_custom(1, 3, 1024, 64, seed=830, dtype=dtype, scale=3.0)
