@@ -556,6 +556,69 @@ def pin_module_projection_library(O):
     return _rel(qkv.reshape(B, n, -1), ref)
 
 
+# --------------------------------------------------------------- gradients ---
+
+def _fd_case(seed, B, H, n, d, m, K, lens, n_iter, init):
+    rng = RNG(seed)
+    q, k, v = (rng.standard_normal((B, H, n, d)) for _ in range(3))
+    w = rng.standard_normal((H, K)) * 0.3 if K else None
+    mask = None if lens is None else (np.arange(n)[None] < np.asarray(lens)[:, None]).astype(np.uint8)
+    dout = rng.standard_normal((B, H, n, d))
+    return q, k, v, w, mask, dout
+
+
+GRAD_CASES = [
+    # seed, B, H, n, d, m, K, valid lengths, n_iter, init
+    (51, 1, 2, 8, 4, 4, 3, [6], 3, 1),
+    (52, 2, 1, 8, 4, 4, 5, [8, 5], 2, 0),
+    (53, 1, 2, 6, 4, 6, 3, [4], 6, 0),       # exact branch (m == n)
+    (54, 1, 1, 12, 3, 3, None, None, 4, 0),
+]
+
+
+def pin_grad_forward(O):
+    """The differentiable forward equals the numpy oracle's output."""
+    from oracle import nystrom_grad as G
+    err = 0.0
+    for seed, B, H, n, d, m, K, lens, it, init in GRAD_CASES:
+        q, k, v, w, mask, _ = _fd_case(seed, B, H, n, d, m, K, lens, it, init)
+        ref = O.nystrom_attention(q, k, v, mask, w, m=m, n_iter=it, init_option=init)
+        got = G.forward(*(torch.from_numpy(x) for x in (q, k, v)), mask,
+                        None if w is None else torch.from_numpy(w), m, it, init).numpy()
+        err = max(err, _rel(got, ref))
+    return err
+
+
+def pin_grad_finite_differences(O):
+    """[P1 2.2-2.6] Every gradient entry against central differences of the
+    numpy oracle (step 1e-6 in float64), on tiny inputs covering both
+    initialisations, a partial mask, the convolution and the exact branch;
+    the derivative of sum(out * dout) is independent of autograd here."""
+    from oracle import nystrom_grad as G
+    err = 0.0
+    h = 1e-6
+    for seed, B, H, n, d, m, K, lens, it, init in GRAD_CASES:
+        q, k, v, w, mask, dout = _fd_case(seed, B, H, n, d, m, K, lens, it, init)
+        got = G.gradients(q, k, v, dout, mask, w, m, it, init)
+
+        def loss(qq, kk, vv, ww):
+            return float((O.nystrom_attention(qq, kk, vv, mask, ww, m=m, n_iter=it, init_option=init) * dout).sum())
+
+        args = [q, k, v, w]
+        for idx in range(4):
+            if args[idx] is None:
+                continue
+            fd = np.zeros_like(args[idx])
+            for pos in np.ndindex(*args[idx].shape):
+                up = [a.copy() if (a is not None and j == idx) else a for j, a in enumerate(args)]
+                dn = [a.copy() if (a is not None and j == idx) else a for j, a in enumerate(args)]
+                up[idx][pos] += h
+                dn[idx][pos] -= h
+                fd[pos] = (loss(*up) - loss(*dn)) / (2 * h)
+            err = max(err, _rel(got[idx], fd))
+    return err
+
+
 ALL_PINS = {
     "scale": (pin_scale, 1e-12),
     "segment_means_direct": (pin_segment_means_direct, 1e-12),
@@ -583,4 +646,6 @@ ALL_PINS = {
     "probs_output_consistency": (pin_probs_output_consistency, 1e-12),
     "module_identity_projection": (pin_module_identity_projection, 1e-13),
     "module_projection_library": (pin_module_projection_library, 1e-13),
+    "grad_forward": (pin_grad_forward, 1e-12),
+    "grad_finite_differences": (pin_grad_finite_differences, 1e-6),
 }

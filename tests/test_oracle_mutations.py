@@ -195,3 +195,80 @@ def test_mutant_is_caught(mutant, monkeypatch):
         if not (err < tol):
             caught.append(pin)
     assert caught, f"mutant {mutant} passed every pin in {pins}"
+
+
+# ------------------------------------------------------ gradient oracle ---
+def _grad_forward_c_detached(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0):
+    """The differentiable forward with the initial scale c treated as a
+    constant (a plausible slip: c comes from maxima)."""
+    import torch
+
+    from oracle import nystrom_grad as G
+    B, H, n, d = q.shape
+    s = d ** -0.25
+    qs, ks = q * s, k * s
+    valid = None if key_mask is None else torch.as_tensor(np.asarray(key_mask) != 0)[:, None, None, :]
+    if m == n:
+        attn = G.softmax_masked(qs @ ks.transpose(-1, -2), valid) @ v
+    else:
+        L = n // m
+        qt = qs.reshape(B, H, m, L, d).mean(dim=-2)
+        kt = ks.reshape(B, H, m, L, d).mean(dim=-2)
+        F = torch.softmax(qs @ kt.transpose(-1, -2), dim=-1)
+        A = torch.softmax(qt @ kt.transpose(-1, -2), dim=-1)
+        Bm = G.softmax_masked(qt @ ks.transpose(-1, -2), valid)
+        colsum, rowsum = A.sum(dim=-2), A.sum(dim=-1)
+        if init_option == 0:
+            c = (colsum.max() * rowsum.max()).reshape(1, 1, 1, 1)
+        else:
+            c = (colsum.max(dim=-1).values * rowsum.max(dim=-1).values)[..., None, None]
+        c = c.detach()
+        I = torch.eye(m, dtype=A.dtype)
+        Z = A.transpose(-1, -2) / c
+        for _ in range(n_iter):
+            X = A @ Z
+            Z = 0.25 * Z @ (13.0 * I - X @ (15.0 * I - X @ (7.0 * I - X)))
+        attn = F @ (Z @ (Bm @ v))
+    if conv_w is not None:
+        attn = attn + G.depthwise_conv_same(v, conv_w)
+    return attn
+
+
+def _grad_softmax_no_mask(s, valid=None):
+    import torch
+    return torch.softmax(s, dim=-1)
+
+
+def _grad_conv_flipped(v, w):
+    from oracle import nystrom_grad as G
+    return _REAL_GRAD_CONV(v, w.flip(-1))
+
+
+_REAL_GRAD_CONV = None
+
+GRAD_MUTANTS = {
+    "grad_c_detached": ({"forward": _grad_forward_c_detached}, ["grad_finite_differences"]),
+    "grad_mask_ignored": ({"softmax_masked": _grad_softmax_no_mask}, ["grad_forward", "grad_finite_differences"]),
+    "grad_conv_flipped": ({"depthwise_conv_same": _grad_conv_flipped}, ["grad_forward"]),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(GRAD_MUTANTS))
+def test_grad_mutant_is_caught(mutant, monkeypatch):
+    global _REAL_GRAD_CONV
+    from oracle import nystrom_grad as G
+    _REAL_GRAD_CONV = G.depthwise_conv_same
+    patches, pins = GRAD_MUTANTS[mutant]
+    for name, fn in patches.items():
+        monkeypatch.setattr(G, name, fn)
+    caught = []
+    for pin in pins:
+        fn, tol = P.ALL_PINS[pin]
+        with np.errstate(all="ignore"):
+            try:
+                err = fn(O)
+            except Exception:  # a crash also counts as caught
+                err = float("inf")
+        if not (err < tol):
+            caught.append(pin)
+    assert caught, f"mutant {mutant} passed every pin in {pins}"
