@@ -45,6 +45,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probs", action="store_true", help="skip timing the attention-weights call")
     ap.add_argument("--no-module", action="store_true", help="skip timing the self-attention module call")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -269,6 +270,42 @@ def time_module(w, steps, warmup, torch, nys, core_ms):
             "note": "inputs resident; the projection's time is the step minus the attention-only step"}
 
 
+def time_backward(w, x, steps, warmup, torch, nys):
+    """The backward pass (nystrom_attention_backward: the forward stages
+    recomputed, then dq, dk, dv, dconv_w) on the workload: step time and
+    per-kernel times."""
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v"))
+    dout = torch.randn(q.shape, device=dev).to(tdt)
+    mask = torch.from_numpy(x["key_mask"]).to(dev) if x["key_mask"] is not None else None
+    conv = torch.from_numpy(x["conv_w"]).to(dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dw = torch.empty(conv.shape, dtype=torch.float32, device=dev)
+
+    def step():
+        nys.attention_backward(q, k, v, dout, mask, conv, m=w.m, n_iter=w.n_iter, init_option=w.init_option,
+                               dq=dq, dk=dk, dv=dv, dconv_w=dw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    nys.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = nys.profile_collect()
+    nys.profile_enable(False)
+    return {"call": "nystrom_attention_backward", "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
+            "kernels_us": {kk: round(1e3 * t / c, 2) for kk, (t, c) in prof.items()}}
+
+
 def cpu_baseline(w, x, budget_s):
     import numpy as np
     from oracle import nystrom_oracle as O
@@ -491,6 +528,9 @@ def main():
                                                     torch, nys)
     module = None if args.no_module else time_module(w, max(5, args.steps // 5), max(2, args.warmup // 2), torch,
                                                      nys, ms)
+    backward = None
+    if not args.no_backward and w.m <= 128:
+        backward = time_backward(w, x, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
     copy_gbs = copy_bandwidth(torch)
     roofline["attainable_copy_GBps"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
@@ -508,7 +548,7 @@ def main():
         "step_us": spread,
         "roofline": roofline, "path": path, "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()}
                                                          for k, v in kern.items()},
-        "cpu_baseline": cpu, "also": also, "attention_weights": weights, "module": module,
+        "cpu_baseline": cpu, "also": also, "attention_weights": weights, "module": module, "backward": backward,
         "source_sha": sha,
     }
     print(json.dumps(line))

@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = [
-    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs", "self_attention",
+    "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs", "self_attention", "attention_backward",
     "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
     "profile_enable", "profile_collect",
     "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
@@ -61,6 +61,9 @@ def _load():
     lib.nystrom_attention_probs.restype = _I
     lib.nystrom_self_attention.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]
     lib.nystrom_self_attention.restype = _I
+    lib.nystrom_attention_backward.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                               _P, _P, _P]
+    lib.nystrom_attention_backward.restype = _I
     lib.nystrom_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.nystrom_workspace_bytes.restype = ctypes.c_size_t
     lib.nystrom_last_error.argtypes = []
@@ -236,6 +239,30 @@ def self_attention(x, w_qkv, b_qkv, H, key_mask=None, conv_w=None, m=64, n_iter=
                                           ksize, B, n, hidden, H, d, m, n_iter, init_option, _ptr(qkv), _ptr(out),
                                           _stream(stream)))
     return out, qkv
+
+
+def attention_backward(q, k, v, dout, key_mask=None, conv_w=None, m=64, n_iter=6, init_option=0, dq=None,
+                       dk=None, dv=None, dconv_w=None, stream=None):
+    """Gradients of sum(out * dout) for the call attention(q, k, v, key_mask,
+    conv_w, m, n_iter, init_option): returns (dq, dk, dv, dconv_w), the
+    first three in q's dtype, dconv_w float32 [H, K] (None without conv_w).
+    Dense [B, H, n, 64] tensors."""
+    import torch
+    for t in (q, k, v, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v and dout must be dense tensors of one shape and dtype")
+    B, H, n, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if conv_w is not None and dconv_w is None:
+        dconv_w = torch.empty(conv_w.shape, dtype=torch.float32, device=q.device)
+    dtype = 1 if q.dtype == torch.bfloat16 else 0
+    ksize = CONV_TAPS if conv_w is None else int(conv_w.shape[-1])
+    _check(_load().nystrom_attention_backward(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w), ksize,
+                                              B, H, n, d, m, n_iter, init_option, _ptr(dout), _ptr(dq), _ptr(dk),
+                                              _ptr(dv), _ptr(dconv_w), _stream(stream)))
+    return dq, dk, dv, dconv_w
 
 
 def workspace_bytes(B, H, n, d, m) -> int:

@@ -1,0 +1,688 @@
+// Backward pass: gradients of sum(out * dout) with respect to q, k, v and
+// the convolution weights, for the Nystrom path.
+//
+// Page: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), sections 2.2 -
+// 2.6 (the forward that is differentiated: d^-1/4 scales, segment means,
+// F = softmax(Qs Kt^T), A = softmax(Qt Kt^T), B = softmax(Qt Ks^T + mask),
+// the iterative inverse Z from Z_0 = A^T / c, out = F (Z (B V)) + conv(V)),
+// and its training use (gradient checkpointing, the Trainer).  The
+// intermediates are recomputed (landmarks, A, Z, B V, W and B's row
+// normalisers come from a forward pass without the output), then, per head
+// (d = 64, up to 128 landmarks, float32 arithmetic throughout):
+//
+//   k_bwd_conv  dv_conv = conv^T(dout) and partial sums of dconv_w;
+//   k_bwd_tok   per token: F, dF = dout W^T, D_t = sum_j F dF,
+//               dS = F (dF - D_t), dQs = dS Kt; per token chunk partial
+//               sums of dW = F^T dout and dKt = dS^T Qs;
+//   k_bwd_mm1   per head: dW, dZ = dW BV^T, dBV = Z^T dW, the iteration run
+//               backwards (Z_k, X_k, X_k^2 and P_k = 13I - 15X + 7X^2 - X^3
+//               recomputed in float32 and kept), dA, and the part dc of the
+//               gradient that flows through the initial scale c;
+//   k_bwd_mm2   c's share of dA (through the maximum column sum: to the
+//               arg-max column, of this head for init option 1, of the one
+//               head holding the maximum over all heads for option 0; the
+//               row-sum factor's share is constant along rows and vanishes
+//               in the softmax), dS_A = A (dA - rowsum(dA A)),
+//               dQt_A = dS_A Kt, dKt += dS_A^T Qt, D_i = dBV_i . BV_i;
+//   k_bwd_key   per key: B from the stored normalisers, dB = dBV V^T,
+//               dS_B = B (dB - D_i), dv = B^T dBV + dv_conv,
+//               dk = d^-1/4 (dS_B^T Qt + dKt[segment] / L); per key chunk
+//               partial sums of dQt_B = dS_B Ks;
+//   k_bwd_qt    dQt = dQt_A + sum of the dQt_B partials;
+//   k_bwd_q     dq = d^-1/4 (dQs + dQt[segment] / L);
+//   k_bwd_wsum  dconv_w = sum of its partials.
+// Every product is a float32 matrix-core product (mm16) over operands in
+// LDS; reductions run in a fixed order, so results are reproducible.
+#pragma once
+
+#include "common.hpp"
+
+namespace nys {
+
+// C (16 x 16) += sum_k A(i, k) B(k, j) over k < K, with A(i, k) at
+// a[i * ai + k * ak] and B(k, j) at b[k * bk + j * bj]: in step s lane
+// (c16, g) feeds A(c16, 4s + g) and B(4s + g, c16); C(4g + r, c16) ends in
+// element r.
+template <int K>
+__device__ __forceinline__ f32x4 mm16(const float* a, int ai, int ak, const float* b, int bk, int bj, f32x4 c) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const float* pa = a + c16 * ai + g * ak;
+  const float* pb = b + g * bk + c16 * bj;
+#pragma unroll 8
+  for (int s = 0; s < K / 4; ++s) c = mfma_f32(pa[4 * s * ak], pb[4 * s * bk], c);
+  return c;
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const uint8_t* key_mask;  // [B][n] or null
+  const float* conv_w;      // [H][conv_k] or null
+  int conv_k;
+  const float* qt;          // [BH][M][64] (carry d^-1/4)
+  const float* kt;
+  const float* A;           // [BH][M][M]
+  const float* BV;          // [BH][M][64]
+  const float* W;           // [BH][M][64]
+  const float* lse;         // [BH][M], log2 units
+  const float* cscale;      // [BH]
+  float* dqf;               // [BH][n][64]: dQs through F
+  float* pw;                // [BH][nct][M][64]: partial dW
+  float* pk;                // [BH][nct][M][64]: partial dKt through F
+  float* pq;                // [BH][nck][M][64]: partial dQt through B
+  float* mm;                // [BH][mm_mats][M][M]: pseudo-inverse backward scratch
+  float* dW;                // [BH][M][64]
+  float* dBV;               // [BH][M][64]
+  float* dQt;               // [BH][M][64]: dQt through A, then the total
+  float* dKt;               // [BH][M][64]: total
+  float* Dv;                // [BH][M]: dBV_i . BV_i
+  float* dc;                // [BH]: gradient reaching c
+  float* cmax;              // [BH]: maximum column sum of A
+  int* cmaxj;               // [BH]: its column
+  float* rmax;              // [BH]: maximum row sum of A
+  float* dvc;               // [BH][n][64]: conv part of dv, or null
+  float* pconv;             // [BH][ncv][conv_k]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dconv_w;           // [H][conv_k] or null
+  int n, H, BH, mr, L, nct, nck, ncv, n_iter, init_option;
+  float s4;                 // d^-1/4
+};
+
+constexpr int BWD_LD = HD + 4;   // float row stride of [.][64] tiles in LDS
+constexpr int BWD_CT = 256;      // tokens per k_bwd_tok workgroup
+constexpr int BWD_CK = 256;      // keys per k_bwd_key workgroup
+constexpr int BWD_GK = 32;       // keys per step of k_bwd_key
+constexpr int BWD_CV = 128;      // tokens per k_bwd_conv workgroup
+
+template <int M>
+constexpr int bwd_tok_waves() {
+  return M <= 64 ? 4 : 2;
+}
+// matrices of the pseudo-inverse backward per head: Z_0 .. Z_n, then X_k,
+// X_k^2, P_k for k < n, then G, Gn, dP, dX, T, dA
+__host__ __device__ constexpr int bwd_mm_mats(int n_iter) { return 4 * n_iter + 1 + 6; }
+
+template <typename IO>
+__device__ __forceinline__ float io_get(const IO* p) {
+  if constexpr (sizeof(IO) == 4)
+    return *reinterpret_cast<const float*>(p);
+  else
+    return bf16u_to_f32(*reinterpret_cast<const u16*>(p));
+}
+template <typename IO>
+__device__ __forceinline__ void io_put(IO* p, float x) {
+  if constexpr (sizeof(IO) == 4)
+    *reinterpret_cast<float*>(p) = x;
+  else
+    *reinterpret_cast<u16*>(p) = f32_to_bf16u(x);
+}
+
+// ---------------------------------------------------------------------------
+template <int M>
+struct BwdTokLayout {
+  static constexpr int NW = bwd_tok_waves<M>(), GT = 16 * NW, LDF = M + 4;
+  static constexpr int OFF_KT = 0;
+  static constexpr int OFF_Q = OFF_KT + M * BWD_LD;
+  static constexpr int OFF_DO = OFF_Q + GT * BWD_LD;
+  static constexpr int OFF_F = OFF_DO + GT * BWD_LD;
+  static constexpr int OFF_DS = OFF_F + GT * LDF;
+  static constexpr int OFF_AW = OFF_DS + GT * LDF;
+  static constexpr int OFF_AK = OFF_AW + M * BWD_LD;
+  static constexpr int FLOATS = OFF_AK + M * BWD_LD;
+  static constexpr int BYTES = 4 * FLOATS;
+  static_assert(BYTES <= 160 * 1024, "k_bwd_tok LDS");
+};
+
+// grid (nct, BH), block 64 NW.
+template <typename IO, int M>
+__global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  using Ly = BwdTokLayout<M>;
+  constexpr int NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, TM = M / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int t0 = chunk * BWD_CT, t1 = min(a.n, t0 + BWD_CT);
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const float* Wg = a.W + (size_t)bh * M * HD;
+  float* const Kt = bw_lds + Ly::OFF_KT;
+  float* const Qg = bw_lds + Ly::OFF_Q;
+  float* const DOg = bw_lds + Ly::OFF_DO;
+  float* const Fg = bw_lds + Ly::OFF_F;
+  float* const DSg = bw_lds + Ly::OFF_DS;
+  float* const AW = bw_lds + Ly::OFF_AW;
+  float* const AK = bw_lds + Ly::OFF_AK;
+  for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
+    Kt[(i / HD) * BWD_LD + i % HD] = a.kt[(size_t)bh * M * HD + i];
+    AW[(i / HD) * BWD_LD + i % HD] = 0.f;
+    AK[(i / HD) * BWD_LD + i % HD] = 0.f;
+  }
+  __syncthreads();
+  for (int gs = t0; gs < t1; gs += GT) {
+    // ---- phase A: the wave's 16 tokens
+    const int tw = gs + 16 * wave;
+    {
+      const int r = lane >> 2, c0 = 16 * (lane & 3), tok = tw + r;
+      float* qd = Qg + (16 * wave + r) * BWD_LD + c0;
+      float* od = DOg + (16 * wave + r) * BWD_LD + c0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float xq[8], xo[8];
+        if (tok < t1) {
+          IOTraits<IO>::load8(Q + (size_t)tok * HD + c0 + 8 * h, xq);
+          IOTraits<IO>::load8(DO + (size_t)tok * HD + c0 + 8 * h, xo);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[e] = xo[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qd[8 * h + e] = xq[e] * a.s4;
+          od[8 * h + e] = xo[e];
+        }
+      }
+    }
+    // S = Qs Kt^T and dF = dout W^T: C(token 4g + r, landmark 16 jt + c16)
+    f32x4 f[TM], df[TM];
+#pragma unroll
+    for (int jt = 0; jt < TM; ++jt) {
+      f[jt] = mm16<HD>(Qg + 16 * wave * BWD_LD, BWD_LD, 1, Kt + 16 * jt * BWD_LD, 1, BWD_LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      df[jt] = mm16<HD>(DOg + 16 * wave * BWD_LD, BWD_LD, 1, Wg + 16 * jt * HD, 1, HD, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) mx = fmaxf(mx, f[jt][r]);
+      mx = max16(mx);
+      float s = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) {
+        f[jt][r] = __expf(f[jt][r] - mx);
+        s += f[jt][r];
+      }
+      const float inv = 1.0f / sum16(s);
+      float dt = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) {
+        f[jt][r] *= inv;
+        dt += f[jt][r] * df[jt][r];
+      }
+      dt = sum16(dt);
+      const int row = 16 * wave + 4 * g + r;
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) {
+        Fg[row * LDF + 16 * jt + c16] = f[jt][r];
+        DSg[row * LDF + 16 * jt + c16] = f[jt][r] * (df[jt][r] - dt);
+      }
+    }
+    // dQs = dS Kt (16 tokens x 64 channels), the wave's own rows
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 c = mm16<M>(DSg + 16 * wave * LDF, LDF, 1, Kt + 16 * ct, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tw + 4 * g + r;
+        if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * HD + 16 * ct + c16] = c[r];
+      }
+    }
+    __syncthreads();
+    // ---- phase B: dW += F^T dout and dKt += dS^T Qs over the group's tokens
+    for (int ti = wave; ti < 2 * TM * 4; ti += NW) {
+      const bool isk = ti >= TM * 4;
+      const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+      const float* A0 = (isk ? DSg : Fg) + 16 * jt;
+      const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+      const f32x4 c = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+      float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * BWD_LD + 16 * ct + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+    }
+    __syncthreads();
+  }
+  float* const pw = a.pw + ((size_t)bh * a.nct + chunk) * M * HD;
+  float* const pk = a.pk + ((size_t)bh * a.nct + chunk) * M * HD;
+  for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
+    pw[i] = AW[(i / HD) * BWD_LD + i % HD];
+    pk[i] = AK[(i / HD) * BWD_LD + i % HD];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide product C = alpha op(A) op(B) + beta C for float32 row-major
+// matrices in global memory: op(A) is R x K, op(B) is K x N; each operand
+// is staged in LDS (row stride + 4) first.  256 threads.
+template <int R, int N, int K>
+__device__ void bgemm(float* C, const float* Ag, bool ta, const float* Bg, bool tb, float alpha, float beta,
+                      float* La, float* Lb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  // stored shapes: A is (ta ? K x R : R x K), B is (tb ? N x K : K x N)
+  const int ar = ta ? K : R, ac = ta ? R : K, br = tb ? N : K, bc = tb ? K : N;
+  const int lda = ac + 4, ldb = bc + 4;
+  __syncthreads();  // earlier results written; LDS free
+  for (int i = threadIdx.x; i < ar * ac; i += 256) La[(i / ac) * lda + i % ac] = Ag[i];
+  for (int i = threadIdx.x; i < br * bc; i += 256) Lb[(i / bc) * ldb + i % bc] = Bg[i];
+  __syncthreads();
+  const int ai = ta ? 1 : lda, ak = ta ? lda : 1;
+  const int bk = tb ? 1 : ldb, bj = tb ? ldb : 1;
+  constexpr int TR = R / 16, TN = N / 16;
+  for (int t = wave; t < TR * TN; t += 4) {
+    const int it = t / TN, jt = t % TN;
+    const f32x4 c = mm16<K>(La + 16 * it * ai, ai, ak, Lb + 16 * jt * bj, bk, bj, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* p = C + (size_t)(16 * it + 4 * g + r) * N + 16 * jt + c16;
+      *p = beta == 0.f ? alpha * c[r] : alpha * c[r] + beta * *p;
+    }
+  }
+}
+
+// two staged operands of up to max(M, 64) x max(M, 64) floats (row stride + 4)
+template <int M>
+constexpr int bwd_mm_side() {
+  return M > HD ? M : HD;
+}
+template <int M>
+constexpr int bwd_mm_lds_bytes() {
+  return 4 * 2 * bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+}
+
+// grid BH, block 256, dynamic LDS bwd_mm_lds_bytes<M>().
+template <int M>
+__global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  constexpr int MM = M * M;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* const La = bw_lds;
+  float* const Lb = bw_lds + bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+  const float* A = a.A + (size_t)bh * MM;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  auto Zk = [&](int k) { return S + (size_t)k * MM; };
+  auto Xk = [&](int k) { return S + (size_t)(a.n_iter + 1 + 3 * k) * MM; };
+  auto X2k = [&](int k) { return Xk(k) + MM; };
+  auto Pk = [&](int k) { return Xk(k) + 2 * MM; };
+  float* const G = S + (size_t)(4 * a.n_iter + 1) * MM;
+  float* const Gn = G + MM;
+  float* const dP = G + 2 * MM;
+  float* const dX = G + 3 * MM;
+  float* const T = G + 4 * MM;
+  float* const dA = G + 5 * MM;
+  float* const dW = a.dW + (size_t)bh * M * HD;
+  const float c = a.cscale[bh];
+
+  // dW and dKt (F part) from the token-chunk partials, in chunk order
+  for (int i = tid; i < M * HD; i += 256) {
+    float sw = 0.f, sk = 0.f;
+    for (int ch = 0; ch < a.nct; ++ch) {
+      sw += a.pw[((size_t)bh * a.nct + ch) * M * HD + i];
+      sk += a.pk[((size_t)bh * a.nct + ch) * M * HD + i];
+    }
+    dW[i] = sw;
+    a.dKt[(size_t)bh * M * HD + i] = sk;
+  }
+  // the iteration again in float32: Z_0 = A^T / c, X = A Z, P = 13I - 15X +
+  // 7X^2 - X^3, Z <- Z P / 4; dA starts at zero
+  for (int i = tid; i < MM; i += 256) {
+    Zk(0)[i] = A[(i % M) * M + i / M] / c;
+    dA[i] = 0.f;
+  }
+  for (int k = 0; k < a.n_iter; ++k) {
+    bgemm<M, M, M>(Xk(k), A, false, Zk(k), false, 1.f, 0.f, La, Lb);
+    bgemm<M, M, M>(X2k(k), Xk(k), false, Xk(k), false, 1.f, 0.f, La, Lb);
+    bgemm<M, M, M>(Pk(k), Xk(k), false, X2k(k), false, -1.f, 0.f, La, Lb);
+    __syncthreads();
+    for (int i = tid; i < MM; i += 256)
+      Pk(k)[i] += (i / M == i % M ? 13.f : 0.f) - 15.f * Xk(k)[i] + 7.f * X2k(k)[i];
+    bgemm<M, M, M>(Zk(k + 1), Zk(k), false, Pk(k), false, 0.25f, 0.f, La, Lb);
+  }
+  // dZ_n = dW BV^T, dBV = Z_n^T dW
+  bgemm<M, M, HD>(G, dW, false, a.BV + (size_t)bh * M * HD, true, 1.f, 0.f, La, Lb);
+  bgemm<M, HD, M>(a.dBV + (size_t)bh * M * HD, Zk(a.n_iter), true, dW, false, 1.f, 0.f, La, Lb);
+  float* g = G;
+  float* gn = Gn;
+  for (int k = a.n_iter - 1; k >= 0; --k) {
+    float* const Z = Zk(k);
+    float* const X = Xk(k);
+    float* const X2 = X2k(k);
+    bgemm<M, M, M>(gn, g, false, Pk(k), true, 0.25f, 0.f, La, Lb);   // dZ_k = G P^T / 4
+    bgemm<M, M, M>(dP, Z, true, g, false, 0.25f, 0.f, La, Lb);        // dP = Z^T G / 4
+    __syncthreads();
+    for (int i = tid; i < MM; i += 256) dX[i] = -15.f * dP[i];
+    bgemm<M, M, M>(dX, dP, false, X, true, 7.f, 1.f, La, Lb);         // + 7 dP X^T
+    bgemm<M, M, M>(dX, X, true, dP, false, 7.f, 1.f, La, Lb);         // + 7 X^T dP
+    bgemm<M, M, M>(dX, dP, false, X2, true, -1.f, 1.f, La, Lb);       // - dP (X^2)^T
+    bgemm<M, M, M>(T, X, true, dP, false, 1.f, 0.f, La, Lb);
+    bgemm<M, M, M>(dX, T, false, X, true, -1.f, 1.f, La, Lb);         // - X^T dP X^T
+    bgemm<M, M, M>(dX, X2, true, dP, false, -1.f, 1.f, La, Lb);       // - (X^2)^T dP
+    bgemm<M, M, M>(dA, dX, false, Z, true, 1.f, 1.f, La, Lb);         // dA += dX Z^T
+    bgemm<M, M, M>(gn, A, true, dX, false, 1.f, 1.f, La, Lb);         // dZ_k += A^T dX
+    float* const t = g;
+    g = gn;
+    gn = t;
+  }
+  __syncthreads();
+  // Z_0 = A^T / c: dA += G^T / c; dc = -sum(G A^T) / c^2; and the arg-max column of A's column sums
+  float part = 0.f;
+  for (int i = tid; i < MM; i += 256) {
+    const int r = i / M, col = i % M;
+    dA[i] += g[col * M + r] / c;
+    part += g[col * M + r] * A[i];
+  }
+  __shared__ float red[256];
+  __shared__ int redj[256];
+  red[tid] = part;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float dcv = -red[0] / (c * c);
+  __syncthreads();
+  float cs = -1.f, rs = 0.f;
+  int cj = 0;
+  if (tid < M) {
+    cs = 0.f;
+    for (int r = 0; r < M; ++r) cs += A[r * M + tid];
+    for (int j = 0; j < M; ++j) rs += A[tid * M + j];
+    cj = tid;
+  }
+  red[tid] = cs;
+  redj[tid] = cj;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s && (red[tid + s] > red[tid] || (red[tid + s] == red[tid] && redj[tid + s] < redj[tid]))) {
+      red[tid] = red[tid + s];
+      redj[tid] = redj[tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.dc[bh] = dcv;
+    a.cmax[bh] = red[0];
+    a.cmaxj[bh] = redj[0];
+  }
+  __syncthreads();
+  red[tid] = tid < M ? rs : 0.f;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  if (tid == 0) a.rmax[bh] = red[0];
+}
+
+// grid BH, block 256, dynamic LDS bwd_mm_lds_bytes<M>().
+template <int M>
+__global__ __launch_bounds__(256) void k_bwd_mm2(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  constexpr int MM = M * M;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* const La = bw_lds;
+  float* const Lb = bw_lds + bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+  const float* A = a.A + (size_t)bh * MM;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
+  float* const dSA = S + (size_t)(4 * a.n_iter + 1 + 4) * MM;  // the T slot
+  // c's share: column j* of the head holding the maximum column sum
+  __shared__ float add;
+  __shared__ int jstar;
+  if (tid == 0) {
+    float dcs = a.dc[bh], rm = a.rmax[bh];
+    bool mine = true;
+    if (a.init_option == 0) {
+      int hs = 0;
+      float best = a.cmax[0];
+      dcs = 0.f;
+      rm = 0.f;
+      for (int h = 0; h < a.BH; ++h) {
+        dcs += a.dc[h];
+        rm = fmaxf(rm, a.rmax[h]);
+        if (a.cmax[h] > best) {
+          best = a.cmax[h];
+          hs = h;
+        }
+      }
+      mine = hs == bh;
+    }
+    add = mine ? dcs * rm : 0.f;
+    jstar = a.cmaxj[bh];
+  }
+  __syncthreads();
+  if (add != 0.f)
+    for (int r = tid; r < M; r += 256) dA[r * M + jstar] += add;
+  __syncthreads();
+  // dS_A = A (dA - rowsum(dA A)), one row per thread
+  for (int r = tid; r < M; r += 256) {
+    float s = 0.f;
+    for (int j = 0; j < M; ++j) s += dA[r * M + j] * A[r * M + j];
+    for (int j = 0; j < M; ++j) dSA[r * M + j] = A[r * M + j] * (dA[r * M + j] - s);
+  }
+  // dQt_A = dS_A Kt; dKt += dS_A^T Qt
+  bgemm<M, HD, M>(a.dQt + (size_t)bh * M * HD, dSA, false, a.kt + (size_t)bh * M * HD, false, 1.f, 0.f, La, Lb);
+  bgemm<M, HD, M>(a.dKt + (size_t)bh * M * HD, dSA, true, a.qt + (size_t)bh * M * HD, false, 1.f, 1.f, La, Lb);
+  // D_i = dBV_i . BV_i
+  for (int r = tid; r < M; r += 256) {
+    float s = 0.f;
+    for (int c = 0; c < HD; ++c)
+      s += a.dBV[((size_t)bh * M + r) * HD + c] * a.BV[((size_t)bh * M + r) * HD + c];
+    a.Dv[(size_t)bh * M + r] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int M>
+struct BwdKeyLayout {
+  static constexpr int LDB = BWD_GK + 4;
+  static constexpr int OFF_QT = 0;
+  static constexpr int OFF_DBV = OFF_QT + M * BWD_LD;
+  static constexpr int OFF_KS = OFF_DBV + M * BWD_LD;
+  static constexpr int OFF_V = OFF_KS + BWD_GK * BWD_LD;
+  static constexpr int OFF_B = OFF_V + BWD_GK * BWD_LD;
+  static constexpr int OFF_DS = OFF_B + M * LDB;
+  static constexpr int OFF_ACC = OFF_DS + M * LDB;
+  static constexpr int OFF_VAL = OFF_ACC + M * BWD_LD;
+  static constexpr int FLOATS = OFF_VAL + BWD_GK;
+  static constexpr int BYTES = 4 * FLOATS;
+  static_assert(BYTES <= 160 * 1024, "k_bwd_key LDS");
+};
+
+// grid (nck, BH), block 256.
+template <typename IO, int M>
+__global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  using Ly = BwdKeyLayout<M>;
+  constexpr int TM = M / 16, LDB = Ly::LDB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x, b = bh / a.H;
+  const int k0 = chunk * BWD_CK, k1 = min(a.n, k0 + BWD_CK);
+  const IO* Kg = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* Vg = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  const float* lse = a.lse + (size_t)bh * M;
+  const float* Dv = a.Dv + (size_t)bh * M;
+  const float* dKt = a.dKt + (size_t)bh * M * HD;
+  float* const Qt = bw_lds + Ly::OFF_QT;
+  float* const dBV = bw_lds + Ly::OFF_DBV;
+  float* const Ks = bw_lds + Ly::OFF_KS;
+  float* const Vs = bw_lds + Ly::OFF_V;
+  float* const Bt = bw_lds + Ly::OFF_B;
+  float* const DS = bw_lds + Ly::OFF_DS;
+  float* const ACC = bw_lds + Ly::OFF_ACC;
+  float* const VAL = bw_lds + Ly::OFF_VAL;
+  for (int i = tid; i < M * HD; i += 256) {
+    const int r = i / HD, c = i % HD;
+    Qt[r * BWD_LD + c] = a.qt[(size_t)bh * M * HD + i];
+    dBV[r * BWD_LD + c] = a.dBV[(size_t)bh * M * HD + i];
+    ACC[r * BWD_LD + c] = 0.f;
+  }
+  const float inv_l = 1.0f / (float)a.L;
+  for (int gk = k0; gk < k1; gk += BWD_GK) {
+    __syncthreads();  // staging done / previous step's reads done
+    for (int i = tid; i < BWD_GK * HD; i += 256) {
+      const int r = i / HD, c = i % HD, key = gk + r;
+      const bool in = key < k1;
+      Ks[r * BWD_LD + c] = in ? io_get(Kg + (size_t)key * HD + c) * a.s4 : 0.f;
+      Vs[r * BWD_LD + c] = in ? io_get(Vg + (size_t)key * HD + c) : 0.f;
+    }
+    if (tid < BWD_GK) {
+      const int key = gk + tid;
+      VAL[tid] = (key < k1 && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
+    for (int t = wave; t < TM * (BWD_GK / 16); t += 4) {
+      const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
+      const f32x4 s = mm16<HD>(Qt + 16 * it * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD,
+                               f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 db = mm16<HD>(dBV + 16 * it * BWD_LD, BWD_LD, 1, Vs + 16 * kt * BWD_LD, 1, BWD_LD,
+                                f32x4{0.f, 0.f, 0.f, 0.f});
+      const float val = VAL[16 * kt + c16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g + r;
+        const float bb = val != 0.f ? exp2f(s[r] * LOG2E - lse[i]) : 0.f;
+        Bt[i * LDB + 16 * kt + c16] = bb;
+        DS[i * LDB + 16 * kt + c16] = bb * (db[r] - Dv[i]);
+      }
+    }
+    __syncthreads();
+    // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[seg] / L): C(key, channel)
+    for (int t = wave; t < 2 * (BWD_GK / 16) * 4; t += 4) {
+      const bool isk = t >= (BWD_GK / 16) * 4;
+      const int tt = t % ((BWD_GK / 16) * 4), kt = tt >> 2, ct = tt & 3;
+      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, BWD_LD, 1,
+                              f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = gk + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
+        if (key >= k1) continue;
+        const size_t o = ((size_t)bh * a.n + key) * HD + ch;
+        if (isk) {
+          const float x = c[r] + dKt[(size_t)(key / a.L) * HD + ch] * inv_l;
+          io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * x);
+        } else {
+          const float x = c[r] + (a.dvc != nullptr ? a.dvc[o] : 0.f);
+          io_put(reinterpret_cast<IO*>(a.dv) + o, x);
+        }
+      }
+    }
+    // dQt_B += dS Ks: C(landmark, channel), summed over the step's keys
+    for (int t = wave; t < TM * 4; t += 4) {
+      const int it = t >> 2, ct = t & 3;
+      const f32x4 c = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+      float* acc = ACC + (16 * it + 4 * g) * BWD_LD + 16 * ct + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+    }
+  }
+  __syncthreads();
+  float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * HD;
+  for (int i = tid; i < M * HD; i += 256) pq[i] = ACC[(i / HD) * BWD_LD + i % HD];
+}
+
+// dQt = dQt_A + sum of the key-chunk partials.  grid BH, block 256.
+template <int M>
+__global__ __launch_bounds__(256) void k_bwd_qt(BwdArgs a) {
+  const int bh = blockIdx.x;
+  for (int i = threadIdx.x; i < M * HD; i += 256) {
+    float s = a.dQt[(size_t)bh * M * HD + i];
+    for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * HD + i];
+    a.dQt[(size_t)bh * M * HD + i] = s;
+  }
+}
+
+// dq = d^-1/4 (dQs + dQt[segment] / L).  grid (ceil(n / 64), BH), block 256:
+// thread = (token, 16-channel quarter).
+template <typename IO, int M>
+__global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
+  const int bh = blockIdx.y;
+  const int tok = blockIdx.x * 64 + (threadIdx.x >> 2), c0 = 16 * (threadIdx.x & 3);
+  if (tok >= a.n) return;
+  const float inv_l = 1.0f / (float)a.L;
+  const float* dqf = a.dqf + ((size_t)bh * a.n + tok) * HD + c0;
+  const float* dqt = a.dQt + ((size_t)bh * M + tok / a.L) * HD + c0;
+  IO* const dq = reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * HD + c0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) io_put(dq + e, a.s4 * (dqf[e] + dqt[e] * inv_l));
+}
+
+// Convolution backward: dv_conv[t] = sum_j w[j] dout[t - j + K/2] and the
+// chunk's partial dconv_w[j] = sum_t,c dout[t][c] v[t + j - K/2][c].
+// grid (ncv, BH), block 256, windows of dout and v (tokens t0 - 32 ..
+// t0 + 160) in LDS.
+constexpr int BWD_CVWIN = BWD_CV + 64;
+constexpr int BWD_CV_LDS = 4 * (2 * BWD_CVWIN * (HD + 1) + 4 * TAPS);
+
+// dynamic LDS BWD_CV_LDS
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  float* const dow = bw_lds;
+  float* const vw = dow + BWD_CVWIN * (HD + 1);
+  float(*wr)[TAPS] = reinterpret_cast<float(*)[TAPS]>(vw + BWD_CVWIN * (HD + 1));
+  const int bh = blockIdx.y, h = bh % a.H, chunk = blockIdx.x, tid = threadIdx.x;
+  const int t0 = chunk * BWD_CV, K = a.conv_k, half = K / 2;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const float* w = a.conv_w + (size_t)h * K;
+  for (int i = tid; i < BWD_CVWIN * HD; i += 256) {
+    const int r = i / HD, c = i % HD, t = t0 - HALO + r;
+    const bool in = t >= 0 && t < a.n;
+    dow[r * (HD + 1) + c] = in ? io_get(DO + (size_t)t * HD + c) : 0.f;
+    vw[r * (HD + 1) + c] = in ? io_get(V + (size_t)t * HD + c) : 0.f;
+  }
+  __syncthreads();
+  // dv_conv: (token, 16-channel quarter) items
+  for (int it = tid; it < BWD_CV * 4; it += 256) {
+    const int tl = it >> 2, c0 = 16 * (it & 3), t = t0 + tl;
+    if (t >= a.n) continue;
+    float s[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    for (int j = 0; j < K; ++j) {
+      const float wj = w[j];
+      const float* row = dow + (tl + HALO - j + half) * (HD + 1) + c0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] += wj * row[e];
+    }
+    float* dst = a.dvc + ((size_t)bh * a.n + t) * HD + c0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dst[e] = s[e];
+  }
+  // partial dconv_w: (tap, 16-channel quarter) items, then the quarters in order
+  for (int it = tid; it < K * 4; it += 256) {
+    const int j = it >> 2, c0 = 16 * (it & 3);
+    float s = 0.f;
+    const int tn = min(BWD_CV, a.n - t0);
+    for (int tl = 0; tl < tn; ++tl) {
+      const float* o = dow + (tl + HALO) * (HD + 1) + c0;
+      const float* vv = vw + (tl + HALO + j - half) * (HD + 1) + c0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += o[e] * vv[e];
+    }
+    wr[it & 3][j] = s;
+  }
+  __syncthreads();
+  if (tid < K) a.pconv[((size_t)bh * a.ncv + chunk) * K + tid] = ((wr[0][tid] + wr[1][tid]) + wr[2][tid]) + wr[3][tid];
+}
+
+// dconv_w[h][j] = sum over batches and chunks (in order).  grid H, block 128.
+__global__ __launch_bounds__(128) void k_bwd_wsum(BwdArgs a) {
+  const int h = blockIdx.x, j = threadIdx.x, K = a.conv_k;
+  if (j >= K) return;
+  const int B = a.BH / a.H;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int ch = 0; ch < a.ncv; ++ch) s += a.pconv[((size_t)(b * a.H + h) * a.ncv + ch) * K + j];
+  a.dconv_w[(size_t)h * K + j] = s;
+}
+
+}  // namespace nys

@@ -37,6 +37,7 @@ struct MergeArgs {
   float* W;            // [BH][M][d]
   __bf16* wf_hi;       // [BH][d/16][M/32][64][8]
   __bf16* wf_lo;
+  float* lse;          // [BH][M] or null: log2 of each B row's normaliser (+inf for a row with no kept key)
   int S, BH;
 };
 
@@ -168,6 +169,7 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
       for (int c = 0; c < 4; ++c) acc[c] += pp[2 + c] * wgt;
     }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    if (a.lse != nullptr && run == 0) a.lse[(size_t)bh * M + t] = tot > 0.f ? mx + log2f(tot) : INFINITY;
     const float4 bv = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     bvs[t] = bv;
     *reinterpret_cast<float4*>(a.BV + ((size_t)bh * M + t) * D + ch) = bv;

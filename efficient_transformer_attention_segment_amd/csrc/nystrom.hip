@@ -41,6 +41,7 @@
 #include "k_out.hpp"
 #include "k_pinv.hpp"
 #include "k_probs.hpp"
+#include "k_bwd.hpp"
 
 using namespace nys;
 
@@ -73,9 +74,10 @@ struct Plan {
   bool record;  // keep every intermediate in the workspace (stage hook)
   Strides si, so;  // element strides of q, k, v and of out
   void* probs;     // attention weights [B, H, n, mr] on request, else null
+  bool bwd;        // forward stages for the backward pass: stop after W, keep B's normalisers
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
-  size_t off_slots, off_junk;
+  size_t off_slots, off_junk, off_lse;
   size_t total;
 };
 
@@ -155,6 +157,7 @@ Plan make_plan(int B, int H, int n, int mr, int d) {
   p.off_W = take(BH * M * D * 4);
   p.off_wfh = take(BH * M * D * 2);
   p.off_wfl = take(BH * M * D * 2);
+  p.off_lse = take(BH * M * 4);
   if (m > 128) {
     p.off_X = take(BH * M * M * 4);
     p.off_T1 = take(BH * M * M * 4);
@@ -363,6 +366,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ma.wf_lo = at<__bf16>(w, p.off_wfl);
   ma.S = p.S;
   ma.BH = p.BH;
+  ma.lse = p.bwd ? at<float>(w, p.off_lse) : nullptr;
   // threads per block: enough chunk subsets per row that each thread folds
   // one batch of 8 chunks (up to 1024 threads; 512 for m = 32)
   const int need = M * ((p.S + 7) / 8);
@@ -376,6 +380,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     HIP_TRY(launch("k_mw", k_mw<M, B16, 512, D>, mwg, dim3(512), 0, st, ma));
   else
     HIP_TRY(launch("k_mw", k_mw<M, B16, NT_MAX, D>, mwg, dim3(NT_MAX), 0, st, ma));
+  if (p.bwd) return NYS_OK;  // the backward pass takes it from here
 
   OutArgs oa;
   oa.q = q;
@@ -778,6 +783,169 @@ int run_module(const void* x, const void* w, const void* b, const uint8_t* mask,
                  nullptr);
 }
 
+// ------------------------------------------------------------ backward ---
+// Forward stages (without the output pass) into the plan's workspace, then
+// the backward kernels into the regions that follow it.
+struct BwdPlan {
+  int nct, nck, ncv, mats;
+  size_t off_dqf, off_pw, off_pk, off_pq, off_mm, off_dW, off_dBV, off_dQt, off_dKt, off_Dv, off_dc, off_cmax,
+      off_cmaxj, off_rmax, off_dvc, off_pconv, total;
+};
+
+BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
+  BwdPlan b{};
+  b.nct = (p.n + BWD_CT - 1) / BWD_CT;
+  b.nck = (p.n + BWD_CK - 1) / BWD_CK;
+  b.ncv = (p.n + BWD_CV - 1) / BWD_CV;
+  b.mats = bwd_mm_mats(n_iter);
+  const size_t BH = p.BH, M = p.m, n = p.n, D = HD;
+  size_t o = p.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  b.off_dqf = take(BH * n * D * 4);
+  b.off_pw = take(BH * b.nct * M * D * 4);
+  b.off_pk = take(BH * b.nct * M * D * 4);
+  b.off_pq = take(BH * b.nck * M * D * 4);
+  b.off_mm = take(BH * b.mats * M * M * 4);
+  b.off_dW = take(BH * M * D * 4);
+  b.off_dBV = take(BH * M * D * 4);
+  b.off_dQt = take(BH * M * D * 4);
+  b.off_dKt = take(BH * M * D * 4);
+  b.off_Dv = take(BH * M * 4);
+  b.off_dc = take(BH * 4);
+  b.off_cmax = take(BH * 4);
+  b.off_cmaxj = take(BH * 4);
+  b.off_rmax = take(BH * 4);
+  b.off_dvc = conv ? take(BH * n * D * 4) : 0;
+  b.off_pconv = conv ? take(BH * b.ncv * (size_t)conv_k * 4) : 0;
+  b.total = o;
+  return b;
+}
+
+template <typename IO, int M>
+int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* q, const void* k, const void* v,
+                    const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option,
+                    const void* dout, void* dq, void* dk, void* dv, float* dconv_w, hipStream_t st) {
+  int rc = launch_nystrom<IO, M, HD>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, nullptr, st);
+  if (rc != NYS_OK) return rc;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.key_mask = mask;
+  a.conv_w = conv_w;
+  a.conv_k = conv_k;
+  a.qt = at<float>(w, p.off_qt);
+  a.kt = at<float>(w, p.off_kt);
+  a.A = at<float>(w, p.off_A);
+  a.BV = at<float>(w, p.off_BV);
+  a.W = at<float>(w, p.off_W);
+  a.lse = at<float>(w, p.off_lse);
+  a.cscale = at<float>(w, p.off_cscale);
+  a.dqf = at<float>(w, bp.off_dqf);
+  a.pw = at<float>(w, bp.off_pw);
+  a.pk = at<float>(w, bp.off_pk);
+  a.pq = at<float>(w, bp.off_pq);
+  a.mm = at<float>(w, bp.off_mm);
+  a.dW = at<float>(w, bp.off_dW);
+  a.dBV = at<float>(w, bp.off_dBV);
+  a.dQt = at<float>(w, bp.off_dQt);
+  a.dKt = at<float>(w, bp.off_dKt);
+  a.Dv = at<float>(w, bp.off_Dv);
+  a.dc = at<float>(w, bp.off_dc);
+  a.cmax = at<float>(w, bp.off_cmax);
+  a.cmaxj = at<int>(w, bp.off_cmaxj);
+  a.rmax = at<float>(w, bp.off_rmax);
+  a.dvc = conv_w != nullptr ? at<float>(w, bp.off_dvc) : nullptr;
+  a.pconv = conv_w != nullptr ? at<float>(w, bp.off_pconv) : nullptr;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dconv_w = dconv_w;
+  a.n = p.n;
+  a.H = p.H;
+  a.BH = p.BH;
+  a.mr = p.mr;
+  a.L = p.L;
+  a.nct = bp.nct;
+  a.nck = bp.nck;
+  a.ncv = bp.ncv;
+  a.n_iter = n_iter;
+  a.init_option = init_option;
+  a.s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  if (conv_w != nullptr) {
+    HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
+    HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)BWD_CV_LDS, st, a));
+  }
+  constexpr int tl = BwdTokLayout<M>::BYTES;
+  HIP_TRY(allow_lds(k_bwd_tok<IO, M>, tl));
+  HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl, st,
+                 a));
+  constexpr int ml = bwd_mm_lds_bytes<M>();
+  HIP_TRY(allow_lds(k_bwd_mm1<M>, ml));
+  HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(256), (uint32_t)ml, st, a));
+  HIP_TRY(allow_lds(k_bwd_mm2<M>, ml));
+  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M>, dim3(p.BH), dim3(256), (uint32_t)ml, st, a));
+  constexpr int kl = BwdKeyLayout<M>::BYTES;
+  HIP_TRY(allow_lds(k_bwd_key<IO, M>, kl));
+  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M>, dim3(bp.nck, p.BH), dim3(256), (uint32_t)kl, st, a));
+  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M>, dim3(p.BH), dim3(256), 0, st, a));
+  HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
+  if (conv_w != nullptr && dconv_w != nullptr)
+    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(128), 0, st, a));
+  return NYS_OK;
+}
+
+template <typename IO>
+int run_backward(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k,
+                 int B, int H, int n, int d, int m, int n_iter, int init_option, const void* dout, void* dq, void* dk,
+                 void* dv, float* dconv_w, hipStream_t st) {
+  int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, dq);
+  if (rc != NYS_OK) return rc;
+  if (!dout || !dk || !dv) return fail(NYS_ERR_INVALID, "dout, dq, dk and dv must be non-NULL");
+  if (conv_w != nullptr) {
+    if (conv_k < 1 || conv_k % 2 == 0)
+      return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
+    if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
+  }
+  if (d != HD) return fail(NYS_ERR_UNSUPPORTED, "backward: d=%d (the backward kernels are built for d=64)", d);
+  if (m == n) return fail(NYS_ERR_UNSUPPORTED, "backward: the exact branch (m == n) has no backward kernels");
+  if (padded_m(m) > 128) return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to 128 landmarks)", m);
+  const size_t bytes = (size_t)B * H * n * HD * sizeof(IO);
+  const void* const ro[4] = {q, k, v, dout};
+  void* const wr[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    if (reinterpret_cast<uintptr_t>(wr[i]) % 16 != 0) return fail(NYS_ERR_INVALID, "dq, dk, dv must be 16-byte aligned");
+    for (int j = 0; j < 4; ++j)
+      if (ranges_meet(wr[i], bytes, ro[j], bytes)) return fail(NYS_ERR_INVALID, "dq, dk, dv must not overlap q, k, v, dout");
+    for (int j = 0; j < i; ++j)
+      if (ranges_meet(wr[i], bytes, wr[j], bytes)) return fail(NYS_ERR_INVALID, "dq, dk, dv must not overlap");
+  }
+  for (const void* ptr : {q, k, v, dout})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(NYS_ERR_INVALID, "q, k, v, dout must be 16-byte aligned");
+  Plan p = make_plan(B, H, n, m, d);
+  p.record = true;  // A is read back
+  p.bwd = true;
+  p.si = p.so = dense(B, H, n, d);
+  const BwdPlan bp = make_bwd_plan(p, n_iter, conv_k, conv_w != nullptr);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace* w = nullptr;
+  rc = get_workspace(st, bp.total, &w);
+  if (rc != NYS_OK) return rc;
+  switch (p.m) {
+    case 32: return launch_backward<IO, 32>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
+    case 64: return launch_backward<IO, 64>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
+    case 96: return launch_backward<IO, 96>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
+    case 128: return launch_backward<IO, 128>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
+    default: break;
+  }
+  return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d", m);
+}
+
 }  // namespace
 
 extern "C" {
@@ -894,6 +1062,24 @@ __attribute__((visibility("default"))) int nystrom_self_attention(
     if (dtype == 1)
       return run_module<u16>(x, w_qkv, b_qkv, key_mask, conv_w, conv_kernel_size, B, n, hidden, H, d, m, n_iter,
                              init_option, qkv, out, stream);
+    return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) int nystrom_attention_backward(
+    int dtype, const void* q, const void* k, const void* v, const uint8_t* key_mask, const float* conv_w,
+    int conv_kernel_size, int B, int H, int n, int d, int m, int n_iter, int init_option, const void* dout, void* dq,
+    void* dk, void* dv, float* dconv_w, struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    if (dtype == 0)
+      return run_backward<float>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option,
+                                 dout, dq, dk, dv, dconv_w, stream);
+    if (dtype == 1)
+      return run_backward<u16>(q, k, v, key_mask, conv_w, conv_kernel_size, B, H, n, d, m, n_iter, init_option, dout,
+                               dq, dk, dv, dconv_w, stream);
     return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");

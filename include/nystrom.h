@@ -178,6 +178,25 @@ int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const vo
                            int init_option, void* qkv, void* out,
                            struct ihipStream_t* stream);
 
+/* Backward pass for training ([P1] sections 2.2-2.6 differentiated; the
+ * pages mention training with gradient checkpointing and the Trainer):
+ * given dout = dL/dout for the output of the same call, writes
+ * dq, dk, dv = dL/dq, dL/dk, dL/dv (the dtype's [B, H, n, d], dense) and,
+ * when conv_w and dconv_w are both non-NULL, dconv_w = dL/dconv_w (float32
+ * [H, conv_kernel_size]).  The intermediates are recomputed from q, k, v
+ * (nothing is kept from the forward call).  The initial scale c is
+ * differentiated through its maxima (the gradient of a maximum goes to its
+ * first arg-max).  All pointers are DEVICE pointers owned by the caller;
+ * dq, dk, dv must not overlap each other or q, k, v, dout.  Built for the
+ * Nystrom path at d = 64 with up to 128 landmarks; NYS_ERR_UNSUPPORTED for
+ * other d, more landmarks, or m == n.  Other errors as nystrom_attention. */
+int nystrom_attention_backward(int dtype, const void* q, const void* k, const void* v,
+                               const uint8_t* key_mask, const float* conv_w,
+                               int conv_kernel_size, int B, int H, int n, int d, int m,
+                               int n_iter, int init_option, const void* dout, void* dq,
+                               void* dk, void* dv, float* dconv_w,
+                               struct ihipStream_t* stream);
+
 /* Bytes of device workspace a call of this shape uses (0 for invalid or
  * unsupported shapes). */
 size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);

@@ -123,6 +123,33 @@ def test_probs_validation(lib, probs):
     assert "probs" in lib.nystrom_last_error().decode()
 
 
+FAKE3 = ctypes.c_void_p(0x1100000)
+FAKE4 = ctypes.c_void_p(0x1900000)
+FAKE5 = ctypes.c_void_p(0x2100000)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -1),
+    (dict(dq=None), -1),
+    (dict(dv=None), -1),
+    (dict(dq=FAKE), -1),                      # dq is q
+    (dict(dk=FAKE3), -1),                     # dk is dq
+    (dict(dv=ctypes.c_void_p(0x2100008)), -1),  # misaligned
+    (dict(d=128), -2),                        # backward kernels are built for d = 64
+    (dict(m=256), -2),                        # exact branch (m == n)
+    (dict(m=160, n=640), -2),                 # more than 128 landmarks
+])
+def test_backward_validation(lib, kw, code):
+    """nystrom_attention_backward rejects bad arguments before any launch
+    (q, k, v, dout at FAKE/FAKE2 ranges; dq, dk, dv at FAKE3..FAKE5)."""
+    a = dict(dtype=0, d=64, m=64, n=256, dq=FAKE3, dk=FAKE4, dv=FAKE5)
+    a.update(kw)
+    rc = lib.nystrom_attention_backward(a["dtype"], FAKE, FAKE, FAKE, NULL, NULL, 65, 1, 2, a["n"], a["d"], a["m"], 6,
+                                        0, FAKE2, a["dq"], a["dk"], a["dv"], NULL, NULL)
+    assert rc == code
+    assert lib.nystrom_last_error().decode() != ""
+
+
 @pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
 def test_landmarks_above_256_unsupported(lib, fn):
     assert call(lib, fn, n=600, m=300) == -2
