@@ -132,7 +132,10 @@ struct BwdTokLayout {
   static constexpr int OFF_DS = OFF_F + GT * LDF;
   static constexpr int OFF_AW = OFF_DS + GT * LDF;
   static constexpr int OFF_AK = OFF_AW + M * BWD_LD;
-  static constexpr int FLOATS = OFF_AK + M * BWD_LD;
+  static constexpr int OFF_W = OFF_AK + M * BWD_LD;
+  // W is staged too where it fits (otherwise read from L2)
+  static constexpr bool W_LDS = 4 * (OFF_W + M * BWD_LD) <= 160 * 1024;
+  static constexpr int FLOATS = OFF_W + (W_LDS ? M * BWD_LD : 0);
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_tok LDS");
 };
@@ -157,10 +160,14 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
   float* const DSg = bw_lds + Ly::OFF_DS;
   float* const AW = bw_lds + Ly::OFF_AW;
   float* const AK = bw_lds + Ly::OFF_AK;
+  float* const Wl = bw_lds + Ly::OFF_W;
+  const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
+  constexpr int WLD = Ly::W_LDS ? BWD_LD : HD;
   for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
     Kt[(i / HD) * BWD_LD + i % HD] = a.kt[(size_t)bh * M * HD + i];
     AW[(i / HD) * BWD_LD + i % HD] = 0.f;
     AK[(i / HD) * BWD_LD + i % HD] = 0.f;
+    if constexpr (Ly::W_LDS) Wl[(i / HD) * BWD_LD + i % HD] = Wg[i];
   }
   __syncthreads();
   for (int gs = t0; gs < t1; gs += GT) {
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 #pragma unroll
     for (int jt = 0; jt < TM; ++jt) {
       f[jt] = mm16<HD>(Qg + 16 * wave * BWD_LD, BWD_LD, 1, Kt + 16 * jt * BWD_LD, 1, BWD_LD, f32x4{0.f, 0.f, 0.f, 0.f});
-      df[jt] = mm16<HD>(DOg + 16 * wave * BWD_LD, BWD_LD, 1, Wg + 16 * jt * HD, 1, HD, f32x4{0.f, 0.f, 0.f, 0.f});
+      df[jt] = mm16<HD>(DOg + 16 * wave * BWD_LD, BWD_LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
       if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 #pragma unroll
@@ -255,25 +262,28 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+constexpr int BWD_MM_NT = 1024;  // threads of the per-head kernels (16 waves)
+
 // Block-wide product C = alpha op(A) op(B) + beta C for float32 row-major
 // matrices in global memory: op(A) is R x K, op(B) is K x N; each operand
-// is staged in LDS (row stride + 4) first.  256 threads.
+// is staged in LDS (row stride + 4) first.  BWD_MM_NT threads.
 template <int R, int N, int K>
 __device__ void bgemm(float* C, const float* Ag, bool ta, const float* Bg, bool tb, float alpha, float beta,
                       float* La, float* Lb) {
+  constexpr int NT = BWD_MM_NT, NWV = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   // stored shapes: A is (ta ? K x R : R x K), B is (tb ? N x K : K x N)
   const int ar = ta ? K : R, ac = ta ? R : K, br = tb ? N : K, bc = tb ? K : N;
   const int lda = ac + 4, ldb = bc + 4;
   __syncthreads();  // earlier results written; LDS free
-  for (int i = threadIdx.x; i < ar * ac; i += 256) La[(i / ac) * lda + i % ac] = Ag[i];
-  for (int i = threadIdx.x; i < br * bc; i += 256) Lb[(i / bc) * ldb + i % bc] = Bg[i];
+  for (int i = threadIdx.x; i < ar * ac; i += NT) La[(i / ac) * lda + i % ac] = Ag[i];
+  for (int i = threadIdx.x; i < br * bc; i += NT) Lb[(i / bc) * ldb + i % bc] = Bg[i];
   __syncthreads();
   const int ai = ta ? 1 : lda, ak = ta ? lda : 1;
   const int bk = tb ? 1 : ldb, bj = tb ? ldb : 1;
   constexpr int TR = R / 16, TN = N / 16;
-  for (int t = wave; t < TR * TN; t += 4) {
+  for (int t = wave; t < TR * TN; t += NWV) {
     const int it = t / TN, jt = t % TN;
     const f32x4 c = mm16<K>(La + 16 * it * ai, ai, ak, Lb + 16 * jt * bj, bk, bj, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -294,9 +304,10 @@ constexpr int bwd_mm_lds_bytes() {
   return 4 * 2 * bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
 }
 
-// grid BH, block 256, dynamic LDS bwd_mm_lds_bytes<M>().
+// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M>().
 template <int M>
-__global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
+  constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int MM = M * M;
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
   const float c = a.cscale[bh];
 
   // dW and dKt (F part) from the token-chunk partials, in chunk order
-  for (int i = tid; i < M * HD; i += 256) {
+  for (int i = tid; i < M * HD; i += NT) {
     float sw = 0.f, sk = 0.f;
     for (int ch = 0; ch < a.nct; ++ch) {
       sw += a.pw[((size_t)bh * a.nct + ch) * M * HD + i];
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
   }
   // the iteration again in float32: Z_0 = A^T / c, X = A Z, P = 13I - 15X +
   // 7X^2 - X^3, Z <- Z P / 4; dA starts at zero
-  for (int i = tid; i < MM; i += 256) {
+  for (int i = tid; i < MM; i += NT) {
     Zk(0)[i] = A[(i % M) * M + i / M] / c;
     dA[i] = 0.f;
   }
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
     bgemm<M, M, M>(X2k(k), Xk(k), false, Xk(k), false, 1.f, 0.f, La, Lb);
     bgemm<M, M, M>(Pk(k), Xk(k), false, X2k(k), false, -1.f, 0.f, La, Lb);
     __syncthreads();
-    for (int i = tid; i < MM; i += 256)
+    for (int i = tid; i < MM; i += NT)
       Pk(k)[i] += (i / M == i % M ? 13.f : 0.f) - 15.f * Xk(k)[i] + 7.f * X2k(k)[i];
     bgemm<M, M, M>(Zk(k + 1), Zk(k), false, Pk(k), false, 0.25f, 0.f, La, Lb);
   }
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
     bgemm<M, M, M>(gn, g, false, Pk(k), true, 0.25f, 0.f, La, Lb);   // dZ_k = G P^T / 4
     bgemm<M, M, M>(dP, Z, true, g, false, 0.25f, 0.f, La, Lb);        // dP = Z^T G / 4
     __syncthreads();
-    for (int i = tid; i < MM; i += 256) dX[i] = -15.f * dP[i];
+    for (int i = tid; i < MM; i += NT) dX[i] = -15.f * dP[i];
     bgemm<M, M, M>(dX, dP, false, X, true, 7.f, 1.f, La, Lb);         // + 7 dP X^T
     bgemm<M, M, M>(dX, X, true, dP, false, 7.f, 1.f, La, Lb);         // + 7 X^T dP
     bgemm<M, M, M>(dX, dP, false, X2, true, -1.f, 1.f, La, Lb);       // - dP (X^2)^T
@@ -370,16 +381,16 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
   __syncthreads();
   // Z_0 = A^T / c: dA += G^T / c; dc = -sum(G A^T) / c^2; and the arg-max column of A's column sums
   float part = 0.f;
-  for (int i = tid; i < MM; i += 256) {
+  for (int i = tid; i < MM; i += NT) {
     const int r = i / M, col = i % M;
     dA[i] += g[col * M + r] / c;
     part += g[col * M + r] * A[i];
   }
-  __shared__ float red[256];
-  __shared__ int redj[256];
+  __shared__ float red[NT];
+  __shared__ int redj[NT];
   red[tid] = part;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
   red[tid] = cs;
   redj[tid] = cj;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (tid < s && (red[tid + s] > red[tid] || (red[tid + s] == red[tid] && redj[tid + s] < redj[tid]))) {
       red[tid] = red[tid + s];
       redj[tid] = redj[tid + s];
@@ -411,16 +422,17 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(BwdArgs a) {
   __syncthreads();
   red[tid] = tid < M ? rs : 0.f;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
     __syncthreads();
   }
   if (tid == 0) a.rmax[bh] = red[0];
 }
 
-// grid BH, block 256, dynamic LDS bwd_mm_lds_bytes<M>().
+// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M>().
 template <int M>
-__global__ __launch_bounds__(256) void k_bwd_mm2(BwdArgs a) {
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
+  constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int MM = M * M;
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -456,10 +468,10 @@ __global__ __launch_bounds__(256) void k_bwd_mm2(BwdArgs a) {
   }
   __syncthreads();
   if (add != 0.f)
-    for (int r = tid; r < M; r += 256) dA[r * M + jstar] += add;
+    for (int r = tid; r < M; r += NT) dA[r * M + jstar] += add;
   __syncthreads();
   // dS_A = A (dA - rowsum(dA A)), one row per thread
-  for (int r = tid; r < M; r += 256) {
+  for (int r = tid; r < M; r += NT) {
     float s = 0.f;
     for (int j = 0; j < M; ++j) s += dA[r * M + j] * A[r * M + j];
     for (int j = 0; j < M; ++j) dSA[r * M + j] = A[r * M + j] * (dA[r * M + j] - s);
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm2(BwdArgs a) {
   bgemm<M, HD, M>(a.dQt + (size_t)bh * M * HD, dSA, false, a.kt + (size_t)bh * M * HD, false, 1.f, 0.f, La, Lb);
   bgemm<M, HD, M>(a.dKt + (size_t)bh * M * HD, dSA, true, a.qt + (size_t)bh * M * HD, false, 1.f, 1.f, La, Lb);
   // D_i = dBV_i . BV_i
-  for (int r = tid; r < M; r += 256) {
+  for (int r = tid; r < M; r += NT) {
     float s = 0.f;
     for (int c = 0; c < HD; ++c)
       s += a.dBV[((size_t)bh * M + r) * HD + c] * a.BV[((size_t)bh * M + r) * HD + c];
@@ -493,9 +505,12 @@ struct BwdKeyLayout {
   static_assert(BYTES <= 160 * 1024, "k_bwd_key LDS");
 };
 
-// grid (nck, BH), block 256.
+constexpr int BWD_KEY_NT = 512;  // threads of k_bwd_key (8 waves)
+
+// grid (nck, BH), block BWD_KEY_NT.
 template <typename IO, int M>
-__global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
+__global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
+  constexpr int NT = BWD_KEY_NT, NWV = NT / 64;
   extern __shared__ __align__(16) float bw_lds[];
   using Ly = BwdKeyLayout<M>;
   constexpr int TM = M / 16, LDB = Ly::LDB;
@@ -517,7 +532,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
   float* const DS = bw_lds + Ly::OFF_DS;
   float* const ACC = bw_lds + Ly::OFF_ACC;
   float* const VAL = bw_lds + Ly::OFF_VAL;
-  for (int i = tid; i < M * HD; i += 256) {
+  for (int i = tid; i < M * HD; i += NT) {
     const int r = i / HD, c = i % HD;
     Qt[r * BWD_LD + c] = a.qt[(size_t)bh * M * HD + i];
     dBV[r * BWD_LD + c] = a.dBV[(size_t)bh * M * HD + i];
@@ -526,11 +541,22 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
   const float inv_l = 1.0f / (float)a.L;
   for (int gk = k0; gk < k1; gk += BWD_GK) {
     __syncthreads();  // staging done / previous step's reads done
-    for (int i = tid; i < BWD_GK * HD; i += 256) {
-      const int r = i / HD, c = i % HD, key = gk + r;
-      const bool in = key < k1;
-      Ks[r * BWD_LD + c] = in ? io_get(Kg + (size_t)key * HD + c) * a.s4 : 0.f;
-      Vs[r * BWD_LD + c] = in ? io_get(Vg + (size_t)key * HD + c) : 0.f;
+    if (tid < BWD_GK * (HD / 8)) {
+      // one 8-element chunk of K and of V per thread
+      const int r = tid / (HD / 8), c = 8 * (tid % (HD / 8)), key = gk + r;
+      float xk[8], xv[8];
+      if (key < k1) {
+        IOTraits<IO>::load8(Kg + (size_t)key * HD + c, xk);
+        IOTraits<IO>::load8(Vg + (size_t)key * HD + c, xv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xk[e] = xv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Ks[r * BWD_LD + c + e] = xk[e] * a.s4;
+        Vs[r * BWD_LD + c + e] = xv[e];
+      }
     }
     if (tid < BWD_GK) {
       const int key = gk + tid;
@@ -538,7 +564,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
     }
     __syncthreads();
     // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
-    for (int t = wave; t < TM * (BWD_GK / 16); t += 4) {
+    for (int t = wave; t < TM * (BWD_GK / 16); t += NWV) {
       const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
       const f32x4 s = mm16<HD>(Qt + 16 * it * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD,
                                f32x4{0.f, 0.f, 0.f, 0.f});
@@ -555,7 +581,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
     }
     __syncthreads();
     // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[seg] / L): C(key, channel)
-    for (int t = wave; t < 2 * (BWD_GK / 16) * 4; t += 4) {
+    for (int t = wave; t < 2 * (BWD_GK / 16) * 4; t += NWV) {
       const bool isk = t >= (BWD_GK / 16) * 4;
       const int tt = t % ((BWD_GK / 16) * 4), kt = tt >> 2, ct = tt & 3;
       const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, BWD_LD, 1,
@@ -575,7 +601,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
       }
     }
     // dQt_B += dS Ks: C(landmark, channel), summed over the step's keys
-    for (int t = wave; t < TM * 4; t += 4) {
+    for (int t = wave; t < TM * 4; t += NWV) {
       const int it = t >> 2, ct = t & 3;
       const f32x4 c = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
       float* acc = ACC + (16 * it + 4 * g) * BWD_LD + 16 * ct + c16;
@@ -585,18 +611,17 @@ __global__ __launch_bounds__(256) void k_bwd_key(BwdArgs a) {
   }
   __syncthreads();
   float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * HD;
-  for (int i = tid; i < M * HD; i += 256) pq[i] = ACC[(i / HD) * BWD_LD + i % HD];
+  for (int i = tid; i < M * HD; i += NT) pq[i] = ACC[(i / HD) * BWD_LD + i % HD];
 }
 
-// dQt = dQt_A + sum of the key-chunk partials.  grid BH, block 256.
+// dQt = dQt_A + sum of the key-chunk partials (in chunk order).
+// grid (M * 64 / 256, BH), block 256: one element per thread.
 template <int M>
 __global__ __launch_bounds__(256) void k_bwd_qt(BwdArgs a) {
-  const int bh = blockIdx.x;
-  for (int i = threadIdx.x; i < M * HD; i += 256) {
-    float s = a.dQt[(size_t)bh * M * HD + i];
-    for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * HD + i];
-    a.dQt[(size_t)bh * M * HD + i] = s;
-  }
+  const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  float s = a.dQt[(size_t)bh * M * HD + i];
+  for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * HD + i];
+  a.dQt[(size_t)bh * M * HD + i] = s;
 }
 
 // dq = d^-1/4 (dQs + dQt[segment] / L).  grid (ceil(n / 64), BH), block 256:
@@ -616,73 +641,130 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 
 // Convolution backward: dv_conv[t] = sum_j w[j] dout[t - j + K/2] and the
 // chunk's partial dconv_w[j] = sum_t,c dout[t][c] v[t + j - K/2][c].
-// grid (ncv, BH), block 256, windows of dout and v (tokens t0 - 32 ..
-// t0 + 160) in LDS.
+// grid (ncv, BH), block 256, float32 windows of dout and v (tokens t0 - 32
+// .. t0 + 160) in LDS.  Lanes own channels (conflict-free LDS, coalesced
+// stores); each thread slides a register window along the sequence, so one
+// LDS read feeds eight multiply-adds.
 constexpr int BWD_CVWIN = BWD_CV + 64;
-constexpr int BWD_CV_LDS = 4 * (2 * BWD_CVWIN * (HD + 1) + 4 * TAPS);
+constexpr int BWD_CVLD = HD + 1;
+constexpr int BWD_CV_LDS = 4 * (2 * BWD_CVWIN * BWD_CVLD + 72 * HD + TAPS);
 
 // dynamic LDS BWD_CV_LDS
 template <typename IO>
 __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   float* const dow = bw_lds;
-  float* const vw = dow + BWD_CVWIN * (HD + 1);
-  float(*wr)[TAPS] = reinterpret_cast<float(*)[TAPS]>(vw + BWD_CVWIN * (HD + 1));
+  float* const vw = dow + BWD_CVWIN * BWD_CVLD;
+  float* const part = vw + BWD_CVWIN * BWD_CVLD;  // [72][64]: per (tap, channel) sums
+  float* const wsh = part + 72 * HD;
   const int bh = blockIdx.y, h = bh % a.H, chunk = blockIdx.x, tid = threadIdx.x;
   const int t0 = chunk * BWD_CV, K = a.conv_k, half = K / 2;
+  const int c = tid & 63, q4 = tid >> 6;
   const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
   const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  const float* w = a.conv_w + (size_t)h * K;
-  for (int i = tid; i < BWD_CVWIN * HD; i += 256) {
-    const int r = i / HD, c = i % HD, t = t0 - HALO + r;
-    const bool in = t >= 0 && t < a.n;
-    dow[r * (HD + 1) + c] = in ? io_get(DO + (size_t)t * HD + c) : 0.f;
-    vw[r * (HD + 1) + c] = in ? io_get(V + (size_t)t * HD + c) : 0.f;
-  }
-  __syncthreads();
-  // dv_conv: (token, 16-channel quarter) items
-  for (int it = tid; it < BWD_CV * 4; it += 256) {
-    const int tl = it >> 2, c0 = 16 * (it & 3), t = t0 + tl;
-    if (t >= a.n) continue;
-    float s[16];
+  {
+    // 8-element chunks: every load of the window is issued before its stores
+    constexpr int NCH = BWD_CVWIN * (HD / 8), PER = NCH / 256;
+    static_assert(NCH % 256 == 0, "window chunks");
+    float xo[PER][8], xv[PER][8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + 256 * u, r = i / (HD / 8), cc = 8 * (i % (HD / 8)), t = t0 - HALO + r;
+      if (t >= 0 && t < a.n) {
+        IOTraits<IO>::load8(DO + (size_t)t * HD + cc, xo[u]);
+        IOTraits<IO>::load8(V + (size_t)t * HD + cc, xv[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xo[u][e] = xv[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + 256 * u, r = i / (HD / 8), cc = 8 * (i % (HD / 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dow[r * BWD_CVLD + cc + e] = xo[u][e];
+        vw[r * BWD_CVLD + cc + e] = xv[u][e];
+      }
+    }
+  }
+  if (tid < K) wsh[tid] = a.conv_w[(size_t)h * K + tid];
+  __syncthreads();
+  // dv_conv: tokens tb .. tb + 7 of channel c; window row of dout[t - j + half]
+  // is (t - t0) + 32 - j + half, so each tap step slides the window by one row
+  for (int tb = 8 * q4; tb < BWD_CV; tb += 32) {
+    float acc[8], win[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[u] = 0.f;
+      win[u] = dow[(tb + u + HALO + half) * BWD_CVLD + c];  // j = 0
+    }
     for (int j = 0; j < K; ++j) {
-      const float wj = w[j];
-      const float* row = dow + (tl + HALO - j + half) * (HD + 1) + c0;
+      const float wj = wsh[j];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] += wj * row[e];
+      for (int u = 0; u < 8; ++u) acc[u] += wj * win[u];
+      // next tap: rows shift down by one
+#pragma unroll
+      for (int u = 7; u > 0; --u) win[u] = win[u - 1];
+      win[0] = dow[max(0, tb + HALO + half - j - 1) * BWD_CVLD + c];  // row < 0 only after the last tap
     }
-    float* dst = a.dvc + ((size_t)bh * a.n + t) * HD + c0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dst[e] = s[e];
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + tb + u;
+      if (t < a.n) a.dvc[((size_t)bh * a.n + t) * HD + c] = acc[u];
+    }
   }
-  // partial dconv_w: (tap, 16-channel quarter) items, then the quarters in order
-  for (int it = tid; it < K * 4; it += 256) {
-    const int j = it >> 2, c0 = 16 * (it & 3);
-    float s = 0.f;
-    const int tn = min(BWD_CV, a.n - t0);
-    for (int tl = 0; tl < tn; ++tl) {
-      const float* o = dow + (tl + HALO) * (HD + 1) + c0;
-      const float* vv = vw + (tl + HALO + j - half) * (HD + 1) + c0;
+  // dconv_w: taps j0 .. j0 + 7 of channel c over the chunk's tokens; the v
+  // row of token t and tap j is (t - t0) + 32 + j - half
+  const int tn = min(BWD_CV, a.n - t0);
+  for (int j0 = 8 * q4; j0 < K; j0 += 32) {
+    float acc[8], win[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += o[e] * vv[e];
+    for (int u = 0; u < 8; ++u) {
+      acc[u] = 0.f;
+      win[u] = vw[min(BWD_CVWIN - 1, HALO + j0 + u - half) * BWD_CVLD + c];  // t = t0
     }
-    wr[it & 3][j] = s;
+    for (int tl = 0; tl < tn; ++tl) {
+      const float o = dow[(tl + HALO) * BWD_CVLD + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += o * win[u];
+#pragma unroll
+      for (int u = 0; u < 7; ++u) win[u] = win[u + 1];
+      // past the window only for taps >= K or after the last token (unused)
+      win[7] = vw[min(BWD_CVWIN - 1, tl + 1 + HALO + j0 + 7 - half) * BWD_CVLD + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < 72) part[(j0 + u) * HD + c] = acc[u];
   }
   __syncthreads();
-  if (tid < K) a.pconv[((size_t)bh * a.ncv + chunk) * K + tid] = ((wr[0][tid] + wr[1][tid]) + wr[2][tid]) + wr[3][tid];
+  if (tid < K) {
+    float sum = 0.f;
+    for (int cc = 0; cc < HD; ++cc) sum += part[tid * HD + cc];
+    a.pconv[((size_t)bh * a.ncv + chunk) * K + tid] = sum;
+  }
 }
 
-// dconv_w[h][j] = sum over batches and chunks (in order).  grid H, block 128.
-__global__ __launch_bounds__(128) void k_bwd_wsum(BwdArgs a) {
-  const int h = blockIdx.x, j = threadIdx.x, K = a.conv_k;
-  if (j >= K) return;
-  const int B = a.BH / a.H;
-  float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int ch = 0; ch < a.ncv; ++ch) s += a.pconv[((size_t)(b * a.H + h) * a.ncv + ch) * K + j];
-  a.dconv_w[(size_t)h * K + j] = s;
+// dconv_w[h][j] = sum over batches and chunks: 8 threads per tap each take
+// every 8th partial, then the 8 sums are added in order.  grid H, block 1024.
+__global__ __launch_bounds__(1024) void k_bwd_wsum(BwdArgs a) {
+  __shared__ float ps[8][TAPS];
+  const int h = blockIdx.x, K = a.conv_k, j = threadIdx.x >> 3, p = threadIdx.x & 7;
+  const int B = a.BH / a.H, cnt = B * a.ncv;
+  if (j < K) {
+    float s = 0.f;
+    for (int i = p; i < cnt; i += 8) {
+      const int b = i / a.ncv, ch = i % a.ncv;
+      s += a.pconv[((size_t)(b * a.H + h) * a.ncv + ch) * K + j];
+    }
+    ps[p][j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    float s = 0.f;
+    for (int q = 0; q < 8; ++q) s += ps[q][threadIdx.x];
+    a.dconv_w[(size_t)h * K + threadIdx.x] = s;
+  }
 }
 
 }  // namespace nys

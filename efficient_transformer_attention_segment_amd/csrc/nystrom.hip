@@ -887,16 +887,16 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
                  a));
   constexpr int ml = bwd_mm_lds_bytes<M>();
   HIP_TRY(allow_lds(k_bwd_mm1<M>, ml));
-  HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(256), (uint32_t)ml, st, a));
+  HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   HIP_TRY(allow_lds(k_bwd_mm2<M>, ml));
-  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M>, dim3(p.BH), dim3(256), (uint32_t)ml, st, a));
+  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   constexpr int kl = BwdKeyLayout<M>::BYTES;
   HIP_TRY(allow_lds(k_bwd_key<IO, M>, kl));
-  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M>, dim3(bp.nck, p.BH), dim3(256), (uint32_t)kl, st, a));
-  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M>, dim3(p.BH), dim3(256), 0, st, a));
+  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
+  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M>, dim3(M * HD / 256, p.BH), dim3(256), 0, st, a));
   HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
   if (conv_w != nullptr && dconv_w != nullptr)
-    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(128), 0, st, a));
+    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(1024), 0, st, a));
   return NYS_OK;
 }
 
