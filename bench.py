@@ -364,11 +364,16 @@ def _short(name: str) -> str:
 # index).  Counter passes each take one counter, on a short bench run.
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {O}/trace -o trace -- "
-             "python3 {R}/bench.py --workload {W} --steps 20 --warmup 5 --also '' --no-cpu-baseline",
+             "python3 {R}/bench.py --workload {W} --steps 20 --warmup 5 --also '' --no-cpu-baseline --no-probs "
+             "--no-module --no-backward",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {O}/fetch -o fetch -- "
-             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline",
+             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline --no-probs "
+             "--no-module --no-backward",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {O}/write -o write -- "
-             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline",
+             "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline --no-probs "
+             "--no-module --no-backward",
+    "trace_all": "rocprofv3 --kernel-trace --stats --output-format csv -d {O}/trace_all -o trace_all -- "
+                 "python3 {R}/bench.py --workload {W} --steps 10 --warmup 3 --also '' --no-cpu-baseline",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {O}/copy_fetch -o copy_fetch -- "
                   "python3 {R}/bench.py --copy-probe-mb 256",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {O}/copy_write -o copy_write -- "
@@ -383,6 +388,8 @@ def summarize(argv):
     commands W O          print the rocprofv3 command lines for workload W
     trace W O OUTDIR      kernel_trace_<workload>.txt: rocprofv3 per-kernel
                           statistics beside the bench's own event timings
+    trace_all W O OUTDIR  kernel_trace_all_<workload>.txt: the same for the
+                          bench with the weights, module and backward calls
     traffic W O OUTDIR    traffic_<kernel>_<workload>.txt for every library
                           kernel: FETCH_SIZE / WRITE_SIZE per launch, scaled
                           by a plain copy of known size
@@ -397,8 +404,8 @@ def summarize(argv):
         return
     outdir = argv[3]
     sha = source_sha()
-    if kind == "trace":
-        stats = _csv_rows(os.path.join(odir, "trace", "trace_kernel_stats.csv"))
+    if kind in ("trace", "trace_all"):
+        stats = _csv_rows(os.path.join(odir, kind, f"{kind}_kernel_stats.csv"))
         bench_line = None   # the same bench command, run without the profiler
         plain = os.path.join(odir, "plain_bench.json")
         if os.path.exists(plain):
@@ -407,24 +414,27 @@ def summarize(argv):
                     if line.startswith("{"):
                         bench_line = json.loads(line)
         lines = [f"# Kernel durations, {w.name}",
-                 f"# command (from /tmp, TMPDIR=/tmp): {cmds['trace']}",
-                 f"# summary: python3 bench.py --summarize trace {widx} {odir} {outdir}",
+                 f"# command (from /tmp, TMPDIR=/tmp): {cmds[kind]}",
+                 f"# summary: python3 bench.py --summarize {kind} {widx} {odir} {outdir}",
                  f"source_sha: {sha}", "",
                  f"# bench column: {cmds['trace'].split(' -- ', 1)[1]} run alone (no profiler), "
                  "kernel-stamped hipEvents",
                  "kernel | calls | rocprof avg_us | min_us | max_us | % of GPU time | bench hipEvent avg_us",
                  "---|---|---|---|---|---|---"]
+        if kind == "trace_all":
+            bench_line = None
+            lines = lines[:5] + ["kernel | calls | rocprof avg_us | min_us | max_us | % of GPU time", "---|---|---|---|---|---"]
         bk = (bench_line or {}).get("kernels", {})
         for r in stats:
             k = _short(r["Name"])
             ev = bk.get(k, {}).get("avg_us")
-            lines.append(f"{r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                         f"{float(r['Percentage']):.2f} | {'' if ev is None else f'{ev:.2f}'}")
+            row = (f"{r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}")
+            lines.append(row if kind == "trace_all" else row + f" | {'' if ev is None else f'{ev:.2f}'}")
         if bench_line:
             lines += ["", f"bench without the profiler: ms_per_step {bench_line['ms_per_step']}, "
                           f"step_us {bench_line.get('step_us')}, value {bench_line['value']} tokens/s"]
-        path = os.path.join(outdir, f"kernel_trace_{w.name}.txt")
+        path = os.path.join(outdir, f"kernel_trace_{'all_' if kind == 'trace_all' else ''}{w.name}.txt")
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(path)

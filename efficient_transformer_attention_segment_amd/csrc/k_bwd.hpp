@@ -767,4 +767,314 @@ __global__ __launch_bounds__(1024) void k_bwd_wsum(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Exact branch (m == n; page section 2.1): P = softmax(Qs Ks^T + mask),
+// out = P V (+ conv).  Flash-style backward in three passes:
+//   k_bwd_xstats  per query: lse (log2 units) and D_t = dout_t . (P V)_t;
+//   k_bwd_xq      per query tile: dS = P (dout V^T - D), dq = s4 dS Ks;
+//   k_bwd_xkv     per key tile: dv = P^T dout (+ dv_conv), dk = s4 dS^T Qs.
+// P is recomputed from the stored lse, so every pass streams the other
+// side in 32-row steps through LDS.
+
+struct XBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const uint8_t* key_mask;
+  const float* dvc;   // conv part of dv or null
+  float* lse;         // [BH][n]
+  float* Dt;          // [BH][n]
+  void* dq;
+  void* dk;
+  void* dv;
+  int n, H;
+  float s4;
+};
+
+constexpr int XB_T = 64;   // rows of the tile a workgroup owns (4 waves x 16)
+constexpr int XB_S = 32;   // rows of the streamed side per step
+
+// Stage rows [r0, r0 + XB_S) of X (scaled) into LDS [XB_S][BWD_LD]; rows past n are zero.
+template <typename IO>
+__device__ __forceinline__ void xb_stage(const IO* X, int r0, int n, float scale, float* dst) {
+  const int tid = threadIdx.x;
+  const int r = tid / (HD / 8), c = 8 * (tid % (HD / 8));  // 256 threads = 32 rows x 8 chunks
+  float x[8];
+  if (r0 + r < n) {
+    IOTraits<IO>::load8(X + (size_t)(r0 + r) * HD + c, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[r * BWD_LD + c + e] = x[e] * scale;
+}
+
+template <typename IO>
+__device__ __forceinline__ void xb_own(const IO* X, int r0, int n, float scale, float* dst) {
+  // the block's 64 own rows: 2 chunks per thread
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = threadIdx.x + 256 * u, r = i / (HD / 8), c = 8 * (i % (HD / 8));
+    float x[8];
+    if (r0 + r < n) {
+      IOTraits<IO>::load8(X + (size_t)(r0 + r) * HD + c, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[r * BWD_LD + c + e] = x[e] * scale;
+  }
+}
+
+constexpr int XB_LDS = 4 * (2 * XB_T * BWD_LD + 3 * XB_S * BWD_LD + XB_T * (XB_S + 4) + 2 * XB_S);
+
+// grid (ceil(n / 64), BH), block 256.  Online softmax over the keys for the
+// block's 64 queries: S (16 x 32 per wave and step) in C layout, o = sum
+// exp2(x - m) V accumulated on the matrix cores through an LDS P tile.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
+  extern __shared__ __align__(16) float xb_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / a.H, q0 = blockIdx.x * XB_T;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  float* const Qs = xb_lds;
+  float* const Ks = Qs + XB_T * BWD_LD;
+  float* const Vs = Ks + XB_S * BWD_LD;
+  float* const Pt = Vs + 2 * XB_S * BWD_LD;  // [64][XB_S + 4]
+  float* const val = Pt + XB_T * (XB_S + 4);
+  xb_own(Q, q0, a.n, a.s4, Qs);
+  // per lane: rows 4g + r of the wave's 16 queries (C layout of S), running
+  // max and sum over the lane's key columns; o accumulated per (query, channel)
+  float mrun[4], lsum[4];
+  f32x4 o[4];  // o[ct][r]: query 4g + r, channel 16 ct + c16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrun[r] = NEG_BIG;
+    lsum[r] = 0.f;
+    o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < a.n; k0 += XB_S) {
+    __syncthreads();
+    xb_stage(K, k0, a.n, a.s4, Ks);
+    xb_stage(V, k0, a.n, 1.f, Vs);
+    if (threadIdx.x < XB_S) {
+      const int key = k0 + threadIdx.x;
+      val[threadIdx.x] = (key < a.n && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    f32x4 s[2];
+    float tmax[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = mm16<HD>(Qs + 16 * wave * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      const bool ok = val[16 * kt + c16] != 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[kt][r] = ok ? s[kt][r] * LOG2E : -INFINITY;
+        tmax[r] = fmaxf(tmax[r], s[kt][r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mnew = fmaxf(mrun[r], max16(tmax[r]));
+      const float alpha = fast_exp2(mrun[r] - mnew);
+      mrun[r] = mnew;
+      lsum[r] *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) o[ct][r] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const float p = fast_exp2(s[kt][r] - mnew);
+        lsum[r] += p;
+        Pt[(16 * wave + 4 * g + r) * (XB_S + 4) + 16 * kt + c16] = p;
+      }
+    }
+    // o(query, channel) += P V: C(query 4g + r, channel 16 ct + c16) -> keep
+    // per lane the r-th query's 4 channel tiles: o[ct][r]
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 c = mm16<XB_S>(Pt + 16 * wave * (XB_S + 4), XB_S + 4, 1, Vs + 16 * ct, BWD_LD, 1,
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[ct][r] += c[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float l = sum16(lsum[r]);
+    const int tok = q0 + 16 * wave + 4 * g + r;
+    float dt = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const float ov = l > 0.f ? o[ct][r] / l : 0.f;
+      const float d = tok < a.n ? io_get(DO + (size_t)tok * HD + 16 * ct + c16) : 0.f;
+      dt += ov * d;
+    }
+    dt = sum16(dt);
+    if (c16 == 0 && tok < a.n) {
+      a.lse[(size_t)bh * a.n + tok] = l > 0.f ? mrun[r] + log2f(l) : INFINITY;
+      a.Dt[(size_t)bh * a.n + tok] = dt;
+    }
+  }
+}
+
+// grid (ceil(n / 64), BH), block 256: dq for the block's 64 queries.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_xq(XBwdArgs a) {
+  extern __shared__ __align__(16) float xb_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / a.H, q0 = blockIdx.x * XB_T;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  float* const Qs = xb_lds;
+  float* const DOs = Qs + XB_T * BWD_LD;
+  float* const Ks = DOs + XB_T * BWD_LD;
+  float* const Vs = Ks + XB_S * BWD_LD;
+  float* const DS = Vs + 2 * XB_S * BWD_LD;  // [64][XB_S + 4]
+  float* const val = DS + XB_T * (XB_S + 4);
+  xb_own(Q, q0, a.n, a.s4, Qs);
+  xb_own(DO, q0, a.n, 1.f, DOs);
+  float lse[4], dt[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = q0 + 16 * wave + 4 * g + r;
+    lse[r] = tok < a.n ? a.lse[(size_t)bh * a.n + tok] : INFINITY;
+    dt[r] = tok < a.n ? a.Dt[(size_t)bh * a.n + tok] : 0.f;
+  }
+  f32x4 dq[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) dq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.n; k0 += XB_S) {
+    __syncthreads();
+    xb_stage(K, k0, a.n, a.s4, Ks);
+    xb_stage(V, k0, a.n, 1.f, Vs);
+    if (threadIdx.x < XB_S) {
+      const int key = k0 + threadIdx.x;
+      val[threadIdx.x] = (key < a.n && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const f32x4 s = mm16<HD>(Qs + 16 * wave * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD,
+                               f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 dp = mm16<HD>(DOs + 16 * wave * BWD_LD, BWD_LD, 1, Vs + 16 * kt * BWD_LD, 1, BWD_LD,
+                                f32x4{0.f, 0.f, 0.f, 0.f});
+      const bool ok = val[16 * kt + c16] != 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = ok ? exp2f(s[r] * LOG2E - lse[r]) : 0.f;
+        DS[(16 * wave + 4 * g + r) * (XB_S + 4) + 16 * kt + c16] = p * (dp[r] - dt[r]);
+      }
+    }
+    // dq += dS Ks (the wave's own 16 rows)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      dq[ct] = mm16<XB_S>(DS + 16 * wave * (XB_S + 4), XB_S + 4, 1, Ks + 16 * ct, BWD_LD, 1, dq[ct]);
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = q0 + 16 * wave + 4 * g + r;
+      if (tok < a.n) io_put(reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * HD + 16 * ct + c16, a.s4 * dq[ct][r]);
+    }
+}
+
+// grid (ceil(n / 64), BH), block 256: dk and dv for the block's 64 keys.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_xkv(XBwdArgs a) {
+  extern __shared__ __align__(16) float xb_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / a.H, k0 = blockIdx.x * XB_T;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  float* const Ks = xb_lds;
+  float* const Vs = Ks + XB_T * BWD_LD;
+  float* const Qs = Vs + XB_T * BWD_LD;
+  float* const DOs = Qs + XB_S * BWD_LD;
+  float* const Pt = DOs + 2 * XB_S * BWD_LD;  // [XB_S queries][64 keys + 4]: P, then dS
+  float* const st = Pt + XB_S * (XB_T + 4);   // lse, D of the step's queries
+  float* const dst = st + XB_S;
+  xb_own(K, k0, a.n, a.s4, Ks);
+  xb_own(V, k0, a.n, 1.f, Vs);
+  // validity of the wave's own keys (rows of the C tiles below)
+  bool ok[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int key = k0 + 16 * wave + 4 * g + r;
+    ok[r] = key < a.n && (mask == nullptr || mask[key] != 0);
+  }
+  f32x4 dk[4], dv[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) dk[ct] = dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t0 = 0; t0 < a.n; t0 += XB_S) {
+    __syncthreads();
+    xb_stage(Q, t0, a.n, a.s4, Qs);
+    xb_stage(DO, t0, a.n, 1.f, DOs);
+    if (threadIdx.x < XB_S) {
+      const int tok = t0 + threadIdx.x;
+      st[threadIdx.x] = tok < a.n ? a.lse[(size_t)bh * a.n + tok] : INFINITY;
+      dst[threadIdx.x] = tok < a.n ? a.Dt[(size_t)bh * a.n + tok] : 0.f;
+    }
+    __syncthreads();
+    // S^T (keys x queries): C(key 4g + r of the wave's 16, query 16 qt + c16)
+    f32x4 p[2], ds[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const f32x4 s = mm16<HD>(Ks + 16 * wave * BWD_LD, BWD_LD, 1, Qs + 16 * qt * BWD_LD, 1, BWD_LD,
+                               f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 dp = mm16<HD>(Vs + 16 * wave * BWD_LD, BWD_LD, 1, DOs + 16 * qt * BWD_LD, 1, BWD_LD,
+                                f32x4{0.f, 0.f, 0.f, 0.f});
+      const int qq = 16 * qt + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[qt][r] = ok[r] ? exp2f(s[r] * LOG2E - st[qq]) : 0.f;
+        ds[qt][r] = p[qt][r] * (dp[r] - dst[qq]);
+      }
+    }
+    // dv += P^T dout, dk += dS^T Qs over the step's 32 queries: the wave's own
+    // 16 keys as rows; P^T / dS^T go through the wave's own LDS columns
+    float* const myP = Pt;  // [query][key]: column 16 wave + 4 g + r
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          myP[(16 * qt + c16) * (XB_T + 4) + 16 * wave + 4 * g + r] = pass == 0 ? p[qt][r] : ds[qt][r];
+      // A(key i, query k) = myP[k][16 wave + i]
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (pass == 0)
+          dv[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, DOs + 16 * ct, BWD_LD, 1, dv[ct]);
+        else
+          dk[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, Qs + 16 * ct, BWD_LD, 1, dk[ct]);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + 16 * wave + 4 * g + r;
+      if (key >= a.n) continue;
+      const size_t o = ((size_t)bh * a.n + key) * HD + 16 * ct + c16;
+      io_put(reinterpret_cast<IO*>(a.dv) + o, dv[ct][r] + (a.dvc != nullptr ? a.dvc[o] : 0.f));
+      io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * dk[ct][r]);
+    }
+}
+
 }  // namespace nys

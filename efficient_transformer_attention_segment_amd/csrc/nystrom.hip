@@ -900,6 +900,69 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   return NYS_OK;
 }
 
+// Exact branch (m == n): the conv backward, then the three flash-style passes.
+template <typename IO>
+int launch_backward_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
+                          const float* conv_w, int conv_k, const void* dout, void* dq, void* dk, void* dv,
+                          float* dconv_w, hipStream_t st) {
+  const size_t BH = (size_t)B * H;
+  const int ncv = (n + BWD_CV - 1) / BWD_CV;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  take(ZERO_BYTES);
+  const size_t off_lse = take(BH * n * 4), off_dt = take(BH * n * 4);
+  const size_t off_dvc = conv_w ? take(BH * n * HD * 4) : 0, off_pconv = conv_w ? take(BH * ncv * conv_k * 4) : 0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace* w = nullptr;
+  int rc = get_workspace(st, o, &w);
+  if (rc != NYS_OK) return rc;
+  BwdArgs c{};
+  c.v = v;
+  c.dout = dout;
+  c.conv_w = conv_w;
+  c.conv_k = conv_k;
+  c.dvc = conv_w ? at<float>(w, off_dvc) : nullptr;
+  c.pconv = conv_w ? at<float>(w, off_pconv) : nullptr;
+  c.dconv_w = dconv_w;
+  c.n = n;
+  c.H = H;
+  c.BH = (int)BH;
+  c.ncv = ncv;
+  if (conv_w != nullptr) {
+    HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
+    HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)BWD_CV_LDS, st, c));
+  }
+  XBwdArgs x{};
+  x.q = q;
+  x.k = k;
+  x.v = v;
+  x.dout = dout;
+  x.key_mask = mask;
+  x.dvc = c.dvc;
+  x.lse = at<float>(w, off_lse);
+  x.Dt = at<float>(w, off_dt);
+  x.dq = dq;
+  x.dk = dk;
+  x.dv = dv;
+  x.n = n;
+  x.H = H;
+  x.s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  const dim3 grid((n + XB_T - 1) / XB_T, (unsigned)BH);
+  HIP_TRY(allow_lds(k_bwd_xstats<IO>, XB_LDS));
+  HIP_TRY(launch("k_bwd_xstats", k_bwd_xstats<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
+  HIP_TRY(allow_lds(k_bwd_xq<IO>, XB_LDS));
+  HIP_TRY(launch("k_bwd_xq", k_bwd_xq<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
+  HIP_TRY(allow_lds(k_bwd_xkv<IO>, XB_LDS));
+  HIP_TRY(launch("k_bwd_xkv", k_bwd_xkv<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
+  if (conv_w != nullptr && dconv_w != nullptr)
+    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(H), dim3(1024), 0, st, c));
+  return NYS_OK;
+}
+
 template <typename IO>
 int run_backward(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k,
                  int B, int H, int n, int d, int m, int n_iter, int init_option, const void* dout, void* dq, void* dk,
@@ -913,8 +976,7 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
   if (d != HD) return fail(NYS_ERR_UNSUPPORTED, "backward: d=%d (the backward kernels are built for d=64)", d);
-  if (m == n) return fail(NYS_ERR_UNSUPPORTED, "backward: the exact branch (m == n) has no backward kernels");
-  if (padded_m(m) > 128) return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to 128 landmarks)", m);
+  if (m != n && padded_m(m) > 128) return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to 128 landmarks)", m);
   const size_t bytes = (size_t)B * H * n * HD * sizeof(IO);
   const void* const ro[4] = {q, k, v, dout};
   void* const wr[3] = {dq, dk, dv};
@@ -927,6 +989,7 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
   }
   for (const void* ptr : {q, k, v, dout})
     if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(NYS_ERR_INVALID, "q, k, v, dout must be 16-byte aligned");
+  if (m == n) return launch_backward_exact<IO>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
   Plan p = make_plan(B, H, n, m, d);
   p.record = true;  // A is read back
   p.bwd = true;

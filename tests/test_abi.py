@@ -136,7 +136,7 @@ FAKE5 = ctypes.c_void_p(0x2100000)
     (dict(dk=FAKE3), -1),                     # dk is dq
     (dict(dv=ctypes.c_void_p(0x2100008)), -1),  # misaligned
     (dict(d=128), -2),                        # backward kernels are built for d = 64
-    (dict(m=256), -2),                        # exact branch (m == n)
+    (dict(d=32, m=256), -2),                  # exact branch (m == n) at d = 32
     (dict(m=160, n=640), -2),                 # more than 128 landmarks
 ])
 def test_backward_validation(lib, kw, code):

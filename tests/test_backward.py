@@ -33,7 +33,9 @@ def _dout(shape, seed, dtype):
     return round_bf16(d) if dtype == "bf16" else d
 
 
-def _check(name, x, dtype, m, n_iter, init, conv=True, seed=0):
+def _check(name, x, dtype, m, n_iter, init, conv=True, seed=0, zero_qk=False):
+    """zero_qk: dq and dk are exactly zero (a single key: the softmax is the
+    constant 1); they are then held to a small absolute bound instead."""
     import torch
 
     import efficient_transformer_attention_segment_amd as nys
@@ -51,6 +53,9 @@ def _check(name, x, dtype, m, n_iter, init, conv=True, seed=0):
     errs = []
     for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref[:3]):
         assert np.isfinite(g_).all(), f"{name}: non-finite {nm}"
+        if zero_qk and nm in ("dq", "dk"):
+            assert np.abs(r_).max() < 1e-12 and np.abs(g_).max() < 1e-3, f"{name}: {nm} not ~0"
+            continue
         errs.append((nm, rel_frob_floor(g_, r_)))
     if cw is not None:
         gw = dw.cpu().double().numpy()
@@ -85,6 +90,18 @@ def test_backward_conv_sizes_and_empty_row(dtype):
     for K in (1, 33):
         x = make_custom(2, 2, 256, 64, seed=995 + K, dtype=dtype, lengths=[256, 0], taps=K)
         _check(f"conv{K}-emptyrow", x, dtype, 64, 6, 0, seed=4)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n", [64, 200, 512, 1])
+def test_backward_exact_branch(dtype, n):
+    """m == n (the pages' default configuration takes this branch): the
+    softmax attention's gradients, with a partial mask, a batch row with no
+    kept key and the convolution."""
+    x = make_custom(2, 2, n, 64, seed=1000 + n, dtype=dtype, lengths=[max(1, n - n // 3), 0])
+    _check(f"exact-n{n}", x, dtype, n, 6, 0, seed=5, zero_qk=n == 1)
+    y = make_custom(1, 2, n, 64, seed=1001 + n, dtype=dtype, lengths=None)
+    _check(f"exact-n{n}-nomask-noconv", y, dtype, n, 6, 0, conv=False, seed=6, zero_qk=n == 1)
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
