@@ -429,6 +429,186 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
   if (tid == 0) a.rmax[bh] = red[0];
 }
 
+// Product on operands already in LDS (row strides lda, ldb; flat
+// pointers), C = alpha op(A) op(B) + beta C with C in LDS or global memory
+// (row stride ldc).  Starts with a barrier (operands written, C free).
+template <int R, int N, int K>
+__device__ void lgemm(float* C, int ldc, const float* La, int lda, bool ta, const float* Lb, int ldb, bool tb,
+                      float alpha, float beta) {
+  constexpr int NWV = BWD_MM_NT / 64, TR = R / 16, TN = N / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  __syncthreads();
+  const int ai = ta ? 1 : lda, ak = ta ? lda : 1;
+  const int bk = tb ? 1 : ldb, bj = tb ? ldb : 1;
+  for (int t = wave; t < TR * TN; t += NWV) {
+    const int it = t / TN, jt = t % TN;
+    const f32x4 c = mm16<K>(La + 16 * it * ai, ai, ak, Lb + 16 * jt * bj, bk, bj, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* p = C + (size_t)(16 * it + 4 * g + r) * ldc + 16 * jt + c16;
+      *p = beta == 0.f ? alpha * c[r] : alpha * c[r] + beta * *p;
+    }
+  }
+}
+
+// LDS image of a row-major M x Mc global matrix (row stride ld).
+__device__ __forceinline__ void lds_load(float* dst, int ld, const float* src, int M, int Mc) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < M * Mc; i += BWD_MM_NT) dst[(i / Mc) * ld + i % Mc] = src[i];
+}
+__device__ __forceinline__ void lds_store(float* dst, const float* src, int ld, int M, int Mc) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < M * Mc; i += BWD_MM_NT) dst[i] = src[(i / Mc) * ld + i % Mc];
+}
+
+constexpr int BWD_MM64_LDS = 4 * 9 * 64 * 68;
+
+// k_bwd_mm1 for 64 landmarks with the working set resident in LDS: A, G,
+// G', dP, dX and the step's Z_k, X_k, X_k^2, P_k (then T) as nine 64 x 64
+// float32 images (row stride 68); the history Z_k, X_k, X_k^2, P_k and the
+// accumulated dA go to the per-head scratch in global memory, as in
+// k_bwd_mm1, and the results are the same products in the same order.
+// grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* const sA = bw_lds;
+  float* sG = sA + SZ;
+  float* sGn = sG + SZ;
+  float* const sdP = sGn + SZ;
+  float* const sdX = sdP + SZ;
+  float* sZ = sdX + SZ;
+  float* const sX = sZ + SZ;
+  float* const sX2 = sX + SZ;
+  float* const sPT = sX2 + SZ;
+  const float* A = a.A + (size_t)bh * MM;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  auto Zk = [&](int k) { return S + (size_t)k * MM; };
+  auto Xk = [&](int k) { return S + (size_t)(a.n_iter + 1 + 3 * k) * MM; };
+  auto X2k = [&](int k) { return Xk(k) + MM; };
+  auto Pk = [&](int k) { return Xk(k) + 2 * MM; };
+  float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
+  float* const dW = a.dW + (size_t)bh * M * HD;
+  const float c = a.cscale[bh];
+
+  for (int i = tid; i < M * HD; i += NT) {
+    float sw = 0.f, sk = 0.f;
+    for (int ch = 0; ch < a.nct; ++ch) {
+      sw += a.pw[((size_t)bh * a.nct + ch) * M * HD + i];
+      sk += a.pk[((size_t)bh * a.nct + ch) * M * HD + i];
+    }
+    dW[i] = sw;
+    a.dKt[(size_t)bh * M * HD + i] = sk;
+  }
+  lds_load(sA, LD, A, M, M);
+  __syncthreads();
+  for (int i = tid; i < MM; i += NT) {
+    const float z = A[(i % M) * M + i / M] / c;
+    sZ[(i / M) * LD + i % M] = z;
+    Zk(0)[i] = z;
+    dA[i] = 0.f;
+  }
+  for (int k = 0; k < a.n_iter; ++k) {
+    lgemm<M, M, M>(sX, LD, sA, LD, false, sZ, LD, false, 1.f, 0.f);
+    lgemm<M, M, M>(sX2, LD, sX, LD, false, sX, LD, false, 1.f, 0.f);
+    lgemm<M, M, M>(sPT, LD, sX, LD, false, sX2, LD, false, -1.f, 0.f);
+    __syncthreads();
+    for (int i = tid; i < MM; i += NT) {
+      const int o = (i / M) * LD + i % M;
+      sPT[o] += (i / M == i % M ? 13.f : 0.f) - 15.f * sX[o] + 7.f * sX2[o];
+      Xk(k)[i] = sX[o];
+      X2k(k)[i] = sX2[o];
+      Pk(k)[i] = sPT[o];
+    }
+    lgemm<M, M, M>(sG, LD, sZ, LD, false, sPT, LD, false, 0.25f, 0.f);  // Z_{k+1} (G as the spare slot)
+    lds_store(Zk(k + 1), sG, LD, M, M);
+    float* const t = sZ;
+    sZ = sG;
+    sG = t;
+  }
+  // dZ_n = dW BV^T and dBV = Z_n^T dW, with dW and BV staged in dP and dX
+  lds_load(sdP, LD, dW, M, HD);
+  lds_load(sdX, LD, a.BV + (size_t)bh * M * HD, M, HD);
+  lgemm<M, M, HD>(sG, LD, sdP, LD, false, sdX, LD, true, 1.f, 0.f);
+  lgemm<M, HD, M>(a.dBV + (size_t)bh * M * HD, HD, sZ, LD, true, sdP, LD, false, 1.f, 0.f);
+  for (int k = a.n_iter - 1; k >= 0; --k) {
+    lds_load(sZ, LD, Zk(k), M, M);
+    lds_load(sX, LD, Xk(k), M, M);
+    lds_load(sX2, LD, X2k(k), M, M);
+    lds_load(sPT, LD, Pk(k), M, M);
+    lgemm<M, M, M>(sGn, LD, sG, LD, false, sPT, LD, true, 0.25f, 0.f);   // dZ_k = G P^T / 4
+    lgemm<M, M, M>(sdP, LD, sZ, LD, true, sG, LD, false, 0.25f, 0.f);    // dP = Z^T G / 4
+    __syncthreads();
+    for (int i = tid; i < MM; i += NT) {
+      const int o = (i / M) * LD + i % M;
+      sdX[o] = -15.f * sdP[o];
+    }
+    lgemm<M, M, M>(sdX, LD, sdP, LD, false, sX, LD, true, 7.f, 1.f);     // + 7 dP X^T
+    lgemm<M, M, M>(sdX, LD, sX, LD, true, sdP, LD, false, 7.f, 1.f);     // + 7 X^T dP
+    lgemm<M, M, M>(sdX, LD, sdP, LD, false, sX2, LD, true, -1.f, 1.f);   // - dP (X^2)^T
+    lgemm<M, M, M>(sPT, LD, sX, LD, true, sdP, LD, false, 1.f, 0.f);     // T = X^T dP
+    lgemm<M, M, M>(sdX, LD, sPT, LD, false, sX, LD, true, -1.f, 1.f);    // - X^T dP X^T
+    lgemm<M, M, M>(sdX, LD, sX2, LD, true, sdP, LD, false, -1.f, 1.f);   // - (X^2)^T dP
+    lgemm<M, M, M>(dA, M, sdX, LD, false, sZ, LD, true, 1.f, 1.f);       // dA += dX Z^T
+    lgemm<M, M, M>(sGn, LD, sA, LD, true, sdX, LD, false, 1.f, 1.f);     // dZ_k += A^T dX
+    float* const t = sG;
+    sG = sGn;
+    sGn = t;
+  }
+  __syncthreads();
+  // Z_0 = A^T / c: dA += G^T / c; dc = -sum(G A^T) / c^2; the arg-max column
+  float part = 0.f;
+  for (int i = tid; i < MM; i += NT) {
+    const int r = i / M, col = i % M;
+    const float gv = sG[col * LD + r];
+    dA[i] += gv / c;
+    part += gv * sA[r * LD + col];
+  }
+  float* const red = sX;  // free now
+  int* const redj = reinterpret_cast<int*>(sX2);
+  red[tid] = part;
+  __syncthreads();
+  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] += red[tid + s2];
+    __syncthreads();
+  }
+  const float dcv = -red[0] / (c * c);
+  __syncthreads();
+  float cs = -1.f, rs = 0.f;
+  int cj = 0;
+  if (tid < M) {
+    cs = 0.f;
+    for (int r = 0; r < M; ++r) cs += A[r * M + tid];
+    for (int j = 0; j < M; ++j) rs += A[tid * M + j];
+    cj = tid;
+  }
+  red[tid] = cs;
+  redj[tid] = cj;
+  __syncthreads();
+  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2 && (red[tid + s2] > red[tid] || (red[tid + s2] == red[tid] && redj[tid + s2] < redj[tid]))) {
+      red[tid] = red[tid + s2];
+      redj[tid] = redj[tid + s2];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.dc[bh] = dcv;
+    a.cmax[bh] = red[0];
+    a.cmaxj[bh] = redj[0];
+  }
+  __syncthreads();
+  red[tid] = tid < M ? rs : 0.f;
+  __syncthreads();
+  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] = fmaxf(red[tid], red[tid + s2]);
+    __syncthreads();
+  }
+  if (tid == 0) a.rmax[bh] = red[0];
+}
+
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M>().
 template <int M>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {

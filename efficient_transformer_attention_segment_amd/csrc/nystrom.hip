@@ -886,8 +886,13 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl, st,
                  a));
   constexpr int ml = bwd_mm_lds_bytes<M>();
-  HIP_TRY(allow_lds(k_bwd_mm1<M>, ml));
-  HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  if constexpr (M == 64) {
+    HIP_TRY(allow_lds(k_bwd_mm1_64, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
+  } else {
+    HIP_TRY(allow_lds(k_bwd_mm1<M>, ml));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  }
   HIP_TRY(allow_lds(k_bwd_mm2<M>, ml));
   HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   constexpr int kl = BwdKeyLayout<M>::BYTES;
