@@ -10,7 +10,9 @@
 // normalisers come from a forward pass without the output), then, per head
 // (d = 64, up to 128 landmarks, float32 arithmetic throughout):
 //
-//   k_bwd_conv  dv_conv = conv^T(dout) and partial sums of dconv_w;
+//   k_bwd_dvconv  dv_conv = conv^T(dout) (the forward convolution with the
+//               taps reversed, on the matrix cores);
+//   k_bwd_conv  partial sums of dconv_w;
 //   k_bwd_tok   per token: F, dF = dout W^T, D_t = sum_j F dF,
 //               dS = F (dF - D_t), dQs = dS Kt; per token chunk partial
 //               sums of dW = F^T dout and dKt = dS^T Qs;
@@ -36,6 +38,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "k_conv.hpp"
 
 namespace nys {
 
@@ -819,109 +822,135 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   for (int e = 0; e < 16; ++e) io_put(dq + e, a.s4 * (dqf[e] + dqt[e] * inv_l));
 }
 
-// Convolution backward: dv_conv[t] = sum_j w[j] dout[t - j + K/2] and the
-// chunk's partial dconv_w[j] = sum_t,c dout[t][c] v[t + j - K/2][c].
-// grid (ncv, BH), block 256, float32 windows of dout and v (tokens t0 - 32
-// .. t0 + 160) in LDS.  Lanes own channels (conflict-free LDS, coalesced
-// stores); each thread slides a register window along the sequence, so one
-// LDS read feeds eight multiply-adds.
-constexpr int BWD_CVWIN = BWD_CV + 64;
-constexpr int BWD_CVLD = HD + 1;
-constexpr int BWD_CV_LDS = 4 * (2 * BWD_CVWIN * BWD_CVLD + 72 * HD + TAPS);
+// dv_conv[t] = sum_j w[j] dout[t - j + K/2]: the forward's convolution of
+// dout with the taps reversed, on the matrix cores as three banded Toeplitz
+// products per 16-token tile (the window of dout staged in LDS, transposed,
+// bf16 hi/lo).  grid (ceil(n / 128), BH), block 256, dynamic LDS
+// BWD_DV_LDS.
+constexpr int BWD_DV_TOK = 128;
+constexpr int BWD_DV_WIN = BWD_DV_TOK + 80;
+constexpr int BWD_DV_LD = BWD_DV_WIN + 8;
+constexpr int BWD_DV_LDS = 2 * 2 * HD * BWD_DV_LD + 4 * TAPS;
 
-// dynamic LDS BWD_CV_LDS
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_dvconv(BwdArgs a) {
+  extern __shared__ __align__(16) __bf16 dv_lds[];
+  constexpr int NS = IOTraits<IO>::NS;
+  __bf16* const vh = dv_lds;
+  __bf16* const vl = vh + HD * BWD_DV_LD;
+  float* const wf = reinterpret_cast<float*>(vl + HD * BWD_DV_LD);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15;
+  const int bh = blockIdx.y, h = bh % a.H, t0 = blockIdx.x * BWD_DV_TOK, K = a.conv_k;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  stage_v_window<IO>(DO, HD, a.n, t0, BWD_DV_WIN, vh, vl, BWD_DV_LD);
+  if (threadIdx.x < K) wf[threadIdx.x] = a.conv_w[(size_t)h * K + K - 1 - threadIdx.x];
+  __syncthreads();
+  Frag2 tap[3];
+  conv_taps(wf, K, tap);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ts = t0 + 32 * wave + 16 * u;
+    if (ts >= a.n) continue;
+    f32x4 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    conv_tile<NS, false>(vh, vl, BWD_DV_LD, ts - t0, tap, oacc);
+    const int tok = ts + c16;
+    if (tok < a.n) store_row16<float, false>(a.dvc + ((size_t)bh * a.n + tok) * HD, oacc);
+  }
+}
+
+// The chunk's partial dconv_w[j] = sum_t,c dout[t][c] v[t + j - K/2][c], on
+// the matrix cores: per 16-token tile at ts, P = dout_tile V_win^T (16 x 96
+// positions ts - 32 .. ts + 63, split-bf16 products), whose entry (t, s)
+// belongs to tap j = s - 32 - t + K/2.  A lane's (column tile, row) slots map
+// to the same taps in every tile, so each lane sums its slots over the
+// workgroup's tiles in registers; the slots of each tap are then added in a
+// fixed order.  grid (ncv, BH), block 256, dynamic LDS BWD_CV_LDS: V window
+// rows t0 - 32 .. t0 + 192 row-major as bf16 hi / lo planes.
+constexpr int BWD_CVWIN = BWD_CV + 96;
+constexpr int BWD_CV_LDS = 2 * 2 * BWD_CVWIN * HD + 4 * (4 * 6 * 4 * 64);
+
 template <typename IO>
 __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
-  extern __shared__ __align__(16) float bw_lds[];
-  float* const dow = bw_lds;
-  float* const vw = dow + BWD_CVWIN * BWD_CVLD;
-  float* const part = vw + BWD_CVWIN * BWD_CVLD;  // [72][64]: per (tap, channel) sums
-  float* const wsh = part + 72 * HD;
-  const int bh = blockIdx.y, h = bh % a.H, chunk = blockIdx.x, tid = threadIdx.x;
-  const int t0 = chunk * BWD_CV, K = a.conv_k, half = K / 2;
-  const int c = tid & 63, q4 = tid >> 6;
+  extern __shared__ __align__(16) __bf16 cv_lds[];
+  constexpr int NS = IOTraits<IO>::NS;
+  __bf16* const vh = cv_lds;
+  __bf16* const vl = vh + BWD_CVWIN * HD;
+  float* const red = reinterpret_cast<float*>(vl + BWD_CVWIN * HD);  // [wave][st][r][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x, t0 = chunk * BWD_CV, K = a.conv_k, half = K / 2;
   const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
   const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  {
-    // 8-element chunks: every load of the window is issued before its stores
-    constexpr int NCH = BWD_CVWIN * (HD / 8), PER = NCH / 256;
-    static_assert(NCH % 256 == 0, "window chunks");
-    float xo[PER][8], xv[PER][8];
+  // V window, row-major, 16-byte chunks swizzled by row (swz)
+  for (int i = threadIdx.x; i < BWD_CVWIN * (HD / 8); i += 256) {
+    const int r = i / (HD / 8), cc = i % (HD / 8), t = t0 - HALO + r;
+    float x[8];
+    if (t >= 0 && t < a.n) {
+      IOTraits<IO>::load8(V + (size_t)t * HD + 8 * cc, x);
+    } else {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + 256 * u, r = i / (HD / 8), cc = 8 * (i % (HD / 8)), t = t0 - HALO + r;
-      if (t >= 0 && t < a.n) {
-        IOTraits<IO>::load8(DO + (size_t)t * HD + cc, xo[u]);
-        IOTraits<IO>::load8(V + (size_t)t * HD + cc, xv[u]);
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    const Frag2 f = make_frag<NS>(x);
+    *reinterpret_cast<bf16x8*>(vh + swz(r, cc)) = f.hi;
+    if constexpr (NS == 3) *reinterpret_cast<bf16x8*>(vl + swz(r, cc)) = f.lo;
+  }
+  __syncthreads();
+  f32x4 acc[6];
+#pragma unroll
+  for (int st = 0; st < 6; ++st) acc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ts = t0 + 32 * wave + 16 * u;  // tile start
+    if (ts >= a.n) continue;
+    const int tok = ts + c16;
+    Frag2 df[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float x[8];
+      if (tok < a.n) {
+        IOTraits<IO>::load8(DO + (size_t)tok * HD + 32 * ks + 8 * g, x);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xo[u][e] = xv[u][e] = 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      df[ks] = make_frag<NS>(x);
+    }
+    // P^T tiles: C(position 16 st + 4 g + r, token c16) = sum_c V[pos][c] dout[tok][c]
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+      const int row = ts - t0 + 16 * st + c16;  // window row of position ts - 32 + 16 st + c16
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag2 vf;
+        vf.hi = *reinterpret_cast<const bf16x8*>(vh + swz(row, 4 * ks + g));
+        if constexpr (NS == 3) vf.lo = *reinterpret_cast<const bf16x8*>(vl + swz(row, 4 * ks + g));
+        acc[st] = mma<NS>(vf, df[ks], acc[st]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + 256 * u, r = i / (HD / 8), cc = 8 * (i % (HD / 8));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dow[r * BWD_CVLD + cc + e] = xo[u][e];
-        vw[r * BWD_CVLD + cc + e] = xv[u][e];
-      }
-    }
   }
-  if (tid < K) wsh[tid] = a.conv_w[(size_t)h * K + tid];
+  // lane (c16 = token t, g) slot (st, r): position offset 16 st + 4 g + r - 32
+  // from the tile start, tap j = 16 st + 4 g + r - 32 - c16 + half
+#pragma unroll
+  for (int st = 0; st < 6; ++st)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * 6 + st) * 4 + r) * 64 + lane] = acc[st][r];
   __syncthreads();
-  // dv_conv: tokens tb .. tb + 7 of channel c; window row of dout[t - j + half]
-  // is (t - t0) + 32 - j + half, so each tap step slides the window by one row
-  for (int tb = 8 * q4; tb < BWD_CV; tb += 32) {
-    float acc[8], win[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc[u] = 0.f;
-      win[u] = dow[(tb + u + HALO + half) * BWD_CVLD + c];  // j = 0
-    }
-    for (int j = 0; j < K; ++j) {
-      const float wj = wsh[j];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += wj * win[u];
-      // next tap: rows shift down by one
-#pragma unroll
-      for (int u = 7; u > 0; --u) win[u] = win[u - 1];
-      win[0] = dow[max(0, tb + HALO + half - j - 1) * BWD_CVLD + c];  // row < 0 only after the last tap
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = t0 + tb + u;
-      if (t < a.n) a.dvc[((size_t)bh * a.n + t) * HD + c] = acc[u];
-    }
-  }
-  // dconv_w: taps j0 .. j0 + 7 of channel c over the chunk's tokens; the v
-  // row of token t and tap j is (t - t0) + 32 + j - half
-  const int tn = min(BWD_CV, a.n - t0);
-  for (int j0 = 8 * q4; j0 < K; j0 += 32) {
-    float acc[8], win[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc[u] = 0.f;
-      win[u] = vw[min(BWD_CVWIN - 1, HALO + j0 + u - half) * BWD_CVLD + c];  // t = t0
-    }
-    for (int tl = 0; tl < tn; ++tl) {
-      const float o = dow[(tl + HALO) * BWD_CVLD + c];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += o * win[u];
-#pragma unroll
-      for (int u = 0; u < 7; ++u) win[u] = win[u + 1];
-      // past the window only for taps >= K or after the last token (unused)
-      win[7] = vw[min(BWD_CVWIN - 1, tl + 1 + HALO + j0 + 7 - half) * BWD_CVLD + c];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j0 + u < 72) part[(j0 + u) * HD + c] = acc[u];
-  }
-  __syncthreads();
-  if (tid < K) {
+  if (threadIdx.x < K) {
+    const int j = threadIdx.x;
     float sum = 0.f;
-    for (int cc = 0; cc < HD; ++cc) sum += part[tid * HD + cc];
-    a.pconv[((size_t)bh * a.ncv + chunk) * K + tid] = sum;
+    // slot (st, gg, r) holds tap j for token cc = 16 st + base, base = 4 gg + r - 32 + half - j:
+    // one column tile st per (gg, r)
+    for (int w = 0; w < 4; ++w)
+      for (int gg = 0; gg < 4; ++gg)
+        for (int r = 0; r < 4; ++r) {
+          const int base = 4 * gg + r - 32 + half - j;  // in [-96, 47]
+          const int st = (111 - base) / 16 - 6;           // ceil(-base / 16) for base > -112
+          const int cc = 16 * st + base;
+          if (st >= 0 && st < 6 && cc < 16) sum += red[((w * 6 + st) * 4 + r) * 64 + 16 * gg + cc];
+        }
+    a.pconv[((size_t)bh * a.ncv + chunk) * K + j] = sum;
   }
 }
 

@@ -878,8 +878,13 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.init_option = init_option;
   a.s4 = 1.0f / sqrtf(sqrtf((float)HD));
   if (conv_w != nullptr) {
-    HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
-    HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)BWD_CV_LDS, st, a));
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO>, BWD_DV_LDS));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
+                   (uint32_t)BWD_DV_LDS, st, a));
+    if (dconv_w != nullptr) {
+      HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)BWD_CV_LDS, st, a));
+    }
   }
   constexpr int tl = BwdTokLayout<M>::BYTES;
   HIP_TRY(allow_lds(k_bwd_tok<IO, M>, tl));
@@ -938,8 +943,13 @@ int launch_backward_exact(int B, int H, int n, const void* q, const void* k, con
   c.BH = (int)BH;
   c.ncv = ncv;
   if (conv_w != nullptr) {
-    HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
-    HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)BWD_CV_LDS, st, c));
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO>, BWD_DV_LDS));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO>, dim3((n + BWD_DV_TOK - 1) / BWD_DV_TOK, (unsigned)BH), dim3(256),
+                   (uint32_t)BWD_DV_LDS, st, c));
+    if (dconv_w != nullptr) {
+      HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)BWD_CV_LDS, st, c));
+    }
   }
   XBwdArgs x{};
   x.q = q;
