@@ -46,14 +46,24 @@ namespace nys {
 // a[i * ai + k * ak] and B(k, j) at b[k * bk + j * bj]: in step s lane
 // (c16, g) feeds A(c16, 4s + g) and B(4s + g, c16); C(4g + r, c16) ends in
 // element r.
+// The k steps alternate between four accumulators (summed at the end, in a
+// fixed order), so consecutive matrix-core operations do not wait on each
+// other's results.
 template <int K>
 __device__ __forceinline__ f32x4 mm16(const float* a, int ai, int ak, const float* b, int bk, int bj, f32x4 c) {
+  constexpr int NS = K / 4, NA = NS % 4 == 0 ? 4 : (NS % 2 == 0 ? 2 : 1);
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const float* pa = a + c16 * ai + g * ak;
   const float* pb = b + g * bk + c16 * bj;
-#pragma unroll 8
-  for (int s = 0; s < K / 4; ++s) c = mfma_f32(pa[4 * s * ak], pb[4 * s * bk], c);
-  return c;
+  f32x4 acc[NA];
+  acc[0] = c;
+#pragma unroll
+  for (int i = 1; i < NA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc[s % NA] = mfma_f32(pa[4 * s * ak], pb[4 * s * bk], acc[s % NA]);
+#pragma unroll
+  for (int i = 1; i < NA; ++i) acc[0] += acc[i];
+  return acc[0];
 }
 
 struct BwdArgs {
