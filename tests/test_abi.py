@@ -150,6 +150,27 @@ def test_backward_validation(lib, kw, code):
     assert lib.nystrom_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -1),
+    (dict(x=None), -1),
+    (dict(qkv=None), -1),
+    (dict(hidden=6), -1),                     # 24-byte rows: not 16-byte multiples
+    (dict(qkv=FAKE), -1),                     # qkv overlaps x
+    (dict(d=48), -2),                         # head size not built
+    (dict(m=48), -1),                         # n % m != 0 (n = 256)
+])
+def test_module_validation(lib, kw, code):
+    """nystrom_self_attention checks everything before the projection GEMM
+    is enqueued (x at FAKE, weights at FAKE2, qkv at FAKE3, out at FAKE4)."""
+    a = dict(dtype=0, x=FAKE, w=FAKE2, qkv=FAKE3, out=FAKE4, hidden=64, d=64, m=64)
+    a.update(kw)
+    H = 1
+    rc = lib.nystrom_self_attention(a["dtype"], a["x"], a["w"], NULL, NULL, NULL, 65, 1, 256, a["hidden"], H,
+                                    a["d"], a["m"], 6, 0, a["qkv"], a["out"], NULL)
+    assert rc == code
+    assert lib.nystrom_last_error().decode() != ""
+
+
 @pytest.mark.parametrize("fn", ["nystrom_attention", "nystrom_attention_bf16"])
 def test_landmarks_above_256_unsupported(lib, fn):
     assert call(lib, fn, n=600, m=300) == -2
