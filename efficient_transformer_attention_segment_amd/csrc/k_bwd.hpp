@@ -143,9 +143,12 @@ struct BwdTokLayout {
   static constexpr int OFF_DO = OFF_Q + GT * BWD_LD;
   static constexpr int OFF_F = OFF_DO + GT * BWD_LD;
   static constexpr int OFF_DS = OFF_F + GT * LDF;
+  // the dW / dKt accumulators: in registers (each wave owns fixed tiles) up
+  // to 64 landmarks, in LDS above
+  static constexpr bool ACC_REG = M <= 64;
   static constexpr int OFF_AW = OFF_DS + GT * LDF;
-  static constexpr int OFF_AK = OFF_AW + M * BWD_LD;
-  static constexpr int OFF_W = OFF_AK + M * BWD_LD;
+  static constexpr int OFF_AK = OFF_AW + (ACC_REG ? 0 : M * BWD_LD);
+  static constexpr int OFF_W = OFF_AK + (ACC_REG ? 0 : M * BWD_LD);
   // W is staged too where it fits (otherwise read from L2)
   static constexpr bool W_LDS = 4 * (OFF_W + M * BWD_LD) <= 160 * 1024;
   static constexpr int FLOATS = OFF_W + (W_LDS ? M * BWD_LD : 0);
@@ -178,10 +181,16 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
   constexpr int WLD = Ly::W_LDS ? BWD_LD : HD;
   for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
     Kt[(i / HD) * BWD_LD + i % HD] = a.kt[(size_t)bh * M * HD + i];
-    AW[(i / HD) * BWD_LD + i % HD] = 0.f;
-    AK[(i / HD) * BWD_LD + i % HD] = 0.f;
+    if constexpr (!Ly::ACC_REG) {
+      AW[(i / HD) * BWD_LD + i % HD] = 0.f;
+      AK[(i / HD) * BWD_LD + i % HD] = 0.f;
+    }
     if constexpr (Ly::W_LDS) Wl[(i / HD) * BWD_LD + i % HD] = Wg[i];
   }
+  constexpr int NACC = Ly::ACC_REG ? (2 * TM * 4 + NW - 1) / NW : 1;
+  f32x4 racc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   for (int gs = t0; gs < t1; gs += GT) {
     // ---- phase A: the wave's 16 tokens
@@ -254,23 +263,47 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
     }
     __syncthreads();
     // ---- phase B: dW += F^T dout and dKt += dS^T Qs over the group's tokens
-    for (int ti = wave; ti < 2 * TM * 4; ti += NW) {
-      const bool isk = ti >= TM * 4;
-      const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
-      const float* A0 = (isk ? DSg : Fg) + 16 * jt;
-      const float* B0 = (isk ? Qg : DOg) + 16 * ct;
-      const f32x4 c = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
-      float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * BWD_LD + 16 * ct + c16;
+    if constexpr (Ly::ACC_REG) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+      for (int j = 0; j < NACC; ++j) {
+        const int ti = wave + NW * j;
+        const bool isk = ti >= TM * 4;
+        const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+        const float* A0 = (isk ? DSg : Fg) + 16 * jt;
+        const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+        racc[j] = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, racc[j]);
+      }
+    } else {
+      for (int ti = wave; ti < 2 * TM * 4; ti += NW) {
+        const bool isk = ti >= TM * 4;
+        const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+        const float* A0 = (isk ? DSg : Fg) + 16 * jt;
+        const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+        const f32x4 c = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+        float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * BWD_LD + 16 * ct + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+      }
     }
     __syncthreads();
   }
   float* const pw = a.pw + ((size_t)bh * a.nct + chunk) * M * HD;
   float* const pk = a.pk + ((size_t)bh * a.nct + chunk) * M * HD;
-  for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
-    pw[i] = AW[(i / HD) * BWD_LD + i % HD];
-    pk[i] = AK[(i / HD) * BWD_LD + i % HD];
+  if constexpr (Ly::ACC_REG) {
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) {
+      const int ti = wave + NW * j;
+      const bool isk = ti >= TM * 4;
+      const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+      float* const dst = isk ? pk : pw;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * HD + 16 * ct + c16] = racc[j][r];
+    }
+  } else {
+    for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
+      pw[i] = AW[(i / HD) * BWD_LD + i % HD];
+      pk[i] = AK[(i / HD) * BWD_LD + i % HD];
+    }
   }
 }
 
@@ -691,8 +724,7 @@ struct BwdKeyLayout {
   static constexpr int OFF_V = OFF_KS + BWD_GK * BWD_LD;
   static constexpr int OFF_B = OFF_V + BWD_GK * BWD_LD;
   static constexpr int OFF_DS = OFF_B + M * LDB;
-  static constexpr int OFF_ACC = OFF_DS + M * LDB;
-  static constexpr int OFF_VAL = OFF_ACC + M * BWD_LD;
+  static constexpr int OFF_VAL = OFF_DS + M * LDB;
   static constexpr int FLOATS = OFF_VAL + BWD_GK;
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_key LDS");
@@ -723,14 +755,17 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   float* const Vs = bw_lds + Ly::OFF_V;
   float* const Bt = bw_lds + Ly::OFF_B;
   float* const DS = bw_lds + Ly::OFF_DS;
-  float* const ACC = bw_lds + Ly::OFF_ACC;
   float* const VAL = bw_lds + Ly::OFF_VAL;
   for (int i = tid; i < M * HD; i += NT) {
     const int r = i / HD, c = i % HD;
     Qt[r * BWD_LD + c] = a.qt[(size_t)bh * M * HD + i];
     dBV[r * BWD_LD + c] = a.dBV[(size_t)bh * M * HD + i];
-    ACC[r * BWD_LD + c] = 0.f;
   }
+  // dQt_B tiles (landmark tile, channel tile) owned by this wave: t = wave + NWV j
+  constexpr int NACC = (TM * 4 + NWV - 1) / NWV;
+  f32x4 acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float inv_l = 1.0f / (float)a.L;
   for (int gk = k0; gk < k1; gk += BWD_GK) {
     __syncthreads();  // staging done / previous step's reads done
@@ -794,17 +829,25 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
       }
     }
     // dQt_B += dS Ks: C(landmark, channel), summed over the step's keys
-    for (int t = wave; t < TM * 4; t += NWV) {
-      const int it = t >> 2, ct = t & 3;
-      const f32x4 c = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
-      float* acc = ACC + (16 * it + 4 * g) * BWD_LD + 16 * ct + c16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+    for (int j = 0; j < NACC; ++j) {
+      const int t = wave + NWV * j;
+      if (t < TM * 4) {
+        const int it = t >> 2, ct = t & 3;
+        acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, BWD_LD, 1, acc[j]);
+      }
     }
   }
-  __syncthreads();
   float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * HD;
-  for (int i = tid; i < M * HD; i += NT) pq[i] = ACC[(i / HD) * BWD_LD + i % HD];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) {
+    const int t = wave + NWV * j;
+    if (t < TM * 4) {
+      const int it = t >> 2, ct = t & 3;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pq[(size_t)(16 * it + 4 * g + r) * HD + 16 * ct + c16] = acc[j][r];
+    }
+  }
 }
 
 // dQt = dQt_A + sum of the key-chunk partials (in chunk order).
