@@ -246,7 +246,7 @@ def attention_backward(q, k, v, dout, key_mask=None, conv_w=None, m=64, n_iter=6
     """Gradients of sum(out * dout) for the call attention(q, k, v, key_mask,
     conv_w, m, n_iter, init_option): returns (dq, dk, dv, dconv_w), the
     first three in q's dtype, dconv_w float32 [H, K] (None without conv_w).
-    Dense [B, H, n, 64] tensors."""
+    Dense [B, H, n, d] tensors, d in {32, 64, 128}."""
     import torch
     for t in (q, k, v, dout):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():

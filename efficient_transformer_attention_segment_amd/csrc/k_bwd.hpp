@@ -8,7 +8,8 @@
 // and its training use (gradient checkpointing, the Trainer).  The
 // intermediates are recomputed (landmarks, A, Z, B V, W and B's row
 // normalisers come from a forward pass without the output), then, per head
-// (d = 64, up to 128 landmarks, float32 arithmetic throughout):
+// (head size d = 32 or 64 with up to 128 landmarks, d = 128 with up to 64;
+// float32 arithmetic throughout):
 //
 //   k_bwd_dvconv  dv_conv = conv^T(dout) (the forward convolution with the
 //               taps reversed, on the matrix cores);
@@ -74,28 +75,28 @@ struct BwdArgs {
   const uint8_t* key_mask;  // [B][n] or null
   const float* conv_w;      // [H][conv_k] or null
   int conv_k;
-  const float* qt;          // [BH][M][64] (carry d^-1/4)
+  const float* qt;          // [BH][M][d] (carry d^-1/4)
   const float* kt;
   const float* A;           // [BH][M][M]
-  const float* BV;          // [BH][M][64]
-  const float* W;           // [BH][M][64]
+  const float* BV;          // [BH][M][d]
+  const float* W;           // [BH][M][d]
   const float* lse;         // [BH][M], log2 units
   const float* cscale;      // [BH]
-  float* dqf;               // [BH][n][64]: dQs through F
-  float* pw;                // [BH][nct][M][64]: partial dW
-  float* pk;                // [BH][nct][M][64]: partial dKt through F
-  float* pq;                // [BH][nck][M][64]: partial dQt through B
+  float* dqf;               // [BH][n][d]: dQs through F
+  float* pw;                // [BH][nct][M][d]: partial dW
+  float* pk;                // [BH][nct][M][d]: partial dKt through F
+  float* pq;                // [BH][nck][M][d]: partial dQt through B
   float* mm;                // [BH][mm_mats][M][M]: pseudo-inverse backward scratch
-  float* dW;                // [BH][M][64]
-  float* dBV;               // [BH][M][64]
-  float* dQt;               // [BH][M][64]: dQt through A, then the total
-  float* dKt;               // [BH][M][64]: total
+  float* dW;                // [BH][M][d]
+  float* dBV;               // [BH][M][d]
+  float* dQt;               // [BH][M][d]: dQt through A, then the total
+  float* dKt;               // [BH][M][d]: total
   float* Dv;                // [BH][M]: dBV_i . BV_i
   float* dc;                // [BH]: gradient reaching c
   float* cmax;              // [BH]: maximum column sum of A
   int* cmaxj;               // [BH]: its column
   float* rmax;              // [BH]: maximum row sum of A
-  float* dvc;               // [BH][n][64]: conv part of dv, or null
+  float* dvc;               // [BH][n][d]: conv part of dv, or null
   float* pconv;             // [BH][ncv][conv_k]
   void* dq;
   void* dk;
@@ -105,7 +106,8 @@ struct BwdArgs {
   float s4;                 // d^-1/4
 };
 
-constexpr int BWD_LD = HD + 4;   // float row stride of [.][64] tiles in LDS
+// Kernels are templated on the head size D (32, 64 or 128); [.][D] float
+// tiles in LDS have row stride D + 4.
 constexpr int BWD_CT = 256;      // tokens per k_bwd_tok workgroup
 constexpr int BWD_CK = 256;      // keys per k_bwd_key workgroup
 constexpr int BWD_GK = 32;       // keys per step of k_bwd_key
@@ -135,40 +137,40 @@ __device__ __forceinline__ void io_put(IO* p, float x) {
 }
 
 // ---------------------------------------------------------------------------
-template <int M>
+template <int M, int D>
 struct BwdTokLayout {
-  static constexpr int NW = bwd_tok_waves<M>(), GT = 16 * NW, LDF = M + 4;
+  static constexpr int NW = bwd_tok_waves<M>(), GT = 16 * NW, LDF = M + 4, LD = D + 4;
   static constexpr int OFF_KT = 0;
-  static constexpr int OFF_Q = OFF_KT + M * BWD_LD;
-  static constexpr int OFF_DO = OFF_Q + GT * BWD_LD;
-  static constexpr int OFF_F = OFF_DO + GT * BWD_LD;
+  static constexpr int OFF_Q = OFF_KT + M * LD;
+  static constexpr int OFF_DO = OFF_Q + GT * LD;
+  static constexpr int OFF_F = OFF_DO + GT * LD;
   static constexpr int OFF_DS = OFF_F + GT * LDF;
   // the dW / dKt accumulators: in registers (each wave owns fixed tiles) up
   // to 64 landmarks, in LDS above
   static constexpr bool ACC_REG = M <= 64;
   static constexpr int OFF_AW = OFF_DS + GT * LDF;
-  static constexpr int OFF_AK = OFF_AW + (ACC_REG ? 0 : M * BWD_LD);
-  static constexpr int OFF_W = OFF_AK + (ACC_REG ? 0 : M * BWD_LD);
+  static constexpr int OFF_AK = OFF_AW + (ACC_REG ? 0 : M * LD);
+  static constexpr int OFF_W = OFF_AK + (ACC_REG ? 0 : M * LD);
   // W is staged too where it fits (otherwise read from L2)
-  static constexpr bool W_LDS = 4 * (OFF_W + M * BWD_LD) <= 160 * 1024;
-  static constexpr int FLOATS = OFF_W + (W_LDS ? M * BWD_LD : 0);
+  static constexpr bool W_LDS = 4 * (OFF_W + M * LD) <= 160 * 1024;
+  static constexpr int FLOATS = OFF_W + (W_LDS ? M * LD : 0);
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_tok LDS");
 };
 
 // grid (nct, BH), block 64 NW.
-template <typename IO, int M>
+template <typename IO, int M, int D>
 __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
-  using Ly = BwdTokLayout<M>;
-  constexpr int NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, TM = M / 16;
+  using Ly = BwdTokLayout<M, D>;
+  constexpr int NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, LD = Ly::LD, TM = M / 16, CT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int t0 = chunk * BWD_CT, t1 = min(a.n, t0 + BWD_CT);
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
-  const float* Wg = a.W + (size_t)bh * M * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
+  const float* Wg = a.W + (size_t)bh * M * D;
   float* const Kt = bw_lds + Ly::OFF_KT;
   float* const Qg = bw_lds + Ly::OFF_Q;
   float* const DOg = bw_lds + Ly::OFF_DO;
@@ -178,33 +180,34 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
   float* const AK = bw_lds + Ly::OFF_AK;
   float* const Wl = bw_lds + Ly::OFF_W;
   const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
-  constexpr int WLD = Ly::W_LDS ? BWD_LD : HD;
-  for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
-    Kt[(i / HD) * BWD_LD + i % HD] = a.kt[(size_t)bh * M * HD + i];
+  constexpr int WLD = Ly::W_LDS ? LD : D;
+  for (int i = threadIdx.x; i < M * D; i += 64 * NW) {
+    Kt[(i / D) * LD + i % D] = a.kt[(size_t)bh * M * D + i];
     if constexpr (!Ly::ACC_REG) {
-      AW[(i / HD) * BWD_LD + i % HD] = 0.f;
-      AK[(i / HD) * BWD_LD + i % HD] = 0.f;
+      AW[(i / D) * LD + i % D] = 0.f;
+      AK[(i / D) * LD + i % D] = 0.f;
     }
-    if constexpr (Ly::W_LDS) Wl[(i / HD) * BWD_LD + i % HD] = Wg[i];
+    if constexpr (Ly::W_LDS) Wl[(i / D) * LD + i % D] = Wg[i];
   }
-  constexpr int NACC = Ly::ACC_REG ? (2 * TM * 4 + NW - 1) / NW : 1;
+  constexpr int NACC = Ly::ACC_REG ? 2 * TM * CT / NW : 1;
+  static_assert(!Ly::ACC_REG || (2 * TM * CT) % NW == 0, "every wave owns the same number of tiles");
   f32x4 racc[NACC];
 #pragma unroll
   for (int j = 0; j < NACC; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   for (int gs = t0; gs < t1; gs += GT) {
-    // ---- phase A: the wave's 16 tokens
+    // ---- phase A: the wave's 16 tokens (4 lanes per token, D / 4 channels each)
     const int tw = gs + 16 * wave;
     {
-      const int r = lane >> 2, c0 = 16 * (lane & 3), tok = tw + r;
-      float* qd = Qg + (16 * wave + r) * BWD_LD + c0;
-      float* od = DOg + (16 * wave + r) * BWD_LD + c0;
+      const int r = lane >> 2, c0 = (D / 4) * (lane & 3), tok = tw + r;
+      float* qd = Qg + (16 * wave + r) * LD + c0;
+      float* od = DOg + (16 * wave + r) * LD + c0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < D / 32; ++h) {
         float xq[8], xo[8];
         if (tok < t1) {
-          IOTraits<IO>::load8(Q + (size_t)tok * HD + c0 + 8 * h, xq);
-          IOTraits<IO>::load8(DO + (size_t)tok * HD + c0 + 8 * h, xo);
+          IOTraits<IO>::load8(Q + (size_t)tok * D + c0 + 8 * h, xq);
+          IOTraits<IO>::load8(DO + (size_t)tok * D + c0 + 8 * h, xo);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) xq[e] = xo[e] = 0.f;
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
     f32x4 f[TM], df[TM];
 #pragma unroll
     for (int jt = 0; jt < TM; ++jt) {
-      f[jt] = mm16<HD>(Qg + 16 * wave * BWD_LD, BWD_LD, 1, Kt + 16 * jt * BWD_LD, 1, BWD_LD, f32x4{0.f, 0.f, 0.f, 0.f});
-      df[jt] = mm16<HD>(DOg + 16 * wave * BWD_LD, BWD_LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+      f[jt] = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      df[jt] = mm16<D>(DOg + 16 * wave * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
       if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 #pragma unroll
@@ -251,58 +254,59 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
         DSg[row * LDF + 16 * jt + c16] = f[jt][r] * (df[jt][r] - dt);
       }
     }
-    // dQs = dS Kt (16 tokens x 64 channels), the wave's own rows
+    // dQs = dS Kt (16 tokens x D channels), the wave's own rows
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 c = mm16<M>(DSg + 16 * wave * LDF, LDF, 1, Kt + 16 * ct, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int ct = 0; ct < CT; ++ct) {
+      const f32x4 c = mm16<M>(DSg + 16 * wave * LDF, LDF, 1, Kt + 16 * ct, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tw + 4 * g + r;
-        if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * HD + 16 * ct + c16] = c[r];
+        if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * D + 16 * ct + c16] = c[r];
       }
     }
     __syncthreads();
-    // ---- phase B: dW += F^T dout and dKt += dS^T Qs over the group's tokens
+    // ---- phase B: dW += F^T dout and dKt += dS^T Qs over the group's tokens;
+    // tile ti = (landmark tile jt, channel tile ct), the dKt tiles after the dW tiles
     if constexpr (Ly::ACC_REG) {
 #pragma unroll
       for (int j = 0; j < NACC; ++j) {
         const int ti = wave + NW * j;
-        const bool isk = ti >= TM * 4;
-        const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+        const bool isk = ti >= TM * CT;
+        const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
         const float* A0 = (isk ? DSg : Fg) + 16 * jt;
         const float* B0 = (isk ? Qg : DOg) + 16 * ct;
-        racc[j] = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, racc[j]);
+        racc[j] = mm16<GT>(A0, 1, LDF, B0, LD, 1, racc[j]);
       }
     } else {
-      for (int ti = wave; ti < 2 * TM * 4; ti += NW) {
-        const bool isk = ti >= TM * 4;
-        const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+      for (int ti = wave; ti < 2 * TM * CT; ti += NW) {
+        const bool isk = ti >= TM * CT;
+        const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
         const float* A0 = (isk ? DSg : Fg) + 16 * jt;
         const float* B0 = (isk ? Qg : DOg) + 16 * ct;
-        const f32x4 c = mm16<GT>(A0, 1, LDF, B0, BWD_LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
-        float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * BWD_LD + 16 * ct + c16;
+        const f32x4 c = mm16<GT>(A0, 1, LDF, B0, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+        float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * LD + 16 * ct + c16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r * BWD_LD] += c[r];
+        for (int r = 0; r < 4; ++r) acc[r * LD] += c[r];
       }
     }
     __syncthreads();
   }
-  float* const pw = a.pw + ((size_t)bh * a.nct + chunk) * M * HD;
-  float* const pk = a.pk + ((size_t)bh * a.nct + chunk) * M * HD;
+  float* const pw = a.pw + ((size_t)bh * a.nct + chunk) * M * D;
+  float* const pk = a.pk + ((size_t)bh * a.nct + chunk) * M * D;
   if constexpr (Ly::ACC_REG) {
 #pragma unroll
     for (int j = 0; j < NACC; ++j) {
       const int ti = wave + NW * j;
-      const bool isk = ti >= TM * 4;
-      const int tt = ti % (TM * 4), jt = tt >> 2, ct = tt & 3;
+      const bool isk = ti >= TM * CT;
+      const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
       float* const dst = isk ? pk : pw;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * HD + 16 * ct + c16] = racc[j][r];
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * D + 16 * ct + c16] = racc[j][r];
     }
   } else {
-    for (int i = threadIdx.x; i < M * HD; i += 64 * NW) {
-      pw[i] = AW[(i / HD) * BWD_LD + i % HD];
-      pk[i] = AK[(i / HD) * BWD_LD + i % HD];
+    for (int i = threadIdx.x; i < M * D; i += 64 * NW) {
+      pw[i] = AW[(i / D) * LD + i % D];
+      pk[i] = AK[(i / D) * LD + i % D];
     }
   }
 }
@@ -340,25 +344,25 @@ __device__ void bgemm(float* C, const float* Ag, bool ta, const float* Bg, bool 
   }
 }
 
-// two staged operands of up to max(M, 64) x max(M, 64) floats (row stride + 4)
-template <int M>
+// two staged operands of up to max(M, D) x max(M, D) floats (row stride + 4)
+template <int M, int D>
 constexpr int bwd_mm_side() {
-  return M > HD ? M : HD;
+  return M > D ? M : D;
 }
-template <int M>
+template <int M, int D>
 constexpr int bwd_mm_lds_bytes() {
-  return 4 * 2 * bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+  return 4 * 2 * bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
 }
 
-// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M>().
-template <int M>
+// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
+template <int M, int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
   constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int MM = M * M;
   const int bh = blockIdx.x, tid = threadIdx.x;
   float* const La = bw_lds;
-  float* const Lb = bw_lds + bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+  float* const Lb = bw_lds + bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
   const float* A = a.A + (size_t)bh * MM;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
   auto Zk = [&](int k) { return S + (size_t)k * MM; };
@@ -371,18 +375,18 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
   float* const dX = G + 3 * MM;
   float* const T = G + 4 * MM;
   float* const dA = G + 5 * MM;
-  float* const dW = a.dW + (size_t)bh * M * HD;
+  float* const dW = a.dW + (size_t)bh * M * D;
   const float c = a.cscale[bh];
 
   // dW and dKt (F part) from the token-chunk partials, in chunk order
-  for (int i = tid; i < M * HD; i += NT) {
+  for (int i = tid; i < M * D; i += NT) {
     float sw = 0.f, sk = 0.f;
     for (int ch = 0; ch < a.nct; ++ch) {
-      sw += a.pw[((size_t)bh * a.nct + ch) * M * HD + i];
-      sk += a.pk[((size_t)bh * a.nct + ch) * M * HD + i];
+      sw += a.pw[((size_t)bh * a.nct + ch) * M * D + i];
+      sk += a.pk[((size_t)bh * a.nct + ch) * M * D + i];
     }
     dW[i] = sw;
-    a.dKt[(size_t)bh * M * HD + i] = sk;
+    a.dKt[(size_t)bh * M * D + i] = sk;
   }
   // the iteration again in float32: Z_0 = A^T / c, X = A Z, P = 13I - 15X +
   // 7X^2 - X^3, Z <- Z P / 4; dA starts at zero
@@ -400,8 +404,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
     bgemm<M, M, M>(Zk(k + 1), Zk(k), false, Pk(k), false, 0.25f, 0.f, La, Lb);
   }
   // dZ_n = dW BV^T, dBV = Z_n^T dW
-  bgemm<M, M, HD>(G, dW, false, a.BV + (size_t)bh * M * HD, true, 1.f, 0.f, La, Lb);
-  bgemm<M, HD, M>(a.dBV + (size_t)bh * M * HD, Zk(a.n_iter), true, dW, false, 1.f, 0.f, La, Lb);
+  bgemm<M, M, D>(G, dW, false, a.BV + (size_t)bh * M * D, true, 1.f, 0.f, La, Lb);
+  bgemm<M, D, M>(a.dBV + (size_t)bh * M * D, Zk(a.n_iter), true, dW, false, 1.f, 0.f, La, Lb);
   float* g = G;
   float* gn = Gn;
   for (int k = a.n_iter - 1; k >= 0; --k) {
@@ -516,6 +520,7 @@ constexpr int BWD_MM64_LDS = 4 * 9 * 64 * 68;
 // accumulated dA go to the per-head scratch in global memory, as in
 // k_bwd_mm1, and the results are the same products in the same order.
 // grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
+template <int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
@@ -536,17 +541,17 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   auto X2k = [&](int k) { return Xk(k) + MM; };
   auto Pk = [&](int k) { return Xk(k) + 2 * MM; };
   float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
-  float* const dW = a.dW + (size_t)bh * M * HD;
+  float* const dW = a.dW + (size_t)bh * M * D;
   const float c = a.cscale[bh];
 
-  for (int i = tid; i < M * HD; i += NT) {
+  for (int i = tid; i < M * D; i += NT) {
     float sw = 0.f, sk = 0.f;
     for (int ch = 0; ch < a.nct; ++ch) {
-      sw += a.pw[((size_t)bh * a.nct + ch) * M * HD + i];
-      sk += a.pk[((size_t)bh * a.nct + ch) * M * HD + i];
+      sw += a.pw[((size_t)bh * a.nct + ch) * M * D + i];
+      sk += a.pk[((size_t)bh * a.nct + ch) * M * D + i];
     }
     dW[i] = sw;
-    a.dKt[(size_t)bh * M * HD + i] = sk;
+    a.dKt[(size_t)bh * M * D + i] = sk;
   }
   lds_load(sA, LD, A, M, M);
   __syncthreads();
@@ -574,11 +579,17 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
     sZ = sG;
     sG = t;
   }
-  // dZ_n = dW BV^T and dBV = Z_n^T dW, with dW and BV staged in dP and dX
-  lds_load(sdP, LD, dW, M, HD);
-  lds_load(sdX, LD, a.BV + (size_t)bh * M * HD, M, HD);
-  lgemm<M, M, HD>(sG, LD, sdP, LD, false, sdX, LD, true, 1.f, 0.f);
-  lgemm<M, HD, M>(a.dBV + (size_t)bh * M * HD, HD, sZ, LD, true, sdP, LD, false, 1.f, 0.f);
+  // dZ_n = dW BV^T and dBV = Z_n^T dW, with dW and BV staged in the dP and
+  // dX slots (for D = 128, rows of D + 4 floats: dW across the dP and dX
+  // slots, BV across the X and X^2 slots, which the loop below reloads)
+  constexpr int LDW = D <= M ? LD : D + 4;
+  static_assert(M * LDW <= 2 * SZ, "dW and BV fit two slots");
+  float* const sW = sdP;
+  float* const sBV = D <= M ? sdX : sX;
+  lds_load(sW, LDW, dW, M, D);
+  lds_load(sBV, LDW, a.BV + (size_t)bh * M * D, M, D);
+  lgemm<M, M, D>(sG, LD, sW, LDW, false, sBV, LDW, true, 1.f, 0.f);
+  lgemm<M, D, M>(a.dBV + (size_t)bh * M * D, D, sZ, LD, true, sW, LDW, false, 1.f, 0.f);
   for (int k = a.n_iter - 1; k >= 0; --k) {
     lds_load(sZ, LD, Zk(k), M, M);
     lds_load(sX, LD, Xk(k), M, M);
@@ -655,15 +666,15 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   if (tid == 0) a.rmax[bh] = red[0];
 }
 
-// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M>().
-template <int M>
+// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
+template <int M, int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
   constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int MM = M * M;
   const int bh = blockIdx.x, tid = threadIdx.x;
   float* const La = bw_lds;
-  float* const Lb = bw_lds + bwd_mm_side<M>() * (bwd_mm_side<M>() + 4);
+  float* const Lb = bw_lds + bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
   const float* A = a.A + (size_t)bh * MM;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
   float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
@@ -703,26 +714,26 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
     for (int j = 0; j < M; ++j) dSA[r * M + j] = A[r * M + j] * (dA[r * M + j] - s);
   }
   // dQt_A = dS_A Kt; dKt += dS_A^T Qt
-  bgemm<M, HD, M>(a.dQt + (size_t)bh * M * HD, dSA, false, a.kt + (size_t)bh * M * HD, false, 1.f, 0.f, La, Lb);
-  bgemm<M, HD, M>(a.dKt + (size_t)bh * M * HD, dSA, true, a.qt + (size_t)bh * M * HD, false, 1.f, 1.f, La, Lb);
+  bgemm<M, D, M>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La, Lb);
+  bgemm<M, D, M>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La, Lb);
   // D_i = dBV_i . BV_i
   for (int r = tid; r < M; r += NT) {
     float s = 0.f;
-    for (int c = 0; c < HD; ++c)
-      s += a.dBV[((size_t)bh * M + r) * HD + c] * a.BV[((size_t)bh * M + r) * HD + c];
+    for (int c = 0; c < D; ++c)
+      s += a.dBV[((size_t)bh * M + r) * D + c] * a.BV[((size_t)bh * M + r) * D + c];
     a.Dv[(size_t)bh * M + r] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int M>
+template <int M, int D>
 struct BwdKeyLayout {
-  static constexpr int LDB = BWD_GK + 4;
+  static constexpr int LDB = BWD_GK + 4, LD = D + 4;
   static constexpr int OFF_QT = 0;
-  static constexpr int OFF_DBV = OFF_QT + M * BWD_LD;
-  static constexpr int OFF_KS = OFF_DBV + M * BWD_LD;
-  static constexpr int OFF_V = OFF_KS + BWD_GK * BWD_LD;
-  static constexpr int OFF_B = OFF_V + BWD_GK * BWD_LD;
+  static constexpr int OFF_DBV = OFF_QT + M * LD;
+  static constexpr int OFF_KS = OFF_DBV + M * LD;
+  static constexpr int OFF_V = OFF_KS + BWD_GK * LD;
+  static constexpr int OFF_B = OFF_V + BWD_GK * LD;
   static constexpr int OFF_DS = OFF_B + M * LDB;
   static constexpr int OFF_VAL = OFF_DS + M * LDB;
   static constexpr int FLOATS = OFF_VAL + BWD_GK;
@@ -733,22 +744,22 @@ struct BwdKeyLayout {
 constexpr int BWD_KEY_NT = 512;  // threads of k_bwd_key (8 waves)
 
 // grid (nck, BH), block BWD_KEY_NT.
-template <typename IO, int M>
+template <typename IO, int M, int D>
 __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   constexpr int NT = BWD_KEY_NT, NWV = NT / 64;
   extern __shared__ __align__(16) float bw_lds[];
-  using Ly = BwdKeyLayout<M>;
-  constexpr int TM = M / 16, LDB = Ly::LDB;
+  using Ly = BwdKeyLayout<M, D>;
+  constexpr int TM = M / 16, CT = D / 16, LDB = Ly::LDB, LD = Ly::LD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x, b = bh / a.H;
   const int k0 = chunk * BWD_CK, k1 = min(a.n, k0 + BWD_CK);
-  const IO* Kg = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* Vg = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
+  const IO* Kg = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
+  const IO* Vg = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   const float* lse = a.lse + (size_t)bh * M;
   const float* Dv = a.Dv + (size_t)bh * M;
-  const float* dKt = a.dKt + (size_t)bh * M * HD;
+  const float* dKt = a.dKt + (size_t)bh * M * D;
   float* const Qt = bw_lds + Ly::OFF_QT;
   float* const dBV = bw_lds + Ly::OFF_DBV;
   float* const Ks = bw_lds + Ly::OFF_KS;
@@ -756,34 +767,35 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   float* const Bt = bw_lds + Ly::OFF_B;
   float* const DS = bw_lds + Ly::OFF_DS;
   float* const VAL = bw_lds + Ly::OFF_VAL;
-  for (int i = tid; i < M * HD; i += NT) {
-    const int r = i / HD, c = i % HD;
-    Qt[r * BWD_LD + c] = a.qt[(size_t)bh * M * HD + i];
-    dBV[r * BWD_LD + c] = a.dBV[(size_t)bh * M * HD + i];
+  for (int i = tid; i < M * D; i += NT) {
+    const int r = i / D, c = i % D;
+    Qt[r * LD + c] = a.qt[(size_t)bh * M * D + i];
+    dBV[r * LD + c] = a.dBV[(size_t)bh * M * D + i];
   }
   // dQt_B tiles (landmark tile, channel tile) owned by this wave: t = wave + NWV j
-  constexpr int NACC = (TM * 4 + NWV - 1) / NWV;
+  constexpr int NACC = (TM * CT + NWV - 1) / NWV;
   f32x4 acc[NACC];
 #pragma unroll
   for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float inv_l = 1.0f / (float)a.L;
   for (int gk = k0; gk < k1; gk += BWD_GK) {
     __syncthreads();  // staging done / previous step's reads done
-    if (tid < BWD_GK * (HD / 8)) {
+    static_assert(BWD_GK * (D / 8) <= NT, "one chunk of K and of V per thread");
+    if (tid < BWD_GK * (D / 8)) {
       // one 8-element chunk of K and of V per thread
-      const int r = tid / (HD / 8), c = 8 * (tid % (HD / 8)), key = gk + r;
+      const int r = tid / (D / 8), c = 8 * (tid % (D / 8)), key = gk + r;
       float xk[8], xv[8];
       if (key < k1) {
-        IOTraits<IO>::load8(Kg + (size_t)key * HD + c, xk);
-        IOTraits<IO>::load8(Vg + (size_t)key * HD + c, xv);
+        IOTraits<IO>::load8(Kg + (size_t)key * D + c, xk);
+        IOTraits<IO>::load8(Vg + (size_t)key * D + c, xv);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xk[e] = xv[e] = 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        Ks[r * BWD_LD + c + e] = xk[e] * a.s4;
-        Vs[r * BWD_LD + c + e] = xv[e];
+        Ks[r * LD + c + e] = xk[e] * a.s4;
+        Vs[r * LD + c + e] = xv[e];
       }
     }
     if (tid < BWD_GK) {
@@ -794,9 +806,9 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
     // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
     for (int t = wave; t < TM * (BWD_GK / 16); t += NWV) {
       const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
-      const f32x4 s = mm16<HD>(Qt + 16 * it * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD,
+      const f32x4 s = mm16<D>(Qt + 16 * it * LD, LD, 1, Ks + 16 * kt * LD, 1, LD,
                                f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 db = mm16<HD>(dBV + 16 * it * BWD_LD, BWD_LD, 1, Vs + 16 * kt * BWD_LD, 1, BWD_LD,
+      const f32x4 db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD,
                                 f32x4{0.f, 0.f, 0.f, 0.f});
       const float val = VAL[16 * kt + c16];
 #pragma unroll
@@ -809,18 +821,18 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
     }
     __syncthreads();
     // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[seg] / L): C(key, channel)
-    for (int t = wave; t < 2 * (BWD_GK / 16) * 4; t += NWV) {
-      const bool isk = t >= (BWD_GK / 16) * 4;
-      const int tt = t % ((BWD_GK / 16) * 4), kt = tt >> 2, ct = tt & 3;
-      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, BWD_LD, 1,
+    for (int t = wave; t < 2 * (BWD_GK / 16) * CT; t += NWV) {
+      const bool isk = t >= (BWD_GK / 16) * CT;
+      const int tt = t % ((BWD_GK / 16) * CT), kt = tt / CT, ct = tt % CT;
+      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, LD, 1,
                               f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = gk + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
         if (key >= k1) continue;
-        const size_t o = ((size_t)bh * a.n + key) * HD + ch;
+        const size_t o = ((size_t)bh * a.n + key) * D + ch;
         if (isk) {
-          const float x = c[r] + dKt[(size_t)(key / a.L) * HD + ch] * inv_l;
+          const float x = c[r] + dKt[(size_t)(key / a.L) * D + ch] * inv_l;
           io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * x);
         } else {
           const float x = c[r] + (a.dvc != nullptr ? a.dvc[o] : 0.f);
@@ -832,70 +844,73 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NACC; ++j) {
       const int t = wave + NWV * j;
-      if (t < TM * 4) {
-        const int it = t >> 2, ct = t & 3;
-        acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, BWD_LD, 1, acc[j]);
+      if (t < TM * CT) {
+        const int it = t / CT, ct = t % CT;
+        acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, LD, 1, acc[j]);
       }
     }
   }
-  float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * HD;
+  float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * D;
 #pragma unroll
   for (int j = 0; j < NACC; ++j) {
     const int t = wave + NWV * j;
-    if (t < TM * 4) {
-      const int it = t >> 2, ct = t & 3;
+    if (t < TM * CT) {
+      const int it = t / CT, ct = t % CT;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pq[(size_t)(16 * it + 4 * g + r) * HD + 16 * ct + c16] = acc[j][r];
+      for (int r = 0; r < 4; ++r) pq[(size_t)(16 * it + 4 * g + r) * D + 16 * ct + c16] = acc[j][r];
     }
   }
 }
 
 // dQt = dQt_A + sum of the key-chunk partials (in chunk order).
-// grid (M * 64 / 256, BH), block 256: one element per thread.
-template <int M>
+// grid (M * D / 256, BH), block 256: one element per thread.
+template <int M, int D>
 __global__ __launch_bounds__(256) void k_bwd_qt(BwdArgs a) {
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
-  float s = a.dQt[(size_t)bh * M * HD + i];
-  for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * HD + i];
-  a.dQt[(size_t)bh * M * HD + i] = s;
+  float s = a.dQt[(size_t)bh * M * D + i];
+  for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * D + i];
+  a.dQt[(size_t)bh * M * D + i] = s;
 }
 
 // dq = d^-1/4 (dQs + dQt[segment] / L).  grid (ceil(n / 64), BH), block 256:
-// thread = (token, 16-channel quarter).
-template <typename IO, int M>
+// thread = (token, quarter of the D channels).
+template <typename IO, int M, int D>
 __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   const int bh = blockIdx.y;
-  const int tok = blockIdx.x * 64 + (threadIdx.x >> 2), c0 = 16 * (threadIdx.x & 3);
+  const int tok = blockIdx.x * 64 + (threadIdx.x >> 2), c0 = (D / 4) * (threadIdx.x & 3);
   if (tok >= a.n) return;
   const float inv_l = 1.0f / (float)a.L;
-  const float* dqf = a.dqf + ((size_t)bh * a.n + tok) * HD + c0;
-  const float* dqt = a.dQt + ((size_t)bh * M + tok / a.L) * HD + c0;
-  IO* const dq = reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * HD + c0;
+  const float* dqf = a.dqf + ((size_t)bh * a.n + tok) * D + c0;
+  const float* dqt = a.dQt + ((size_t)bh * M + tok / a.L) * D + c0;
+  IO* const dq = reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * D + c0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) io_put(dq + e, a.s4 * (dqf[e] + dqt[e] * inv_l));
+  for (int e = 0; e < D / 4; ++e) io_put(dq + e, a.s4 * (dqf[e] + dqt[e] * inv_l));
 }
 
 // dv_conv[t] = sum_j w[j] dout[t - j + K/2]: the forward's convolution of
 // dout with the taps reversed, on the matrix cores as three banded Toeplitz
 // products per 16-token tile (the window of dout staged in LDS, transposed,
 // bf16 hi/lo).  grid (ceil(n / 128), BH), block 256, dynamic LDS
-// BWD_DV_LDS.
+// bwd_dv_lds<D>().
 constexpr int BWD_DV_TOK = 128;
 constexpr int BWD_DV_WIN = BWD_DV_TOK + 80;
 constexpr int BWD_DV_LD = BWD_DV_WIN + 8;
-constexpr int BWD_DV_LDS = 2 * 2 * HD * BWD_DV_LD + 4 * TAPS;
+template <int D>
+constexpr int bwd_dv_lds() {
+  return 2 * 2 * D * BWD_DV_LD + 4 * TAPS;
+}
 
-template <typename IO>
+template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_bwd_dvconv(BwdArgs a) {
   extern __shared__ __align__(16) __bf16 dv_lds[];
   constexpr int NS = IOTraits<IO>::NS;
   __bf16* const vh = dv_lds;
-  __bf16* const vl = vh + HD * BWD_DV_LD;
-  float* const wf = reinterpret_cast<float*>(vl + HD * BWD_DV_LD);
+  __bf16* const vl = vh + D * BWD_DV_LD;
+  float* const wf = reinterpret_cast<float*>(vl + D * BWD_DV_LD);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15;
   const int bh = blockIdx.y, h = bh % a.H, t0 = blockIdx.x * BWD_DV_TOK, K = a.conv_k;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
-  stage_v_window<IO>(DO, HD, a.n, t0, BWD_DV_WIN, vh, vl, BWD_DV_LD);
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
+  stage_v_window<IO, D>(DO, D, a.n, t0, BWD_DV_WIN, vh, vl, BWD_DV_LD);
   if (threadIdx.x < K) wf[threadIdx.x] = a.conv_w[(size_t)h * K + K - 1 - threadIdx.x];
   __syncthreads();
   Frag2 tap[3];
@@ -904,12 +919,12 @@ __global__ __launch_bounds__(256) void k_bwd_dvconv(BwdArgs a) {
   for (int u = 0; u < 2; ++u) {
     const int ts = t0 + 32 * wave + 16 * u;
     if (ts >= a.n) continue;
-    f32x4 oacc[4];
+    f32x4 oacc[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    conv_tile<NS, false>(vh, vl, BWD_DV_LD, ts - t0, tap, oacc);
+    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    conv_tile<NS, false, D>(vh, vl, BWD_DV_LD, ts - t0, tap, oacc);
     const int tok = ts + c16;
-    if (tok < a.n) store_row16<float, false>(a.dvc + ((size_t)bh * a.n + tok) * HD, oacc);
+    if (tok < a.n) store_row16<float, false, D>(a.dvc + ((size_t)bh * a.n + tok) * D, oacc);
   }
 }
 
@@ -919,35 +934,44 @@ __global__ __launch_bounds__(256) void k_bwd_dvconv(BwdArgs a) {
 // belongs to tap j = s - 32 - t + K/2.  A lane's (column tile, row) slots map
 // to the same taps in every tile, so each lane sums its slots over the
 // workgroup's tiles in registers; the slots of each tap are then added in a
-// fixed order.  grid (ncv, BH), block 256, dynamic LDS BWD_CV_LDS: V window
-// rows t0 - 32 .. t0 + 192 row-major as bf16 hi / lo planes.
+// fixed order.  grid (ncv, BH), block 256, dynamic LDS bwd_cv_lds<D>(): V
+// window rows t0 - 32 .. t0 + 192 row-major as bf16 hi / lo planes, the
+// 16-byte chunks of a row XOR-swizzled by its low row bits (cv_swz).
 constexpr int BWD_CVWIN = BWD_CV + 96;
-constexpr int BWD_CV_LDS = 2 * 2 * BWD_CVWIN * HD + 4 * (4 * 6 * 4 * 64);
+template <int D>
+constexpr int bwd_cv_lds() {
+  return 2 * 2 * BWD_CVWIN * D + 4 * (4 * 6 * 4 * 64);
+}
+template <int D>
+__device__ __forceinline__ int cv_swz(int row, int chunk) {
+  constexpr int MASK = (D / 8 < 8 ? D / 8 : 8) - 1;
+  return row * D + 8 * (chunk ^ (row & MASK));
+}
 
-template <typename IO>
+template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
   extern __shared__ __align__(16) __bf16 cv_lds[];
   constexpr int NS = IOTraits<IO>::NS;
   __bf16* const vh = cv_lds;
-  __bf16* const vl = vh + BWD_CVWIN * HD;
-  float* const red = reinterpret_cast<float*>(vl + BWD_CVWIN * HD);  // [wave][st][r][lane]
+  __bf16* const vl = vh + BWD_CVWIN * D;
+  float* const red = reinterpret_cast<float*>(vl + BWD_CVWIN * D);  // [wave][st][r][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x, t0 = chunk * BWD_CV, K = a.conv_k, half = K / 2;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  // V window, row-major, 16-byte chunks swizzled by row (swz)
-  for (int i = threadIdx.x; i < BWD_CVWIN * (HD / 8); i += 256) {
-    const int r = i / (HD / 8), cc = i % (HD / 8), t = t0 - HALO + r;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
+  // V window, row-major, 16-byte chunks swizzled by row
+  for (int i = threadIdx.x; i < BWD_CVWIN * (D / 8); i += 256) {
+    const int r = i / (D / 8), cc = i % (D / 8), t = t0 - HALO + r;
     float x[8];
     if (t >= 0 && t < a.n) {
-      IOTraits<IO>::load8(V + (size_t)t * HD + 8 * cc, x);
+      IOTraits<IO>::load8(V + (size_t)t * D + 8 * cc, x);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
     const Frag2 f = make_frag<NS>(x);
-    *reinterpret_cast<bf16x8*>(vh + swz(r, cc)) = f.hi;
-    if constexpr (NS == 3) *reinterpret_cast<bf16x8*>(vl + swz(r, cc)) = f.lo;
+    *reinterpret_cast<bf16x8*>(vh + cv_swz<D>(r, cc)) = f.hi;
+    if constexpr (NS == 3) *reinterpret_cast<bf16x8*>(vl + cv_swz<D>(r, cc)) = f.lo;
   }
   __syncthreads();
   f32x4 acc[6];
@@ -958,12 +982,13 @@ __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
     const int ts = t0 + 32 * wave + 16 * u;  // tile start
     if (ts >= a.n) continue;
     const int tok = ts + c16;
-    Frag2 df[2];
+    constexpr int KS = D / 32;  // 32-channel steps of the products
+    Frag2 df[KS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       float x[8];
       if (tok < a.n) {
-        IOTraits<IO>::load8(DO + (size_t)tok * HD + 32 * ks + 8 * g, x);
+        IOTraits<IO>::load8(DO + (size_t)tok * D + 32 * ks + 8 * g, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -975,10 +1000,10 @@ __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
     for (int st = 0; st < 6; ++st) {
       const int row = ts - t0 + 16 * st + c16;  // window row of position ts - 32 + 16 st + c16
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         Frag2 vf;
-        vf.hi = *reinterpret_cast<const bf16x8*>(vh + swz(row, 4 * ks + g));
-        if constexpr (NS == 3) vf.lo = *reinterpret_cast<const bf16x8*>(vl + swz(row, 4 * ks + g));
+        vf.hi = *reinterpret_cast<const bf16x8*>(vh + cv_swz<D>(row, 4 * ks + g));
+        if constexpr (NS == 3) vf.lo = *reinterpret_cast<const bf16x8*>(vl + cv_swz<D>(row, 4 * ks + g));
         acc[st] = mma<NS>(vf, df[ks], acc[st]);
       }
     }
@@ -1057,75 +1082,78 @@ struct XBwdArgs {
 constexpr int XB_T = 64;   // rows of the tile a workgroup owns (4 waves x 16)
 constexpr int XB_S = 32;   // rows of the streamed side per step
 
-// Stage rows [r0, r0 + XB_S) of X (scaled) into LDS [XB_S][BWD_LD]; rows past n are zero.
-template <typename IO>
-__device__ __forceinline__ void xb_stage(const IO* X, int r0, int n, float scale, float* dst) {
-  const int tid = threadIdx.x;
-  const int r = tid / (HD / 8), c = 8 * (tid % (HD / 8));  // 256 threads = 32 rows x 8 chunks
-  float x[8];
-  if (r0 + r < n) {
-    IOTraits<IO>::load8(X + (size_t)(r0 + r) * HD + c, x);
-  } else {
+// Stage rows [r0, r0 + R) of X (scaled) into LDS [R][D + 4] with 256
+// threads, one 8-element chunk per thread and step; rows past n are zero.
+template <typename IO, int D, int R>
+__device__ __forceinline__ void xb_rows(const IO* X, int r0, int n, float scale, float* dst) {
+  constexpr int CPR = D / 8;
+  static_assert((R * CPR) % 256 == 0 || R * CPR < 256, "whole steps");
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[r * BWD_LD + c + e] = x[e] * scale;
-}
-
-template <typename IO>
-__device__ __forceinline__ void xb_own(const IO* X, int r0, int n, float scale, float* dst) {
-  // the block's 64 own rows: 2 chunks per thread
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = threadIdx.x + 256 * u, r = i / (HD / 8), c = 8 * (i % (HD / 8));
+  for (int u = 0; u < (R * CPR + 255) / 256; ++u) {
+    const int i = threadIdx.x + 256 * u, r = i / CPR, c = 8 * (i % CPR);
+    if (i >= R * CPR) break;
     float x[8];
     if (r0 + r < n) {
-      IOTraits<IO>::load8(X + (size_t)(r0 + r) * HD + c, x);
+      IOTraits<IO>::load8(X + (size_t)(r0 + r) * D + c, x);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[r * BWD_LD + c + e] = x[e] * scale;
+    for (int e = 0; e < 8; ++e) dst[r * (D + 4) + c + e] = x[e] * scale;
   }
 }
+// the streamed side's XB_S rows
+template <typename IO, int D>
+__device__ __forceinline__ void xb_stage(const IO* X, int r0, int n, float scale, float* dst) {
+  xb_rows<IO, D, XB_S>(X, r0, n, scale, dst);
+}
+// the block's XB_T own rows
+template <typename IO, int D>
+__device__ __forceinline__ void xb_own(const IO* X, int r0, int n, float scale, float* dst) {
+  xb_rows<IO, D, XB_T>(X, r0, n, scale, dst);
+}
 
-constexpr int XB_LDS = 4 * (2 * XB_T * BWD_LD + 3 * XB_S * BWD_LD + XB_T * (XB_S + 4) + 2 * XB_S);
+template <int D>
+constexpr int xb_lds_bytes() {
+  return 4 * (2 * XB_T * (D + 4) + 3 * XB_S * (D + 4) + XB_T * (XB_S + 4) + 2 * XB_S);
+}
 
 // grid (ceil(n / 64), BH), block 256.  Online softmax over the keys for the
 // block's 64 queries: S (16 x 32 per wave and step) in C layout, o = sum
 // exp2(x - m) V accumulated on the matrix cores through an LDS P tile.
-template <typename IO>
+template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
   extern __shared__ __align__(16) float xb_lds[];
+  constexpr int LD = D + 4, CT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / a.H, q0 = blockIdx.x * XB_T;
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   float* const Qs = xb_lds;
-  float* const Ks = Qs + XB_T * BWD_LD;
-  float* const Vs = Ks + XB_S * BWD_LD;
-  float* const Pt = Vs + 2 * XB_S * BWD_LD;  // [64][XB_S + 4]
+  float* const Ks = Qs + XB_T * LD;
+  float* const Vs = Ks + XB_S * LD;
+  float* const Pt = Vs + 2 * XB_S * LD;  // [64][XB_S + 4]
   float* const val = Pt + XB_T * (XB_S + 4);
-  xb_own(Q, q0, a.n, a.s4, Qs);
+  xb_own<IO, D>(Q, q0, a.n, a.s4, Qs);
   // per lane: rows 4g + r of the wave's 16 queries (C layout of S), running
   // max and sum over the lane's key columns; o accumulated per (query, channel)
   float mrun[4], lsum[4];
-  f32x4 o[4];  // o[ct][r]: query 4g + r, channel 16 ct + c16
+  f32x4 o[CT];  // o[ct][r]: query 4g + r, channel 16 ct + c16
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     mrun[r] = NEG_BIG;
     lsum[r] = 0.f;
-    o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < a.n; k0 += XB_S) {
     __syncthreads();
-    xb_stage(K, k0, a.n, a.s4, Ks);
-    xb_stage(V, k0, a.n, 1.f, Vs);
+    xb_stage<IO, D>(K, k0, a.n, a.s4, Ks);
+    xb_stage<IO, D>(V, k0, a.n, 1.f, Vs);
     if (threadIdx.x < XB_S) {
       const int key = k0 + threadIdx.x;
       val[threadIdx.x] = (key < a.n && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
@@ -1135,7 +1163,7 @@ __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
     float tmax[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = mm16<HD>(Qs + 16 * wave * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      s[kt] = mm16<D>(Qs + 16 * wave * LD, LD, 1, Ks + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
       const bool ok = val[16 * kt + c16] != 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1150,7 +1178,7 @@ __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
       mrun[r] = mnew;
       lsum[r] *= alpha;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) o[ct][r] *= alpha;
+      for (int ct = 0; ct < CT; ++ct) o[ct][r] *= alpha;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const float p = fast_exp2(s[kt][r] - mnew);
@@ -1159,10 +1187,10 @@ __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
       }
     }
     // o(query, channel) += P V: C(query 4g + r, channel 16 ct + c16) -> keep
-    // per lane the r-th query's 4 channel tiles: o[ct][r]
+    // per lane the r-th query's channel tiles: o[ct][r]
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 c = mm16<XB_S>(Pt + 16 * wave * (XB_S + 4), XB_S + 4, 1, Vs + 16 * ct, BWD_LD, 1,
+    for (int ct = 0; ct < CT; ++ct) {
+      const f32x4 c = mm16<XB_S>(Pt + 16 * wave * (XB_S + 4), XB_S + 4, 1, Vs + 16 * ct, LD, 1,
                                  f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[ct][r] += c[r];
@@ -1174,9 +1202,9 @@ __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
     const int tok = q0 + 16 * wave + 4 * g + r;
     float dt = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const float ov = l > 0.f ? o[ct][r] / l : 0.f;
-      const float d = tok < a.n ? io_get(DO + (size_t)tok * HD + 16 * ct + c16) : 0.f;
+      const float d = tok < a.n ? io_get(DO + (size_t)tok * D + 16 * ct + c16) : 0.f;
       dt += ov * d;
     }
     dt = sum16(dt);
@@ -1188,24 +1216,25 @@ __global__ __launch_bounds__(256) void k_bwd_xstats(XBwdArgs a) {
 }
 
 // grid (ceil(n / 64), BH), block 256: dq for the block's 64 queries.
-template <typename IO>
+template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_bwd_xq(XBwdArgs a) {
   extern __shared__ __align__(16) float xb_lds[];
+  constexpr int LD = D + 4, CT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / a.H, q0 = blockIdx.x * XB_T;
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   float* const Qs = xb_lds;
-  float* const DOs = Qs + XB_T * BWD_LD;
-  float* const Ks = DOs + XB_T * BWD_LD;
-  float* const Vs = Ks + XB_S * BWD_LD;
-  float* const DS = Vs + 2 * XB_S * BWD_LD;  // [64][XB_S + 4]
+  float* const DOs = Qs + XB_T * LD;
+  float* const Ks = DOs + XB_T * LD;
+  float* const Vs = Ks + XB_S * LD;
+  float* const DS = Vs + 2 * XB_S * LD;  // [64][XB_S + 4]
   float* const val = DS + XB_T * (XB_S + 4);
-  xb_own(Q, q0, a.n, a.s4, Qs);
-  xb_own(DO, q0, a.n, 1.f, DOs);
+  xb_own<IO, D>(Q, q0, a.n, a.s4, Qs);
+  xb_own<IO, D>(DO, q0, a.n, 1.f, DOs);
   float lse[4], dt[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -1213,13 +1242,13 @@ __global__ __launch_bounds__(256) void k_bwd_xq(XBwdArgs a) {
     lse[r] = tok < a.n ? a.lse[(size_t)bh * a.n + tok] : INFINITY;
     dt[r] = tok < a.n ? a.Dt[(size_t)bh * a.n + tok] : 0.f;
   }
-  f32x4 dq[4];
+  f32x4 dq[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) dq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct) dq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < a.n; k0 += XB_S) {
     __syncthreads();
-    xb_stage(K, k0, a.n, a.s4, Ks);
-    xb_stage(V, k0, a.n, 1.f, Vs);
+    xb_stage<IO, D>(K, k0, a.n, a.s4, Ks);
+    xb_stage<IO, D>(V, k0, a.n, 1.f, Vs);
     if (threadIdx.x < XB_S) {
       const int key = k0 + threadIdx.x;
       val[threadIdx.x] = (key < a.n && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
@@ -1227,9 +1256,9 @@ __global__ __launch_bounds__(256) void k_bwd_xq(XBwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const f32x4 s = mm16<HD>(Qs + 16 * wave * BWD_LD, BWD_LD, 1, Ks + 16 * kt * BWD_LD, 1, BWD_LD,
+      const f32x4 s = mm16<D>(Qs + 16 * wave * LD, LD, 1, Ks + 16 * kt * LD, 1, LD,
                                f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 dp = mm16<HD>(DOs + 16 * wave * BWD_LD, BWD_LD, 1, Vs + 16 * kt * BWD_LD, 1, BWD_LD,
+      const f32x4 dp = mm16<D>(DOs + 16 * wave * LD, LD, 1, Vs + 16 * kt * LD, 1, LD,
                                 f32x4{0.f, 0.f, 0.f, 0.f});
       const bool ok = val[16 * kt + c16] != 0.f;
 #pragma unroll
@@ -1240,38 +1269,39 @@ __global__ __launch_bounds__(256) void k_bwd_xq(XBwdArgs a) {
     }
     // dq += dS Ks (the wave's own 16 rows)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      dq[ct] = mm16<XB_S>(DS + 16 * wave * (XB_S + 4), XB_S + 4, 1, Ks + 16 * ct, BWD_LD, 1, dq[ct]);
+    for (int ct = 0; ct < CT; ++ct)
+      dq[ct] = mm16<XB_S>(DS + 16 * wave * (XB_S + 4), XB_S + 4, 1, Ks + 16 * ct, LD, 1, dq[ct]);
   }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = q0 + 16 * wave + 4 * g + r;
-      if (tok < a.n) io_put(reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * HD + 16 * ct + c16, a.s4 * dq[ct][r]);
+      if (tok < a.n) io_put(reinterpret_cast<IO*>(a.dq) + ((size_t)bh * a.n + tok) * D + 16 * ct + c16, a.s4 * dq[ct][r]);
     }
 }
 
 // grid (ceil(n / 64), BH), block 256: dk and dv for the block's 64 keys.
-template <typename IO>
+template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_bwd_xkv(XBwdArgs a) {
   extern __shared__ __align__(16) float xb_lds[];
+  constexpr int LD = D + 4, CT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / a.H, k0 = blockIdx.x * XB_T;
-  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * HD;
-  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * HD;
-  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * HD;
-  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * HD;
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* K = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
+  const IO* V = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   float* const Ks = xb_lds;
-  float* const Vs = Ks + XB_T * BWD_LD;
-  float* const Qs = Vs + XB_T * BWD_LD;
-  float* const DOs = Qs + XB_S * BWD_LD;
-  float* const Pt = DOs + 2 * XB_S * BWD_LD;  // [XB_S queries][64 keys + 4]: P, then dS
+  float* const Vs = Ks + XB_T * LD;
+  float* const Qs = Vs + XB_T * LD;
+  float* const DOs = Qs + XB_S * LD;
+  float* const Pt = DOs + 2 * XB_S * LD;  // [XB_S queries][64 keys + 4]: P, then dS
   float* const st = Pt + XB_S * (XB_T + 4);   // lse, D of the step's queries
   float* const dst = st + XB_S;
-  xb_own(K, k0, a.n, a.s4, Ks);
-  xb_own(V, k0, a.n, 1.f, Vs);
+  xb_own<IO, D>(K, k0, a.n, a.s4, Ks);
+  xb_own<IO, D>(V, k0, a.n, 1.f, Vs);
   // validity of the wave's own keys (rows of the C tiles below)
   bool ok[4];
 #pragma unroll
@@ -1279,13 +1309,13 @@ __global__ __launch_bounds__(256) void k_bwd_xkv(XBwdArgs a) {
     const int key = k0 + 16 * wave + 4 * g + r;
     ok[r] = key < a.n && (mask == nullptr || mask[key] != 0);
   }
-  f32x4 dk[4], dv[4];
+  f32x4 dk[CT], dv[CT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) dk[ct] = dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int t0 = 0; t0 < a.n; t0 += XB_S) {
     __syncthreads();
-    xb_stage(Q, t0, a.n, a.s4, Qs);
-    xb_stage(DO, t0, a.n, 1.f, DOs);
+    xb_stage<IO, D>(Q, t0, a.n, a.s4, Qs);
+    xb_stage<IO, D>(DO, t0, a.n, 1.f, DOs);
     if (threadIdx.x < XB_S) {
       const int tok = t0 + threadIdx.x;
       st[threadIdx.x] = tok < a.n ? a.lse[(size_t)bh * a.n + tok] : INFINITY;
@@ -1296,9 +1326,9 @@ __global__ __launch_bounds__(256) void k_bwd_xkv(XBwdArgs a) {
     f32x4 p[2], ds[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const f32x4 s = mm16<HD>(Ks + 16 * wave * BWD_LD, BWD_LD, 1, Qs + 16 * qt * BWD_LD, 1, BWD_LD,
+      const f32x4 s = mm16<D>(Ks + 16 * wave * LD, LD, 1, Qs + 16 * qt * LD, 1, LD,
                                f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 dp = mm16<HD>(Vs + 16 * wave * BWD_LD, BWD_LD, 1, DOs + 16 * qt * BWD_LD, 1, BWD_LD,
+      const f32x4 dp = mm16<D>(Vs + 16 * wave * LD, LD, 1, DOs + 16 * qt * LD, 1, LD,
                                 f32x4{0.f, 0.f, 0.f, 0.f});
       const int qq = 16 * qt + c16;
 #pragma unroll
@@ -1319,21 +1349,21 @@ __global__ __launch_bounds__(256) void k_bwd_xkv(XBwdArgs a) {
           myP[(16 * qt + c16) * (XB_T + 4) + 16 * wave + 4 * g + r] = pass == 0 ? p[qt][r] : ds[qt][r];
       // A(key i, query k) = myP[k][16 wave + i]
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         if (pass == 0)
-          dv[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, DOs + 16 * ct, BWD_LD, 1, dv[ct]);
+          dv[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, DOs + 16 * ct, LD, 1, dv[ct]);
         else
-          dk[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, Qs + 16 * ct, BWD_LD, 1, dk[ct]);
+          dk[ct] = mm16<XB_S>(myP + 16 * wave, 1, XB_T + 4, Qs + 16 * ct, LD, 1, dk[ct]);
       }
     }
   }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = k0 + 16 * wave + 4 * g + r;
       if (key >= a.n) continue;
-      const size_t o = ((size_t)bh * a.n + key) * HD + 16 * ct + c16;
+      const size_t o = ((size_t)bh * a.n + key) * D + 16 * ct + c16;
       io_put(reinterpret_cast<IO*>(a.dv) + o, dv[ct][r] + (a.dvc != nullptr ? a.dvc[o] : 0.f));
       io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * dk[ct][r]);
     }

@@ -798,7 +798,7 @@ BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   b.nck = (p.n + BWD_CK - 1) / BWD_CK;
   b.ncv = (p.n + BWD_CV - 1) / BWD_CV;
   b.mats = bwd_mm_mats(n_iter);
-  const size_t BH = p.BH, M = p.m, n = p.n, D = HD;
+  const size_t BH = p.BH, M = p.m, n = p.n, D = p.D;
   size_t o = p.total;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -825,11 +825,11 @@ BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   return b;
 }
 
-template <typename IO, int M>
+template <typename IO, int M, int D>
 int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* q, const void* k, const void* v,
                     const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option,
                     const void* dout, void* dq, void* dk, void* dv, float* dconv_w, hipStream_t st) {
-  int rc = launch_nystrom<IO, M, HD>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, nullptr, st);
+  int rc = launch_nystrom<IO, M, D>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, nullptr, st);
   if (rc != NYS_OK) return rc;
   BwdArgs a{};
   a.q = q;
@@ -876,42 +876,44 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.ncv = bp.ncv;
   a.n_iter = n_iter;
   a.init_option = init_option;
-  a.s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  a.s4 = 1.0f / sqrtf(sqrtf((float)D));
   if (conv_w != nullptr) {
-    HIP_TRY(allow_lds(k_bwd_dvconv<IO>, BWD_DV_LDS));
-    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
-                   (uint32_t)BWD_DV_LDS, st, a));
+    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
+                   (uint32_t)dl, st, a));
     if (dconv_w != nullptr) {
-      HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
-      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)BWD_CV_LDS, st, a));
+      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)cl, st, a));
     }
   }
-  constexpr int tl = BwdTokLayout<M>::BYTES;
-  HIP_TRY(allow_lds(k_bwd_tok<IO, M>, tl));
-  HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl, st,
-                 a));
-  constexpr int ml = bwd_mm_lds_bytes<M>();
+  constexpr int tl = BwdTokLayout<M, D>::BYTES;
+  HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
+  HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
+                 st, a));
+  constexpr int ml = bwd_mm_lds_bytes<M, D>();
   if constexpr (M == 64) {
-    HIP_TRY(allow_lds(k_bwd_mm1_64, BWD_MM64_LDS));
-    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
+    HIP_TRY(allow_lds(k_bwd_mm1_64<D>, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
   } else {
-    HIP_TRY(allow_lds(k_bwd_mm1<M>, ml));
-    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+    HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   }
-  HIP_TRY(allow_lds(k_bwd_mm2<M>, ml));
-  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
-  constexpr int kl = BwdKeyLayout<M>::BYTES;
-  HIP_TRY(allow_lds(k_bwd_key<IO, M>, kl));
-  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
-  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M>, dim3(M * HD / 256, p.BH), dim3(256), 0, st, a));
-  HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
+  HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
+  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  constexpr int kl = BwdKeyLayout<M, D>::BYTES;
+  HIP_TRY(allow_lds(k_bwd_key<IO, M, D>, kl));
+  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M, D>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
+  static_assert((M * D) % 256 == 0, "k_bwd_qt: one element per thread");
+  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M, D>, dim3(M * D / 256, p.BH), dim3(256), 0, st, a));
+  HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M, D>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
   if (conv_w != nullptr && dconv_w != nullptr)
     HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(1024), 0, st, a));
   return NYS_OK;
 }
 
 // Exact branch (m == n): the conv backward, then the three flash-style passes.
-template <typename IO>
+template <typename IO, int D>
 int launch_backward_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
                           const float* conv_w, int conv_k, const void* dout, void* dq, void* dk, void* dv,
                           float* dconv_w, hipStream_t st) {
@@ -925,7 +927,7 @@ int launch_backward_exact(int B, int H, int n, const void* q, const void* k, con
   };
   take(ZERO_BYTES);
   const size_t off_lse = take(BH * n * 4), off_dt = take(BH * n * 4);
-  const size_t off_dvc = conv_w ? take(BH * n * HD * 4) : 0, off_pconv = conv_w ? take(BH * ncv * conv_k * 4) : 0;
+  const size_t off_dvc = conv_w ? take(BH * n * D * 4) : 0, off_pconv = conv_w ? take(BH * ncv * conv_k * 4) : 0;
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace* w = nullptr;
   int rc = get_workspace(st, o, &w);
@@ -943,12 +945,13 @@ int launch_backward_exact(int B, int H, int n, const void* q, const void* k, con
   c.BH = (int)BH;
   c.ncv = ncv;
   if (conv_w != nullptr) {
-    HIP_TRY(allow_lds(k_bwd_dvconv<IO>, BWD_DV_LDS));
-    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO>, dim3((n + BWD_DV_TOK - 1) / BWD_DV_TOK, (unsigned)BH), dim3(256),
-                   (uint32_t)BWD_DV_LDS, st, c));
+    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((n + BWD_DV_TOK - 1) / BWD_DV_TOK, (unsigned)BH),
+                   dim3(256), (uint32_t)dl, st, c));
     if (dconv_w != nullptr) {
-      HIP_TRY(allow_lds(k_bwd_conv<IO>, BWD_CV_LDS));
-      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)BWD_CV_LDS, st, c));
+      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)cl, st, c));
     }
   }
   XBwdArgs x{};
@@ -965,14 +968,15 @@ int launch_backward_exact(int B, int H, int n, const void* q, const void* k, con
   x.dv = dv;
   x.n = n;
   x.H = H;
-  x.s4 = 1.0f / sqrtf(sqrtf((float)HD));
+  x.s4 = 1.0f / sqrtf(sqrtf((float)D));
   const dim3 grid((n + XB_T - 1) / XB_T, (unsigned)BH);
-  HIP_TRY(allow_lds(k_bwd_xstats<IO>, XB_LDS));
-  HIP_TRY(launch("k_bwd_xstats", k_bwd_xstats<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
-  HIP_TRY(allow_lds(k_bwd_xq<IO>, XB_LDS));
-  HIP_TRY(launch("k_bwd_xq", k_bwd_xq<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
-  HIP_TRY(allow_lds(k_bwd_xkv<IO>, XB_LDS));
-  HIP_TRY(launch("k_bwd_xkv", k_bwd_xkv<IO>, grid, dim3(256), (uint32_t)XB_LDS, st, x));
+  constexpr int xl = xb_lds_bytes<D>();
+  HIP_TRY(allow_lds(k_bwd_xstats<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xstats", k_bwd_xstats<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
+  HIP_TRY(allow_lds(k_bwd_xq<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xq", k_bwd_xq<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
+  HIP_TRY(allow_lds(k_bwd_xkv<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xkv", k_bwd_xkv<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
   if (conv_w != nullptr && dconv_w != nullptr)
     HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(H), dim3(1024), 0, st, c));
   return NYS_OK;
@@ -990,9 +994,10 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
       return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
-  if (d != HD) return fail(NYS_ERR_UNSUPPORTED, "backward: d=%d (the backward kernels are built for d=64)", d);
-  if (m != n && padded_m(m) > 128) return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to 128 landmarks)", m);
-  const size_t bytes = (size_t)B * H * n * HD * sizeof(IO);
+  const int m_max = d == 128 ? 64 : 128;  // the token pass's LDS tiles bound M * d
+  if (m != n && padded_m(m) > m_max)
+    return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to %d landmarks at d=%d)", m, m_max, d);
+  const size_t bytes = (size_t)B * H * n * d * sizeof(IO);
   const void* const ro[4] = {q, k, v, dout};
   void* const wr[3] = {dq, dk, dv};
   for (int i = 0; i < 3; ++i) {
@@ -1004,7 +1009,13 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
   }
   for (const void* ptr : {q, k, v, dout})
     if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(NYS_ERR_INVALID, "q, k, v, dout must be 16-byte aligned");
-  if (m == n) return launch_backward_exact<IO>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+  if (m == n) {
+    switch (d) {
+      case 32: return launch_backward_exact<IO, 32>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+      case 64: return launch_backward_exact<IO, 64>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+      default: return launch_backward_exact<IO, 128>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+    }
+  }
   Plan p = make_plan(B, H, n, m, d);
   p.record = true;  // A is read back
   p.bwd = true;
@@ -1014,14 +1025,24 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
   Workspace* w = nullptr;
   rc = get_workspace(st, bp.total, &w);
   if (rc != NYS_OK) return rc;
-  switch (p.m) {
-    case 32: return launch_backward<IO, 32>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
-    case 64: return launch_backward<IO, 64>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
-    case 96: return launch_backward<IO, 96>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
-    case 128: return launch_backward<IO, 128>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, dconv_w, st);
+#define NYS_BWD(MM, DD)                                                                                            \
+  return launch_backward<IO, MM, DD>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, \
+                                     dconv_w, st)
+  switch (d * 1000 + p.m) {
+    case 32032: NYS_BWD(32, 32);
+    case 32064: NYS_BWD(64, 32);
+    case 32096: NYS_BWD(96, 32);
+    case 32128: NYS_BWD(128, 32);
+    case 64032: NYS_BWD(32, 64);
+    case 64064: NYS_BWD(64, 64);
+    case 64096: NYS_BWD(96, 64);
+    case 64128: NYS_BWD(128, 64);
+    case 128032: NYS_BWD(32, 128);
+    case 128064: NYS_BWD(64, 128);
     default: break;
   }
-  return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d", m);
+#undef NYS_BWD
+  return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d, d=%d", m, d);
 }
 
 }  // namespace

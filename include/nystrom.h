@@ -187,10 +187,10 @@ int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const vo
  * (nothing is kept from the forward call).  The initial scale c is
  * differentiated through its maxima (the gradient of a maximum goes to its
  * first arg-max).  All pointers are DEVICE pointers owned by the caller;
- * dq, dk, dv must not overlap each other or q, k, v, dout.  Built for
- * d = 64: the Nystrom path with up to 128 landmarks, and the exact branch
- * (m == n, any n).  NYS_ERR_UNSUPPORTED for other d or more landmarks.
- * Other errors as nystrom_attention. */
+ * dq, dk, dv must not overlap each other or q, k, v, dout.  Head sizes
+ * d = 32, 64 and 128: the exact branch (m == n, any n) at each, the Nystrom
+ * path with up to 128 landmarks at d = 32 and 64 and up to 64 at d = 128
+ * (NYS_ERR_UNSUPPORTED for more).  Other errors as nystrom_attention. */
 int nystrom_attention_backward(int dtype, const void* q, const void* k, const void* v,
                                const uint8_t* key_mask, const float* conv_w,
                                int conv_kernel_size, int B, int H, int n, int d, int m,

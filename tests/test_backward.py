@@ -104,6 +104,18 @@ def test_backward_exact_branch(dtype, n):
     _check(f"exact-n{n}-nomask-noconv", y, dtype, n, 6, 0, conv=False, seed=6, zero_qk=n == 1)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d,m,n", [(32, 64, 512), (32, 128, 512), (32, 50, 400), (32, 200, 200),
+                                   (128, 64, 512), (128, 32, 96), (128, 50, 400), (128, 200, 200)])
+def test_backward_head_sizes(dtype, d, m, n):
+    """Head sizes 32 and 128: the Nystrom path (up to 128 landmarks at
+    d = 32, up to 64 at d = 128; padded landmark counts) and the exact
+    branch (m == n), with a partial mask and the convolution."""
+    x = make_custom(2, 2, n, d, seed=1010 + d + m, dtype=dtype, lengths=[n, n - n // 3])
+    _check(f"d{d}-m{m}-n{n}", x, dtype, m, 6, 0, seed=7)
+    _check(f"d{d}-m{m}-n{n}-init1-noconv", x, dtype, m, 6, 1, conv=False, seed=8)
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_backward_workload(idx):
     """The workloads at their full sizes (up to 128 landmarks)."""
