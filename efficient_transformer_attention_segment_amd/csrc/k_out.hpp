@@ -337,8 +337,18 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
   __shared__ __align__(16) __bf16 ring[CONV ? Ly::RING_ELEMS : 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y, h = bh % a.H;
-  const int tb = blockIdx.x * R;
+  // XCD-aware placement: workgroup i of the launch runs on XCD i mod 8, so
+  // when the head count is a multiple of 8 the linear index is remapped to
+  // put every range of a head on one XCD (its landmark and W^T fragments,
+  // and the V rows neighbouring ranges share, then come into one L2)
+  int by = blockIdx.y, bx = blockIdx.x;
+  if ((gridDim.y & 7) == 0) {
+    const int L = blockIdx.x + blockIdx.y * gridDim.x, s = L >> 3;
+    by = (L & 7) + 8 * (s / gridDim.x);
+    bx = s % gridDim.x;
+  }
+  const int bh = by, h = bh % a.H;
+  const int tb = bx * R;
   const int te = min(a.n, tb + R);
   const int nunits = (te - tb + OUTS_UNIT - 1) / OUTS_UNIT;
   const u16* Q = reinterpret_cast<const u16*>(a.q) + a.in.base(bh, a.H);
