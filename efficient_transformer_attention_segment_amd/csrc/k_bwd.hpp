@@ -314,6 +314,48 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 // ---------------------------------------------------------------------------
 constexpr int BWD_MM_NT = 1024;  // threads of the per-head kernels (16 waves)
 
+// LDS barrier without the global-memory drain of __syncthreads(): the
+// kernels below keep global stores (the iteration's history) and prefetch
+// loads in flight across it; only LDS writes must be complete.
+__device__ __forceinline__ void lds_sync() {
+  wait_lgkm0();
+  barrier_only();
+}
+
+// Sum of the nch chunk partials p[ch * stride + i] for the four consecutive
+// elements i .. i + 3 (16-byte aligned), in chunk order; up to 8 loads in
+// flight per tensor.
+__device__ __forceinline__ float4 sum_chunks4(const float* p, size_t stride, int nch) {
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      x[u] = c0 + u < nch ? *reinterpret_cast<const float4*>(p + (size_t)(c0 + u) * stride)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s.x += x[u].x;
+      s.y += x[u].y;
+      s.z += x[u].z;
+      s.w += x[u].w;
+    }
+  }
+  return s;
+}
+
+// dW and dKt (F part) of one head from the token-chunk partials: each
+// thread sums four consecutive elements over the chunks, in chunk order.
+template <int M, int D>
+__device__ __forceinline__ void reduce_token_partials(const BwdArgs& a, int bh, float* dW) {
+  for (int i = 4 * threadIdx.x; i < M * D; i += 4 * BWD_MM_NT) {
+    const size_t off = (size_t)bh * a.nct * M * D + i;
+    *reinterpret_cast<float4*>(dW + i) = sum_chunks4(a.pw + off, (size_t)M * D, a.nct);
+    *reinterpret_cast<float4*>(a.dKt + (size_t)bh * M * D + i) = sum_chunks4(a.pk + off, (size_t)M * D, a.nct);
+  }
+}
+
+
 // Block-wide product C = alpha op(A) op(B) + beta C for float32 row-major
 // matrices in global memory: op(A) is R x K, op(B) is K x N; each operand
 // is staged in LDS (row stride + 4) first.  BWD_MM_NT threads.
@@ -379,15 +421,7 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
   const float c = a.cscale[bh];
 
   // dW and dKt (F part) from the token-chunk partials, in chunk order
-  for (int i = tid; i < M * D; i += NT) {
-    float sw = 0.f, sk = 0.f;
-    for (int ch = 0; ch < a.nct; ++ch) {
-      sw += a.pw[((size_t)bh * a.nct + ch) * M * D + i];
-      sk += a.pk[((size_t)bh * a.nct + ch) * M * D + i];
-    }
-    dW[i] = sw;
-    a.dKt[(size_t)bh * M * D + i] = sk;
-  }
+  reduce_token_partials<M, D>(a, bh, dW);
   // the iteration again in float32: Z_0 = A^T / c, X = A Z, P = 13I - 15X +
   // 7X^2 - X^3, Z <- Z P / 4; dA starts at zero
   for (int i = tid; i < MM; i += NT) {
@@ -481,14 +515,14 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
 
 // Product on operands already in LDS (row strides lda, ldb; flat
 // pointers), C = alpha op(A) op(B) + beta C with C in LDS or global memory
-// (row stride ldc).  Starts with a barrier (operands written, C free).
+// (row stride ldc).  Starts with an LDS barrier (operands written, C free).
 template <int R, int N, int K>
 __device__ void lgemm(float* C, int ldc, const float* La, int lda, bool ta, const float* Lb, int ldb, bool tb,
                       float alpha, float beta) {
   constexpr int NWV = BWD_MM_NT / 64, TR = R / 16, TN = N / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  __syncthreads();
+  lds_sync();
   const int ai = ta ? 1 : lda, ak = ta ? lda : 1;
   const int bk = tb ? 1 : ldb, bj = tb ? ldb : 1;
   for (int t = wave; t < TR * TN; t += NWV) {
@@ -502,13 +536,24 @@ __device__ void lgemm(float* C, int ldc, const float* La, int lda, bool ta, cons
   }
 }
 
+// The calling wave's tile (it, jt) = (wave / 4, wave % 4) of a 64 x 64
+// product on LDS operands, added to acc (16 waves: one tile each).
+__device__ __forceinline__ f32x4 ltile64(const float* La, int lda, bool ta, const float* Lb, int ldb, bool tb,
+                                         f32x4 acc) {
+  const int wave = threadIdx.x >> 6, it = wave >> 2, jt = wave & 3;
+  lds_sync();
+  const int ai = ta ? 1 : lda, ak = ta ? lda : 1;
+  const int bk = tb ? 1 : ldb, bj = tb ? ldb : 1;
+  return mm16<64>(La + 16 * it * ai, ai, ak, Lb + 16 * jt * bj, bk, bj, acc);
+}
+
 // LDS image of a row-major M x Mc global matrix (row stride ld).
 __device__ __forceinline__ void lds_load(float* dst, int ld, const float* src, int M, int Mc) {
-  __syncthreads();
+  lds_sync();
   for (int i = threadIdx.x; i < M * Mc; i += BWD_MM_NT) dst[(i / Mc) * ld + i % Mc] = src[i];
 }
 __device__ __forceinline__ void lds_store(float* dst, const float* src, int ld, int M, int Mc) {
-  __syncthreads();
+  lds_sync();
   for (int i = threadIdx.x; i < M * Mc; i += BWD_MM_NT) dst[i] = src[(i / Mc) * ld + i % Mc];
 }
 
@@ -516,15 +561,18 @@ constexpr int BWD_MM64_LDS = 4 * 9 * 64 * 68;
 
 // k_bwd_mm1 for 64 landmarks with the working set resident in LDS: A, G,
 // G', dP, dX and the step's Z_k, X_k, X_k^2, P_k (then T) as nine 64 x 64
-// float32 images (row stride 68); the history Z_k, X_k, X_k^2, P_k and the
-// accumulated dA go to the per-head scratch in global memory, as in
-// k_bwd_mm1, and the results are the same products in the same order.
+// float32 images (row stride 68); the history Z_k, X_k, X_k^2, P_k goes to
+// the per-head scratch in global memory and comes back one step at a time
+// (the four matrices of a step in one batch of loads), and each wave keeps
+// its 16 x 16 tile of the accumulated dA in registers.  The products and
+// their order are those of k_bwd_mm1.
 // grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
 template <int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
   const int bh = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   float* const sA = bw_lds;
   float* sG = sA + SZ;
   float* sGn = sG + SZ;
@@ -544,28 +592,19 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   float* const dW = a.dW + (size_t)bh * M * D;
   const float c = a.cscale[bh];
 
-  for (int i = tid; i < M * D; i += NT) {
-    float sw = 0.f, sk = 0.f;
-    for (int ch = 0; ch < a.nct; ++ch) {
-      sw += a.pw[((size_t)bh * a.nct + ch) * M * D + i];
-      sk += a.pk[((size_t)bh * a.nct + ch) * M * D + i];
-    }
-    dW[i] = sw;
-    a.dKt[(size_t)bh * M * D + i] = sk;
-  }
+  reduce_token_partials<M, D>(a, bh, dW);
   lds_load(sA, LD, A, M, M);
-  __syncthreads();
+  lds_sync();
   for (int i = tid; i < MM; i += NT) {
-    const float z = A[(i % M) * M + i / M] / c;
+    const float z = sA[(i % M) * LD + i / M] / c;
     sZ[(i / M) * LD + i % M] = z;
     Zk(0)[i] = z;
-    dA[i] = 0.f;
   }
   for (int k = 0; k < a.n_iter; ++k) {
     lgemm<M, M, M>(sX, LD, sA, LD, false, sZ, LD, false, 1.f, 0.f);
     lgemm<M, M, M>(sX2, LD, sX, LD, false, sX, LD, false, 1.f, 0.f);
     lgemm<M, M, M>(sPT, LD, sX, LD, false, sX2, LD, false, -1.f, 0.f);
-    __syncthreads();
+    lds_sync();
     for (int i = tid; i < MM; i += NT) {
       const int o = (i / M) * LD + i % M;
       sPT[o] += (i / M == i % M ? 13.f : 0.f) - 15.f * sX[o] + 7.f * sX2[o];
@@ -590,14 +629,35 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   lds_load(sBV, LDW, a.BV + (size_t)bh * M * D, M, D);
   lgemm<M, M, D>(sG, LD, sW, LDW, false, sBV, LDW, true, 1.f, 0.f);
   lgemm<M, D, M>(a.dBV + (size_t)bh * M * D, D, sZ, LD, true, sW, LDW, false, 1.f, 0.f);
+  // the history stores are complete before any of it is read back
+  wait_vmcnt<0>();
+  f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};  // this wave's tile of dA
   for (int k = a.n_iter - 1; k >= 0; --k) {
-    lds_load(sZ, LD, Zk(k), M, M);
-    lds_load(sX, LD, Xk(k), M, M);
-    lds_load(sX2, LD, X2k(k), M, M);
-    lds_load(sPT, LD, Pk(k), M, M);
+    {
+      // Z_k, X_k, X_k^2, P_k into LDS: every load of the step in flight at once
+      constexpr int PER = MM / NT;
+      float hz[PER], hx[PER], hx2[PER], hp[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * NT;
+        hz[u] = Zk(k)[i];
+        hx[u] = Xk(k)[i];
+        hx2[u] = X2k(k)[i];
+        hp[u] = Pk(k)[i];
+      }
+      lds_sync();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * NT, o = (i / M) * LD + i % M;
+        sZ[o] = hz[u];
+        sX[o] = hx[u];
+        sX2[o] = hx2[u];
+        sPT[o] = hp[u];
+      }
+    }
     lgemm<M, M, M>(sGn, LD, sG, LD, false, sPT, LD, true, 0.25f, 0.f);   // dZ_k = G P^T / 4
     lgemm<M, M, M>(sdP, LD, sZ, LD, true, sG, LD, false, 0.25f, 0.f);    // dP = Z^T G / 4
-    __syncthreads();
+    lds_sync();
     for (int i = tid; i < MM; i += NT) {
       const int o = (i / M) * LD + i % M;
       sdX[o] = -15.f * sdP[o];
@@ -608,20 +668,24 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
     lgemm<M, M, M>(sPT, LD, sX, LD, true, sdP, LD, false, 1.f, 0.f);     // T = X^T dP
     lgemm<M, M, M>(sdX, LD, sPT, LD, false, sX, LD, true, -1.f, 1.f);    // - X^T dP X^T
     lgemm<M, M, M>(sdX, LD, sX2, LD, true, sdP, LD, false, -1.f, 1.f);   // - (X^2)^T dP
-    lgemm<M, M, M>(dA, M, sdX, LD, false, sZ, LD, true, 1.f, 1.f);       // dA += dX Z^T
+    dacc = ltile64(sdX, LD, false, sZ, LD, true, dacc);                   // dA += dX Z^T
     lgemm<M, M, M>(sGn, LD, sA, LD, true, sdX, LD, false, 1.f, 1.f);     // dZ_k += A^T dX
     float* const t = sG;
     sG = sGn;
     sGn = t;
   }
-  __syncthreads();
-  // Z_0 = A^T / c: dA += G^T / c; dc = -sum(G A^T) / c^2; the arg-max column
+  lds_sync();
+  // Z_0 = A^T / c: dA += G^T / c, written with the wave's tile; dc = -sum(G A^T) / c^2
   float part = 0.f;
-  for (int i = tid; i < MM; i += NT) {
-    const int r = i / M, col = i % M;
-    const float gv = sG[col * LD + r];
-    dA[i] += gv / c;
-    part += gv * sA[r * LD + col];
+  {
+    const int it = wave >> 2, jt = wave & 3, col = 16 * jt + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * it + 4 * g + r;
+      const float gv = sG[col * LD + row];
+      dA[row * M + col] = dacc[r] + gv / c;
+      part += gv * sA[row * LD + col];
+    }
   }
   float* const red = sX;  // free now
   int* const redj = reinterpret_cast<int*>(sX2);
@@ -637,8 +701,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   int cj = 0;
   if (tid < M) {
     cs = 0.f;
-    for (int r = 0; r < M; ++r) cs += A[r * M + tid];
-    for (int j = 0; j < M; ++j) rs += A[tid * M + j];
+    for (int r = 0; r < M; ++r) cs += sA[r * LD + tid];
+    for (int j = 0; j < M; ++j) rs += sA[tid * LD + j];
     cj = tid;
   }
   red[tid] = cs;
@@ -666,62 +730,87 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   if (tid == 0) a.rmax[bh] = red[0];
 }
 
-// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
+// grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().  Row
+// work runs 16 threads to a row (a row's 16 threads are 16 consecutive
+// lanes, reduced with sum16).
 template <int M, int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
   constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
-  constexpr int MM = M * M;
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  constexpr int MM = M * M, RPP = NT / 16;
+  const int bh = blockIdx.x, tid = threadIdx.x, l16 = tid & 15;
   float* const La = bw_lds;
   float* const Lb = bw_lds + bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
   const float* A = a.A + (size_t)bh * MM;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
-  float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
+  const float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
   float* const dSA = S + (size_t)(4 * a.n_iter + 1 + 4) * MM;  // the T slot
-  // c's share: column j* of the head holding the maximum column sum
-  __shared__ float add;
-  __shared__ int jstar;
-  if (tid == 0) {
-    float dcs = a.dc[bh], rm = a.rmax[bh];
-    bool mine = true;
-    if (a.init_option == 0) {
-      int hs = 0;
-      float best = a.cmax[0];
-      dcs = 0.f;
-      rm = 0.f;
-      for (int h = 0; h < a.BH; ++h) {
-        dcs += a.dc[h];
-        rm = fmaxf(rm, a.rmax[h]);
-        if (a.cmax[h] > best) {
-          best = a.cmax[h];
-          hs = h;
+  // c's share, added to column j* of dA: for option 0 only in the head
+  // holding the maximum column sum over all heads (the first such head),
+  // with the sum of every head's dc and the largest row sum
+  float add;
+  if (a.init_option == 0) {
+    __shared__ float rsum[NT], rmx[NT], rbest[NT];
+    __shared__ int rh[NT];
+    float sdc = 0.f, srm = 0.f, best = -INFINITY;
+    int hb = 0x7fffffff;
+    for (int h = tid; h < a.BH; h += NT) {
+      sdc += a.dc[h];
+      srm = fmaxf(srm, a.rmax[h]);
+      const float cm = a.cmax[h];
+      if (cm > best) {
+        best = cm;
+        hb = h;
+      }
+    }
+    rsum[tid] = sdc;
+    rmx[tid] = srm;
+    rbest[tid] = best;
+    rh[tid] = hb;
+    __syncthreads();
+    for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+      if (tid < s2) {
+        rsum[tid] += rsum[tid + s2];
+        rmx[tid] = fmaxf(rmx[tid], rmx[tid + s2]);
+        if (rbest[tid + s2] > rbest[tid] || (rbest[tid + s2] == rbest[tid] && rh[tid + s2] < rh[tid])) {
+          rbest[tid] = rbest[tid + s2];
+          rh[tid] = rh[tid + s2];
         }
       }
-      mine = hs == bh;
+      __syncthreads();
     }
-    add = mine ? dcs * rm : 0.f;
-    jstar = a.cmaxj[bh];
+    add = rh[0] == bh ? rsum[0] * rmx[0] : 0.f;
+  } else {
+    add = a.dc[bh] * a.rmax[bh];
   }
-  __syncthreads();
-  if (add != 0.f)
-    for (int r = tid; r < M; r += NT) dA[r * M + jstar] += add;
-  __syncthreads();
-  // dS_A = A (dA - rowsum(dA A)), one row per thread
-  for (int r = tid; r < M; r += NT) {
+  const int jstar = a.cmaxj[bh];
+  // dS_A = A (dA - rowsum(dA A))
+  for (int r = tid / 16; r < M; r += RPP) {
+    float av[M / 16], dv[M / 16];
     float s = 0.f;
-    for (int j = 0; j < M; ++j) s += dA[r * M + j] * A[r * M + j];
-    for (int j = 0; j < M; ++j) dSA[r * M + j] = A[r * M + j] * (dA[r * M + j] - s);
+#pragma unroll
+    for (int u = 0; u < M / 16; ++u) {
+      const int j = l16 + 16 * u;
+      av[u] = A[r * M + j];
+      dv[u] = dA[r * M + j] + (j == jstar ? add : 0.f);
+      s += dv[u] * av[u];
+    }
+    s = sum16(s);
+#pragma unroll
+    for (int u = 0; u < M / 16; ++u) dSA[r * M + l16 + 16 * u] = av[u] * (dv[u] - s);
   }
-  // dQt_A = dS_A Kt; dKt += dS_A^T Qt
+  // dQt_A = dS_A Kt; dKt += dS_A^T Qt (bgemm starts with a block barrier)
   bgemm<M, D, M>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La, Lb);
   bgemm<M, D, M>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La, Lb);
   // D_i = dBV_i . BV_i
-  for (int r = tid; r < M; r += NT) {
+  for (int r = tid / 16; r < M; r += RPP) {
+    const float* x = a.dBV + ((size_t)bh * M + r) * D;
+    const float* y = a.BV + ((size_t)bh * M + r) * D;
     float s = 0.f;
-    for (int c = 0; c < D; ++c)
-      s += a.dBV[((size_t)bh * M + r) * D + c] * a.BV[((size_t)bh * M + r) * D + c];
-    a.Dv[(size_t)bh * M + r] = s;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) s += x[l16 + 16 * u] * y[l16 + 16 * u];
+    s = sum16(s);
+    if (l16 == 0) a.Dv[(size_t)bh * M + r] = s;
   }
 }
 
@@ -1040,9 +1129,15 @@ __global__ __launch_bounds__(1024) void k_bwd_wsum(BwdArgs a) {
   const int B = a.BH / a.H, cnt = B * a.ncv;
   if (j < K) {
     float s = 0.f;
-    for (int i = p; i < cnt; i += 8) {
-      const int b = i / a.ncv, ch = i % a.ncv;
-      s += a.pconv[((size_t)(b * a.H + h) * a.ncv + ch) * K + j];
+    for (int i0 = p; i0 < cnt; i0 += 64) {
+      float x[8];  // eight loads in flight, added in order
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + 8 * u, b = i / a.ncv, ch = i % a.ncv;
+        x[u] = i < cnt ? a.pconv[((size_t)(b * a.H + h) * a.ncv + ch) * K + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
     }
     ps[p][j] = s;
   }

@@ -235,6 +235,29 @@ int get_workspace(hipStream_t st, size_t bytes, Workspace** out) {
   return NYS_OK;
 }
 
+// A side stream per device, for work that can run beside the call's own
+// stream (forked from it and joined back with events, so the caller sees one
+// ordered sequence).  Default priority; non-blocking with respect to the
+// null stream.  Guarded by g_mu.
+struct Side {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::map<int, Side> g_side;
+
+int get_side(Side** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  Side& s = g_side[dev];
+  if (s.st == nullptr) {
+    HIP_TRY(hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&s.fork, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&s.join, hipEventDisableTiming));
+  }
+  *out = &s;
+  return NYS_OK;
+}
+
 template <typename T>
 T* at(Workspace* w, size_t off) {
   return reinterpret_cast<T*>(w->buf + off);
@@ -877,20 +900,30 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.n_iter = n_iter;
   a.init_option = init_option;
   a.s4 = 1.0f / sqrtf(sqrtf((float)D));
-  if (conv_w != nullptr) {
-    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
-    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
-    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
-                   (uint32_t)dl, st, a));
-    if (dconv_w != nullptr) {
-      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
-      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)cl, st, a));
-    }
-  }
   constexpr int tl = BwdTokLayout<M, D>::BYTES;
   HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
   HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
                  st, a));
+  // The conv's backward needs only dout, v and the weights.  It runs on the
+  // side stream beside the per-head chain (k_bwd_mm1, k_bwd_mm2: one
+  // workgroup per head, so most CUs are free meanwhile) and joins back
+  // before the key pass, which adds its part of dv.
+  Side* sd = nullptr;
+  if (conv_w != nullptr) {
+    rc = get_side(&sd);
+    if (rc != NYS_OK) return rc;
+    HIP_TRY(hipEventRecord(sd->fork, st));
+    HIP_TRY(hipStreamWaitEvent(sd->st, sd->fork, 0));
+    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
+                   (uint32_t)dl, sd->st, a));
+    if (dconv_w != nullptr) {
+      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)cl, sd->st, a));
+    }
+    HIP_TRY(hipEventRecord(sd->join, sd->st));
+  }
   constexpr int ml = bwd_mm_lds_bytes<M, D>();
   if constexpr (M == 64) {
     HIP_TRY(allow_lds(k_bwd_mm1_64<D>, BWD_MM64_LDS));
@@ -901,6 +934,7 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   }
   HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
   HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  if (sd != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
   constexpr int kl = BwdKeyLayout<M, D>::BYTES;
   HIP_TRY(allow_lds(k_bwd_key<IO, M, D>, kl));
   HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M, D>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
@@ -1200,6 +1234,12 @@ __attribute__((visibility("default"))) void nystrom_release(void) {
     if (kv.second.buf) (void)hipFree(kv.second.buf);
   }
   g_ws.clear();
+  for (auto& kv : g_side) {
+    (void)hipStreamDestroy(kv.second.st);
+    (void)hipEventDestroy(kv.second.fork);
+    (void)hipEventDestroy(kv.second.join);
+  }
+  g_side.clear();
   std::lock_guard<std::mutex> lk2(g_lt_mu);
   for (auto& kv : g_lt_ws) {
     if (kv.second.buf) (void)hipFree(kv.second.buf);
