@@ -312,6 +312,313 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// Token pass on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), for
+// D <= 64 and M * D <= 64 * 64 (the LDS tiles and register accumulators
+// grow with both).  Float32 operands are split hi + lo (products hi*hi +
+// hi*lo + lo*hi, relative error about 2^-16); q and dout rows of bf16 I/O
+// are exact bf16, so their products take two passes.  Each wave works alone
+// on 32-token steps (steps wave, wave + 4, ... of the workgroup's chunk):
+//   S = q Kt^T (then * d^-1/4) and dF = dout W^T for its two 16-token
+//   tiles (q, dout rows staged in the wave's own LDS area; Kt, W staged
+//   once per workgroup), the row softmax, dS = F (dF - D_t);
+//   dW += F^T dout and dKt += dS^T q over the 32 tokens: the contraction
+//   runs over tokens in the paired k order, which is exactly what the two
+//   tiles' C registers hold, so F and dS enter as A operands straight from
+//   registers and dout, q as B operands by transposed LDS reads;
+//   dQs = dS Kt: dS^T goes to the wave's LDS tile, A by transposed reads.
+// dW and dKt stay in registers over all of a wave's steps; at the end the
+// four waves' sums are added in wave order and written as the chunk's
+// partials.  No workgroup barrier inside the token loop.
+constexpr int BWD_T2_CT = 1024;  // tokens per workgroup
+
+__host__ __device__ constexpr bool bwd_tok2(int M, int D) { return D <= 64 && M * D <= 64 * 64; }
+// tokens per token-pass workgroup (the chunk of one dW / dKt partial)
+__host__ __device__ constexpr int bwd_tok_chunk(int M, int D) { return bwd_tok2(M, D) ? BWD_T2_CT : BWD_CT; }
+
+template <typename IO, int M, int D>
+struct BwdTok2Layout {
+  static constexpr int NSQ = sizeof(IO) == 2 ? 1 : 2;  // bf16 planes of the staged q / dout rows
+  static constexpr int KLD = D + 8;                    // element row stride of Kt, W, q, dout tiles
+  static constexpr int SLD = 32 + 4;                   // element row stride of the dS^T tile
+  // offsets in bf16 elements
+  static constexpr int KT = 0;                    // Kt hi, lo planes [M][KLD]
+  static constexpr int WT = KT + 2 * M * KLD;     // W hi, lo
+  static constexpr int WAVE0 = WT + 2 * M * KLD;  // per-wave areas
+  static constexpr int QW = 0;                    // q rows [32][KLD], NSQ planes
+  static constexpr int DW = QW + NSQ * 32 * KLD;  // dout rows
+  static constexpr int SW = DW + NSQ * 32 * KLD;  // dS^T hi, lo [M][SLD]
+  static constexpr int PER_WAVE = SW + 2 * M * SLD;
+  static constexpr int BYTES = 2 * (WAVE0 + 4 * PER_WAVE);
+  static_assert(BYTES <= 160 * 1024, "k_bwd_tok2 LDS");
+  static_assert(4 * M * D <= BYTES, "the epilogue sums [M][D] floats in LDS");
+};
+
+// N consecutive elements of one I/O row, held in registers between a global
+// load and its LDS store (bf16: raw bits, stored as the exact hi plane;
+// float32: split into hi and lo planes at the store).
+template <typename IO, int N>
+struct RowBuf;
+template <int N>
+struct RowBuf<u16, N> {
+  uint4 v[N / 8];
+  __device__ __forceinline__ void load(const u16* p, bool ok) {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) v[i] = ok ? *reinterpret_cast<const uint4*>(p + 8 * i) : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ void store(__bf16* hi, __bf16*) const {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) *reinterpret_cast<uint4*>(hi + 8 * i) = v[i];
+  }
+};
+template <int N>
+struct RowBuf<float, N> {
+  float4 v[N / 4];
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i)
+      v[i] = ok ? *reinterpret_cast<const float4*>(p + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ __forceinline__ void store(__bf16* hi, __bf16* lo) const {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const float x[8] = {v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w,
+                          v[2 * i + 1].x, v[2 * i + 1].y, v[2 * i + 1].z, v[2 * i + 1].w};
+      const Frag2 f = split8(x);
+      *reinterpret_cast<bf16x8*>(hi + 8 * i) = f.hi;
+      *reinterpret_cast<bf16x8*>(lo + 8 * i) = f.lo;
+    }
+  }
+};
+
+// B operand of rows k0 .. k0 + 3 and k1 .. k1 + 3 (element e < 4: row k0 + e,
+// e >= 4: row k1 + e - 4) and column col0 + lane % 16 of a row-major bf16
+// tile (row stride ld), by two transposed reads.
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* X, int ld, int k0, int k1, int col0) {
+  const int c16 = threadIdx.x & 15;
+  const int off = (c16 >> 2) * ld + col0 + 4 * (c16 & 3);
+  return cat44(lds_read_tr(X + k0 * ld + off), lds_read_tr(X + k1 * ld + off));
+}
+
+// grid (ceil(n / BWD_T2_CT), BH), block 256, dynamic LDS BwdTok2Layout::BYTES.
+template <typename IO, int M, int D>
+__global__ __launch_bounds__(256) void k_bwd_tok2(BwdArgs a) {
+  extern __shared__ __align__(16) __bf16 t2_lds[];
+  using Ly = BwdTok2Layout<IO, M, D>;
+  constexpr int NSQ = Ly::NSQ, KLD = Ly::KLD, SLD = Ly::SLD;
+  constexpr int TM = M / 16, CT = D / 16, KD = D / 32, KM = M / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int t0 = chunk * BWD_T2_CT, t1 = min(a.n, t0 + BWD_T2_CT);
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
+  __bf16* const Kh = t2_lds + Ly::KT;
+  __bf16* const Kl = Kh + M * KLD;
+  __bf16* const Wh = t2_lds + Ly::WT;
+  __bf16* const Wl = Wh + M * KLD;
+  __bf16* const wb = t2_lds + Ly::WAVE0 + wave * Ly::PER_WAVE;
+  __bf16* const Qp = wb + Ly::QW;  // plane p at Qp + p * 32 * KLD
+  __bf16* const Dp = wb + Ly::DW;
+  __bf16* const Sh = wb + Ly::SW;
+  __bf16* const Sl = Sh + M * SLD;
+
+  // Kt and W (float32 [M][D]) as bf16 hi / lo planes
+  for (int i = threadIdx.x; i < M * D / 8; i += 256) {
+    const int r = i / (D / 8), c = 8 * (i % (D / 8));
+    float x[8];
+    IOTraits<float>::load8(a.kt + ((size_t)bh * M + r) * D + c, x);
+    const Frag2 fk = split8(x);
+    *reinterpret_cast<bf16x8*>(Kh + r * KLD + c) = fk.hi;
+    *reinterpret_cast<bf16x8*>(Kl + r * KLD + c) = fk.lo;
+    IOTraits<float>::load8(a.W + ((size_t)bh * M + r) * D + c, x);
+    const Frag2 fw = split8(x);
+    *reinterpret_cast<bf16x8*>(Wh + r * KLD + c) = fw.hi;
+    *reinterpret_cast<bf16x8*>(Wl + r * KLD + c) = fw.lo;
+  }
+
+  // staging lanes: token lane / 2 of the step, channels (lane % 2) D / 2 ..
+  const int sr = lane >> 1, sc = (lane & 1) * (D / 2);
+  const int nsteps = (t1 - t0 + 31) / 32;
+  RowBuf<IO, D / 2> bq, bd;
+  auto fetch = [&](int step) {
+    const int tok = t0 + 32 * step + sr;
+    const bool ok = tok < t1;
+    const size_t o = (size_t)(ok ? tok : t0) * D + sc;
+    bq.load(Q + o, ok);
+    bd.load(DO + o, ok);
+  };
+  if (wave < nsteps) fetch(wave);
+  f32x4 accW[TM][CT], accK[TM][CT];
+#pragma unroll
+  for (int jt = 0; jt < TM; ++jt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) accW[jt][ct] = accK[jt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // Kt, W staged
+
+  for (int step = wave; step < nsteps; step += 4) {
+    const int ts = t0 + 32 * step;
+    // this step's rows into the wave's area (its reads of the last step are
+    // done: a wave's LDS accesses complete in order), then the next fetch
+    bq.store(Qp + sr * KLD + sc, Qp + 32 * KLD + sr * KLD + sc);
+    bd.store(Dp + sr * KLD + sc, Dp + 32 * KLD + sr * KLD + sc);
+    if (step + 4 < nsteps) fetch(step + 4);
+
+    // S = q Kt^T and dF = dout W^T: C(token 16 rt + 4g + r, landmark 16 jt + c16)
+    f32x4 s[2][TM], df[2][TM];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      Frag2 qa[KD], da[KD];
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) {
+        const int o = (16 * rt + c16) * KLD + 32 * ks + 8 * g;
+        qa[ks].hi = *reinterpret_cast<const bf16x8*>(Qp + o);
+        da[ks].hi = *reinterpret_cast<const bf16x8*>(Dp + o);
+        if constexpr (NSQ == 2) {
+          qa[ks].lo = *reinterpret_cast<const bf16x8*>(Qp + 32 * KLD + o);
+          da[ks].lo = *reinterpret_cast<const bf16x8*>(Dp + 32 * KLD + o);
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) {
+        f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f}, cd = cs;
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+          const int o = (16 * jt + c16) * KLD + 32 * ks + 8 * g;
+          const bf16x8 kh = *reinterpret_cast<const bf16x8*>(Kh + o);
+          const bf16x8 kl = *reinterpret_cast<const bf16x8*>(Kl + o);
+          const bf16x8 wh = *reinterpret_cast<const bf16x8*>(Wh + o);
+          const bf16x8 wl = *reinterpret_cast<const bf16x8*>(Wl + o);
+          cs = mfma(qa[ks].hi, kh, cs);
+          cs = mfma(qa[ks].hi, kl, cs);
+          cd = mfma(da[ks].hi, wh, cd);
+          cd = mfma(da[ks].hi, wl, cd);
+          if constexpr (NSQ == 2) {
+            cs = mfma(qa[ks].lo, kh, cs);
+            cd = mfma(da[ks].lo, wh, cd);
+          }
+        }
+        s[rt][jt] = cs * a.s4;
+        df[rt][jt] = cd;
+        if (16 * jt + c16 >= a.mr) s[rt][jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+    }
+    // row softmax F and dS = F (dF - D_t), in place of s and df
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) mx = fmaxf(mx, s[rt][jt][r]);
+        mx = max16(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) {
+          s[rt][jt][r] = __expf(s[rt][jt][r] - mx);
+          sum += s[rt][jt][r];
+        }
+        const float inv = 1.0f / sum16(sum);
+        float dt = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) {
+          s[rt][jt][r] *= inv;
+          dt += s[rt][jt][r] * df[rt][jt][r];
+        }
+        dt = sum16(dt);
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) df[rt][jt][r] = s[rt][jt][r] * (df[rt][jt][r] - dt);
+      }
+    // dW += F^T dout, dKt += dS^T q over the step's 32 tokens (paired k order)
+#pragma unroll
+    for (int jt = 0; jt < TM; ++jt) {
+      const float fx[8] = {s[0][jt][0], s[0][jt][1], s[0][jt][2], s[0][jt][3],
+                           s[1][jt][0], s[1][jt][1], s[1][jt][2], s[1][jt][3]};
+      const float sx[8] = {df[0][jt][0], df[0][jt][1], df[0][jt][2], df[0][jt][3],
+                           df[1][jt][0], df[1][jt][1], df[1][jt][2], df[1][jt][3]};
+      const Frag2 fa = split8(fx), sa = split8(sx);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 dbh = tr_frag(Dp, KLD, 4 * g, 16 + 4 * g, 16 * ct);
+        const bf16x8 qbh = tr_frag(Qp, KLD, 4 * g, 16 + 4 * g, 16 * ct);
+        accW[jt][ct] = mfma(fa.hi, dbh, accW[jt][ct]);
+        accW[jt][ct] = mfma(fa.lo, dbh, accW[jt][ct]);
+        accK[jt][ct] = mfma(sa.hi, qbh, accK[jt][ct]);
+        accK[jt][ct] = mfma(sa.lo, qbh, accK[jt][ct]);
+        if constexpr (NSQ == 2) {
+          accW[jt][ct] = mfma(fa.hi, tr_frag(Dp + 32 * KLD, KLD, 4 * g, 16 + 4 * g, 16 * ct), accW[jt][ct]);
+          accK[jt][ct] = mfma(sa.hi, tr_frag(Qp + 32 * KLD, KLD, 4 * g, 16 + 4 * g, 16 * ct), accK[jt][ct]);
+        }
+      }
+    }
+    // dQs = dS Kt: dS^T (hi, lo) into the wave's tile, then A by transposed reads
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int jt = 0; jt < TM; ++jt) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          __bf16 x, y;
+          split1(df[rt][jt][r], x, y);
+          h[r] = x;
+          l[r] = y;
+        }
+        const int o = (16 * jt + c16) * SLD + 16 * rt + 4 * g;
+        *reinterpret_cast<bf16x4*>(Sh + o) = h;
+        *reinterpret_cast<bf16x4*>(Sl + o) = l;
+      }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KM; ++kk) {
+          const int k0 = 32 * kk + 8 * g;
+          Frag2 sa, kb;
+          sa.hi = tr_frag(Sh, SLD, k0, k0 + 4, 16 * rt);
+          sa.lo = tr_frag(Sl, SLD, k0, k0 + 4, 16 * rt);
+          kb.hi = tr_frag(Kh, KLD, k0, k0 + 4, 16 * ct);
+          kb.lo = tr_frag(Kl, KLD, k0, k0 + 4, 16 * ct);
+          c = mma<3>(sa, kb, c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = ts + 16 * rt + 4 * g + r;
+          if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * D + 16 * ct + c16] = c[r];
+        }
+      }
+  }
+
+  // the four waves' sums, added in wave order in LDS ([M][D] floats), then
+  // written as the chunk's partials (dKt scaled by d^-1/4 here)
+  float* const red = reinterpret_cast<float*>(t2_lds);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();  // LDS free (token loop done) / previous pass stored
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float* const p = red + (16 * jt + 4 * g + r) * D + 16 * ct + c16;
+              const float v = pass == 0 ? accW[jt][ct][r] : a.s4 * accK[jt][ct][r];
+              *p = w == 0 ? v : *p + v;
+            }
+      }
+      __syncthreads();
+    }
+    float* const dst = (pass == 0 ? a.pw : a.pk) + ((size_t)bh * a.nct + chunk) * M * D;
+    for (int i = 4 * threadIdx.x; i < M * D; i += 4 * 256)
+      *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(red + i);
+  }
+}
+
+// ---------------------------------------------------------------------------
 constexpr int BWD_MM_NT = 1024;  // threads of the per-head kernels (16 waves)
 
 // LDS barrier without the global-memory drain of __syncthreads(): the

@@ -817,7 +817,8 @@ struct BwdPlan {
 
 BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   BwdPlan b{};
-  b.nct = (p.n + BWD_CT - 1) / BWD_CT;
+  const int ct = bwd_tok_chunk(p.m, p.D);
+  b.nct = (p.n + ct - 1) / ct;
   b.nck = (p.n + BWD_CK - 1) / BWD_CK;
   b.ncv = (p.n + BWD_CV - 1) / BWD_CV;
   b.mats = bwd_mm_mats(n_iter);
@@ -900,10 +901,16 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.n_iter = n_iter;
   a.init_option = init_option;
   a.s4 = 1.0f / sqrtf(sqrtf((float)D));
-  constexpr int tl = BwdTokLayout<M, D>::BYTES;
-  HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
-  HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
-                 st, a));
+  if constexpr (bwd_tok2(M, D)) {
+    constexpr int tl = BwdTok2Layout<IO, M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_tok2<IO, M, D>, tl));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok2<IO, M, D>, dim3(bp.nct, p.BH), dim3(256), (uint32_t)tl, st, a));
+  } else {
+    constexpr int tl = BwdTokLayout<M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
+                   st, a));
+  }
   // The conv's backward needs only dout, v and the weights.  It runs on the
   // side stream beside the per-head chain (k_bwd_mm1, k_bwd_mm2: one
   // workgroup per head, so most CUs are free meanwhile) and joins back
