@@ -1258,6 +1258,289 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key pass on the bf16 matrix cores, for the shapes of k_bwd_tok2 (split
+// hi / lo operands; k and v rows of bf16 I/O are exact).  Each wave works
+// alone on 32-key steps (steps wave, wave + 4, ... of the chunk):
+//   S = Qt Ks^T and dB = dBV v^T as C tiles (landmark 16 it + 4g + r, key
+//   16 kt + lane % 16), B = exp2(S log2 e - lse) on kept keys, dS = B (dB -
+//   D_i) (no cross-lane work: B's normalisers are stored);
+//   dv = B^T dBV and dk = dS^T Qt: the contraction runs over landmarks in
+//   the paired k order (two stacked landmark tiles), so B and dS enter as A
+//   operands from registers, dBV and Qt as B operands by transposed reads;
+//   dQt += dS Ks: dS^T goes to the wave's LDS tile, A by transposed reads,
+//   summed over all of the wave's steps in registers; the four waves' sums
+//   are added in wave order at the end.
+constexpr int BWD_K2_CK = 1024;  // keys per workgroup
+
+__host__ __device__ constexpr int bwd_key_chunk(int M, int D) { return bwd_tok2(M, D) ? BWD_K2_CK : BWD_CK; }
+
+template <typename IO, int M, int D>
+struct BwdKey2Layout {
+  static constexpr int NSK = sizeof(IO) == 2 ? 1 : 2;  // bf16 planes of the staged k / v rows
+  static constexpr int KLD = D + 8;                    // element row stride of Qt, dBV, k, v tiles
+  static constexpr int SLD = M + 8;                    // element row stride of the dS^T tile
+  static constexpr int QT = 0;                    // Qt hi, lo [M][KLD]
+  static constexpr int DB = QT + 2 * M * KLD;     // dBV hi, lo
+  static constexpr int WAVE0 = DB + 2 * M * KLD;  // per-wave areas
+  static constexpr int KW = 0;                    // k rows [32][KLD], NSK planes
+  static constexpr int VW = KW + NSK * 32 * KLD;  // v rows
+  static constexpr int SW = VW + NSK * 32 * KLD;  // dS^T hi, lo [32][SLD]
+  static constexpr int PER_WAVE = SW + 2 * 32 * SLD;
+  static constexpr int BYTES = 2 * (WAVE0 + 4 * PER_WAVE);
+  static_assert(BYTES <= 160 * 1024, "k_bwd_key2 LDS");
+  static_assert(4 * M * D <= BYTES, "the epilogue sums [M][D] floats in LDS");
+};
+
+// grid (ceil(n / BWD_K2_CK), BH), block 256, dynamic LDS BwdKey2Layout::BYTES.
+template <typename IO, int M, int D>
+__global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
+  extern __shared__ __align__(16) __bf16 k2_lds[];
+  using Ly = BwdKey2Layout<IO, M, D>;
+  constexpr int NSK = Ly::NSK, KLD = Ly::KLD, SLD = Ly::SLD;
+  constexpr int TM = M / 16, CT = D / 16, KD = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x, b = bh / a.H;
+  const int k0c = chunk * BWD_K2_CK, k1 = min(a.n, k0c + BWD_K2_CK);
+  const IO* Kg = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
+  const IO* Vg = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
+  const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
+  const float* dKt = a.dKt + (size_t)bh * M * D;
+  __bf16* const Qh = k2_lds + Ly::QT;
+  __bf16* const Ql = Qh + M * KLD;
+  __bf16* const Bh = k2_lds + Ly::DB;
+  __bf16* const Bl = Bh + M * KLD;
+  __bf16* const wb = k2_lds + Ly::WAVE0 + wave * Ly::PER_WAVE;
+  __bf16* const Kp = wb + Ly::KW;  // plane p at Kp + p * 32 * KLD
+  __bf16* const Vp = wb + Ly::VW;
+  __bf16* const Sh = wb + Ly::SW;
+  __bf16* const Sl = Sh + 32 * SLD;
+
+  // Qt and dBV (float32 [M][D]) as bf16 hi / lo planes
+  for (int i = threadIdx.x; i < M * D / 8; i += 256) {
+    const int r = i / (D / 8), c = 8 * (i % (D / 8));
+    float x[8];
+    IOTraits<float>::load8(a.qt + ((size_t)bh * M + r) * D + c, x);
+    const Frag2 fq = split8(x);
+    *reinterpret_cast<bf16x8*>(Qh + r * KLD + c) = fq.hi;
+    *reinterpret_cast<bf16x8*>(Ql + r * KLD + c) = fq.lo;
+    IOTraits<float>::load8(a.dBV + ((size_t)bh * M + r) * D + c, x);
+    const Frag2 fb = split8(x);
+    *reinterpret_cast<bf16x8*>(Bh + r * KLD + c) = fb.hi;
+    *reinterpret_cast<bf16x8*>(Bl + r * KLD + c) = fb.lo;
+  }
+  // the lane's rows 16 it + 4g + r: B's log2 normalisers and D_i
+  float lse[TM][4], dv_i[TM][4];
+#pragma unroll
+  for (int it = 0; it < TM; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * it + 4 * g + r;
+      lse[it][r] = a.lse[(size_t)bh * M + i];
+      dv_i[it][r] = a.Dv[(size_t)bh * M + i];
+    }
+
+  const int sr = lane >> 1, sc = (lane & 1) * (D / 2);
+  const int nsteps = (k1 - k0c + 31) / 32;
+  RowBuf<IO, D / 2> bk, bv;
+  // per step, also the lane's mask bits, conv part of dv and dKt[segment]
+  // elements (C layout: key 16 kt + 4g + r, channel 16 ct + c16), fetched a
+  // step ahead with the k and v rows
+  bool pkeep[2];
+  float pdvc[2][4][CT], pdkt[2][4][CT];
+  auto fetch = [&](int step) {
+    const int ks = k0c + 32 * step;
+    {
+      const int key = ks + sr;
+      const bool ok = key < k1;
+      const size_t o = (size_t)(ok ? key : k0c) * D + sc;
+      bk.load(Kg + o, ok);
+      bv.load(Vg + o, ok);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = ks + 16 * kt + c16;
+      pkeep[kt] = key < k1 && (mask == nullptr || mask[key] != 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = ks + 16 * kt + 4 * g + r;
+        const bool ok = kr < k1;
+        const int seg = (ok ? kr : k0c) / a.L;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int ch = 16 * ct + c16;
+          pdvc[kt][r][ct] = (ok && a.dvc != nullptr) ? a.dvc[((size_t)bh * a.n + kr) * D + ch] : 0.f;
+          pdkt[kt][r][ct] = dKt[(size_t)seg * D + ch];
+        }
+      }
+    }
+  };
+  if (wave < nsteps) fetch(wave);
+  f32x4 accQ[TM][CT];
+#pragma unroll
+  for (int it = 0; it < TM; ++it)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) accQ[it][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float inv_l = 1.0f / (float)a.L;
+  __syncthreads();  // Qt, dBV staged
+
+  for (int step = wave; step < nsteps; step += 4) {
+    const int ks0 = k0c + 32 * step;
+    bk.store(Kp + sr * KLD + sc, Kp + 32 * KLD + sr * KLD + sc);
+    bv.store(Vp + sr * KLD + sc, Vp + 32 * KLD + sr * KLD + sc);
+    // this step's prefetched values, then the next step's fetch
+    bool keep[2];
+    float cdvc[2][4][CT], cdkt[2][4][CT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      keep[kt] = pkeep[kt];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          cdvc[kt][r][ct] = pdvc[kt][r][ct];
+          cdkt[kt][r][ct] = pdkt[kt][r][ct];
+        }
+    }
+    if (step + 4 < nsteps) fetch(step + 4);
+    // S = Qt k^T (Qt carries d^-1/4; k gets it here) and dB = dBV v^T
+    f32x4 s[TM][2], db[TM][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      Frag2 kb[KD], vb[KD];
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) {
+        const int o = (16 * kt + c16) * KLD + 32 * ks + 8 * g;
+        kb[ks].hi = *reinterpret_cast<const bf16x8*>(Kp + o);
+        vb[ks].hi = *reinterpret_cast<const bf16x8*>(Vp + o);
+        if constexpr (NSK == 2) {
+          kb[ks].lo = *reinterpret_cast<const bf16x8*>(Kp + 32 * KLD + o);
+          vb[ks].lo = *reinterpret_cast<const bf16x8*>(Vp + 32 * KLD + o);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < TM; ++it) {
+        f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f}, cd = cs;
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+          const int o = (16 * it + c16) * KLD + 32 * ks + 8 * g;
+          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(Qh + o);
+          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(Ql + o);
+          const bf16x8 bh_ = *reinterpret_cast<const bf16x8*>(Bh + o);
+          const bf16x8 bl_ = *reinterpret_cast<const bf16x8*>(Bl + o);
+          cs = mfma(qh, kb[ks].hi, cs);
+          cs = mfma(ql, kb[ks].hi, cs);
+          cd = mfma(bh_, vb[ks].hi, cd);
+          cd = mfma(bl_, vb[ks].hi, cd);
+          if constexpr (NSK == 2) {
+            cs = mfma(qh, kb[ks].lo, cs);
+            cd = mfma(bh_, vb[ks].lo, cd);
+          }
+        }
+        // B and dS = B (dB - D_i), in place of s and db
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float bb = keep[kt] ? exp2f(cs[r] * a.s4 * LOG2E - lse[it][r]) : 0.f;
+          s[it][kt][r] = bb;
+          db[it][kt][r] = bb * (cd[r] - dv_i[it][r]);
+        }
+      }
+    }
+    // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[segment] / L):
+    // C(key 16 kt + 4g + r, channel 16 ct + c16), landmarks in the paired k order
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 cv[CT], ck[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) cv[ct] = ck[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < TM / 2; ++p) {
+        const float bx[8] = {s[2 * p][kt][0], s[2 * p][kt][1], s[2 * p][kt][2], s[2 * p][kt][3],
+                             s[2 * p + 1][kt][0], s[2 * p + 1][kt][1], s[2 * p + 1][kt][2], s[2 * p + 1][kt][3]};
+        const float sx[8] = {db[2 * p][kt][0], db[2 * p][kt][1], db[2 * p][kt][2], db[2 * p][kt][3],
+                             db[2 * p + 1][kt][0], db[2 * p + 1][kt][1], db[2 * p + 1][kt][2], db[2 * p + 1][kt][3]};
+        const Frag2 ba = split8(bx), sa = split8(sx);
+        const int i0 = 32 * p + 4 * g, i1 = i0 + 16;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Frag2 dbv, qt;
+          dbv.hi = tr_frag(Bh, KLD, i0, i1, 16 * ct);
+          dbv.lo = tr_frag(Bl, KLD, i0, i1, 16 * ct);
+          qt.hi = tr_frag(Qh, KLD, i0, i1, 16 * ct);
+          qt.lo = tr_frag(Ql, KLD, i0, i1, 16 * ct);
+          cv[ct] = mma<3>(ba, dbv, cv[ct]);
+          ck[ct] = mma<3>(sa, qt, ck[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = ks0 + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
+          if (key >= k1) continue;
+          const size_t o = ((size_t)bh * a.n + key) * D + ch;
+          io_put(reinterpret_cast<IO*>(a.dv) + o, cv[ct][r] + cdvc[kt][r][ct]);
+          io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * (ck[ct][r] + cdkt[kt][r][ct] * inv_l));
+        }
+    }
+    // dQt += dS k (times d^-1/4 at the end): dS^T (hi, lo) into the wave's
+    // tile [key][landmark], A by transposed reads (k = key, 8g + e)
+#pragma unroll
+    for (int it = 0; it < TM; ++it)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          __bf16 x, y;
+          split1(db[it][kt][r], x, y);
+          h[r] = x;
+          l[r] = y;
+        }
+        const int o = (16 * kt + c16) * SLD + 16 * it + 4 * g;
+        *reinterpret_cast<bf16x4*>(Sh + o) = h;
+        *reinterpret_cast<bf16x4*>(Sl + o) = l;
+      }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      bf16x8 kbh = tr_frag(Kp, KLD, 8 * g, 8 * g + 4, 16 * ct), kbl;
+      if constexpr (NSK == 2) kbl = tr_frag(Kp + 32 * KLD, KLD, 8 * g, 8 * g + 4, 16 * ct);
+#pragma unroll
+      for (int it = 0; it < TM; ++it) {
+        const bf16x8 sh = tr_frag(Sh, SLD, 8 * g, 8 * g + 4, 16 * it);
+        const bf16x8 sl = tr_frag(Sl, SLD, 8 * g, 8 * g + 4, 16 * it);
+        accQ[it][ct] = mfma(sh, kbh, accQ[it][ct]);
+        accQ[it][ct] = mfma(sl, kbh, accQ[it][ct]);
+        if constexpr (NSK == 2) accQ[it][ct] = mfma(sh, kbl, accQ[it][ct]);
+      }
+    }
+  }
+
+  // the four waves' sums in wave order, then the chunk's partial of dQt
+  float* const red = reinterpret_cast<float*>(k2_lds);
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int it = 0; it < TM; ++it)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* const p = red + (16 * it + 4 * g + r) * D + 16 * ct + c16;
+            const float v = a.s4 * accQ[it][ct][r];
+            *p = w == 0 ? v : *p + v;
+          }
+    }
+    __syncthreads();
+  }
+  float* const dst = a.pq + ((size_t)bh * a.nck + chunk) * M * D;
+  for (int i = 4 * threadIdx.x; i < M * D; i += 4 * 256)
+    *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(red + i);
+}
+
 // dQt = dQt_A + sum of the key-chunk partials (in chunk order).
 // grid (M * D / 256, BH), block 256: one element per thread.
 template <int M, int D>

@@ -819,7 +819,8 @@ BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   BwdPlan b{};
   const int ct = bwd_tok_chunk(p.m, p.D);
   b.nct = (p.n + ct - 1) / ct;
-  b.nck = (p.n + BWD_CK - 1) / BWD_CK;
+  const int ck = bwd_key_chunk(p.m, p.D);
+  b.nck = (p.n + ck - 1) / ck;
   b.ncv = (p.n + BWD_CV - 1) / BWD_CV;
   b.mats = bwd_mm_mats(n_iter);
   const size_t BH = p.BH, M = p.m, n = p.n, D = p.D;
@@ -942,9 +943,15 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
   HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   if (sd != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
-  constexpr int kl = BwdKeyLayout<M, D>::BYTES;
-  HIP_TRY(allow_lds(k_bwd_key<IO, M, D>, kl));
-  HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M, D>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
+  if constexpr (bwd_tok2(M, D)) {
+    constexpr int kl = BwdKey2Layout<IO, M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_key2<IO, M, D>, kl));
+    HIP_TRY(launch("k_bwd_key", k_bwd_key2<IO, M, D>, dim3(bp.nck, p.BH), dim3(256), (uint32_t)kl, st, a));
+  } else {
+    constexpr int kl = BwdKeyLayout<M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_key<IO, M, D>, kl));
+    HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M, D>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
+  }
   static_assert((M * D) % 256 == 0, "k_bwd_qt: one element per thread");
   HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M, D>, dim3(M * D / 256, p.BH), dim3(256), 0, st, a));
   HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M, D>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
