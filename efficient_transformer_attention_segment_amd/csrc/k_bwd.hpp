@@ -872,9 +872,11 @@ constexpr int BWD_MM64_LDS = 4 * 9 * 64 * 68;
 // the per-head scratch in global memory and comes back one step at a time
 // (the four matrices of a step in one batch of loads), and each wave keeps
 // its 16 x 16 tile of the accumulated dA in registers.  The products and
-// their order are those of k_bwd_mm1.
+// their order are those of k_bwd_mm1.  PART 0 runs it all; PART 1 only the
+// forward iteration (the history needs only A, so it can run beside the
+// token pass); PART 2 the rest, taking Z_n from the history.
 // grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
-template <int D>
+template <int D, int PART>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
@@ -899,8 +901,10 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   float* const dW = a.dW + (size_t)bh * M * D;
   const float c = a.cscale[bh];
 
-  reduce_token_partials<M, D>(a, bh, dW);
+  if constexpr (PART != 1) reduce_token_partials<M, D>(a, bh, dW);
   lds_load(sA, LD, A, M, M);
+  if constexpr (PART == 2) lds_load(sZ, LD, Zk(a.n_iter), M, M);
+  if constexpr (PART != 2) {
   lds_sync();
   for (int i = tid; i < MM; i += NT) {
     const float z = sA[(i % M) * LD + i / M] / c;
@@ -924,6 +928,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
     float* const t = sZ;
     sZ = sG;
     sG = t;
+  }
+  if constexpr (PART == 1) return;
   }
   // dZ_n = dW BV^T and dBV = Z_n^T dW, with dW and BV staged in the dP and
   // dX slots (for D = 128, rows of D + 4 floats: dW across the dP and dX

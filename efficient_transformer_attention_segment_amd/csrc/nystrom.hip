@@ -241,7 +241,7 @@ int get_workspace(hipStream_t st, size_t bytes, Workspace** out) {
 // null stream.  Guarded by g_mu.
 struct Side {
   hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, mid = nullptr, done = nullptr;
 };
 std::map<int, Side> g_side;
 
@@ -253,6 +253,8 @@ int get_side(Side** out) {
     HIP_TRY(hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking));
     HIP_TRY(hipEventCreateWithFlags(&s.fork, hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&s.join, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&s.mid, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
   }
   *out = &s;
   return NYS_OK;
@@ -902,6 +904,24 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.n_iter = n_iter;
   a.init_option = init_option;
   a.s4 = 1.0f / sqrtf(sqrtf((float)D));
+  // Side stream: for 64 landmarks the forward half of the per-head chain
+  // (it needs only A) runs beside the token pass, which leaves CUs free;
+  // then the conv's backward (it needs only dout, v and the weights) runs
+  // beside the rest of the chain (one workgroup per head).  Both join back
+  // before the kernels that read their results.
+  constexpr bool SPLIT = M == 64;
+  Side* sd = nullptr;
+  if (SPLIT || conv_w != nullptr) {
+    rc = get_side(&sd);
+    if (rc != NYS_OK) return rc;
+    HIP_TRY(hipEventRecord(sd->fork, st));
+    HIP_TRY(hipStreamWaitEvent(sd->st, sd->fork, 0));
+  }
+  if constexpr (SPLIT) {
+    HIP_TRY(allow_lds(k_bwd_mm1_64<D, 1>, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1f", k_bwd_mm1_64<D, 1>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, sd->st, a));
+    HIP_TRY(hipEventRecord(sd->mid, sd->st));
+  }
   if constexpr (bwd_tok2(M, D)) {
     constexpr int tl = BwdTok2Layout<IO, M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok2<IO, M, D>, tl));
@@ -912,16 +932,9 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
                    st, a));
   }
-  // The conv's backward needs only dout, v and the weights.  It runs on the
-  // side stream beside the per-head chain (k_bwd_mm1, k_bwd_mm2: one
-  // workgroup per head, so most CUs are free meanwhile) and joins back
-  // before the key pass, which adds its part of dv.
-  Side* sd = nullptr;
   if (conv_w != nullptr) {
-    rc = get_side(&sd);
-    if (rc != NYS_OK) return rc;
-    HIP_TRY(hipEventRecord(sd->fork, st));
-    HIP_TRY(hipStreamWaitEvent(sd->st, sd->fork, 0));
+    HIP_TRY(hipEventRecord(sd->done, st));  // token pass done
+    HIP_TRY(hipStreamWaitEvent(sd->st, sd->done, 0));
     constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
     HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
     HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
@@ -933,16 +946,17 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     HIP_TRY(hipEventRecord(sd->join, sd->st));
   }
   constexpr int ml = bwd_mm_lds_bytes<M, D>();
-  if constexpr (M == 64) {
-    HIP_TRY(allow_lds(k_bwd_mm1_64<D>, BWD_MM64_LDS));
-    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
+  if constexpr (SPLIT) {
+    HIP_TRY(hipStreamWaitEvent(st, sd->mid, 0));
+    HIP_TRY(allow_lds(k_bwd_mm1_64<D, 2>, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64<D, 2>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
   } else {
     HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
     HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   }
   HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
   HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
-  if (sd != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
+  if (conv_w != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
   if constexpr (bwd_tok2(M, D)) {
     constexpr int kl = BwdKey2Layout<IO, M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_key2<IO, M, D>, kl));
@@ -1252,6 +1266,8 @@ __attribute__((visibility("default"))) void nystrom_release(void) {
     (void)hipStreamDestroy(kv.second.st);
     (void)hipEventDestroy(kv.second.fork);
     (void)hipEventDestroy(kv.second.join);
+    (void)hipEventDestroy(kv.second.mid);
+    (void)hipEventDestroy(kv.second.done);
   }
   g_side.clear();
   std::lock_guard<std::mutex> lk2(g_lt_mu);
