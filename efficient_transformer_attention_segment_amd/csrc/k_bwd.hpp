@@ -9,14 +9,15 @@
 // intermediates are recomputed (landmarks, A, Z, B V, W and B's row
 // normalisers come from a forward pass without the output), then, per head
 // (head size d = 32 or 64 with up to 128 landmarks, d = 128 with up to 64;
-// float32 arithmetic throughout):
+// float32 accumulation throughout):
 //
 //   k_bwd_dvconv  dv_conv = conv^T(dout) (the forward convolution with the
 //               taps reversed, on the matrix cores);
 //   k_bwd_conv  partial sums of dconv_w;
 //   k_bwd_tok   per token: F, dF = dout W^T, D_t = sum_j F dF,
 //               dS = F (dF - D_t), dQs = dS Kt; per token chunk partial
-//               sums of dW = F^T dout and dKt = dS^T Qs;
+//               sums of dW = F^T dout and dKt = dS^T Qs (k_bwd_tok2 on the
+//               bf16 matrix cores where d <= 64 and m d <= 64 * 64);
 //   k_bwd_mm1   per head: dW, dZ = dW BV^T, dBV = Z^T dW, the iteration run
 //               backwards (Z_k, X_k, X_k^2 and P_k = 13I - 15X + 7X^2 - X^3
 //               recomputed in float32 and kept), dA, and the part dc of the
@@ -30,12 +31,16 @@
 //   k_bwd_key   per key: B from the stored normalisers, dB = dBV V^T,
 //               dS_B = B (dB - D_i), dv = B^T dBV + dv_conv,
 //               dk = d^-1/4 (dS_B^T Qt + dKt[segment] / L); per key chunk
-//               partial sums of dQt_B = dS_B Ks;
+//               partial sums of dQt_B = dS_B Ks (k_bwd_key2 on the bf16
+//               matrix cores for the shapes of k_bwd_tok2);
 //   k_bwd_qt    dQt = dQt_A + sum of the dQt_B partials;
 //   k_bwd_q     dq = d^-1/4 (dQs + dQt[segment] / L);
 //   k_bwd_wsum  dconv_w = sum of its partials.
-// Every product is a float32 matrix-core product (mm16) over operands in
-// LDS; reductions run in a fixed order, so results are reproducible.
+// The per-head products and the token / key passes above 64 x 64 are
+// float32 matrix-core products (mm16) over operands in LDS; k_bwd_tok2 and
+// k_bwd_key2 use split-bf16 products (hi*hi + hi*lo + lo*hi, relative error
+// about 2^-16; exact bf16 inputs skip their lo plane), as do the conv
+// kernels.  Reductions run in a fixed order, so results are reproducible.
 #pragma once
 
 #include "common.hpp"
