@@ -869,20 +869,107 @@ __device__ __forceinline__ void lds_store(float* dst, const float* src, int ld, 
   for (int i = threadIdx.x; i < M * Mc; i += BWD_MM_NT) dst[i] = src[(i / Mc) * ld + i % Mc];
 }
 
-constexpr int BWD_MM64_LDS = 4 * 9 * 64 * 68;
+constexpr int BWD_MM64_LDS = 4 * 6 * 64 * 68;
 
-// k_bwd_mm1 for 64 landmarks with the working set resident in LDS: A, G,
-// G', dP, dX and the step's Z_k, X_k, X_k^2, P_k (then T) as nine 64 x 64
-// float32 images (row stride 68); the history Z_k, X_k, X_k^2, P_k goes to
-// the per-head scratch in global memory and comes back one step at a time
-// (the four matrices of a step in one batch of loads), and each wave keeps
-// its 16 x 16 tile of the accumulated dA in registers.  The products and
-// their order are those of k_bwd_mm1.  PART 0 runs it all; PART 1 only the
-// forward iteration (the history needs only A, so it can run beside the
-// token pass); PART 2 the rest, taking Z_n from the history.
+// The forward half of the 64-landmark per-head chain: the iteration again
+// in float32 (Z_0 = A^T / c, X = A Z, X^2, P = 13I - 15X + 7X^2 - X^3,
+// Z <- Z P / 4) with the history Z_k, X_k, X_k^2, P_k written to the
+// per-head scratch for k_bwd_mm1b64, and A's largest column sum (its first
+// column) and largest row sum.  It needs only A, so it runs beside the
+// token pass.  A, Z, X, X^2, P and a spare slot as float32 images in LDS
+// (row stride 68), 16 waves.
 // grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
-template <int D, int PART>
-__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1f64(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* const sA = bw_lds;
+  float* sZ = sA + SZ;
+  float* sG = sZ + SZ;  // spare slot
+  float* const sX = sG + SZ;
+  float* const sX2 = sX + SZ;
+  float* const sPT = sX2 + SZ;
+  const float* A = a.A + (size_t)bh * MM;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  auto Zk = [&](int k) { return S + (size_t)k * MM; };
+  auto Xk = [&](int k) { return S + (size_t)(a.n_iter + 1 + 3 * k) * MM; };
+  auto X2k = [&](int k) { return Xk(k) + MM; };
+  auto Pk = [&](int k) { return Xk(k) + 2 * MM; };
+  const float c = a.cscale[bh];
+
+  lds_load(sA, LD, A, M, M);
+  lds_sync();
+  for (int i = tid; i < MM; i += NT) {
+    const float z = sA[(i % M) * LD + i / M] / c;
+    sZ[(i / M) * LD + i % M] = z;
+    Zk(0)[i] = z;
+  }
+  for (int k = 0; k < a.n_iter; ++k) {
+    lgemm<M, M, M>(sX, LD, sA, LD, false, sZ, LD, false, 1.f, 0.f);
+    lgemm<M, M, M>(sX2, LD, sX, LD, false, sX, LD, false, 1.f, 0.f);
+    lgemm<M, M, M>(sPT, LD, sX, LD, false, sX2, LD, false, -1.f, 0.f);
+    lds_sync();
+    for (int i = tid; i < MM; i += NT) {
+      const int o = (i / M) * LD + i % M;
+      sPT[o] += (i / M == i % M ? 13.f : 0.f) - 15.f * sX[o] + 7.f * sX2[o];
+      Xk(k)[i] = sX[o];
+      X2k(k)[i] = sX2[o];
+      Pk(k)[i] = sPT[o];
+    }
+    lgemm<M, M, M>(sG, LD, sZ, LD, false, sPT, LD, false, 0.25f, 0.f);  // Z_{k+1} (into the spare slot)
+    lds_store(Zk(k + 1), sG, LD, M, M);
+    float* const t = sZ;
+    sZ = sG;
+    sG = t;
+  }
+  // A's largest column sum (the first such column) and largest row sum
+  lds_sync();
+  float* const red = sX;
+  int* const redj = reinterpret_cast<int*>(sX2);
+  float cs = -1.f, rs = 0.f;
+  int cj = 0;
+  if (tid < M) {
+    cs = 0.f;
+    for (int r = 0; r < M; ++r) cs += sA[r * LD + tid];
+    for (int j = 0; j < M; ++j) rs += sA[tid * LD + j];
+    cj = tid;
+  }
+  red[tid] = cs;
+  redj[tid] = cj;
+  __syncthreads();
+  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2 && (red[tid + s2] > red[tid] || (red[tid + s2] == red[tid] && redj[tid + s2] < redj[tid]))) {
+      red[tid] = red[tid + s2];
+      redj[tid] = redj[tid + s2];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.cmax[bh] = red[0];
+    a.cmaxj[bh] = redj[0];
+  }
+  __syncthreads();
+  red[tid] = tid < M ? rs : 0.f;
+  __syncthreads();
+  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
+    if (tid < s2) red[tid] = fmaxf(red[tid], red[tid + s2]);
+    __syncthreads();
+  }
+  if (tid == 0) a.rmax[bh] = red[0];
+}
+
+// The backward half of the 64-landmark per-head chain in float32 (float32
+// I/O): the products of k_bwd_mm1b64 on the float32 matrix cores over
+// float32 images of A, G, G', dP, dX, Z_k, X_k, X_k^2 and P_k (then T) in
+// LDS (row stride 68); the history comes back one step at a time (the four
+// matrices of a step in one batch of loads) and each wave keeps its 16 x 16
+// tile of dA in registers.  Once the iteration has converged a relative
+// error e in its products grows to about e cond(A), so float32 I/O keeps
+// float32 products here as in the forward iteration.
+// grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64B_LDS.
+constexpr int BWD_MM64B_LDS = 4 * 9 * 64 * 68;
+template <int D>
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1b64_f32(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -906,36 +993,9 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
   float* const dW = a.dW + (size_t)bh * M * D;
   const float c = a.cscale[bh];
 
-  if constexpr (PART != 1) reduce_token_partials<M, D>(a, bh, dW);
+  reduce_token_partials<M, D>(a, bh, dW);
   lds_load(sA, LD, A, M, M);
-  if constexpr (PART == 2) lds_load(sZ, LD, Zk(a.n_iter), M, M);
-  if constexpr (PART != 2) {
-  lds_sync();
-  for (int i = tid; i < MM; i += NT) {
-    const float z = sA[(i % M) * LD + i / M] / c;
-    sZ[(i / M) * LD + i % M] = z;
-    Zk(0)[i] = z;
-  }
-  for (int k = 0; k < a.n_iter; ++k) {
-    lgemm<M, M, M>(sX, LD, sA, LD, false, sZ, LD, false, 1.f, 0.f);
-    lgemm<M, M, M>(sX2, LD, sX, LD, false, sX, LD, false, 1.f, 0.f);
-    lgemm<M, M, M>(sPT, LD, sX, LD, false, sX2, LD, false, -1.f, 0.f);
-    lds_sync();
-    for (int i = tid; i < MM; i += NT) {
-      const int o = (i / M) * LD + i % M;
-      sPT[o] += (i / M == i % M ? 13.f : 0.f) - 15.f * sX[o] + 7.f * sX2[o];
-      Xk(k)[i] = sX[o];
-      X2k(k)[i] = sX2[o];
-      Pk(k)[i] = sPT[o];
-    }
-    lgemm<M, M, M>(sG, LD, sZ, LD, false, sPT, LD, false, 0.25f, 0.f);  // Z_{k+1} (G as the spare slot)
-    lds_store(Zk(k + 1), sG, LD, M, M);
-    float* const t = sZ;
-    sZ = sG;
-    sG = t;
-  }
-  if constexpr (PART == 1) return;
-  }
+  lds_load(sZ, LD, Zk(a.n_iter), M, M);
   // dZ_n = dW BV^T and dBV = Z_n^T dW, with dW and BV staged in the dP and
   // dX slots (for D = 128, rows of D + 4 floats: dW across the dP and dX
   // slots, BV across the X and X^2 slots, which the loop below reloads)
@@ -1006,46 +1066,203 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1_64(BwdArgs a) {
     }
   }
   float* const red = sX;  // free now
-  int* const redj = reinterpret_cast<int*>(sX2);
   red[tid] = part;
   __syncthreads();
   for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
     if (tid < s2) red[tid] += red[tid + s2];
     __syncthreads();
   }
-  const float dcv = -red[0] / (c * c);
-  __syncthreads();
-  float cs = -1.f, rs = 0.f;
-  int cj = 0;
-  if (tid < M) {
-    cs = 0.f;
-    for (int r = 0; r < M; ++r) cs += sA[r * LD + tid];
-    for (int j = 0; j < M; ++j) rs += sA[tid * LD + j];
-    cj = tid;
-  }
-  red[tid] = cs;
-  redj[tid] = cj;
-  __syncthreads();
-  for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
-    if (tid < s2 && (red[tid + s2] > red[tid] || (red[tid + s2] == red[tid] && redj[tid + s2] < redj[tid]))) {
-      red[tid] = red[tid + s2];
-      redj[tid] = redj[tid + s2];
+  if (tid == 0) a.dc[bh] = -red[0] / (c * c);
+}
+
+// ---------------------------------------------------------------------------
+// The backward half of the 64-landmark per-head chain on the bf16 matrix
+// cores (bf16 I/O).  Every 64 x 64 operand lives in LDS as split-bf16 hi / lo planes
+// (row-major, row stride PL_LD), so a product of two of them is six
+// v_mfma_f32_16x16x32_bf16 per 16 x 16 tile; each of the 16 waves owns one
+// output tile (it, jt) = (wave / 4, wave % 4) of every product and keeps
+// the running sums (dZ_k, dX, dA) in float32 registers.  Operand access:
+// "row" reads 8 consecutive k of a row (an operand Y, or Y^T on the right),
+// "tr" reads 8 consecutive k of a column by transposed reads (Y^T on the
+// left, Y on the right).  The history Z_k, X_k, X_k^2, P_k comes from
+// k_bwd_mm1f in float32 and is split as it is staged, one step ahead.
+constexpr int PL_LD = 64 + 8;                 // bf16 row stride of a plane
+constexpr int PL_MAT = 2 * 64 * PL_LD;        // elements of one split matrix
+constexpr int BWD_MM1B_LDS = 8 * PL_MAT * 2;  // eight split matrices (bytes)
+
+// C tile (16 it.., 16 jt..) += op(X) op(Y) over k < 64, op(X) = X (row) or
+// X^T (TX, tr), op(Y) = Y^T (row) or Y (TY, tr); planes hi at p, lo at p + 64 PL_LD.
+template <bool TX, bool TY>
+__device__ __forceinline__ f32x4 pmm(const __bf16* X, const __bf16* Y, int it, int jt, f32x4 acc) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k0 = 32 * ks + 8 * g;
+    Frag2 a, b;
+    if constexpr (TX) {
+      a.hi = tr_frag(X, PL_LD, k0, k0 + 4, 16 * it);
+      a.lo = tr_frag(X + 64 * PL_LD, PL_LD, k0, k0 + 4, 16 * it);
+    } else {
+      a.hi = *reinterpret_cast<const bf16x8*>(X + (16 * it + c16) * PL_LD + k0);
+      a.lo = *reinterpret_cast<const bf16x8*>(X + 64 * PL_LD + (16 * it + c16) * PL_LD + k0);
     }
-    __syncthreads();
+    if constexpr (TY) {
+      b.hi = tr_frag(Y, PL_LD, k0, k0 + 4, 16 * jt);
+      b.lo = tr_frag(Y + 64 * PL_LD, PL_LD, k0, k0 + 4, 16 * jt);
+    } else {
+      b.hi = *reinterpret_cast<const bf16x8*>(Y + (16 * jt + c16) * PL_LD + k0);
+      b.lo = *reinterpret_cast<const bf16x8*>(Y + 64 * PL_LD + (16 * jt + c16) * PL_LD + k0);
+    }
+    acc = mma<3>(a, b, acc);
   }
-  if (tid == 0) {
-    a.dc[bh] = dcv;
-    a.cmax[bh] = red[0];
-    a.cmaxj[bh] = redj[0];
+  return acc;
+}
+
+// The wave's C tile (rows 16 it + 4g + r, column 16 jt + c16) into a split matrix.
+__device__ __forceinline__ void put_tile(__bf16* Y, int it, int jt, f32x4 v) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    __bf16 h, l;
+    split1(v[r], h, l);
+    const int o = (16 * it + 4 * g + r) * PL_LD + 16 * jt + c16;
+    Y[o] = h;
+    Y[64 * PL_LD + o] = l;
   }
-  __syncthreads();
-  red[tid] = tid < M ? rs : 0.f;
+}
+
+// Four consecutive elements (4 threadIdx.x .. + 3 of a row-major float32
+// 64 x 64 matrix) into a split matrix.
+__device__ __forceinline__ void put4(__bf16* Y, float4 v) {
+  const int i = 4 * threadIdx.x, row = i >> 6, col = i & 63;
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  bf16x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __bf16 a, b;
+    split1(x[e], a, b);
+    h[e] = a;
+    l[e] = b;
+  }
+  *reinterpret_cast<bf16x4*>(Y + row * PL_LD + col) = h;
+  *reinterpret_cast<bf16x4*>(Y + 64 * PL_LD + row * PL_LD + col) = l;
+}
+
+// grid BH, block BWD_MM_NT, dynamic LDS BWD_MM1B_LDS.
+template <int D>
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1b64(BwdArgs a) {
+  extern __shared__ __align__(16) __bf16 pl_lds[];
+  constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
+  static_assert(4 * NT == MM, "one float4 of each matrix per thread");
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int it = wave >> 2, jt = wave & 3;
+  const float* A = a.A + (size_t)bh * MM;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  auto Zk = [&](int k) { return S + (size_t)k * MM; };
+  auto Xk = [&](int k) { return S + (size_t)(a.n_iter + 1 + 3 * k) * MM; };
+  auto X2k = [&](int k) { return Xk(k) + MM; };
+  auto Pk = [&](int k) { return Xk(k) + 2 * MM; };
+  float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
+  float* const dW = a.dW + (size_t)bh * M * D;
+  const float c = a.cscale[bh];
+  __bf16* const pA = pl_lds;
+  __bf16* const pG = pA + PL_MAT;
+  __bf16* const pdP = pG + PL_MAT;
+  __bf16* const pdX = pdP + PL_MAT;
+  __bf16* const pZ = pdX + PL_MAT;
+  __bf16* const pX = pZ + PL_MAT;
+  __bf16* const pX2 = pX + PL_MAT;
+  __bf16* const pPT = pX2 + PL_MAT;  // P_k, then T
+
+  // ---- setup in float32 (the LDS is used as float32 images first):
+  // dW, dZ_n = G = dW BV^T, dBV = Z_n^T dW
+  float* const fl = reinterpret_cast<float*>(pl_lds);
+  constexpr int LDW = D <= M ? LD : D + 4;
+  float* const sZ = fl;
+  float* const sG = sZ + SZ;
+  float* const sW = sG + SZ;
+  float* const sBV = sW + M * LDW;
+  static_assert(4 * (2 * SZ + 2 * M * LDW) <= BWD_MM1B_LDS, "setup images fit");
+  reduce_token_partials<M, D>(a, bh, dW);
+  lds_load(sZ, LD, Zk(a.n_iter), M, M);
+  lds_load(sW, LDW, dW, M, D);
+  lds_load(sBV, LDW, a.BV + (size_t)bh * M * D, M, D);
+  lgemm<M, M, D>(sG, LD, sW, LDW, false, sBV, LDW, true, 1.f, 0.f);
+  lgemm<M, D, M>(a.dBV + (size_t)bh * M * D, D, sZ, LD, true, sW, LDW, false, 1.f, 0.f);
+  lds_sync();
+  f32x4 gt;  // the wave's tile of G (float32)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gt[r] = sG[(16 * it + 4 * g + r) * LD + 16 * jt + c16];
+  // the first step's history and A, as split matrices (after every wave's
+  // read of the float32 images)
+  float4 hz = make_float4(0.f, 0.f, 0.f, 0.f), hx = hz, hx2 = hz, hp = hz;
+  const float4 av = *reinterpret_cast<const float4*>(A + 4 * tid);
+  if (a.n_iter > 0) {
+    const int k = a.n_iter - 1;
+    hz = *reinterpret_cast<const float4*>(Zk(k) + 4 * tid);
+    hx = *reinterpret_cast<const float4*>(Xk(k) + 4 * tid);
+    hx2 = *reinterpret_cast<const float4*>(X2k(k) + 4 * tid);
+    hp = *reinterpret_cast<const float4*>(Pk(k) + 4 * tid);
+  }
+  lds_sync();
+  put4(pA, av);
+  put_tile(pG, it, jt, gt);
+
+  f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = a.n_iter - 1; k >= 0; --k) {
+    lds_sync();  // the last step's reads of Z, X, X^2, T are done
+    put4(pZ, hz);
+    put4(pX, hx);
+    put4(pX2, hx2);
+    put4(pPT, hp);
+    if (k > 0) {
+      hz = *reinterpret_cast<const float4*>(Zk(k - 1) + 4 * tid);
+      hx = *reinterpret_cast<const float4*>(Xk(k - 1) + 4 * tid);
+      hx2 = *reinterpret_cast<const float4*>(X2k(k - 1) + 4 * tid);
+      hp = *reinterpret_cast<const float4*>(Pk(k - 1) + 4 * tid);
+    }
+    lds_sync();
+    const f32x4 z0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 gn = pmm<false, false>(pG, pPT, it, jt, z0) * 0.25f;  // dZ_k = G P^T / 4 ...
+    const f32x4 dp = pmm<true, true>(pZ, pG, it, jt, z0) * 0.25f;  // dP = Z^T G / 4
+    put_tile(pdP, it, jt, dp);
+    lds_sync();
+    const f32x4 t = pmm<true, true>(pX, pdP, it, jt, z0);  // T = X^T dP
+    f32x4 dx = -15.f * dp + 7.f * pmm<false, false>(pdP, pX, it, jt, z0) + 7.f * t -
+               pmm<false, false>(pdP, pX2, it, jt, z0);
+    put_tile(pPT, it, jt, t);  // P's readers (the first product) are a barrier back
+    lds_sync();
+    dx -= pmm<false, false>(pPT, pX, it, jt, z0) + pmm<true, true>(pX2, pdP, it, jt, z0);  // - T X^T - (X^2)^T dP
+    put_tile(pdX, it, jt, dx);
+    lds_sync();
+    dacc = pmm<false, false>(pdX, pZ, it, jt, dacc);  // dA += dX Z^T
+    gn = pmm<true, true>(pA, pdX, it, jt, gn);        // ... + A^T dX
+    gt = gn;
+    put_tile(pG, it, jt, gt);  // G's last readers (the two products at the top) are two barriers back
+  }
+  // Z_0 = A^T / c: dA += G^T / c (G in float32 through LDS); dc = -sum(G A^T) / c^2
+  lds_sync();
+  float* const gf = fl;  // [64][LD] float32, over the planes (all reads done)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gf[(16 * it + 4 * g + r) * LD + 16 * jt + c16] = gt[r];
+  lds_sync();
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 16 * it + 4 * g + r, col = 16 * jt + c16;
+    const float gv = gf[col * LD + row];
+    dA[row * M + col] = dacc[r] + gv / c;
+    part += gv * A[row * M + col];
+  }
+  float* const red = fl + SZ;
+  red[tid] = part;
   __syncthreads();
   for (int s2 = NT / 2; s2 > 0; s2 >>= 1) {
-    if (tid < s2) red[tid] = fmaxf(red[tid], red[tid + s2]);
+    if (tid < s2) red[tid] += red[tid + s2];
     __syncthreads();
   }
-  if (tid == 0) a.rmax[bh] = red[0];
+  if (tid == 0) a.dc[bh] = -red[0] / (c * c);
 }
 
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().  Row

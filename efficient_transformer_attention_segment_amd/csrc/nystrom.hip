@@ -918,8 +918,8 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     HIP_TRY(hipStreamWaitEvent(sd->st, sd->fork, 0));
   }
   if constexpr (SPLIT) {
-    HIP_TRY(allow_lds(k_bwd_mm1_64<D, 1>, BWD_MM64_LDS));
-    HIP_TRY(launch("k_bwd_mm1f", k_bwd_mm1_64<D, 1>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, sd->st, a));
+    HIP_TRY(allow_lds(k_bwd_mm1f64, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1f", k_bwd_mm1f64, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, sd->st, a));
     HIP_TRY(hipEventRecord(sd->mid, sd->st));
   }
   if constexpr (bwd_tok2(M, D)) {
@@ -948,8 +948,13 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   constexpr int ml = bwd_mm_lds_bytes<M, D>();
   if constexpr (SPLIT) {
     HIP_TRY(hipStreamWaitEvent(st, sd->mid, 0));
-    HIP_TRY(allow_lds(k_bwd_mm1_64<D, 2>, BWD_MM64_LDS));
-    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1_64<D, 2>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, st, a));
+    if constexpr (sizeof(IO) == 4) {
+      HIP_TRY(allow_lds(k_bwd_mm1b64_f32<D>, BWD_MM64B_LDS));
+      HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64_f32<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64B_LDS, st, a));
+    } else {
+      HIP_TRY(allow_lds(k_bwd_mm1b64<D>, BWD_MM1B_LDS));
+      HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM1B_LDS, st, a));
+    }
   } else {
     HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
     HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
