@@ -138,3 +138,31 @@ def test_backward_deterministic():
     for o in outs[1:]:
         for a_, b_ in zip(o, outs[0]):
             assert torch.equal(a_, b_)
+
+
+def test_backward_user_streams():
+    """Calls on two user streams (each with its own workspace; the library's
+    side stream forks from and joins back into the calling stream) give the
+    default stream's results bit for bit, with the calls of both streams in
+    flight together."""
+    import torch
+
+    import efficient_transformer_attention_segment_amd as nys
+    x = make_custom(2, 3, 512, 64, seed=1020, dtype="bf16", lengths=[512, 333])
+    do = to_dev(_dout(x["q"].shape, 6, "bf16"), "bf16")
+    args = [to_dev(x[n_], "bf16") for n_ in ("q", "k", "v")]
+    km, cw = to_dev(x["key_mask"], None), to_dev(x["conv_w"], None)
+    announce("backward user streams")
+    ref = nys.attention_backward(*args, do, km, cw, m=64)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(4):
+        s = s1 if i % 2 == 0 else s2
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            outs.append(nys.attention_backward(*args, do, km, cw, m=64, stream=s))
+    torch.cuda.synchronize()
+    for o in outs:
+        for a_, b_ in zip(o, ref):
+            assert torch.equal(a_, b_)
