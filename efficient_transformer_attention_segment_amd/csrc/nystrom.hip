@@ -97,6 +97,11 @@ int pow2floor(int x) {
   while (p * 2 <= x) p *= 2;
   return p;
 }
+int pow2ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
 
 // Landmark count of the kernels: the method's m rounded up to a multiple of
 // 32.  The padding landmarks are zero rows of Qt and Kt, get no weight in
@@ -116,9 +121,13 @@ Plan make_plan(int B, int H, int n, int mr, int d) {
   p.BH = B * H;
   p.L = n / mr;
   // landmark blocks: d / 8 threads per row, RS row slots per landmark, lpw
-  // landmarks per block (at most 32, which divides m)
+  // landmarks per block (at most 32, which divides m).  Eight rows per slot
+  // where segments are long; for short segments enough slots (at most the
+  // segment length) that the grid has about two blocks per CU.
   const int tpr = d / 8;
-  p.RS = std::min(256 / tpr, std::max(std::max(1, 256 / (tpr * 32)), pow2floor(std::max(1, p.L / 8))));
+  const int rs_fill =
+      std::min(pow2ceil((int)std::max(1LL, (2LL * 256 * 256) / ((long long)m * tpr * p.BH))), pow2floor(p.L));
+  p.RS = std::min(256 / tpr, std::max({1, 256 / (tpr * 32), pow2floor(std::max(1, p.L / 8)), rs_fill}));
   p.lpw = 256 / (tpr * p.RS);
   // key chunks for the B V partials: as many blocks as stay resident in one
   // round next to the pseudo-inverse blocks (two blocks per CU)
