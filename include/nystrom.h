@@ -190,7 +190,11 @@ int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const vo
  * dq, dk, dv must not overlap each other or q, k, v, dout.  Head sizes
  * d = 32, 64 and 128: the exact branch (m == n, any n) at each, the Nystrom
  * path with up to 128 landmarks at d = 32 and 64 and up to 64 at d = 128
- * (NYS_ERR_UNSUPPORTED for more).  Other errors as nystrom_attention. */
+ * (NYS_ERR_UNSUPPORTED for more).  Part of the work runs on a
+ * library-owned side stream of the device (default priority), forked from
+ * `stream` and joined back into it with events, so the call is ordered on
+ * `stream` like any other; the first call on a device creates that stream
+ * (nystrom_release destroys it).  Other errors as nystrom_attention. */
 int nystrom_attention_backward(int dtype, const void* q, const void* k, const void* v,
                                const uint8_t* key_mask, const float* conv_w,
                                int conv_kernel_size, int B, int H, int n, int d, int m,
@@ -205,8 +209,9 @@ size_t nystrom_workspace_bytes(int B, int H, int n, int d, int m);
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* nystrom_last_error(void);
 
-/* Free every cached workspace (all devices and streams).  Must not be
- * called while work the library enqueued may still be running. */
+/* Free every cached workspace (all devices and streams) and destroy the
+ * backward pass's side streams.  Must not be called while work the library
+ * enqueued may still be running. */
 void nystrom_release(void);
 
 /* Test hook: run the Nystrom path (m != n) like nystrom_attention[_bf16]
