@@ -269,9 +269,15 @@ __device__ __forceinline__ void vgroup_load(const u16* V, long long st, int n, i
 __device__ __forceinline__ void vgroup_store(const VGroup& b, int G, __bf16* ring) {
   const int t = threadIdx.x;
   const int r = OUTS_UNIT * G + (t >> 2);
+  // rows with bit 3 set keep the two 8-byte halves of each chunk swapped, so
+  // that the transposed reads of rows r and r + 8 (lane groups 0 and 1 of
+  // one read) fall in different banks
+  const bool sw = (r >> 3) & 1;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    *reinterpret_cast<uint4*>(ring + vring_pos(r, 2 * (t & 3) + c)) = b.x[c];
+  for (int c = 0; c < 2; ++c) {
+    const uint4 v = b.x[c];
+    *reinterpret_cast<uint4*>(ring + vring_pos(r, 2 * (t & 3) + c)) = sw ? make_uint4(v.z, v.w, v.x, v.y) : v;
+  }
 }
 
 // Per-lane constants of the conv reads of the wave's tile: read (kk, half, dt)
@@ -292,7 +298,8 @@ __device__ __forceinline__ void conv_lane_init(ConvLane& cl) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const int c0 = dmap_run<true>(dt, c16 & 3);
-        cl.coff[kk][half][dt] = 8 * ((c0 >> 3) ^ (2 * (rel & 3))) + (c0 & 7);  // rel & 3 == row & 3
+        // rel & 3 == row & 3 and rel & 8 == row & 8 (rows differ from rel by a multiple of 64)
+        cl.coff[kk][half][dt] = 8 * ((c0 >> 3) ^ (2 * (rel & 3))) + ((c0 & 7) ^ (4 * ((rel >> 3) & 1)));
       }
     }
 }
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     const int rsub = lane >> 3;
     for (int c = wave; c < M / 8; c += 4) {
       const int row = 8 * c + rsub;
-      const int chunk = (lane & 7) ^ (row & 7);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
       dma16(kt + (size_t)row * HD + 8 * chunk, kt_s + 8 * c * HD);
     }
     for (int c = wave; c < 4 * KS; c += 4) dma16(wf + (size_t)c * 512 + 8 * lane, wf_s + 512 * c);
@@ -409,7 +416,8 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
       sacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_s + swz(16 * it + c16, 4 * ks + g));
+        const int kr = 16 * it + c16;  // chunks XOR-swizzled by (row / 2) % 8: 16 rows, 64 distinct banks
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_s + kr * HD + 8 * ((4 * ks + g) ^ ((kr >> 1) & 7)));
         sacc[it] = mfma(kf, q[ks], sacc[it]);
       }
     }
