@@ -230,7 +230,12 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
 // units.  48 KB of LDS at m = 64 lets three workgroups share a CU.
 //
 // Ring layout: row r has its 16-byte chunk c at chunk position c ^ (2 (r & 3)),
-// so the four rows of one transposed conv read fall on different bank halves.
+// so the four rows of one transposed conv read fall on different bank halves,
+// and rows with bit 3 set keep the two 8-byte halves of each chunk swapped,
+// so the rows r and r + 8 that two lane groups read in the same cycle fall on
+// different banks too.  The key landmarks sit in LDS with their 16-byte chunks
+// XOR-swizzled by (row / 2) % 8, which spreads the 16 rows of a fragment read
+// over all 64 banks.
 // Each lane's conv reads sit at a fixed row offset from the unit's first token,
 // so their addresses are a per-unit row term plus per-lane constants.
 
