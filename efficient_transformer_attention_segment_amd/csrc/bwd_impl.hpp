@@ -1,0 +1,320 @@
+// Backward launch sequences (Nystrom path and exact branch), shared by
+// bwd_f32.hip and bwd_bf16.hip, each of which instantiates run_backward for
+// its I/O type.  The forward stages the backward recomputes come from the
+// forward units (dispatch_m with the plan's bwd flag set).
+#pragma once
+
+#include <cmath>
+
+#include "host.hpp"
+#include "k_bwd.hpp"
+
+namespace nys {
+namespace host {
+
+// ------------------------------------------------------------ backward ---
+// Forward stages (without the output pass) into the plan's workspace, then
+// the backward kernels into the regions that follow it.
+struct BwdPlan {
+  int nct, nck, ncv, mats;
+  size_t off_dqf, off_pw, off_pk, off_pq, off_mm, off_dW, off_dBV, off_dQt, off_dKt, off_Dv, off_dc, off_cmax,
+      off_cmaxj, off_rmax, off_dvc, off_pconv, total;
+};
+
+inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
+  BwdPlan b{};
+  const int ct = bwd_tok_chunk(p.m, p.D);
+  b.nct = (p.n + ct - 1) / ct;
+  const int ck = bwd_key_chunk(p.m, p.D);
+  b.nck = (p.n + ck - 1) / ck;
+  b.ncv = (p.n + BWD_CV - 1) / BWD_CV;
+  b.mats = bwd_mm_mats(n_iter);
+  const size_t BH = p.BH, M = p.m, n = p.n, D = p.D;
+  size_t o = p.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  b.off_dqf = take(BH * n * D * 4);
+  b.off_pw = take(BH * b.nct * M * D * 4);
+  b.off_pk = take(BH * b.nct * M * D * 4);
+  b.off_pq = take(BH * b.nck * M * D * 4);
+  b.off_mm = take(BH * b.mats * M * M * 4);
+  b.off_dW = take(BH * M * D * 4);
+  b.off_dBV = take(BH * M * D * 4);
+  b.off_dQt = take(BH * M * D * 4);
+  b.off_dKt = take(BH * M * D * 4);
+  b.off_Dv = take(BH * M * 4);
+  b.off_dc = take(BH * 4);
+  b.off_cmax = take(BH * 4);
+  b.off_cmaxj = take(BH * 4);
+  b.off_rmax = take(BH * 4);
+  b.off_dvc = conv ? take(BH * n * D * 4) : 0;
+  b.off_pconv = conv ? take(BH * b.ncv * (size_t)conv_k * 4) : 0;
+  b.total = o;
+  return b;
+}
+
+template <typename IO, int M, int D>
+int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* q, const void* k, const void* v,
+                    const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option,
+                    const void* dout, void* dq, void* dk, void* dv, float* dconv_w, hipStream_t st) {
+  int rc = dispatch_m<IO, D>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, nullptr, st);
+  if (rc != NYS_OK) return rc;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.key_mask = mask;
+  a.conv_w = conv_w;
+  a.conv_k = conv_k;
+  a.qt = at<float>(w, p.off_qt);
+  a.kt = at<float>(w, p.off_kt);
+  a.A = at<float>(w, p.off_A);
+  a.BV = at<float>(w, p.off_BV);
+  a.W = at<float>(w, p.off_W);
+  a.lse = at<float>(w, p.off_lse);
+  a.cscale = at<float>(w, p.off_cscale);
+  a.dqf = at<float>(w, bp.off_dqf);
+  a.pw = at<float>(w, bp.off_pw);
+  a.pk = at<float>(w, bp.off_pk);
+  a.pq = at<float>(w, bp.off_pq);
+  a.mm = at<float>(w, bp.off_mm);
+  a.dW = at<float>(w, bp.off_dW);
+  a.dBV = at<float>(w, bp.off_dBV);
+  a.dQt = at<float>(w, bp.off_dQt);
+  a.dKt = at<float>(w, bp.off_dKt);
+  a.Dv = at<float>(w, bp.off_Dv);
+  a.dc = at<float>(w, bp.off_dc);
+  a.cmax = at<float>(w, bp.off_cmax);
+  a.cmaxj = at<int>(w, bp.off_cmaxj);
+  a.rmax = at<float>(w, bp.off_rmax);
+  a.dvc = conv_w != nullptr ? at<float>(w, bp.off_dvc) : nullptr;
+  a.pconv = conv_w != nullptr ? at<float>(w, bp.off_pconv) : nullptr;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dconv_w = dconv_w;
+  a.n = p.n;
+  a.H = p.H;
+  a.BH = p.BH;
+  a.mr = p.mr;
+  a.L = p.L;
+  a.nct = bp.nct;
+  a.nck = bp.nck;
+  a.ncv = bp.ncv;
+  a.n_iter = n_iter;
+  a.init_option = init_option;
+  a.s4 = 1.0f / sqrtf(sqrtf((float)D));
+  // Side stream: for 64 landmarks the forward half of the per-head chain
+  // (it needs only A) runs beside the token pass, which leaves CUs free;
+  // then the conv's backward (it needs only dout, v and the weights) runs
+  // beside the rest of the chain (one workgroup per head).  Both join back
+  // before the kernels that read their results.
+  constexpr bool SPLIT = M == 64;
+  Side* sd = nullptr;
+  if (SPLIT || conv_w != nullptr) {
+    rc = get_side(&sd);
+    if (rc != NYS_OK) return rc;
+    HIP_TRY(hipEventRecord(sd->fork, st));
+    HIP_TRY(hipStreamWaitEvent(sd->st, sd->fork, 0));
+  }
+  if constexpr (SPLIT) {
+    HIP_TRY(allow_lds(k_bwd_mm1f64, BWD_MM64_LDS));
+    HIP_TRY(launch("k_bwd_mm1f", k_bwd_mm1f64, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, sd->st, a));
+    HIP_TRY(hipEventRecord(sd->mid, sd->st));
+  }
+  if constexpr (bwd_tok2(M, D)) {
+    constexpr int tl = BwdTok2Layout<IO, M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_tok2<IO, M, D>, tl));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok2<IO, M, D>, dim3(bp.nct, p.BH), dim3(256), (uint32_t)tl, st, a));
+  } else {
+    constexpr int tl = BwdTokLayout<M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
+                   st, a));
+  }
+  if (conv_w != nullptr) {
+    HIP_TRY(hipEventRecord(sd->done, st));  // token pass done
+    HIP_TRY(hipStreamWaitEvent(sd->st, sd->done, 0));
+    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((p.n + BWD_DV_TOK - 1) / BWD_DV_TOK, p.BH), dim3(256),
+                   (uint32_t)dl, sd->st, a));
+    if (dconv_w != nullptr) {
+      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)cl, sd->st, a));
+    }
+    HIP_TRY(hipEventRecord(sd->join, sd->st));
+  }
+  constexpr int ml = bwd_mm_lds_bytes<M, D>();
+  if constexpr (SPLIT) {
+    HIP_TRY(hipStreamWaitEvent(st, sd->mid, 0));
+    if constexpr (sizeof(IO) == 4) {
+      HIP_TRY(allow_lds(k_bwd_mm1b64_f32<D>, BWD_MM64B_LDS));
+      HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64_f32<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64B_LDS, st, a));
+    } else {
+      HIP_TRY(allow_lds(k_bwd_mm1b64<D>, BWD_MM1B_LDS));
+      HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM1B_LDS, st, a));
+    }
+  } else {
+    HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
+    HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  }
+  HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
+  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  if (conv_w != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
+  if constexpr (bwd_tok2(M, D)) {
+    constexpr int kl = BwdKey2Layout<IO, M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_key2<IO, M, D>, kl));
+    HIP_TRY(launch("k_bwd_key", k_bwd_key2<IO, M, D>, dim3(bp.nck, p.BH), dim3(256), (uint32_t)kl, st, a));
+  } else {
+    constexpr int kl = BwdKeyLayout<M, D>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_key<IO, M, D>, kl));
+    HIP_TRY(launch("k_bwd_key", k_bwd_key<IO, M, D>, dim3(bp.nck, p.BH), dim3(BWD_KEY_NT), (uint32_t)kl, st, a));
+  }
+  static_assert((M * D) % 256 == 0, "k_bwd_qt: one element per thread");
+  HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M, D>, dim3(M * D / 256, p.BH), dim3(256), 0, st, a));
+  HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M, D>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
+  if (conv_w != nullptr && dconv_w != nullptr)
+    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(1024), 0, st, a));
+  return NYS_OK;
+}
+
+// Exact branch (m == n): the conv backward, then the three flash-style passes.
+template <typename IO, int D>
+int launch_backward_exact(int B, int H, int n, const void* q, const void* k, const void* v, const uint8_t* mask,
+                          const float* conv_w, int conv_k, const void* dout, void* dq, void* dk, void* dv,
+                          float* dconv_w, hipStream_t st) {
+  const size_t BH = (size_t)B * H;
+  const int ncv = (n + BWD_CV - 1) / BWD_CV;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  take(ZERO_BYTES);
+  const size_t off_lse = take(BH * n * 4), off_dt = take(BH * n * 4);
+  const size_t off_dvc = conv_w ? take(BH * n * D * 4) : 0, off_pconv = conv_w ? take(BH * ncv * conv_k * 4) : 0;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace* w = nullptr;
+  int rc = get_workspace(st, o, &w);
+  if (rc != NYS_OK) return rc;
+  BwdArgs c{};
+  c.v = v;
+  c.dout = dout;
+  c.conv_w = conv_w;
+  c.conv_k = conv_k;
+  c.dvc = conv_w ? at<float>(w, off_dvc) : nullptr;
+  c.pconv = conv_w ? at<float>(w, off_pconv) : nullptr;
+  c.dconv_w = dconv_w;
+  c.n = n;
+  c.H = H;
+  c.BH = (int)BH;
+  c.ncv = ncv;
+  if (conv_w != nullptr) {
+    constexpr int dl = bwd_dv_lds<D>(), cl = bwd_cv_lds<D>();
+    HIP_TRY(allow_lds(k_bwd_dvconv<IO, D>, dl));
+    HIP_TRY(launch("k_bwd_dvconv", k_bwd_dvconv<IO, D>, dim3((n + BWD_DV_TOK - 1) / BWD_DV_TOK, (unsigned)BH),
+                   dim3(256), (uint32_t)dl, st, c));
+    if (dconv_w != nullptr) {
+      HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
+      HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(ncv, (unsigned)BH), dim3(256), (uint32_t)cl, st, c));
+    }
+  }
+  XBwdArgs x{};
+  x.q = q;
+  x.k = k;
+  x.v = v;
+  x.dout = dout;
+  x.key_mask = mask;
+  x.dvc = c.dvc;
+  x.lse = at<float>(w, off_lse);
+  x.Dt = at<float>(w, off_dt);
+  x.dq = dq;
+  x.dk = dk;
+  x.dv = dv;
+  x.n = n;
+  x.H = H;
+  x.s4 = 1.0f / sqrtf(sqrtf((float)D));
+  const dim3 grid((n + XB_T - 1) / XB_T, (unsigned)BH);
+  constexpr int xl = xb_lds_bytes<D>();
+  HIP_TRY(allow_lds(k_bwd_xstats<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xstats", k_bwd_xstats<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
+  HIP_TRY(allow_lds(k_bwd_xq<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xq", k_bwd_xq<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
+  HIP_TRY(allow_lds(k_bwd_xkv<IO, D>, xl));
+  HIP_TRY(launch("k_bwd_xkv", k_bwd_xkv<IO, D>, grid, dim3(256), (uint32_t)xl, st, x));
+  if (conv_w != nullptr && dconv_w != nullptr)
+    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(H), dim3(1024), 0, st, c));
+  return NYS_OK;
+}
+
+template <typename IO>
+int run_backward(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k,
+                 int B, int H, int n, int d, int m, int n_iter, int init_option, const void* dout, void* dq, void* dk,
+                 void* dv, float* dconv_w, hipStream_t st) {
+  int rc = validate(sizeof(IO), q, k, v, B, H, n, d, m, n_iter, init_option, dq);
+  if (rc != NYS_OK) return rc;
+  if (!dout || !dk || !dv) return fail(NYS_ERR_INVALID, "dout, dq, dk and dv must be non-NULL");
+  if (conv_w != nullptr) {
+    if (conv_k < 1 || conv_k % 2 == 0)
+      return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
+    if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
+  }
+  const int m_max = d == 128 ? 64 : 128;  // the token pass's LDS tiles bound M * d
+  if (m != n && padded_m(m) > m_max)
+    return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to %d landmarks at d=%d)", m, m_max, d);
+  const size_t bytes = (size_t)B * H * n * d * sizeof(IO);
+  const void* const ro[4] = {q, k, v, dout};
+  void* const wr[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    if (reinterpret_cast<uintptr_t>(wr[i]) % 16 != 0) return fail(NYS_ERR_INVALID, "dq, dk, dv must be 16-byte aligned");
+    for (int j = 0; j < 4; ++j)
+      if (ranges_meet(wr[i], bytes, ro[j], bytes)) return fail(NYS_ERR_INVALID, "dq, dk, dv must not overlap q, k, v, dout");
+    for (int j = 0; j < i; ++j)
+      if (ranges_meet(wr[i], bytes, wr[j], bytes)) return fail(NYS_ERR_INVALID, "dq, dk, dv must not overlap");
+  }
+  for (const void* ptr : {q, k, v, dout})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(NYS_ERR_INVALID, "q, k, v, dout must be 16-byte aligned");
+  if (m == n) {
+    switch (d) {
+      case 32: return launch_backward_exact<IO, 32>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+      case 64: return launch_backward_exact<IO, 64>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+      default: return launch_backward_exact<IO, 128>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
+    }
+  }
+  Plan p = make_plan(B, H, n, m, d);
+  p.record = true;  // A is read back
+  p.bwd = true;
+  p.si = p.so = dense(B, H, n, d);
+  const BwdPlan bp = make_bwd_plan(p, n_iter, conv_k, conv_w != nullptr);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace* w = nullptr;
+  rc = get_workspace(st, bp.total, &w);
+  if (rc != NYS_OK) return rc;
+#define NYS_BWD(MM, DD)                                                                                            \
+  return launch_backward<IO, MM, DD>(p, bp, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, dout, dq, dk, dv, \
+                                     dconv_w, st)
+  switch (d * 1000 + p.m) {
+    case 32032: NYS_BWD(32, 32);
+    case 32064: NYS_BWD(64, 32);
+    case 32096: NYS_BWD(96, 32);
+    case 32128: NYS_BWD(128, 32);
+    case 64032: NYS_BWD(32, 64);
+    case 64064: NYS_BWD(64, 64);
+    case 64096: NYS_BWD(96, 64);
+    case 64128: NYS_BWD(128, 64);
+    case 128032: NYS_BWD(32, 128);
+    case 128064: NYS_BWD(64, 128);
+    default: break;
+  }
+#undef NYS_BWD
+  return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d, d=%d", m, d);
+}
+
+}  // namespace host
+}  // namespace nys

@@ -1,0 +1,10 @@
+// Forward Nystrom path, float32 I/O, head size 64.
+#include "fwd_impl.hpp"
+
+namespace nys {
+namespace host {
+
+template int dispatch_m<float, 64>(int, const Plan&, Workspace*, const void*, const void*, const void*, const uint8_t*, const float*, int, int, int, void*, hipStream_t);
+
+}  // namespace host
+}  // namespace nys

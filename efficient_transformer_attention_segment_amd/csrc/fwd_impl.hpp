@@ -1,0 +1,273 @@
+// Forward launch sequence of the Nystrom path, shared by the per-type
+// translation units fwd_f32.hip, fwd_bf16.hip and fwd_bf16x.hip, each of
+// which instantiates dispatch_m for its (I/O type, head size) pairs.
+//
+// Launch sequence for one Nystrom call (all on the caller's stream):
+//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo)
+//   2 k_gram       per head A = softmax(Qt Kt^T), its max column / row sum;
+//                  only when the pseudo-inverse blocks cannot form A
+//                  themselves (m > 128, or the original init with more
+//                  heads than can meet in one resident round)
+//   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
+//                  blocks (m <= 128) and the B V partial blocks, so the
+//                  pseudo-inverse chain runs beside the K/V stream
+//     (m > 128: k_pinv_init + 4 k_pinv_gemm launches per iteration)
+//   4 k_mw         B V from the partials, W = Z (B V) and its operand
+//                  fragments
+//   5 k_out_stream F W + conv(V) -> out (bf16 I/O; k_out for float32)
+// Kernel boundaries are the only cross-workgroup synchronisation, apart
+// from the one meeting of the pseudo-inverse blocks for the original init
+// (data handed between workgroups of one launch across XCDs would need L2
+// write-back and invalidation, which cost far more here than a launch).
+#pragma once
+
+#include <cmath>
+
+#include "host.hpp"
+#include "k_bv.hpp"
+#include "k_landmark.hpp"
+#include "k_merge.hpp"
+#include "k_out.hpp"
+#include "k_pinv.hpp"
+#include "k_probs.hpp"
+
+namespace nys {
+namespace host {
+
+// --------------------------------------------------------- launches ---
+template <typename IO, int M, int D>
+int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
+                   const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
+                   hipStream_t st) {
+  const float s4 = 1.0f / sqrtf(sqrtf((float)D));
+  LandmarkArgs la;
+  la.n = p.n;
+  la.H = p.H;
+  la.in = p.si;
+  la.m = M;
+  la.mr = p.mr;
+  la.L = p.L;
+  la.RS = p.RS;
+  la.lpw = p.lpw;
+  la.BH = p.BH;
+  la.scale = s4 / (float)p.L;
+  la.qt = at<float>(w, p.off_qt);
+  la.kt = at<float>(w, p.off_kt);
+  la.qt_hi = at<__bf16>(w, p.off_qth);
+  la.qt_lo = at<__bf16>(w, p.off_qtl);
+  la.kt_hi = at<__bf16>(w, p.off_kth);
+  la.kt_lo = at<__bf16>(w, p.off_ktl);
+  la.A = at<float>(w, p.off_A);
+  la.colmax = at<float>(w, p.off_colmax);
+  la.rowmax = at<float>(w, p.off_rowmax);
+  la.slots = at<unsigned long long>(w, p.off_slots);
+  HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
+                 (const IO*)k, la));
+  // the pseudo-inverse blocks form A themselves only at d = 64 (their LDS
+  // plan holds 64-channel landmarks)
+  const bool fuse_gram = D == HD && M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
+  if (!fuse_gram) {
+    constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4, D>();
+    HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4, D>, glds));
+    HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4, D>, dim3(p.BH), dim3(64 * gram_waves<M>()), (uint32_t)glds,
+                   st, la));
+  }
+
+  PinvArgs pa;
+  pa.A = la.A;
+  pa.colmax = la.colmax;
+  pa.rowmax = la.rowmax;
+  pa.Z = at<float>(w, p.off_Z);
+  pa.cscale = at<float>(w, p.off_cscale);
+  pa.BH = p.BH;
+  pa.n_iter = n_iter;
+  pa.init_option = init_option;
+  pa.f16 = (sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER) ? 1 : 0;
+  pa.fuse_gram = fuse_gram ? 1 : 0;
+  pa.npinv = p.npinv;
+  pa.record = p.record ? 1 : 0;
+  pa.la = la;
+  BvArgs ba;
+  ba.k = k;
+  ba.v = v;
+  ba.key_mask = mask;
+  ba.qt_hi = la.qt_hi;
+  ba.qt_lo = la.qt_lo;
+  ba.pmax = at<float>(w, p.off_pmax);
+  ba.psum = at<float>(w, p.off_psum);
+  ba.pacc = at<float>(w, p.off_pacc);
+  ba.n = p.n;
+  ba.H = p.H;
+  ba.S = p.S;
+  ba.tpc = p.tpc;
+  ba.ntiles = p.ntiles;
+  ba.lscale = s4;
+  ba.in = p.si;
+  size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
+  lds2 = std::max<size_t>(lds2, bv_fold_bytes<M, D>());
+  if constexpr (M <= 128)
+    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
+                                                  : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
+  // the padding-landmark and ragged-tile code only in the instance that needs it
+  const bool pad = p.mr < M, edge = pad || p.n % 32 != 0;
+  auto launch_bv = [&](auto kern) -> int {
+    HIP_TRY(allow_lds(kern, lds2));
+    HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), (uint32_t)lds2, st, pa,
+                   ba, p.npinv));
+    return NYS_OK;
+  };
+  const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D>) : launch_bv(k_pinv_bv<IO, M, false, D>);
+  if (brc != NYS_OK) return brc;
+
+  const float* Zfinal = pa.Z;
+  if constexpr (M > 128) {
+    HIP_TRY(launch("k_pinv_init", k_pinv_init, dim3((M / 32) * (M / 32), p.BH), dim3(256), 0, st, pa, M));
+    float* Zc = pa.Z;
+    float* Zn = at<float>(w, p.off_Z2);
+    float* X = at<float>(w, p.off_X);
+    float* T1 = at<float>(w, p.off_T1);
+    float* T2 = at<float>(w, p.off_T2);
+    const dim3 gg((M / 32) * (M / 32), p.BH);
+    for (int it = 0; it < n_iter; ++it) {
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)pa.A, (const float*)Zc, X,
+                     0.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)X, (const float*)X, T1,
+                     7.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)X, (const float*)T1, T2,
+                     15.f, 1.f));
+      HIP_TRY(launch("k_pinv_gemm", k_pinv_gemm<sizeof(IO) == 4, M>, gg, dim3(256), 0, st, (const float*)Zc, (const float*)T2, Zn,
+                     13.f, 0.25f));
+      std::swap(Zc, Zn);
+    }
+    Zfinal = Zc;
+  }
+
+  MergeArgs ma;
+  ma.pmax = ba.pmax;
+  ma.psum = ba.psum;
+  ma.pacc = ba.pacc;
+  ma.Z = Zfinal;
+  ma.BV = at<float>(w, p.off_BV);
+  ma.W = at<float>(w, p.off_W);
+  ma.wf_hi = at<__bf16>(w, p.off_wfh);
+  ma.wf_lo = at<__bf16>(w, p.off_wfl);
+  ma.S = p.S;
+  ma.BH = p.BH;
+  ma.lse = p.bwd ? at<float>(w, p.off_lse) : nullptr;
+  // threads per block: enough chunk subsets per row that each thread folds
+  // one batch of 8 chunks (up to 1024 threads; 512 for m = 32)
+  const int need = M * ((p.S + 7) / 8);
+  // the bf16 output pass at d = 64 takes W^T in its own channel order
+  constexpr bool B16 = sizeof(IO) == 2 && D == HD;
+  constexpr int NT_MAX = M >= 64 ? 1024 : 512;
+  const dim3 mwg(mw_blocks(p.BH, D));
+  if (need <= 256)
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 256, D>, mwg, dim3(256), 0, st, ma));
+  else if (need <= 512 || NT_MAX == 512)
+    HIP_TRY(launch("k_mw", k_mw<M, B16, 512, D>, mwg, dim3(512), 0, st, ma));
+  else
+    HIP_TRY(launch("k_mw", k_mw<M, B16, NT_MAX, D>, mwg, dim3(NT_MAX), 0, st, ma));
+  if (p.bwd) return NYS_OK;  // the backward pass takes it from here
+
+  OutArgs oa;
+  oa.q = q;
+  oa.v = v;
+  oa.zero = at<__bf16>(w, p.off_zero);
+  oa.conv_w = conv_w;
+  oa.conv_k = conv_k;
+  oa.kt_hi = la.kt_hi;
+  oa.kt_lo = la.kt_lo;
+  oa.wf_hi = ma.wf_hi;
+  oa.wf_lo = ma.wf_lo;
+  oa.out = out;
+  oa.n = p.n;
+  oa.H = p.H;
+  oa.lscale = s4;
+  oa.in = p.si;
+  oa.out_s = p.so;
+  oa.mr = p.mr;
+  if constexpr (sizeof(IO) == 2 && D == HD) {
+    // persistent output pass: a token range of one head per workgroup, sized
+    // so the grid fills the CUs at the occupancy its LDS allows in at most
+    // one resident round (a second, partial round would cost a whole
+    // workgroup lifetime)
+    constexpr size_t lds4 = OutStreamLayout<M>::LDS_BYTES;
+    constexpr int per_cu = std::min<int>(4, (int)(160 * 1024 / lds4));
+    const int slots = 256 * per_cu;
+    const int want = std::max(1, slots / p.BH);  // workgroups per head
+    const int R = OUTS_UNIT * ((p.n + want * OUTS_UNIT - 1) / (want * OUTS_UNIT));
+    const int nbh = (p.n + R - 1) / R;
+    u16* const junk = at<u16>(w, p.off_junk);
+    auto launch_out = [&](auto kern) -> int {
+      HIP_TRY(launch("k_out_stream", kern, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, junk));
+      return NYS_OK;
+    };
+    const int orc = conv_w != nullptr ? (pad ? launch_out(k_out_stream<M, true, true>)
+                                             : launch_out(k_out_stream<M, true, false>))
+                                      : (pad ? launch_out(k_out_stream<M, false, true>)
+                                             : launch_out(k_out_stream<M, false, false>));
+    if (orc != NYS_OK) return orc;
+  } else {
+    using OL = OutLayout<IO, M, D>;
+    auto launch_out = [&](auto kern) -> int {
+      HIP_TRY(allow_lds(kern, OL::LDS_BYTES));
+      HIP_TRY(launch("k_out", kern, dim3((p.n + OL::TOK - 1) / OL::TOK, p.BH), dim3(256), (uint32_t)OL::LDS_BYTES, st,
+                     oa));
+      return NYS_OK;
+    };
+    const int orc = pad ? launch_out(k_out<IO, M, true, D>) : launch_out(k_out<IO, M, false, D>);
+    if (orc != NYS_OK) return orc;
+  }
+
+  if (p.probs != nullptr) {
+    ProbsArgs pr{};
+    pr.q = q;
+    pr.kt_hi = la.kt_hi;
+    pr.kt_lo = la.kt_lo;
+    pr.Z = Zfinal;
+    pr.probs = p.probs;
+    pr.n = p.n;
+    pr.H = p.H;
+    pr.mr = p.mr;
+    pr.ldp = p.mr;
+    pr.lscale = s4;
+    pr.in = p.si;
+    using PL = ProbsLayout<IO, M, D>;
+    const int ntb = (p.n + PROBS_TOK - 1) / PROBS_TOK;
+    const dim3 grid(((ntb + 7) / 8) * 8 * PL::NCB, p.BH);
+    auto launch_probs = [&](auto kern) -> int {
+      HIP_TRY(allow_lds(kern, PL::LDS_BYTES));
+      HIP_TRY(launch("k_probs", kern, grid, dim3(256), (uint32_t)PL::LDS_BYTES, st, pr));
+      return NYS_OK;
+    };
+    const int prc = pad ? launch_probs(k_probs<IO, M, true, D>) : launch_probs(k_probs<IO, M, false, D>);
+    if (prc != NYS_OK) return prc;
+  }
+  return NYS_OK;
+}
+
+template <typename IO, int D>
+int dispatch_m(int m, const Plan& p, Workspace* w, const void* q, const void* k, const void* v,
+               const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option, void* out,
+               hipStream_t st) {
+#define NYS_M(MM) \
+  case MM:        \
+    return launch_nystrom<IO, MM, D>(p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
+  switch (m) {
+    NYS_M(32)
+    NYS_M(64)
+    NYS_M(96)
+    NYS_M(128)
+    NYS_M(160)
+    NYS_M(192)
+    NYS_M(224)
+    NYS_M(256)
+    default: break;
+  }
+#undef NYS_M
+  return fail(NYS_ERR_UNSUPPORTED, "m=%d has no kernel instance", m);
+}
+
+
+}  // namespace host
+}  // namespace nys

@@ -879,7 +879,7 @@ constexpr int BWD_MM64_LDS = 4 * 6 * 64 * 68;
 // token pass.  A, Z, X, X^2, P and a spare slot as float32 images in LDS
 // (row stride 68), 16 waves.
 // grid BH, block BWD_MM_NT, dynamic LDS BWD_MM64_LDS.
-__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1f64(BwdArgs a) {
+static __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1f64(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   constexpr int M = 64, MM = M * M, LD = M + 4, SZ = M * LD, NT = BWD_MM_NT;
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -1941,7 +1941,7 @@ __global__ __launch_bounds__(256) void k_bwd_conv(BwdArgs a) {
 
 // dconv_w[h][j] = sum over batches and chunks: 8 threads per tap each take
 // every 8th partial, then the 8 sums are added in order.  grid H, block 1024.
-__global__ __launch_bounds__(1024) void k_bwd_wsum(BwdArgs a) {
+static __global__ __launch_bounds__(1024) void k_bwd_wsum(BwdArgs a) {
   __shared__ float ps[8][TAPS];
   const int h = blockIdx.x, K = a.conv_k, j = threadIdx.x >> 3, p = threadIdx.x & 7;
   const int B = a.BH / a.H, cnt = B * a.ncv;

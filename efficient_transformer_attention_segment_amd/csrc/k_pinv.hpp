@@ -868,7 +868,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
 // grid: BH blocks of 256: c, then Z = A^T / c.
 // grid ((M/32)^2, BH), block 256: c, then the 32 x 32 tile (tr, tc) of
 // Z = A^T / c through an LDS tile (coalesced reads and writes).
-__global__ __launch_bounds__(256) void k_pinv_init(PinvArgs a, int M) {
+static __global__ __launch_bounds__(256) void k_pinv_init(PinvArgs a, int M) {
   __shared__ float tile[32][33];
   const int bh = blockIdx.y;
   const int nb = M / 32;
