@@ -18,7 +18,7 @@ import os
 __all__ = [
     "NystromError", "nystrom_attention", "nystrom_attention_bf16", "attention", "attention_with_probs", "self_attention", "attention_backward",
     "workspace_bytes", "last_error", "release", "debug_stages", "library_path",
-    "profile_enable", "profile_collect",
+    "profile_enable", "profile_collect", "check_status", "debug_set_rendezvous_spins", "debug_set_workspace_cap",
     "NYS_OK", "NYS_ERR_INVALID", "NYS_ERR_UNSUPPORTED", "NYS_ERR_HIP",
 ]
 
@@ -73,6 +73,12 @@ def _load():
     lib.nystrom_debug_stages.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P]
     lib.nystrom_debug_stages.restype = _I
+    lib.nystrom_check_status.argtypes = [_P]
+    lib.nystrom_check_status.restype = _I
+    lib.nystrom_debug_set_rendezvous_spins.argtypes = [ctypes.c_uint]
+    lib.nystrom_debug_set_rendezvous_spins.restype = None
+    lib.nystrom_debug_set_workspace_cap.argtypes = [ctypes.c_size_t]
+    lib.nystrom_debug_set_workspace_cap.restype = None
     lib.nystrom_profile_enable.argtypes = [_I]
     lib.nystrom_profile_enable.restype = None
     lib.nystrom_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -109,6 +115,52 @@ def _stream(stream):
     return ctypes.c_void_p(getattr(stream, "cuda_stream", stream) or 0)
 
 
+def _check_io(q, k, v, out, dtype=None):
+    """q, k, v (and out when given): 4-D CUDA tensors on one device with one
+    dtype, float32 or bfloat16 (``dtype`` when the entry point fixes it).
+    Nothing reaches the library before these checks pass: it takes raw
+    device pointers and cannot tell a host pointer or a wrong element type
+    from a valid one."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, n, d]")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q, k, v must be float32 or bfloat16, not {q.dtype}")
+    if dtype is not None and q.dtype != dtype:
+        raise ValueError(f"this entry point takes {dtype} tensors, got {q.dtype}")
+
+
+def _check_aux(ref, B, H, n, key_mask, conv_w):
+    """key_mask: uint8 or bool [B, n], dense, on ref's device; conv_w: float32
+    [H, K], dense, on ref's device (a Conv2d weight [H, 1, K, 1] must be
+    reshaped to [H, K] first)."""
+    import torch
+    if key_mask is not None:
+        if not isinstance(key_mask, torch.Tensor) or key_mask.device != ref.device:
+            raise ValueError(f"key_mask must be a tensor on {ref.device}")
+        if key_mask.dtype not in (torch.uint8, torch.bool):
+            raise ValueError(f"key_mask must be uint8 or bool (1 keeps a key), not {key_mask.dtype}")
+        if tuple(key_mask.shape) != (B, n) or not key_mask.is_contiguous():
+            raise ValueError(f"key_mask must be a dense [B, n] = [{B}, {n}] tensor, got {tuple(key_mask.shape)}")
+    if conv_w is not None:
+        if not isinstance(conv_w, torch.Tensor) or conv_w.device != ref.device:
+            raise ValueError(f"conv_w must be a tensor on {ref.device}")
+        if conv_w.dtype != torch.float32:
+            raise ValueError(f"conv_w must be float32, not {conv_w.dtype}")
+        if conv_w.dim() != 2 or conv_w.shape[0] != H or not conv_w.is_contiguous():
+            raise ValueError(f"conv_w must be a dense [H, K] = [{H}, K] tensor, got {tuple(conv_w.shape)} "
+                             "(reshape a Conv2d weight [H, 1, K, 1] to [H, K])")
+
+
 def _raw_call(fn, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
     B, H, n, d = q.shape
     return fn(_ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w), B, H, n, d, m, n_iter,
@@ -128,9 +180,12 @@ def _dense(t) -> bool:
 
 
 def _call(name, q, k, v, key_mask, conv_w, m, n_iter, init_option, out, stream):
-    lib = _load()
+    import torch
+    _check_io(q, k, v, out, torch.bfloat16 if name.endswith("bf16") else torch.float32)
     if not (k.shape == v.shape == out.shape == q.shape):
         raise ValueError("q, k, v and out must have one shape [B, H, n, d]")
+    _check_aux(q, q.shape[0], q.shape[1], q.shape[2], key_mask, conv_w)
+    lib = _load()
     if not all(_dense(t) for t in (q, k, v, out)):
         # strided views of [B, H, n, 64] (channels contiguous): one set of
         # strides for q, k, v and one for out
@@ -190,8 +245,12 @@ def attention_with_probs(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, in
     strides) and out may be strided views with contiguous channels; probs
     is dense.  Returns (out, probs)."""
     import torch
+    _check_io(q, k, v, out)
     if not (k.shape == v.shape == q.shape):
         raise ValueError("q, k and v must have one shape [B, H, n, d]")
+    _check_aux(q, q.shape[0], q.shape[1], q.shape[2], key_mask, conv_w)
+    if probs is not None and (not probs.is_cuda or probs.device != q.device or probs.dtype != q.dtype):
+        raise ValueError("probs must be a CUDA tensor on q's device with q's dtype")
     if q.stride() != k.stride() or k.stride() != v.stride() or q.stride(-1) != 1:
         raise ValueError("q, k and v must share strides, with contiguous channels")
     B, H, n, d = q.shape
@@ -218,10 +277,20 @@ def self_attention(x, w_qkv, b_qkv, H, key_mask=None, conv_w=None, m=64, n_iter=
     w_qkv [3 H d, hidden] (query, key, value weights stacked), b_qkv [3 H d]
     or None.  Returns (out [B, n, H d], qkv [B, n, 3, H, d])."""
     import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 3:
+        raise ValueError("x must be a CUDA tensor [B, n, hidden]")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x must be float32 or bfloat16, not {x.dtype}")
+    for name, t in (("w_qkv", w_qkv), ("b_qkv", b_qkv), ("qkv", qkv), ("out", out)):
+        if t is not None and (not t.is_cuda or t.device != x.device or t.dtype != x.dtype):
+            raise ValueError(f"{name} must be a CUDA tensor on x's device with x's dtype")
     B, n, hidden = x.shape
     if w_qkv.dim() != 2 or w_qkv.shape[1] != hidden or w_qkv.shape[0] % (3 * H) != 0:
         raise ValueError("w_qkv must be [3 H d, hidden]")
     d = w_qkv.shape[0] // (3 * H)
+    if b_qkv is not None and tuple(b_qkv.shape) != (3 * H * d,):
+        raise ValueError("b_qkv must be [3 H d]")
+    _check_aux(x, B, H, n, key_mask, conv_w)
     for t in (x, w_qkv, b_qkv):
         if t is not None and (not t.is_contiguous() or t.dtype != x.dtype):
             raise ValueError("x, w_qkv and b_qkv must be dense and share x's dtype")
@@ -248,21 +317,48 @@ def attention_backward(q, k, v, dout, key_mask=None, conv_w=None, m=64, n_iter=6
     first three in q's dtype, dconv_w float32 [H, K] (None without conv_w).
     Dense [B, H, n, d] tensors, d in {32, 64, 128}."""
     import torch
+    _check_io(q, k, v, dout)
     for t in (q, k, v, dout):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("q, k, v and dout must be dense tensors of one shape and dtype")
     B, H, n, d = q.shape
+    _check_aux(q, B, H, n, key_mask, conv_w)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if (not t.is_cuda or t.device != q.device or t.shape != q.shape or t.dtype != q.dtype
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a dense CUDA tensor of q's shape, dtype and device")
     if conv_w is not None and dconv_w is None:
         dconv_w = torch.empty(conv_w.shape, dtype=torch.float32, device=q.device)
+    if dconv_w is not None and (conv_w is None or not dconv_w.is_cuda or dconv_w.device != q.device
+                                or dconv_w.dtype != torch.float32 or dconv_w.shape != conv_w.shape
+                                or not dconv_w.is_contiguous()):
+        raise ValueError("dconv_w must be a dense float32 CUDA tensor of conv_w's shape (and needs conv_w)")
     dtype = 1 if q.dtype == torch.bfloat16 else 0
     ksize = CONV_TAPS if conv_w is None else int(conv_w.shape[-1])
     _check(_load().nystrom_attention_backward(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(key_mask), _ptr(conv_w), ksize,
                                               B, H, n, d, m, n_iter, init_option, _ptr(dout), _ptr(dq), _ptr(dk),
                                               _ptr(dv), _ptr(dconv_w), _stream(stream)))
     return dq, dk, dv, dconv_w
+
+
+def check_status(stream=None) -> None:
+    """Synchronise the stream and raise NystromError if a call on it since
+    the last check gave up waiting at the pseudo-inverse rendezvous (its
+    output is NaN)."""
+    _check(_load().nystrom_check_status(_stream(stream)))
+
+
+def debug_set_rendezvous_spins(spins: int) -> None:
+    """Test hook: bound on the rendezvous polls (default 2**20)."""
+    _load().nystrom_debug_set_rendezvous_spins(int(spins))
+
+
+def debug_set_workspace_cap(nbytes: int) -> None:
+    """Test hook: cap the device workspace (0 = no cap)."""
+    _load().nystrom_debug_set_workspace_cap(int(nbytes))
 
 
 def workspace_bytes(B, H, n, d, m) -> int:
@@ -295,7 +391,11 @@ def debug_stages(q, k, v, key_mask=None, conv_w=None, m=64, n_iter=6, init_optio
     """Run the Nystrom path and return (out, stages) where stages holds the
     float32 intermediates qt, kt, A, c, Z, BV, W as CUDA tensors."""
     import torch
+    _check_io(q, k, v, None)
     B, H, n, d = q.shape
+    if not (k.shape == v.shape == q.shape) or not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k and v must be dense tensors of one shape [B, H, n, d]")
+    _check_aux(q, B, H, n, key_mask, conv_w)
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
     st = dict(qt=torch.empty(B, H, m, d, **f32), kt=torch.empty(B, H, m, d, **f32),

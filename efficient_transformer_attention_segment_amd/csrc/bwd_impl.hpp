@@ -196,7 +196,7 @@ int launch_backward_exact(int B, int H, int n, const void* q, const void* k, con
     o = align_up(o + bytes);
     return at;
   };
-  take(ZERO_BYTES);
+  take(HEAD_BYTES);  // zero page and status word, as in every workspace
   const size_t off_lse = take(BH * n * 4), off_dt = take(BH * n * 4);
   const size_t off_dvc = conv_w ? take(BH * n * D * 4) : 0, off_pconv = conv_w ? take(BH * ncv * conv_k * 4) : 0;
   std::lock_guard<std::mutex> lk(g_mu);

@@ -63,9 +63,32 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.slots = at<unsigned long long>(w, p.off_slots);
   HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
+  size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
+  lds2 = std::max<size_t>(lds2, bv_fold_bytes<M, D>());
+  if constexpr (M <= 128)
+    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
+                                                  : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
+  // the padding-landmark and ragged-tile code only in the instance that needs it
+  const bool pad = p.mr < M, edge = pad || p.n % 32 != 0;
+  // The original init's one rendezvous needs every pseudo-inverse block
+  // resident at once.  They are the first blocks of their launch, so they
+  // are dispatched first; fuse only while they fit in half of the slots the
+  // device offers the launch (and at most 128, the slots one wave polls).
+  static const int fuse_cap = [&] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    const void* kern = edge ? reinterpret_cast<const void*>(k_pinv_bv<IO, M, true, D>)
+                            : reinterpret_cast<const void*>(k_pinv_bv<IO, M, false, D>);
+    if (allow_lds(edge ? k_pinv_bv<IO, M, true, D> : k_pinv_bv<IO, M, false, D>, lds2) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * bv_waves<M>(), lds2) != hipSuccess)
+      return 0;
+    return std::min(FUSED_GRAM_MAX_BLOCKS, per_cu * cus / 2);
+  }();
   // the pseudo-inverse blocks form A themselves only at d = 64 (their LDS
   // plan holds 64-channel landmarks)
-  const bool fuse_gram = D == HD && M <= 128 && (init_option != 0 || p.npinv <= FUSED_GRAM_MAX_BLOCKS);
+  const bool fuse_gram = D == HD && M <= 128 && (init_option != 0 || p.npinv <= fuse_cap);
   if (!fuse_gram) {
     constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4, D>();
     HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4, D>, glds));
@@ -86,6 +109,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.fuse_gram = fuse_gram ? 1 : 0;
   pa.npinv = p.npinv;
   pa.record = p.record ? 1 : 0;
+  pa.spins = g_spins;
+  pa.status = at<unsigned>(w, STATUS_OFF);
   pa.la = la;
   BvArgs ba;
   ba.k = k;
@@ -103,13 +128,6 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
   ba.in = p.si;
-  size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
-  lds2 = std::max<size_t>(lds2, bv_fold_bytes<M, D>());
-  if constexpr (M <= 128)
-    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
-                                                  : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
-  // the padding-landmark and ragged-tile code only in the instance that needs it
-  const bool pad = p.mr < M, edge = pad || p.n % 32 != 0;
   auto launch_bv = [&](auto kern) -> int {
     HIP_TRY(allow_lds(kern, lds2));
     HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), (uint32_t)lds2, st, pa,

@@ -46,7 +46,7 @@ struct Plan {
   bool bwd;        // forward stages for the backward pass: stop after W, keep B's normalisers
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
-  size_t off_slots, off_junk, off_lse, off_status;
+  size_t off_slots, off_junk, off_lse;
   size_t total;
 };
 
@@ -118,6 +118,15 @@ struct Workspace {
 // uses a cached workspace.
 extern std::mutex g_mu;
 int get_workspace(hipStream_t st, size_t bytes, Workspace** out);
+// Test hooks: a cap on the workspace size (0 = none; a larger request fails
+// with NYS_ERR_HIP before anything is enqueued) and the rendezvous poll bound.
+extern size_t g_ws_cap;
+extern unsigned g_spins;
+constexpr unsigned RENDEZVOUS_SPINS_DEFAULT = 1u << 20;  // about a second of polls
+// Bytes at the start of every workspace that are cleared when it is
+// allocated: the zero page, then the device status word (STATUS_OFF).
+constexpr size_t STATUS_OFF = ZERO_BYTES;
+constexpr size_t HEAD_BYTES = ZERO_BYTES + 256;
 
 // A side stream per device, for work that can run beside the call's own
 // stream (forked from it and joined back with events, so the caller sees one

@@ -389,7 +389,8 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
       for (int ks = 0; ks < D / 32; ++ks) {
         const size_t off = ((size_t)bh * M + 16 * lt + c16) * D + 32 * ks + 8 * g;
         qf[o][ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
-        qf[o][ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
+        // bf16 keys: one bf16 pass (hi plane) against exact bf16 operands
+        if constexpr (IOTraits<IO>::NS == 3) qf[o][ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
       }
     }
   }

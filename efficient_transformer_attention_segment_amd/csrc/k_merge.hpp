@@ -236,7 +236,8 @@ __device__ void mw_body(const MergeArgs& a, int bh, int run, float* L) {
     const Frag2 f = split8(x);
     const size_t ent = ((size_t)bh * (D / 16) * KS + (size_t)dt * KS + kb) * 64 + ln;
     *reinterpret_cast<bf16x8*>(a.wf_hi + ent * 8) = f.hi;
-    *reinterpret_cast<bf16x8*>(a.wf_lo + ent * 8) = f.lo;
+    // the bf16 output pass multiplies by W^T in one bf16 pass (its hi plane)
+    if constexpr (!B16) *reinterpret_cast<bf16x8*>(a.wf_lo + ent * 8) = f.lo;
   }
 }
 

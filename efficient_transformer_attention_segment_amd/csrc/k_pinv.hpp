@@ -47,12 +47,16 @@ struct PinvArgs {
   int fuse_gram;        // 1: each block forms its own head's A first (m <= 128)
   int npinv;            // pseudo-inverse blocks in the launch (<= 128: slots polled by one wave)
   int record;           // 1: also write A to global (fuse_gram; for the stage hook)
+  unsigned spins;       // bound on the rendezvous polls (option 0 with fuse_gram)
+  unsigned* status;     // bit 0 set when a rendezvous ran out of polls
   LandmarkArgs la;      // landmarks in, A / colmax / rowmax out (fuse_gram)
 };
 
-// Bound on the rendezvous wait (about a second of polls); past it the
-// scale becomes NaN so that the result is visibly wrong instead of hanging.
-constexpr unsigned RENDEZVOUS_SPINS = 1u << 20;
+// Past the bound on the rendezvous wait (a.spins polls; about a second by
+// default) the scale becomes NaN, so the result is visibly wrong instead of
+// hanging, and the block sets this bit of the status word, which the host
+// reports.
+constexpr unsigned STATUS_RENDEZVOUS_TIMEOUT = 1u;
 
 __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
   if (a.init_option == 0) {
@@ -289,7 +293,8 @@ __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     float c = __builtin_nanf("");
-    for (unsigned it = 0; it < RENDEZVOUS_SPINS; ++it) {
+    bool met = false;
+    for (unsigned it = 0; it < a.spins; ++it) {
       bool ok = true;
       float cmx = 0.f, rmx = 0.f;
 #pragma unroll
@@ -306,11 +311,15 @@ __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
       }
       if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
         c = wave_max(cmx) * wave_max(rmx);
+        met = true;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    if (lane == 0) wred[0] = c;
+    if (lane == 0) {
+      wred[0] = c;
+      if (!met) __hip_atomic_fetch_or(a.status, STATUS_RENDEZVOUS_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   return wred[0];

@@ -28,6 +28,8 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 std::mutex g_mu;
+size_t g_ws_cap = 0;
+unsigned g_spins = RENDEZVOUS_SPINS_DEFAULT;
 
 int pow2floor(int x) {
   int p = 1;
@@ -76,7 +78,7 @@ Plan make_plan(int B, int H, int n, int mr, int d) {
     o = align_up(o + bytes);
     return at;
   };
-  p.off_zero = take(ZERO_BYTES);
+  p.off_zero = take(HEAD_BYTES);  // zero page, then the status word
   p.off_slots = take(BH * 16);
   p.off_junk = take(16 * HD * 2);  // output rows of tiles past a workgroup's range
   p.off_qt = take(BH * M * D * 4);
@@ -116,6 +118,8 @@ std::map<int, Side> g_side;
 int get_workspace(hipStream_t st, size_t bytes, Workspace** out) {
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
+  if (g_ws_cap != 0 && bytes > g_ws_cap)
+    return fail(NYS_ERR_HIP, "workspace of %zu bytes exceeds the cap of %zu bytes", bytes, g_ws_cap);
   Workspace& w = g_ws[{dev, st}];
   if (w.cap < bytes) {
     HIP_TRY(hipStreamSynchronize(st));
@@ -124,7 +128,7 @@ int get_workspace(hipStream_t st, size_t bytes, Workspace** out) {
     w.cap = 0;
     HIP_TRY(hipMalloc(&w.buf, bytes));
     w.cap = bytes;
-    HIP_TRY(hipMemsetAsync(w.buf, 0, ZERO_BYTES, st));
+    HIP_TRY(hipMemsetAsync(w.buf, 0, HEAD_BYTES, st));
   }
   *out = &w;
   return NYS_OK;
@@ -619,6 +623,39 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
   } catch (...) {
     return fail(NYS_ERR_HIP, "unexpected host exception");
   }
+}
+
+__attribute__((visibility("default"))) int nystrom_check_status(struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    HIP_TRY(hipStreamSynchronize(stream));
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || it->second.buf == nullptr) return NYS_OK;
+    unsigned status = 0;
+    void* const word = it->second.buf + STATUS_OFF;
+    HIP_TRY(hipMemcpy(&status, word, sizeof status, hipMemcpyDeviceToHost));
+    if (status == 0) return NYS_OK;
+    const unsigned zero = 0;
+    HIP_TRY(hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice));
+    return fail(NYS_ERR_HIP,
+                "a call on this stream gave up waiting for the pseudo-inverse blocks' rendezvous (original init): "
+                "its scale c and output are NaN; the blocks were not all resident together");
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
+__attribute__((visibility("default"))) void nystrom_debug_set_rendezvous_spins(unsigned spins) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_spins = spins;
+}
+
+__attribute__((visibility("default"))) void nystrom_debug_set_workspace_cap(size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_ws_cap = bytes;
 }
 
 __attribute__((visibility("default"))) void nystrom_profile_enable(int on) {

@@ -234,6 +234,29 @@ int nystrom_debug_stages(int dtype, const void* q, const void* k,
                          float* z, float* bv, float* w,
                          struct ihipStream_t* stream);
 
+/* Device-side status of the work enqueued on `stream` ([P1] 2.5: the
+ * original init's scale c is a maximum over every head, for which the
+ * per-head pseudo-inverse blocks of one launch meet once; the wait is
+ * bounded, and a block that gives up sets c to NaN, so its output is NaN,
+ * and records the timeout in the stream's workspace).  Synchronises
+ * `stream`, then returns NYS_OK, or NYS_ERR_HIP with a message in
+ * nystrom_last_error() when a call on `stream` since the previous check
+ * timed out (the record is cleared by the check).  The wait can only run
+ * out when the blocks are not all resident together, e.g. when other work
+ * fills the device's compute units. */
+int nystrom_check_status(struct ihipStream_t* stream);
+
+/* Test hooks for the failure paths (not for production use; both settings
+ * are process-wide and stay until changed):
+ *   nystrom_debug_set_rendezvous_spins: the bound on the rendezvous polls
+ *     above (default 2^20, about a second; 0 makes every wait give up at
+ *     once, so every kernel still exits normally);
+ *   nystrom_debug_set_workspace_cap: a cap in bytes on the device workspace
+ *     (0 = none); a call that needs more fails with NYS_ERR_HIP before
+ *     anything is enqueued, so out is not written. */
+void nystrom_debug_set_rendezvous_spins(unsigned spins);
+void nystrom_debug_set_workspace_cap(size_t bytes);
+
 /* Kernel timing for benchmarks (not part of the computation).  While
  * enabled (on != 0), every call brackets each kernel it launches with a
  * pair of hipEvents recorded on the call's stream.  nystrom_profile_collect

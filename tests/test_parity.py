@@ -50,6 +50,56 @@ def test_workload_peaked(idx):
     _check(f"workload{idx}-peaked", x, w.dtype, w.m, w.n_iter, w.init_option, conv=False)
 
 
+# Centred attention error: the attention term minus 1 vbar^T, vbar the mean
+# of the batch row's kept V rows, i.e. what separates the computed attention
+# from a uniform average.  In workloads 3-5 the softmaxes are nearly uniform
+# (logit std 0.125, 0.022, 0.0625), so the attention-only output is mostly
+# 1 vbar^T (the centred term is 1.8e-2, 1.9e-3 and 3.8e-3 of its norm) and
+# its relative error alone would not see a wrong deviation from uniform.
+# The bf16 output's own rounding (2^-9 of |out|) is already of the size of
+# the centred term, so the gate is on what the kernels add beyond it: per
+# (b, h) slice, with e the centred error of the GPU output and r that of
+# the oracle output rounded to bf16 (RNE), the excess sqrt(max(e^2 - r^2, 0))
+# estimates the centred error before the final rounding.  The gate is 5x the
+# excess measured on MI355X with these kernels; an attention path with the
+# wrong deviation from uniform has an excess near 1.
+CENTRED_EXCESS_MEASURED = {3: 2.83e-2, 4: 1.82e-1, 5: 9.49e-2}
+
+
+def _centred(o, x, mask):
+    v = x["v"].astype(np.float64)
+    if mask and x.get("key_mask") is not None:
+        keep = x["key_mask"].astype(np.float64)[:, None, :, None]
+    else:
+        keep = np.ones(v.shape[:1] + (1,) + v.shape[2:3] + (1,))
+    vbar = (v * keep).sum(axis=2, keepdims=True) / keep.sum(axis=2, keepdims=True)
+    return o - vbar
+
+
+def _slice_rel(a, b):
+    num = np.sqrt(((a - b) ** 2).sum(axis=(-1, -2)))
+    return num / np.sqrt((b ** 2).sum(axis=(-1, -2)))
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_workload_centred_attention(idx):
+    import torch
+    w = WORKLOADS[idx]
+    x = make_inputs(w)
+    announce(f"workload{idx}-centred dtype={w.dtype}")
+    got = run_gpu(x, w.dtype, w.m, w.n_iter, w.init_option, conv=False)
+    ref = oracle_out(x, w.m, w.n_iter, w.init_option, conv=False)
+    rounded = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    cref = _centred(ref, x, True)
+    e = _slice_rel(_centred(got, x, True), cref)
+    r = _slice_rel(_centred(rounded, x, True), cref)
+    excess = float(np.sqrt(np.maximum(e ** 2 - r ** 2, 0.0)).max())
+    gate = 5.0 * CENTRED_EXCESS_MEASURED[idx]
+    announce(f"workload{idx}-centred: max error {e.max():.3e}, rounding floor {r.max():.3e}, "
+             f"excess {excess:.3e} (gate {gate:.2e})")
+    assert excess < gate
+
+
 # ------------------------------------------------------------- edge cases ---
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("n", [256, 100, 1, 33])

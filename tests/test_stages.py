@@ -9,10 +9,41 @@ from gpu_util import announce, to_dev
 
 pytestmark = pytest.mark.gpu
 
+# Generic gates (padded landmark counts and other shapes without a
+# measured record below).
 STAGE_TOL = {
     "fp32": dict(qt=1e-6, kt=1e-6, A=1e-5, c=1e-6, Z=2e-3, BV=1e-4, W=2e-3),
     "bf16": dict(qt=1e-6, kt=1e-6, A=1e-5, c=1e-6, Z=5e-3, BV=5e-3, W=1e-2),
 }
+
+# Per-workload gates from an error model: each stage's relative error as
+# measured on MI355X with these kernels (the path is deterministic, so a
+# rerun gives the same bits), times five, with a floor of 1e-6.  What sets
+# the measured values:
+#   qt, kt, A, c   float32 sums and float32 / split-bf16 Gram products: ~1e-7;
+#   Z (fp32 I/O)   float32 matrix-core products: ~1e-6;
+#   Z (bf16 I/O)   single fp16 products (11-bit operands) for m <= 128, whose
+#                  rounding the 24-product chain amplifies by up to cond(A);
+#                  split-bf16 products for m = 256, where A is nearly J/m
+#                  (logit std ~0.004) and far worse conditioned;
+#   BV, W (bf16)   bf16 softmax weights P and bf16 V operands (2^-9 per
+#                  element) averaged over the keys: ~1e-3.
+# A stage degraded by more than 5x (a wrong operand scaling, a dropped
+# split term, a mis-ordered product) fails here even where the final output
+# stays within its 2e-2 gate.
+MEASURED = {
+    (1, 1.0): dict(qt=5.0e-8, kt=5.1e-8, A=7.8e-8, c=1.6e-7, Z=6.1e-7, BV=4.6e-6, W=8.1e-6),
+    (2, 1.0): dict(qt=5.8e-8, kt=5.8e-8, A=6.1e-8, c=1.5e-7, Z=8.8e-7, BV=4.6e-6, W=9.0e-6),
+    (3, 1.0): dict(qt=3.1e-8, kt=3.1e-8, A=8.8e-8, c=3.2e-7, Z=7.0e-5, BV=1.5e-3, W=3.2e-3),
+    (4, 1.0): dict(qt=3.1e-8, kt=3.1e-8, A=5.5e-8, c=1.6e-7, Z=1.4e-4, BV=1.2e-3, W=2.9e-4),
+    (5, 1.0): dict(qt=3.2e-8, kt=3.2e-8, A=5.8e-8, c=9.1e-8, Z=1.1e-3, BV=1.3e-3, W=3.8e-4),
+    (2, 4.0): dict(qt=5.8e-8, kt=5.8e-8, A=4.3e-7, c=1.2e-7, Z=1.1e-6, BV=1.2e-5, W=1.3e-5),
+    (3, 4.0): dict(qt=3.1e-8, kt=3.1e-8, A=1.1e-6, c=2.8e-7, Z=3.4e-4, BV=3.5e-3, W=3.5e-3),
+}
+
+
+def stage_gates(idx, peak):
+    return {k: max(1e-6, 5.0 * v) for k, v in MEASURED[(idx, peak)].items()}
 
 
 def _rel(a, b):
@@ -44,9 +75,9 @@ def test_stages(idx, peak):
                 Z=_rel(got["Z"], ref["Z"]), BV=_rel(got["BV"], ref["BV"]),
                 W=_rel(got["W"], ref["W"]))
     announce("  " + " ".join(f"{k2}={v2:.2e}" for k2, v2 in errs.items()))
-    tol = STAGE_TOL[w.dtype]
-    bad = {k2: v2 for k2, v2 in errs.items() if not v2 < tol[k2]}
-    assert not bad, f"stage errors above tolerance: {bad}"
+    tol = stage_gates(idx, peak)
+    bad = {k2: (v2, tol[k2]) for k2, v2 in errs.items() if not v2 < tol[k2]}
+    assert not bad, f"stage errors above the gates (error, gate): {bad}"
 
 
 @pytest.mark.parametrize("dtype,m,n", [("fp32", 48, 480), ("bf16", 50, 400), ("bf16", 144, 576)])
