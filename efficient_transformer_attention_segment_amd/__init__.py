@@ -56,6 +56,9 @@ def _load():
     lib.nystrom_attention_ex.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                          _P, _L, _L, _L, _P]
     lib.nystrom_attention_ex.restype = _I
+    lib.nystrom_attention_noalloc.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                              _P, _L, _L, _L, _P]
+    lib.nystrom_attention_noalloc.restype = _I
     lib.nystrom_attention_probs.argtypes = [_I, _P, _P, _P, _L, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                             _P, _L, _L, _L, _P, _P]
     lib.nystrom_attention_probs.restype = _I

@@ -9,6 +9,10 @@
 
 #include "host.hpp"
 
+// Device scratch of the allocation-free entry point (see static_scratch):
+// one copy per device, for the life of the process.
+static __device__ __align__(256) char scratch[NYS_NOALLOC_SCRATCH_BYTES];
+
 namespace nys {
 namespace host {
 
@@ -257,9 +261,16 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
         Strides so, int B,
         int H, int n,
         int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout,
-        void* probs = nullptr) {
+        void* probs = nullptr, Workspace* fixed = nullptr) {
   int rc = check_call(sizeof(IO), q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, probs);
   if (rc != NYS_OK) return rc;
+  if (fixed != nullptr && m != n) {
+    const size_t need = make_plan(B, H, n, m, d).total;
+    if (need > fixed->cap)
+      return fail(NYS_ERR_UNSUPPORTED,
+                  "this shape needs %zu bytes of scratch; the allocation-free entry point has %zu (NYS_NOALLOC_SCRATCH_BYTES)",
+                  need, fixed->cap);
+  }
   if (m == n) {
     if (d == 32) return launch_exact<IO, 32>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
     if (d == 128) return launch_exact<IO, 128>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
@@ -271,15 +282,61 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
   p.so = so;
   p.probs = probs;
   std::lock_guard<std::mutex> lk(g_mu);
-  Workspace* w = nullptr;
-  rc = get_workspace(st, p.total, &w);
-  if (rc != NYS_OK) return rc;
+  Workspace* w = fixed;
+  if (w == nullptr) {
+    rc = get_workspace(st, p.total, &w);
+    if (rc != NYS_OK) return rc;
+  }
   rc = d == 32    ? dispatch_m<IO, 32>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st)
        : d == 128 ? dispatch_m<IO, 128>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st)
                   : dispatch_m<IO, 64>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st);
   if (wout) *wout = w;
   if (pout) *pout = p;
   return rc;
+}
+
+// --------------------------------------- allocation-free entry point ---
+// nystrom_attention_noalloc runs the same launch sequence in a fixed scratch
+// array instead of the grow-only workspace, for callers that cannot
+// allocate.  Each device holds its own copy of the array (at its own
+// address) from module load to process end; the host never passes the
+// array's name to a kernel, only the address hipGetSymbolAddress gives for
+// the current device.
+
+// Fills n 16-byte words at p with zeros (a kernel rather than a memset, so
+// a caller may capture it in a graph).
+__global__ __launch_bounds__(256) void k_fill_zero(uint4* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+std::mutex g_scratch_mu;
+std::map<int, char*> g_scratch;  // device -> address of its scratch array
+
+// The scratch array of the current device: its address is looked up once
+// per device (with the device current), and at that first use the head of
+// the array (the zero page every kernel reads as zero rows, and the status
+// word) is cleared by a fill kernel on `st`.
+int static_scratch(hipStream_t st, Workspace* out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(NYS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    if (reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+      return fail(NYS_ERR_HIP, "scratch array on device %d is not 256-byte aligned", dev);
+    constexpr size_t words = HEAD_BYTES / 16;
+    hipLaunchKernelGGL(k_fill_zero, dim3((words + 255) / 256), dim3(256), 0, st, static_cast<uint4*>(ptr), words);
+    HIP_TRY(hipGetLastError());
+    it = g_scratch.emplace(dev, static_cast<char*>(ptr)).first;
+  }
+  out->buf = it->second;
+  out->cap = NYS_NOALLOC_SCRATCH_BYTES;
+  return NYS_OK;
 }
 
 // ------------------------------------------- module: the q/k/v projection ---
@@ -486,6 +543,33 @@ __attribute__((visibility("default"))) int nystrom_attention_ex(
   }
 }
 
+__attribute__((visibility("default"))) int nystrom_attention_noalloc(
+    int dtype, const void* q, const void* k, const void* v, long long in_batch_stride, long long in_head_stride,
+    long long in_token_stride, const uint8_t* key_mask, const float* conv_w, int conv_kernel_size, int B, int H, int n,
+    int d, int m, int n_iter, int init_option, void* out, long long out_batch_stride, long long out_head_stride,
+    long long out_token_stride, struct ihipStream_t* stream) {
+  try {
+    g_err.clear();
+    if (dtype != 0 && dtype != 1) return fail(NYS_ERR_INVALID, "dtype=%d is not 0 (float32) or 1 (bf16)", dtype);
+    const Strides si{in_batch_stride, in_head_stride, in_token_stride};
+    const Strides so{out_batch_stride, out_head_stride, out_token_stride};
+    // every host-side check first: an invalid call touches nothing, not even the scratch
+    int rc = check_call(dtype == 0 ? 4 : 2, q, k, v, si, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter,
+                        init_option, out, nullptr);
+    if (rc != NYS_OK) return rc;
+    Workspace ws;
+    rc = static_scratch(stream, &ws);
+    if (rc != NYS_OK) return rc;
+    if (dtype == 0)
+      return run<float>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                        stream, nullptr, nullptr, nullptr, &ws);
+    return run<u16>(q, k, v, si, key_mask, conv_w, conv_kernel_size, so, B, H, n, d, m, n_iter, init_option, out,
+                    stream, nullptr, nullptr, nullptr, &ws);
+  } catch (...) {
+    return fail(NYS_ERR_HIP, "unexpected host exception");
+  }
+}
+
 __attribute__((visibility("default"))) int nystrom_attention_probs(
     int dtype, const void* q, const void* k, const void* v, long long in_batch_stride, long long in_head_stride,
     long long in_token_stride, const uint8_t* key_mask, const float* conv_w, int conv_kernel_size, int B, int H, int n,
@@ -631,15 +715,30 @@ __attribute__((visibility("default"))) int nystrom_check_status(struct ihipStrea
     HIP_TRY(hipStreamSynchronize(stream));
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || it->second.buf == nullptr) return NYS_OK;
+    // the stream's workspace and the device's allocation-free scratch
+    char* words[2] = {nullptr, nullptr};
+    {
+      std::lock_guard<std::mutex> lk(g_mu);
+      auto it = g_ws.find({dev, stream});
+      if (it != g_ws.end() && it->second.buf != nullptr) words[0] = it->second.buf + STATUS_OFF;
+    }
+    {
+      std::lock_guard<std::mutex> lk(g_scratch_mu);
+      auto it = g_scratch.find(dev);
+      if (it != g_scratch.end()) words[1] = it->second + STATUS_OFF;
+    }
     unsigned status = 0;
-    void* const word = it->second.buf + STATUS_OFF;
-    HIP_TRY(hipMemcpy(&status, word, sizeof status, hipMemcpyDeviceToHost));
+    for (char* word : words) {
+      if (word == nullptr) continue;
+      unsigned s = 0;
+      HIP_TRY(hipMemcpy(&s, word, sizeof s, hipMemcpyDeviceToHost));
+      if (s != 0) {
+        const unsigned zero = 0;
+        HIP_TRY(hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice));
+      }
+      status |= s;
+    }
     if (status == 0) return NYS_OK;
-    const unsigned zero = 0;
-    HIP_TRY(hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice));
     return fail(NYS_ERR_HIP,
                 "a call on this stream gave up waiting for the pseudo-inverse blocks' rendezvous (original init): "
                 "its scale c and output are NaN; the blocks were not all resident together");

@@ -131,6 +131,31 @@ int nystrom_attention_ex(int dtype, const void* q, const void* k, const void* v,
                          long long out_batch_stride, long long out_head_stride,
                          long long out_token_stride, struct ihipStream_t* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * operation, arguments and errors of nystrom_attention_ex, with its
+ * scratch in a fixed library-owned device array of
+ * NYS_NOALLOC_SCRATCH_BYTES (one per device, held from the first call on
+ * that device until the process ends) instead of the grow-only workspace.
+ * The call allocates nothing (no hipMalloc, no hipFree, no allocating
+ * library routine); the caller still owns q, k, v, key_mask, conv_w and
+ * out.  Shapes whose scratch would exceed the array are rejected with
+ * NYS_ERR_UNSUPPORTED before anything is enqueued (every workload up to
+ * B H = 4 x 12 at n = 4096, m = 64, or n = 65536 at H = 4, m = 256, fits).
+ * The first call on a device enqueues one small kernel on `stream` that
+ * clears the head of the array.  Every call on a device shares that
+ * device's array, and each call's kernels clear what they need zeroed;
+ * calls that may overlap on one device (on different streams, or from
+ * different threads) race on it, so the caller must order them. */
+#define NYS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int nystrom_attention_noalloc(int dtype, const void* q, const void* k, const void* v,
+                              long long in_batch_stride, long long in_head_stride,
+                              long long in_token_stride, const uint8_t* key_mask,
+                              const float* conv_w, int conv_kernel_size, int B, int H,
+                              int n, int d, int m, int n_iter, int init_option, void* out,
+                              long long out_batch_stride, long long out_head_stride,
+                              long long out_token_stride, struct ihipStream_t* stream);
+
 /* nystrom_attention_ex, and also the attention weights (output_attentions).
  *
  * Page [P1] section 2.4 names attention_probs = kernel_1 times the iterative
