@@ -11,7 +11,9 @@
 //   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
 //                  blocks (m <= 128) and the B V partial blocks, so the
 //                  pseudo-inverse chain runs beside the K/V stream
-//     (m > 128: k_pinv_init + 4 k_pinv_gemm launches per iteration)
+//     (m > 128, bf16 I/O: k_gram_rows, then 3 k_pinv_mm launches per
+//     iteration before it; float32 I/O: k_gram, then k_pinv_init and 4
+//     k_pinv_gemm launches per iteration after it)
 //   4 k_mw         B V from the partials, W = Z (B V) and its operand
 //                  fragments
 //   5 k_out_stream F W + conv(V) -> out (bf16 I/O; k_out for float32)
@@ -29,6 +31,7 @@
 #include "k_merge.hpp"
 #include "k_out.hpp"
 #include "k_pinv.hpp"
+#include "k_pinv_mm.hpp"
 #include "k_probs.hpp"
 
 namespace nys {
@@ -89,7 +92,27 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   // the pseudo-inverse blocks form A themselves only at d = 64 (their LDS
   // plan holds 64-channel landmarks)
   const bool fuse_gram = D == HD && M <= 128 && (init_option != 0 || p.npinv <= fuse_cap);
-  if (!fuse_gram) {
+  // More than 128 landmarks with bf16 I/O and 1 .. 8 iterations: the
+  // expanded three-level iteration on fp16 products (k_pinv_mm.hpp), from
+  // a row-split Gram.  Otherwise (float32 I/O, n_iter 0 or above 8) the
+  // one-block Gram and the literal four-product iteration.  (On a side
+  // stream beside the B V launch the chain was slower, 234 against 206 us
+  // at 1 x 4 x 65536, m = 256: the B V blocks hold every CU, so the side
+  // launches only queue behind them.)
+  constexpr bool MM_OK = M > 128 && sizeof(IO) == 2;
+  const bool mm_path = MM_OK && n_iter >= 1 && n_iter <= PINV_F16_MAX_ITER;
+  const hipStream_t pst = st;  // stream of the pseudo-inverse launches
+  if constexpr (MM_OK) {
+    if (mm_path) {
+      constexpr int grl = gram_rows_lds_bytes<M, D>();
+      HIP_TRY(allow_lds(k_gram_rows<M, D>, grl));
+      float* const colpart = at<float>(w, p.off_colpart);
+      float* const rowpart = at<float>(w, p.off_rowpart);
+      HIP_TRY(launch("k_gram_rows", k_gram_rows<M, D>, dim3(M / 32, p.BH), dim3(128), (uint32_t)grl, pst, la,
+                     at<float>(w, p.off_AT), colpart, rowpart));
+    }
+  }
+  if (!fuse_gram && !mm_path) {
     constexpr size_t glds = gram_lds_bytes<M, sizeof(IO) == 4, D>();
     HIP_TRY(allow_lds(k_gram<M, sizeof(IO) == 4, D>, glds));
     HIP_TRY(launch("k_gram", k_gram<M, sizeof(IO) == 4, D>, dim3(p.BH), dim3(64 * gram_waves<M>()), (uint32_t)glds,
@@ -138,7 +161,44 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   if (brc != NYS_OK) return brc;
 
   const float* Zfinal = pa.Z;
-  if constexpr (M > 128) {
+  if constexpr (MM_OK) {
+    if (mm_path) {
+      PinvMMArgs mm;
+      mm.A = la.A;
+      mm.AT = at<float>(w, p.off_AT);
+      mm.X = at<float>(w, p.off_X);
+      mm.Xt = at<float>(w, p.off_Xt);
+      mm.X2t = at<float>(w, p.off_X2t);
+      mm.W = at<float>(w, p.off_T2);
+      mm.pa = pa;
+      mm.colpart = at<float>(w, p.off_colpart);
+      mm.colmax = la.colmax;
+      mm.rowmax = la.rowmax;
+      mm.rowpart = at<float>(w, p.off_rowpart);
+      float* Zb[2] = {at<float>(w, p.off_Z), at<float>(w, p.off_Z2)};
+      float* Ztb[2] = {at<float>(w, p.off_Zt), at<float>(w, p.off_Zt2)};
+      constexpr int NT2 = (M / PMM_T) * (M / PMM_T);
+      constexpr int l1 = pinv_mm_lds_bytes<M, 1>(), l2 = pinv_mm_lds_bytes<M, 2>(), l3 = pinv_mm_lds_bytes<M, 3>();
+      HIP_TRY(allow_lds(k_pinv_mm<M, 1>, l1));
+      HIP_TRY(allow_lds(k_pinv_mm<M, 2>, l2));
+      HIP_TRY(allow_lds(k_pinv_mm<M, 3>, l3));
+      for (int it = 0; it < n_iter; ++it) {
+        mm.first = it == 0 ? 1 : 0;
+        mm.Z = Zb[it % 2];
+        mm.Zt = Ztb[it % 2];
+        mm.Zn = Zb[(it + 1) % 2];
+        mm.Znt = Ztb[(it + 1) % 2];
+        HIP_TRY(launch("k_pinv_mm1", k_pinv_mm<M, 1>, dim3(pinv_mm_grid(NT2, p.BH)), dim3(256), (uint32_t)l1, pst,
+                       mm));
+        HIP_TRY(launch("k_pinv_mm2", k_pinv_mm<M, 2>, dim3(pinv_mm_grid(2 * NT2, p.BH)), dim3(256), (uint32_t)l2,
+                       pst, mm));
+        HIP_TRY(launch("k_pinv_mm3", k_pinv_mm<M, 3>, dim3(pinv_mm_grid(NT2, p.BH)), dim3(256), (uint32_t)l3, pst,
+                       mm));
+      }
+      Zfinal = Zb[n_iter % 2];
+    }
+  }
+  if constexpr (M > 128) if (!mm_path) {
     HIP_TRY(launch("k_pinv_init", k_pinv_init, dim3((M / 32) * (M / 32), p.BH), dim3(256), 0, st, pa, M));
     float* Zc = pa.Z;
     float* Zn = at<float>(w, p.off_Z2);

@@ -47,6 +47,7 @@ struct Plan {
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
   size_t off_slots, off_junk, off_lse;
+  size_t off_AT, off_Xt, off_X2t, off_Zt, off_Zt2, off_colpart, off_rowpart;  // m > 128, bf16 I/O
   size_t total;
 };
 

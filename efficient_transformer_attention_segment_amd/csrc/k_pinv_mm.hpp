@@ -1,0 +1,349 @@
+// Iterative Moore-Penrose inverse for more than 128 landmarks (bf16 I/O):
+// a launch sequence over global memory, three launches per iteration.
+//
+// Page: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), section 2.5:
+// Z_0 = A^T / c, then n_iter times X = A Z and
+// Z <- (1/4) Z (13 I - X (15 I - X (7 I - X))).
+//
+// The update is evaluated with the product expanded,
+//   Z' = (13 Z - 15 Z X + 7 Z X^2 - Z X^3) / 4,
+// which equals the nested form in exact arithmetic, as
+//   level 1  X  = A Z
+//   level 2  X2 = X X  and  W = Z X          (independent: one launch)
+//   level 3  Z' = (13 Z - 15 W + 7 W X - W X2) / 4
+// X is still recomputed from A and Z every iteration (self-correcting).
+// Every product operand is a matrix the iteration produced (Z, X, W, X2),
+// never a shifted difference such as 13 I - T2 whose rounding to a 16-bit
+// operand loses its small part: with single fp16 products this order keeps
+// the iterate within about 1e-4 of the float64 iteration where the nested
+// order, rounded the same way, drifts by several per cent.  The linear
+// combinations run in float32 in the epilogues.
+//
+// k_gram_rows: A = softmax(Qt Kt^T) by 32-row blocks (grid (M / 32, BH)),
+//   split-bf16 products as in the one-block Gram; writes A, A^T and per
+//   block the column sums and the largest row sum.
+// k_pinv_mm<LEVEL>: 32 x 32 output tiles (4 waves of one 16 x 16 tile
+//   each, K = M in fp16 16x16x32 matrix-core steps), every tile of a head on
+//   one XCD.  Level 1 of the first iteration also forms c from the Gram
+//   partials (column sums of the row blocks added in order).  Operand
+//   panels are read as float32 rows (the left factor's rows, and the rows
+//   of the right factor's transpose, which every level also writes), scaled
+//   and rounded to fp16 into LDS once per block.  In the first iteration
+//   Z = A^T / c is read from A^T (rows of Z) and A (rows of Z^T).
+#pragma once
+
+#include "common.hpp"
+#include "k_landmark.hpp"
+#include "k_pinv.hpp"
+
+namespace nys {
+
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------ Gram rows ---
+template <int M, int D>
+constexpr int gram_rows_lds_bytes() {
+  return 2 * M * (D + 8) * 2 + 4 * (2 * M + 2);
+}
+
+// grid (M / 32, BH), 128 threads: wave w forms row tile 2 blockIdx.x + w.
+template <int M, int D>
+__global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __restrict__ AT,
+                                                   float* __restrict__ colpart, float* __restrict__ rowpart) {
+  extern __shared__ __align__(16) char gr_smem[];
+  constexpr int TM = M / 16, DK = D / 32, KLD = D + 8;
+  __bf16* const kb = reinterpret_cast<__bf16*>(gr_smem);  // hi rows 0 .. M-1, lo rows M .. 2M-1
+  float* const csum = reinterpret_cast<float*>(gr_smem + 2 * M * KLD * 2);
+  float* const rmx = csum + 2 * M;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, rt = 2 * blockIdx.x + wave;
+  {
+    const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * D);
+    const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * D);
+    for (int i = threadIdx.x; i < M * (D / 8); i += 128) {
+      *reinterpret_cast<uint4*>(kb + (i / (D / 8)) * KLD + 8 * (i % (D / 8))) = kh[i];
+      *reinterpret_cast<uint4*>(kb + (M + i / (D / 8)) * KLD + 8 * (i % (D / 8))) = kl[i];
+    }
+  }
+  Frag2 af[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    const size_t off = ((size_t)bh * M + rt * 16 + c16) * D + ks * 32 + g * 8;
+    af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
+    af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
+  }
+  __syncthreads();
+  f32x4 acc[TM];
+#pragma unroll
+  for (int ct = 0; ct < TM; ++ct) {
+    acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      const int row = ct * 16 + c16, col = ks * 32 + g * 8;
+      Frag2 bf;
+      bf.hi = *reinterpret_cast<const bf16x8*>(kb + row * KLD + col);
+      bf.lo = *reinterpret_cast<const bf16x8*>(kb + (M + row) * KLD + col);
+      acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+    }
+  }
+  if (a.mr < M) pad_mask_cols(acc, a.mr);
+  float rmax_w = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) mx = fmaxf(mx, acc[ct][r]);
+    mx = max16(mx);
+    float s = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+      const float p = fast_exp2((acc[ct][r] - mx) * LOG2E);
+      acc[ct][r] = p;
+      s += p;
+    }
+    s = sum16(s);
+    const float inv = rt * 16 + g * 4 + r < a.mr ? 1.0f / s : 0.f;
+    float rs = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+      acc[ct][r] *= inv;
+      rs += acc[ct][r];
+    }
+    rmax_w = fmaxf(rmax_w, sum16(rs));
+  }
+  float* const Ah = a.A + (size_t)bh * M * M;
+  float* const ATh = AT + (size_t)bh * M * M;
+  const int row4 = rt * 16 + 4 * g;
+#pragma unroll
+  for (int ct = 0; ct < TM; ++ct) {
+    const int col = ct * 16 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ah[(size_t)(row4 + r) * M + col] = acc[ct][r];
+    *reinterpret_cast<float4*>(ATh + (size_t)col * M + row4) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+    const float cs = sum_g(acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3]);
+    if (g == 0) csum[wave * M + col] = cs;
+  }
+  rmax_w = max_g(rmax_w);
+  if (lane == 0) rmx[wave] = rmax_w;
+  __syncthreads();
+  float* const cp = colpart + ((size_t)bh * (M / 32) + blockIdx.x) * M;
+  for (int j = threadIdx.x; j < M; j += 128) cp[j] = csum[j] + csum[M + j];
+  if (threadIdx.x == 0) rowpart[(size_t)bh * (M / 32) + blockIdx.x] = fmaxf(rmx[0], rmx[1]);
+}
+
+// -------------------------------------------------------------- products ---
+struct PinvMMArgs {
+  const float* A;    // [BH][M][M] rows of A
+  const float* AT;   // [BH][M][M] rows of A^T
+  const float* Z;    // rows of Z_k (k >= 1)
+  const float* Zt;   // rows of Z_k^T
+  float* X;          // rows of X
+  float* Xt;         // rows of X^T
+  float* X2t;        // rows of (X^2)^T
+  float* W;          // rows of W = Z X
+  float* Zn;         // rows of Z_{k+1}
+  float* Znt;        // rows of Z_{k+1}^T
+  const float* colpart;  // [BH][M / 32][M] Gram column-sum partials
+  const float* rowpart;  // [BH][M / 32] Gram row-sum maxima
+  float* colmax;     // [BH] out: head's largest column sum of A
+  float* rowmax;     // [BH] out: head's largest row sum of A
+  PinvArgs pa;       // BH, init option; cscale out
+  int first;         // 1: k = 0, Z = A^T / c
+};
+
+constexpr int PMM_T = 32;  // output tile
+
+template <int M>
+constexpr int pinv_mm_ld() {
+  return M + 8;  // fp16 panel row stride (16-byte chunks land on distinct banks)
+}
+template <int M, int LEVEL>
+constexpr int pinv_mm_lds_bytes() {
+  return (LEVEL == 3 ? 3 : 2) * PMM_T * pinv_mm_ld<M>() * 2;
+}
+
+// Rows r0 .. r0 + 31 of a float32 [M][M] matrix, times s, as fp16 rows of
+// an LDS panel (row stride pinv_mm_ld): the loads first (N float4 per
+// thread), then the stores.
+template <int M>
+struct PanelLoad {
+  static constexpr int N = PMM_T * M / 4 / 256;
+  float4 x[N];
+  __device__ __forceinline__ void load(const float* src, int r0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + 256 * i;  // float4 index within the panel
+      x[i] = *reinterpret_cast<const float4*>(src + (size_t)(r0 + idx / (M / 4)) * M + 4 * (idx % (M / 4)));
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* lds, float s) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 h = {(_Float16)(x[i].x * s), (_Float16)(x[i].y * s), (_Float16)(x[i].z * s), (_Float16)(x[i].w * s)};
+      *reinterpret_cast<h4*>(lds + (idx / (M / 4)) * pinv_mm_ld<M>() + 4 * (idx % (M / 4))) = h;
+    }
+  }
+};
+
+// C tile (16 x 16) of the wave: sum_k Lp[16 it + i][k] Rp[16 jt + j][k].
+template <int M>
+__device__ __forceinline__ f32x4 panel_mm(const _Float16* Lp, const _Float16* Rp, int it, int jt) {
+  constexpr int LD = pinv_mm_ld<M>();
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const _Float16* pa = Lp + (16 * it + c16) * LD + 8 * g;
+  const _Float16* pb = Rp + (16 * jt + c16) * LD + 8 * g;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < M / 32; ++ks) {
+    const h16x8 av = *reinterpret_cast<const h16x8*>(pa + 32 * ks);
+    const h16x8 bv = *reinterpret_cast<const h16x8*>(pb + 32 * ks);
+    acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[ks & 1], 0, 0, 0);
+  }
+  return acc[0] + acc[1];
+}
+
+// Stores the wave's C tile (rows row4 .. row4 + 3, column col) of a
+// product into C (row-major) and, when Ct is given, C^T (row-major).
+__device__ __forceinline__ void store_c(float* C, float* Ct, int M, int row4, int col, const f32x4 v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(size_t)(row4 + r) * M + col] = v[r];
+  if (Ct != nullptr) *reinterpret_cast<float4*>(Ct + (size_t)col * M + row4) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Workgroups per launch: tiles per head (T = (M / 32)^2 for levels 1 and
+// 3, 2 T for level 2: X2 tiles, then W tiles) for every head, placed so that
+// all of a head's tiles run on one XCD (workgroup i of a launch runs on XCD
+// i mod 8): the matrices one launch writes are then read by the next from
+// the L2 of the XCD that wrote them.  Heads h and h + 8 share XCD h mod 8.
+__host__ __device__ constexpr int pinv_mm_grid(int tiles, int BH) { return 8 * tiles * ((BH + 7) / 8); }
+
+// c for head bh from the Gram partials (k_gram_rows): the largest column sum
+// (row blocks added in order) times the largest row sum, over every head for
+// the original init, over head bh alone for the exact-coefficient init.  Also
+// head bh's own two maxima.  Whole workgroup (256 threads); red: 12 floats.
+template <int M>
+__device__ float pinv_c_from_parts(const float* colpart, const float* rowpart, int bh, int BH, int init_option,
+                                   float* red, float& cm_own, float& rm_own) {
+  constexpr int NB = M / 32;
+  const int h0 = init_option == 0 ? 0 : bh, h1 = init_option == 0 ? BH : bh + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float cm = 0.f, rm = 0.f, cmo = 0.f, rmo = 0.f;
+  for (int i = threadIdx.x; i < (h1 - h0) * M; i += 256) {
+    const int h = h0 + i / M, j = i % M;
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s += colpart[((size_t)h * NB + b) * M + j];
+    cm = fmaxf(cm, s);
+    if (h == bh) cmo = fmaxf(cmo, s);
+  }
+  for (int i = threadIdx.x; i < (h1 - h0) * NB; i += 256) {
+    const float r = rowpart[(size_t)h0 * NB + i];
+    rm = fmaxf(rm, r);
+    if (h0 + i / NB == bh) rmo = fmaxf(rmo, r);
+  }
+  cm = wave_max(cm);
+  rm = wave_max(rm);
+  cmo = wave_max(cmo);
+  rmo = wave_max(rmo);
+  if (lane == 0) {
+    red[wave] = cm;
+    red[4 + wave] = rm;
+    red[8 + wave] = cmo;
+    red[12 + wave] = rmo;
+  }
+  __syncthreads();
+  auto max4 = [&](int o) { return fmaxf(fmaxf(red[o], red[o + 1]), fmaxf(red[o + 2], red[o + 3])); };
+  cm_own = max4(8);
+  rm_own = max4(12);
+  return max4(0) * max4(4);
+}
+
+template <int M, int LEVEL>
+__global__ __launch_bounds__(256) void k_pinv_mm(PinvMMArgs a) {
+  extern __shared__ __align__(16) _Float16 pm_lds[];
+  __shared__ float red[16];
+  constexpr int NT = M / PMM_T, LD = pinv_mm_ld<M>(), PANEL = PMM_T * LD;
+  constexpr int TILES = (LEVEL == 2 ? 2 : 1) * NT * NT;
+  const int L = blockIdx.x, xcd = L & 7, s = L >> 3;
+  const int bh = xcd + 8 * (s / TILES);
+  if (bh >= a.pa.BH) return;  // whole workgroup, before any barrier
+  const int t2 = s % TILES;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const bool second = LEVEL == 2 && t2 >= NT * NT;  // level 2: the W = Z X tiles
+  const int tile = second ? t2 - NT * NT : t2;
+  const int ti = tile / NT, tj = tile % NT;
+  const size_t mo = (size_t)bh * M * M;
+  // 1 / c: level 1 of the first iteration forms c from the Gram partials
+  // (and writes it with the head's maxima); later launches read it back
+  float invc = 1.f;
+  if (a.first) {
+    if (LEVEL == 1) {
+      float cmo, rmo;
+      const float c = pinv_c_from_parts<M>(a.colpart, a.rowpart, bh, a.pa.BH, a.pa.init_option, red, cmo, rmo);
+      if (tile == 0 && threadIdx.x == 0) {
+        a.pa.cscale[bh] = c;
+        a.colmax[bh] = cmo;
+        a.rowmax[bh] = rmo;
+      }
+      invc = 1.0f / c;
+    } else {
+      invc = 1.0f / a.pa.cscale[bh];
+    }
+  }
+  // rows of Z and of Z^T (A^T / c and A / c in the first iteration)
+  const float* const Zr = a.first ? a.AT + mo : a.Z + mo;
+  const float* const Ztr = a.first ? a.A + mo : a.Zt + mo;
+  _Float16* const P0 = pm_lds;
+  _Float16* const P1 = pm_lds + PANEL;
+  _Float16* const P2 = pm_lds + 2 * PANEL;
+  const int r0 = PMM_T * ti, c0 = PMM_T * tj;
+  if constexpr (LEVEL == 1) {  // X = A Z
+    PanelLoad<M> l, r;
+    l.load(a.A + mo, r0);
+    r.load(Ztr, c0);
+    l.store(P0, 1.f);
+    r.store(P1, invc);
+  } else if constexpr (LEVEL == 2) {  // X2 = X X, or W = Z X
+    PanelLoad<M> l, r;
+    l.load(second ? Zr : a.X + mo, r0);
+    r.load(a.Xt + mo, c0);
+    l.store(P0, second ? invc : 1.f);
+    r.store(P1, 1.f);
+  } else {  // Z' = (13 Z - 15 W + 7 W X - W X2) / 4
+    PanelLoad<M> l, r1, r2;
+    l.load(a.W + mo, r0);
+    r1.load(a.Xt + mo, c0);
+    r2.load(a.X2t + mo, c0);
+    l.store(P0, 1.f);
+    r1.store(P1, 1.f);
+    r2.store(P2, 1.f);
+  }
+  __syncthreads();
+  const int it = wave >> 1, jt = wave & 1;
+  const int row4 = r0 + 16 * it + 4 * g, col = c0 + 16 * jt + c16;
+  const f32x4 acc = panel_mm<M>(P0, P1, it, jt);
+  if constexpr (LEVEL == 1) {
+    store_c(a.X + mo, a.Xt + mo, M, row4, col, acc);
+  } else if constexpr (LEVEL == 2) {
+    if (second)
+      store_c(a.W + mo, nullptr, M, row4, col, acc);
+    else  // X^2 is only ever a right factor: its transpose alone
+      *reinterpret_cast<float4*>(a.X2t + mo + (size_t)col * M + row4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+    const f32x4 v = panel_mm<M>(P0, P2, it, jt);
+    f32x4 z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float zr = Zr[(size_t)(row4 + r) * M + col] * invc;
+      const float wr = a.W[mo + (size_t)(row4 + r) * M + col];
+      z[r] = 0.25f * (13.f * zr - 15.f * wr + 7.f * acc[r] - v[r]);
+    }
+    store_c(a.Zn + mo, a.Znt + mo, M, row4, col, z);
+  }
+}
+
+}  // namespace nys

@@ -109,6 +109,13 @@ Plan make_plan(int B, int H, int n, int mr, int d) {
     p.off_T1 = take(BH * M * M * 4);
     p.off_T2 = take(BH * M * M * 4);
     p.off_Z2 = take(BH * M * M * 4);
+    p.off_AT = take(BH * M * M * 4);
+    p.off_Xt = take(BH * M * M * 4);
+    p.off_X2t = take(BH * M * M * 4);
+    p.off_Zt = take(BH * M * M * 4);
+    p.off_Zt2 = take(BH * M * M * 4);
+    p.off_colpart = take(BH * (M / 32) * M * 4);
+    p.off_rowpart = take(BH * (M / 32) * 4);
   }
   p.total = o;
   return p;

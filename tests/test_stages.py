@@ -36,7 +36,7 @@ MEASURED = {
     (2, 1.0): dict(qt=5.8e-8, kt=5.8e-8, A=6.1e-8, c=1.5e-7, Z=8.8e-7, BV=4.6e-6, W=9.0e-6),
     (3, 1.0): dict(qt=3.1e-8, kt=3.1e-8, A=8.8e-8, c=3.2e-7, Z=7.0e-5, BV=1.5e-3, W=3.2e-3),
     (4, 1.0): dict(qt=3.1e-8, kt=3.1e-8, A=5.5e-8, c=1.6e-7, Z=1.4e-4, BV=1.2e-3, W=2.9e-4),
-    (5, 1.0): dict(qt=3.2e-8, kt=3.2e-8, A=5.8e-8, c=9.1e-8, Z=1.1e-3, BV=1.3e-3, W=3.8e-4),
+    (5, 1.0): dict(qt=3.2e-8, kt=3.2e-8, A=5.8e-8, c=9.1e-8, Z=8.0e-5, BV=1.3e-3, W=5.0e-4),
     (2, 4.0): dict(qt=5.8e-8, kt=5.8e-8, A=4.3e-7, c=1.2e-7, Z=1.1e-6, BV=1.2e-5, W=1.3e-5),
     (3, 4.0): dict(qt=3.1e-8, kt=3.1e-8, A=1.1e-6, c=2.8e-7, Z=3.4e-4, BV=3.5e-3, W=3.5e-3),
 }
