@@ -133,8 +133,8 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   } else {
     constexpr int tl = BwdTokLayout<M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));
-    HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH), dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl,
-                   st, a));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok<IO, M, D>, dim3(bp.nct, p.BH, BwdTokLayout<M, D>::SPLIT),
+                   dim3(64 * bwd_tok_waves<M>()), (uint32_t)tl, st, a));
   }
   if (conv_w != nullptr) {
     HIP_TRY(hipEventRecord(sd->done, st));  // token pass done
@@ -265,7 +265,7 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
       return fail(NYS_ERR_INVALID, "conv_kernel_size=%d: 'same' padding needs an odd size >= 1", conv_k);
     if (conv_k > TAPS) return fail(NYS_ERR_UNSUPPORTED, "conv_kernel_size=%d: at most %d taps", conv_k, TAPS);
   }
-  const int m_max = d == 128 ? 64 : 128;  // the token pass's LDS tiles bound M * d
+  const int m_max = d == 128 ? 64 : 256;  // the token pass's LDS tiles bound M * d
   if (m != n && padded_m(m) > m_max)
     return fail(NYS_ERR_UNSUPPORTED, "backward: m=%d (up to %d landmarks at d=%d)", m, m_max, d);
   const size_t bytes = (size_t)B * H * n * d * sizeof(IO);
@@ -304,10 +304,18 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
     case 32064: NYS_BWD(64, 32);
     case 32096: NYS_BWD(96, 32);
     case 32128: NYS_BWD(128, 32);
+    case 32160: NYS_BWD(160, 32);
+    case 32192: NYS_BWD(192, 32);
+    case 32224: NYS_BWD(224, 32);
+    case 32256: NYS_BWD(256, 32);
     case 64032: NYS_BWD(32, 64);
     case 64064: NYS_BWD(64, 64);
     case 64096: NYS_BWD(96, 64);
     case 64128: NYS_BWD(128, 64);
+    case 64160: NYS_BWD(160, 64);
+    case 64192: NYS_BWD(192, 64);
+    case 64224: NYS_BWD(224, 64);
+    case 64256: NYS_BWD(256, 64);
     case 128032: NYS_BWD(32, 128);
     case 128064: NYS_BWD(64, 128);
     default: break;

@@ -8,8 +8,11 @@
 // and its training use (gradient checkpointing, the Trainer).  The
 // intermediates are recomputed (landmarks, A, Z, B V, W and B's row
 // normalisers come from a forward pass without the output), then, per head
-// (head size d = 32 or 64 with up to 128 landmarks, d = 128 with up to 64;
-// float32 accumulation throughout):
+// (head size d = 32 or 64 with up to 256 landmarks, d = 128 with up to 64;
+// float32 accumulation throughout; above 128 landmarks the token pass is
+// split by channel halves at d = 64, the key landmarks and Qt / dBV are read
+// from L2, and the per-head products take their contraction in LDS-sized
+// steps):
 //
 //   k_bwd_dvconv  dv_conv = conv^T(dout) (the forward convolution with the
 //               taps reversed, on the matrix cores);
@@ -145,8 +148,15 @@ __device__ __forceinline__ void io_put(IO* p, float x) {
 template <int M, int D>
 struct BwdTokLayout {
   static constexpr int NW = bwd_tok_waves<M>(), GT = 16 * NW, LDF = M + 4, LD = D + 4;
+  // Above 128 landmarks the key landmarks stay in L2, and at d = 64 the pass
+  // is split by channels: workgroup z of a token chunk accumulates dW, dKt
+  // and writes dQs for channels [z DC, (z + 1) DC) only (each half forms the
+  // whole S, dF and softmax of its tokens; the halves share nothing).
+  static constexpr bool KT_LDS = M <= 128;
+  static constexpr int SPLIT = (M > 128 && D > 32) ? 2 : 1;
+  static constexpr int DC = D / SPLIT, LDC = DC + 4;
   static constexpr int OFF_KT = 0;
-  static constexpr int OFF_Q = OFF_KT + M * LD;
+  static constexpr int OFF_Q = OFF_KT + (KT_LDS ? M * LD : 0);
   static constexpr int OFF_DO = OFF_Q + GT * LD;
   static constexpr int OFF_F = OFF_DO + GT * LD;
   static constexpr int OFF_DS = OFF_F + GT * LDF;
@@ -154,29 +164,33 @@ struct BwdTokLayout {
   // to 64 landmarks, in LDS above
   static constexpr bool ACC_REG = M <= 64;
   static constexpr int OFF_AW = OFF_DS + GT * LDF;
-  static constexpr int OFF_AK = OFF_AW + (ACC_REG ? 0 : M * LD);
-  static constexpr int OFF_W = OFF_AK + (ACC_REG ? 0 : M * LD);
+  static constexpr int OFF_AK = OFF_AW + (ACC_REG ? 0 : M * LDC);
+  static constexpr int OFF_W = OFF_AK + (ACC_REG ? 0 : M * LDC);
   // W is staged too where it fits (otherwise read from L2)
   static constexpr bool W_LDS = 4 * (OFF_W + M * LD) <= 160 * 1024;
   static constexpr int FLOATS = OFF_W + (W_LDS ? M * LD : 0);
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_tok LDS");
+  static_assert(!ACC_REG || SPLIT == 1, "register accumulators cover every channel");
 };
 
-// grid (nct, BH), block 64 NW.
+// grid (nct, BH, Ly::SPLIT), block 64 NW.
 template <typename IO, int M, int D>
 __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   using Ly = BwdTokLayout<M, D>;
   constexpr int NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, LD = Ly::LD, TM = M / 16, CT = D / 16;
+  constexpr int DC = Ly::DC, LDC = Ly::LDC, CTC = DC / 16;  // this workgroup's channels
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int ct0 = blockIdx.z * CTC;  // first channel tile of this workgroup
   const int t0 = chunk * BWD_CT, t1 = min(a.n, t0 + BWD_CT);
   const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
   const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
   const float* Wg = a.W + (size_t)bh * M * D;
-  float* const Kt = bw_lds + Ly::OFF_KT;
+  const float* const Kt = Ly::KT_LDS ? bw_lds + Ly::OFF_KT : a.kt + (size_t)bh * M * D;
+  constexpr int KLD = Ly::KT_LDS ? LD : D;
   float* const Qg = bw_lds + Ly::OFF_Q;
   float* const DOg = bw_lds + Ly::OFF_DO;
   float* const Fg = bw_lds + Ly::OFF_F;
@@ -187,12 +201,14 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
   const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
   constexpr int WLD = Ly::W_LDS ? LD : D;
   for (int i = threadIdx.x; i < M * D; i += 64 * NW) {
-    Kt[(i / D) * LD + i % D] = a.kt[(size_t)bh * M * D + i];
-    if constexpr (!Ly::ACC_REG) {
-      AW[(i / D) * LD + i % D] = 0.f;
-      AK[(i / D) * LD + i % D] = 0.f;
-    }
+    if constexpr (Ly::KT_LDS) bw_lds[Ly::OFF_KT + (i / D) * LD + i % D] = a.kt[(size_t)bh * M * D + i];
     if constexpr (Ly::W_LDS) Wl[(i / D) * LD + i % D] = Wg[i];
+  }
+  if constexpr (!Ly::ACC_REG) {
+    for (int i = threadIdx.x; i < M * DC; i += 64 * NW) {
+      AW[(i / DC) * LDC + i % DC] = 0.f;
+      AK[(i / DC) * LDC + i % DC] = 0.f;
+    }
   }
   constexpr int NACC = Ly::ACC_REG ? 2 * TM * CT / NW : 1;
   static_assert(!Ly::ACC_REG || (2 * TM * CT) % NW == 0, "every wave owns the same number of tiles");
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
     f32x4 f[TM], df[TM];
 #pragma unroll
     for (int jt = 0; jt < TM; ++jt) {
-      f[jt] = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      f[jt] = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * KLD, 1, KLD, f32x4{0.f, 0.f, 0.f, 0.f});
       df[jt] = mm16<D>(DOg + 16 * wave * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
       if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
@@ -259,10 +275,11 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
         DSg[row * LDF + 16 * jt + c16] = f[jt][r] * (df[jt][r] - dt);
       }
     }
-    // dQs = dS Kt (16 tokens x D channels), the wave's own rows
+    // dQs = dS Kt (16 tokens x this workgroup's channels), the wave's own rows
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const f32x4 c = mm16<M>(DSg + 16 * wave * LDF, LDF, 1, Kt + 16 * ct, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int cc = 0; cc < CTC; ++cc) {
+      const int ct = ct0 + cc;
+      const f32x4 c = mm16<M>(DSg + 16 * wave * LDF, LDF, 1, Kt + 16 * ct, KLD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tw + 4 * g + r;
@@ -283,15 +300,15 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
         racc[j] = mm16<GT>(A0, 1, LDF, B0, LD, 1, racc[j]);
       }
     } else {
-      for (int ti = wave; ti < 2 * TM * CT; ti += NW) {
-        const bool isk = ti >= TM * CT;
-        const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
+      for (int ti = wave; ti < 2 * TM * CTC; ti += NW) {
+        const bool isk = ti >= TM * CTC;
+        const int tt = ti % (TM * CTC), jt = tt / CTC, cc = tt % CTC;
         const float* A0 = (isk ? DSg : Fg) + 16 * jt;
-        const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+        const float* B0 = (isk ? Qg : DOg) + 16 * (ct0 + cc);
         const f32x4 c = mm16<GT>(A0, 1, LDF, B0, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
-        float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * LD + 16 * ct + c16;
+        float* acc = (isk ? AK : AW) + (16 * jt + 4 * g) * LDC + 16 * cc + c16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r * LD] += c[r];
+        for (int r = 0; r < 4; ++r) acc[r * LDC] += c[r];
       }
     }
     __syncthreads();
@@ -309,9 +326,10 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
       for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * D + 16 * ct + c16] = racc[j][r];
     }
   } else {
-    for (int i = threadIdx.x; i < M * D; i += 64 * NW) {
-      pw[i] = AW[(i / D) * LD + i % D];
-      pk[i] = AK[(i / D) * LD + i % D];
+    for (int i = threadIdx.x; i < M * DC; i += 64 * NW) {
+      const int r = i / DC, c = i % DC;
+      pw[(size_t)r * D + 16 * ct0 + c] = AW[r * LDC + c];
+      pk[(size_t)r * D + 16 * ct0 + c] = AK[r * LDC + c];
     }
   }
 }
@@ -698,14 +716,97 @@ __device__ void bgemm(float* C, const float* Ag, bool ta, const float* Bg, bool 
   }
 }
 
-// two staged operands of up to max(M, D) x max(M, D) floats (row stride + 4)
+// Above 128 landmarks the two whole operands no longer fit in LDS: the same
+// product with the contraction taken in steps of KC, each step's slices of
+// op(A) (R x KC) and op(B) (KC x N) staged in LDS, and every wave's C tiles
+// held in registers across the steps.
+constexpr int BWD_KC = 32;
+
+template <int R, int N, int K>
+__device__ void bgemm_kt(float* C, const float* Ag, bool ta, const float* Bg, bool tb, float alpha, float beta,
+                         float* La, float* Lb) {
+  constexpr int NT = BWD_MM_NT, NWV = NT / 64, KC = BWD_KC;
+  constexpr int TR = R / 16, TN = N / 16, TILES = TR * TN, TPW = (TILES + NWV - 1) / NWV;
+  constexpr int LDA = KC + 4, LDB = N + 4;
+  static_assert(K % KC == 0, "whole contraction steps");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    __syncthreads();  // earlier results written; the previous step's reads done
+    // stored shapes: A is (ta ? K x R : R x K), B is (tb ? N x K : K x N)
+    for (int i = tid; i < R * KC; i += NT) {
+      int r, kk;
+      float x;
+      if (ta) {
+        kk = i / R, r = i % R;
+        x = Ag[(size_t)(k0 + kk) * R + r];
+      } else {
+        r = i / KC, kk = i % KC;
+        x = Ag[(size_t)r * K + k0 + kk];
+      }
+      La[r * LDA + kk] = x;
+    }
+    for (int i = tid; i < KC * N; i += NT) {
+      int kk, j;
+      float x;
+      if (tb) {
+        j = i / KC, kk = i % KC;
+        x = Bg[(size_t)j * K + k0 + kk];
+      } else {
+        kk = i / N, j = i % N;
+        x = Bg[(size_t)(k0 + kk) * N + j];
+      }
+      Lb[kk * LDB + j] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + NWV * u;
+      if (t < TILES)
+        acc[u] = mm16<KC>(La + 16 * (t / TN) * LDA, LDA, 1, Lb + 16 * (t % TN), LDB, 1, acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave + NWV * u;
+    if (t >= TILES) continue;
+    const int it = t / TN, jt = t % TN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* p = C + (size_t)(16 * it + 4 * g + r) * N + 16 * jt + c16;
+      *p = beta == 0.f ? alpha * acc[u][r] : alpha * acc[u][r] + beta * *p;
+    }
+  }
+}
+
+// two staged operands of up to max(M, D) x max(M, D) floats (row stride + 4),
+// or above 128 landmarks one contraction step of each (bgemm_kt)
 template <int M, int D>
 constexpr int bwd_mm_side() {
   return M > D ? M : D;
 }
 template <int M, int D>
+constexpr bool bwd_mm_tiled() {
+  return bwd_mm_side<M, D>() > 128;
+}
+template <int M, int D>
 constexpr int bwd_mm_lds_bytes() {
-  return 4 * 2 * bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
+  return bwd_mm_tiled<M, D>() ? 4 * (bwd_mm_side<M, D>() * (BWD_KC + 4) + BWD_KC * (bwd_mm_side<M, D>() + 4))
+                              : 4 * 2 * bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
+}
+
+// The per-head product of the chain kernels: whole operands in LDS, or in
+// contraction steps where they do not fit.
+template <int R, int N, int K, int M, int D>
+__device__ __forceinline__ void bgemm_h(float* C, const float* Ag, bool ta, const float* Bg, bool tb, float alpha,
+                                        float beta, float* La, float* Lb) {
+  if constexpr (bwd_mm_tiled<M, D>())
+    bgemm_kt<R, N, K>(C, Ag, ta, Bg, tb, alpha, beta, La, Lb);
+  else
+    bgemm<R, N, K>(C, Ag, ta, Bg, tb, alpha, beta, La, Lb);
 }
 
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
@@ -716,7 +817,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
   constexpr int MM = M * M;
   const int bh = blockIdx.x, tid = threadIdx.x;
   float* const La = bw_lds;
-  float* const Lb = bw_lds + bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
+  float* const Lb = bw_lds + (bwd_mm_tiled<M, D>() ? bwd_mm_side<M, D>() * (BWD_KC + 4)
+                                                    : bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4));
   const float* A = a.A + (size_t)bh * MM;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
   auto Zk = [&](int k) { return S + (size_t)k * MM; };
@@ -741,35 +843,35 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
     dA[i] = 0.f;
   }
   for (int k = 0; k < a.n_iter; ++k) {
-    bgemm<M, M, M>(Xk(k), A, false, Zk(k), false, 1.f, 0.f, La, Lb);
-    bgemm<M, M, M>(X2k(k), Xk(k), false, Xk(k), false, 1.f, 0.f, La, Lb);
-    bgemm<M, M, M>(Pk(k), Xk(k), false, X2k(k), false, -1.f, 0.f, La, Lb);
+    bgemm_h<M, M, M, M, D>(Xk(k), A, false, Zk(k), false, 1.f, 0.f, La, Lb);
+    bgemm_h<M, M, M, M, D>(X2k(k), Xk(k), false, Xk(k), false, 1.f, 0.f, La, Lb);
+    bgemm_h<M, M, M, M, D>(Pk(k), Xk(k), false, X2k(k), false, -1.f, 0.f, La, Lb);
     __syncthreads();
     for (int i = tid; i < MM; i += NT)
       Pk(k)[i] += (i / M == i % M ? 13.f : 0.f) - 15.f * Xk(k)[i] + 7.f * X2k(k)[i];
-    bgemm<M, M, M>(Zk(k + 1), Zk(k), false, Pk(k), false, 0.25f, 0.f, La, Lb);
+    bgemm_h<M, M, M, M, D>(Zk(k + 1), Zk(k), false, Pk(k), false, 0.25f, 0.f, La, Lb);
   }
   // dZ_n = dW BV^T, dBV = Z_n^T dW
-  bgemm<M, M, D>(G, dW, false, a.BV + (size_t)bh * M * D, true, 1.f, 0.f, La, Lb);
-  bgemm<M, D, M>(a.dBV + (size_t)bh * M * D, Zk(a.n_iter), true, dW, false, 1.f, 0.f, La, Lb);
+  bgemm_h<M, M, D, M, D>(G, dW, false, a.BV + (size_t)bh * M * D, true, 1.f, 0.f, La, Lb);
+  bgemm_h<M, D, M, M, D>(a.dBV + (size_t)bh * M * D, Zk(a.n_iter), true, dW, false, 1.f, 0.f, La, Lb);
   float* g = G;
   float* gn = Gn;
   for (int k = a.n_iter - 1; k >= 0; --k) {
     float* const Z = Zk(k);
     float* const X = Xk(k);
     float* const X2 = X2k(k);
-    bgemm<M, M, M>(gn, g, false, Pk(k), true, 0.25f, 0.f, La, Lb);   // dZ_k = G P^T / 4
-    bgemm<M, M, M>(dP, Z, true, g, false, 0.25f, 0.f, La, Lb);        // dP = Z^T G / 4
+    bgemm_h<M, M, M, M, D>(gn, g, false, Pk(k), true, 0.25f, 0.f, La, Lb);   // dZ_k = G P^T / 4
+    bgemm_h<M, M, M, M, D>(dP, Z, true, g, false, 0.25f, 0.f, La, Lb);        // dP = Z^T G / 4
     __syncthreads();
     for (int i = tid; i < MM; i += NT) dX[i] = -15.f * dP[i];
-    bgemm<M, M, M>(dX, dP, false, X, true, 7.f, 1.f, La, Lb);         // + 7 dP X^T
-    bgemm<M, M, M>(dX, X, true, dP, false, 7.f, 1.f, La, Lb);         // + 7 X^T dP
-    bgemm<M, M, M>(dX, dP, false, X2, true, -1.f, 1.f, La, Lb);       // - dP (X^2)^T
-    bgemm<M, M, M>(T, X, true, dP, false, 1.f, 0.f, La, Lb);
-    bgemm<M, M, M>(dX, T, false, X, true, -1.f, 1.f, La, Lb);         // - X^T dP X^T
-    bgemm<M, M, M>(dX, X2, true, dP, false, -1.f, 1.f, La, Lb);       // - (X^2)^T dP
-    bgemm<M, M, M>(dA, dX, false, Z, true, 1.f, 1.f, La, Lb);         // dA += dX Z^T
-    bgemm<M, M, M>(gn, A, true, dX, false, 1.f, 1.f, La, Lb);         // dZ_k += A^T dX
+    bgemm_h<M, M, M, M, D>(dX, dP, false, X, true, 7.f, 1.f, La, Lb);         // + 7 dP X^T
+    bgemm_h<M, M, M, M, D>(dX, X, true, dP, false, 7.f, 1.f, La, Lb);         // + 7 X^T dP
+    bgemm_h<M, M, M, M, D>(dX, dP, false, X2, true, -1.f, 1.f, La, Lb);       // - dP (X^2)^T
+    bgemm_h<M, M, M, M, D>(T, X, true, dP, false, 1.f, 0.f, La, Lb);
+    bgemm_h<M, M, M, M, D>(dX, T, false, X, true, -1.f, 1.f, La, Lb);         // - X^T dP X^T
+    bgemm_h<M, M, M, M, D>(dX, X2, true, dP, false, -1.f, 1.f, La, Lb);       // - (X^2)^T dP
+    bgemm_h<M, M, M, M, D>(dA, dX, false, Z, true, 1.f, 1.f, La, Lb);         // dA += dX Z^T
+    bgemm_h<M, M, M, M, D>(gn, A, true, dX, false, 1.f, 1.f, La, Lb);         // dZ_k += A^T dX
     float* const t = g;
     g = gn;
     gn = t;
@@ -1275,7 +1377,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
   constexpr int MM = M * M, RPP = NT / 16;
   const int bh = blockIdx.x, tid = threadIdx.x, l16 = tid & 15;
   float* const La = bw_lds;
-  float* const Lb = bw_lds + bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4);
+  float* const Lb = bw_lds + (bwd_mm_tiled<M, D>() ? bwd_mm_side<M, D>() * (BWD_KC + 4)
+                                                    : bwd_mm_side<M, D>() * (bwd_mm_side<M, D>() + 4));
   const float* A = a.A + (size_t)bh * MM;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
   const float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
@@ -1335,8 +1438,8 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
     for (int u = 0; u < M / 16; ++u) dSA[r * M + l16 + 16 * u] = av[u] * (dv[u] - s);
   }
   // dQt_A = dS_A Kt; dKt += dS_A^T Qt (bgemm starts with a block barrier)
-  bgemm<M, D, M>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La, Lb);
-  bgemm<M, D, M>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La, Lb);
+  bgemm_h<M, D, M, M, D>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La, Lb);
+  bgemm_h<M, D, M, M, D>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La, Lb);
   // D_i = dBV_i . BV_i
   for (int r = tid / 16; r < M; r += RPP) {
     const float* x = a.dBV + ((size_t)bh * M + r) * D;
@@ -1353,9 +1456,11 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
 template <int M, int D>
 struct BwdKeyLayout {
   static constexpr int LDB = BWD_GK + 4, LD = D + 4;
+  // above 128 landmarks Qt and dBV are read from L2 instead of LDS
+  static constexpr bool QT_LDS = M <= 128;
   static constexpr int OFF_QT = 0;
-  static constexpr int OFF_DBV = OFF_QT + M * LD;
-  static constexpr int OFF_KS = OFF_DBV + M * LD;
+  static constexpr int OFF_DBV = OFF_QT + (QT_LDS ? M * LD : 0);
+  static constexpr int OFF_KS = OFF_DBV + (QT_LDS ? M * LD : 0);
   static constexpr int OFF_V = OFF_KS + BWD_GK * LD;
   static constexpr int OFF_B = OFF_V + BWD_GK * LD;
   static constexpr int OFF_DS = OFF_B + M * LDB;
@@ -1384,17 +1489,20 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   const float* lse = a.lse + (size_t)bh * M;
   const float* Dv = a.Dv + (size_t)bh * M;
   const float* dKt = a.dKt + (size_t)bh * M * D;
-  float* const Qt = bw_lds + Ly::OFF_QT;
-  float* const dBV = bw_lds + Ly::OFF_DBV;
+  constexpr int QLD = Ly::QT_LDS ? LD : D;  // row stride of Qt and dBV
+  const float* const Qt = Ly::QT_LDS ? bw_lds + Ly::OFF_QT : a.qt + (size_t)bh * M * D;
+  const float* const dBV = Ly::QT_LDS ? bw_lds + Ly::OFF_DBV : a.dBV + (size_t)bh * M * D;
   float* const Ks = bw_lds + Ly::OFF_KS;
   float* const Vs = bw_lds + Ly::OFF_V;
   float* const Bt = bw_lds + Ly::OFF_B;
   float* const DS = bw_lds + Ly::OFF_DS;
   float* const VAL = bw_lds + Ly::OFF_VAL;
-  for (int i = tid; i < M * D; i += NT) {
-    const int r = i / D, c = i % D;
-    Qt[r * LD + c] = a.qt[(size_t)bh * M * D + i];
-    dBV[r * LD + c] = a.dBV[(size_t)bh * M * D + i];
+  if constexpr (Ly::QT_LDS) {
+    for (int i = tid; i < M * D; i += NT) {
+      const int r = i / D, c = i % D;
+      bw_lds[Ly::OFF_QT + r * LD + c] = a.qt[(size_t)bh * M * D + i];
+      bw_lds[Ly::OFF_DBV + r * LD + c] = a.dBV[(size_t)bh * M * D + i];
+    }
   }
   // dQt_B tiles (landmark tile, channel tile) owned by this wave: t = wave + NWV j
   constexpr int NACC = (TM * CT + NWV - 1) / NWV;
@@ -1430,9 +1538,9 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
     // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
     for (int t = wave; t < TM * (BWD_GK / 16); t += NWV) {
       const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
-      const f32x4 s = mm16<D>(Qt + 16 * it * LD, LD, 1, Ks + 16 * kt * LD, 1, LD,
+      const f32x4 s = mm16<D>(Qt + 16 * it * QLD, QLD, 1, Ks + 16 * kt * LD, 1, LD,
                                f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD,
+      const f32x4 db = mm16<D>(dBV + 16 * it * QLD, QLD, 1, Vs + 16 * kt * LD, 1, LD,
                                 f32x4{0.f, 0.f, 0.f, 0.f});
       const float val = VAL[16 * kt + c16];
 #pragma unroll
@@ -1448,7 +1556,7 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
     for (int t = wave; t < 2 * (BWD_GK / 16) * CT; t += NWV) {
       const bool isk = t >= (BWD_GK / 16) * CT;
       const int tt = t % ((BWD_GK / 16) * CT), kt = tt / CT, ct = tt % CT;
-      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, LD, 1,
+      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, QLD, 1,
                               f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

@@ -214,7 +214,7 @@ int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const vo
  * first arg-max).  All pointers are DEVICE pointers owned by the caller;
  * dq, dk, dv must not overlap each other or q, k, v, dout.  Head sizes
  * d = 32, 64 and 128: the exact branch (m == n, any n) at each, the Nystrom
- * path with up to 128 landmarks at d = 32 and 64 and up to 64 at d = 128
+ * path with up to 256 landmarks at d = 32 and 64 and up to 64 at d = 128
  * (NYS_ERR_UNSUPPORTED for more).  Part of the work runs on a
  * library-owned side stream of the device (default priority), forked from
  * `stream` and joined back into it with events, so the call is ordered on

@@ -138,8 +138,8 @@ FAKE5 = ctypes.c_void_p(0x2100000)
     (dict(d=48), -2),                         # head size not built
     (dict(d=128, m=128), -2),                 # more than 64 landmarks at d = 128
     (dict(d=128, m=80, n=480), -2),           # 80 landmarks pad to 96 > 64 at d = 128
-    (dict(m=160, n=640), -2),                 # more than 128 landmarks
-    (dict(d=32, m=160, n=640), -2),           # the same at d = 32
+    (dict(m=512, n=1024), -2),                # more than 256 landmarks
+    (dict(d=32, m=300, n=600), -2),           # the same at d = 32
 ])
 def test_backward_validation(lib, kw, code):
     """nystrom_attention_backward rejects bad arguments before any launch
