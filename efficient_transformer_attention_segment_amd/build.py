@@ -36,8 +36,6 @@ CFLAGS = [
 ]
 LDFLAGS = [
     "-shared", f"--offload-arch={ARCH}",
-    # the module's q/k/v projection is one library GEMM
-    "-lhipblaslt",
 ]
 
 

@@ -180,6 +180,12 @@ template <typename IO, int D>
 int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, const void* k, const void* v,
                  const uint8_t* mask, const float* conv_w, int conv_k, void* out, void* probs, hipStream_t st);
 
+// The module's projection y = x W^T + b, [rows][cols] from x [rows][hidden]
+// and W [cols][hidden] (module.hip).
+template <typename IO>
+int qkv_projection(const void* x, const void* w, const void* bias, int rows, int hidden, int cols, void* y,
+                   hipStream_t st);
+
 // The backward pass (bwd_*.hip).
 template <typename IO>
 int run_backward(const void* q, const void* k, const void* v, const uint8_t* mask, const float* conv_w, int conv_k,

@@ -1,0 +1,247 @@
+// The self-attention module's q/k/v projection: y = x W^T + b.
+//
+// Page: "Nystromformer 源码解析与实战指南" (blog.gitcode.com), section 2.2: q,
+// k and v come from three linear projections of the hidden states (the
+// query, key and value weights, stacked here as one [3 H d, hidden] matrix
+// in nn.Linear's [out, in] layout), split into heads.
+//
+// x [rows][K] and W [N][K] are both K-contiguous, so every matrix-core
+// operand is a 16-byte run of one row.
+//
+// k_qkv_bf16: 128 x 128 output tiles, 4 waves of 64 x 64 (three workgroups
+//   per CU), the contraction in steps of 64: each step's tiles are stored
+//   from registers into one LDS stage (rows of 128 bytes, 16-byte chunks
+//   XOR-swizzled by (row / 2) & 7 so the fragment reads of 16 rows hit
+//   distinct banks) while the next step's tiles load into registers;
+//   LDS-only barriers, so those loads stay in flight across them.  Each
+//   wave forms the transposed tile, y^T = W x^T, on v_mfma_f32_16x16x32_bf16,
+//   so a lane holds 4 consecutive output columns of one row: the bias is
+//   added in float32 and 4 bf16 values are stored at once.  Every XCD walks
+//   its own row tiles first for each column tile (qkv_tile).
+// k_qkv_f32: float32 I/O on the float32 matrix core (v_mfma_f32_16x16x4f32),
+//   64 x 64 tiles, register-staged float32 LDS tiles, for float32 accuracy.
+#pragma once
+
+#include "common.hpp"
+
+namespace nys {
+
+struct QkvArgs {
+  const void* x;     // [rows][K]
+  const void* w;     // [N][K]
+  const void* bias;  // [N] or null
+  void* y;           // [rows][N]
+  int rows, N, K;
+};
+
+constexpr int QB_BM = 128, QB_BN = 128, QB_BK = 64, QB_NT = 256;
+constexpr int QB_ATILE = QB_BM * QB_BK, QB_BTILE = QB_BN * QB_BK;  // bf16 elements
+constexpr int QB_LDS = (QB_ATILE + QB_BTILE) * 2;  // bytes: one stage
+
+// Tiles (tm, tn) of a launch: linear index L runs on XCD L % 8; XCD x takes
+// the row tiles x, x + 8, ... and walks them first for each column tile, so
+// its x panels (a few MB) stay in its L2 while the W tiles stream past (the
+// other order keeps all of W live beside the panels and overflows the L2).
+__host__ __device__ inline int qkv_grid(int rows, int N, int BM, int BN) {
+  const int tm = (rows + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  return 8 * tn * ((tm + 7) / 8);
+}
+__device__ __forceinline__ void qkv_tile(int rows, int N, int BM, int BN, int& tm, int& tn) {
+  const int L = blockIdx.x, xcd = L & 7, s = L >> 3;
+  const int mx = ((rows + BM - 1) / BM + 7) / 8;  // row tiles per XCD
+  tn = s / mx;
+  tm = xcd + 8 * (s % mx);
+  (void)N;
+}
+
+// Tile rows of 64 bf16 (128 bytes) with 16-byte chunk c of row r at chunk
+// position c ^ ((r >> 1) & 7): the 16 rows of one fragment read (two
+// parities x eight positions) then cover all 64 banks.
+__device__ __forceinline__ int qswz(int row, int chunk) {
+  if constexpr (QB_BK == 128)
+    return row * QB_BK + 8 * (chunk ^ (row & 15));  // 256-byte rows: 16 positions per row
+  else
+    return row * QB_BK + 8 * (chunk ^ ((row >> 1) & 7));
+}
+
+// grid qkv_grid(rows, N, QB_BM, QB_BN), QB_NT threads (waves of 64 x 64,
+// QB_BM / 64 along the rows), dynamic LDS QB_LDS (one stage: the next step's
+// tiles wait in registers while this step's are multiplied).
+__global__ __launch_bounds__(QB_NT) void k_qkv_bf16(QkvArgs a) {
+  extern __shared__ __align__(16) __bf16 qb_lds[];
+  int tm, tn;
+  qkv_tile(a.rows, a.N, QB_BM, QB_BN, tm, tn);
+  if (tm * QB_BM >= a.rows) return;  // whole workgroup, before any barrier
+  const int m0 = tm * QB_BM, n0 = tn * QB_BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  constexpr int WMS = QB_BM / 64;  // waves along the rows
+  const int wm = wave % WMS, wn = wave / WMS;  // the wave's 64 x 64 part
+  const u16* X = static_cast<const u16*>(a.x);
+  const u16* Wt = static_cast<const u16*>(a.w);
+  const int nk = (a.K + QB_BK - 1) / QB_BK;
+  __bf16* const At = qb_lds;
+  __bf16* const Bt = qb_lds + QB_ATILE;
+  // per thread: QA 16-byte chunks of the A tile and QBn of the B tile
+  constexpr int QA = QB_ATILE / 8 / QB_NT, QBn = QB_BTILE / 8 / QB_NT;
+  uint4 ra[QA], rb[QBn];
+  auto load = [&](int ks) {
+    const int k0 = ks * QB_BK;
+#pragma unroll
+    for (int u = 0; u < QA; ++u) {
+      const int idx = tid + QB_NT * u, row = idx / (QB_BK / 8), ch = idx % (QB_BK / 8);
+      const int gr = m0 + row, gk = k0 + 8 * ch;
+      ra[u] = (gr < a.rows && gk < a.K) ? *reinterpret_cast<const uint4*>(X + (size_t)gr * a.K + gk)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < QBn; ++u) {
+      const int idx = tid + QB_NT * u, row = idx / (QB_BK / 8), ch = idx % (QB_BK / 8);
+      const int gr = n0 + row, gk = k0 + 8 * ch;
+      rb[u] = (gr < a.N && gk < a.K) ? *reinterpret_cast<const uint4*>(Wt + (size_t)gr * a.K + gk)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < QA; ++u) {
+      const int idx = tid + QB_NT * u;
+      *reinterpret_cast<uint4*>(At + qswz(idx / (QB_BK / 8), idx % (QB_BK / 8))) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < QBn; ++u) {
+      const int idx = tid + QB_NT * u;
+      *reinterpret_cast<uint4*>(Bt + qswz(idx / (QB_BK / 8), idx % (QB_BK / 8))) = rb[u];
+    }
+  };
+  f32x4 acc[4][4];  // [n subtile j][m subtile i]: y^T tiles
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS-only barriers: a fence would also drain the next step's loads
+  load(0);
+  for (int ks = 0; ks < nk; ++ks) {
+    store();
+    wait_lgkm0();
+    barrier_only();
+    if (ks + 1 < nk) load(ks + 1);  // in flight while this step is multiplied
+#pragma unroll
+    for (int kh = 0; kh < QB_BK / 32; ++kh) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(At + qswz(64 * wm + 16 * i + c16, 4 * kh + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(Bt + qswz(64 * wn + 16 * j + c16, 4 * kh + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = mfma(bfr[j], af[i], acc[j][i]);
+    }
+    wait_lgkm0();
+    barrier_only();  // every wave has read the tiles before the next store
+  }
+
+  // lane holds y[m][n .. n + 3] with m = m0 + 64 wm + 16 i + c16 and
+  // n = n0 + 64 wn + 16 j + 4 g
+  const u16* const bias = static_cast<const u16*>(a.bias);
+  u16* const Y = static_cast<u16*>(a.y);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 64 * wn + 16 * j + 4 * g;
+    if (n >= a.N) continue;  // N is a multiple of 4 (16-byte rows of 3 H d)
+    float b4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+      const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+      b4[0] = bf16u_to_f32(bw.x & 0xffffu);
+      b4[1] = bf16u_to_f32(bw.x >> 16);
+      b4[2] = bf16u_to_f32(bw.y & 0xffffu);
+      b4[3] = bf16u_to_f32(bw.y >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 64 * wm + 16 * i + c16;
+      if (m >= a.rows) continue;
+      const f32x4 v = acc[j][i];
+      *reinterpret_cast<uint2*>(Y + (size_t)m * a.N + n) =
+          make_uint2(pack_bf16x2(v[0] + b4[0], v[1] + b4[1]), pack_bf16x2(v[2] + b4[2], v[3] + b4[3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- float32 ---
+constexpr int QF_BM = 64, QF_BN = 64, QF_BK = 32, QF_LD = QF_BK + 4;
+
+// grid qkv_grid(rows, N, 64, 64), 256 threads (4 waves of 32 x 32).
+__global__ __launch_bounds__(256) void k_qkv_f32(QkvArgs a) {
+  __shared__ __align__(16) float As[QF_BM * QF_LD];
+  __shared__ __align__(16) float Bs[QF_BN * QF_LD];
+  int tm, tn;
+  qkv_tile(a.rows, a.N, QF_BM, QF_BN, tm, tn);
+  if (tm * QF_BM >= a.rows) return;
+  const int m0 = tm * QF_BM, n0 = tn * QF_BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wm = wave & 1, wn = wave >> 1;
+  const float* X = static_cast<const float*>(a.x);
+  const float* Wt = static_cast<const float*>(a.w);
+  f32x4 acc[2][2];  // [n subtile][m subtile]: y^T tiles
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.K; k0 += QF_BK) {
+    // 64 rows x 8 float4 of each operand: 2 of each per thread
+    float4 xa[2], xb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u, r = idx >> 3, c4 = idx & 7, k = k0 + 4 * c4;
+      const bool kin = k < a.K;
+      xa[u] = (m0 + r < a.rows && kin) ? *reinterpret_cast<const float4*>(X + (size_t)(m0 + r) * a.K + k)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      xb[u] = (n0 + r < a.N && kin) ? *reinterpret_cast<const float4*>(Wt + (size_t)(n0 + r) * a.K + k)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();  // the previous step's reads are done
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u, r = idx >> 3, c4 = idx & 7;
+      *reinterpret_cast<float4*>(As + r * QF_LD + 4 * c4) = xa[u];
+      *reinterpret_cast<float4*>(Bs + r * QF_LD + 4 * c4) = xb[u];
+    }
+    __syncthreads();
+    // k step s: lane (g, c16) feeds W[n][k0 + 4s + g] and x[m][k0 + 4s + g]
+#pragma unroll
+    for (int s4 = 0; s4 < QF_BK / 4; ++s4) {
+      float av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = As[(32 * wm + 16 * i + c16) * QF_LD + 4 * s4 + g];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[j] = Bs[(32 * wn + 16 * j + c16) * QF_LD + 4 * s4 + g];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[j][i] = mfma_f32(bv[j], av[i], acc[j][i]);
+    }
+  }
+  const float* const bias = static_cast<const float*>(a.bias);
+  float* const Y = static_cast<float*>(a.y);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 32 * wn + 16 * j + 4 * g;
+    if (n >= a.N) continue;
+    const float4 b4 = bias != nullptr ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = m0 + 32 * wm + 16 * i + c16;
+      if (m >= a.rows) continue;
+      const f32x4 v = acc[j][i];
+      *reinterpret_cast<float4*>(Y + (size_t)m * a.N + n) = make_float4(v[0] + b4.x, v[1] + b4.y, v[2] + b4.z, v[3] + b4.w);
+    }
+  }
+}
+
+}  // namespace nys

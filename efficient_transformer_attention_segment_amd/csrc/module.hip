@@ -1,0 +1,25 @@
+// The self-attention module's q/k/v projection (k_qkv.hpp) and its launch.
+#include "host.hpp"
+#include "k_qkv.hpp"
+
+namespace nys {
+namespace host {
+
+template <typename IO>
+int qkv_projection(const void* x, const void* w, const void* bias, int rows, int hidden, int cols, void* y,
+                   hipStream_t st) {
+  QkvArgs a{x, w, bias, y, rows, cols, hidden};
+  if constexpr (sizeof(IO) == 2) {
+    HIP_TRY(allow_lds(k_qkv_bf16, QB_LDS));
+    HIP_TRY(launch("k_qkv", k_qkv_bf16, dim3(qkv_grid(rows, cols, QB_BM, QB_BN)), dim3(QB_NT), (uint32_t)QB_LDS, st, a));
+  } else {
+    HIP_TRY(launch("k_qkv", k_qkv_f32, dim3(qkv_grid(rows, cols, QF_BM, QF_BN)), dim3(256), 0, st, a));
+  }
+  return NYS_OK;
+}
+
+template int qkv_projection<float>(const void*, const void*, const void*, int, int, int, void*, hipStream_t);
+template int qkv_projection<u16>(const void*, const void*, const void*, int, int, int, void*, hipStream_t);
+
+}  // namespace host
+}  // namespace nys

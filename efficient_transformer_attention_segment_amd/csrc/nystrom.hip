@@ -2,8 +2,6 @@
 // workspace, the plan of each call and the C ABI declared in
 // include/nystrom.h.  The launch sequences live in the kernel translation
 // units (fwd_*.hip, exact.hip, bwd_*.hip; see host.hpp).
-#include <hipblaslt/hipblaslt.h>
-
 #include <cmath>
 #include <tuple>
 
@@ -347,89 +345,9 @@ int static_scratch(hipStream_t st, Workspace* out) {
 }
 
 // ------------------------------------------- module: the q/k/v projection ---
-// One library GEMM (hipBLASLt) writes x W^T + b as [B n, 3 H d] = [B, n, 3,
-// H, d]; the attention kernels then read q, k, v from it in place through
+// One hand-written GEMM (module.hip) writes x W^T + b as [B n, 3 H d] = [B, n,
+// 3, H, d]; the attention kernels then read q, k, v from it in place through
 // strides and write the context as [B, n, H d].
-struct LtPlan {
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
-  size_t ws = 0;
-};
-std::mutex g_lt_mu;
-std::map<int, hipblasLtHandle_t> g_lt;                                         // per device
-std::map<std::tuple<int, int, int, int, int, bool>, LtPlan> g_lt_plans;        // dev, dtype, rows, hidden, cols, bias
-std::map<std::pair<int, hipStream_t>, Workspace> g_lt_ws;                      // GEMM workspace per stream
-constexpr size_t LT_MAX_WS = 32u << 20;
-
-#define LT_TRY(expr)                                                                                  \
-  do {                                                                                              \
-    hipblasStatus_t s_ = (expr);                                                                    \
-    if (s_ != HIPBLAS_STATUS_SUCCESS) return fail(NYS_ERR_HIP, "%s: hipBLASLt status %d", #expr, (int)s_); \
-  } while (0)
-
-// y[rows][cols] = x[rows][hidden] W[cols][hidden]^T (+ bias[cols]), row-major,
-// float32 accumulation.  In column-major terms y^T = op_T(W) x^T.
-template <typename IO>
-int qkv_projection(const void* x, const void* w, const void* bias, int rows, int hidden, int cols, void* y,
-                   hipStream_t st) {
-  int dev = 0;
-  HIP_TRY(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_lt_mu);
-  hipblasLtHandle_t& h = g_lt[dev];
-  if (h == nullptr) LT_TRY(hipblasLtCreate(&h));
-  const hipDataType t = sizeof(IO) == 4 ? HIP_R_32F : HIP_R_16BF;
-  const auto key = std::make_tuple(dev, (int)sizeof(IO), rows, hidden, cols, bias != nullptr);
-  auto it = g_lt_plans.find(key);
-  if (it == g_lt_plans.end()) {
-    LtPlan p;
-    LT_TRY(hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F));
-    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta));
-    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb));
-    if (bias != nullptr) {
-      const hipblasLtEpilogue_t epi = HIPBLASLT_EPILOGUE_BIAS;
-      const int32_t bt = t;
-      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi));
-      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bt, sizeof bt));
-      LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias));
-    }
-    LT_TRY(hipblasLtMatrixLayoutCreate(&p.la, t, hidden, cols, hidden));
-    LT_TRY(hipblasLtMatrixLayoutCreate(&p.lb, t, hidden, rows, hidden));
-    LT_TRY(hipblasLtMatrixLayoutCreate(&p.lc, t, cols, rows, cols));
-    hipblasLtMatmulPreference_t pref = nullptr;
-    LT_TRY(hipblasLtMatmulPreferenceCreate(&pref));
-    const uint64_t wsmax = LT_MAX_WS;
-    hipblasStatus_t s0 =
-        hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax, sizeof wsmax);
-    hipblasLtMatmulHeuristicResult_t res[1];
-    int nres = 0;
-    if (s0 == HIPBLAS_STATUS_SUCCESS)
-      s0 = hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.la, p.lb, p.lc, p.lc, pref, 1, res, &nres);
-    (void)hipblasLtMatmulPreferenceDestroy(pref);
-    LT_TRY(s0);
-    if (nres < 1) return fail(NYS_ERR_UNSUPPORTED, "hipBLASLt has no algorithm for the %d x %d x %d projection", rows,
-                              cols, hidden);
-    p.algo = res[0].algo;
-    p.ws = res[0].workspaceSize;
-    it = g_lt_plans.emplace(key, p).first;
-  }
-  LtPlan& p = it->second;
-  if (bias != nullptr)
-    LT_TRY(hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof bias));
-  Workspace& ws = g_lt_ws[{dev, st}];
-  if (ws.cap < p.ws) {
-    HIP_TRY(hipStreamSynchronize(st));
-    if (ws.buf) HIP_TRY(hipFree(ws.buf));
-    ws.buf = nullptr;
-    ws.cap = 0;
-    HIP_TRY(hipMalloc(&ws.buf, p.ws));
-    ws.cap = p.ws;
-  }
-  const float alpha = 1.f, beta = 0.f;
-  LT_TRY(hipblasLtMatmul(h, p.op, &alpha, w, p.la, x, p.lb, &beta, y, p.lc, y, p.lc, &p.algo, ws.buf, p.ws, st));
-  return NYS_OK;
-}
 
 template <typename IO>
 int run_module(const void* x, const void* w, const void* b, const uint8_t* mask, const float* conv_w, int conv_k,
@@ -445,6 +363,8 @@ int run_module(const void* x, const void* w, const void* b, const uint8_t* mask,
   if (((size_t)hidden * e) % 16 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(qkv) % 16 != 0)
     return fail(NYS_ERR_INVALID, "x, w_qkv and qkv must be 16-byte aligned with hidden * element size a multiple of 16");
+  if (b != nullptr && reinterpret_cast<uintptr_t>(b) % (4 * e) != 0)
+    return fail(NYS_ERR_INVALID, "b_qkv must be aligned to 4 elements");
   const size_t qkv_bytes = (size_t)rows * cols * e;
   if (ranges_meet(qkv, qkv_bytes, x, (size_t)rows * hidden * e) ||
       ranges_meet(qkv, qkv_bytes, w, (size_t)cols * hidden * e) ||
@@ -658,11 +578,6 @@ __attribute__((visibility("default"))) void nystrom_release(void) {
     (void)hipEventDestroy(kv.second.done);
   }
   g_side.clear();
-  std::lock_guard<std::mutex> lk2(g_lt_mu);
-  for (auto& kv : g_lt_ws) {
-    if (kv.second.buf) (void)hipFree(kv.second.buf);
-  }
-  g_lt_ws.clear();
 }
 
 __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const void* q, const void* k,

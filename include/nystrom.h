@@ -188,15 +188,16 @@ int nystrom_attention_probs(int dtype, const void* q, const void* k, const void*
  *   w_qkv  [3 H d, hidden]     query, key and value weights stacked in that
  *                              order, each in nn.Linear's [out, in] layout
  *   b_qkv  [3 H d] or NULL     their biases
- *   qkv    [B, n, 3, H, d]     receives x w_qkv^T + b_qkv (one hipBLASLt GEMM,
- *                              float32 accumulation, rounded to the dtype);
+ *   qkv    [B, n, 3, H, d]     receives x w_qkv^T + b_qkv (one matrix-core
+ *                              GEMM of this library, float32 accumulation,
+ *                              rounded to the dtype);
  *                              the attention reads q, k, v from it in place
  *   out    [B, n, H d]         the context, head h in columns [h d, (h+1) d)
  * All in the dtype (0 float32, 1 bf16), dense, DEVICE memory owned by the
  * caller; qkv must not overlap x, w_qkv, b_qkv or out.  key_mask, conv_w,
  * conv_kernel_size, m, n_iter, init_option and the errors as
- * nystrom_attention_ex; every check runs before the GEMM is enqueued.
- * NYS_ERR_UNSUPPORTED also when hipBLASLt has no algorithm for the shape. */
+ * nystrom_attention_ex; every check runs before the GEMM is enqueued;
+ * NYS_ERR_INVALID also for b_qkv not aligned to 4 elements. */
 int nystrom_self_attention(int dtype, const void* x, const void* w_qkv, const void* b_qkv,
                            const uint8_t* key_mask, const float* conv_w, int conv_kernel_size,
                            int B, int n, int hidden, int H, int d, int m, int n_iter,
