@@ -111,6 +111,26 @@ def read_traffic(kernel: str, wname: str, sha: str):
         return None
 
 
+def read_trace_avg(kernel: str, wname: str, sha: str):
+    """The rocprofv3 average duration (us) of `kernel` in
+    profiles/kernel_trace_<workload>.txt, or None unless that summary was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{wname}.txt")
+    if not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    if f"source_sha: {sha}" not in lines:
+        return None
+    for line in lines:
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) >= 3 and _short(cells[0]) == kernel:
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
 def make_replicas(w, x, count, torch):
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -244,9 +264,9 @@ def time_probs(w, x, steps, warmup, torch, nys):
 
 def time_module(w, steps, warmup, torch, nys, core_ms):
     """The self-attention module at the workload's shape (hidden = H d): the
-    stacked q/k/v projection (one hipBLASLt GEMM) and the attention reading
-    its output in place.  The projection's share is the step time minus the
-    attention-only step time measured above."""
+    stacked q/k/v projection (the library's GEMM, k_qkv) and the attention
+    reading its output in place; the projection kernel is timed with the
+    library's kernel-stamped events."""
     from efficient_transformer_attention_segment_amd.workloads import make_module_inputs
     hidden = w.H * w.d
     inp = make_module_inputs(w.B, w.n, hidden, w.H, w.d, seed=2000 + w.index, dtype=w.dtype,
@@ -271,13 +291,23 @@ def time_module(w, steps, warmup, torch, nys, core_ms):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    nys.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = nys.profile_collect()
+    nys.profile_enable(False)
     flops = 2 * w.B * w.n * hidden * 3 * w.H * w.d
-    proj_ms = ms - core_ms
+    tot, cnt = prof.get("k_qkv", (0.0, 1))
+    gemm_us = 1e3 * tot / cnt
     return {"call": "nystrom_self_attention", "hidden": hidden, "ms_per_step": round(ms, 5),
-            "tokens_per_s": round(w.tokens / (ms / 1e3), 1), "projection_flops": flops,
-            "projection_ms_est": round(proj_ms, 5),
-            "projection_tflops_est": round(flops / (proj_ms * 1e-3) / 1e12, 1) if proj_ms > 0 else None,
-            "note": "inputs resident; the projection's time is the step minus the attention-only step"}
+            "tokens_per_s": round(w.tokens / (ms / 1e3), 1), "attention_only_ms": round(core_ms, 5),
+            "projection_kernel": "k_qkv", "projection_us": round(gemm_us, 2), "projection_flops": flops,
+            "projection_tflops": round(flops / (gemm_us * 1e-6) / 1e12, 1) if gemm_us > 0 else None,
+            "projection_mfma_frac": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)
+            if gemm_us > 0 else None,
+            "kernels_us": {kk: round(1e3 * t / c, 2) for kk, (t, c) in prof.items()},
+            "note": "inputs resident"}
 
 
 def time_backward(w, x, steps, warmup, torch, nys):
@@ -384,6 +414,10 @@ PROFILE_COMMANDS = {
              "--no-module --no-backward",
     "trace_all": "rocprofv3 --kernel-trace --stats --output-format csv -d {O}/trace_all -o trace_all -- "
                  "python3 {R}/bench.py --workload {W} --steps 10 --warmup 3 --also '' --no-cpu-baseline",
+    "sq": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_INSTS_LDS "
+          "SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA --output-format csv -d {O}/sq -o sq -- "
+          "python3 {R}/bench.py --workload {W} --steps 5 --warmup 2 --also '' --no-cpu-baseline --no-probs "
+          "--no-module --no-backward",
     "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {O}/copy_fetch -o copy_fetch -- "
                   "python3 {R}/bench.py --copy-probe-mb 256",
     "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {O}/copy_write -o copy_write -- "
@@ -403,6 +437,11 @@ def summarize(argv):
     traffic W O OUTDIR    traffic_<kernel>_<workload>.txt for every library
                           kernel: FETCH_SIZE / WRITE_SIZE per launch, scaled
                           by a plain copy of known size
+    counters W O OUTDIR   counters_<workload>.txt: per kernel the SQ counters
+                          of one pass (matrix-core busy fraction against the
+                          kernel's rocprof duration on all 1024 SIMDs at
+                          2.4 GHz, wave wait fractions, LDS bank conflict
+                          cycles per LDS instruction)
     """
     from efficient_transformer_attention_segment_amd.workloads import WORKLOADS
     kind, widx, odir = argv[0], int(argv[1]), argv[2]
@@ -489,6 +528,48 @@ def summarize(argv):
                 f.write("\n".join(lines) + "\n")
             print(path)
         return
+    if kind == "counters":
+        rows = _csv_rows(os.path.join(odir, "sq", "sq_counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            k = _short(r["Kernel_Name"])
+            if not k.startswith("k_"):
+                continue
+            d = acc.setdefault(k, {})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        trace = {}
+        tpath = os.path.join(odir, "trace", "trace_kernel_stats.csv")
+        if os.path.exists(tpath):
+            for r in _csv_rows(tpath):
+                trace[_short(r["Name"])] = float(r["AverageNs"]) / 1e3
+        lines = [f"# SQ counters per launch, {w.name}",
+                 f"# command (from /tmp, TMPDIR=/tmp): {cmds['sq']}",
+                 f"# durations: {cmds['trace']}",
+                 f"# summary: python3 bench.py --summarize counters {widx} {odir} {outdir}",
+                 f"source_sha: {sha}", "",
+                 "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x rocprof avg duration x 2.4 GHz);",
+                 "# wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES; wait_inst = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES;",
+                 "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (cycles per LDS instruction)",
+                 "kernel | launches | rocprof avg_us | SQ_INSTS_MFMA | mfma_busy | wait | wait_inst | "
+                 "SQ_INSTS_LDS | lds_conflict",
+                 "---|---|---|---|---|---|---|---|---"]
+        for k in sorted(acc):
+            d = {c: sum(v) / len(v) for c, v in acc[k].items()}
+            n = len(next(iter(acc[k].values())))
+            us = trace.get(k)
+            busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            mb = busy / (1024 * us * 1e-6 * 2.4e9) if us else None
+            wc = d.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+            li = d.get("SQ_INSTS_LDS", 0.0)
+            lines.append(f"{k} | {n} | {'' if us is None else f'{us:.2f}'} | {d.get('SQ_INSTS_MFMA', 0):.0f} | "
+                         f"{'' if mb is None else f'{mb:.3f}'} | {d.get('SQ_WAIT_ANY', 0) / wc:.3f} | "
+                         f"{d.get('SQ_WAIT_INST_ANY', 0) / wc:.3f} | {li:.0f} | "
+                         f"{(d.get('SQ_LDS_BANK_CONFLICT', 0) / li) if li else 0:.3f}")
+        path = os.path.join(outdir, f"counters_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(path)
+        return
     raise SystemExit(f"unknown summary kind {kind!r}")
 
 
@@ -520,16 +601,25 @@ def main():
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
     dom_us = kern[dom]["avg_us"]
     achieved = per_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(dom, w.name, sha), "kernel": dom,
-                "kernel_avg_us": round(dom_us, 2),
-                "algorithmic_bytes_per_launch": per_bytes.get(dom, 0)}
     flops = algorithmic_flops(w)
     path = {"bytes": path_bytes, "hbm_frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
             "roofline_us": round(1e6 * max(path_bytes / (HBM_PEAK_GBS * 1e9),
                                            flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)), 2)}
+    rp_us = read_trace_avg(dom, w.name, sha)
+    rp_ach = per_bytes.get(dom, 0) / (rp_us * 1e-6) / 1e9 if rp_us else None
+    # frac: the dominant kernel (live kernel-stamped events); call_frac: the
+    # whole call's roofline time over its measured time, the measure the
+    # 50 % target is stated in
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(dom, w.name, sha), "kernel": dom,
+                "kernel_avg_us": round(dom_us, 2),
+                "algorithmic_bytes_per_launch": per_bytes.get(dom, 0),
+                "rocprof_avg_us": rp_us,
+                "frac_rocprof": round(rp_ach / HBM_PEAK_GBS, 4) if rp_ach else None,
+                "call_frac": round(path["roofline_us"] / (ms * 1e3), 4),
+                "call_roofline_us": path["roofline_us"]}
     also = []
     for s in [s for s in args.also.split(",") if s.strip()]:
         wi = WORKLOADS[int(s)]
@@ -538,18 +628,19 @@ def main():
         msi, profi, _, _, _, _ = time_workload(wi, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
         pb, pathb = algorithmic_bytes(wi)
         fl = algorithmic_flops(wi)
+        rl_us = 1e6 * max(pathb / (HBM_PEAK_GBS * 1e9), fl / (MFMA_PEAK_TFLOPS[wi.dtype] * 1e12))
         also.append({"workload": wi.name, "dtype": wi.dtype, "ms_per_step": round(msi, 4),
                      "tokens_per_s": round(wi.tokens / (msi / 1e3), 1),
                      "path_hbm_frac": round(pathb / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "path_roofline_us": round(1e6 * max(pathb / (HBM_PEAK_GBS * 1e9),
-                                                         fl / (MFMA_PEAK_TFLOPS[wi.dtype] * 1e12)), 2),
+                     "path_roofline_us": round(rl_us, 2),
+                     "call_frac": round(rl_us / (msi * 1e3), 4),
                      "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
     weights = None if args.no_probs else time_probs(w, x, max(5, args.steps // 5), max(2, args.warmup // 2),
                                                     torch, nys)
     module = None if args.no_module else time_module(w, max(5, args.steps // 5), max(2, args.warmup // 2), torch,
                                                      nys, ms)
     backward = None
-    if not args.no_backward and w.m <= 128:
+    if not args.no_backward:
         backward = time_backward(w, x, max(5, args.steps // 5), max(2, args.warmup // 2), torch, nys)
     copy_gbs = copy_bandwidth(torch)
     roofline["attainable_copy_GBps"] = round(copy_gbs, 1)

@@ -269,21 +269,22 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     // so the grid fills the CUs at the occupancy its LDS allows in at most
     // one resident round (a second, partial round would cost a whole
     // workgroup lifetime)
-    constexpr size_t lds4 = OutStreamLayout<M>::LDS_BYTES;
+    constexpr int NW = outs_waves<M>(), UNIT = outs_unit<NW>();
+    constexpr size_t lds4 = OutStreamLayout<M, NW>::LDS_BYTES;
     constexpr int per_cu = std::min<int>(4, (int)(160 * 1024 / lds4));
     const int slots = 256 * per_cu;
     const int want = std::max(1, slots / p.BH);  // workgroups per head
-    const int R = OUTS_UNIT * ((p.n + want * OUTS_UNIT - 1) / (want * OUTS_UNIT));
+    const int R = UNIT * ((p.n + want * UNIT - 1) / (want * UNIT));
     const int nbh = (p.n + R - 1) / R;
     u16* const junk = at<u16>(w, p.off_junk);
     auto launch_out = [&](auto kern) -> int {
-      HIP_TRY(launch("k_out_stream", kern, dim3(nbh, p.BH), dim3(256), 0u, st, oa, R, junk));
+      HIP_TRY(launch("k_out_stream", kern, dim3(nbh, p.BH), dim3(64 * NW), 0u, st, oa, R, junk));
       return NYS_OK;
     };
-    const int orc = conv_w != nullptr ? (pad ? launch_out(k_out_stream<M, true, true>)
-                                             : launch_out(k_out_stream<M, true, false>))
-                                      : (pad ? launch_out(k_out_stream<M, false, true>)
-                                             : launch_out(k_out_stream<M, false, false>));
+    const int orc = conv_w != nullptr ? (pad ? launch_out(k_out_stream<M, true, true, NW>)
+                                             : launch_out(k_out_stream<M, true, false, NW>))
+                                      : (pad ? launch_out(k_out_stream<M, false, true, NW>)
+                                             : launch_out(k_out_stream<M, false, false, NW>));
     if (orc != NYS_OK) return orc;
   } else {
     using OL = OutLayout<IO, M, D>;

@@ -239,30 +239,52 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
 // Each lane's conv reads sit at a fixed row offset from the unit's first token,
 // so their addresses are a per-unit row term plus per-lane constants.
 
-constexpr int OUTS_UNIT = 64;   // tokens per unit (and rows per ring group)
-constexpr int OUTS_RING = 256;  // ring rows (4 groups)
+// A workgroup of NW waves (4, or 8 where LDS allows only one workgroup per
+// CU) takes units of 16 NW tokens, one 16-token tile per wave; the V ring
+// holds four units' rows.
+template <int NW>
+constexpr int outs_unit() {
+  return 16 * NW;  // tokens per unit (and rows per ring group)
+}
+template <int NW>
+constexpr int outs_ring() {
+  return 4 * outs_unit<NW>();  // ring rows (4 groups)
+}
+constexpr int OUTS_UNIT = outs_unit<4>();
 
+// The wave count of the persistent output pass: 8 above 192 landmarks (the
+// landmarks and W^T fragments alone take 64 KB, so one workgroup per CU: 8
+// waves hide twice the latency of 4, 42 -> 38 us at 1 x 4 x 65536, m = 256),
+// otherwise 4 (several workgroups per CU; 8 waves there were slower, 19.5 ->
+// 25.6 us at 4 x 12 x 4096, m = 64).
 template <int M>
+constexpr int outs_waves() {
+  return M > 192 ? 8 : 4;
+}
+
+template <int M, int NW = 4>
 struct OutStreamLayout {
   static constexpr int KS = M / 32;
   static constexpr int KT_ELEMS = M * HD;
   static constexpr int WF_ELEMS = 4 * KS * 64 * 8;
-  static constexpr int RING_ELEMS = OUTS_RING * HD;
+  static constexpr int RING_ELEMS = outs_ring<NW>() * HD;
   static constexpr int LDS_BYTES = 2 * (KT_ELEMS + WF_ELEMS + RING_ELEMS);
 };
 
+template <int NW>
 __device__ __forceinline__ int vring_pos(int r, int chunk) {
-  return (r & (OUTS_RING - 1)) * HD + 8 * (chunk ^ (2 * (r & 3)));
+  return (r & (outs_ring<NW>() - 1)) * HD + 8 * (chunk ^ (2 * (r & 3)));
 }
 
 // One group in flight through registers: thread t holds 32 bytes of row
-// 64 G + t / 4 (16-byte chunks 2 (t % 4) and 2 (t % 4) + 1); zero outside [0, n).
+// UNIT G + t / 4 (16-byte chunks 2 (t % 4) and 2 (t % 4) + 1); zero outside [0, n).
 struct VGroup {
   uint4 x[2];
 };
+template <int NW>
 __device__ __forceinline__ void vgroup_load(const u16* V, long long st, int n, int G, VGroup& b) {
   const int t = threadIdx.x;
-  const int r = OUTS_UNIT * G + (t >> 2);
+  const int r = outs_unit<NW>() * G + (t >> 2);
   if (r >= 0 && r < n) {
     const uint4* src = reinterpret_cast<const uint4*>(V + r * st) + 2 * (t & 3);
     b.x[0] = src[0];
@@ -271,9 +293,10 @@ __device__ __forceinline__ void vgroup_load(const u16* V, long long st, int n, i
     b.x[0] = b.x[1] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
+template <int NW>
 __device__ __forceinline__ void vgroup_store(const VGroup& b, int G, __bf16* ring) {
   const int t = threadIdx.x;
-  const int r = OUTS_UNIT * G + (t >> 2);
+  const int r = outs_unit<NW>() * G + (t >> 2);
   // rows with bit 3 set keep the two 8-byte halves of each chunk swapped, so
   // that the transposed reads of rows r and r + 8 (lane groups 0 and 1 of
   // one read) fall in different banks
@@ -281,7 +304,7 @@ __device__ __forceinline__ void vgroup_store(const VGroup& b, int G, __bf16* rin
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const uint4 v = b.x[c];
-    *reinterpret_cast<uint4*>(ring + vring_pos(r, 2 * (t & 3) + c)) = sw ? make_uint4(v.z, v.w, v.x, v.y) : v;
+    *reinterpret_cast<uint4*>(ring + vring_pos<NW>(r, 2 * (t & 3) + c)) = sw ? make_uint4(v.z, v.w, v.x, v.y) : v;
   }
 }
 
@@ -312,12 +335,14 @@ __device__ __forceinline__ void conv_lane_init(ConvLane& cl) {
 // Convolution of the wave's 16-token tile of the unit starting at t0 from
 // the ring (window rows ts - 32 .. ts + 63 in three 32-row steps; taps beyond
 // the 80 needed are 0).
+template <int NW>
 __device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int t0, const ConvLane& cl, const Frag2 (&tap)[3],
                                                f32x4 (&oacc)[4]) {
+  constexpr int RING = outs_ring<NW>();
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    const __bf16* r0 = ring + ((t0 + cl.rel[kk][0]) & (OUTS_RING - 1)) * HD;
-    const __bf16* r1 = ring + ((t0 + cl.rel[kk][1]) & (OUTS_RING - 1)) * HD;
+    const __bf16* r0 = ring + ((t0 + cl.rel[kk][0]) & (RING - 1)) * HD;
+    const __bf16* r1 = ring + ((t0 + cl.rel[kk][1]) & (RING - 1)) * HD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const bf16x4 x0 = lds_read_tr(r0 + cl.coff[kk][0][dt]);
@@ -340,9 +365,10 @@ __device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int 
 // [x R, min(n, (x + 1) R)), R a multiple of 64.  junk: >= 16 * 64 bf16, the
 // destination of tiles past the range.  Two Q register buffers alternate
 // between even and odd units (loaded two units before use).
-template <int M, bool CONV, bool PAD>
-__global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk) {
-  using Ly = OutStreamLayout<M>;
+template <int M, bool CONV, bool PAD, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_out_stream(OutArgs a, int R, u16* junk) {
+  constexpr int OUTS_UNIT = outs_unit<NW>();
+  using Ly = OutStreamLayout<M, NW>;
   constexpr int KS = Ly::KS, TM = M / 16;
   __shared__ __align__(16) __bf16 kt_s[Ly::KT_ELEMS];
   __shared__ __align__(16) __bf16 wf_s[Ly::WF_ELEMS];
@@ -374,12 +400,12 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     const __bf16* kt = a.kt_hi + (size_t)bh * M * HD;
     const __bf16* wf = a.wf_hi + (size_t)bh * 4 * KS * 64 * 8;
     const int rsub = lane >> 3;
-    for (int c = wave; c < M / 8; c += 4) {
+    for (int c = wave; c < M / 8; c += NW) {
       const int row = 8 * c + rsub;
       const int chunk = (lane & 7) ^ ((row >> 1) & 7);
       dma16(kt + (size_t)row * HD + 8 * chunk, kt_s + 8 * c * HD);
     }
-    for (int c = wave; c < 4 * KS; c += 4) dma16(wf + (size_t)c * 512 + 8 * lane, wf_s + 512 * c);
+    for (int c = wave; c < 4 * KS; c += NW) dma16(wf + (size_t)c * 512 + 8 * lane, wf_s + 512 * c);
   }
   const int G0 = tb / OUTS_UNIT;
   const int Glast = G0 + nunits;  // last group any unit reads (rows up to the range end + 32)
@@ -389,11 +415,11 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     VGroup pre[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      if (G0 - 1 + i <= Glast) vgroup_load(V, st, a.n, G0 - 1 + i, pre[i]);
+      if (G0 - 1 + i <= Glast) vgroup_load<NW>(V, st, a.n, G0 - 1 + i, pre[i]);
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      if (G0 - 1 + i <= Glast) vgroup_store(pre[i], G0 - 1 + i, ring);
-    if (G0 + 2 <= Glast) vgroup_load(V, st, a.n, G0 + 2, vb);
+      if (G0 - 1 + i <= Glast) vgroup_store<NW>(pre[i], G0 - 1 + i, ring);
+    if (G0 + 2 <= Glast) vgroup_load<NW>(V, st, a.n, G0 + 2, vb);
     conv_lane_init(cl);
   }
   bf16x8 qb[2][2];
@@ -410,8 +436,8 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
     const int G = t0 / OUTS_UNIT;
     if (u > 0) __syncthreads();  // last unit's ring writes are visible; its reads of the slot reused below are done
     if constexpr (CONV) {
-      if (G + 2 <= Glast) vgroup_store(vb, G + 2, ring);  // slot of G - 2: last read by the previous unit
-      if (G + 3 <= Glast) vgroup_load(V, st, a.n, G + 3, vb);
+      if (G + 2 <= Glast) vgroup_store<NW>(vb, G + 2, ring);  // slot of G - 2: last read by the previous unit
+      if (G + 3 <= Glast) vgroup_load<NW>(V, st, a.n, G + 3, vb);
     }
     const int ts = t0 + 16 * wave;
     // S^T = Kt Q^T: sacc[it][r] = logit(token ts + c16, landmark 16 it + 4g + r)
@@ -462,7 +488,7 @@ __global__ __launch_bounds__(256) void k_out_stream(OutArgs a, int R, u16* junk)
         oacc[dt] = mfma(wf, pf, oacc[dt]);
       }
     }
-    if constexpr (CONV) conv_tile_ring(ring, t0, cl, tap, oacc);
+    if constexpr (CONV) conv_tile_ring<NW>(ring, t0, cl, tap, oacc);
     u16* dst = ts + c16 < te ? O + (ts + c16) * ot : junk + c16 * HD;
     store_row16<u16, true>(dst, oacc);
   };
