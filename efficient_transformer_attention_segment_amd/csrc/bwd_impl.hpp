@@ -287,7 +287,7 @@ int run_backward(const void* q, const void* k, const void* v, const uint8_t* mas
       default: return launch_backward_exact<IO, 128>(B, H, n, q, k, v, mask, conv_w, conv_k, dout, dq, dk, dv, dconv_w, st);
     }
   }
-  Plan p = make_plan(B, H, n, m, d);
+  Plan p = make_plan(B, H, n, m, d, (int)sizeof(IO));
   p.record = true;  // A is read back
   p.bwd = true;
   p.si = p.so = dense(B, H, n, d);

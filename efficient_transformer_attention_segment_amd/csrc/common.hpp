@@ -162,6 +162,13 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
 
+// Landmark row groups of the B V blocks (k_bv.hpp) for I/O elements of esize
+// bytes, M (padded) landmarks and head size d; the host sizes the key chunks
+// and the partials with the same rule.
+__host__ __device__ constexpr int bv_row_groups_for(int esize, int M, int d) {
+  return (esize == 2 && d == HD && M == 128) ? 2 : 1;
+}
+
 // Element strides of a [B, H, n, 64] tensor view: batch, head and token; the
 // 64 channels of a token are contiguous.  Dense [B, H, n, 64] is
 // {H n 64, n 64, 64}; [B, n, H, 64] is {n H 64, 64, H 64}.

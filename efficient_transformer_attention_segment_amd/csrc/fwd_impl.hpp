@@ -67,7 +67,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                  (const IO*)k, la));
   size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
-  lds2 = std::max<size_t>(lds2, bv_fold_bytes<M, D>());
+  lds2 = std::max<size_t>(lds2, bv_fold_bytes<bv_rows<IO, M, D>(), D>());
   if constexpr (M <= 128)
     lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
                                                   : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
@@ -85,7 +85,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     const void* kern = edge ? reinterpret_cast<const void*>(k_pinv_bv<IO, M, true, D>)
                             : reinterpret_cast<const void*>(k_pinv_bv<IO, M, false, D>);
     if (allow_lds(edge ? k_pinv_bv<IO, M, true, D> : k_pinv_bv<IO, M, false, D>, lds2) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * bv_waves<M>(), lds2) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * bv_launch_waves<IO, M, D>(), lds2) !=
+            hipSuccess)
       return 0;
     return std::min(FUSED_GRAM_MAX_BLOCKS, per_cu * cus / 2);
   }();
@@ -136,6 +137,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.status = at<unsigned>(w, STATUS_OFF);
   pa.la = la;
   BvArgs ba;
+  ba.BH = p.BH;
   ba.k = k;
   ba.v = v;
   ba.key_mask = mask;
@@ -151,10 +153,12 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
   ba.in = p.si;
+  constexpr int RG = bv_row_groups<IO, M, D>();
+  const int nbv = RG == 1 ? p.BH * p.S : 8 * RG * ((p.BH * p.S + 7) / 8);
   auto launch_bv = [&](auto kern) -> int {
     HIP_TRY(allow_lds(kern, lds2));
-    HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + p.BH * p.S), dim3(64 * bv_waves<M>()), (uint32_t)lds2, st, pa,
-                   ba, p.npinv));
+    HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + nbv), dim3(64 * bv_launch_waves<IO, M, D>()), (uint32_t)lds2,
+                   st, pa, ba, p.npinv));
     return NYS_OK;
   };
   const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D>) : launch_bv(k_pinv_bv<IO, M, false, D>);

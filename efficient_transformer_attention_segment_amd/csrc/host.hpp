@@ -68,7 +68,9 @@ constexpr int FUSED_GRAM_MAX_BLOCKS = 128;
 // the pseudo-inverse and contribute nothing to W or the output.
 inline int padded_m(int m) { return (m + 31) & ~31; }
 
-Plan make_plan(int B, int H, int n, int mr, int d);
+// esize: bytes per I/O element (the B V blocks' row groups depend on it; 4
+// gives the largest workspace).
+Plan make_plan(int B, int H, int n, int mr, int d, int esize = 4);
 
 // ------------------------------------------------------- kernel timing ---
 // Every launch goes through launch().  While timing is enabled it uses

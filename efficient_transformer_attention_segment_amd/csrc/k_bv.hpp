@@ -324,6 +324,7 @@ __device__ __forceinline__ void kv_stream_dma(const u16* __restrict__ K, const u
 }
 
 struct BvArgs {
+  int BH;                   // heads (for the row-group block mapping)
   const void* k;
   const void* v;
   const uint8_t* key_mask;  // [B][n] or null
@@ -344,6 +345,30 @@ constexpr int bv_waves() {
   return M <= 128 ? nwaves<M>() : 4;
 }
 
+// Row groups of the B V blocks.  With bf16 I/O at d = 64 and 128 landmarks,
+// a B V block covers half of the landmark rows of its key chunk: two blocks
+// per (head, chunk), each the 64-landmark block with a row offset, so the
+// chunks can be twice as long for the same number of blocks and the
+// partials that k_mw merges halve.  The two row groups of one chunk run on
+// one XCD (their blocks are 8 apart), where its K and V tiles are fetched
+// into L2 once.  At 256 landmarks the split does not pay: with four 64-row
+// groups the live K and V tiles of an XCD outgrow its L2 (B V launch 35 ->
+// 49 us at 1 x 4 x 65536, k_mw 19 -> 13 us), and two 128-row groups still
+// lose 2 us over the two launches.
+template <typename IO, int M, int D>
+constexpr int bv_row_groups() {
+  return bv_row_groups_for((int)sizeof(IO), M, D);
+}
+// Rows and waves of one B V block, and the waves of the whole launch.
+template <typename IO, int M, int D>
+constexpr int bv_rows() {
+  return M / bv_row_groups<IO, M, D>();
+}
+template <typename IO, int M, int D>
+constexpr int bv_launch_waves() {
+  return bv_row_groups<IO, M, D>() > 1 ? nwaves<M>() : bv_waves<M>();
+}
+
 // Partial B V of one (head, key chunk): all M landmarks.  With NW waves
 // and TM landmark tiles, wave w owns landmark tiles {w, w + NW, ...}; when
 // there are twice as many waves as tiles (m <= 64) the tile's two waves
@@ -357,10 +382,11 @@ constexpr int bv_fold_bytes() {
   return 4 * (M / 16) * 64 * (2 + D / 4);
 }
 
-template <typename IO, int M, bool EDGE, int D = HD>
-__device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
-  constexpr int TM = M / 16;
-  constexpr int NW = bv_waves<M>();
+// MB landmark rows r0 .. r0 + MB - 1 of M (MB = M without row groups).
+template <typename IO, int M, bool EDGE, int D = HD, int MB = M>
+__device__ void bv_block(const BvArgs& a, int bh, int chunk, int r0, __bf16* lds) {
+  constexpr int TM = MB / 16;
+  constexpr int NW = bv_waves<MB>();
   constexpr int KP = (M <= 128 && NW % TM == 0) ? NW / TM : 1;
   constexpr int NWT = KP > 1 ? TM : NW;  // waves per key parity
   constexpr int TPW = (TM + NWT - 1) / NWT;
@@ -387,7 +413,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
     if (o < nown) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const size_t off = ((size_t)bh * M + 16 * lt + c16) * D + 32 * ks + 8 * g;
+        const size_t off = ((size_t)bh * M + r0 + 16 * lt + c16) * D + 32 * ks + 8 * g;
         qf[o][ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
         // bf16 keys: one bf16 pass (hi plane) against exact bf16 operands
         if constexpr (IOTraits<IO>::NS == 3) qf[o][ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
@@ -442,7 +468,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
 #pragma unroll
   for (int o = 0; o < TPW; ++o) {
     if (o >= nown || kp != 0) break;
-    const int i = 16 * (wave + NWT * o) + c16;
+    const int i = r0 + 16 * (wave + NWT * o) + c16;
     const float ls = sum_g(lsum[o]);
     const size_t row = ((size_t)bh * a.S + chunk) * M + i;
     if (g == 0) {
@@ -464,7 +490,7 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, __bf16* lds) {
 // key tile (n not a multiple of 32); the code for them is compiled only into
 // this instance, so the common shapes pay nothing for it.
 template <typename IO, int M, bool EDGE, int D = HD>
-__global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
+__global__ __launch_bounds__((64 * bv_launch_waves<IO, M, D>())) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
     if constexpr (M <= 128) {
@@ -478,7 +504,16 @@ __global__ __launch_bounds__(64 * bv_waves<M>()) void k_pinv_bv(PinvArgs pa, BvA
     return;
   }
   const int id = blockIdx.x - npinv;
-  bv_block<IO, M, EDGE, D>(ba, id / ba.S, id % ba.S, lds_dyn);
+  constexpr int RG = bv_row_groups<IO, M, D>();
+  if constexpr (RG == 1) {
+    bv_block<IO, M, EDGE, D>(ba, id / ba.S, id % ba.S, 0, lds_dyn);
+  } else {
+    // blocks 8 apart take the row groups of one (head, chunk)
+    const int rg = (id / 8) % RG, rest = id % 8 + 8 * (id / (8 * RG));
+    if (rest >= ba.BH * ba.S) return;  // grid rounding; whole workgroup, before any barrier
+    constexpr int MB = bv_rows<IO, M, D>();
+    bv_block<IO, M, EDGE, D, MB>(ba, rest / ba.S, rest % ba.S, MB * rg, lds_dyn);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -44,7 +44,7 @@ int pow2ceil(int x) {
   return p;
 }
 
-Plan make_plan(int B, int H, int n, int mr, int d) {
+Plan make_plan(int B, int H, int n, int mr, int d, int esize) {
   Plan p{};
   const int m = padded_m(mr);
   p.D = d;
@@ -69,8 +69,9 @@ Plan make_plan(int B, int H, int n, int mr, int d) {
   p.ntiles = (n + 31) / 32;  // the last tile is ragged when n % 32 != 0
   p.npinv = m <= 128 ? p.BH : 0;
   const int resident = 2 * 256;
+  const int rg = bv_row_groups_for(esize, m, d);  // B V blocks per (head, chunk)
   const int target = std::max(p.BH, resident - p.npinv);
-  int S = std::max(1, std::min(p.ntiles, target / p.BH));
+  int S = std::max(1, std::min(p.ntiles, target / (p.BH * rg)));
   p.tpc = (p.ntiles + S - 1) / S;
   p.S = (p.ntiles + p.tpc - 1) / p.tpc;
   const size_t BH = p.BH, M = m, D = d;
@@ -270,7 +271,7 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
   int rc = check_call(sizeof(IO), q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, probs);
   if (rc != NYS_OK) return rc;
   if (fixed != nullptr && m != n) {
-    const size_t need = make_plan(B, H, n, m, d).total;
+    const size_t need = make_plan(B, H, n, m, d, (int)sizeof(IO)).total;
     if (need > fixed->cap)
       return fail(NYS_ERR_UNSUPPORTED,
                   "this shape needs %zu bytes of scratch; the allocation-free entry point has %zu (NYS_NOALLOC_SCRATCH_BYTES)",
@@ -281,7 +282,7 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
     if (d == 128) return launch_exact<IO, 128>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
     return launch_exact<IO, 64>(B, H, n, si, so, q, k, v, mask, conv_w, conv_k, out, probs, st);
   }
-  Plan p = make_plan(B, H, n, m, d);
+  Plan p = make_plan(B, H, n, m, d, (int)sizeof(IO));
   p.record = pout != nullptr;  // the stage hook reads the intermediates back
   p.si = si;
   p.so = so;
