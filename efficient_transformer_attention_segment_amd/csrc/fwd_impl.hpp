@@ -11,8 +11,8 @@
 //   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
 //                  blocks (m <= 128) and the B V partial blocks, so the
 //                  pseudo-inverse chain runs beside the K/V stream
-//     (m > 128, bf16 I/O: k_gram_rows, then 3 k_pinv_mm launches per
-//     iteration before it; float32 I/O: k_gram, then k_pinv_init and 4
+//     (m > 128, bf16 I/O: k_gram_rows before it, and 3 k_pinv_mm launches
+//     per iteration after it; float32 I/O: k_gram, then k_pinv_init and 4
 //     k_pinv_gemm launches per iteration after it)
 //   4 k_mw         B V from the partials, W = Z (B V) and its operand
 //                  fragments
@@ -110,7 +110,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
       float* const colpart = at<float>(w, p.off_colpart);
       float* const rowpart = at<float>(w, p.off_rowpart);
       HIP_TRY(launch("k_gram_rows", k_gram_rows<M, D>, dim3(M / 32, p.BH), dim3(128), (uint32_t)grl, pst, la,
-                     at<float>(w, p.off_AT), colpart, rowpart));
+                     at<float>(w, p.off_AT), at<u16>(w, p.off_T1), colpart, rowpart));
     }
   }
   if (!fuse_gram && !mm_path) {
@@ -170,17 +170,20 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
       PinvMMArgs mm;
       mm.A = la.A;
       mm.AT = at<float>(w, p.off_AT);
-      mm.X = at<float>(w, p.off_X);
-      mm.Xt = at<float>(w, p.off_Xt);
-      mm.X2t = at<float>(w, p.off_X2t);
+      mm.A16 = at<u16>(w, p.off_T1);
+      mm.Z = pa.Z;
+      mm.Z16 = at<u16>(w, p.off_Z2);
+      mm.Zt16 = at<u16>(w, p.off_Zt);
+      mm.X16 = at<u16>(w, p.off_X);
+      mm.Xt16 = at<u16>(w, p.off_Xt);
+      mm.X2t16 = at<u16>(w, p.off_X2t);
       mm.W = at<float>(w, p.off_T2);
+      mm.W16 = at<u16>(w, p.off_Zt2);
       mm.pa = pa;
       mm.colpart = at<float>(w, p.off_colpart);
       mm.colmax = la.colmax;
       mm.rowmax = la.rowmax;
       mm.rowpart = at<float>(w, p.off_rowpart);
-      float* Zb[2] = {at<float>(w, p.off_Z), at<float>(w, p.off_Z2)};
-      float* Ztb[2] = {at<float>(w, p.off_Zt), at<float>(w, p.off_Zt2)};
       constexpr int NT2 = (M / PMM_T) * (M / PMM_T);
       constexpr int l1 = pinv_mm_lds_bytes<M, 1>(), l2 = pinv_mm_lds_bytes<M, 2>(), l3 = pinv_mm_lds_bytes<M, 3>();
       HIP_TRY(allow_lds(k_pinv_mm<M, 1>, l1));
@@ -188,10 +191,6 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
       HIP_TRY(allow_lds(k_pinv_mm<M, 3>, l3));
       for (int it = 0; it < n_iter; ++it) {
         mm.first = it == 0 ? 1 : 0;
-        mm.Z = Zb[it % 2];
-        mm.Zt = Ztb[it % 2];
-        mm.Zn = Zb[(it + 1) % 2];
-        mm.Znt = Ztb[(it + 1) % 2];
         HIP_TRY(launch("k_pinv_mm1", k_pinv_mm<M, 1>, dim3(pinv_mm_grid(NT2, p.BH)), dim3(256), (uint32_t)l1, pst,
                        mm));
         HIP_TRY(launch("k_pinv_mm2", k_pinv_mm<M, 2>, dim3(pinv_mm_grid(2 * NT2, p.BH)), dim3(256), (uint32_t)l2,
@@ -199,7 +198,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
         HIP_TRY(launch("k_pinv_mm3", k_pinv_mm<M, 3>, dim3(pinv_mm_grid(NT2, p.BH)), dim3(256), (uint32_t)l3, pst,
                        mm));
       }
-      Zfinal = Zb[n_iter % 2];
+      Zfinal = pa.Z;
     }
   }
   if constexpr (M > 128) if (!mm_path) {

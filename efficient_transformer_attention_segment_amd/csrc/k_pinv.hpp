@@ -268,10 +268,14 @@ __device__ float pinv_prologue(const PinvArgs& a, int bh, float* L) {
   if (!a.fuse_gram) {
     constexpr int NT = 64 * NW, TOT = M * M / 4, CNT = (TOT + NT - 1) / NT;
     const float4* A = reinterpret_cast<const float4*>(a.A + (size_t)bh * M * M);
+    // every element of x is assigned (out-of-range slots read element 0 and
+    // are not stored), so the array stays in registers
     float4 x[CNT];
 #pragma unroll
-    for (int k = 0; k < CNT; ++k)
-      if (threadIdx.x + k * NT < TOT) x[k] = A[threadIdx.x + k * NT];
+    for (int k = 0; k < CNT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      x[k] = A[i < TOT ? i : 0];
+    }
 #pragma unroll
     for (int k = 0; k < CNT; ++k) {
       const int i = threadIdx.x + k * NT, row = i / (M / 4), c4 = i % (M / 4);

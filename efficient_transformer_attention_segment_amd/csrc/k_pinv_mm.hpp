@@ -26,10 +26,15 @@
 //   each, K = M in fp16 16x16x32 matrix-core steps), every tile of a head on
 //   one XCD.  Level 1 of the first iteration also forms c from the Gram
 //   partials (column sums of the row blocks added in order).  Operand
-//   panels are read as float32 rows (the left factor's rows, and the rows
-//   of the right factor's transpose, which every level also writes), scaled
-//   and rounded to fp16 into LDS once per block.  In the first iteration
-//   Z = A^T / c is read from A^T (rows of Z) and A (rows of Z^T).
+//   panels are 32 rows of the left factor and 32 rows of the right factor's
+//   transpose, copied into LDS once per block.  The matrices that serve as
+//   operands are kept in global memory as fp16 rows (A, X, X^T, (X^2)^T, W,
+//   Z, Z^T), rounded once by the launch that forms them: each workgroup's
+//   inputs come from the Infinity Cache at a rate of a few tens of GB/s per
+//   CU, so halving the bytes of its two or three panels is what shortens the
+//   launch.  Z and W are also kept in float32 for the linear combination.
+//   In the first iteration Z = A^T / c is read from the float32 A^T (rows of
+//   Z) and A (rows of Z^T), scaled and rounded on the way into LDS.
 #pragma once
 
 #include "common.hpp"
@@ -48,7 +53,7 @@ constexpr int gram_rows_lds_bytes() {
 
 // grid (M / 32, BH), 128 threads: wave w forms row tile 2 blockIdx.x + w.
 template <int M, int D>
-__global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __restrict__ AT,
+__global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __restrict__ AT, u16* __restrict__ A16,
                                                    float* __restrict__ colpart, float* __restrict__ rowpart) {
   extern __shared__ __align__(16) char gr_smem[];
   constexpr int TM = M / 16, DK = D / 32, KLD = D + 8;
@@ -114,12 +119,16 @@ __global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __rest
   }
   float* const Ah = a.A + (size_t)bh * M * M;
   float* const ATh = AT + (size_t)bh * M * M;
+  _Float16* const A16h = reinterpret_cast<_Float16*>(A16) + (size_t)bh * M * M;
   const int row4 = rt * 16 + 4 * g;
 #pragma unroll
   for (int ct = 0; ct < TM; ++ct) {
     const int col = ct * 16 + c16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ah[(size_t)(row4 + r) * M + col] = acc[ct][r];
+    for (int r = 0; r < 4; ++r) {
+      Ah[(size_t)(row4 + r) * M + col] = acc[ct][r];
+      A16h[(size_t)(row4 + r) * M + col] = (_Float16)acc[ct][r];
+    }
     *reinterpret_cast<float4*>(ATh + (size_t)col * M + row4) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
     const float cs = sum_g(acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3]);
     if (g == 0) csum[wave * M + col] = cs;
@@ -134,16 +143,18 @@ __global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __rest
 
 // -------------------------------------------------------------- products ---
 struct PinvMMArgs {
-  const float* A;    // [BH][M][M] rows of A
-  const float* AT;   // [BH][M][M] rows of A^T
-  const float* Z;    // rows of Z_k (k >= 1)
-  const float* Zt;   // rows of Z_k^T
-  float* X;          // rows of X
-  float* Xt;         // rows of X^T
-  float* X2t;        // rows of (X^2)^T
-  float* W;          // rows of W = Z X
-  float* Zn;         // rows of Z_{k+1}
-  float* Znt;        // rows of Z_{k+1}^T
+  // [BH][M][M] each; fp16 matrices as _Float16 bit patterns
+  const float* A;    // rows of A (float32: the first iteration's Z^T = A / c)
+  const float* AT;   // rows of A^T (float32: the first iteration's Z = A^T / c)
+  const u16* A16;    // rows of A
+  float* Z;          // rows of Z (float32), updated in place by level 3
+  u16* Z16;          // rows of Z
+  u16* Zt16;         // rows of Z^T
+  u16* X16;          // rows of X
+  u16* Xt16;         // rows of X^T
+  u16* X2t16;        // rows of (X^2)^T
+  float* W;          // rows of W = Z X (float32)
+  u16* W16;          // rows of W
   const float* colpart;  // [BH][M / 32][M] Gram column-sum partials
   const float* rowpart;  // [BH][M / 32] Gram row-sum maxima
   float* colmax;     // [BH] out: head's largest column sum of A
@@ -188,6 +199,45 @@ struct PanelLoad {
   }
 };
 
+// Rows r0 .. r0 + 31 of an fp16 [M][M] matrix into an LDS panel: the loads
+// first (N 16-byte pieces per thread), then the stores.
+template <int M>
+struct PanelLoad16 {
+  static constexpr int TOT = PMM_T * M / 8, N = (TOT + 255) / 256;  // 8-element pieces
+  uint4 x[N];
+  __device__ __forceinline__ void load(const u16* src, int r0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int idx = threadIdx.x + 256 * i;  // piece index within the panel
+      if (TOT % 256 != 0 && idx >= TOT) idx = 0;  // past the panel: a valid address, not stored
+      x[i] = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + idx / (M / 8)) * M + 8 * (idx % (M / 8)));
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (TOT % 256 == 0 || idx < TOT)
+        *reinterpret_cast<uint4*>(lds + (idx / (M / 8)) * pinv_mm_ld<M>() + 8 * (idx % (M / 8))) = x[i];
+    }
+  }
+};
+
+// Panel from float32 rows times s (first iteration) or from fp16 rows.
+template <int M>
+__device__ __forceinline__ void load_panel(_Float16* lds, bool f32, const float* src32, float s, const u16* src16,
+                                           int r0) {
+  if (f32) {
+    PanelLoad<M> l;
+    l.load(src32, r0);
+    l.store(lds, s);
+  } else {
+    PanelLoad16<M> l;
+    l.load(src16, r0);
+    l.store(lds);
+  }
+}
+
 // C tile (16 x 16) of the wave: sum_k Lp[16 it + i][k] Rp[16 jt + j][k].
 template <int M>
 __device__ __forceinline__ f32x4 panel_mm(const _Float16* Lp, const _Float16* Rp, int it, int jt) {
@@ -206,11 +256,21 @@ __device__ __forceinline__ f32x4 panel_mm(const _Float16* Lp, const _Float16* Rp
 }
 
 // Stores the wave's C tile (rows row4 .. row4 + 3, column col) of a
-// product into C (row-major) and, when Ct is given, C^T (row-major).
-__device__ __forceinline__ void store_c(float* C, float* Ct, int M, int row4, int col, const f32x4 v) {
+// product: float32 rows into C32, fp16 rows into C16 and fp16 rows of the
+// transpose into Ct16, each when given.
+__device__ __forceinline__ void store_c(float* C32, u16* C16, u16* Ct16, int M, int row4, int col, const f32x4 v) {
+  if (C32 != nullptr) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) C[(size_t)(row4 + r) * M + col] = v[r];
-  if (Ct != nullptr) *reinterpret_cast<float4*>(Ct + (size_t)col * M + row4) = make_float4(v[0], v[1], v[2], v[3]);
+    for (int r = 0; r < 4; ++r) C32[(size_t)(row4 + r) * M + col] = v[r];
+  }
+  if (C16 != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) reinterpret_cast<_Float16*>(C16)[(size_t)(row4 + r) * M + col] = (_Float16)v[r];
+  }
+  if (Ct16 != nullptr) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<h4*>(Ct16 + (size_t)col * M + row4) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+  }
 }
 
 // Workgroups per launch: tiles per head (T = (M / 32)^2 for levels 1 and
@@ -294,45 +354,45 @@ __global__ __launch_bounds__(256) void k_pinv_mm(PinvMMArgs a) {
       invc = 1.0f / a.pa.cscale[bh];
     }
   }
-  // rows of Z and of Z^T (A^T / c and A / c in the first iteration)
+  // float32 rows of Z (A^T / c in the first iteration) for level 3
   const float* const Zr = a.first ? a.AT + mo : a.Z + mo;
-  const float* const Ztr = a.first ? a.A + mo : a.Zt + mo;
   _Float16* const P0 = pm_lds;
   _Float16* const P1 = pm_lds + PANEL;
   _Float16* const P2 = pm_lds + 2 * PANEL;
   const int r0 = PMM_T * ti, c0 = PMM_T * tj;
-  if constexpr (LEVEL == 1) {  // X = A Z
-    PanelLoad<M> l, r;
-    l.load(a.A + mo, r0);
-    r.load(Ztr, c0);
-    l.store(P0, 1.f);
-    r.store(P1, invc);
-  } else if constexpr (LEVEL == 2) {  // X2 = X X, or W = Z X
-    PanelLoad<M> l, r;
-    l.load(second ? Zr : a.X + mo, r0);
-    r.load(a.Xt + mo, c0);
-    l.store(P0, second ? invc : 1.f);
-    r.store(P1, 1.f);
+  if constexpr (LEVEL == 1) {  // X = A Z: rows of A, rows of Z^T (A / c first)
+    PanelLoad16<M> l;
+    l.load(a.A16 + mo, r0);
+    load_panel<M>(P1, a.first, a.A + mo, invc, a.Zt16 + mo, c0);
+    l.store(P0);
+  } else if constexpr (LEVEL == 2) {  // X2 = X X, or W = Z X (Z = A^T / c first)
+    PanelLoad16<M> r;
+    r.load(a.Xt16 + mo, c0);
+    if (second)
+      load_panel<M>(P0, a.first, a.AT + mo, invc, a.Z16 + mo, r0);
+    else
+      load_panel<M>(P0, false, nullptr, 1.f, a.X16 + mo, r0);
+    r.store(P1);
   } else {  // Z' = (13 Z - 15 W + 7 W X - W X2) / 4
-    PanelLoad<M> l, r1, r2;
-    l.load(a.W + mo, r0);
-    r1.load(a.Xt + mo, c0);
-    r2.load(a.X2t + mo, c0);
-    l.store(P0, 1.f);
-    r1.store(P1, 1.f);
-    r2.store(P2, 1.f);
+    PanelLoad16<M> l, r1, r2;
+    l.load(a.W16 + mo, r0);
+    r1.load(a.Xt16 + mo, c0);
+    r2.load(a.X2t16 + mo, c0);
+    l.store(P0);
+    r1.store(P1);
+    r2.store(P2);
   }
   __syncthreads();
   const int it = wave >> 1, jt = wave & 1;
   const int row4 = r0 + 16 * it + 4 * g, col = c0 + 16 * jt + c16;
   const f32x4 acc = panel_mm<M>(P0, P1, it, jt);
   if constexpr (LEVEL == 1) {
-    store_c(a.X + mo, a.Xt + mo, M, row4, col, acc);
+    store_c(nullptr, a.X16 + mo, a.Xt16 + mo, M, row4, col, acc);
   } else if constexpr (LEVEL == 2) {
     if (second)
-      store_c(a.W + mo, nullptr, M, row4, col, acc);
+      store_c(a.W + mo, a.W16 + mo, nullptr, M, row4, col, acc);
     else  // X^2 is only ever a right factor: its transpose alone
-      *reinterpret_cast<float4*>(a.X2t + mo + (size_t)col * M + row4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      store_c(nullptr, nullptr, a.X2t16 + mo, M, row4, col, acc);
   } else {
     const f32x4 v = panel_mm<M>(P0, P2, it, jt);
     f32x4 z;
@@ -342,7 +402,8 @@ __global__ __launch_bounds__(256) void k_pinv_mm(PinvMMArgs a) {
       const float wr = a.W[mo + (size_t)(row4 + r) * M + col];
       z[r] = 0.25f * (13.f * zr - 15.f * wr + 7.f * acc[r] - v[r]);
     }
-    store_c(a.Zn + mo, a.Znt + mo, M, row4, col, z);
+    // over Z in place: this tile is the only reader of its float32 Z
+    store_c(a.Z + mo, a.Z16 + mo, a.Zt16 + mo, M, row4, col, z);
   }
 }
 

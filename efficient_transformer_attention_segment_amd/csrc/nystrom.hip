@@ -601,9 +601,12 @@ __attribute__((visibility("default"))) int nystrom_debug_stages(int dtype, const
     HIP_TRY(hipStreamSynchronize(stream));
     std::lock_guard<std::mutex> lk(g_mu);
     const size_t BH = p.BH, M = p.m, mr = p.mr;  // workspace rows M, caller rows mr
-    // after n_iter > 0 with m > 128 the final iterate lives in one of two buffers
+    // with m > 128 the literal four-product iteration (float32 I/O, or more
+    // than PINV_F16_MAX_ITER iterations) alternates between two buffers; the
+    // expanded bf16 iteration updates Z in place
+    const bool two_level = dtype == 1 && n_iter >= 1 && n_iter <= PINV_F16_MAX_ITER;
     size_t zoff = p.off_Z;
-    if (M > 128 && (n_iter % 2) == 1) zoff = p.off_Z2;
+    if (M > 128 && !two_level && (n_iter % 2) == 1) zoff = p.off_Z2;
     char* const base = static_cast<char*>(w->buf);
     // [BH][M][d] -> [BH][mr][d]
     struct Rows {
