@@ -64,11 +64,29 @@ __global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __rest
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, rt = 2 * blockIdx.x + wave;
   {
+    // the K~ planes into LDS in batches of 8 pieces per thread, every load of
+    // a batch issued before its stores (one round trip per batch instead of
+    // one per piece)
     const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * D);
     const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * D);
-    for (int i = threadIdx.x; i < M * (D / 8); i += 128) {
-      *reinterpret_cast<uint4*>(kb + (i / (D / 8)) * KLD + 8 * (i % (D / 8))) = kh[i];
-      *reinterpret_cast<uint4*>(kb + (M + i / (D / 8)) * KLD + 8 * (i % (D / 8))) = kl[i];
+    constexpr int PIECES = M * (D / 8), PER = PIECES / 128, BATCH = 4;
+    static_assert(PIECES % 128 == 0, "whole rounds of the block");
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += BATCH) {
+      uint4 xh[BATCH], xl[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (b0 + j < PER) {
+          xh[j] = kh[threadIdx.x + 128 * (b0 + j)];
+          xl[j] = kl[threadIdx.x + 128 * (b0 + j)];
+        }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (b0 + j < PER) {
+          const int i = threadIdx.x + 128 * (b0 + j);
+          *reinterpret_cast<uint4*>(kb + (i / (D / 8)) * KLD + 8 * (i % (D / 8))) = xh[j];
+          *reinterpret_cast<uint4*>(kb + (M + i / (D / 8)) * KLD + 8 * (i % (D / 8))) = xl[j];
+        }
     }
   }
   Frag2 af[DK];
