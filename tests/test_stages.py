@@ -22,10 +22,14 @@ STAGE_TOL = {
 # the measured values:
 #   qt, kt, A, c   float32 sums and float32 / split-bf16 Gram products: ~1e-7;
 #   Z (fp32 I/O)   float32 matrix-core products: ~1e-6;
-#   Z (bf16 I/O)   single fp16 products (11-bit operands) for m <= 128, whose
-#                  rounding the 24-product chain amplifies by up to cond(A);
-#                  split-bf16 products for m = 256, where A is nearly J/m
-#                  (logit std ~0.004) and far worse conditioned;
+#   Z (bf16 I/O)   single fp16 products (11-bit operands), whose rounding
+#                  the chain of products amplifies by up to cond(A): the
+#                  nested form in LDS for m <= 128, the expanded form
+#                  (13 Z - 15 ZX + 7 ZX^2 - ZX^3) / 4 above, which rounds no
+#                  shifted difference to 16 bits (at m = 256, where A is
+#                  nearly J/m with logit std ~0.004 and far worse
+#                  conditioned, the nested form rounded that way drifts by
+#                  several per cent);
 #   BV, W (bf16)   bf16 softmax weights P and bf16 V operands (2^-9 per
 #                  element) averaged over the keys: ~1e-3.
 # A stage degraded by more than 5x (a wrong operand scaling, a dropped
