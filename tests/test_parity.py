@@ -228,6 +228,19 @@ def test_iteration_counts(dtype, n_iter):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("m", [128, 256])
+@pytest.mark.parametrize("n_iter", [0, 1, 8, 9])
+def test_iteration_counts_many_landmarks(dtype, m, n_iter):
+    """Every pseudo-inverse path at 128 and 256 landmarks: at bf16 I/O the
+    fp16 iteration up to 8 steps and the split-bf16 one from 9 (in LDS at
+    m = 128, the launch chains above 128), at float32 I/O the float32 ones,
+    and n_iter = 0 (Z = A^T / c) on each; the original init with a ragged
+    mask."""
+    x = make_custom(1, 2, 4 * m, 64, seed=810 + m + n_iter, dtype=dtype, lengths=[4 * m - 100])
+    _check(f"niter{n_iter}-m{m}", x, dtype, m, n_iter, 0, conv=False)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_zero_valid_keys(dtype):
     """A batch row with every key masked: B V = 0, output = conv(V), no NaN."""
     x = make_custom(2, 2, 256, 64, seed=901, dtype=dtype, lengths=[256, 0])
