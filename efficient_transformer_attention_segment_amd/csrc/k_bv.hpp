@@ -116,17 +116,20 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][D / 32], const F
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) s[kst] = mma<NS>(kf[kst][ks], qf[o][ks], s[kst]);
     }
+    // raw logits (the scale is positive, so the maximum is taken before it
+    // and the scale enters the exponent's fma: one VALU op less per key)
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = s[kst][r] * lscale2;
+        float v = s[kst][r];
         if constexpr (MASKED) v = valid[4 * kst + r] ? v : -INFINITY;
         x[4 * kst + r] = v;
         tmax = fmaxf(tmax, v);
       }
+    tmax *= lscale2;
     if (__builtin_amdgcn_ballot_w64(tmax > mrun[o] + RESCALE_LOG2) != 0) {
       const float mnew = fmaxf(mrun[o], max_g(tmax));
       const float alpha = fast_exp2(mrun[o] - mnew);
@@ -138,7 +141,7 @@ __device__ __forceinline__ void kv_compute(const Frag2 (&kf)[2][D / 32], const F
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(x[e] - mrun[o]);
+      p[e] = fast_exp2(fmaf(x[e], lscale2, -mrun[o]));  // a masked key: exp2(-inf) = 0
       lsum[o] += p[e];
     }
     const Frag2 pf = make_frag<NS>(p);
