@@ -637,7 +637,10 @@ def main():
                      "kernels_us": {k: round(1e3 * t / c, 2) for k, (t, c) in profi.items()}})
     weights = None if args.no_probs else time_probs(w, x, max(5, args.steps // 5), max(2, args.warmup // 2),
                                                     torch, nys)
-    module = None if args.no_module else time_module(w, max(5, args.steps // 5), max(2, args.warmup // 2), torch,
+    # the projection GEMM keeps the matrix cores busy and reaches its steady
+    # rate only after ~10 ms of such work (measured: 87 us per GEMM after 30
+    # calls, 70 us after 200), so the module gets 100 untimed warm-up calls
+    module = None if args.no_module else time_module(w, max(10, args.steps // 5), max(100, args.warmup * 10), torch,
                                                      nys, ms)
     backward = None
     if not args.no_backward:

@@ -156,10 +156,27 @@ __device__ __forceinline__ float wave_max(float v) {
 // from its own global address, land at lds_base + 16 l.  Completion is
 // tracked by the wave's vmcnt; other waves see the data after the issuing
 // wave has waited and all waves have passed a barrier.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Nontemporal (streaming) store, for results that no later kernel of the
+// call reads: such lines are not kept in L2 ahead of the operands that other
+// workgroups of the same launch still re-read from it.  T: a scalar or an
+// ext_vector_type vector.
+template <typename T>
+__device__ __forceinline__ void st_nt(void* p, T v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+// The same copy with the nontemporal (streaming) cache policy, for data read
+// for the last time.
+__device__ __forceinline__ void dma16_nt(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 2);
 }
 
 // Landmark row groups of the B V blocks (k_bv.hpp) for I/O elements of esize

@@ -236,7 +236,10 @@ __device__ __forceinline__ void dma_issue_tile(const u16* __restrict__ K, const 
     const int chunk = (lane & 7) ^ (row & 7);
     const long long src = (key0 + row) * st + 8 * chunk;
     __bf16* dst = lds + ((id < 4 ? 0 : DMA_NBUF) + buf) * DMA_TILE + 8 * (id & 3) * HD;
-    dma16((id < 4 ? K : V) + src, dst);
+    if (id < 4)
+      dma16_nt(K + src, dst);  // the call's last read of K
+    else
+      dma16(V + src, dst);  // V is read again by the output pass
   }
   if constexpr (MASK) {
     uint8_t* mb = reinterpret_cast<uint8_t*>(lds + 2 * DMA_NBUF * DMA_TILE) + 32 * buf;
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(256) void k_exact(ExactArgs a) {
     conv_tile<NS, false, D>(Vh, Vl, EXACT_VWLD, 16 * wave, tap, acc[0]);
   }
   if (tok < a.n)
-    store_row16<IO, false, D>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, acc[0]);
+    store_row16<IO, false, D, true>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, acc[0]);
 }
 
 }  // namespace nys

@@ -43,16 +43,20 @@ __device__ __forceinline__ int dmap_run(int dt, int a) {
 }
 
 // Store the lane's D / 4 output channels of one token row (B16 order only
-// for D = 64).
-template <typename IO, bool B16, int D = HD>
+// for D = 64); NT: nontemporal stores (final outputs nothing reads back).
+template <typename IO, bool B16, int D = HD, bool NT = false>
 __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[D / 16]) {
   static_assert(!B16 || D == 64, "the bf16 channel order is defined for d = 64");
   const int g = (threadIdx.x & 63) >> 4;
   if constexpr (sizeof(IO) == 4) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + dmap<B16>(dt, 4 * g)) =
-          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    for (int dt = 0; dt < D / 16; ++dt) {
+      float* const p = reinterpret_cast<float*>(row) + dmap<B16>(dt, 4 * g);
+      if constexpr (NT)
+        st_nt<f32x4>(p, acc[dt]);
+      else
+        *reinterpret_cast<float4*>(p) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    }
   } else if constexpr (B16) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -61,14 +65,22 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[D / 16])
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 2; ++r) w[2 * b + r] = pack_bf16x2(acc[2 * h + b][2 * r], acc[2 * h + b][2 * r + 1]);
-      *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(row) + 32 * h + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+      u16* const p = reinterpret_cast<u16*>(row) + 32 * h + 8 * g;
+      if constexpr (NT)
+        st_nt<u32x4>(p, u32x4{w[0], w[1], w[2], w[3]});
+      else
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const uint32_t w0 = pack_bf16x2(acc[dt][0], acc[dt][1]);
       const uint32_t w1 = pack_bf16x2(acc[dt][2], acc[dt][3]);
-      *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(row) + 16 * dt + 4 * g) = make_uint2(w0, w1);
+      u16* const p = reinterpret_cast<u16*>(row) + 16 * dt + 4 * g;
+      if constexpr (NT)
+        st_nt<u32x2>(p, u32x2{w0, w1});
+      else
+        *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
     }
   }
 }

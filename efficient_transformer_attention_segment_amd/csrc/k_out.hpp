@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_out(OutArgs a) {
     }
     if (a.conv_w != nullptr) conv_tile<NS, false, D>(vh, vl, Ly::VWLD, ts - t0, tap, oacc);
     if (tok < a.n)
-      store_row16<IO, false, D>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, oacc);
+      store_row16<IO, false, D, true>(reinterpret_cast<IO*>(a.out) + a.out_s.base(bh, a.H) + tok * a.out_s.t, oacc);
   }
 }
 
@@ -354,11 +354,13 @@ __device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int t0, const
   }
 }
 
+// Q rows are read here for the last time in the call: streaming loads, so
+// they do not displace what this pass and the call still re-read (V, W, Kt).
 __device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int tok, bf16x8 (&qf)[2]) {
   const int g = (threadIdx.x & 63) >> 4;
   const u16* row = Q + min(tok, n - 1) * st + 8 * g;
-  qf[0] = *reinterpret_cast<const bf16x8*>(row);
-  qf[1] = *reinterpret_cast<const bf16x8*>(row + 32);
+  qf[0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row));
+  qf[1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 32));
 }
 
 // grid (blocks per head, B H), 256 threads; workgroup x covers tokens
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(64 * NW) void k_out_stream(OutArgs a, int R, u16* j
     }
     if constexpr (CONV) conv_tile_ring<NW>(ring, t0, cl, tap, oacc);
     u16* dst = ts + c16 < te ? O + (ts + c16) * ot : junk + c16 * HD;
-    store_row16<u16, true>(dst, oacc);
+    store_row16<u16, true, HD, true>(dst, oacc);
   };
   int u = 0;
   for (; u + 1 < nunits; u += 2) {
