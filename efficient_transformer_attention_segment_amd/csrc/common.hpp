@@ -286,4 +286,18 @@ __device__ __forceinline__ Frag2 make_frag(const float* x) {
   }
 }
 
+// Where the module's bf16 projection writes the landmarks it forms in its
+// epilogue (k_qkv.hpp), in the landmark pass's layout.
+struct QkvLandmarks {
+  float* qt;  // [B H][m][64] float32
+  float* kt;
+  __bf16* qt_hi;  // [B H][m][64] bf16 split of qt / kt
+  __bf16* qt_lo;
+  __bf16* kt_hi;
+  __bf16* kt_lo;
+  unsigned long long* slots;  // [B H][2]: cleared
+  int n, H, m, L;             // tokens per sequence, heads, landmarks, segment length (divides 64)
+  float scale;                // d^-1/4 / L
+};
+
 }  // namespace nys

@@ -3,7 +3,8 @@
 // which instantiates dispatch_m for its (I/O type, head size) pairs.
 //
 // Launch sequence for one Nystrom call (all on the caller's stream):
-//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo)
+//   1 k_landmark   landmarks Qt, Kt (+ bf16 hi/lo); skipped when the
+//                  module's projection has formed them (k_qkv.hpp)
 //   2 k_gram       per head A = softmax(Qt Kt^T), its max column / row sum;
 //                  only when the pseudo-inverse blocks cannot form A
 //                  themselves (m > 128, or the original init with more
@@ -64,8 +65,9 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   la.colmax = at<float>(w, p.off_colmax);
   la.rowmax = at<float>(w, p.off_rowmax);
   la.slots = at<unsigned long long>(w, p.off_slots);
-  HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
-                 (const IO*)k, la));
+  if (!p.landmarks_ready)  // else the module's projection formed them in its epilogue
+    HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
+                   (const IO*)k, la));
   size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
   lds2 = std::max<size_t>(lds2, bv_fold_bytes<bv_rows<IO, M, D>(), D>());
   if constexpr (M <= 128)
@@ -253,6 +255,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   OutArgs oa;
   oa.q = q;
   oa.v = v;
+  oa.q_stream = p.inputs_fresh ? 0 : 1;
   oa.zero = at<__bf16>(w, p.off_zero);
   oa.conv_w = conv_w;
   oa.conv_k = conv_k;

@@ -44,6 +44,8 @@ struct Plan {
   Strides si, so;  // element strides of q, k, v and of out
   void* probs;     // attention weights [B, H, n, mr] on request, else null
   bool bwd;        // forward stages for the backward pass: stop after W, keep B's normalisers
+  bool landmarks_ready = false;  // Qt, Kt (+ hi/lo) and the meeting slots already written (module fold)
+  bool inputs_fresh = false;     // q, k, v written just before the call (the module's projection)
   size_t off_qt, off_kt, off_qth, off_qtl, off_kth, off_ktl, off_A, off_Z, off_colmax, off_rowmax, off_cscale;
   size_t off_pmax, off_psum, off_pacc, off_BV, off_W, off_wfh, off_wfl, off_X, off_T1, off_T2, off_Z2, off_zero;
   size_t off_slots, off_junk, off_lse;
@@ -183,10 +185,11 @@ int launch_exact(int B, int H, int n, Strides si, Strides so, const void* q, con
                  const uint8_t* mask, const float* conv_w, int conv_k, void* out, void* probs, hipStream_t st);
 
 // The module's projection y = x W^T + b, [rows][cols] from x [rows][hidden]
-// and W [cols][hidden] (module.hip).
+// and W [cols][hidden] (module.hip); with lm != null (bf16 only) it also
+// forms the landmarks in its epilogue.
 template <typename IO>
 int qkv_projection(const void* x, const void* w, const void* bias, int rows, int hidden, int cols, void* y,
-                   hipStream_t st);
+                   hipStream_t st, const QkvLandmarks* lm = nullptr);
 
 // The backward pass (bwd_*.hip).
 template <typename IO>

@@ -42,6 +42,7 @@ struct OutArgs {
   int mr;                // landmarks of the method (M = mr rounded up to 32)
   float lscale;          // d^-1/4
   Strides in, out_s;     // of q and v, and of out
+  int q_stream;          // bf16 output pass: read Q with streaming loads (0 when Q was just written)
 };
 
 // Logits of padding landmarks (16 it + 4g + r >= mr) -> -inf, in S^T tiles.
@@ -363,13 +364,20 @@ __device__ __forceinline__ void conv_tile_ring(const __bf16* ring, int t0, const
   }
 }
 
-// Q rows are read here for the last time in the call: streaming loads, so
-// they do not displace what this pass and the call still re-read (V, W, Kt).
-__device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int tok, bf16x8 (&qf)[2]) {
+// Q rows are read here for the last time in the call: streaming loads
+// (stream != 0), so they do not displace what this pass and the call still
+// re-read (V, W, Kt).  The module's q, written by its projection just
+// before, is read with ordinary loads.
+__device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int tok, bf16x8 (&qf)[2], int stream) {
   const int g = (threadIdx.x & 63) >> 4;
   const u16* row = Q + min(tok, n - 1) * st + 8 * g;
-  qf[0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row));
-  qf[1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 32));
+  if (stream) {
+    qf[0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row));
+    qf[1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(row + 32));
+  } else {
+    qf[0] = *reinterpret_cast<const bf16x8*>(row);
+    qf[1] = *reinterpret_cast<const bf16x8*>(row + 32);
+  }
 }
 
 // grid (blocks per head, B H), 256 threads; workgroup x covers tokens
@@ -434,8 +442,8 @@ __global__ __launch_bounds__(64 * NW) void k_out_stream(OutArgs a, int R, u16* j
     conv_lane_init(cl);
   }
   bf16x8 qb[2][2];
-  load_q16(Q, st, a.n, tb + 16 * wave + c16, qb[0]);
-  if (nunits > 1) load_q16(Q, st, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1]);
+  load_q16(Q, st, a.n, tb + 16 * wave + c16, qb[0], a.q_stream);
+  if (nunits > 1) load_q16(Q, st, a.n, tb + OUTS_UNIT + 16 * wave + c16, qb[1], a.q_stream);
   Frag2 tap[3];
   if constexpr (CONV) conv_taps(a.conv_w + (size_t)h * a.conv_k, a.conv_k, tap);
   wait_vmcnt<0>();  // the landmark / fragment copies (the register loads are tracked by the compiler)
@@ -463,7 +471,7 @@ __global__ __launch_bounds__(64 * NW) void k_out_stream(OutArgs a, int R, u16* j
         sacc[it] = mfma(kf, q[ks], sacc[it]);
       }
     }
-    if (u + 2 < nunits) load_q16(Q, st, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q);  // unit u + 2
+    if (u + 2 < nunits) load_q16(Q, st, a.n, t0 + 2 * OUTS_UNIT + 16 * wave + c16, q, a.q_stream);  // unit u + 2
     if constexpr (PAD) pad_mask_rows(sacc, a.mr);
     float mx = -INFINITY;
 #pragma unroll

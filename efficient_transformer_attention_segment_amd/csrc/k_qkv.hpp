@@ -26,12 +26,26 @@
 
 namespace nys {
 
+// Landmarks formed in the bf16 projection's epilogue (section 2.3 of the
+// same page: each landmark is the mean of n / m contiguous scaled q or k
+// rows).  Used when d = 64, the landmark count is a multiple of 32 and the
+// segment length L = n / m divides 64: every wave's 64 output rows then hold
+// whole segments of one sequence, and its 64 output columns are one head's
+// q, k or v channels.  The wave sums, per segment, the bf16 values it
+// stores (what the landmark pass would read back) in float32, scales by
+// d^-1/4 / L and writes the landmark rows as the landmark pass does (float32
+// and the bf16 hi/lo split); workgroup 0 also clears the meeting slots.
+// (QkvLandmarks, the landmark targets, is declared in common.hpp for the
+// host side too.)
+
 struct QkvArgs {
   const void* x;     // [rows][K]
   const void* w;     // [N][K]
   const void* bias;  // [N] or null
   void* y;           // [rows][N]
   int rows, N, K;
+  int fold;          // bf16 only: form the landmarks (lm) in the epilogue
+  QkvLandmarks lm;
 };
 
 constexpr int QB_BM = 128, QB_BN = 128, QB_BK = 64, QB_NT = 256;
@@ -62,6 +76,69 @@ __device__ __forceinline__ int qswz(int row, int chunk) {
     return row * QB_BK + 8 * (chunk ^ (row & 15));  // 256-byte rows: 16 positions per row
   else
     return row * QB_BK + 8 * (chunk ^ ((row >> 1) & 7));
+}
+
+// Sum of v over aligned groups of G lanes within each 16-lane row (G = 1,
+// 2, 4, 8 or 16; every lane of a group gets the group's sum).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<DPP_QUAD_1032>(v);
+  if constexpr (G >= 4) v += dpp<DPP_QUAD_2301>(v);
+  if constexpr (G >= 8) v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  if constexpr (G >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+// The landmark rows of one wave's 64 x 64 output block (rows r0 .. r0 + 63,
+// columns c0 .. c0 + 63) from its stored bf16 values yv[j][i] (lane: row
+// r0 + 16 i + lane % 16, columns c0 + 16 j + 4 (lane / 16) + 0..3).  L:
+// segment length (divides 64).  Segments of L rows: for L >= 16 the sum over
+// L / 16 row tiles in registers, then over the 16 lanes of a row; for
+// L < 16 over groups of L lanes.  Fixed order, so deterministic.
+template <int L>
+__device__ __forceinline__ void qkv_landmarks(const QkvLandmarks& lm, const uint2 (&yv)[4][4], int r0, int c0,
+                                              int rows, int N) {
+  const int hd = lm.H * HD;
+  if (c0 >= N || r0 >= rows) return;
+  const int which = c0 / hd;  // 0: q, 1: k, 2: v (no landmarks)
+  if (which >= 2) return;
+  const int h = (c0 - which * hd) / HD;
+  const int b = r0 / lm.n, t0 = r0 - b * lm.n;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  float* const dst = which == 0 ? lm.qt : lm.kt;
+  __bf16* const dhi = which == 0 ? lm.qt_hi : lm.kt_hi;
+  __bf16* const dlo = which == 0 ? lm.qt_lo : lm.kt_lo;
+  const size_t head = (size_t)(b * lm.H + h) * lm.m;
+  constexpr int TI = L >= 16 ? L / 16 : 1;  // row tiles per segment
+  constexpr int GL = L >= 16 ? 16 : L;      // lanes per segment within a row tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i0 = 0; i0 < 4; i0 += TI) {
+      float sv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = i0; i < i0 + TI; ++i) {
+        sv[0] += bf16u_to_f32(yv[j][i].x & 0xffffu);
+        sv[1] += bf16u_to_f32(yv[j][i].x >> 16);
+        sv[2] += bf16u_to_f32(yv[j][i].y & 0xffffu);
+        sv[3] += bf16u_to_f32(yv[j][i].y >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = group_sum<GL>(sv[e]) * lm.scale;
+      if (c16 % GL == 0) {
+        const int l = (t0 + 16 * i0 + c16) / L;  // landmark
+        const size_t o = (head + l) * HD + 16 * j + 4 * g;
+        *reinterpret_cast<float4*>(dst + o) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        __bf16 hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split1(sv[e], hi[e], lo[e]);
+        *reinterpret_cast<uint2*>(dhi + o) = make_uint2(__builtin_bit_cast(uint32_t, bf16x2{hi[0], hi[1]}),
+                                                        __builtin_bit_cast(uint32_t, bf16x2{hi[2], hi[3]}));
+        *reinterpret_cast<uint2*>(dlo + o) = make_uint2(__builtin_bit_cast(uint32_t, bf16x2{lo[0], lo[1]}),
+                                                        __builtin_bit_cast(uint32_t, bf16x2{lo[2], lo[3]}));
+      }
+    }
+  }
 }
 
 // grid qkv_grid(rows, N, QB_BM, QB_BN), QB_NT threads (waves of 64 x 64,
@@ -114,6 +191,16 @@ __global__ __launch_bounds__(QB_NT) void k_qkv_bf16(QkvArgs a) {
       *reinterpret_cast<uint4*>(Bt + qswz(idx / (QB_BK / 8), idx % (QB_BK / 8))) = rb[u];
     }
   };
+  // the bias of the lane's output columns, loaded here so that it arrives
+  // during the contraction (loaded in the epilogue, each load's round trip
+  // would end the tile)
+  const u16* const bias = static_cast<const u16*>(a.bias);
+  uint2 bq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 64 * wn + 16 * j + 4 * g;
+    bq[j] = (bias != nullptr && n < a.N) ? *reinterpret_cast<const uint2*>(bias + n) : make_uint2(0u, 0u);
+  }
   f32x4 acc[4][4];  // [n subtile j][m subtile i]: y^T tiles
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -147,27 +234,33 @@ __global__ __launch_bounds__(QB_NT) void k_qkv_bf16(QkvArgs a) {
 
   // lane holds y[m][n .. n + 3] with m = m0 + 64 wm + 16 i + c16 and
   // n = n0 + 64 wn + 16 j + 4 g
-  const u16* const bias = static_cast<const u16*>(a.bias);
   u16* const Y = static_cast<u16*>(a.y);
+  uint2 yv[4][4];  // [j][i]: the stored bf16 values (kept for the landmarks)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + 64 * wn + 16 * j + 4 * g;
-    if (n >= a.N) continue;  // N is a multiple of 4 (16-byte rows of 3 H d)
-    float b4[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr) {
-      const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
-      b4[0] = bf16u_to_f32(bw.x & 0xffffu);
-      b4[1] = bf16u_to_f32(bw.x >> 16);
-      b4[2] = bf16u_to_f32(bw.y & 0xffffu);
-      b4[3] = bf16u_to_f32(bw.y >> 16);
-    }
+    const float b4[4] = {bf16u_to_f32(bq[j].x & 0xffffu), bf16u_to_f32(bq[j].x >> 16),
+                         bf16u_to_f32(bq[j].y & 0xffffu), bf16u_to_f32(bq[j].y >> 16)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 64 * wm + 16 * i + c16;
-      if (m >= a.rows) continue;
       const f32x4 v = acc[j][i];
-      *reinterpret_cast<uint2*>(Y + (size_t)m * a.N + n) =
-          make_uint2(pack_bf16x2(v[0] + b4[0], v[1] + b4[1]), pack_bf16x2(v[2] + b4[2], v[3] + b4[3]));
+      yv[j][i] = make_uint2(pack_bf16x2(v[0] + b4[0], v[1] + b4[1]), pack_bf16x2(v[2] + b4[2], v[3] + b4[3]));
+      const int m = m0 + 64 * wm + 16 * i + c16;
+      if (n < a.N && m < a.rows)  // N is a multiple of 4 (16-byte rows of 3 H d)
+        *reinterpret_cast<uint2*>(Y + (size_t)m * a.N + n) = yv[j][i];
+    }
+  }
+  if (a.fold) {
+    if (blockIdx.x == 0)
+      for (int t = threadIdx.x; t < 2 * a.lm.H * (a.rows / a.lm.n); t += QB_NT) a.lm.slots[t] = 0ull;
+    switch (a.lm.L) {
+      case 2: qkv_landmarks<2>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      case 4: qkv_landmarks<4>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      case 8: qkv_landmarks<8>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      case 16: qkv_landmarks<16>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      case 32: qkv_landmarks<32>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      case 64: qkv_landmarks<64>(a.lm, yv, m0 + 64 * wm, n0 + 64 * wn, a.rows, a.N); break;
+      default: break;
     }
   }
 }
@@ -188,6 +281,13 @@ __global__ __launch_bounds__(256) void k_qkv_f32(QkvArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const float* X = static_cast<const float*>(a.x);
   const float* Wt = static_cast<const float*>(a.w);
+  const float* const bias = static_cast<const float*>(a.bias);
+  float4 bq[2];  // the lane's bias, loaded before the contraction
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 32 * wn + 16 * j + 4 * g;
+    bq[j] = (bias != nullptr && n < a.N) ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   f32x4 acc[2][2];  // [n subtile][m subtile]: y^T tiles
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -227,13 +327,12 @@ __global__ __launch_bounds__(256) void k_qkv_f32(QkvArgs a) {
         for (int i = 0; i < 2; ++i) acc[j][i] = mfma_f32(bv[j], av[i], acc[j][i]);
     }
   }
-  const float* const bias = static_cast<const float*>(a.bias);
   float* const Y = static_cast<float*>(a.y);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + 32 * wn + 16 * j + 4 * g;
     if (n >= a.N) continue;
-    const float4 b4 = bias != nullptr ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b4 = bq[j];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int m = m0 + 32 * wm + 16 * i + c16;

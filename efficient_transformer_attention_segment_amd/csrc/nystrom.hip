@@ -3,6 +3,7 @@
 // include/nystrom.h.  The launch sequences live in the kernel translation
 // units (fwd_*.hip, exact.hip, bwd_*.hip; see host.hpp).
 #include <cmath>
+#include <functional>
 #include <tuple>
 
 #include "host.hpp"
@@ -267,7 +268,8 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
         Strides so, int B,
         int H, int n,
         int d, int m, int n_iter, int init_option, void* out, hipStream_t st, Workspace** wout, Plan* pout,
-        void* probs = nullptr, Workspace* fixed = nullptr) {
+        void* probs = nullptr, Workspace* fixed = nullptr,
+        const std::function<int(Plan&, Workspace*)>* pre = nullptr) {
   int rc = check_call(sizeof(IO), q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, probs);
   if (rc != NYS_OK) return rc;
   if (fixed != nullptr && m != n) {
@@ -291,6 +293,10 @@ int run(const void* q, const void* k, const void* v, Strides si, const uint8_t* 
   Workspace* w = fixed;
   if (w == nullptr) {
     rc = get_workspace(st, p.total, &w);
+    if (rc != NYS_OK) return rc;
+  }
+  if (pre != nullptr) {  // launches that write into the workspace first (the module's projection)
+    rc = (*pre)(p, w);
     if (rc != NYS_OK) return rc;
   }
   rc = d == 32    ? dispatch_m<IO, 32>(p.m, p, w, q, k, v, mask, conv_w, conv_k, n_iter, init_option, out, st)
@@ -379,10 +385,34 @@ int run_module(const void* x, const void* w, const void* b, const uint8_t* mask,
   const IO* const v = q + 2 * (size_t)H * d;
   int rc = check_call(e, q, k, v, si, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, nullptr);
   if (rc != NYS_OK) return rc;
-  rc = qkv_projection<IO>(x, w, b, (int)rows, hidden, (int)cols, qkv, st);
-  if (rc != NYS_OK) return rc;
+  // bf16, d = 64, landmarks a multiple of 32 and segments of L = n / m
+  // tokens with L dividing 64: the projection forms the landmarks in its
+  // epilogue (every 64-row output block holds whole segments of one
+  // sequence) and the landmark pass is skipped
+  const int L = n / m;
+  const bool fold = sizeof(IO) == 2 && d == HD && m != n && m % 32 == 0 && L >= 2 && 64 % L == 0;
+  if (m == n) {  // the exact branch takes no workspace
+    rc = qkv_projection<IO>(x, w, b, (int)rows, hidden, (int)cols, qkv, st);
+    if (rc != NYS_OK) return rc;
+    return run<IO>(q, k, v, si, mask, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, st, nullptr,
+                   nullptr);
+  }
+  // the projection runs once the workspace is known: the attention then
+  // knows that q, k, v were just written (and where the landmarks are)
+  const std::function<int(Plan&, Workspace*)> pre = [&](Plan& p, Workspace* ws) {
+    const float s4 = 1.0f / sqrtf(sqrtf((float)HD));
+    const QkvLandmarks lm{at<float>(ws, p.off_qt),  at<float>(ws, p.off_kt),  at<__bf16>(ws, p.off_qth),
+                          at<__bf16>(ws, p.off_qtl), at<__bf16>(ws, p.off_kth), at<__bf16>(ws, p.off_ktl),
+                          at<unsigned long long>(ws, p.off_slots), n, H, p.m, p.L, s4 / (float)p.L};
+    const int r = qkv_projection<IO>(x, w, b, (int)rows, hidden, (int)cols, qkv, st, fold ? &lm : nullptr);
+    if (r == NYS_OK) {
+      p.landmarks_ready = fold;
+      p.inputs_fresh = true;
+    }
+    return r;
+  };
   return run<IO>(q, k, v, si, mask, conv_w, conv_k, so, B, H, n, d, m, n_iter, init_option, out, st, nullptr,
-                 nullptr);
+                 nullptr, nullptr, nullptr, &pre);
 }
 
 }  // namespace host
