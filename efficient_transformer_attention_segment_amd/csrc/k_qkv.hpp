@@ -16,8 +16,9 @@
 //   LDS-only barriers, so those loads stay in flight across them.  Each
 //   wave forms the transposed tile, y^T = W x^T, on v_mfma_f32_16x16x32_bf16,
 //   so a lane holds 4 consecutive output columns of one row: the bias is
-//   added in float32 and 4 bf16 values are stored at once.  Every XCD walks
-//   its own row tiles first for each column tile (qkv_tile).
+//   added in float32, and the wave's 64 x 64 bf16 block is staged in LDS and
+//   stored as whole 128-byte rows (16 bytes per lane).  Every XCD walks its
+//   own row tiles first for each column tile (qkv_tile).
 // k_qkv_f32: float32 I/O on the float32 matrix core (v_mfma_f32_16x16x4f32),
 //   64 x 64 tiles, register-staged float32 LDS tiles, for float32 accuracy.
 #pragma once
@@ -50,7 +51,13 @@ struct QkvArgs {
 
 constexpr int QB_BM = 128, QB_BN = 128, QB_BK = 64, QB_NT = 256;
 constexpr int QB_ATILE = QB_BM * QB_BK, QB_BTILE = QB_BN * QB_BK;  // bf16 elements
-constexpr int QB_LDS = (QB_ATILE + QB_BTILE) * 2;  // bytes: one stage
+// output staging after the contraction: each wave's 64 x 64 bf16 block with
+// row stride QB_SLD (144 bytes, so the 16 rows of a fragment store start on
+// distinct banks), in LDS past nothing the tiles still need
+constexpr int QB_SLD = 72;
+constexpr int QB_LDS_TILES = (QB_ATILE + QB_BTILE) * 2;  // bytes: one stage
+constexpr int QB_LDS_OUT = (QB_NT / 64) * 64 * QB_SLD * 2;
+constexpr int QB_LDS = QB_LDS_TILES > QB_LDS_OUT ? QB_LDS_TILES : QB_LDS_OUT;
 
 // Tiles (tm, tn) of a launch: linear index L runs on XCD L % 8; XCD x takes
 // the row tiles x, x + 8, ... and walks them first for each column tile, so
@@ -235,19 +242,36 @@ __global__ __launch_bounds__(QB_NT) void k_qkv_bf16(QkvArgs a) {
   // lane holds y[m][n .. n + 3] with m = m0 + 64 wm + 16 i + c16 and
   // n = n0 + 64 wn + 16 j + 4 g
   u16* const Y = static_cast<u16*>(a.y);
+  // the wave's block goes through LDS (every wave is past the last read of
+  // the tile stage) so that the stores below write whole 128-byte rows: with
+  // 8-byte pieces of rows (4 stores per line) the output stream evicts the x
+  // and W panels that later tiles re-read from L2
+  u16* const stg = reinterpret_cast<u16*>(qb_lds) + wave * (64 * QB_SLD);
   uint2 yv[4][4];  // [j][i]: the stored bf16 values (kept for the landmarks)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 64 * wn + 16 * j + 4 * g;
     const float b4[4] = {bf16u_to_f32(bq[j].x & 0xffffu), bf16u_to_f32(bq[j].x >> 16),
                          bf16u_to_f32(bq[j].y & 0xffffu), bf16u_to_f32(bq[j].y >> 16)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 v = acc[j][i];
       yv[j][i] = make_uint2(pack_bf16x2(v[0] + b4[0], v[1] + b4[1]), pack_bf16x2(v[2] + b4[2], v[3] + b4[3]));
-      const int m = m0 + 64 * wm + 16 * i + c16;
-      if (n < a.N && m < a.rows)  // N is a multiple of 4 (16-byte rows of 3 H d)
-        *reinterpret_cast<uint2*>(Y + (size_t)m * a.N + n) = yv[j][i];
+      *reinterpret_cast<uint2*>(stg + (16 * i + c16) * QB_SLD + 16 * j + 4 * g) = yv[j][i];
+    }
+  }
+  wait_lgkm0();
+  // lane l: row l / 8 + 8 s of the block, 16 bytes at column 8 (l % 8)
+#pragma unroll
+  for (int sidx = 0; sidx < 8; ++sidx) {
+    const int r = lane / 8 + 8 * sidx, c8 = lane % 8;
+    const uint4 val = *reinterpret_cast<const uint4*>(stg + r * QB_SLD + 8 * c8);
+    const int m = m0 + 64 * wm + r, n = n0 + 64 * wn + 8 * c8;
+    if (m < a.rows) {
+      u16* const dst = Y + (size_t)m * a.N + n;
+      if (n + 8 <= a.N)
+        *reinterpret_cast<uint4*>(dst) = val;
+      else if (n < a.N)  // N is a multiple of 4 (16-byte rows of 3 H d)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
     }
   }
   if (a.fold) {
