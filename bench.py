@@ -638,9 +638,10 @@ def main():
     weights = None if args.no_probs else time_probs(w, x, max(5, args.steps // 5), max(2, args.warmup // 2),
                                                     torch, nys)
     # the projection GEMM keeps the matrix cores busy and reaches its steady
-    # rate only after ~10 ms of such work (measured: 87 us per GEMM after 30
-    # calls, 70 us after 200), so the module gets 100 untimed warm-up calls
-    module = None if args.no_module else time_module(w, max(10, args.steps // 5), max(100, args.warmup * 10), torch,
+    # rate only after tens of milliseconds of such work (measured: 87 us per
+    # GEMM after 30 calls, 70 us after 200), so the module gets 200 untimed
+    # warm-up calls and 50 timed ones (about 30 ms in all)
+    module = None if args.no_module else time_module(w, max(50, args.steps), max(200, args.warmup * 20), torch,
                                                      nys, ms)
     backward = None
     if not args.no_backward:
