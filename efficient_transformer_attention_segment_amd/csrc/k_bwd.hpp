@@ -143,6 +143,14 @@ __device__ __forceinline__ void io_put(IO* p, float x) {
   else
     *reinterpret_cast<u16*>(p) = f32_to_bf16u(x);
 }
+// Four consecutive elements (16-byte aligned for float32, 8-byte for bf16).
+template <typename IO>
+__device__ __forceinline__ void io_put4(IO* p, const f32x4 x) {
+  if constexpr (sizeof(IO) == 4)
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  else
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+}
 
 // ---------------------------------------------------------------------------
 template <int M, int D>
@@ -1681,10 +1689,11 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
   const int nsteps = (k1 - k0c + 31) / 32;
   RowBuf<IO, D / 2> bk, bv;
   // per step, also the lane's mask bits, conv part of dv and dKt[segment]
-  // elements (C layout: key 16 kt + 4g + r, channel 16 ct + c16), fetched a
-  // step ahead with the k and v rows
+  // elements (transposed C layout: key 16 kt + lane % 16, channels 16 ct +
+  // 4g .. + 3, one 16-byte load each), fetched a step ahead with the k and v
+  // rows
   bool pkeep[2];
-  float pdvc[2][4][CT], pdkt[2][4][CT];
+  float4 pdvc[2][CT], pdkt[2][CT];
   auto fetch = [&](int step) {
     const int ks = k0c + 32 * step;
     {
@@ -1697,18 +1706,16 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = ks + 16 * kt + c16;
-      pkeep[kt] = key < k1 && (mask == nullptr || mask[key] != 0);
+      const bool ok = key < k1;
+      pkeep[kt] = ok && (mask == nullptr || mask[key] != 0);
+      const int seg = (ok ? key : k0c) / a.L;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = ks + 16 * kt + 4 * g + r;
-        const bool ok = kr < k1;
-        const int seg = (ok ? kr : k0c) / a.L;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int ch = 16 * ct + c16;
-          pdvc[kt][r][ct] = (ok && a.dvc != nullptr) ? a.dvc[((size_t)bh * a.n + kr) * D + ch] : 0.f;
-          pdkt[kt][r][ct] = dKt[(size_t)seg * D + ch];
-        }
+      for (int ct = 0; ct < CT; ++ct) {
+        const int ch = 16 * ct + 4 * g;
+        pdvc[kt][ct] = (ok && a.dvc != nullptr)
+                           ? *reinterpret_cast<const float4*>(a.dvc + ((size_t)bh * a.n + key) * D + ch)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        pdkt[kt][ct] = *reinterpret_cast<const float4*>(dKt + (size_t)seg * D + ch);
       }
     }
   };
@@ -1727,17 +1734,15 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
     bv.store(Vp + sr * KLD + sc, Vp + 32 * KLD + sr * KLD + sc);
     // this step's prefetched values, then the next step's fetch
     bool keep[2];
-    float cdvc[2][4][CT], cdkt[2][4][CT];
+    float4 cdvc[2][CT], cdkt[2][CT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       keep[kt] = pkeep[kt];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          cdvc[kt][r][ct] = pdvc[kt][r][ct];
-          cdkt[kt][r][ct] = pdkt[kt][r][ct];
-        }
+      for (int ct = 0; ct < CT; ++ct) {
+        cdvc[kt][ct] = pdvc[kt][ct];
+        cdkt[kt][ct] = pdkt[kt][ct];
+      }
     }
     if (step + 4 < nsteps) fetch(step + 4);
     // S = Qt k^T (Qt carries d^-1/4; k gets it here) and dB = dBV v^T
@@ -1783,8 +1788,10 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
         }
       }
     }
-    // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[segment] / L):
-    // C(key 16 kt + 4g + r, channel 16 ct + c16), landmarks in the paired k order
+    // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[segment] / L),
+    // formed transposed: C^T(channel 16 ct + 4g + r, key 16 kt + lane % 16),
+    // landmarks in the paired k order (B and dS, from registers, as the B
+    // operand), so a lane stores 4 consecutive channels of one key
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x4 cv[CT], ck[CT];
@@ -1805,20 +1812,23 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
           dbv.lo = tr_frag(Bl, KLD, i0, i1, 16 * ct);
           qt.hi = tr_frag(Qh, KLD, i0, i1, 16 * ct);
           qt.lo = tr_frag(Ql, KLD, i0, i1, 16 * ct);
-          cv[ct] = mma<3>(ba, dbv, cv[ct]);
-          ck[ct] = mma<3>(sa, qt, ck[ct]);
+          cv[ct] = mma<3>(dbv, ba, cv[ct]);
+          ck[ct] = mma<3>(qt, sa, ck[ct]);
         }
       }
+      const int key = ks0 + 16 * kt + c16;
+      if (key < k1) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = ks0 + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
-          if (key >= k1) continue;
-          const size_t o = ((size_t)bh * a.n + key) * D + ch;
-          io_put(reinterpret_cast<IO*>(a.dv) + o, cv[ct][r] + cdvc[kt][r][ct]);
-          io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * (ck[ct][r] + cdkt[kt][r][ct] * inv_l));
+        for (int ct = 0; ct < CT; ++ct) {
+          const size_t o = ((size_t)bh * a.n + key) * D + 16 * ct + 4 * g;
+          const float4 dc = cdvc[kt][ct], kc = cdkt[kt][ct];
+          io_put4(reinterpret_cast<IO*>(a.dv) + o,
+                  f32x4{cv[ct][0] + dc.x, cv[ct][1] + dc.y, cv[ct][2] + dc.z, cv[ct][3] + dc.w});
+          io_put4(reinterpret_cast<IO*>(a.dk) + o,
+                  f32x4{a.s4 * (ck[ct][0] + kc.x * inv_l), a.s4 * (ck[ct][1] + kc.y * inv_l),
+                        a.s4 * (ck[ct][2] + kc.z * inv_l), a.s4 * (ck[ct][3] + kc.w * inv_l)});
         }
+      }
     }
     // dQt += dS k (times d^-1/4 at the end): dS^T (hi, lo) into the wave's
     // tile [key][landmark], A by transposed reads (k = key, 8g + e)
