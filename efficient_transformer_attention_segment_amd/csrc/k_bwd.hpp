@@ -356,7 +356,8 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 //   runs over tokens in the paired k order, which is exactly what the two
 //   tiles' C registers hold, so F and dS enter as A operands straight from
 //   registers and dout, q as B operands by transposed LDS reads;
-//   dQs = dS Kt: dS^T goes to the wave's LDS tile, A by transposed reads.
+//   dQs = dS Kt: dS^T goes to the wave's LDS tile, read back transposed;
+//   the product is formed as dQs^T, so a lane stores 4 channels of a token.
 // dW and dKt stay in registers over all of a wave's steps; at the end the
 // four waves' sums are added in wave order and written as the chunk's
 // partials.  No workgroup barrier inside the token loop.
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void k_bwd_tok2(BwdArgs a) {
         }
       }
     }
-    // dQs = dS Kt: dS^T (hi, lo) into the wave's tile, then A by transposed reads
+    // dQs = dS Kt: dS^T (hi, lo) into the wave's tile, then read back by transposed reads
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -598,6 +599,8 @@ __global__ __launch_bounds__(256) void k_bwd_tok2(BwdArgs a) {
         *reinterpret_cast<bf16x4*>(Sh + o) = h;
         *reinterpret_cast<bf16x4*>(Sl + o) = l;
       }
+    // formed transposed, C^T(channel 16 ct + 4g + r, token 16 rt + lane % 16),
+    // so a lane stores 4 consecutive channels of one token at once
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -611,13 +614,12 @@ __global__ __launch_bounds__(256) void k_bwd_tok2(BwdArgs a) {
           sa.lo = tr_frag(Sl, SLD, k0, k0 + 4, 16 * rt);
           kb.hi = tr_frag(Kh, KLD, k0, k0 + 4, 16 * ct);
           kb.lo = tr_frag(Kl, KLD, k0, k0 + 4, 16 * ct);
-          c = mma<3>(sa, kb, c);
+          c = mma<3>(kb, sa, c);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = ts + 16 * rt + 4 * g + r;
-          if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * D + 16 * ct + c16] = c[r];
-        }
+        const int tok = ts + 16 * rt + c16;
+        if (tok < t1)
+          *reinterpret_cast<float4*>(a.dqf + ((size_t)bh * a.n + tok) * D + 16 * ct + 4 * g) =
+              make_float4(c[0], c[1], c[2], c[3]);
       }
   }
 
