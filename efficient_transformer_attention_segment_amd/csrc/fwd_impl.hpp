@@ -318,7 +318,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     pr.lscale = s4;
     pr.in = p.si;
     using PL = ProbsLayout<IO, M, D>;
-    const int ntb = (p.n + PROBS_TOK - 1) / PROBS_TOK;
+    pr.grp = probs_groups(p.n, p.BH, PL::NCB);
+    const int ntb = (p.n + PROBS_TOK * pr.grp - 1) / (PROBS_TOK * pr.grp);
     const dim3 grid(((ntb + 7) / 8) * 8 * PL::NCB, p.BH);
     auto launch_probs = [&](auto kern) -> int {
       HIP_TRY(allow_lds(kern, PL::LDS_BYTES));

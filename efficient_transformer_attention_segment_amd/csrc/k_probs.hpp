@@ -23,6 +23,8 @@
 // no kept key is all zeros.
 #pragma once
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "k_out.hpp"
 
@@ -39,11 +41,22 @@ struct ProbsArgs {
   int n, H;
   int mr;                   // columns written: landmarks of the method (n when exact)
   int ldp;                  // row length of probs
+  int grp;                  // token groups of PROBS_TOK per workgroup (Nystrom path)
   float lscale;             // logit factor (d^-1/4 against Kt, d^-1/2 exact)
   Strides in;
 };
 
-constexpr int PROBS_TOK = 128;  // tokens per workgroup (4 waves x 2 tiles)
+constexpr int PROBS_TOK = 128;  // tokens per group (4 waves x 2 tiles)
+constexpr int PROBS_GRP_MAX = 8;  // token groups per workgroup at most
+
+// Token groups per workgroup (the staged Kt and Z serve all of them): as
+// many as keep about three workgroups per CU (768 on 256 CUs), at most
+// PROBS_GRP_MAX.  Measured: two groups at 4 x 12 x 4096 (one or four were
+// slower), four or more at 1 x 4 x 65536.
+inline int probs_groups(int n, int BH, int ncb) {
+  const long long blocks = (long long)((n + PROBS_TOK - 1) / PROBS_TOK) * BH * ncb;
+  return (int)std::max(1LL, std::min((long long)PROBS_GRP_MAX, blocks / 768));
+}
 constexpr int PROBS_CB = 64;    // landmark columns per workgroup
 
 template <typename IO, int M, int D>
@@ -84,7 +97,7 @@ __device__ __forceinline__ void store_probs4(IO* row, int col, int ncol, bool ve
   }
 }
 
-// grid: (ceil(ceil(n / 128) / 8) * 8 * NCB, BH), block 256, dynamic LDS
+// grid: (ceil(ceil(n / (128 grp)) / 8) * 8 * NCB, BH), block 256, dynamic LDS
 // ProbsLayout<IO, M, D>::LDS_BYTES.
 template <typename IO, int M, bool PAD, int D = HD>
 __global__ __launch_bounds__(256) void k_probs(ProbsArgs a) {
@@ -96,8 +109,9 @@ __global__ __launch_bounds__(256) void k_probs(ProbsArgs a) {
   const int bh = blockIdx.y;
   // blocks i, i + 8, ... (same XCD) take the column blocks of one token block
   const int grp = blockIdx.x / (8 * Ly::NCB), w8 = blockIdx.x % (8 * Ly::NCB);
-  const int cb = w8 / 8, t0 = (grp * 8 + (w8 % 8)) * PROBS_TOK;
-  if (t0 >= a.n) return;  // whole workgroup, before any barrier
+  const int cb = w8 / 8, tw0 = (grp * 8 + (w8 % 8)) * PROBS_TOK * a.grp;
+  if (tw0 >= a.n) return;  // whole workgroup, before any barrier
+  int t0 = tw0;
   const int col0 = cb * PROBS_CB;
   const IO* Q = reinterpret_cast<const IO*>(a.q) + a.in.base(bh, a.H);
   const long long st = a.in.t;
@@ -155,6 +169,21 @@ __global__ __launch_bounds__(256) void k_probs(ProbsArgs a) {
   }
   __syncthreads();
 
+  for (int gi = 0; gi < a.grp; ++gi) {
+  t0 = tw0 + gi * PROBS_TOK;
+  if (t0 >= a.n) break;
+  if (gi > 0) {  // this group's Q fragments
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tok = min(t0 + 32 * wave + 16 * u + c16, a.n - 1);
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        float x[8];
+        IOTraits<IO>::load8(Q + tok * st + 32 * ks + 8 * g, x);
+        qf2[u][ks] = make_frag<NS>(x);
+      }
+    }
+  }
   const int njt = min(4, (M - col0) / 16);
   const bool vec = (a.ldp & 3) == 0;
   const float ls2 = a.lscale * LOG2E;
@@ -221,6 +250,7 @@ __global__ __launch_bounds__(256) void k_probs(ProbsArgs a) {
         store_probs4<IO>(row, col0 + 16 * jt + 4 * g, a.mr, vec, pacc[jt]);
       }
     }
+  }
   }
 }
 
