@@ -68,11 +68,20 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   if (!p.landmarks_ready)  // else the module's projection formed them in its epilogue
     HIP_TRY(launch("k_landmark", k_landmark<IO, M, D>, dim3(M / p.lpw, p.BH), dim3(256), 0, st, (const IO*)q,
                    (const IO*)k, la));
-  size_t lds2 = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
-  lds2 = std::max<size_t>(lds2, bv_fold_bytes<bv_rows<IO, M, D>(), D>());
-  if constexpr (M <= 128)
-    lds2 = std::max<size_t>(lds2, sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>()
-                                                  : std::max(pinv_lds_bytes<M, false>(), pinv_lds_bytes<M, true>()));
+  // the pseudo-inverse encoding (bf16 I/O): fp16 products up to
+  // PINV_F16_MAX_ITER iterations, split bf16 beyond
+  const bool f16 = sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER;
+  size_t lds_bv = (sizeof(IO) == 2 && D == HD) ? (size_t)DMA_LDS_BYTES : (size_t)KV<IO, D>::LDS_BYTES;
+  lds_bv = std::max<size_t>(lds_bv, bv_fold_bytes<bv_rows<IO, M, D>(), D>());
+  // the launch's LDS (B V blocks and the chosen encoding's pseudo-inverse
+  // blocks), and the most either encoding needs (for the occupancy bound)
+  size_t lds2 = lds_bv, lds_max = lds_bv;
+  if constexpr (M <= 128) {
+    const size_t pf = sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M, true>();
+    const size_t ps = sizeof(IO) == 4 ? pinv_lds_bytes_f32<M>() : pinv_lds_bytes<M, false>();
+    lds2 = std::max(lds_bv, f16 ? pf : ps);
+    lds_max = std::max({lds_bv, pf, ps});
+  }
   // the padding-landmark and ragged-tile code only in the instance that needs it
   const bool pad = p.mr < M, edge = pad || p.n % 32 != 0;
   // The original init's one rendezvous needs every pseudo-inverse block
@@ -84,10 +93,11 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    const void* kern = edge ? reinterpret_cast<const void*>(k_pinv_bv<IO, M, true, D>)
-                            : reinterpret_cast<const void*>(k_pinv_bv<IO, M, false, D>);
-    if (allow_lds(edge ? k_pinv_bv<IO, M, true, D> : k_pinv_bv<IO, M, false, D>, lds2) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * bv_launch_waves<IO, M, D>(), lds2) !=
+    // every instance has the same block size; the largest LDS of either
+    // encoding gives a bound that holds for both
+    const void* kern = reinterpret_cast<const void*>(k_pinv_bv<IO, M, true, D>);
+    if (allow_lds(k_pinv_bv<IO, M, true, D>, lds_max) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * bv_launch_waves<IO, M, D>(), lds_max) !=
             hipSuccess)
       return 0;
     return std::min(FUSED_GRAM_MAX_BLOCKS, per_cu * cus / 2);
@@ -131,7 +141,7 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.BH = p.BH;
   pa.n_iter = n_iter;
   pa.init_option = init_option;
-  pa.f16 = (sizeof(IO) == 2 && n_iter <= PINV_F16_MAX_ITER) ? 1 : 0;
+  pa.f16 = f16 ? 1 : 0;
   pa.fuse_gram = fuse_gram ? 1 : 0;
   pa.npinv = p.npinv;
   pa.record = p.record ? 1 : 0;
@@ -150,20 +160,58 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.pacc = at<float>(w, p.off_pacc);
   ba.n = p.n;
   ba.H = p.H;
-  ba.S = p.S;
-  ba.tpc = p.tpc;
   ba.ntiles = p.ntiles;
   ba.lscale = s4;
   ba.in = p.si;
   constexpr int RG = bv_row_groups<IO, M, D>();
-  const int nbv = RG == 1 ? p.BH * p.S : 8 * RG * ((p.BH * p.S + 7) / 8);
+  // The plan sizes the key chunks for two resident blocks per CU.  Where
+  // the instance that runs holds fewer (its registers or LDS), fewer and
+  // longer chunks keep the launch to one round: a second round of B V
+  // blocks would start only as the first ends.  (At 1 x 8 x 16384 with 128
+  // landmarks one block fits a CU: 496 B V blocks ran in two rounds.)  The
+  // chunk count never grows past the plan's, which sizes the partials.
+  int S = p.S, tpc = p.tpc;
+  // blocks per CU of each instance (by edge, encoding; lds2 follows them)
+  static int occ[2][2] = {{-1, -1}, {-1, -1}}, cus = 0;
   auto launch_bv = [&](auto kern) -> int {
     HIP_TRY(allow_lds(kern, lds2));
+    int& per_cu = occ[edge ? 1 : 0][f16 ? 1 : 0];
+    if (per_cu < 0) {
+      int dev = 0, pc = 0, nc = 0;
+      HIP_TRY(hipGetDevice(&dev));
+      HIP_TRY(hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev));
+      HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, reinterpret_cast<const void*>(kern),
+                                                           64 * bv_launch_waves<IO, M, D>(), lds2));
+      cus = nc;
+      per_cu = pc;
+    }
+    const int resident = per_cu * cus;
+    if (per_cu >= 1 && resident < 2 * 256) {
+      const int target = std::max(p.BH, resident - p.npinv);
+      const int s1 = std::max(1, std::min(p.ntiles, target / (p.BH * RG)));
+      const int t1 = (p.ntiles + s1 - 1) / s1;
+      const int s2 = (p.ntiles + t1 - 1) / t1;
+      if (s2 < S) {
+        S = s2;
+        tpc = t1;
+      }
+    }
+    ba.S = S;
+    ba.tpc = tpc;
+    const int nbv = RG == 1 ? p.BH * S : 8 * RG * ((p.BH * S + 7) / 8);
     HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + nbv), dim3(64 * bv_launch_waves<IO, M, D>()), (uint32_t)lds2,
                    st, pa, ba, p.npinv));
     return NYS_OK;
   };
-  const int brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D>) : launch_bv(k_pinv_bv<IO, M, false, D>);
+  int brc;
+  if constexpr (sizeof(IO) == 2 && M <= 128) {
+    if (f16)
+      brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D, true>) : launch_bv(k_pinv_bv<IO, M, false, D, true>);
+    else
+      brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D, false>) : launch_bv(k_pinv_bv<IO, M, false, D, false>);
+  } else {
+    brc = edge ? launch_bv(k_pinv_bv<IO, M, true, D>) : launch_bv(k_pinv_bv<IO, M, false, D>);
+  }
   if (brc != NYS_OK) return brc;
 
   const float* Zfinal = pa.Z;
@@ -234,12 +282,12 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ma.W = at<float>(w, p.off_W);
   ma.wf_hi = at<__bf16>(w, p.off_wfh);
   ma.wf_lo = at<__bf16>(w, p.off_wfl);
-  ma.S = p.S;
+  ma.S = S;
   ma.BH = p.BH;
   ma.lse = p.bwd ? at<float>(w, p.off_lse) : nullptr;
   // threads per block: enough chunk subsets per row that each thread folds
   // one batch of 8 chunks (up to 1024 threads; 512 for m = 32)
-  const int need = M * ((p.S + 7) / 8);
+  const int need = M * ((S + 7) / 8);
   // the bf16 output pass at d = 64 takes W^T in its own channel order
   constexpr bool B16 = sizeof(IO) == 2 && D == HD;
   constexpr int NT_MAX = M >= 64 ? 1024 : 512;

@@ -495,17 +495,19 @@ __device__ void bv_block(const BvArgs& a, int bh, int chunk, int r0, __bf16* lds
 // EDGE: some padding landmarks (m not a multiple of 32) or a ragged last
 // key tile (n not a multiple of 32); the code for them is compiled only into
 // this instance, so the common shapes pay nothing for it.
-template <typename IO, int M, bool EDGE, int D = HD>
+// F16: the pseudo-inverse encoding of bf16 I/O (single fp16 or split bf16
+// products; pa.f16 must match).  Each encoding is its own instance, so the
+// register allocation of one is not shaped by the other (with both in one
+// kernel the 128-landmark instance spilled 51 VGPRs to scratch).
+template <typename IO, int M, bool EDGE, int D = HD, bool F16 = false>
 __global__ __launch_bounds__((64 * bv_launch_waves<IO, M, D>())) void k_pinv_bv(PinvArgs pa, BvArgs ba, int npinv) {
   extern __shared__ __align__(16) __bf16 lds_dyn[];
   if ((int)blockIdx.x < npinv) {
     if constexpr (M <= 128) {
       if constexpr (sizeof(IO) == 4)
         pinv_block_f32<M, EDGE>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
-      else if (pa.f16)
-        pinv_block<M, true, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
       else
-        pinv_block<M, false, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
+        pinv_block<M, F16, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
     }
     return;
   }

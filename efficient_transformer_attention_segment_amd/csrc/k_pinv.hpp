@@ -73,19 +73,23 @@ __device__ __forceinline__ float pinv_scale(const PinvArgs& a, int bh) {
 }
 
 // LDS use before the iteration starts (float offsets).  Qt and Kt are staged
-// at the bottom (dead once A is formed); A (row stride M + 4), the column-sum
-// scratch and the wave maxima sit above both the staging area and the
-// iteration's first region R0 (R0_BYTES), so that Z_0 can be written to R0
-// while A is still being read.
-template <int M, int R0_BYTES, int NW>
+// at the bottom; A (row stride M + 4), the column-sum scratch and the wave
+// maxima overwrite the staging area once every wave holds its rows of A in
+// registers (a barrier in between), and the iteration's regions overwrite A
+// once every wave has read its A operands and its Z_0 elements (another
+// barrier), so the prologue needs no more LDS than the larger of the staging
+// area and A.  (At 128 landmarks this keeps a pseudo-inverse block within
+// half of the CU's LDS, so a B V block fits beside it.)
+template <int M, int NW>
 struct ProLayout {
   static constexpr int QLD = HD + 4, ALD = M + 4, TM = M / 16;
   static constexpr int OFF_QT = 0, OFF_KT = M * QLD;  // float32 staging (float32 I/O)
   static constexpr int STAGE = 2 * M * QLD;           // floats: float32 Qt, Kt, or the four bf16 planes
-  static constexpr int OFF_A = (R0_BYTES / 4 > STAGE) ? R0_BYTES / 4 : STAGE;
+  static constexpr int OFF_A = 0;
   static constexpr int OFF_CSUM = OFF_A + M * ALD;
   static constexpr int OFF_WRED = OFF_CSUM + TM * M;
-  static constexpr int BYTES = 4 * (OFF_WRED + 2 * NW);
+  static constexpr int END = OFF_WRED + 2 * NW;
+  static constexpr int BYTES = 4 * (END > STAGE ? END : STAGE);
 };
 
 // A = softmax(Qt Kt^T) for one head into LDS (store_a_lds copies it to
@@ -143,8 +147,14 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
     wait_vmcnt<0>();
   }
   __syncthreads();
+  // one row tile per wave (TM <= NW); its rows of A stay in registers until
+  // every wave is done with the staging area, which A then overwrites
+  static_assert(TM <= NW, "one row tile of A per wave");
   float rmax_w = 0.f;
-  for (int rt = wave; rt < TM; rt += NW) {
+  f32x4 acc[TM];
+  float cs[TM];
+  const int rt = wave;
+  if (rt < TM) {
     // operands: element e of lane (g, c16) is k = 32 ks + 8 g + e
     float ax[2][8];
     Frag2 af[2];
@@ -159,7 +169,6 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
         af[ks].lo = *reinterpret_cast<const bf16x8*>(Bs + M * HD + swz(row, 4 * ks + g));
       }
     }
-    f32x4 acc[TM];
 #pragma unroll
     for (int ct = 0; ct < TM; ++ct) {
       acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -210,18 +219,21 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
       rmax_w = fmaxf(rmax_w, rs);
     }
 #pragma unroll
+    for (int ct = 0; ct < TM; ++ct) cs[ct] = sum_g(acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3]);
+  }
+  rmax_w = max_g(rmax_w);
+  __syncthreads();  // the staging area is dead from here on
+  if (rt < TM) {
+#pragma unroll
     for (int ct = 0; ct < TM; ++ct) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * rt + 4 * g + r;
         Al[row * ALD + 16 * ct + c16] = acc[ct][r];
       }
-      float cs = acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3];
-      cs = sum_g(cs);
-      if (g == 0) csum[rt * M + 16 * ct + c16] = cs;
+      if (g == 0) csum[rt * M + 16 * ct + c16] = cs[ct];
     }
   }
-  rmax_w = max_g(rmax_w);
   if (lane == 0) wred[wave] = rmax_w;
   __syncthreads();
   // column sums in a fixed order, then the block maximum
@@ -444,7 +456,7 @@ constexpr int pinv_ld() {
 template <int M, bool F16>
 constexpr int pinv_lds_bytes() {
   constexpr int iter = 2 * POp<F16>::NP * M * pinv_ld<M>() * 2;  // two regions of NP planes
-  constexpr int pro = ProLayout<M, POp<F16>::NP * M * pinv_ld<M>() * 2, nwaves<M>()>::BYTES;
+  constexpr int pro = ProLayout<M, nwaves<M>()>::BYTES;
   return iter > pro ? iter : pro;
 }
 
@@ -554,7 +566,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
   u16* const R1 = lds + P::NP * PL;
   float* Zg = a.Z + (size_t)bh * M * M;
 
-  using Ly = ProLayout<M, P::NP * PL * 2, nwaves<M>()>;
+  using Ly = ProLayout<M, nwaves<M>()>;
   const float c = pinv_prologue<M, false, nwaves<M>(), Ly, PAD>(a, bh, reinterpret_cast<float*>(lds));
   const float invc = 1.0f / c;
   const float* const Al = reinterpret_cast<const float*>(lds) + Ly::OFF_A;  // A, row stride Ly::ALD
@@ -605,8 +617,14 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
         const int i = h + WPG * j;
 #pragma unroll
         for (int q = 0; q < 4; ++q) Zacc[r][j][q] = Al[(16 * i + 4 * g + q) * Ly::ALD + rows[r]] * invc;
-        rowstore4<LD, PL, F16>(R0, rows[r], 16 * i + 4 * g, Zacc[r][j]);
       }
+  }
+  __syncthreads();  // A is dead: R0 overwrites it
+  if (own) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int j = 0; j < CT; ++j) rowstore4<LD, PL, F16>(R0, rows[r], 16 * (h + WPG * j) + 4 * g, Zacc[r][j]);
   }
   __syncthreads();
 
@@ -709,7 +727,7 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
 template <int M>
 constexpr int pinv_lds_bytes_f32() {
   constexpr int iter = 2 * M * (M + 4) * 4;  // two float32 regions, row stride M + 4
-  constexpr int pro = ProLayout<M, M * (M + 4) * 4, nwaves<M>()>::BYTES;
+  constexpr int pro = ProLayout<M, nwaves<M>()>::BYTES;
   return iter > pro ? iter : pro;
 }
 
@@ -752,7 +770,7 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
   float* const R1 = lds + M * LD;
   float* Zg = a.Z + (size_t)bh * M * M;
 
-  using Ly = ProLayout<M, M * LD * 4, nwaves<M>()>;
+  using Ly = ProLayout<M, nwaves<M>()>;
   const float c = pinv_prologue<M, true, nwaves<M>(), Ly, PAD>(a, bh, lds);
   const float invc = 1.0f / c;
   const float* const Al = lds + Ly::OFF_A;  // A, row stride Ly::ALD
@@ -785,8 +803,12 @@ __device__ void pinv_block_f32(const PinvArgs& a, int bh, float* lds) {
       const int col = 16 * (h + WPT * j) + c16;
       const float4 z = *reinterpret_cast<const float4*>(Al + col * Ly::ALD + row4);
       Zacc[j] = f32x4{z.x * invc, z.y * invc, z.z * invc, z.w * invc};
-      store_t<LD>(R0, col, row4, Zacc[j]);
     }
+  }
+  __syncthreads();  // A is dead: R0 overwrites it
+  if (own) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) store_t<LD>(R0, 16 * (h + WPT * j) + c16, row4, Zacc[j]);
   }
   __syncthreads();
 
