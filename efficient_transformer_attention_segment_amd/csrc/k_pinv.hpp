@@ -169,26 +169,42 @@ __device__ void gram_lds(const LandmarkArgs& a, int bh, float* L) {
         af[ks].lo = *reinterpret_cast<const bf16x8*>(Bs + M * HD + swz(row, 4 * ks + g));
       }
     }
+    // column tiles in pairs: both tiles' operand reads are issued before
+    // their products, and the two accumulation chains interleave
 #pragma unroll
-    for (int ct = 0; ct < TM; ++ct) {
-      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c2 = 0; c2 < TM; c2 += 2) {
+      if constexpr (F32) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int row = 16 * ct + c16, col = 32 * ks + 8 * g;
-        if constexpr (F32) {
-          float x[8];
+        for (int ct = c2; ct < c2 + 2; ++ct) {
+          acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = Ks[row * QLD + col + e];
-          acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
-        } else {
-          Frag2 bf;
-          bf.hi = *reinterpret_cast<const bf16x8*>(Bs + 2 * M * HD + swz(row, 4 * ks + g));
-          bf.lo = *reinterpret_cast<const bf16x8*>(Bs + 3 * M * HD + swz(row, 4 * ks + g));
-          acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+          for (int ks = 0; ks < 2; ++ks) {
+            const int row = 16 * ct + c16, col = 32 * ks + 8 * g;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = Ks[row * QLD + col + e];
+            acc[ct] = mma8_f32(ax[ks], x, acc[ct]);
+          }
         }
+      } else {
+        Frag2 bf[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int row = 16 * (c2 + u) + c16;
+            bf[u][ks].hi = *reinterpret_cast<const bf16x8*>(Bs + 2 * M * HD + swz(row, 4 * ks + g));
+            bf[u][ks].lo = *reinterpret_cast<const bf16x8*>(Bs + 3 * M * HD + swz(row, 4 * ks + g));
+          }
+        acc[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[c2 + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) acc[c2 + u] = mma<3>(af[ks], bf[u][ks], acc[c2 + u]);
       }
-      // keep the next tile's operand reads from being hoisted above this
-      // tile (all of them at once would not fit the register budget)
+      // keep the next pair's operand reads from being hoisted above this
+      // pair (all of them at once would not fit the register budget)
       asm volatile("" ::: "memory");
     }
     // row softmax: row 16rt + 4g + r, columns spread over ct and lane & 15;
@@ -604,9 +620,11 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = Al[rows[r] * Ly::ALD + 32 * ks + 8 * g + e];
+        // 8 consecutive floats of a row (16-byte aligned: the row stride is a
+        // multiple of 4 floats)
+        const float4* ap = reinterpret_cast<const float4*>(Al + rows[r] * Ly::ALD + 32 * ks + 8 * g);
+        const float4 u = ap[0], v = ap[1];
+        const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
         Af[r][ks] = P::make(x);
       }
     // Z_0 = A^T / c: Zacc[r][j][q] = Z_0[rows[r]][16i + 4g + q], i = h + WPG j
@@ -641,6 +659,10 @@ __device__ void pinv_block(const PinvArgs& a, int bh, u16* lds) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r][j] = P::mma(lf, Rf[r][ks], acc[r][j]);
       }
+      // split operands at 128 landmarks: keep the next column tile's reads
+      // from being hoisted above this one (they would not fit beside the
+      // iteration's live fragments and accumulators, and spilled)
+      if constexpr (!F16 && M > 64) asm volatile("" ::: "memory");
     }
   };
   using Std = std::integral_constant<bool, false>;
