@@ -12,7 +12,8 @@
 //   3 k_pinv_bv    one launch holding both the per-head pseudo-inverse
 //                  blocks (m <= 128) and the B V partial blocks, so the
 //                  pseudo-inverse chain runs beside the K/V stream
-//     (m > 128, bf16 I/O: k_gram_rows before it, and 3 k_pinv_mm launches
+//     (m > 128, bf16 I/O: A by row blocks in its first blocks at d = 64,
+//     k_gram_rows before it at other head sizes, and 3 k_pinv_mm launches
 //     per iteration after it; float32 I/O: k_gram, then k_pinv_init and 4
 //     k_pinv_gemm launches per iteration after it)
 //   4 k_mw         B V from the partials, W = Z (B V) and its operand
@@ -115,14 +116,24 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   constexpr bool MM_OK = M > 128 && sizeof(IO) == 2;
   const bool mm_path = MM_OK && n_iter >= 1 && n_iter <= PINV_F16_MAX_ITER;
   const hipStream_t pst = st;  // stream of the pseudo-inverse launches
+  // Blocks of the B V launch before its B V blocks: the pseudo-inverse
+  // blocks (m <= 128), or above 128 landmarks at d = 64 the row-split Gram
+  // (a launch of its own at other head sizes, whose B V launch keeps its LDS
+  // plan).
+  constexpr bool GRAM_IN_BV = MM_OK && D == HD;
+  int npre = p.npinv;
   if constexpr (MM_OK) {
     if (mm_path) {
       constexpr int grl = gram_rows_lds_bytes<M, D>();
-      HIP_TRY(allow_lds(k_gram_rows<M, D>, grl));
-      float* const colpart = at<float>(w, p.off_colpart);
-      float* const rowpart = at<float>(w, p.off_rowpart);
-      HIP_TRY(launch("k_gram_rows", k_gram_rows<M, D>, dim3(M / 32, p.BH), dim3(128), (uint32_t)grl, pst, la,
-                     at<float>(w, p.off_AT), at<u16>(w, p.off_T1), colpart, rowpart));
+      if constexpr (GRAM_IN_BV) {
+        npre = gram_rows_blocks<M>(p.BH);
+        lds2 = std::max<size_t>(lds2, grl);
+      } else {
+        HIP_TRY(allow_lds(k_gram_rows<M, D>, grl));
+        HIP_TRY(launch("k_gram_rows", k_gram_rows<M, D>, dim3(gram_rows_blocks<M>(p.BH)), dim3(256), (uint32_t)grl,
+                       pst, la, at<float>(w, p.off_AT), at<u16>(w, p.off_T1), at<float>(w, p.off_colpart),
+                       at<float>(w, p.off_rowpart)));
+      }
     }
   }
   if (!fuse_gram && !mm_path) {
@@ -143,11 +154,15 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   pa.init_option = init_option;
   pa.f16 = f16 ? 1 : 0;
   pa.fuse_gram = fuse_gram ? 1 : 0;
-  pa.npinv = p.npinv;
+  pa.npinv = npre;
   pa.record = p.record ? 1 : 0;
   pa.spins = g_spins;
   pa.status = at<unsigned>(w, STATUS_OFF);
   pa.la = la;
+  pa.gAT = at<float>(w, p.off_AT);
+  pa.gA16 = at<u16>(w, p.off_T1);
+  pa.colpart = at<float>(w, p.off_colpart);
+  pa.rowpart = at<float>(w, p.off_rowpart);
   BvArgs ba;
   ba.BH = p.BH;
   ba.k = k;
@@ -164,19 +179,23 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
   ba.lscale = s4;
   ba.in = p.si;
   constexpr int RG = bv_row_groups<IO, M, D>();
-  // The plan sizes the key chunks for two resident blocks per CU.  Where
-  // the instance that runs holds fewer (its registers or LDS), fewer and
+  // The plan sizes the key chunks for two resident blocks per CU beside the
+  // pseudo-inverse blocks.  Where the instance that runs holds fewer (its
+  // registers or LDS), or other blocks precede the B V blocks, fewer and
   // longer chunks keep the launch to one round: a second round of B V
   // blocks would start only as the first ends.  (At 1 x 8 x 16384 with 128
   // landmarks one block fits a CU: 496 B V blocks ran in two rounds.)  The
   // chunk count never grows past the plan's, which sizes the partials.
   int S = p.S, tpc = p.tpc;
-  // blocks per CU of each instance (by edge, encoding; lds2 follows them)
+  // blocks per CU of each instance (by edge and encoding) at the LDS size
+  // it was last launched with
   static int occ[2][2] = {{-1, -1}, {-1, -1}}, cus = 0;
+  static size_t occ_lds[2][2] = {{0, 0}, {0, 0}};
   auto launch_bv = [&](auto kern) -> int {
     HIP_TRY(allow_lds(kern, lds2));
     int& per_cu = occ[edge ? 1 : 0][f16 ? 1 : 0];
-    if (per_cu < 0) {
+    size_t& per_lds = occ_lds[edge ? 1 : 0][f16 ? 1 : 0];
+    if (per_cu < 0 || per_lds != lds2) {
       int dev = 0, pc = 0, nc = 0;
       HIP_TRY(hipGetDevice(&dev));
       HIP_TRY(hipDeviceGetAttribute(&nc, hipDeviceAttributeMultiprocessorCount, dev));
@@ -184,10 +203,11 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
                                                            64 * bv_launch_waves<IO, M, D>(), lds2));
       cus = nc;
       per_cu = pc;
+      per_lds = lds2;
     }
     const int resident = per_cu * cus;
-    if (per_cu >= 1 && resident < 2 * 256) {
-      const int target = std::max(p.BH, resident - p.npinv);
+    if (per_cu >= 1) {
+      const int target = std::max(p.BH, resident - npre);
       const int s1 = std::max(1, std::min(p.ntiles, target / (p.BH * RG)));
       const int t1 = (p.ntiles + s1 - 1) / s1;
       const int s2 = (p.ntiles + t1 - 1) / t1;
@@ -199,8 +219,8 @@ int launch_nystrom(const Plan& p, Workspace* w, const void* q, const void* k, co
     ba.S = S;
     ba.tpc = tpc;
     const int nbv = RG == 1 ? p.BH * S : 8 * RG * ((p.BH * S + 7) / 8);
-    HIP_TRY(launch("k_pinv_bv", kern, dim3(p.npinv + nbv), dim3(64 * bv_launch_waves<IO, M, D>()), (uint32_t)lds2,
-                   st, pa, ba, p.npinv));
+    HIP_TRY(launch("k_pinv_bv", kern, dim3(npre + nbv), dim3(64 * bv_launch_waves<IO, M, D>()), (uint32_t)lds2,
+                   st, pa, ba, npre));
     return NYS_OK;
   };
   int brc;

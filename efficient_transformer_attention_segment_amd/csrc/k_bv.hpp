@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "k_conv.hpp"
 #include "k_pinv.hpp"
+#include "k_pinv_mm.hpp"
 
 namespace nys {
 
@@ -508,6 +509,9 @@ __global__ __launch_bounds__((64 * bv_launch_waves<IO, M, D>())) void k_pinv_bv(
         pinv_block_f32<M, EDGE>(pa, blockIdx.x, reinterpret_cast<float*>(lds_dyn));
       else
         pinv_block<M, F16, EDGE>(pa, blockIdx.x, reinterpret_cast<u16*>(lds_dyn));
+    } else if constexpr (sizeof(IO) == 2 && D == HD && bv_launch_waves<IO, M, D>() == 4) {
+      gram_rows_body<M, D>(pa.la, pa.gAT, pa.gA16, pa.colpart, pa.rowpart, blockIdx.x,
+                           reinterpret_cast<char*>(lds_dyn));
     }
     return;
   }

@@ -50,6 +50,12 @@ struct PinvArgs {
   unsigned spins;       // bound on the rendezvous polls (option 0 with fuse_gram)
   unsigned* status;     // bit 0 set when a rendezvous ran out of polls
   LandmarkArgs la;      // landmarks in, A / colmax / rowmax out (fuse_gram)
+  // more than 128 landmarks at d = 64: the first npinv blocks of the B V
+  // launch form A by row blocks instead (gram_rows_body)
+  float* gAT;           // [BH][M][M] A^T
+  u16* gA16;            // [BH][M][M] A as fp16
+  float* colpart;       // [BH][M / 32][M] column sums per row block
+  float* rowpart;       // [BH][M / 32] largest row sum per row block
 };
 
 // Past the bound on the rendezvous wait (a.spins polls; about a second by

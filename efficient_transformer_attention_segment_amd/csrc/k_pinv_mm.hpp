@@ -19,9 +19,10 @@
 // order, rounded the same way, drifts by several per cent.  The linear
 // combinations run in float32 in the epilogues.
 //
-// k_gram_rows: A = softmax(Qt Kt^T) by 32-row blocks (grid (M / 32, BH)),
-//   split-bf16 products as in the one-block Gram; writes A, A^T and per
-//   block the column sums and the largest row sum.
+// gram_rows_body: A = softmax(Qt Kt^T) by 32-row blocks, split-bf16
+//   products as in the one-block Gram; writes A, A^T and per row block the
+//   column sums and the largest row sum.  At d = 64 it runs in the first
+//   workgroups of the B V launch, otherwise as k_gram_rows.
 // k_pinv_mm<LEVEL>: 32 x 32 output tiles (4 waves of one 16 x 16 tile
 //   each, K = M in fp16 16x16x32 matrix-core steps), every tile of a head on
 //   one XCD.  Level 1 of the first iteration also forms c from the Gram
@@ -46,117 +47,160 @@ namespace nys {
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ Gram rows ---
+// A = softmax(Qt Kt^T) by 32-row blocks, for the B V launch: its first
+// gram_rows_blocks() workgroups run this instead of B V partials (the
+// launch's blocks have four waves; a wave pair forms one 32-row block, so a
+// workgroup covers two row blocks of one head), which saves a launch of its
+// own before the B V stream.
 template <int M, int D>
 constexpr int gram_rows_lds_bytes() {
-  return 2 * M * (D + 8) * 2 + 4 * (2 * M + 2);
+  return 2 * M * (D + 8) * 2 + 4 * (4 * M + 4);
+}
+// row-block pairs per head
+template <int M>
+constexpr int gram_rows_per_head() {
+  return (M / 32 + 1) / 2;
+}
+template <int M>
+inline int gram_rows_blocks(int BH) {
+  return BH * gram_rows_per_head<M>();
 }
 
-// grid (M / 32, BH), 128 threads: wave w forms row tile 2 blockIdx.x + w.
+// Workgroup blk (256 threads): head blk / gram_rows_per_head, wave w forms
+// row tile 2 rb + (w & 1) of row block rb = 2 (blk % gram_rows_per_head) +
+// (w >> 1) (a wave pair past the last row block only meets the barriers).
+// Writes A (float32 and fp16), A^T (float32) and, per row block, the column
+// sums and the largest row sum.
 template <int M, int D>
-__global__ __launch_bounds__(128) void k_gram_rows(LandmarkArgs a, float* __restrict__ AT, u16* __restrict__ A16,
-                                                   float* __restrict__ colpart, float* __restrict__ rowpart) {
-  extern __shared__ __align__(16) char gr_smem[];
-  constexpr int TM = M / 16, DK = D / 32, KLD = D + 8;
+__device__ void gram_rows_body(const LandmarkArgs& a, float* __restrict__ AT, u16* __restrict__ A16,
+                               float* __restrict__ colpart, float* __restrict__ rowpart, int blk, char* gr_smem) {
+  constexpr int TM = M / 16, DK = D / 32, KLD = D + 8, NT = 256, RB = M / 32;
   __bf16* const kb = reinterpret_cast<__bf16*>(gr_smem);  // hi rows 0 .. M-1, lo rows M .. 2M-1
-  float* const csum = reinterpret_cast<float*>(gr_smem + 2 * M * KLD * 2);
-  float* const rmx = csum + 2 * M;
+  float* const csum = reinterpret_cast<float*>(gr_smem + 2 * M * KLD * 2);  // [4 waves][M]
+  float* const rmx = csum + 4 * M;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y, rt = 2 * blockIdx.x + wave;
+  const int bh = blk / gram_rows_per_head<M>();
+  const int rb = 2 * (blk % gram_rows_per_head<M>()) + (wave >> 1);
+  const bool live = rb < RB;
+  const int rt = 2 * rb + (wave & 1);
   {
-    // the K~ planes into LDS in batches of 8 pieces per thread, every load of
+    // the K~ planes into LDS in batches of 4 pieces per thread, every load of
     // a batch issued before its stores (one round trip per batch instead of
     // one per piece)
     const uint4* kh = reinterpret_cast<const uint4*>(a.kt_hi + (size_t)bh * M * D);
     const uint4* kl = reinterpret_cast<const uint4*>(a.kt_lo + (size_t)bh * M * D);
-    constexpr int PIECES = M * (D / 8), PER = PIECES / 128, BATCH = 4;
-    static_assert(PIECES % 128 == 0, "whole rounds of the block");
+    constexpr int PIECES = M * (D / 8), PER = (PIECES + NT - 1) / NT, BATCH = 4;
 #pragma unroll
     for (int b0 = 0; b0 < PER; b0 += BATCH) {
       uint4 xh[BATCH], xl[BATCH];
+      // every element is assigned (an index past the planes reads piece 0
+      // and is not stored), so the arrays stay in registers
 #pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        if (b0 + j < PER) {
-          xh[j] = kh[threadIdx.x + 128 * (b0 + j)];
-          xl[j] = kl[threadIdx.x + 128 * (b0 + j)];
-        }
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = threadIdx.x + NT * (b0 + j);
+        const int ic = (b0 + j < PER && i < PIECES) ? i : 0;
+        xh[j] = kh[ic];
+        xl[j] = kl[ic];
+      }
 #pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        if (b0 + j < PER) {
-          const int i = threadIdx.x + 128 * (b0 + j);
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = threadIdx.x + NT * (b0 + j);
+        if (b0 + j < PER && i < PIECES) {
           *reinterpret_cast<uint4*>(kb + (i / (D / 8)) * KLD + 8 * (i % (D / 8))) = xh[j];
           *reinterpret_cast<uint4*>(kb + (M + i / (D / 8)) * KLD + 8 * (i % (D / 8))) = xl[j];
         }
+      }
     }
   }
   Frag2 af[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) {
-    const size_t off = ((size_t)bh * M + rt * 16 + c16) * D + ks * 32 + g * 8;
-    af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
-    af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
-  }
-  __syncthreads();
-  f32x4 acc[TM];
-#pragma unroll
-  for (int ct = 0; ct < TM; ++ct) {
-    acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      const int row = ct * 16 + c16, col = ks * 32 + g * 8;
-      Frag2 bf;
-      bf.hi = *reinterpret_cast<const bf16x8*>(kb + row * KLD + col);
-      bf.lo = *reinterpret_cast<const bf16x8*>(kb + (M + row) * KLD + col);
-      acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+      const size_t off = ((size_t)bh * M + rt * 16 + c16) * D + ks * 32 + g * 8;
+      af[ks].hi = *reinterpret_cast<const bf16x8*>(a.qt_hi + off);
+      af[ks].lo = *reinterpret_cast<const bf16x8*>(a.qt_lo + off);
     }
   }
-  if (a.mr < M) pad_mask_cols(acc, a.mr);
+  __syncthreads();
   float rmax_w = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mx = NEG_BIG;
-#pragma unroll
-    for (int ct = 0; ct < TM; ++ct) mx = fmaxf(mx, acc[ct][r]);
-    mx = max16(mx);
-    float s = 0.f;
+  if (live) {
+    f32x4 acc[TM];
 #pragma unroll
     for (int ct = 0; ct < TM; ++ct) {
-      const float p = fast_exp2((acc[ct][r] - mx) * LOG2E);
-      acc[ct][r] = p;
-      s += p;
-    }
-    s = sum16(s);
-    const float inv = rt * 16 + g * 4 + r < a.mr ? 1.0f / s : 0.f;
-    float rs = 0.f;
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < TM; ++ct) {
-      acc[ct][r] *= inv;
-      rs += acc[ct][r];
+      for (int ks = 0; ks < DK; ++ks) {
+        const int row = ct * 16 + c16, col = ks * 32 + g * 8;
+        Frag2 bf;
+        bf.hi = *reinterpret_cast<const bf16x8*>(kb + row * KLD + col);
+        bf.lo = *reinterpret_cast<const bf16x8*>(kb + (M + row) * KLD + col);
+        acc[ct] = mma<3>(af[ks], bf, acc[ct]);
+      }
     }
-    rmax_w = fmaxf(rmax_w, sum16(rs));
-  }
-  float* const Ah = a.A + (size_t)bh * M * M;
-  float* const ATh = AT + (size_t)bh * M * M;
-  _Float16* const A16h = reinterpret_cast<_Float16*>(A16) + (size_t)bh * M * M;
-  const int row4 = rt * 16 + 4 * g;
-#pragma unroll
-  for (int ct = 0; ct < TM; ++ct) {
-    const int col = ct * 16 + c16;
+    if (a.mr < M) pad_mask_cols(acc, a.mr);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      Ah[(size_t)(row4 + r) * M + col] = acc[ct][r];
-      A16h[(size_t)(row4 + r) * M + col] = (_Float16)acc[ct][r];
+      float mx = NEG_BIG;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) mx = fmaxf(mx, acc[ct][r]);
+      mx = max16(mx);
+      float s = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        const float p = fast_exp2((acc[ct][r] - mx) * LOG2E);
+        acc[ct][r] = p;
+        s += p;
+      }
+      s = sum16(s);
+      const float inv = rt * 16 + g * 4 + r < a.mr ? 1.0f / s : 0.f;
+      float rs = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < TM; ++ct) {
+        acc[ct][r] *= inv;
+        rs += acc[ct][r];
+      }
+      rmax_w = fmaxf(rmax_w, sum16(rs));
     }
-    *reinterpret_cast<float4*>(ATh + (size_t)col * M + row4) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
-    const float cs = sum_g(acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3]);
-    if (g == 0) csum[wave * M + col] = cs;
+    float* const Ah = a.A + (size_t)bh * M * M;
+    float* const ATh = AT + (size_t)bh * M * M;
+    _Float16* const A16h = reinterpret_cast<_Float16*>(A16) + (size_t)bh * M * M;
+    const int row4 = rt * 16 + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < TM; ++ct) {
+      const int col = ct * 16 + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Ah[(size_t)(row4 + r) * M + col] = acc[ct][r];
+        A16h[(size_t)(row4 + r) * M + col] = (_Float16)acc[ct][r];
+      }
+      *reinterpret_cast<float4*>(ATh + (size_t)col * M + row4) =
+          make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+      const float cs = sum_g(acc[ct][0] + acc[ct][1] + acc[ct][2] + acc[ct][3]);
+      if (g == 0) csum[wave * M + col] = cs;
+    }
   }
   rmax_w = max_g(rmax_w);
   if (lane == 0) rmx[wave] = rmax_w;
   __syncthreads();
-  float* const cp = colpart + ((size_t)bh * (M / 32) + blockIdx.x) * M;
-  for (int j = threadIdx.x; j < M; j += 128) cp[j] = csum[j] + csum[M + j];
-  if (threadIdx.x == 0) rowpart[(size_t)bh * (M / 32) + blockIdx.x] = fmaxf(rmx[0], rmx[1]);
+  // the row block of each wave pair: column sums of its two row tiles
+  // (added in the order of the tiles) and its largest row sum
+  const int pr = threadIdx.x >> 7, pt = threadIdx.x & 127;  // pair, thread within the pair
+  const int rbp = 2 * (blk % gram_rows_per_head<M>()) + pr;
+  if (rbp < RB) {
+    float* const cp = colpart + ((size_t)bh * RB + rbp) * M;
+    for (int j = pt; j < M; j += 128) cp[j] = csum[(2 * pr) * M + j] + csum[(2 * pr + 1) * M + j];
+    if (pt == 0) rowpart[(size_t)bh * RB + rbp] = fmaxf(rmx[2 * pr], rmx[2 * pr + 1]);
+  }
+}
+
+// The same as a launch of its own (head sizes other than 64, whose B V
+// launch keeps its own LDS plan): grid gram_rows_blocks(BH), 256 threads.
+template <int M, int D>
+__global__ __launch_bounds__(256) void k_gram_rows(LandmarkArgs a, float* __restrict__ AT, u16* __restrict__ A16,
+                                                   float* __restrict__ colpart, float* __restrict__ rowpart) {
+  extern __shared__ __align__(16) char gr_smem[];
+  gram_rows_body<M, D>(a, AT, A16, colpart, rowpart, blockIdx.x, gr_smem);
 }
 
 // -------------------------------------------------------------- products ---
@@ -298,7 +342,7 @@ __device__ __forceinline__ void store_c(float* C32, u16* C16, u16* Ct16, int M, 
 // the L2 of the XCD that wrote them.  Heads h and h + 8 share XCD h mod 8.
 __host__ __device__ constexpr int pinv_mm_grid(int tiles, int BH) { return 8 * tiles * ((BH + 7) / 8); }
 
-// c for head bh from the Gram partials (k_gram_rows): the largest column sum
+// c for head bh from the Gram partials (gram_rows_body): the largest column sum
 // (row blocks added in order) times the largest row sum, over every head for
 // the original init, over head bh alone for the exact-coefficient init.  Also
 // head bh's own two maxima.  Whole workgroup (256 threads); red: 12 floats.
