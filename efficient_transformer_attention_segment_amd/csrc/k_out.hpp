@@ -380,40 +380,6 @@ __device__ __forceinline__ void load_q16(const u16* Q, long long st, int n, int 
   }
 }
 
-// Store a wave's 16-token output tile (C-tile layout of the bf16 pass: lane
-// (g, c16) holds channels dmap(dt, 4 g) .. + 3 of token ts + c16, which
-// packs to the 16-byte chunks g and 4 + g of its 128-byte row) as whole
-// rows: one lane swap (row_ror:8 inside each 16-lane row) gives every store
-// instruction all eight chunks of eight rows, tokens ts .. ts + 7 first,
-// then ts + 8 .. ts + 15, so each 128-byte line is written by a single
-// instruction (half-line pieces from two instructions cost HBM traffic).
-// Rows at or past te go to junk (16 rows).  Streaming stores: the call
-// never reads the output.
-__device__ __forceinline__ void store_tile16_rows(u16* O, long long ot, int ts, int te, u16* junk,
-                                                  const f32x4 (&acc)[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-  uint32_t v[2][4];  // chunk g (h = 0) and chunk 4 + g (h = 1) of row c16
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) v[h][2 * b + r] = pack_bf16x2(acc[2 * h + b][2 * r], acc[2 * h + b][2 * r + 1]);
-  const bool lo = c16 < 8;
-  uint32_t x[4], y[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[k] = lo ? v[1][k] : v[0][k];
-    y[k] = (uint32_t)__builtin_amdgcn_mov_dpp((int)x[k], 0x128, 0xf, 0xf, false);  // row_ror:8
-  }
-  // store A: row c16 & 7; store B: row c16 | 8; both at chunk g + 4 (c16 >> 3)
-  const int ra = c16 & 7, rb = c16 | 8, chunk = g + 4 * (c16 >> 3);
-  u16* const pa = (ts + ra < te ? O + (ts + ra) * ot : junk + ra * HD) + 8 * chunk;
-  u16* const pb = (ts + rb < te ? O + (ts + rb) * ot : junk + rb * HD) + 8 * chunk;
-  st_nt<u32x4>(pa, lo ? u32x4{v[0][0], v[0][1], v[0][2], v[0][3]} : u32x4{y[0], y[1], y[2], y[3]});
-  st_nt<u32x4>(pb, lo ? u32x4{y[0], y[1], y[2], y[3]} : u32x4{v[1][0], v[1][1], v[1][2], v[1][3]});
-}
-
 // grid (blocks per head, B H), 256 threads; workgroup x covers tokens
 // [x R, min(n, (x + 1) R)), R a multiple of 64.  junk: >= 16 * 64 bf16, the
 // destination of tiles past the range.  Two Q register buffers alternate
@@ -542,7 +508,8 @@ __global__ __launch_bounds__(64 * NW) void k_out_stream(OutArgs a, int R, u16* j
       }
     }
     if constexpr (CONV) conv_tile_ring<NW>(ring, t0, cl, tap, oacc);
-    store_tile16_rows(O, ot, ts, te, junk, oacc);
+    u16* dst = ts + c16 < te ? O + (ts + c16) * ot : junk + c16 * HD;
+    store_row16<u16, true, HD, true>(dst, oacc);
   };
   int u = 0;
   for (; u + 1 < nunits; u += 2) {
