@@ -390,9 +390,21 @@ __global__ __launch_bounds__(256) void k_pinv_mm(PinvMMArgs a) {
   constexpr int NT = M / PMM_T, LD = pinv_mm_ld<M>(), PANEL = PMM_T * LD;
   constexpr int TILES = (LEVEL == 2 ? 2 : 1) * NT * NT;
   const int L = blockIdx.x, xcd = L & 7, s = L >> 3;
-  const int bh = xcd + 8 * (s / TILES);
+  // Every tile of a head on one XCD (its operand panels then come into one
+  // L2); with at most four heads a head takes two XCDs, x and x + 4, each
+  // half of its tiles, so each CU holds one workgroup instead of two
+  // (what bounds a launch is the rate at which a CU receives its panels).
+  int bh, t2;
+  if (a.pa.BH <= 4) {
+    constexpr int H0 = (TILES + 1) / 2;
+    bh = xcd & 3;
+    t2 = (xcd >> 2) * H0 + s;
+    if (s >= H0 || t2 >= TILES) return;  // whole workgroup, before any barrier
+  } else {
+    bh = xcd + 8 * (s / TILES);
+    t2 = s % TILES;
+  }
   if (bh >= a.pa.BH) return;  // whole workgroup, before any barrier
-  const int t2 = s % TILES;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const bool second = LEVEL == 2 && t2 >= NT * NT;  // level 2: the W = Z X tiles
