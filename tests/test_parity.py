@@ -240,6 +240,17 @@ def test_iteration_counts_many_landmarks(dtype, m, n_iter):
     _check(f"niter{n_iter}-m{m}", x, dtype, m, n_iter, 0, conv=False)
 
 
+@pytest.mark.parametrize("B,H,m,n", [(1, 1, 256, 1024), (1, 3, 160, 640), (2, 3, 192, 768), (3, 3, 224, 448)])
+def test_head_counts_many_landmarks(B, H, m, n):
+    """Above 128 landmarks (bf16, d = 64) the B V launch forms A by row
+    blocks in its first workgroups and the chain places a head's tiles on
+    one XCD, or on two with at most four heads: one head, three, six and
+    nine (two groups of eight XCDs), an odd row-block count (m = 160, 224)."""
+    x = make_custom(B, H, n, 64, seed=830 + B * H + m, dtype="bf16", lengths=[n - 7 * b for b in range(B)])
+    _check(f"B{B}H{H}-m{m}", x, "bf16", m, 6, 0)
+    _check(f"B{B}H{H}-m{m}-init1", x, "bf16", m, 6, 1, conv=False)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_zero_valid_keys(dtype):
     """A batch row with every key masked: B V = 0, output = conv(V), no NaN."""
