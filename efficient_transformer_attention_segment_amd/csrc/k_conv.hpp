@@ -87,27 +87,57 @@ __device__ __forceinline__ void store_row16(IO* row, const f32x4 (&acc)[D / 16])
 
 // Stage V rows [t0 - 32, t0 - 32 + win) of one head (D channels),
 // transposed, into Vh[d * ld + row] (and Vl when split).  Rows outside
-// [0, n) are zero.
+// [0, n) are zero.  win and ld are even.  A thread takes two consecutive
+// rows of four channels and stores each channel's two rows as one 4-byte
+// word; a wave's 64 items are 16 row pairs x 4 channel groups, so at the
+// row strides used here (4 channels apart, 4 ld / 2 words, an odd multiple
+// of 16 banks) one store of the wave writes 64 distinct banks.  (Storing one
+// row's 2-byte elements at a time put eight channels on the same banks.)
 template <typename IO, int D = HD>
 __device__ void stage_v_window(const IO* __restrict__ V, long long st, int n, int t0, int win, __bf16* Vh, __bf16* Vl,
                                int ld) {
-  constexpr int NS = IOTraits<IO>::NS, CPR = D / 8;
-  for (int idx = threadIdx.x; idx < win * CPR; idx += blockDim.x) {
-    const int row = idx / CPR, cc = idx % CPR;
-    const int s = t0 - HALO + row;
-    float x[8];
-    if (s >= 0 && s < n) {
-      IOTraits<IO>::load8(V + s * st + 8 * cc, x);
-    } else {
+  constexpr int NS = IOTraits<IO>::NS, GB = D / 16;  // blocks of four 4-channel groups
+  const int pairs = win / 2;
+  const int items = ((pairs + 15) / 16) * GB * 64;
+  uint32_t* const wh = reinterpret_cast<uint32_t*>(Vh);
+  uint32_t* const wl = reinterpret_cast<uint32_t*>(Vl);
+  const int ldw = ld / 2;  // row stride in words
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int blk = it >> 6, l = it & 63;
+    const int p = 16 * (blk / GB) + (l & 15), cg = 4 * (blk % GB) + (l >> 4);
+    if (p >= pairs) continue;
+    float x[2][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int r = 0; r < 2; ++r) {
+      const int s = t0 - HALO + 2 * p + r;
+      if (s >= 0 && s < n) {
+        if constexpr (sizeof(IO) == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(V) + s * st + 4 * cg);
+          x[r][0] = v.x;
+          x[r][1] = v.y;
+          x[r][2] = v.z;
+          x[r][3] = v.w;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const u16*>(V) + s * st + 4 * cg);
+          x[r][0] = __uint_as_float(v.x << 16);
+          x[r][1] = __uint_as_float(v.x & 0xffff0000u);
+          x[r][2] = __uint_as_float(v.y << 16);
+          x[r][3] = __uint_as_float(v.y & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[r][e] = 0.f;
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 h, l;
-      split1(x[e], h, l);
-      Vh[(8 * cc + e) * ld + row] = h;
-      if constexpr (NS == 3) Vl[(8 * cc + e) * ld + row] = l;
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h0, l0, h1, l1;
+      split1(x[0][e], h0, l0);
+      split1(x[1][e], h1, l1);
+      const int w = (4 * cg + e) * ldw + p;  // rows 2p, 2p + 1 of channel 4 cg + e
+      wh[w] = (uint32_t)__builtin_bit_cast(u16, h0) | ((uint32_t)__builtin_bit_cast(u16, h1) << 16);
+      if constexpr (NS == 3)
+        wl[w] = (uint32_t)__builtin_bit_cast(u16, l0) | ((uint32_t)__builtin_bit_cast(u16, l1) << 16);
     }
   }
 }
