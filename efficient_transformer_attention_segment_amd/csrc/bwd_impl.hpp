@@ -56,6 +56,135 @@ inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   return b;
 }
 
+// The pseudo-inverse backward above 64 landmarks as a launch chain
+// (k_bwd_chain, every head per launch): the iteration again from Z_0 (X_k,
+// X_k^2, P_k and Z_k+1 kept), dZ_n = dW BV^T with dBV = Z_n^T dW, then per
+// iteration, last first, with G the gradient reaching Z_k+1:
+//   dZ_k = G P^T / 4 and dP = Z^T G / 4;
+//   T = X^T dP and dX = 7 dP X^T + 7 X^T dP - dP (X^2)^T - (X^2)^T dP - 15 dP;
+//   dX -= T X^T;
+//   dA += dX Z^T and dZ_k += A^T dX.
+// The same products and scratch layout as k_bwd_mm1 (the matrices of a head
+// at a.mm + h * bwd_mm_mats(n_iter) M^2).
+template <int M, int D>
+int launch_bwd_chain(const Plan& p, const BwdArgs& a, int n_iter, hipStream_t st) {
+  constexpr int KMAX = M > D ? M : D;
+  constexpr long long MM = (long long)M * M, MD = (long long)M * D;
+  static_assert(M * M >= M * D / 4, "k_bwd_chain_pre: one thread per four dW elements");
+  const long long sm = (long long)bwd_mm_mats(n_iter) * MM;
+  float* const S = a.mm;
+  auto Z = [&](int k) { return S + k * MM; };
+  auto X = [&](int k) { return S + (n_iter + 1 + 3 * k) * MM; };
+  auto X2 = [&](int k) { return X(k) + MM; };
+  auto P = [&](int k) { return X(k) + 2 * MM; };
+  float* const G = S + (4 * n_iter + 1) * MM;
+  float* const Gn = G + MM;
+  float* const dP = G + 2 * MM;
+  float* const dX = G + 3 * MM;
+  float* const T = G + 4 * MM;
+  float* const dA = G + 5 * MM;
+  HIP_TRY(launch("k_bwd_chain_pre", k_bwd_chain_pre<M, D>, dim3((unsigned)((MM + 255) / 256), p.BH), dim3(256), 0, st,
+                 a));
+  constexpr int lds = chain_lds_bytes<KMAX>();
+  HIP_TRY(allow_lds(k_bwd_chain<KMAX>, lds));
+  // op(A) is R x K and op(B) is K x N
+  auto term = [](const float* x, long long sx, bool tx, const float* y, long long sy, bool ty, float alpha,
+                 const ChainOut& o) {
+    ChainTerm t{};
+    t.a = x;
+    t.b = y;
+    t.sa = sx;
+    t.sb = sy;
+    t.ta = tx;
+    t.tb = ty;
+    t.lda = tx ? o.R : o.K;
+    t.ldb = ty ? o.K : o.N;
+    t.alpha = alpha;
+    return t;
+  };
+  auto out = [](float* c, long long sc, int R, int N, int K, float beta) {
+    ChainOut o{};
+    o.c = c;
+    o.sc = sc;
+    o.R = R;
+    o.N = N;
+    o.K = K;
+    o.ldc = N;
+    o.beta = beta;
+    return o;
+  };
+  auto go = [&](const ChainOut& o0, const ChainOut* o1) {
+    ChainLaunch L{};
+    L.o[0] = o0;
+    L.tiles0 = chain_tiles(o0.R, o0.N);
+    int tiles = L.tiles0;
+    if (o1 != nullptr) {
+      L.o[1] = *o1;
+      tiles += chain_tiles(o1->R, o1->N);
+    }
+    return launch("k_bwd_chain", k_bwd_chain<KMAX>, dim3(tiles, p.BH), dim3(256), (uint32_t)lds, st, L);
+  };
+  for (int k = 0; k < n_iter; ++k) {
+    ChainOut o = out(X(k), sm, M, M, M, 0.f);  // X = A Z
+    o.t[o.nt++] = term(a.A, MM, false, Z(k), sm, false, 1.f, o);
+    HIP_TRY(go(o, nullptr));
+    o = out(X2(k), sm, M, M, M, 0.f);  // X^2
+    o.t[o.nt++] = term(X(k), sm, false, X(k), sm, false, 1.f, o);
+    HIP_TRY(go(o, nullptr));
+    o = out(P(k), sm, M, M, M, 0.f);  // P = 13I - 15X + 7X^2 - X^3
+    o.t[o.nt++] = term(X(k), sm, false, X2(k), sm, false, -1.f, o);
+    o.e1 = X(k);
+    o.g1 = -15.f;
+    o.e2 = X2(k);
+    o.g2 = 7.f;
+    o.eye = 13.f;
+    HIP_TRY(go(o, nullptr));
+    o = out(Z(k + 1), sm, M, M, M, 0.f);  // Z <- Z P / 4
+    o.t[o.nt++] = term(Z(k), sm, false, P(k), sm, false, 0.25f, o);
+    HIP_TRY(go(o, nullptr));
+  }
+  {
+    ChainOut o0 = out(G, sm, M, M, D, 0.f);  // dZ_n = dW BV^T
+    o0.t[o0.nt++] = term(a.dW, MD, false, a.BV, MD, true, 1.f, o0);
+    ChainOut o1 = out(a.dBV, MD, M, D, M, 0.f);  // dBV = Z_n^T dW
+    o1.t[o1.nt++] = term(Z(n_iter), sm, true, a.dW, MD, false, 1.f, o1);
+    HIP_TRY(go(o0, &o1));
+  }
+  float* g = G;
+  float* gn = Gn;
+  for (int k = n_iter - 1; k >= 0; --k) {
+    ChainOut o0 = out(gn, sm, M, M, M, 0.f);
+    o0.t[o0.nt++] = term(g, sm, false, P(k), sm, true, 0.25f, o0);
+    ChainOut o1 = out(dP, sm, M, M, M, 0.f);
+    o1.t[o1.nt++] = term(Z(k), sm, true, g, sm, false, 0.25f, o1);
+    HIP_TRY(go(o0, &o1));
+    o0 = out(T, sm, M, M, M, 0.f);
+    o0.t[o0.nt++] = term(X(k), sm, true, dP, sm, false, 1.f, o0);
+    o1 = out(dX, sm, M, M, M, 0.f);
+    o1.t[o1.nt++] = term(dP, sm, false, X(k), sm, true, 7.f, o1);
+    o1.t[o1.nt++] = term(X(k), sm, true, dP, sm, false, 7.f, o1);
+    o1.t[o1.nt++] = term(dP, sm, false, X2(k), sm, true, -1.f, o1);
+    o1.t[o1.nt++] = term(X2(k), sm, true, dP, sm, false, -1.f, o1);
+    o1.e1 = dP;
+    o1.g1 = -15.f;
+    HIP_TRY(go(o0, &o1));
+    o0 = out(dX, sm, M, M, M, 1.f);
+    o0.t[o0.nt++] = term(T, sm, false, X(k), sm, true, -1.f, o0);
+    HIP_TRY(go(o0, nullptr));
+    o0 = out(dA, sm, M, M, M, 1.f);
+    o0.t[o0.nt++] = term(dX, sm, false, Z(k), sm, true, 1.f, o0);
+    o1 = out(gn, sm, M, M, M, 1.f);
+    o1.t[o1.nt++] = term(a.A, MM, true, dX, sm, false, 1.f, o1);
+    HIP_TRY(go(o0, &o1));
+    float* const t = g;
+    g = gn;
+    gn = t;
+  }
+  const int gsel = 4 * n_iter + 1 + (g == G ? 0 : 1);
+  HIP_TRY(launch("k_bwd_chain_post", k_bwd_chain_post<M>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a, gsel));
+  return NYS_OK;
+}
+
 template <typename IO, int M, int D>
 int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* q, const void* k, const void* v,
                     const uint8_t* mask, const float* conv_w, int conv_k, int n_iter, int init_option,
@@ -159,6 +288,9 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
       HIP_TRY(allow_lds(k_bwd_mm1b64<D>, BWD_MM1B_LDS));
       HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM1B_LDS, st, a));
     }
+  } else if constexpr (M > 64) {
+    rc = launch_bwd_chain<M, D>(p, a, n_iter, st);
+    if (rc != NYS_OK) return rc;
   } else {
     HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
     HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));

@@ -161,6 +161,8 @@ struct BwdTokLayout {
   // and writes dQs for channels [z DC, (z + 1) DC) only (each half forms the
   // whole S, dF and softmax of its tokens; the halves share nothing).
   static constexpr bool KT_LDS = M <= 128;
+  // S and dF through LDS rather than whole rows in registers
+  static constexpr bool S_LDS = M > 128;
   static constexpr int SPLIT = (M > 128 && D > 32) ? 2 : 1;
   static constexpr int DC = D / SPLIT, LDC = DC + 4;
   static constexpr int OFF_KT = 0;
@@ -249,38 +251,85 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
       }
     }
     // S = Qs Kt^T and dF = dout W^T: C(token 4g + r, landmark 16 jt + c16)
-    f32x4 f[TM], df[TM];
-#pragma unroll
-    for (int jt = 0; jt < TM; ++jt) {
-      f[jt] = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * KLD, 1, KLD, f32x4{0.f, 0.f, 0.f, 0.f});
-      df[jt] = mm16<D>(DOg + 16 * wave * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
-      if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jt = 0; jt < TM; ++jt) mx = fmaxf(mx, f[jt][r]);
-      mx = max16(mx);
-      float s = 0.f;
-#pragma unroll
+    if constexpr (Ly::S_LDS) {
+      // above 128 landmarks S and dF go to LDS one tile at a time (whole
+      // rows of both stay out of the registers), then the row softmax runs
+      // over the wave's 16 rows there, four lanes per row
+#pragma unroll 1
       for (int jt = 0; jt < TM; ++jt) {
-        f[jt][r] = __expf(f[jt][r] - mx);
-        s += f[jt][r];
+        f32x4 f = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * KLD, 1, KLD, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 df = mm16<D>(DOg + 16 * wave * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (16 * jt + c16 >= a.mr) f = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * wave + 4 * g + r;
+          Fg[row * LDF + 16 * jt + c16] = f[r];
+          DSg[row * LDF + 16 * jt + c16] = df[r];
+        }
       }
-      const float inv = 1.0f / sum16(s);
-      float dt = 0.f;
-#pragma unroll
-      for (int jt = 0; jt < TM; ++jt) {
-        f[jt][r] *= inv;
-        dt += f[jt][r] * df[jt][r];
+      __syncthreads();
+      {
+        const int row = 16 * wave + (lane >> 2), q4 = lane & 3;
+        float* const fr = Fg + row * LDF;
+        float* const dr = DSg + row * LDF;
+        float mx = -INFINITY;
+        for (int c = q4; c < M; c += 4) mx = fmaxf(mx, fr[c]);
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        float s = 0.f;
+        for (int c = q4; c < M; c += 4) {
+          const float e = __expf(fr[c] - mx);
+          fr[c] = e;
+          s += e;
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        const float inv = 1.0f / s;
+        float dt = 0.f;
+        for (int c = q4; c < M; c += 4) {
+          const float fv = fr[c] * inv;
+          fr[c] = fv;
+          dt += fv * dr[c];
+        }
+        dt += __shfl_xor(dt, 1);
+        dt += __shfl_xor(dt, 2);
+        for (int c = q4; c < M; c += 4) dr[c] = fr[c] * (dr[c] - dt);
       }
-      dt = sum16(dt);
-      const int row = 16 * wave + 4 * g + r;
+      __syncthreads();
+    } else {
+      f32x4 f[TM], df[TM];
 #pragma unroll
       for (int jt = 0; jt < TM; ++jt) {
-        Fg[row * LDF + 16 * jt + c16] = f[jt][r];
-        DSg[row * LDF + 16 * jt + c16] = f[jt][r] * (df[jt][r] - dt);
+        f[jt] = mm16<D>(Qg + 16 * wave * LD, LD, 1, Kt + 16 * jt * KLD, 1, KLD, f32x4{0.f, 0.f, 0.f, 0.f});
+        df[jt] = mm16<D>(DOg + 16 * wave * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (16 * jt + c16 >= a.mr) f[jt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) mx = fmaxf(mx, f[jt][r]);
+        mx = max16(mx);
+        float s = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) {
+          f[jt][r] = __expf(f[jt][r] - mx);
+          s += f[jt][r];
+        }
+        const float inv = 1.0f / sum16(s);
+        float dt = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) {
+          f[jt][r] *= inv;
+          dt += f[jt][r] * df[jt][r];
+        }
+        dt = sum16(dt);
+        const int row = 16 * wave + 4 * g + r;
+#pragma unroll
+        for (int jt = 0; jt < TM; ++jt) {
+          Fg[row * LDF + 16 * jt + c16] = f[jt][r];
+          DSg[row * LDF + 16 * jt + c16] = f[jt][r] * (df[jt][r] - dt);
+        }
       }
     }
     // dQs = dS Kt (16 tokens x this workgroup's channels), the wave's own rows
@@ -819,6 +868,63 @@ __device__ __forceinline__ void bgemm_h(float* C, const float* Ag, bool ta, cons
     bgemm<R, N, K>(C, Ag, ta, Bg, tb, alpha, beta, La, Lb);
 }
 
+// The end of the pseudo-inverse backward of head bh, given the gradient g
+// reaching Z_0 = A^T / c: dA += g^T / c, dc = -sum(g A^T) / c^2, the
+// maximum column sum of A with its column and the maximum row sum.
+// BWD_MM_NT threads; g and dA are written before the call.
+template <int M>
+__device__ void mm1_tail(const BwdArgs& a, int bh, const float* A, const float* g, float* dA, float c) {
+  constexpr int MM = M * M, NT = BWD_MM_NT;
+  const int tid = threadIdx.x;
+  float part = 0.f;
+  for (int i = tid; i < MM; i += NT) {
+    const int r = i / M, col = i % M;
+    dA[i] += g[col * M + r] / c;
+    part += g[col * M + r] * A[i];
+  }
+  __shared__ float red[NT];
+  __shared__ int redj[NT];
+  red[tid] = part;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float dcv = -red[0] / (c * c);
+  __syncthreads();
+  float cs = -1.f, rs = 0.f;
+  int cj = 0;
+  if (tid < M) {
+    cs = 0.f;
+    for (int r = 0; r < M; ++r) cs += A[r * M + tid];
+    for (int j = 0; j < M; ++j) rs += A[tid * M + j];
+    cj = tid;
+  }
+  red[tid] = cs;
+  redj[tid] = cj;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s && (red[tid + s] > red[tid] || (red[tid + s] == red[tid] && redj[tid + s] < redj[tid]))) {
+      red[tid] = red[tid + s];
+      redj[tid] = redj[tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.dc[bh] = dcv;
+    a.cmax[bh] = red[0];
+    a.cmaxj[bh] = redj[0];
+  }
+  __syncthreads();
+  red[tid] = tid < M ? rs : 0.f;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  if (tid == 0) a.rmax[bh] = red[0];
+}
+
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
 template <int M, int D>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
@@ -887,54 +993,161 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1(BwdArgs a) {
     gn = t;
   }
   __syncthreads();
-  // Z_0 = A^T / c: dA += G^T / c; dc = -sum(G A^T) / c^2; and the arg-max column of A's column sums
-  float part = 0.f;
-  for (int i = tid; i < MM; i += NT) {
-    const int r = i / M, col = i % M;
-    dA[i] += g[col * M + r] / c;
-    part += g[col * M + r] * A[i];
-  }
-  __shared__ float red[NT];
-  __shared__ int redj[NT];
-  red[tid] = part;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const float dcv = -red[0] / (c * c);
-  __syncthreads();
-  float cs = -1.f, rs = 0.f;
-  int cj = 0;
-  if (tid < M) {
-    cs = 0.f;
-    for (int r = 0; r < M; ++r) cs += A[r * M + tid];
-    for (int j = 0; j < M; ++j) rs += A[tid * M + j];
-    cj = tid;
-  }
-  red[tid] = cs;
-  redj[tid] = cj;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (tid < s && (red[tid + s] > red[tid] || (red[tid + s] == red[tid] && redj[tid + s] < redj[tid]))) {
-      red[tid] = red[tid + s];
-      redj[tid] = redj[tid + s];
+  mm1_tail<M>(a, bh, A, g, dA, c);
+}
+
+// ---------------------------------------------------------------------------
+// Above 64 landmarks the pseudo-inverse backward runs as a chain of launches
+// over every head at once instead of one workgroup per head: each launch is
+// one or two independent products (the same for all heads), each output a
+// sum of up to four products plus elementwise terms,
+//   C = sum_t alpha_t op(A_t) op(B_t) + beta C + g1 E1 + g2 E2 + eye I,
+// with float32 row-major matrices, head h's at base + h * stride.  A
+// workgroup of four waves forms one 32 x 32 tile of one output (a 16 x 16
+// tile per wave); the 32-row strips of op(A) and op(B)^T over the whole
+// contraction are staged in LDS per product.
+struct ChainTerm {
+  const float* a;
+  const float* b;
+  long long sa, sb;   // per-head strides (floats)
+  int ta, tb;         // op = transpose
+  int lda, ldb;       // stored row strides
+  float alpha;
+};
+struct ChainOut {
+  float* c;
+  const float* e1;    // same shape and strides as C, or null
+  const float* e2;
+  long long sc;
+  int R, N, K, ldc, nt;
+  float beta, g1, g2, eye;
+  ChainTerm t[4];
+};
+struct ChainLaunch {
+  ChainOut o[2];
+  int tiles0;         // workgroups of output 0; the rest are output 1's
+};
+
+__host__ __device__ constexpr int chain_tiles(int R, int N) { return ((R + 31) / 32) * ((N + 31) / 32); }
+template <int KMAX>
+constexpr int chain_lds_bytes() {
+  return 2 * 32 * (KMAX + 4) * 4;
+}
+
+// Rows [r0, r0 + 32) of op(X) (K columns) into dst[32][K + 4]; X is stored
+// K x rows (trans) or rows x K, row stride ld.  Rows at or past nrows are
+// skipped (no wave reads them).
+__device__ __forceinline__ void chain_stage(float* dst, const float* x, int ld, bool trans, int r0, int nrows,
+                                            int K, int ldl) {
+  const int tid = threadIdx.x;
+  if (!trans) {
+    const int k4 = K / 4;
+    for (int i = tid; i < 32 * k4; i += 256) {
+      const int rr = i / k4, kq = i % k4;
+      if (r0 + rr < nrows)
+        *reinterpret_cast<float4*>(dst + rr * ldl + 4 * kq) =
+            *reinterpret_cast<const float4*>(x + (size_t)(r0 + rr) * ld + 4 * kq);
     }
+  } else {
+    // eight lanes per stored row (32 consecutive floats), one row per k
+    for (int i = tid; i < 8 * K; i += 256) {
+      const int rq = i % 8, k = i / 8;
+      if (r0 + 4 * rq < nrows) {
+        const float4 v = *reinterpret_cast<const float4*>(x + (size_t)k * ld + r0 + 4 * rq);
+        dst[(4 * rq + 0) * ldl + k] = v.x;
+        dst[(4 * rq + 1) * ldl + k] = v.y;
+        dst[(4 * rq + 2) * ldl + k] = v.z;
+        dst[(4 * rq + 3) * ldl + k] = v.w;
+      }
+    }
+  }
+}
+
+// grid (tiles of output 0 + tiles of output 1, BH), block 256, dynamic LDS
+// chain_lds_bytes<KMAX>().
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_bwd_chain(ChainLaunch L) {
+  extern __shared__ __align__(16) float bw_lds[];
+  constexpr int LDL = KMAX + 4;
+  float* const As = bw_lds;
+  float* const Bs = bw_lds + 32 * LDL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y;
+  const bool second = (int)blockIdx.x >= L.tiles0;
+  const ChainOut& o = second ? L.o[1] : L.o[0];
+  const int tile = (int)blockIdx.x - (second ? L.tiles0 : 0);
+  const int tn = (o.N + 31) / 32;
+  const int r0 = 32 * (tile / tn), c0 = 32 * (tile % tn);
+  const int it = wave >> 1, jt = wave & 1;
+  const bool live = r0 + 16 * it < o.R && c0 + 16 * jt < o.N;
+  const int K = o.K;
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < o.nt; ++t) {
+    const ChainTerm& tm = o.t[t];
+    __syncthreads();  // the previous product's reads done
+    chain_stage(As, tm.a + (size_t)bh * tm.sa, tm.lda, tm.ta != 0, r0, o.R, K, LDL);
+    chain_stage(Bs, tm.b + (size_t)bh * tm.sb, tm.ldb, tm.tb == 0, c0, o.N, K, LDL);
     __syncthreads();
+    if (live) {
+      const float* pa = As + (16 * it + c16) * LDL + g;
+      const float* pb = Bs + (16 * jt + c16) * LDL + g;
+      f32x4 acc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // K is a multiple of 16: four accumulators, one per k step mod 4
+      for (int s = 0; s < K / 4; s += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = mfma_f32(pa[4 * (s + u)], pb[4 * (s + u)], acc[u]);
+      }
+      const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      tot += tm.alpha * sum;
+    }
   }
-  if (tid == 0) {
-    a.dc[bh] = dcv;
-    a.cmax[bh] = red[0];
-    a.cmaxj[bh] = redj[0];
+  if (!live) return;
+  float* const C = o.c + (size_t)bh * o.sc;
+  const float* const E1 = o.e1 != nullptr ? o.e1 + (size_t)bh * o.sc : nullptr;
+  const float* const E2 = o.e2 != nullptr ? o.e2 + (size_t)bh * o.sc : nullptr;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = r0 + 16 * it + 4 * g + r, col = c0 + 16 * jt + c16;
+    const size_t i = (size_t)row * o.ldc + col;
+    float v = tot[r];
+    if (o.beta != 0.f) v += o.beta * C[i];
+    if (E1 != nullptr) v += o.g1 * E1[i];
+    if (E2 != nullptr) v += o.g2 * E2[i];
+    if (row == col) v += o.eye;
+    C[i] = v;
   }
-  __syncthreads();
-  red[tid] = tid < M ? rs : 0.f;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
+}
+
+// Start of the chain: dW and dKt (F part) from the token-chunk partials,
+// Z_0 = A^T / c and dA = 0.  grid (ceil(M M / 256), BH), block 256.
+template <int M, int D>
+__global__ __launch_bounds__(256) void k_bwd_chain_pre(BwdArgs a) {
+  constexpr int MM = M * M;
+  const int bh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  if (e < MM) {
+    S[e] = a.A[(size_t)bh * MM + (e % M) * M + e / M] / a.cscale[bh];
+    S[(size_t)(4 * a.n_iter + 1 + 5) * MM + e] = 0.f;  // dA
   }
-  if (tid == 0) a.rmax[bh] = red[0];
+  if (4 * e < M * D) {
+    const size_t off = (size_t)bh * a.nct * M * D + 4 * e;
+    *reinterpret_cast<float4*>(a.dW + (size_t)bh * M * D + 4 * e) = sum_chunks4(a.pw + off, (size_t)M * D, a.nct);
+    *reinterpret_cast<float4*>(a.dKt + (size_t)bh * M * D + 4 * e) = sum_chunks4(a.pk + off, (size_t)M * D, a.nct);
+  }
+}
+
+// End of the chain: mm1_tail with the gradient reaching Z_0 in matrix gsel
+// of the scratch (the G or Gn slot).  grid BH, block BWD_MM_NT.
+template <int M>
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_chain_post(BwdArgs a, int gsel) {
+  constexpr int MM = M * M;
+  const int bh = blockIdx.x;
+  float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
+  mm1_tail<M>(a, bh, a.A + (size_t)bh * MM, S + (size_t)gsel * MM, S + (size_t)(4 * a.n_iter + 1 + 5) * MM,
+              a.cscale[bh]);
 }
 
 // Product on operands already in LDS (row strides lda, ldb; flat

@@ -86,6 +86,15 @@ def test_backward_iterations(dtype, n_iter):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n_iter", [0, 12])
+def test_backward_iterations_many_landmarks(dtype, n_iter):
+    """The launch-chain pseudo-inverse backward (above 64 landmarks) with no
+    iteration and with twelve."""
+    x = make_custom(1, 3, 1024, 64, seed=993 + n_iter, dtype=dtype, lengths=[900])
+    _check(f"m128-iter{n_iter}", x, dtype, 128, n_iter, 0, seed=3)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_backward_conv_sizes_and_empty_row(dtype):
     """Conv kernel sizes 1 and 33, and a batch row with no kept key."""
     for K in (1, 33):
