@@ -259,6 +259,10 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     constexpr int tl = BwdTok2Layout<IO, M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok2<IO, M, D>, tl));
     HIP_TRY(launch("k_bwd_tok", k_bwd_tok2<IO, M, D>, dim3(bp.nct, p.BH), dim3(256), (uint32_t)tl, st, a));
+  } else if constexpr (bwd_tok3(M, D)) {
+    constexpr int tl = BwdTok3Layout<M>::BYTES;
+    HIP_TRY(allow_lds(k_bwd_tok3<IO, M>, tl));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok3<IO, M>, dim3(bp.nct, p.BH), dim3(256), (uint32_t)tl, st, a));
   } else {
     constexpr int tl = BwdTokLayout<M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));

@@ -120,6 +120,9 @@ constexpr int BWD_CT = 256;      // tokens per k_bwd_tok workgroup
 constexpr int BWD_CK = 256;      // keys per k_bwd_key workgroup
 constexpr int BWD_GK = 32;       // keys per step of k_bwd_key
 constexpr int BWD_CV = 128;      // tokens per k_bwd_conv workgroup
+constexpr int BWD_T3_CT = 512;   // tokens per k_bwd_tok3 workgroup
+// the four-wave token pass for head size 64 above 64 landmarks
+__host__ __device__ constexpr bool bwd_tok3(int M, int D) { return D == 64 && M > 64; }
 
 template <int M>
 constexpr int bwd_tok_waves() {
@@ -392,6 +395,166 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// Token pass for head size 64 above 64 landmarks: four waves share each
+// 32-token group, Kt (and W where it fits) stay in LDS for the whole chunk,
+// and every wave holds its share of the dW / dKt tiles in registers:
+//   S = Qs Kt^T and dF = dout W^T tile by tile into LDS (the 2 x M/16 tile
+//   pairs dealt over the waves), the row softmax there (eight lanes per
+//   row), dS = F (dF - D_t); dQs = dS Kt (eight 16 x 16 tiles, two per
+//   wave); dW += F^T dout and dKt += dS^T Qs over the group's tokens
+//   (2 M/16 x 4 tiles, M/8 per wave).
+// Float32 matrix-core products (mm16) over float32 LDS operands.
+template <int M>
+struct BwdTok3Layout {
+  static constexpr int D = 64, NW = 4, GT = 32, LDF = M + 4, LD = D + 4;
+  static constexpr int OFF_KT = 0;
+  static constexpr int OFF_Q = OFF_KT + M * LD;
+  static constexpr int OFF_DO = OFF_Q + GT * LD;
+  static constexpr int OFF_F = OFF_DO + GT * LD;
+  static constexpr int OFF_DS = OFF_F + GT * LDF;
+  static constexpr int OFF_W = OFF_DS + GT * LDF;
+  static constexpr bool W_LDS = 4 * (OFF_W + M * LD) <= 160 * 1024;
+  static constexpr int FLOATS = OFF_W + (W_LDS ? M * LD : 0);
+  static constexpr int BYTES = 4 * FLOATS;
+  static_assert(BYTES <= 160 * 1024, "k_bwd_tok3 LDS");
+};
+
+// grid (nct, BH), block 256.
+template <typename IO, int M>
+__global__ __launch_bounds__(256) void k_bwd_tok3(BwdArgs a) {
+  extern __shared__ __align__(16) float bw_lds[];
+  using Ly = BwdTok3Layout<M>;
+  constexpr int D = 64, NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, LD = Ly::LD, TM = M / 16, CT = D / 16;
+  constexpr int NACC = 2 * TM * CT / NW;
+  static_assert((2 * TM * CT) % NW == 0 && M % 16 == 0, "every wave owns the same number of tiles");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int t0 = chunk * BWD_T3_CT, t1 = min(a.n, t0 + BWD_T3_CT);
+  const IO* Q = reinterpret_cast<const IO*>(a.q) + (size_t)bh * a.n * D;
+  const IO* DO = reinterpret_cast<const IO*>(a.dout) + (size_t)bh * a.n * D;
+  const float* const Wg = a.W + (size_t)bh * M * D;
+  const float* const Ktg = a.kt + (size_t)bh * M * D;
+  float* const Kt = bw_lds + Ly::OFF_KT;
+  float* const Qg = bw_lds + Ly::OFF_Q;
+  float* const DOg = bw_lds + Ly::OFF_DO;
+  float* const Fg = bw_lds + Ly::OFF_F;
+  float* const DSg = bw_lds + Ly::OFF_DS;
+  float* const Wl = bw_lds + Ly::OFF_W;
+  const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
+  constexpr int WLD = Ly::W_LDS ? LD : D;
+  for (int i = tid; i < M * D / 4; i += 256) {
+    const int r = i / (D / 4), c = 4 * (i % (D / 4));
+    *reinterpret_cast<float4*>(Kt + r * LD + c) = *reinterpret_cast<const float4*>(Ktg + (size_t)r * D + c);
+    if constexpr (Ly::W_LDS)
+      *reinterpret_cast<float4*>(Wl + r * LD + c) = *reinterpret_cast<const float4*>(Wg + (size_t)r * D + c);
+  }
+  f32x4 racc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int gs = t0; gs < t1; gs += GT) {
+    // q (scaled) and dout rows of the group: eight lanes per token, eight channels each
+    {
+      const int r = tid >> 3, c0 = 8 * (tid & 7), tok = gs + r;
+      float xq[8], xo[8];
+      if (tok < t1) {
+        IOTraits<IO>::load8(Q + (size_t)tok * D + c0, xq);
+        IOTraits<IO>::load8(DO + (size_t)tok * D + c0, xo);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xq[e] = xo[e] = 0.f;
+      }
+      float* const qd = Qg + r * LD + c0;
+      float* const od = DOg + r * LD + c0;
+      *reinterpret_cast<float4*>(qd) = make_float4(xq[0] * a.s4, xq[1] * a.s4, xq[2] * a.s4, xq[3] * a.s4);
+      *reinterpret_cast<float4*>(qd + 4) = make_float4(xq[4] * a.s4, xq[5] * a.s4, xq[6] * a.s4, xq[7] * a.s4);
+      *reinterpret_cast<float4*>(od) = make_float4(xo[0], xo[1], xo[2], xo[3]);
+      *reinterpret_cast<float4*>(od + 4) = make_float4(xo[4], xo[5], xo[6], xo[7]);
+    }
+    __syncthreads();  // rows staged (and, the first time, Kt / W)
+    // S and dF tile pairs p = (token tile p % 2, landmark tile p / 2): C(token 4g + r, landmark c16)
+    for (int p = wave; p < 2 * TM; p += NW) {
+      const int tt = p & 1, jt = p >> 1;
+      f32x4 f = mm16<D>(Qg + 16 * tt * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 df = mm16<D>(DOg + 16 * tt * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (16 * jt + c16 >= a.mr) f = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * tt + 4 * g + r;
+        Fg[row * LDF + 16 * jt + c16] = f[r];
+        DSg[row * LDF + 16 * jt + c16] = df[r];
+      }
+    }
+    __syncthreads();
+    // row softmax and dS, eight lanes per row
+    {
+      const int row = tid >> 3, q8 = tid & 7;
+      float* const fr = Fg + row * LDF;
+      float* const dr = DSg + row * LDF;
+      float mx = -INFINITY;
+      for (int c = q8; c < M; c += 8) mx = fmaxf(mx, fr[c]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      float s = 0.f;
+      for (int c = q8; c < M; c += 8) {
+        const float e = __expf(fr[c] - mx);
+        fr[c] = e;
+        s += e;
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      const float inv = 1.0f / s;
+      float dt = 0.f;
+      for (int c = q8; c < M; c += 8) {
+        const float fv = fr[c] * inv;
+        fr[c] = fv;
+        dt += fv * dr[c];
+      }
+      dt += __shfl_xor(dt, 1);
+      dt += __shfl_xor(dt, 2);
+      dt += __shfl_xor(dt, 4);
+      for (int c = q8; c < M; c += 8) dr[c] = fr[c] * (dr[c] - dt);
+    }
+    __syncthreads();
+    // dQs = dS Kt: tiles (token tile, channel tile), two per wave
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = wave + NW * u, tt = p / CT, ct = p % CT;
+      const f32x4 c = mm16<M>(DSg + 16 * tt * LDF, LDF, 1, Kt + 16 * ct, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = gs + 16 * tt + 4 * g + r;
+        if (tok < t1) a.dqf[((size_t)bh * a.n + tok) * D + 16 * ct + c16] = c[r];
+      }
+    }
+    // dW += F^T dout and dKt += dS^T Qs; tile ti = (landmark tile, channel tile), the dKt tiles after the dW tiles
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) {
+      const int ti = wave + NW * j;
+      const bool isk = ti >= TM * CT;
+      const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
+      const float* A0 = (isk ? DSg : Fg) + 16 * jt;
+      const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+      racc[j] = mm16<GT>(A0, 1, LDF, B0, LD, 1, racc[j]);
+    }
+    __syncthreads();  // the group's rows free
+  }
+  float* const pw = a.pw + ((size_t)bh * a.nct + chunk) * M * D;
+  float* const pk = a.pk + ((size_t)bh * a.nct + chunk) * M * D;
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) {
+    const int ti = wave + NW * j;
+    const bool isk = ti >= TM * CT;
+    const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
+    float* const dst = isk ? pk : pw;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * D + 16 * ct + c16] = racc[j][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Token pass on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), for
 // D <= 64 and M * D <= 64 * 64 (the LDS tiles and register accumulators
 // grow with both).  Float32 operands are split hi + lo (products hi*hi +
@@ -414,7 +577,9 @@ constexpr int BWD_T2_CT = 1024;  // tokens per workgroup
 
 __host__ __device__ constexpr bool bwd_tok2(int M, int D) { return D <= 64 && M * D <= 64 * 64; }
 // tokens per token-pass workgroup (the chunk of one dW / dKt partial)
-__host__ __device__ constexpr int bwd_tok_chunk(int M, int D) { return bwd_tok2(M, D) ? BWD_T2_CT : BWD_CT; }
+__host__ __device__ constexpr int bwd_tok_chunk(int M, int D) {
+  return bwd_tok2(M, D) ? BWD_T2_CT : (bwd_tok3(M, D) ? BWD_T3_CT : BWD_CT);
+}
 
 template <typename IO, int M, int D>
 struct BwdTok2Layout {
