@@ -18,7 +18,7 @@ namespace host {
 struct BwdPlan {
   int nct, nck, ncv, mats;
   size_t off_dqf, off_pw, off_pk, off_pq, off_mm, off_dW, off_dBV, off_dQt, off_dKt, off_Dv, off_dc, off_cmax,
-      off_cmaxj, off_rmax, off_dvc, off_pconv, total;
+      off_cmaxj, off_rmax, off_dvc, off_pconv, off_dvk, total;
 };
 
 inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
@@ -52,6 +52,7 @@ inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
   b.off_rmax = take(BH * 4);
   b.off_dvc = conv ? take(BH * n * D * 4) : 0;
   b.off_pconv = conv ? take(BH * b.ncv * (size_t)conv_k * 4) : 0;
+  b.off_dvk = M > 128 ? take(2 * BH * n * D * 4) : 0;  // the key pass's first-half dv, dk
   b.total = o;
   return b;
 }
@@ -222,6 +223,7 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.rmax = at<float>(w, bp.off_rmax);
   a.dvc = conv_w != nullptr ? at<float>(w, bp.off_dvc) : nullptr;
   a.pconv = conv_w != nullptr ? at<float>(w, bp.off_pconv) : nullptr;
+  a.dvk = M > 128 ? at<float>(w, bp.off_dvk) : nullptr;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

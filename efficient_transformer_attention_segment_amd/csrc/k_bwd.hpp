@@ -105,6 +105,7 @@ struct BwdArgs {
   int* cmaxj;               // [BH]: its column
   float* rmax;              // [BH]: maximum row sum of A
   float* dvc;               // [BH][n][d]: conv part of dv, or null
+  float* dvk;               // [2][BH][n][d]: the key pass's first-half dv, dk (above 128 landmarks)
   float* pconv;             // [BH][ncv][conv_k]
   void* dq;
   void* dk;
@@ -121,6 +122,7 @@ constexpr int BWD_CK = 256;      // keys per k_bwd_key workgroup
 constexpr int BWD_GK = 32;       // keys per step of k_bwd_key
 constexpr int BWD_CV = 128;      // tokens per k_bwd_conv workgroup
 constexpr int BWD_T3_CT = 512;   // tokens per k_bwd_tok3 workgroup
+constexpr int BWD_CK2 = 512;     // keys per k_bwd_key workgroup above 128 landmarks
 // the four-wave token pass for head size 64 above 64 landmarks
 __host__ __device__ constexpr bool bwd_tok3(int M, int D) { return D == 64 && M > 64; }
 
@@ -579,6 +581,11 @@ __host__ __device__ constexpr bool bwd_tok2(int M, int D) { return D <= 64 && M 
 // tokens per token-pass workgroup (the chunk of one dW / dKt partial)
 __host__ __device__ constexpr int bwd_tok_chunk(int M, int D) {
   return bwd_tok2(M, D) ? BWD_T2_CT : (bwd_tok3(M, D) ? BWD_T3_CT : BWD_CT);
+}
+// keys per key-pass workgroup (the chunk of one dQt partial)
+constexpr int BWD_K2_CK = 1024;  // k_bwd_key2
+__host__ __device__ constexpr int bwd_key_chunk(int M, int D) {
+  return bwd_tok2(M, D) ? BWD_K2_CK : (M > 128 ? BWD_CK2 : BWD_CK);
 }
 
 template <typename IO, int M, int D>
@@ -1844,18 +1851,23 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
 template <int M, int D>
 struct BwdKeyLayout {
   static constexpr int LDB = BWD_GK + 4, LD = D + 4;
-  // above 128 landmarks Qt and dBV are read from L2 instead of LDS
-  static constexpr bool QT_LDS = M <= 128;
+  // above 128 landmarks the pass takes the landmarks in two halves of MH
+  // rows (Qt, dBV and the B / dS tiles of one half in LDS at a time); the
+  // first half's dv / dk contributions go to a float32 buffer and come back,
+  // to the lane that wrote them, in the second
+  static constexpr int NHALF = M > 128 ? 2 : 1;
+  static constexpr int MH = NHALF == 1 ? M : (M / 2 + 15) / 16 * 16;
   static constexpr int OFF_QT = 0;
-  static constexpr int OFF_DBV = OFF_QT + (QT_LDS ? M * LD : 0);
-  static constexpr int OFF_KS = OFF_DBV + (QT_LDS ? M * LD : 0);
+  static constexpr int OFF_DBV = OFF_QT + MH * LD;
+  static constexpr int OFF_KS = OFF_DBV + MH * LD;
   static constexpr int OFF_V = OFF_KS + BWD_GK * LD;
   static constexpr int OFF_B = OFF_V + BWD_GK * LD;
-  static constexpr int OFF_DS = OFF_B + M * LDB;
-  static constexpr int OFF_VAL = OFF_DS + M * LDB;
+  static constexpr int OFF_DS = OFF_B + MH * LDB;
+  static constexpr int OFF_VAL = OFF_DS + MH * LDB;
   static constexpr int FLOATS = OFF_VAL + BWD_GK;
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_key LDS");
+  static_assert(NHALF * MH >= M, "the halves cover every landmark");
 };
 
 constexpr int BWD_KEY_NT = 512;  // threads of k_bwd_key (8 waves)
@@ -1866,118 +1878,134 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   constexpr int NT = BWD_KEY_NT, NWV = NT / 64;
   extern __shared__ __align__(16) float bw_lds[];
   using Ly = BwdKeyLayout<M, D>;
-  constexpr int TM = M / 16, CT = D / 16, LDB = Ly::LDB, LD = Ly::LD;
+  constexpr int NH = Ly::NHALF, MH = Ly::MH, TH = MH / 16, CT = D / 16, LDB = Ly::LDB, LD = Ly::LD;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x, b = bh / a.H;
-  const int k0 = chunk * BWD_CK, k1 = min(a.n, k0 + BWD_CK);
+  const int ck = bwd_key_chunk(M, D);
+  const int k0 = chunk * ck, k1 = min(a.n, k0 + ck);
   const IO* Kg = reinterpret_cast<const IO*>(a.k) + (size_t)bh * a.n * D;
   const IO* Vg = reinterpret_cast<const IO*>(a.v) + (size_t)bh * a.n * D;
   const uint8_t* mask = a.key_mask ? a.key_mask + (size_t)b * a.n : nullptr;
   const float* lse = a.lse + (size_t)bh * M;
   const float* Dv = a.Dv + (size_t)bh * M;
   const float* dKt = a.dKt + (size_t)bh * M * D;
-  constexpr int QLD = Ly::QT_LDS ? LD : D;  // row stride of Qt and dBV
-  const float* const Qt = Ly::QT_LDS ? bw_lds + Ly::OFF_QT : a.qt + (size_t)bh * M * D;
-  const float* const dBV = Ly::QT_LDS ? bw_lds + Ly::OFF_DBV : a.dBV + (size_t)bh * M * D;
+  float* const Qt = bw_lds + Ly::OFF_QT;
+  float* const dBV = bw_lds + Ly::OFF_DBV;
   float* const Ks = bw_lds + Ly::OFF_KS;
   float* const Vs = bw_lds + Ly::OFF_V;
   float* const Bt = bw_lds + Ly::OFF_B;
   float* const DS = bw_lds + Ly::OFF_DS;
   float* const VAL = bw_lds + Ly::OFF_VAL;
-  if constexpr (Ly::QT_LDS) {
-    for (int i = tid; i < M * D; i += NT) {
-      const int r = i / D, c = i % D;
-      bw_lds[Ly::OFF_QT + r * LD + c] = a.qt[(size_t)bh * M * D + i];
-      bw_lds[Ly::OFF_DBV + r * LD + c] = a.dBV[(size_t)bh * M * D + i];
-    }
-  }
-  // dQt_B tiles (landmark tile, channel tile) owned by this wave: t = wave + NWV j
-  constexpr int NACC = (TM * CT + NWV - 1) / NWV;
-  f32x4 acc[NACC];
-#pragma unroll
-  for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the first half's dv, then dk, contributions ([BH][n][D] each)
+  float* const hv = a.dvk;
+  float* const hk = a.dvk != nullptr ? a.dvk + (size_t)a.BH * a.n * D : nullptr;
   const float inv_l = 1.0f / (float)a.L;
-  for (int gk = k0; gk < k1; gk += BWD_GK) {
-    __syncthreads();  // staging done / previous step's reads done
-    static_assert(BWD_GK * (D / 8) <= NT, "one chunk of K and of V per thread");
-    if (tid < BWD_GK * (D / 8)) {
-      // one 8-element chunk of K and of V per thread
-      const int r = tid / (D / 8), c = 8 * (tid % (D / 8)), key = gk + r;
-      float xk[8], xv[8];
-      if (key < k1) {
-        IOTraits<IO>::load8(Kg + (size_t)key * D + c, xk);
-        IOTraits<IO>::load8(Vg + (size_t)key * D + c, xv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xk[e] = xv[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Ks[r * LD + c + e] = xk[e] * a.s4;
-        Vs[r * LD + c + e] = xv[e];
-      }
+  // dQt_B tiles (landmark tile of the half, channel tile) owned by this wave: t = wave + NWV j
+  constexpr int NACC = (TH * CT + NWV - 1) / NWV;
+  for (int h = 0; h < NH; ++h) {
+    const int i0 = h * MH;  // the half's first landmark; rows at or past M are zero
+    __syncthreads();        // the previous half's reads done
+    for (int i = tid; i < MH * D; i += NT) {
+      const int r = i / D, c = i % D;
+      const bool in = i0 + r < M;
+      Qt[r * LD + c] = in ? a.qt[((size_t)bh * M + i0 + r) * D + c] : 0.f;
+      dBV[r * LD + c] = in ? a.dBV[((size_t)bh * M + i0 + r) * D + c] : 0.f;
     }
-    if (tid < BWD_GK) {
-      const int key = gk + tid;
-      VAL[tid] = (key < k1 && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
-    }
-    __syncthreads();
-    // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
-    for (int t = wave; t < TM * (BWD_GK / 16); t += NWV) {
-      const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
-      const f32x4 s = mm16<D>(Qt + 16 * it * QLD, QLD, 1, Ks + 16 * kt * LD, 1, LD,
-                               f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 db = mm16<D>(dBV + 16 * it * QLD, QLD, 1, Vs + 16 * kt * LD, 1, LD,
-                                f32x4{0.f, 0.f, 0.f, 0.f});
-      const float val = VAL[16 * kt + c16];
+    f32x4 acc[NACC];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * g + r;
-        const float bb = val != 0.f ? exp2f(s[r] * LOG2E - lse[i]) : 0.f;
-        Bt[i * LDB + 16 * kt + c16] = bb;
-        DS[i * LDB + 16 * kt + c16] = bb * (db[r] - Dv[i]);
-      }
-    }
-    __syncthreads();
-    // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[seg] / L): C(key, channel)
-    for (int t = wave; t < 2 * (BWD_GK / 16) * CT; t += NWV) {
-      const bool isk = t >= (BWD_GK / 16) * CT;
-      const int tt = t % ((BWD_GK / 16) * CT), kt = tt / CT, ct = tt % CT;
-      const f32x4 c = mm16<M>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, QLD, 1,
-                              f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = gk + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
-        if (key >= k1) continue;
-        const size_t o = ((size_t)bh * a.n + key) * D + ch;
-        if (isk) {
-          const float x = c[r] + dKt[(size_t)(key / a.L) * D + ch] * inv_l;
-          io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * x);
+    for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gk = k0; gk < k1; gk += BWD_GK) {
+      __syncthreads();  // staging done / previous step's reads done
+      static_assert(BWD_GK * (D / 8) <= NT, "one chunk of K and of V per thread");
+      if (tid < BWD_GK * (D / 8)) {
+        // one 8-element chunk of K and of V per thread
+        const int r = tid / (D / 8), c = 8 * (tid % (D / 8)), key = gk + r;
+        float xk[8], xv[8];
+        if (key < k1) {
+          IOTraits<IO>::load8(Kg + (size_t)key * D + c, xk);
+          IOTraits<IO>::load8(Vg + (size_t)key * D + c, xv);
         } else {
-          const float x = c[r] + (a.dvc != nullptr ? a.dvc[o] : 0.f);
-          io_put(reinterpret_cast<IO*>(a.dv) + o, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xk[e] = xv[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          Ks[r * LD + c + e] = xk[e] * a.s4;
+          Vs[r * LD + c + e] = xv[e];
+        }
+      }
+      if (tid < BWD_GK) {
+        const int key = gk + tid;
+        VAL[tid] = (key < k1 && (mask == nullptr || mask[key] != 0)) ? 1.f : 0.f;
+      }
+      __syncthreads();
+      // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
+      for (int t = wave; t < TH * (BWD_GK / 16); t += NWV) {
+        const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
+        const f32x4 s = mm16<D>(Qt + 16 * it * LD, LD, 1, Ks + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+        const float val = VAL[16 * kt + c16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int il = 16 * it + 4 * g + r, i = i0 + il;
+          const bool on = val != 0.f && i < M;
+          const float bb = on ? exp2f(s[r] * LOG2E - lse[i]) : 0.f;
+          Bt[il * LDB + 16 * kt + c16] = bb;
+          DS[il * LDB + 16 * kt + c16] = i < M ? bb * (db[r] - Dv[i]) : 0.f;
+        }
+      }
+      __syncthreads();
+      // dv = B^T dBV + dv_conv and dk = d^-1/4 (dS^T Qt + dKt[seg] / L): C(key, channel)
+      for (int t = wave; t < 2 * (BWD_GK / 16) * CT; t += NWV) {
+        const bool isk = t >= (BWD_GK / 16) * CT;
+        const int tt = t % ((BWD_GK / 16) * CT), kt = tt / CT, ct = tt % CT;
+        const f32x4 c = mm16<MH>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, LD, 1,
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = gk + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
+          if (key >= k1) continue;
+          const size_t o = ((size_t)bh * a.n + key) * D + ch;
+          float x = c[r];
+          if constexpr (NH == 2) {
+            if (h == 0) {
+              (isk ? hk : hv)[o] = x;
+              continue;
+            }
+            x = (isk ? hk : hv)[o] + x;
+          }
+          if (isk) {
+            x += dKt[(size_t)(key / a.L) * D + ch] * inv_l;
+            io_put(reinterpret_cast<IO*>(a.dk) + o, a.s4 * x);
+          } else {
+            x += a.dvc != nullptr ? a.dvc[o] : 0.f;
+            io_put(reinterpret_cast<IO*>(a.dv) + o, x);
+          }
+        }
+      }
+      // dQt_B += dS Ks: C(landmark, channel), summed over the step's keys
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) {
+        const int t = wave + NWV * j;
+        if (t < TH * CT) {
+          const int it = t / CT, ct = t % CT;
+          acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, LD, 1, acc[j]);
         }
       }
     }
-    // dQt_B += dS Ks: C(landmark, channel), summed over the step's keys
+    float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * D;
 #pragma unroll
     for (int j = 0; j < NACC; ++j) {
       const int t = wave + NWV * j;
-      if (t < TM * CT) {
+      if (t < TH * CT) {
         const int it = t / CT, ct = t % CT;
-        acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, LD, 1, acc[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i0 + 16 * it + 4 * g + r;
+          if (row < M) pq[(size_t)row * D + 16 * ct + c16] = acc[j][r];
+        }
       }
-    }
-  }
-  float* const pq = a.pq + ((size_t)bh * a.nck + chunk) * M * D;
-#pragma unroll
-  for (int j = 0; j < NACC; ++j) {
-    const int t = wave + NWV * j;
-    if (t < TM * CT) {
-      const int it = t / CT, ct = t % CT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pq[(size_t)(16 * it + 4 * g + r) * D + 16 * ct + c16] = acc[j][r];
     }
   }
 }
@@ -1995,9 +2023,6 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
 //   dQt += dS Ks: dS^T goes to the wave's LDS tile, A by transposed reads,
 //   summed over all of the wave's steps in registers; the four waves' sums
 //   are added in wave order at the end.
-constexpr int BWD_K2_CK = 1024;  // keys per workgroup
-
-__host__ __device__ constexpr int bwd_key_chunk(int M, int D) { return bwd_tok2(M, D) ? BWD_K2_CK : BWD_CK; }
 
 template <typename IO, int M, int D>
 struct BwdKey2Layout {
