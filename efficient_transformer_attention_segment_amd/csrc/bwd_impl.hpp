@@ -58,39 +58,34 @@ inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
 }
 
 // The pseudo-inverse backward above 64 landmarks as a launch chain
-// (k_bwd_chain, every head per launch): the iteration again from Z_0 (X_k,
-// X_k^2, P_k and Z_k+1 kept), dZ_n = dW BV^T with dBV = Z_n^T dW, then per
-// iteration, last first, with G the gradient reaching Z_k+1:
+// (k_bwd_chain, every head per launch).  Forward half (it needs only A and
+// c, so it runs beside the token pass): Z_0, then per iteration X_k = A Z_k,
+// X_k^2, P_k and Z_k+1 (all kept).  Backward half: dW and dKt from the token
+// partials, dZ_n = dW BV^T with dBV = Z_n^T dW, then per iteration, last
+// first, with G the gradient reaching Z_k+1:
 //   dZ_k = G P^T / 4 and dP = Z^T G / 4;
 //   T = X^T dP and dX = 7 dP X^T + 7 X^T dP - dP (X^2)^T - (X^2)^T dP - 15 dP;
 //   dX -= T X^T;
-//   dA += dX Z^T and dZ_k += A^T dX.
-// The same products and scratch layout as k_bwd_mm1 (the matrices of a head
-// at a.mm + h * bwd_mm_mats(n_iter) M^2).
+//   dA += dX Z^T and dZ_k += A^T dX;
+// and the end (k_bwd_chain_post).  The same products and scratch layout as
+// k_bwd_mm1 (the matrices of a head at a.mm + h * bwd_mm_mats(n_iter) M^2).
 template <int M, int D>
-int launch_bwd_chain(const Plan& p, const BwdArgs& a, int n_iter, hipStream_t st) {
-  constexpr int KMAX = M > D ? M : D;
-  constexpr long long MM = (long long)M * M, MD = (long long)M * D;
-  static_assert(M * M >= M * D / 4, "k_bwd_chain_pre: one thread per four dW elements");
-  const long long sm = (long long)bwd_mm_mats(n_iter) * MM;
-  float* const S = a.mm;
-  auto Z = [&](int k) { return S + k * MM; };
-  auto X = [&](int k) { return S + (n_iter + 1 + 3 * k) * MM; };
-  auto X2 = [&](int k) { return X(k) + MM; };
-  auto P = [&](int k) { return X(k) + 2 * MM; };
-  float* const G = S + (4 * n_iter + 1) * MM;
-  float* const Gn = G + MM;
-  float* const dP = G + 2 * MM;
-  float* const dX = G + 3 * MM;
-  float* const T = G + 4 * MM;
-  float* const dA = G + 5 * MM;
-  HIP_TRY(launch("k_bwd_chain_pre", k_bwd_chain_pre<M, D>, dim3((unsigned)((MM + 255) / 256), p.BH), dim3(256), 0, st,
-                 a));
-  constexpr int lds = chain_lds_bytes<KMAX>();
-  HIP_TRY(allow_lds(k_bwd_chain<KMAX>, lds));
-  // op(A) is R x K and op(B) is K x N
-  auto term = [](const float* x, long long sx, bool tx, const float* y, long long sy, bool ty, float alpha,
-                 const ChainOut& o) {
+struct BwdChain {
+  static constexpr int KMAX = M > D ? M : D;
+  static constexpr long long MM = (long long)M * M, MD = (long long)M * D;
+  const Plan& p;
+  const BwdArgs& a;
+  int n_iter;
+  long long sm;  // per-head stride of the scratch matrices
+  BwdChain(const Plan& p_, const BwdArgs& a_, int n) : p(p_), a(a_), n_iter(n), sm((long long)bwd_mm_mats(n) * MM) {}
+  float* Z(int k) const { return a.mm + k * MM; }
+  float* X(int k) const { return a.mm + (n_iter + 1 + 3 * k) * MM; }
+  float* X2(int k) const { return X(k) + MM; }
+  float* P(int k) const { return X(k) + 2 * MM; }
+  float* G() const { return a.mm + (4 * n_iter + 1) * MM; }
+  // op(x) is R x K and op(y) is K x N
+  static ChainTerm term(const float* x, long long sx, bool tx, const float* y, long long sy, bool ty, float alpha,
+                        const ChainOut& o) {
     ChainTerm t{};
     t.a = x;
     t.b = y;
@@ -102,8 +97,8 @@ int launch_bwd_chain(const Plan& p, const BwdArgs& a, int n_iter, hipStream_t st
     t.ldb = ty ? o.K : o.N;
     t.alpha = alpha;
     return t;
-  };
-  auto out = [](float* c, long long sc, int R, int N, int K, float beta) {
+  }
+  static ChainOut out(float* c, long long sc, int R, int N, int K, float beta) {
     ChainOut o{};
     o.c = c;
     o.sc = sc;
@@ -113,8 +108,8 @@ int launch_bwd_chain(const Plan& p, const BwdArgs& a, int n_iter, hipStream_t st
     o.ldc = N;
     o.beta = beta;
     return o;
-  };
-  auto go = [&](const ChainOut& o0, const ChainOut* o1) {
+  }
+  hipError_t go(const ChainOut& o0, const ChainOut* o1, hipStream_t st) const {
     ChainLaunch L{};
     L.o[0] = o0;
     L.tiles0 = chain_tiles(o0.R, o0.N);
@@ -123,68 +118,88 @@ int launch_bwd_chain(const Plan& p, const BwdArgs& a, int n_iter, hipStream_t st
       L.o[1] = *o1;
       tiles += chain_tiles(o1->R, o1->N);
     }
-    return launch("k_bwd_chain", k_bwd_chain<KMAX>, dim3(tiles, p.BH), dim3(256), (uint32_t)lds, st, L);
-  };
-  for (int k = 0; k < n_iter; ++k) {
-    ChainOut o = out(X(k), sm, M, M, M, 0.f);  // X = A Z
-    o.t[o.nt++] = term(a.A, MM, false, Z(k), sm, false, 1.f, o);
-    HIP_TRY(go(o, nullptr));
-    o = out(X2(k), sm, M, M, M, 0.f);  // X^2
-    o.t[o.nt++] = term(X(k), sm, false, X(k), sm, false, 1.f, o);
-    HIP_TRY(go(o, nullptr));
-    o = out(P(k), sm, M, M, M, 0.f);  // P = 13I - 15X + 7X^2 - X^3
-    o.t[o.nt++] = term(X(k), sm, false, X2(k), sm, false, -1.f, o);
-    o.e1 = X(k);
-    o.g1 = -15.f;
-    o.e2 = X2(k);
-    o.g2 = 7.f;
-    o.eye = 13.f;
-    HIP_TRY(go(o, nullptr));
-    o = out(Z(k + 1), sm, M, M, M, 0.f);  // Z <- Z P / 4
-    o.t[o.nt++] = term(Z(k), sm, false, P(k), sm, false, 0.25f, o);
-    HIP_TRY(go(o, nullptr));
+    return launch("k_bwd_chain", k_bwd_chain<KMAX>, dim3(tiles, p.BH), dim3(256), (uint32_t)chain_lds_bytes<KMAX>(),
+                  st, L);
   }
-  {
-    ChainOut o0 = out(G, sm, M, M, D, 0.f);  // dZ_n = dW BV^T
-    o0.t[o0.nt++] = term(a.dW, MD, false, a.BV, MD, true, 1.f, o0);
-    ChainOut o1 = out(a.dBV, MD, M, D, M, 0.f);  // dBV = Z_n^T dW
-    o1.t[o1.nt++] = term(Z(n_iter), sm, true, a.dW, MD, false, 1.f, o1);
-    HIP_TRY(go(o0, &o1));
+  int forward(hipStream_t st) const {
+    HIP_TRY(launch("k_bwd_chain_init", k_bwd_chain_init<M>, dim3((unsigned)((MM + 255) / 256), p.BH), dim3(256), 0,
+                   st, a));
+    HIP_TRY(allow_lds(k_bwd_chain<KMAX>, chain_lds_bytes<KMAX>()));
+    for (int k = 0; k < n_iter; ++k) {
+      ChainOut o = out(X(k), sm, M, M, M, 0.f);  // X = A Z
+      o.t[o.nt++] = term(a.A, MM, false, Z(k), sm, false, 1.f, o);
+      HIP_TRY(go(o, nullptr, st));
+      o = out(X2(k), sm, M, M, M, 0.f);  // X^2
+      o.t[o.nt++] = term(X(k), sm, false, X(k), sm, false, 1.f, o);
+      HIP_TRY(go(o, nullptr, st));
+      o = out(P(k), sm, M, M, M, 0.f);  // P = 13I - 15X + 7X^2 - X^3
+      o.t[o.nt++] = term(X(k), sm, false, X2(k), sm, false, -1.f, o);
+      o.e1 = X(k);
+      o.g1 = -15.f;
+      o.e2 = X2(k);
+      o.g2 = 7.f;
+      o.eye = 13.f;
+      HIP_TRY(go(o, nullptr, st));
+      o = out(Z(k + 1), sm, M, M, M, 0.f);  // Z <- Z P / 4
+      o.t[o.nt++] = term(Z(k), sm, false, P(k), sm, false, 0.25f, o);
+      HIP_TRY(go(o, nullptr, st));
+    }
+    return NYS_OK;
   }
-  float* g = G;
-  float* gn = Gn;
-  for (int k = n_iter - 1; k >= 0; --k) {
-    ChainOut o0 = out(gn, sm, M, M, M, 0.f);
-    o0.t[o0.nt++] = term(g, sm, false, P(k), sm, true, 0.25f, o0);
-    ChainOut o1 = out(dP, sm, M, M, M, 0.f);
-    o1.t[o1.nt++] = term(Z(k), sm, true, g, sm, false, 0.25f, o1);
-    HIP_TRY(go(o0, &o1));
-    o0 = out(T, sm, M, M, M, 0.f);
-    o0.t[o0.nt++] = term(X(k), sm, true, dP, sm, false, 1.f, o0);
-    o1 = out(dX, sm, M, M, M, 0.f);
-    o1.t[o1.nt++] = term(dP, sm, false, X(k), sm, true, 7.f, o1);
-    o1.t[o1.nt++] = term(X(k), sm, true, dP, sm, false, 7.f, o1);
-    o1.t[o1.nt++] = term(dP, sm, false, X2(k), sm, true, -1.f, o1);
-    o1.t[o1.nt++] = term(X2(k), sm, true, dP, sm, false, -1.f, o1);
-    o1.e1 = dP;
-    o1.g1 = -15.f;
-    HIP_TRY(go(o0, &o1));
-    o0 = out(dX, sm, M, M, M, 1.f);
-    o0.t[o0.nt++] = term(T, sm, false, X(k), sm, true, -1.f, o0);
-    HIP_TRY(go(o0, nullptr));
-    o0 = out(dA, sm, M, M, M, 1.f);
-    o0.t[o0.nt++] = term(dX, sm, false, Z(k), sm, true, 1.f, o0);
-    o1 = out(gn, sm, M, M, M, 1.f);
-    o1.t[o1.nt++] = term(a.A, MM, true, dX, sm, false, 1.f, o1);
-    HIP_TRY(go(o0, &o1));
-    float* const t = g;
-    g = gn;
-    gn = t;
+  // after the token pass on st; the forward half joins through fwd_done
+  int backward(hipStream_t st, hipEvent_t fwd_done) const {
+    static_assert(M * D % 4 == 0, "four-element groups");
+    HIP_TRY(launch("k_bwd_chain_sum", k_bwd_chain_sum<M, D>, dim3((unsigned)((MD + 255) / 256), p.BH), dim3(256), 0,
+                   st, a));
+    if (fwd_done != nullptr) HIP_TRY(hipStreamWaitEvent(st, fwd_done, 0));
+    float* const Gm = G();
+    float* const Gn = Gm + MM;
+    float* const dP = Gm + 2 * MM;
+    float* const dX = Gm + 3 * MM;
+    float* const T = Gm + 4 * MM;
+    float* const dA = Gm + 5 * MM;
+    {
+      ChainOut o0 = out(Gm, sm, M, M, D, 0.f);  // dZ_n = dW BV^T
+      o0.t[o0.nt++] = term(a.dW, MD, false, a.BV, MD, true, 1.f, o0);
+      ChainOut o1 = out(a.dBV, MD, M, D, M, 0.f);  // dBV = Z_n^T dW
+      o1.t[o1.nt++] = term(Z(n_iter), sm, true, a.dW, MD, false, 1.f, o1);
+      HIP_TRY(go(o0, &o1, st));
+    }
+    float* g = Gm;
+    float* gn = Gn;
+    for (int k = n_iter - 1; k >= 0; --k) {
+      ChainOut o0 = out(gn, sm, M, M, M, 0.f);
+      o0.t[o0.nt++] = term(g, sm, false, P(k), sm, true, 0.25f, o0);
+      ChainOut o1 = out(dP, sm, M, M, M, 0.f);
+      o1.t[o1.nt++] = term(Z(k), sm, true, g, sm, false, 0.25f, o1);
+      HIP_TRY(go(o0, &o1, st));
+      o0 = out(T, sm, M, M, M, 0.f);
+      o0.t[o0.nt++] = term(X(k), sm, true, dP, sm, false, 1.f, o0);
+      o1 = out(dX, sm, M, M, M, 0.f);
+      o1.t[o1.nt++] = term(dP, sm, false, X(k), sm, true, 7.f, o1);
+      o1.t[o1.nt++] = term(X(k), sm, true, dP, sm, false, 7.f, o1);
+      o1.t[o1.nt++] = term(dP, sm, false, X2(k), sm, true, -1.f, o1);
+      o1.t[o1.nt++] = term(X2(k), sm, true, dP, sm, false, -1.f, o1);
+      o1.e1 = dP;
+      o1.g1 = -15.f;
+      HIP_TRY(go(o0, &o1, st));
+      o0 = out(dX, sm, M, M, M, 1.f);
+      o0.t[o0.nt++] = term(T, sm, false, X(k), sm, true, -1.f, o0);
+      HIP_TRY(go(o0, nullptr, st));
+      o0 = out(dA, sm, M, M, M, 1.f);
+      o0.t[o0.nt++] = term(dX, sm, false, Z(k), sm, true, 1.f, o0);
+      o1 = out(gn, sm, M, M, M, 1.f);
+      o1.t[o1.nt++] = term(a.A, MM, true, dX, sm, false, 1.f, o1);
+      HIP_TRY(go(o0, &o1, st));
+      float* const t = g;
+      g = gn;
+      gn = t;
+    }
+    const int gsel = 4 * n_iter + 1 + (g == Gm ? 0 : 1);
+    HIP_TRY(launch("k_bwd_chain_post", k_bwd_chain_post<M>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a, gsel));
+    return NYS_OK;
   }
-  const int gsel = 4 * n_iter + 1 + (g == G ? 0 : 1);
-  HIP_TRY(launch("k_bwd_chain_post", k_bwd_chain_post<M>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a, gsel));
-  return NYS_OK;
-}
+};
 
 template <typename IO, int M, int D>
 int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* q, const void* k, const void* v,
@@ -239,14 +254,15 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   a.n_iter = n_iter;
   a.init_option = init_option;
   a.s4 = 1.0f / sqrtf(sqrtf((float)D));
-  // Side stream: for 64 landmarks the forward half of the per-head chain
-  // (it needs only A) runs beside the token pass, which leaves CUs free;
-  // then the conv's backward (it needs only dout, v and the weights) runs
-  // beside the rest of the chain (one workgroup per head).  Both join back
-  // before the kernels that read their results.
-  constexpr bool SPLIT = M == 64;
+  // Side stream: the forward half of the pseudo-inverse backward (it needs
+  // only A and c: one workgroup per head at 64 landmarks, the launch chain
+  // above) runs beside the token pass; then the conv's backward (it needs
+  // only dout, v and the weights) runs beside the rest of the chain.  Both
+  // join back before the kernels that read their results.
+  constexpr bool SPLIT = M == 64, CHAIN = M > 64;
+  const BwdChain<M, D> chain(p, a, n_iter);
   Side* sd = nullptr;
-  if (SPLIT || conv_w != nullptr) {
+  if (SPLIT || CHAIN || conv_w != nullptr) {
     rc = get_side(&sd);
     if (rc != NYS_OK) return rc;
     HIP_TRY(hipEventRecord(sd->fork, st));
@@ -255,6 +271,11 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   if constexpr (SPLIT) {
     HIP_TRY(allow_lds(k_bwd_mm1f64, BWD_MM64_LDS));
     HIP_TRY(launch("k_bwd_mm1f", k_bwd_mm1f64, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM64_LDS, sd->st, a));
+    HIP_TRY(hipEventRecord(sd->mid, sd->st));
+  }
+  if constexpr (CHAIN) {
+    rc = chain.forward(sd->st);
+    if (rc != NYS_OK) return rc;
     HIP_TRY(hipEventRecord(sd->mid, sd->st));
   }
   if constexpr (bwd_tok2(M, D)) {
@@ -294,8 +315,8 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
       HIP_TRY(allow_lds(k_bwd_mm1b64<D>, BWD_MM1B_LDS));
       HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1b64<D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)BWD_MM1B_LDS, st, a));
     }
-  } else if constexpr (M > 64) {
-    rc = launch_bwd_chain<M, D>(p, a, n_iter, st);
+  } else if constexpr (CHAIN) {
+    rc = chain.backward(st, sd->mid);
     if (rc != NYS_OK) return rc;
   } else {
     HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));

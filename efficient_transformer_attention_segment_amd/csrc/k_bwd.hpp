@@ -1293,10 +1293,10 @@ __global__ __launch_bounds__(256) void k_bwd_chain(ChainLaunch L) {
   }
 }
 
-// Start of the chain: dW and dKt (F part) from the token-chunk partials,
-// Z_0 = A^T / c and dA = 0.  grid (ceil(M M / 256), BH), block 256.
-template <int M, int D>
-__global__ __launch_bounds__(256) void k_bwd_chain_pre(BwdArgs a) {
+// Start of the chain (it needs only A and c): Z_0 = A^T / c and dA = 0.
+// grid (ceil(M M / 256), BH), block 256.
+template <int M>
+__global__ __launch_bounds__(256) void k_bwd_chain_init(BwdArgs a) {
   constexpr int MM = M * M;
   const int bh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
@@ -1304,10 +1304,39 @@ __global__ __launch_bounds__(256) void k_bwd_chain_pre(BwdArgs a) {
     S[e] = a.A[(size_t)bh * MM + (e % M) * M + e / M] / a.cscale[bh];
     S[(size_t)(4 * a.n_iter + 1 + 5) * MM + e] = 0.f;  // dA
   }
-  if (4 * e < M * D) {
-    const size_t off = (size_t)bh * a.nct * M * D + 4 * e;
-    *reinterpret_cast<float4*>(a.dW + (size_t)bh * M * D + 4 * e) = sum_chunks4(a.pw + off, (size_t)M * D, a.nct);
-    *reinterpret_cast<float4*>(a.dKt + (size_t)bh * M * D + 4 * e) = sum_chunks4(a.pk + off, (size_t)M * D, a.nct);
+}
+
+// dW and dKt (F part) from the token-chunk partials: wave p of a workgroup
+// sums chunks p, p + 4, p + 8, ... (in that order) of 64 four-element
+// groups, then the four sums are added in wave order.  grid
+// (ceil(M D / 256), BH), block 256.
+template <int M, int D>
+__global__ __launch_bounds__(256) void k_bwd_chain_sum(BwdArgs a) {
+  constexpr int MD = M * D, NP = 4;
+  __shared__ float4 part[NP][2][64];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int q = 4 * (blockIdx.x * 64 + lane);  // first element of the group
+  float4 sw = make_float4(0.f, 0.f, 0.f, 0.f), sk = sw;
+  if (q < MD) {
+    const size_t off = ((size_t)bh * a.nct + p) * MD + q;
+    const int cnt = (a.nct - p + NP - 1) / NP;
+    sw = sum_chunks4(a.pw + off, (size_t)NP * MD, cnt);
+    sk = sum_chunks4(a.pk + off, (size_t)NP * MD, cnt);
+  }
+  part[p][0][lane] = sw;
+  part[p][1][lane] = sk;
+  __syncthreads();
+  if (p < 2 && q < MD) {
+    float4 t = part[0][p][lane];
+#pragma unroll
+    for (int u = 1; u < NP; ++u) {
+      const float4 x = part[u][p][lane];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    *reinterpret_cast<float4*>((p == 0 ? a.dW : a.dKt) + (size_t)bh * MD + q) = t;
   }
 }
 
