@@ -67,7 +67,8 @@ inline BwdPlan make_bwd_plan(const Plan& p, int n_iter, int conv_k, bool conv) {
 //   T = X^T dP and dX = 7 dP X^T + 7 X^T dP - dP (X^2)^T - (X^2)^T dP - 15 dP;
 //   dX -= T X^T;
 //   dA += dX Z^T and dZ_k += A^T dX;
-// and the end (k_bwd_chain_post).  The same products and scratch layout as
+// and the end (k_bwd_chain_post, k_bwd_chain_dc; A's statistics come from
+// k_bwd_chain_stats in the forward half).  The same products and scratch layout as
 // k_bwd_mm1 (the matrices of a head at a.mm + h * bwd_mm_mats(n_iter) M^2).
 template <int M, int D>
 struct BwdChain {
@@ -124,6 +125,7 @@ struct BwdChain {
   int forward(hipStream_t st) const {
     HIP_TRY(launch("k_bwd_chain_init", k_bwd_chain_init<M>, dim3((unsigned)((MM + 255) / 256), p.BH), dim3(256), 0,
                    st, a));
+    HIP_TRY(launch("k_bwd_chain_stats", k_bwd_chain_stats<M>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a));
     HIP_TRY(allow_lds(k_bwd_chain<KMAX>, chain_lds_bytes<KMAX>()));
     for (int k = 0; k < n_iter; ++k) {
       ChainOut o = out(X(k), sm, M, M, M, 0.f);  // X = A Z
@@ -196,7 +198,9 @@ struct BwdChain {
       gn = t;
     }
     const int gsel = 4 * n_iter + 1 + (g == Gm ? 0 : 1);
-    HIP_TRY(launch("k_bwd_chain_post", k_bwd_chain_post<M>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a, gsel));
+    HIP_TRY(launch("k_bwd_chain_post", k_bwd_chain_post<M>, dim3((M / 32) * (M / 32), p.BH), dim3(256), 0, st, a,
+                   gsel));
+    HIP_TRY(launch("k_bwd_chain_dc", k_bwd_chain_dc<M>, dim3(p.BH), dim3(64), 0, st, a));
     return NYS_OK;
   }
 };

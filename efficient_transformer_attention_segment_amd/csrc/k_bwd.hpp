@@ -1040,30 +1040,14 @@ __device__ __forceinline__ void bgemm_h(float* C, const float* Ag, bool ta, cons
     bgemm<R, N, K>(C, Ag, ta, Bg, tb, alpha, beta, La, Lb);
 }
 
-// The end of the pseudo-inverse backward of head bh, given the gradient g
-// reaching Z_0 = A^T / c: dA += g^T / c, dc = -sum(g A^T) / c^2, the
-// maximum column sum of A with its column and the maximum row sum.
-// BWD_MM_NT threads; g and dA are written before the call.
+// A's maximum column sum with its column, and its maximum row sum (head bh).
+// BWD_MM_NT threads.
 template <int M>
-__device__ void mm1_tail(const BwdArgs& a, int bh, const float* A, const float* g, float* dA, float c) {
-  constexpr int MM = M * M, NT = BWD_MM_NT;
+__device__ void mm1_stats(const BwdArgs& a, int bh, const float* A) {
+  constexpr int NT = BWD_MM_NT;
   const int tid = threadIdx.x;
-  float part = 0.f;
-  for (int i = tid; i < MM; i += NT) {
-    const int r = i / M, col = i % M;
-    dA[i] += g[col * M + r] / c;
-    part += g[col * M + r] * A[i];
-  }
   __shared__ float red[NT];
   __shared__ int redj[NT];
-  red[tid] = part;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const float dcv = -red[0] / (c * c);
-  __syncthreads();
   float cs = -1.f, rs = 0.f;
   int cj = 0;
   if (tid < M) {
@@ -1083,7 +1067,6 @@ __device__ void mm1_tail(const BwdArgs& a, int bh, const float* A, const float* 
     __syncthreads();
   }
   if (tid == 0) {
-    a.dc[bh] = dcv;
     a.cmax[bh] = red[0];
     a.cmaxj[bh] = redj[0];
   }
@@ -1095,6 +1078,32 @@ __device__ void mm1_tail(const BwdArgs& a, int bh, const float* A, const float* 
     __syncthreads();
   }
   if (tid == 0) a.rmax[bh] = red[0];
+}
+
+// The end of the pseudo-inverse backward of head bh, given the gradient g
+// reaching Z_0 = A^T / c: dA += g^T / c, dc = -sum(g A^T) / c^2, and A's
+// statistics (mm1_stats).  BWD_MM_NT threads; g and dA are written before
+// the call.
+template <int M>
+__device__ void mm1_tail(const BwdArgs& a, int bh, const float* A, const float* g, float* dA, float c) {
+  constexpr int MM = M * M, NT = BWD_MM_NT;
+  const int tid = threadIdx.x;
+  float part = 0.f;
+  for (int i = tid; i < MM; i += NT) {
+    const int r = i / M, col = i % M;
+    dA[i] += g[col * M + r] / c;
+    part += g[col * M + r] * A[i];
+  }
+  __shared__ float dred[NT];
+  dred[tid] = part;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s) dred[tid] += dred[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) a.dc[bh] = -dred[0] / (c * c);
+  __syncthreads();
+  mm1_stats<M>(a, bh, A);
 }
 
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().
@@ -1340,15 +1349,68 @@ __global__ __launch_bounds__(256) void k_bwd_chain_sum(BwdArgs a) {
   }
 }
 
-// End of the chain: mm1_tail with the gradient reaching Z_0 in matrix gsel
-// of the scratch (the G or Gn slot).  grid BH, block BWD_MM_NT.
+// A's statistics for the chain (they need only A).  grid BH, block
+// BWD_MM_NT.
 template <int M>
-__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_chain_post(BwdArgs a, int gsel) {
-  constexpr int MM = M * M;
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(BWD_MM_NT) void k_bwd_chain_stats(BwdArgs a) {
+  mm1_stats<M>(a, blockIdx.x, a.A + (size_t)blockIdx.x * M * M);
+}
+
+// End of the chain, with g the gradient reaching Z_0 (matrix gsel of the
+// scratch, the G or Gn slot): dA += g^T / c over 32 x 32 tiles (g's tile
+// transposed through LDS), and per tile the partial sum of g^T * A for dc
+// (into the dX slot, which the chain no longer needs).  grid ((M / 32)^2,
+// BH), block 256.
+template <int M>
+__global__ __launch_bounds__(256) void k_bwd_chain_post(BwdArgs a, int gsel) {
+  constexpr int MM = M * M, TPR = M / 32;
+  static_assert(M % 32 == 0, "whole 32 x 32 tiles");
+  __shared__ float tg[32][33];
+  __shared__ float red[256];
+  const int bh = blockIdx.y, tid = threadIdx.x, blk = blockIdx.x;
+  const int r0 = 32 * (blk / TPR), c0 = 32 * (blk % TPR);
   float* const S = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM;
-  mm1_tail<M>(a, bh, a.A + (size_t)bh * MM, S + (size_t)gsel * MM, S + (size_t)(4 * a.n_iter + 1 + 5) * MM,
-              a.cscale[bh]);
+  const float* const g = S + (size_t)gsel * MM;
+  float* const dA = S + (size_t)(4 * a.n_iter + 1 + 5) * MM;
+  const float* const A = a.A + (size_t)bh * MM;
+  const float c = a.cscale[bh];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e, y = idx / 32, x = idx % 32;
+    tg[y][x] = g[(size_t)(c0 + y) * M + r0 + x];
+  }
+  __syncthreads();
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e, y = idx / 32, x = idx % 32;
+    const size_t i = (size_t)(r0 + y) * M + c0 + x;
+    const float gv = tg[x][y];  // g[c0 + x][r0 + y]
+    dA[i] += gv / c;
+    part += gv * A[i];
+  }
+  red[tid] = part;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) S[(size_t)(4 * a.n_iter + 1 + 3) * MM + blk] = red[0];
+}
+
+// dc = -sum(g A^T) / c^2 from the tiles' partial sums, in tile order.
+// grid BH, block 64.
+template <int M>
+__global__ __launch_bounds__(64) void k_bwd_chain_dc(BwdArgs a) {
+  constexpr int MM = M * M, NB = (M / 32) * (M / 32);
+  const int bh = blockIdx.x;
+  const float* const p = a.mm + (size_t)bh * bwd_mm_mats(a.n_iter) * MM + (size_t)(4 * a.n_iter + 1 + 3) * MM;
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int i = 0; i < NB; ++i) s += p[i];
+    const float c = a.cscale[bh];
+    a.dc[bh] = -s / (c * c);
+  }
 }
 
 // Product on operands already in LDS (row strides lda, ldb; flat
