@@ -289,7 +289,8 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   } else if constexpr (bwd_tok3(M, D)) {
     constexpr int tl = BwdTok3Layout<M>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok3<IO, M>, tl));
-    HIP_TRY(launch("k_bwd_tok", k_bwd_tok3<IO, M>, dim3(bp.nct, p.BH), dim3(256), (uint32_t)tl, st, a));
+    HIP_TRY(launch("k_bwd_tok", k_bwd_tok3<IO, M>, dim3(bp.nct, p.BH), dim3(64 * BwdTok3Layout<M>::NW), (uint32_t)tl,
+                   st, a));
   } else {
     constexpr int tl = BwdTokLayout<M, D>::BYTES;
     HIP_TRY(allow_lds(k_bwd_tok<IO, M, D>, tl));

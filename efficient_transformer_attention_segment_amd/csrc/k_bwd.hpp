@@ -397,18 +397,18 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Token pass for head size 64 above 64 landmarks: four waves share each
+// Token pass for head size 64 above 64 landmarks: eight waves share each
 // 32-token group, Kt (and W where it fits) stay in LDS for the whole chunk,
 // and every wave holds its share of the dW / dKt tiles in registers:
 //   S = Qs Kt^T and dF = dout W^T tile by tile into LDS (the 2 x M/16 tile
-//   pairs dealt over the waves), the row softmax there (eight lanes per
-//   row), dS = F (dF - D_t); dQs = dS Kt (eight 16 x 16 tiles, two per
+//   pairs dealt over the waves), the row softmax there (sixteen lanes per
+//   row), dS = F (dF - D_t); dQs = dS Kt (eight 16 x 16 tiles, one per
 //   wave); dW += F^T dout and dKt += dS^T Qs over the group's tokens
-//   (2 M/16 x 4 tiles, M/8 per wave).
+//   (2 M/16 x 4 tiles, M/16 per wave).
 // Float32 matrix-core products (mm16) over float32 LDS operands.
 template <int M>
 struct BwdTok3Layout {
-  static constexpr int D = 64, NW = 4, GT = 32, LDF = M + 4, LD = D + 4;
+  static constexpr int D = 64, NW = 8, GT = 32, LDF = M + 4, LD = D + 4;
   static constexpr int OFF_KT = 0;
   static constexpr int OFF_Q = OFF_KT + M * LD;
   static constexpr int OFF_DO = OFF_Q + GT * LD;
@@ -421,14 +421,16 @@ struct BwdTok3Layout {
   static_assert(BYTES <= 160 * 1024, "k_bwd_tok3 LDS");
 };
 
-// grid (nct, BH), block 256.
+// grid (nct, BH), block 64 BwdTok3Layout::NW.
 template <typename IO, int M>
-__global__ __launch_bounds__(256) void k_bwd_tok3(BwdArgs a) {
+__global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs a) {
   extern __shared__ __align__(16) float bw_lds[];
   using Ly = BwdTok3Layout<M>;
   constexpr int D = 64, NW = Ly::NW, GT = Ly::GT, LDF = Ly::LDF, LD = Ly::LD, TM = M / 16, CT = D / 16;
   constexpr int NACC = 2 * TM * CT / NW;
+  constexpr int NTH = 64 * NW, LPR = NTH / GT;  // threads; lanes per row in the softmax
   static_assert((2 * TM * CT) % NW == 0 && M % 16 == 0, "every wave owns the same number of tiles");
+  static_assert(NTH >= 8 * GT && LPR <= 64 && (LPR & (LPR - 1)) == 0, "staging and softmax lane layout");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, chunk = blockIdx.x;
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) void k_bwd_tok3(BwdArgs a) {
   float* const Wl = bw_lds + Ly::OFF_W;
   const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
   constexpr int WLD = Ly::W_LDS ? LD : D;
-  for (int i = tid; i < M * D / 4; i += 256) {
+  for (int i = tid; i < M * D / 4; i += NTH) {
     const int r = i / (D / 4), c = 4 * (i % (D / 4));
     *reinterpret_cast<float4*>(Kt + r * LD + c) = *reinterpret_cast<const float4*>(Ktg + (size_t)r * D + c);
     if constexpr (Ly::W_LDS)
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(256) void k_bwd_tok3(BwdArgs a) {
   for (int j = 0; j < NACC; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int gs = t0; gs < t1; gs += GT) {
     // q (scaled) and dout rows of the group: eight lanes per token, eight channels each
-    {
+    if (tid < 8 * GT) {
       const int r = tid >> 3, c0 = 8 * (tid & 7), tok = gs + r;
       float xq[8], xo[8];
       if (tok < t1) {
@@ -488,42 +490,38 @@ __global__ __launch_bounds__(256) void k_bwd_tok3(BwdArgs a) {
       }
     }
     __syncthreads();
-    // row softmax and dS, eight lanes per row
+    // row softmax and dS, LPR lanes per row
     {
-      const int row = tid >> 3, q8 = tid & 7;
+      const int row = tid / LPR, q = tid % LPR;
       float* const fr = Fg + row * LDF;
       float* const dr = DSg + row * LDF;
       float mx = -INFINITY;
-      for (int c = q8; c < M; c += 8) mx = fmaxf(mx, fr[c]);
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      for (int c = q; c < M; c += LPR) mx = fmaxf(mx, fr[c]);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       float s = 0.f;
-      for (int c = q8; c < M; c += 8) {
+      for (int c = q; c < M; c += LPR) {
         const float e = __expf(fr[c] - mx);
         fr[c] = e;
         s += e;
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
       const float inv = 1.0f / s;
       float dt = 0.f;
-      for (int c = q8; c < M; c += 8) {
+      for (int c = q; c < M; c += LPR) {
         const float fv = fr[c] * inv;
         fr[c] = fv;
         dt += fv * dr[c];
       }
-      dt += __shfl_xor(dt, 1);
-      dt += __shfl_xor(dt, 2);
-      dt += __shfl_xor(dt, 4);
-      for (int c = q8; c < M; c += 8) dr[c] = fr[c] * (dr[c] - dt);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) dt += __shfl_xor(dt, o);
+      for (int c = q; c < M; c += LPR) dr[c] = fr[c] * (dr[c] - dt);
     }
     __syncthreads();
-    // dQs = dS Kt: tiles (token tile, channel tile), two per wave
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int p = wave + NW * u, tt = p / CT, ct = p % CT;
+    // dQs = dS Kt: tiles (token tile, channel tile) dealt over the waves
+    for (int p = wave; p < 2 * CT; p += NW) {
+      const int tt = p / CT, ct = p % CT;
       const f32x4 c = mm16<M>(DSg + 16 * tt * LDF, LDF, 1, Kt + 16 * ct, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
