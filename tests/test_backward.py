@@ -137,14 +137,20 @@ def test_backward_workload(idx):
     _check(f"workload{idx}", x, w.dtype, w.m, w.n_iter, w.init_option, seed=10 + idx)
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("m", [64, 128, 256])
+def test_backward_deterministic(m):
+    """Repeated calls give identical gradients (fixed reduction orders; above
+    64 landmarks the launch chain, the side stream and, above 128, the key
+    pass's first-half buffer)."""
     import torch
 
     import efficient_transformer_attention_segment_amd as nys
-    x = make_custom(2, 2, 512, 64, seed=999, dtype="bf16", lengths=[512, 300])
+    n = max(512, 4 * m)
+    x = make_custom(2, 2, n, 64, seed=999 + m, dtype="bf16", lengths=[n, (3 * n) // 5])
     do = to_dev(_dout(x["q"].shape, 5, "bf16"), "bf16")
     args = [to_dev(x[n_], "bf16") for n_ in ("q", "k", "v")]
-    outs = [nys.attention_backward(*args, do, to_dev(x["key_mask"], None), to_dev(x["conv_w"], None), m=64)
+    announce(f"backward deterministic m{m} n{n}")
+    outs = [nys.attention_backward(*args, do, to_dev(x["key_mask"], None), to_dev(x["conv_w"], None), m=m)
             for _ in range(3)]
     torch.cuda.synchronize()
     for o in outs[1:]:
@@ -152,7 +158,8 @@ def test_backward_deterministic():
             assert torch.equal(a_, b_)
 
 
-def test_backward_user_streams():
+@pytest.mark.parametrize("m", [64, 256])
+def test_backward_user_streams(m):
     """Calls on two user streams (each with its own workspace; the library's
     side stream forks from and joins back into the calling stream) give the
     default stream's results bit for bit, with the calls of both streams in
@@ -160,12 +167,13 @@ def test_backward_user_streams():
     import torch
 
     import efficient_transformer_attention_segment_amd as nys
-    x = make_custom(2, 3, 512, 64, seed=1020, dtype="bf16", lengths=[512, 333])
+    n = max(512, 4 * m)
+    x = make_custom(2, 3, n, 64, seed=1020 + m, dtype="bf16", lengths=[n, (2 * n) // 3])
     do = to_dev(_dout(x["q"].shape, 6, "bf16"), "bf16")
     args = [to_dev(x[n_], "bf16") for n_ in ("q", "k", "v")]
     km, cw = to_dev(x["key_mask"], None), to_dev(x["conv_w"], None)
-    announce("backward user streams")
-    ref = nys.attention_backward(*args, do, km, cw, m=64)
+    announce(f"backward user streams m{m} n{n}")
+    ref = nys.attention_backward(*args, do, km, cw, m=m)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
@@ -173,7 +181,7 @@ def test_backward_user_streams():
         s = s1 if i % 2 == 0 else s2
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            outs.append(nys.attention_backward(*args, do, km, cw, m=64, stream=s))
+            outs.append(nys.attention_backward(*args, do, km, cw, m=m, stream=s))
     torch.cuda.synchronize()
     for o in outs:
         for a_, b_ in zip(o, ref):
