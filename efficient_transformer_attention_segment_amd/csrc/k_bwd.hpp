@@ -1215,28 +1215,43 @@ constexpr int chain_lds_bytes() {
 
 // Rows [r0, r0 + 32) of op(X) (K columns) into dst[32][K + 4]; X is stored
 // K x rows (trans) or rows x K, row stride ld.  Rows at or past nrows are
-// skipped (no wave reads them).
-__device__ __forceinline__ void chain_stage(float* dst, const float* x, int ld, bool trans, int r0, int nrows,
-                                            int K, int ldl) {
-  const int tid = threadIdx.x;
-  if (!trans) {
-    const int k4 = K / 4;
-    for (int i = tid; i < 32 * k4; i += 256) {
+// skipped (no wave reads them).  chain_load takes a thread's K / 32 16-byte
+// pieces into registers, chain_store puts them in LDS, so both operands'
+// loads are in flight together.
+template <int KMAX>
+__device__ __forceinline__ void chain_load(float4 (&v)[KMAX / 32], const float* x, int ld, bool trans, int r0,
+                                           int nrows, int K) {
+  const int tid = threadIdx.x, npc = 8 * K, k4 = K / 4;  // pieces: 32 rows x K / 4
+#pragma unroll
+  for (int u = 0; u < KMAX / 32; ++u) {
+    const int i = tid + 256 * u;
+    if (!trans) {
       const int rr = i / k4, kq = i % k4;
-      if (r0 + rr < nrows)
-        *reinterpret_cast<float4*>(dst + rr * ldl + 4 * kq) =
-            *reinterpret_cast<const float4*>(x + (size_t)(r0 + rr) * ld + 4 * kq);
-    }
-  } else {
-    // eight lanes per stored row (32 consecutive floats), one row per k
-    for (int i = tid; i < 8 * K; i += 256) {
+      if (i < npc && r0 + rr < nrows) v[u] = *reinterpret_cast<const float4*>(x + (size_t)(r0 + rr) * ld + 4 * kq);
+    } else {
+      // eight lanes per stored row (32 consecutive floats), one row per k
       const int rq = i % 8, k = i / 8;
-      if (r0 + 4 * rq < nrows) {
-        const float4 v = *reinterpret_cast<const float4*>(x + (size_t)k * ld + r0 + 4 * rq);
-        dst[(4 * rq + 0) * ldl + k] = v.x;
-        dst[(4 * rq + 1) * ldl + k] = v.y;
-        dst[(4 * rq + 2) * ldl + k] = v.z;
-        dst[(4 * rq + 3) * ldl + k] = v.w;
+      if (i < npc && r0 + 4 * rq < nrows) v[u] = *reinterpret_cast<const float4*>(x + (size_t)k * ld + r0 + 4 * rq);
+    }
+  }
+}
+template <int KMAX>
+__device__ __forceinline__ void chain_store(float* dst, const float4 (&v)[KMAX / 32], bool trans, int r0, int nrows,
+                                            int K, int ldl) {
+  const int tid = threadIdx.x, npc = 8 * K, k4 = K / 4;
+#pragma unroll
+  for (int u = 0; u < KMAX / 32; ++u) {
+    const int i = tid + 256 * u;
+    if (!trans) {
+      const int rr = i / k4, kq = i % k4;
+      if (i < npc && r0 + rr < nrows) *reinterpret_cast<float4*>(dst + rr * ldl + 4 * kq) = v[u];
+    } else {
+      const int rq = i % 8, k = i / 8;
+      if (i < npc && r0 + 4 * rq < nrows) {
+        dst[(4 * rq + 0) * ldl + k] = v[u].x;
+        dst[(4 * rq + 1) * ldl + k] = v[u].y;
+        dst[(4 * rq + 2) * ldl + k] = v[u].z;
+        dst[(4 * rq + 3) * ldl + k] = v[u].w;
       }
     }
   }
@@ -1264,9 +1279,12 @@ __global__ __launch_bounds__(256) void k_bwd_chain(ChainLaunch L) {
   f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < o.nt; ++t) {
     const ChainTerm& tm = o.t[t];
+    float4 va[KMAX / 32], vb[KMAX / 32];
+    chain_load<KMAX>(va, tm.a + (size_t)bh * tm.sa, tm.lda, tm.ta != 0, r0, o.R, K);
+    chain_load<KMAX>(vb, tm.b + (size_t)bh * tm.sb, tm.ldb, tm.tb == 0, c0, o.N, K);
     __syncthreads();  // the previous product's reads done
-    chain_stage(As, tm.a + (size_t)bh * tm.sa, tm.lda, tm.ta != 0, r0, o.R, K, LDL);
-    chain_stage(Bs, tm.b + (size_t)bh * tm.sb, tm.ldb, tm.tb == 0, c0, o.N, K, LDL);
+    chain_store<KMAX>(As, va, tm.ta != 0, r0, o.R, K, LDL);
+    chain_store<KMAX>(Bs, vb, tm.tb == 0, c0, o.N, K, LDL);
     __syncthreads();
     if (live) {
       const float* pa = As + (16 * it + c16) * LDL + g;
