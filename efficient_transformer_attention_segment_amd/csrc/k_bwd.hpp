@@ -9,10 +9,10 @@
 // intermediates are recomputed (landmarks, A, Z, B V, W and B's row
 // normalisers come from a forward pass without the output), then, per head
 // (head size d = 32 or 64 with up to 256 landmarks, d = 128 with up to 64;
-// float32 accumulation throughout; above 128 landmarks the token pass is
-// split by channel halves at d = 64, the key landmarks and Qt / dBV are read
-// from L2, and the per-head products take their contraction in LDS-sized
-// steps):
+// float32 accumulation throughout; above 64 landmarks at d = 64 the token
+// pass is k_bwd_tok3, above 128 landmarks the key pass takes the landmarks
+// in two halves, and above 64 landmarks the per-head products run as a
+// launch chain over all heads, k_bwd_chain):
 //
 //   k_bwd_dvconv  dv_conv = conv^T(dout) (the forward convolution with the
 //               taps reversed, on the matrix cores);
@@ -20,11 +20,15 @@
 //   k_bwd_tok   per token: F, dF = dout W^T, D_t = sum_j F dF,
 //               dS = F (dF - D_t), dQs = dS Kt; per token chunk partial
 //               sums of dW = F^T dout and dKt = dS^T Qs (k_bwd_tok2 on the
-//               bf16 matrix cores where d <= 64 and m d <= 64 * 64);
+//               bf16 matrix cores where d <= 64 and m d <= 64 * 64;
+//               k_bwd_tok3, eight waves per token group with Kt and W in
+//               LDS, at d = 64 above 64 landmarks);
 //   k_bwd_mm1   per head: dW, dZ = dW BV^T, dBV = Z^T dW, the iteration run
 //               backwards (Z_k, X_k, X_k^2 and P_k = 13I - 15X + 7X^2 - X^3
 //               recomputed in float32 and kept), dA, and the part dc of the
-//               gradient that flows through the initial scale c;
+//               gradient that flows through the initial scale c (above
+//               64 landmarks the same products as the k_bwd_chain launches,
+//               with k_bwd_chain_init / _stats / _sum / _post / _dc);
 //   k_bwd_mm2   c's share of dA (through the maximum column sum: to the
 //               arg-max column, of this head for init option 1, of the one
 //               head holding the maximum over all heads for option 0; the
