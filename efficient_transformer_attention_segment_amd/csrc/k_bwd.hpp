@@ -2403,14 +2403,32 @@ __global__ __launch_bounds__(256) void k_bwd_key2(BwdArgs a) {
     *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(red + i);
 }
 
-// dQt = dQt_A + sum of the key-chunk partials (in chunk order).
-// grid (M * D / 256, BH), block 256: one element per thread.
+// dQt = dQt_A + sum of the key-chunk partials: a workgroup covers 256
+// elements as 64 four-element groups; wave p sums chunks p, p + 4, p + 8,
+// ... (in that order), then dQt_A and the four sums are added in wave
+// order.  grid (M * D / 256, BH), block 256.
 template <int M, int D>
 __global__ __launch_bounds__(256) void k_bwd_qt(BwdArgs a) {
-  const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
-  float s = a.dQt[(size_t)bh * M * D + i];
-  for (int ch = 0; ch < a.nck; ++ch) s += a.pq[((size_t)bh * a.nck + ch) * M * D + i];
-  a.dQt[(size_t)bh * M * D + i] = s;
+  constexpr int MD = M * D, NP = 4;
+  __shared__ float4 part[NP][64];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int q = 4 * (blockIdx.x * 64 + lane);
+  const int cnt = (a.nck - p + NP - 1) / NP;
+  part[p][lane] = sum_chunks4(a.pq + ((size_t)bh * a.nck + p) * MD + q, (size_t)NP * MD, cnt);
+  __syncthreads();
+  if (p == 0) {
+    float4* const dst = reinterpret_cast<float4*>(a.dQt + (size_t)bh * MD + q);
+    float4 t = *dst;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const float4 x = part[u][lane];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+    }
+    *dst = t;
+  }
 }
 
 // dq = d^-1/4 (dQs + dQt[segment] / L).  grid (ceil(n / 64), BH), block 256:
