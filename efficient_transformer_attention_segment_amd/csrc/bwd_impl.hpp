@@ -203,6 +203,17 @@ struct BwdChain {
     HIP_TRY(launch("k_bwd_chain_dc", k_bwd_chain_dc<M>, dim3(p.BH), dim3(64), 0, st, a));
     return NYS_OK;
   }
+  // after k_bwd_mm2<M, D, true> (dS_A in the T slot): dQt_A = dS_A Kt and
+  // dKt += dS_A^T Qt
+  int mm2_products(hipStream_t st) const {
+    const float* const dSA = G() + 4 * MM;
+    ChainOut o0 = out(a.dQt, MD, M, D, M, 0.f);
+    o0.t[o0.nt++] = term(dSA, sm, false, a.kt, MD, false, 1.f, o0);
+    ChainOut o1 = out(a.dKt, MD, M, D, M, 1.f);
+    o1.t[o1.nt++] = term(dSA, sm, true, a.qt, MD, false, 1.f, o1);
+    HIP_TRY(go(o0, &o1, st));
+    return NYS_OK;
+  }
 };
 
 template <typename IO, int M, int D>
@@ -327,8 +338,14 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     HIP_TRY(allow_lds(k_bwd_mm1<M, D>, ml));
     HIP_TRY(launch("k_bwd_mm1", k_bwd_mm1<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
   }
-  HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
-  HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  if constexpr (CHAIN) {
+    HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D, true>, dim3(p.BH), dim3(BWD_MM_NT), 0, st, a));
+    rc = chain.mm2_products(st);
+    if (rc != NYS_OK) return rc;
+  } else {
+    HIP_TRY(allow_lds(k_bwd_mm2<M, D>, ml));
+    HIP_TRY(launch("k_bwd_mm2", k_bwd_mm2<M, D>, dim3(p.BH), dim3(BWD_MM_NT), (uint32_t)ml, st, a));
+  }
   if (conv_w != nullptr) HIP_TRY(hipStreamWaitEvent(st, sd->join, 0));
   if constexpr (bwd_tok2(M, D)) {
     constexpr int kl = BwdKey2Layout<IO, M, D>::BYTES;

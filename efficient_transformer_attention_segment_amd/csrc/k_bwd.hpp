@@ -1876,7 +1876,7 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm1b64(BwdArgs a) {
 // grid BH, block BWD_MM_NT, dynamic LDS bwd_mm_lds_bytes<M, D>().  Row
 // work runs 16 threads to a row (a row's 16 threads are 16 consecutive
 // lanes, reduced with sum16).
-template <int M, int D>
+template <int M, int D, bool CHAINED = false>
 __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
   constexpr int NT = BWD_MM_NT;
   extern __shared__ __align__(16) float bw_lds[];
@@ -1943,9 +1943,14 @@ __global__ __launch_bounds__(BWD_MM_NT) void k_bwd_mm2(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < M / 16; ++u) dSA[r * M + l16 + 16 * u] = av[u] * (dv[u] - s);
   }
-  // dQt_A = dS_A Kt; dKt += dS_A^T Qt (bgemm starts with a block barrier)
-  bgemm_h<M, D, M, M, D>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La, Lb);
-  bgemm_h<M, D, M, M, D>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La, Lb);
+  // dQt_A = dS_A Kt; dKt += dS_A^T Qt (bgemm starts with a block barrier;
+  // CHAINED: one k_bwd_chain launch over all heads after this kernel)
+  if constexpr (!CHAINED) {
+    bgemm_h<M, D, M, M, D>(a.dQt + (size_t)bh * M * D, dSA, false, a.kt + (size_t)bh * M * D, false, 1.f, 0.f, La,
+                           Lb);
+    bgemm_h<M, D, M, M, D>(a.dKt + (size_t)bh * M * D, dSA, true, a.qt + (size_t)bh * M * D, false, 1.f, 1.f, La,
+                           Lb);
+  }
   // D_i = dBV_i . BV_i
   for (int r = tid / 16; r < M; r += RPP) {
     const float* x = a.dBV + ((size_t)bh * M + r) * D;
