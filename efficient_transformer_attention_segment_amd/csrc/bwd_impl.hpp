@@ -272,8 +272,9 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   // Side stream: the forward half of the pseudo-inverse backward (it needs
   // only A and c: one workgroup per head at 64 landmarks, the launch chain
   // above) runs beside the token pass; then the conv's backward (it needs
-  // only dout, v and the weights) runs beside the rest of the chain.  Both
-  // join back before the kernels that read their results.
+  // only dout, v and the weights, and ends with dconv_w) runs beside the
+  // rest of the chain.  Both join back before the kernels that read their
+  // results.
   constexpr bool SPLIT = M == 64, CHAIN = M > 64;
   const BwdChain<M, D> chain(p, a, n_iter);
   Side* sd = nullptr;
@@ -318,6 +319,7 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
     if (dconv_w != nullptr) {
       HIP_TRY(allow_lds(k_bwd_conv<IO, D>, cl));
       HIP_TRY(launch("k_bwd_conv", k_bwd_conv<IO, D>, dim3(bp.ncv, p.BH), dim3(256), (uint32_t)cl, sd->st, a));
+      HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(1024), 0, sd->st, a));
     }
     HIP_TRY(hipEventRecord(sd->join, sd->st));
   }
@@ -359,8 +361,6 @@ int launch_backward(const Plan& p, const BwdPlan& bp, Workspace* w, const void* 
   static_assert((M * D) % 256 == 0, "k_bwd_qt: one element per thread");
   HIP_TRY(launch("k_bwd_qt", k_bwd_qt<M, D>, dim3(M * D / 256, p.BH), dim3(256), 0, st, a));
   HIP_TRY(launch("k_bwd_q", k_bwd_q<IO, M, D>, dim3((p.n + 63) / 64, p.BH), dim3(256), 0, st, a));
-  if (conv_w != nullptr && dconv_w != nullptr)
-    HIP_TRY(launch("k_bwd_wsum", k_bwd_wsum, dim3(p.H), dim3(1024), 0, st, a));
   return NYS_OK;
 }
 
