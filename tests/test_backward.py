@@ -95,6 +95,14 @@ def test_backward_iterations_many_landmarks(dtype, n_iter):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_backward_many_heads_many_landmarks(dtype):
+    """96 heads above 64 landmarks: every launch of the chain covers all
+    heads, and init option 0 takes its maximum over all of them."""
+    x = make_custom(8, 12, 512, 64, seed=1030, dtype=dtype, lengths=[512 - 37 * j for j in range(8)])
+    _check("B8-H12-m128", x, dtype, 128, 6, 0, seed=9)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_backward_conv_sizes_and_empty_row(dtype):
     """Conv kernel sizes 1 and 33, and a batch row with no kept key."""
     for K in (1, 33):
