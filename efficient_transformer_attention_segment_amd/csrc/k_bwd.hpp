@@ -409,7 +409,11 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 //   row), dS = F (dF - D_t); dQs = dS Kt (eight 16 x 16 tiles, one per
 //   wave); dW += F^T dout and dKt += dS^T Qs over the group's tokens
 //   (2 M/16 x 4 tiles, M/16 per wave).
-// Float32 matrix-core products (mm16) over float32 LDS operands.
+// Float32 matrix-core products (mm16) over float32 LDS operands, except
+// dW and dKt at bf16 I/O: there dout and q (staged unscaled, exact bf16;
+// S and the dKt partials take the d^-1/4 instead) are bf16 operands and F,
+// dS split hi + lo, two v_mfma_f32_16x16x32_bf16 per tile over the group's
+// 32 tokens (relative error about 2^-16).
 template <int M>
 struct BwdTok3Layout {
   static constexpr int D = 64, NW = 8, GT = 32, LDF = M + 4, LD = D + 4;
@@ -451,6 +455,8 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
   float* const Wl = bw_lds + Ly::OFF_W;
   const float* const Wsrc = Ly::W_LDS ? Wl : Wg;
   constexpr int WLD = Ly::W_LDS ? LD : D;
+  constexpr bool BF = sizeof(IO) == 2;  // dW / dKt on the bf16 matrix cores
+  const float qs = BF ? 1.f : a.s4;     // the scale staged with q
   for (int i = tid; i < M * D / 4; i += NTH) {
     const int r = i / (D / 4), c = 4 * (i % (D / 4));
     *reinterpret_cast<float4*>(Kt + r * LD + c) = *reinterpret_cast<const float4*>(Ktg + (size_t)r * D + c);
@@ -474,8 +480,8 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
       }
       float* const qd = Qg + r * LD + c0;
       float* const od = DOg + r * LD + c0;
-      *reinterpret_cast<float4*>(qd) = make_float4(xq[0] * a.s4, xq[1] * a.s4, xq[2] * a.s4, xq[3] * a.s4);
-      *reinterpret_cast<float4*>(qd + 4) = make_float4(xq[4] * a.s4, xq[5] * a.s4, xq[6] * a.s4, xq[7] * a.s4);
+      *reinterpret_cast<float4*>(qd) = make_float4(xq[0] * qs, xq[1] * qs, xq[2] * qs, xq[3] * qs);
+      *reinterpret_cast<float4*>(qd + 4) = make_float4(xq[4] * qs, xq[5] * qs, xq[6] * qs, xq[7] * qs);
       *reinterpret_cast<float4*>(od) = make_float4(xo[0], xo[1], xo[2], xo[3]);
       *reinterpret_cast<float4*>(od + 4) = make_float4(xo[4], xo[5], xo[6], xo[7]);
     }
@@ -484,6 +490,7 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
     for (int p = wave; p < 2 * TM; p += NW) {
       const int tt = p & 1, jt = p >> 1;
       f32x4 f = mm16<D>(Qg + 16 * tt * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+      if constexpr (BF) f *= a.s4;
       const f32x4 df = mm16<D>(DOg + 16 * tt * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
       if (16 * jt + c16 >= a.mr) f = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -534,14 +541,41 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
       }
     }
     // dW += F^T dout and dKt += dS^T Qs; tile ti = (landmark tile, channel tile), the dKt tiles after the dW tiles
+    if constexpr (BF) {
+      // a wave's channel tile is the same for all of its tiles (NW % CT == 0):
+      // its dout and q fragments (token 8g + e, channel c16) are formed once
+      static_assert(NW % CT == 0 && GT == 32, "one 16 x 16 x 32 product per tile");
+      const int ctw = wave % CT;
+      bf16x8 bdo, bq;
 #pragma unroll
-    for (int j = 0; j < NACC; ++j) {
-      const int ti = wave + NW * j;
-      const bool isk = ti >= TM * CT;
-      const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
-      const float* A0 = (isk ? DSg : Fg) + 16 * jt;
-      const float* B0 = (isk ? Qg : DOg) + 16 * ct;
-      racc[j] = mm16<GT>(A0, 1, LDF, B0, LD, 1, racc[j]);
+      for (int e = 0; e < 8; ++e) {
+        bdo[e] = (__bf16)DOg[(8 * g + e) * LD + 16 * ctw + c16];
+        bq[e] = (__bf16)Qg[(8 * g + e) * LD + 16 * ctw + c16];
+      }
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) {
+        const int ti = wave + NW * j;
+        const bool isk = ti >= TM * CT;
+        const int jt = (ti % (TM * CT)) / CT;
+        const float* const X = (isk ? DSg : Fg) + 16 * jt + c16;
+        float xa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[e] = X[(8 * g + e) * LDF];
+        const Frag2 fa = split8(xa);
+        const bf16x8 b = isk ? bq : bdo;
+        racc[j] = mfma(fa.hi, b, racc[j]);
+        racc[j] = mfma(fa.lo, b, racc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) {
+        const int ti = wave + NW * j;
+        const bool isk = ti >= TM * CT;
+        const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
+        const float* A0 = (isk ? DSg : Fg) + 16 * jt;
+        const float* B0 = (isk ? Qg : DOg) + 16 * ct;
+        racc[j] = mm16<GT>(A0, 1, LDF, B0, LD, 1, racc[j]);
+      }
     }
     __syncthreads();  // the group's rows free
   }
@@ -553,8 +587,9 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
     const bool isk = ti >= TM * CT;
     const int tt = ti % (TM * CT), jt = tt / CT, ct = tt % CT;
     float* const dst = isk ? pk : pw;
+    const float sc = BF && isk ? a.s4 : 1.f;  // q was staged unscaled
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * D + 16 * ct + c16] = racc[j][r];
+    for (int r = 0; r < 4; ++r) dst[(size_t)(16 * jt + 4 * g + r) * D + 16 * ct + c16] = sc * racc[j][r];
   }
 }
 
