@@ -409,11 +409,12 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 //   row), dS = F (dF - D_t); dQs = dS Kt (eight 16 x 16 tiles, one per
 //   wave); dW += F^T dout and dKt += dS^T Qs over the group's tokens
 //   (2 M/16 x 4 tiles, M/16 per wave).
-// Float32 matrix-core products (mm16) over float32 LDS operands, except
-// dW and dKt at bf16 I/O: there dout and q (staged unscaled, exact bf16;
-// S and the dKt partials take the d^-1/4 instead) are bf16 operands and F,
-// dS split hi + lo, two v_mfma_f32_16x16x32_bf16 per tile over the group's
-// 32 tokens (relative error about 2^-16).
+// Float32 matrix-core products (mm16) over float32 LDS operands, except at
+// bf16 I/O: there S, dF, dW and dKt run on v_mfma_f32_16x16x32_bf16 with
+// dout and q as exact bf16 operands (q staged unscaled; S and the dKt
+// partials take the d^-1/4 instead) and Kt, W, F, dS split hi + lo (two
+// products per 32-element contraction block; relative error about 2^-16).
+// dQs stays on float32 products.
 template <int M>
 struct BwdTok3Layout {
   static constexpr int D = 64, NW = 8, GT = 32, LDF = M + 4, LD = D + 4;
@@ -487,11 +488,42 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
     }
     __syncthreads();  // rows staged (and, the first time, Kt / W)
     // S and dF tile pairs p = (token tile p % 2, landmark tile p / 2): C(token 4g + r, landmark c16)
+    // at bf16 I/O a wave's token tile is p & 1 = wave & 1 for all its pairs
+    // (NW even): its q and dout fragments (token c16, channels 32 kb + 8g + e)
+    // are formed once
+    static_assert(NW % 2 == 0, "a fixed token tile per wave");
+    bf16x8 aq[D / 32], ado[D / 32];
+    if constexpr (BF) {
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const float* const qr = Qg + (16 * (wave & 1) + c16) * LD + 32 * kb + 8 * g;
+        const float* const dr = DOg + (16 * (wave & 1) + c16) * LD + 32 * kb + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          aq[kb][e] = (__bf16)qr[e];
+          ado[kb][e] = (__bf16)dr[e];
+        }
+      }
+    }
     for (int p = wave; p < 2 * TM; p += NW) {
       const int tt = p & 1, jt = p >> 1;
-      f32x4 f = mm16<D>(Qg + 16 * tt * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
-      if constexpr (BF) f *= a.s4;
-      const f32x4 df = mm16<D>(DOg + 16 * tt * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 f, df;
+      if constexpr (BF) {
+        f = df = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+          const Frag2 bk = split8(Kt + (16 * jt + c16) * LD + 32 * kb + 8 * g);
+          const Frag2 bw = split8(Wsrc + (16 * jt + c16) * WLD + 32 * kb + 8 * g);
+          f = mfma(aq[kb], bk.hi, f);
+          f = mfma(aq[kb], bk.lo, f);
+          df = mfma(ado[kb], bw.hi, df);
+          df = mfma(ado[kb], bw.lo, df);
+        }
+        f *= a.s4;
+      } else {
+        f = mm16<D>(Qg + 16 * tt * LD, LD, 1, Kt + 16 * jt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+        df = mm16<D>(DOg + 16 * tt * LD, LD, 1, Wsrc + 16 * jt * WLD, 1, WLD, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
       if (16 * jt + c16 >= a.mr) f = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
