@@ -2084,6 +2084,12 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   float* const hv = a.dvk;
   float* const hk = a.dvk != nullptr ? a.dvk + (size_t)a.BH * a.n * D : nullptr;
   const float inv_l = 1.0f / (float)a.L;
+  // at bf16 I/O, S, dB and dQt_B run on the bf16 matrix cores: k (staged
+  // unscaled; S and the dQt_B partials take the d^-1/4 instead) and v are
+  // exact bf16 operands, Qt, dBV and dS split hi + lo (relative error about
+  // 2^-16); dv and dk stay on float32 products
+  constexpr bool BF = sizeof(IO) == 2;
+  const float ks = BF ? 1.f : a.s4;  // the scale staged with k
   // dQt_B tiles (landmark tile of the half, channel tile) owned by this wave: t = wave + NWV j
   constexpr int NACC = (TH * CT + NWV - 1) / NWV;
   for (int h = 0; h < NH; ++h) {
@@ -2114,7 +2120,7 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          Ks[r * LD + c + e] = xk[e] * a.s4;
+          Ks[r * LD + c + e] = xk[e] * ks;
           Vs[r * LD + c + e] = xv[e];
         }
       }
@@ -2126,8 +2132,31 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
       // B (from the stored normalisers) and dS_B = B (dBV V^T - D_i): C(landmark, key)
       for (int t = wave; t < TH * (BWD_GK / 16); t += NWV) {
         const int it = t / (BWD_GK / 16), kt = t % (BWD_GK / 16);
-        const f32x4 s = mm16<D>(Qt + 16 * it * LD, LD, 1, Ks + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 s, db;
+        if constexpr (BF) {
+          // A(landmark c16, channel 32 kb + 8g + e), B(channel, key c16)
+          s = db = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) {
+            const int ch = 32 * kb + 8 * g;
+            const Frag2 fq = split8(Qt + (16 * it + c16) * LD + ch);
+            const Frag2 fd = split8(dBV + (16 * it + c16) * LD + ch);
+            bf16x8 bk, bv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bk[e] = (__bf16)Ks[(16 * kt + c16) * LD + ch + e];
+              bv[e] = (__bf16)Vs[(16 * kt + c16) * LD + ch + e];
+            }
+            s = mfma(fq.hi, bk, s);
+            s = mfma(fq.lo, bk, s);
+            db = mfma(fd.hi, bv, db);
+            db = mfma(fd.lo, bv, db);
+          }
+          s *= a.s4;
+        } else {
+          s = mm16<D>(Qt + 16 * it * LD, LD, 1, Ks + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+          db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
         const float val = VAL[16 * kt + c16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -2173,7 +2202,18 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
         const int t = wave + NWV * j;
         if (t < TH * CT) {
           const int it = t / CT, ct = t % CT;
-          acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, LD, 1, acc[j]);
+          if constexpr (BF) {
+            // A(landmark c16, key 8g + e), B(key, channel c16)
+            static_assert(BWD_GK == 32, "one 16 x 16 x 32 product per step");
+            const Frag2 fs = split8(DS + (16 * it + c16) * LDB + 8 * g);
+            bf16x8 bk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bk[e] = (__bf16)Ks[(8 * g + e) * LD + 16 * ct + c16];
+            acc[j] = mfma(fs.hi, bk, acc[j]);
+            acc[j] = mfma(fs.lo, bk, acc[j]);
+          } else {
+            acc[j] = mm16<BWD_GK>(DS + 16 * it * LDB, LDB, 1, Ks + 16 * ct, LD, 1, acc[j]);
+          }
         }
       }
     }
@@ -2186,7 +2226,7 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = i0 + 16 * it + 4 * g + r;
-          if (row < M) pq[(size_t)row * D + 16 * ct + c16] = acc[j][r];
+          if (row < M) pq[(size_t)row * D + 16 * ct + c16] = (BF ? a.s4 : 1.f) * acc[j][r];
         }
       }
     }
