@@ -2047,9 +2047,13 @@ struct BwdKeyLayout {
   static constexpr int OFF_B = OFF_V + BWD_GK * LD;
   static constexpr int OFF_DS = OFF_B + MH * LDB;
   static constexpr int OFF_VAL = OFF_DS + MH * LDB;
-  static constexpr int FLOATS = OFF_VAL + BWD_GK;
+  // key-major copies of B (in B's area) and dS for the bf16 dv / dk products
+  static constexpr int LDT = MH + 4;
+  static constexpr int OFF_DST = OFF_VAL + BWD_GK;
+  static constexpr int FLOATS = OFF_DST + BWD_GK * LDT;
   static constexpr int BYTES = 4 * FLOATS;
   static_assert(BYTES <= 160 * 1024, "k_bwd_key LDS");
+  static_assert(BWD_GK * LDT <= MH * LDB, "the key-major B fits in B's area");
   static_assert(NHALF * MH >= M, "the halves cover every landmark");
 };
 
@@ -2090,6 +2094,14 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
   // 2^-16); dv and dk stay on float32 products
   constexpr bool BF = sizeof(IO) == 2;
   const float ks = BF ? 1.f : a.s4;  // the scale staged with k
+  // dv and dk on bf16 products as well where the half is whole 32-landmark
+  // blocks: B and dS also stored key-major (BtT, DST), and each wave's fixed
+  // channel tile of dBV and Qt split into fragments once per half
+  constexpr bool BFV = BF && MH % 32 == 0 && D == 64;
+  constexpr int LDT = Ly::LDT, NKB = BFV ? MH / 32 : 1;
+  float* const BtT = Bt;  // B's area
+  float* const DST = bw_lds + Ly::OFF_DST;
+  static_assert(!BFV || 2 * (BWD_GK / 16) * CT == 2 * NWV, "a dv and a dk tile per wave, same key and channel tile");
   // dQt_B tiles (landmark tile of the half, channel tile) owned by this wave: t = wave + NWV j
   constexpr int NACC = (TH * CT + NWV - 1) / NWV;
   for (int h = 0; h < NH; ++h) {
@@ -2104,6 +2116,22 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
     f32x4 acc[NACC];
 #pragma unroll
     for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag2 fbv[NKB], fbq[NKB];  // B(landmark 32 kb + 8g + e, channel 16 ct + c16) of dBV and Qt
+    if constexpr (BFV) {
+      __syncthreads();  // the half staged
+      const int ctw = wave % CT;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float xv[8], xq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xv[e] = dBV[(32 * kb + 8 * g + e) * LD + 16 * ctw + c16];
+          xq[e] = Qt[(32 * kb + 8 * g + e) * LD + 16 * ctw + c16];
+        }
+        fbv[kb] = split8(xv);
+        fbq[kb] = split8(xq);
+      }
+    }
     for (int gk = k0; gk < k1; gk += BWD_GK) {
       __syncthreads();  // staging done / previous step's reads done
       static_assert(BWD_GK * (D / 8) <= NT, "one chunk of K and of V per thread");
@@ -2158,13 +2186,21 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
           db = mm16<D>(dBV + 16 * it * LD, LD, 1, Vs + 16 * kt * LD, 1, LD, f32x4{0.f, 0.f, 0.f, 0.f});
         }
         const float val = VAL[16 * kt + c16];
+        float bq[4], dq[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int il = 16 * it + 4 * g + r, i = i0 + il;
           const bool on = val != 0.f && i < M;
-          const float bb = on ? exp2f(s[r] * LOG2E - lse[i]) : 0.f;
-          Bt[il * LDB + 16 * kt + c16] = bb;
-          DS[il * LDB + 16 * kt + c16] = i < M ? bb * (db[r] - Dv[i]) : 0.f;
+          bq[r] = on ? exp2f(s[r] * LOG2E - lse[i]) : 0.f;
+          dq[r] = i < M ? bq[r] * (db[r] - Dv[i]) : 0.f;
+          if constexpr (!BFV) Bt[il * LDB + 16 * kt + c16] = bq[r];
+          DS[il * LDB + 16 * kt + c16] = dq[r];
+        }
+        if constexpr (BFV) {
+          // key-major: the lane's four landmarks 16 it + 4g + r are consecutive
+          const int o = (16 * kt + c16) * LDT + 16 * it + 4 * g;
+          *reinterpret_cast<float4*>(BtT + o) = make_float4(bq[0], bq[1], bq[2], bq[3]);
+          *reinterpret_cast<float4*>(DST + o) = make_float4(dq[0], dq[1], dq[2], dq[3]);
         }
       }
       __syncthreads();
@@ -2172,8 +2208,15 @@ __global__ __launch_bounds__(BWD_KEY_NT) void k_bwd_key(BwdArgs a) {
       for (int t = wave; t < 2 * (BWD_GK / 16) * CT; t += NWV) {
         const bool isk = t >= (BWD_GK / 16) * CT;
         const int tt = t % ((BWD_GK / 16) * CT), kt = tt / CT, ct = tt % CT;
-        const f32x4 c = mm16<MH>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, LD, 1,
-                                 f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BFV) {
+          // A(key c16, landmark 32 kb + 8g + e) from the key-major copies
+          const float* const at = (isk ? DST : BtT) + (16 * kt + c16) * LDT + 8 * g;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) c = mma<3>(split8(at + 32 * kb), isk ? fbq[kb] : fbv[kb], c);
+        } else {
+          c = mm16<MH>((isk ? DS : Bt) + 16 * kt, 1, LDB, (isk ? Qt : dBV) + 16 * ct, LD, 1, c);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = gk + 16 * kt + 4 * g + r, ch = 16 * ct + c16;
