@@ -414,7 +414,9 @@ __global__ __launch_bounds__(64 * bwd_tok_waves<M>()) void k_bwd_tok(BwdArgs a) 
 // dout and q as exact bf16 operands (q staged unscaled; S and the dKt
 // partials take the d^-1/4 instead) and Kt, W, F, dS split hi + lo (two
 // products per 32-element contraction block; relative error about 2^-16).
-// dQs stays on float32 products.
+// Up to 192 landmarks dQs does too (three products per block, hi hi, hi lo,
+// lo hi): a wave's dQs tile has the same channel tile all through the
+// chunk, so its Kt fragments are split once into registers.
 template <int M>
 struct BwdTok3Layout {
   static constexpr int D = 64, NW = 8, GT = 32, LDF = M + 4, LD = D + 4;
@@ -467,6 +469,21 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
   f32x4 racc[NACC];
 #pragma unroll
   for (int j = 0; j < NACC; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // dQs on bf16 products: one tile per wave (token tile wave / CT, channel
+  // tile wave % CT), B(landmark 32 kb + 8g + e, channel c16) fragments of Kt
+  constexpr bool BFQ = BF && M <= 192 && M % 32 == 0 && 2 * CT == NW;
+  constexpr int NKB = BFQ ? M / 32 : 1;
+  Frag2 fk[NKB];
+  if constexpr (BFQ) {
+    __syncthreads();  // Kt staged
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float xk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xk[e] = Kt[(32 * kb + 8 * g + e) * LD + 16 * (wave % CT) + c16];
+      fk[kb] = split8(xk);
+    }
+  }
   for (int gs = t0; gs < t1; gs += GT) {
     // q (scaled) and dout rows of the group: eight lanes per token, eight channels each
     if (tid < 8 * GT) {
@@ -565,7 +582,15 @@ __global__ __launch_bounds__(64 * BwdTok3Layout<M>::NW) void k_bwd_tok3(BwdArgs 
     // dQs = dS Kt: tiles (token tile, channel tile) dealt over the waves
     for (int p = wave; p < 2 * CT; p += NW) {
       const int tt = p / CT, ct = p % CT;
-      const f32x4 c = mm16<M>(DSg + 16 * tt * LDF, LDF, 1, Kt + 16 * ct, LD, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BFQ) {
+        // A(token c16, landmark 32 kb + 8g + e)
+        const float* const ar = DSg + (16 * tt + c16) * LDF + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) c = mma<3>(split8(ar + 32 * kb), fk[kb], c);
+      } else {
+        c = mm16<M>(DSg + 16 * tt * LDF, LDF, 1, Kt + 16 * ct, LD, 1, c);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = gs + 16 * tt + 4 * g + r;
